@@ -1,0 +1,400 @@
+"""tGraph oracle: the canonical task/event-graph spec (v1) and a brute-force checker.
+
+TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.  Plain Python/numpy; it
+shares no code with the C++ builder and is compared with it bit for bit.
+
+What the pages fix (MPK summary page, "MPK: A Compiler and Runtime for
+Mega-Kernelizing Tensor Programs -- L2"):
+
+* section 2 (Q2, the method): operators are decomposed into per-tile tasks;
+  an event links two tasks iff the producer's output region overlaps the
+  consumer's input region; the graph is then fused, normalised and
+  linearised into a compact device structure;
+* section 4, "Successor-set fusion (Def 4.1)" and "Predecessor-set fusion
+  (Def 4.2)": events with equal consumer sets, then equal producer sets, merge;
+* section 4, "6 minimum checks" (check 3) and section 7 ("Empty tasks as
+  degree-reduction glue"): normalisation adds one event e' and k empty tasks
+  per fan-out so that every task has <= 1 dependent and <= 1 triggering event;
+* section 4 check 4 (Alg 1): BFS linearisation places the dependent tasks of
+  each dequeued event consecutively, so fan-out is a ``[first, last]`` range;
+* section 4, design-space table: JIT for data-dependent attention, AOT for
+  the rest.
+The HN comment (item 2) fixes the dependency rule: B depends on A iff A
+produces any element B consumes.
+
+Where the pages leave a step open the plainest reading is taken (order of
+Def 4.1 then Def 4.2; Kahn-style BFS that enqueues an event when its last
+producer is placed; a root event for sources and an end event for sinks;
+``counts(e) = |InTasks(e)|``; empty tasks numbered after the originals;
+round-robin AOT placement in linear order).  Balanced tiling: an operator
+with ``N`` output columns is cut, on a quantum of ``q`` columns, into ``T``
+tiles ``[q*floor(n*U/T), min(N, q*floor((n+1)*U/T)))`` with ``U = ceil(N/q)``.
+The fused q/k/v projection writes its columns group-major -- for kv group
+``g``: its ``G`` query heads, then its key head, then its value head -- and
+is tiled within each group (``T_qkv / n_kv_heads`` tiles per group), so each
+q/k-norm + RoPE task reads one contiguous column block produced by the tiles
+of its own group and no projection tile feeds two groups.
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass
+
+import numpy as np
+
+# task types
+EMBED, ATTN_NORM, QKV, QKNORM_ROPE, ATTN, COMBINE, OPROJ, MLP_NORM, GATEUP, DOWN, FINAL_NORM, LMHEAD, ARGMAX, \
+    EMPTY = range(14)
+TYPE_NAMES = ["EMBED", "ATTN_NORM", "QKV", "QKNORM_ROPE", "ATTN", "COMBINE", "OPROJ", "MLP_NORM", "GATEUP", "DOWN",
+              "FINAL_NORM", "LMHEAD", "ARGMAX", "EMPTY"]
+MODE_AOT, MODE_JIT, MODE_EMPTY = 0, 1, 2
+FLAG_HAS_JIT, FLAG_HAS_EMPTY = 1, 2
+
+# tensors: five shared ones, then 13 per layer
+T_E, T_HF, T_LOGITS, T_PMAX, T_NEXT = range(5)
+L_R, L_H, L_QKV, L_Q, L_KC, L_VC, L_PART, L_ATTN, L_O, L_S, L_H2, L_A, L_D = range(13)
+
+
+def layer_tensor(l, k):
+    return 5 + 13 * l + k
+
+
+@dataclass
+class Params:
+    W: int                # worker count
+    S_sched: int = 16     # scheduler wavefronts
+    q: int = 1            # column quantum of GEMV tiles
+    T_qkv: int = 1
+    T_o: int = 1
+    T_gu: int = 1
+    T_down: int = 1
+    T_lm: int = 1
+    S_attn: int = 1
+
+
+def tile_range(N, q, T, n):
+    U = -(-N // q)
+    return q * (n * U // T), min(N, q * ((n + 1) * U // T))
+
+
+def _box(tensor, lo, hi):
+    lo = tuple(lo) + (0,) * (4 - len(lo))
+    hi = tuple(hi) + (1,) * (4 - len(hi))
+    return (tensor, lo, hi)
+
+
+def decompose(cfg, B, P, prm: Params):
+    """Operators -> tasks with their input/output boxes, in program order.
+
+    Returns a list of dicts ``{type, layer, coords, ins, outs}``; a box is
+    ``(tensor_id, lo[4], hi[4])`` (half-open).
+    """
+    L = cfg["n_layers"]; H = cfg["hidden"]; hq = cfg["n_q_heads"]; hkv = cfg["n_kv_heads"]; d = cfg["head_dim"]
+    F = cfg["ffn"]; V = cfg["vocab"]; S = prm.S_attn
+    G = hq // hkv
+    Sg = (G + 2) * d          # qkv columns of one kv group: G q heads, then k, then v
+    maxs = cfg["max_seq_len"]
+    tasks = []
+
+    def add(tp, layer, coords, ins, outs):
+        c = tuple(coords) + (0,) * (3 - len(coords))
+        tasks.append(dict(type=tp, layer=layer, coords=c, ins=ins, outs=outs))
+
+    add(EMBED, -1, (), [], [_box(T_E, (0, 0), (B, H))])
+    for l in range(L):
+        t = lambda k: layer_tensor(l, k)
+        if l == 0:
+            ins = [_box(T_E, (0, 0), (B, H))]
+        else:
+            ins = [_box(layer_tensor(l - 1, L_S), (0, 0), (B, H)), _box(layer_tensor(l - 1, L_D), (0, 0), (B, H))]
+        add(ATTN_NORM, l, (), ins, [_box(t(L_R), (0, 0), (B, H)), _box(t(L_H), (0, 0), (B, H))])
+        tpg = prm.T_qkv // hkv
+        for n in range(prm.T_qkv):
+            g, j = divmod(n, tpg)
+            lo, hi = tile_range(Sg, prm.q, tpg, j)
+            add(QKV, l, (n,), [_box(t(L_H), (0, 0), (B, H))], [_box(t(L_QKV), (0, g * Sg + lo), (B, g * Sg + hi))])
+        for b in range(B):
+            for g in range(hkv):
+                ins = [_box(t(L_QKV), (b, g * Sg), (b + 1, (g + 1) * Sg))]
+                outs = [_box(t(L_Q), (b, g * G * d), (b + 1, (g + 1) * G * d)),
+                        _box(t(L_KC), (b, 0, g, 0), (b + 1, maxs, g + 1, d)),
+                        _box(t(L_VC), (b, 0, g, 0), (b + 1, maxs, g + 1, d))]
+                add(QKNORM_ROPE, l, (b, g), ins, outs)
+        for b in range(B):
+            for g in range(hkv):
+                for s in range(S):
+                    ins = [_box(t(L_Q), (b, g * G * d), (b + 1, (g + 1) * G * d)),
+                           _box(t(L_KC), (b, 0, g, 0), (b + 1, maxs, g + 1, d)),
+                           _box(t(L_VC), (b, 0, g, 0), (b + 1, maxs, g + 1, d))]
+                    add(ATTN, l, (b, g, s), ins, [_box(t(L_PART), (b, g, s, 0), (b + 1, g + 1, s + 1, G * (d + 2)))])
+        for b in range(B):
+            for g in range(hkv):
+                add(COMBINE, l, (b, g), [_box(t(L_PART), (b, g, 0, 0), (b + 1, g + 1, S, G * (d + 2)))],
+                    [_box(t(L_ATTN), (b, g * G * d), (b + 1, (g + 1) * G * d))])
+        for n in range(prm.T_o):
+            lo, hi = tile_range(H, prm.q, prm.T_o, n)
+            add(OPROJ, l, (n,), [_box(t(L_ATTN), (0, 0), (B, hq * d))], [_box(t(L_O), (0, lo), (B, hi))])
+        add(MLP_NORM, l, (), [_box(t(L_R), (0, 0), (B, H)), _box(t(L_O), (0, 0), (B, H))],
+            [_box(t(L_S), (0, 0), (B, H)), _box(t(L_H2), (0, 0), (B, H))])
+        for n in range(prm.T_gu):
+            lo, hi = tile_range(F, prm.q, prm.T_gu, n)
+            add(GATEUP, l, (n,), [_box(t(L_H2), (0, 0), (B, H))], [_box(t(L_A), (0, lo), (B, hi))])
+        for n in range(prm.T_down):
+            lo, hi = tile_range(H, prm.q, prm.T_down, n)
+            add(DOWN, l, (n,), [_box(t(L_A), (0, 0), (B, F))], [_box(t(L_D), (0, lo), (B, hi))])
+    add(FINAL_NORM, -1, (), [_box(layer_tensor(L - 1, L_S), (0, 0), (B, H)),
+                             _box(layer_tensor(L - 1, L_D), (0, 0), (B, H))], [_box(T_HF, (0, 0), (B, H))])
+    for n in range(prm.T_lm):
+        lo, hi = tile_range(V, prm.q, prm.T_lm, n)
+        add(LMHEAD, -1, (n,), [_box(T_HF, (0, 0), (B, H))],
+            [_box(T_LOGITS, (0, lo), (B, hi)), _box(T_PMAX, (0, n, 0), (B, n + 1, 2))])
+    add(ARGMAX, -1, (), [_box(T_PMAX, (0, 0, 0), (B, prm.T_lm, 2))], [_box(T_NEXT, (0,), (B,))])
+    return tasks
+
+
+def producer_sets(tasks):
+    """Brute-force overlap dependencies: ``P[c]`` = producers ``p < c`` whose
+    output box meets an input box of ``c`` on the same tensor (all dims)."""
+    outs, ins = {}, {}
+    for i, t in enumerate(tasks):
+        for (tn, lo, hi) in t["outs"]:
+            outs.setdefault(tn, []).append((i, lo, hi))
+        for (tn, lo, hi) in t["ins"]:
+            ins.setdefault(tn, []).append((i, lo, hi))
+    P = [set() for _ in tasks]
+    for tn, il in ins.items():
+        ol = outs.get(tn)
+        if not ol:
+            continue
+        ot = np.array([x[0] for x in ol]); olo = np.array([x[1] for x in ol]); ohi = np.array([x[2] for x in ol])
+        it = np.array([x[0] for x in il]); ilo = np.array([x[1] for x in il]); ihi = np.array([x[2] for x in il])
+        ov = np.all((olo[:, None, :] < ihi[None, :, :]) & (ilo[None, :, :] < ohi[:, None, :]), axis=2)
+        ov &= ot[:, None] < it[None, :]
+        pi, ci = np.nonzero(ov)
+        for a, b in zip(ot[pi], it[ci]):
+            P[int(b)].add(int(a))
+    return P
+
+
+def canonicalize(tasks, W):
+    """Fusion (Def 4.1 then 4.2), normalisation, Kahn-BFS linearisation,
+    classification and AOT placement.  Returns the exported arrays (dict)."""
+    N = len(tasks)
+    P = producer_sets(tasks)
+
+    # Def 4.1: one event per consumer with all its producers; Def 4.2: merge equal producer sets.
+    groups = {}
+    for c in range(N):
+        if P[c]:
+            groups.setdefault(frozenset(P[c]), []).append(c)
+    fused = sorted(([sorted(k), sorted(v)] for k, v in groups.items()), key=lambda e: min(e[1]))
+    # fixpoint: Out-sets disjoint, In-sets distinct
+    seen_out = set()
+    for _, o in fused:
+        assert not (seen_out & set(o))
+        seen_out |= set(o)
+    assert len({tuple(i) for i, _ in fused}) == len(fused)
+
+    ev_in = [list(i) for i, _ in fused]
+    ev_out = [list(o) for _, o in fused]
+    dep = {}
+    trig = {}
+    for e, o in enumerate(ev_out):
+        for c in o:
+            dep[c] = e
+    trigs_of = [[] for _ in range(N)]
+    for e, i in enumerate(ev_in):
+        for p in i:
+            trigs_of[p].append(e)        # already in pre-order (fused is sorted)
+
+    ttype = [t["type"] for t in tasks]
+    tlayer = [t["layer"] for t in tasks]
+    tcoords = [t["coords"] for t in tasks]
+    torig = list(range(N))
+    n_empty = 0
+    for t in range(N):
+        tr = trigs_of[t]
+        if len(tr) >= 2:
+            ep = len(ev_in)
+            ev_in.append([t]); ev_out.append([])
+            for i, e in enumerate(tr):
+                T = len(ttype)
+                ttype.append(EMPTY); tlayer.append(tlayer[t]); tcoords.append((i, 0, 0))
+                torig.append(-1 - n_empty); n_empty += 1
+                dep[T] = ep; trig[T] = e
+                ev_out[ep].append(T)
+                ev_in[e] = [T if x == t else x for x in ev_in[e]]
+            trig[t] = ep
+        elif len(tr) == 1:
+            trig[t] = tr[0]
+    NT = len(ttype)
+    root = len(ev_in); ev_in.append([]); ev_out.append([])
+    end = len(ev_in); ev_in.append([]); ev_out.append([])
+    for t in range(NT):
+        if t not in dep:
+            dep[t] = root; ev_out[root].append(t)
+        if t not in trig:
+            trig[t] = end; ev_in[end].append(t)
+    NE = len(ev_in)
+    counts = [len(x) for x in ev_in]
+
+    # Kahn-BFS linearisation
+    indeg = list(counts)
+    new_ev = [-1] * NE; new_task = [-1] * NT
+    first = [0] * NE; last = [0] * NE
+    q = deque([root]); ne = 0; nt = 0
+    while q:
+        e = q.popleft()
+        new_ev[e] = ne; ne += 1
+        first[e] = nt
+        for t in sorted(ev_out[e]):
+            new_task[t] = nt; nt += 1
+            f = trig[t]
+            indeg[f] -= 1
+            if indeg[f] == 0:
+                q.append(f)
+        last[e] = nt - 1
+    if nt != NT:
+        raise ValueError("tGraph has a cycle")
+
+    order = sorted(range(NT), key=lambda t: new_task[t])
+    eorder = sorted(range(NE), key=lambda e: new_ev[e])
+    mode = {EMPTY: MODE_EMPTY, ATTN: MODE_JIT}
+    out = {
+        "task_type": np.array([ttype[t] for t in order], dtype=np.uint8),
+        "task_mode": np.array([mode.get(ttype[t], MODE_AOT) for t in order], dtype=np.uint8),
+        "task_layer": np.array([tlayer[t] for t in order], dtype=np.int16),
+        "task_coords": np.array([tcoords[t] for t in order], dtype=np.uint16).reshape(NT, 3),
+        "task_orig": np.array([torig[t] for t in order], dtype=np.int32),
+        "task_dep": np.array([new_ev[dep[t]] for t in order], dtype=np.int32),
+        "task_trig": np.array([new_ev[trig[t]] for t in order], dtype=np.int32),
+        "event_counts": np.array([counts[e] for e in eorder], dtype=np.uint32),
+        "event_first": np.array([first[e] for e in eorder], dtype=np.int32),
+        "event_last": np.array([last[e] for e in eorder], dtype=np.int32),
+    }
+    flags = np.zeros(NE, dtype=np.uint8)
+    for e in range(NE):
+        for t in ev_out[e]:
+            m = mode.get(ttype[t], MODE_AOT)
+            if m == MODE_JIT:
+                flags[new_ev[e]] |= FLAG_HAS_JIT
+            elif m == MODE_EMPTY:
+                flags[new_ev[e]] |= FLAG_HAS_EMPTY
+    out["event_flags"] = flags
+    worker = np.full(NT, -1, dtype=np.int16)
+    lists = [[] for _ in range(W)]
+    k = 0
+    for i in range(NT):
+        if out["task_mode"][i] == MODE_AOT:
+            worker[i] = k % W
+            lists[k % W].append(i)
+            k += 1
+    out["task_worker"] = worker
+    out["aot_offsets"] = np.array(np.cumsum([0] + [len(x) for x in lists]), dtype=np.uint32)
+    out["aot_tasks"] = np.array([i for x in lists for i in x], dtype=np.uint32)
+    out["header"] = dict(NT=NT, NE=NE, root=new_ev[root], end=new_ev[end], n_fused=len(fused),
+                         n_empty=n_empty, n_rewrites=len(ev_in) - 2 - len(fused))
+    return out
+
+
+def build(cfg, B, P, prm: Params):
+    """The whole spec for a decoder: decompose, then canonicalise."""
+    tasks = decompose(cfg, B, P, prm)
+    return canonicalize(tasks, prm.W), tasks
+
+
+# ----------------------------------------------------------------------------- checker
+def check_semantics(g, tasks=None, closure=True):
+    """Checks that hold for any correct tGraph, independent of the spec's
+    numbering choices.  Raises AssertionError on the first violation.
+
+    * each task has exactly one dependent and one triggering event, neither
+      is the wrong end of the graph;
+    * each event's dependent tasks are exactly ``[first, last]`` (contiguity);
+    * ``counts(e)`` equals the number of tasks that trigger ``e``;
+    * the linear order is topological; AOT lists increase; modes/flags agree;
+    * with ``tasks`` given and ``closure``: over real tasks, "c waits for p"
+      in the final graph equals the transitive closure of the overlap edges.
+    """
+    NT = len(g["task_type"]); NE = len(g["event_counts"])
+    hdr = g["header"]
+    root, end = hdr["root"], hdr["end"]
+    dep = g["task_dep"].astype(np.int64); trig = g["task_trig"].astype(np.int64)
+    assert np.all((dep >= 0) & (dep < NE)) and np.all((trig >= 0) & (trig < NE))
+    assert not np.any(dep == end) and not np.any(trig == root)
+    # contiguity
+    first = g["event_first"].astype(np.int64); last = g["event_last"].astype(np.int64)
+    for e in range(NE):
+        idx = np.nonzero(dep == e)[0]
+        if len(idx) == 0:
+            assert first[e] == last[e] + 1, e
+        else:
+            assert idx[0] == first[e] and idx[-1] == last[e] and len(idx) == last[e] - first[e] + 1, e
+    # counts
+    cnt = np.bincount(trig, minlength=NE)
+    assert np.array_equal(cnt, g["event_counts"].astype(np.int64))
+    assert g["event_counts"][root] == 0
+    # topological: every producer of dep(t) precedes t
+    maxprod = np.full(NE, -1, dtype=np.int64)
+    np.maximum.at(maxprod, trig, np.arange(NT))
+    assert np.all(maxprod[dep] < np.arange(NT))
+    # degree-1 structure and modes
+    tt = g["task_type"]; md = g["task_mode"]
+    assert np.all((md == MODE_JIT) == (tt == ATTN)) and np.all((md == MODE_EMPTY) == (tt == EMPTY))
+    for e in range(NE):
+        cons = md[first[e]:last[e] + 1]
+        f = (FLAG_HAS_JIT if np.any(cons == MODE_JIT) else 0) | (FLAG_HAS_EMPTY if np.any(cons == MODE_EMPTY) else 0)
+        assert g["event_flags"][e] == f
+    # AOT lists
+    off = g["aot_offsets"].astype(np.int64); lst = g["aot_tasks"].astype(np.int64)
+    W = len(off) - 1
+    assert off[0] == 0 and off[-1] == len(lst) == int(np.sum(md == MODE_AOT))
+    for w in range(W):
+        seg = lst[off[w]:off[w + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all(g["task_worker"][seg] == w)
+    assert np.all((g["task_worker"] >= 0) == (md == MODE_AOT))
+    if tasks is not None and closure:
+        _check_closure(g, tasks)
+
+
+def _check_closure(g, tasks):
+    N = len(tasks)
+    P = producer_sets(tasks)
+    # closure of the original overlap edges (program order is topological)
+    reach = [0] * N
+    for c in range(N):
+        r = 0
+        for p in P[c]:
+            r |= reach[p] | (1 << p)
+        reach[c] = r
+    # closure of the final graph, restricted to real tasks, in original ids
+    NT = len(g["task_type"])
+    orig = g["task_orig"]; dep = g["task_dep"]; trig = g["task_trig"]
+    prods = {}
+    for t in range(NT):
+        prods.setdefault(int(trig[t]), []).append(t)
+    waits = [0] * NT
+    for t in range(NT):
+        r = 0
+        for p in prods.get(int(dep[t]), []):
+            r |= waits[p]
+            if orig[p] >= 0:
+                r |= 1 << int(orig[p])
+        waits[t] = r
+    seen = 0
+    for t in range(NT):
+        if orig[t] >= 0:
+            assert waits[t] == reach[int(orig[t])], f"closure differs at task {t} (orig {orig[t]})"
+            seen += 1
+    assert seen == N
+
+
+def generic_tasks(specs, regions):
+    """Tasks for the generic canonicalisation entry: ``specs`` is a list of
+    ``(type, layer, c0, c1, c2)``; ``regions`` a list of
+    ``(task, is_out, tensor, lo[4], hi[4])``."""
+    tasks = [dict(type=s[0], layer=s[1], coords=tuple(s[2:5]), ins=[], outs=[]) for s in specs]
+    for (t, is_out, tn, lo, hi) in regions:
+        tasks[t]["outs" if is_out else "ins"].append((tn, tuple(lo), tuple(hi)))
+    return tasks

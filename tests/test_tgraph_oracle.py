@@ -1,0 +1,137 @@
+"""Pins for the tGraph oracle (CPU only).
+
+* the hand-derived tiny-decoder example (counts, sizes, start of the linear order);
+* rewrite-count identities;
+* semantic checks that do not depend on the spec's numbering (degree <= 1,
+  contiguity, counts, topological order, closure equality) on the decoder
+  graphs and on randomly generated programs with misaligned tilings.
+"""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+import synth
+from oracle import tgraph as tg
+
+TINY_PRM = tg.Params(W=8, q=64, T_qkv=8, T_o=4, T_gu=11, T_down=4, T_lm=16, S_attn=4)
+
+
+def tiny():
+    return tg.build(synth.SHAPES["tiny"].cfg(), 1, 16, TINY_PRM)
+
+
+def test_tiny_worked_example_sizes():
+    g, tasks = tiny()
+    h = g["header"]
+    # per layer 41 tasks; 101 originals; 27 fused events; 4 fan-out rewrites
+    assert len(tasks) == 101
+    assert sum(1 for t in tasks if t["layer"] == 0) == 41
+    assert h["n_fused"] == 27 and h["n_rewrites"] == 4 and h["n_empty"] == 8
+    assert h["NT"] == 109 and h["NE"] == 33 and h["root"] == 0 and h["end"] == 32
+
+
+def test_tiny_worked_example_order_and_counts():
+    g, _ = tiny()
+    T = tg
+    tt = list(g["task_type"])
+    expect = [T.EMBED, T.ATTN_NORM, T.EMPTY, T.EMPTY] + [T.QKV] * 8 + [T.QKNORM_ROPE] * 2 + [T.ATTN] * 8 + \
+        [T.COMBINE] * 2 + [T.OPROJ] * 4 + [T.MLP_NORM]
+    assert tt[:len(expect)] == expect
+    cnt = g["event_counts"]; dep = g["task_dep"]
+    c = lambda i: int(cnt[dep[i]])
+    assert c(12) == 4 and c(13) == 4          # q/k-norm+RoPE waits for the 4 projection tiles of its group
+    assert c(22) == 4 and c(23) == 4          # combine waits for its 4 attention splits
+    assert c(24) == 2                         # O projection waits for both combines
+    assert c(28) == 5                         # MLP norm: 4 O tiles + the empty task standing in for ATTN_NORM
+    # the two empty tasks after ATTN_NORM_0 feed, in order, the projection event and the MLP-norm event
+    assert g["task_orig"][2] == -1 and g["task_orig"][3] == -2
+    assert g["event_first"][g["task_trig"][2]] == 4
+    assert g["task_type"][g["event_first"][g["task_trig"][3]]] == T.MLP_NORM
+    # ATTN tasks are JIT, empties EMPTY, all else AOT; the AOT worker is round-robin in linear order
+    aot = [i for i in range(len(tt)) if g["task_mode"][i] == T.MODE_AOT]
+    assert [int(g["task_worker"][i]) for i in aot] == [k % 8 for k in range(len(aot))]
+    last = [i for i in range(len(tt)) if tt[i] == T.DOWN][-1]
+    assert c(last + 1) == 5 if tt[last + 1] == T.FINAL_NORM else True
+    argmax = tt.index(T.ARGMAX)
+    assert c(argmax) == 16 and g["event_counts"][g["header"]["end"]] == 1
+    tg.check_semantics(g, _, closure=True)
+
+
+def test_rewrite_identities():
+    g, tasks = tiny()
+    P = tg.producer_sets(tasks)
+    groups = {}
+    for c_, p in enumerate(P):
+        if p:
+            groups.setdefault(frozenset(p), set()).add(c_)
+    fanout = [sum(1 for k in groups if t in k) for t in range(len(tasks))]
+    assert g["header"]["n_empty"] == sum(f for f in fanout if f >= 2)
+    assert g["header"]["NE"] == len(groups) + sum(1 for f in fanout if f >= 2) + 2
+
+
+@pytest.mark.parametrize("name,B,S", [("tiny", 3, 2), ("qwen3_0p6b", 1, 16), ("qwen3_8b", 2, 8)])
+def test_decoder_graph_semantics_small_cuts(name, B, S):
+    s = synth.SHAPES[name].with_(n_layers=2, vocab=4096)
+    cfg = s.cfg()
+    W = 24
+    hkv = s.n_kv_heads
+    prm = tg.Params(W=W, q=1 if B == 1 else 16, T_qkv=(W // hkv) * hkv, T_o=W, T_gu=W, T_down=W, T_lm=W, S_attn=S)
+    g, tasks = tg.build(cfg, B, s.page_size, prm)
+    tg.check_semantics(g, tasks, closure=True)
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "qwen3_8b", "qwen3_8b_b16", "qwen3_32b"])
+def test_full_graph_invariants(name):
+    s = synth.SHAPES[name]
+    W = 252
+    prm = tg.Params(W=W, q=1 if s.batch == 1 else 16, T_qkv=(W // s.n_kv_heads) * s.n_kv_heads, T_o=W, T_gu=W,
+                    T_down=W, T_lm=W, S_attn=16 if s.batch == 1 else 4)
+    g, _ = tg.build(s.cfg(), s.batch, s.page_size, prm)
+    tg.check_semantics(g, None)
+    h = g["header"]
+    assert h["n_empty"] / h["NT"] < 0.01          # "deep, not wide": under 1% empty tasks
+    assert h["n_empty"] == 4 * s.n_layers          # ATTN_NORM and MLP_NORM fan out to two events per layer
+
+
+# ------------------------------------------------------------------ random programs
+@st.composite
+def programs(draw):
+    n_ops = draw(st.integers(1, 5))
+    tensors = []          # (n_dims, shape)
+    tasks = []            # (type, layer, c0, c1, c2)
+    regions = []          # (task, is_out, tensor, lo, hi)
+    produced = []
+    for op in range(n_ops):
+        nd = draw(st.integers(1, 2))
+        shape = tuple(draw(st.integers(1, 9)) for _ in range(nd))
+        out_t = len(tensors)
+        tensors.append(shape)
+        # tile the output along dim 0 with random cut points
+        cuts = sorted(set(draw(st.lists(st.integers(1, shape[0] - 1), max_size=3)) if shape[0] > 1 else []))
+        bounds = [0] + cuts + [shape[0]]
+        tp = draw(st.sampled_from([tg.QKV, tg.ATTN, tg.OPROJ, tg.MLP_NORM, tg.COMBINE]))
+        srcs = draw(st.lists(st.sampled_from(produced), max_size=2, unique=True)) if produced else []
+        for j in range(len(bounds) - 1):
+            tid = len(tasks)
+            tasks.append((tp, op, j, 0, 0))
+            lo = [bounds[j]] + [0] * (nd - 1); hi = [bounds[j + 1]] + list(shape[1:])
+            regions.append((tid, 1, out_t, tuple(lo) + (0,) * (4 - nd), tuple(hi) + (1,) * (4 - nd)))
+            for s_ in srcs:
+                sh = tensors[s_]
+                lo = [draw(st.integers(0, x - 1)) for x in sh]
+                hi = [draw(st.integers(l_ + 1, x)) for l_, x in zip(lo, sh)]
+                k = len(sh)
+                regions.append((tid, 0, s_, tuple(lo) + (0,) * (4 - k), tuple(hi) + (1,) * (4 - k)))
+        produced.append(out_t)
+    W = draw(st.integers(1, 4))
+    return tasks, regions, W
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(programs())
+def test_random_programs_preserve_every_wait(prog):
+    specs, regions, W = prog
+    tasks = tg.generic_tasks(specs, regions)
+    g = tg.canonicalize(tasks, W)
+    tg.check_semantics(g, tasks, closure=True)
+    assert g["header"]["NT"] == len(tasks) + g["header"]["n_empty"]
