@@ -1,0 +1,172 @@
+"""Decode-step benchmark: one persistent-kernel launch per token on one MI355X.
+
+Default workload: the Qwen3-8B-shaped decoder at batch 1 with 1024 cached
+tokens (bf16 random weights, synthetic inputs resident in HBM).  Prints ONE
+JSON line: decode ms/token (the value), achieved HBM bandwidth against the
+8 TB/s peak, the kernel-per-operator baseline of the same task bodies (plain
+launches and hipGraph replay), and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config qwen3_8b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode ms/token + achieved HBM TB/s (% peak), Qwen3-8B-shape batch 1"
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(s, seq_lens) -> int:
+    """Bytes the step must move: every weight once (projections, norm gains,
+    LM head or tied embedding), B embedding rows and the K/V of L_b + 1 tokens
+    per request and layer; all bf16."""
+    H, d, hq, hkv, F, V, L = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads, s.ffn, s.vocab, s.n_layers
+    per_layer = hq * d * H + 2 * hkv * d * H + H * hq * d + 3 * F * H + 2 * H + (2 * d if s.qk_norm else 0)
+    w = L * per_layer + H + V * H
+    kv = sum(int(x) + 1 for x in seq_lens) * L * 2 * hkv * d
+    return 2 * (w + len(seq_lens) * H + kv)
+
+
+def time_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [a.elapsed_time(b) for a, b in ev]
+    return wall_ms, per
+
+
+def cpu_baseline(s, inp, budget_layers=(2, 4)):
+    """The oracle, as it stands, on a bounded sample: the step cut to k1 and k2
+    layers (embedding, final norm and LM head included); the per-layer cost is
+    the difference, extrapolated to all layers."""
+    import numpy as np
+    from oracle import numerics
+    from tests._util import oracle_weights, bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        cores = os.cpu_count()
+    kv = inp["kv"]
+    k1, k2 = budget_layers
+    w = inp["weights"]
+    times = {}
+    for k in (k1, k2):
+        sk = s.with_(n_layers=k)
+        wk = {"embed": w["embed"], "final_norm": w["final_norm"], "lm_head": w["lm_head"], "layers": w["layers"][:k]}
+        ow = oracle_weights(wk, lazy=True)
+        kp = bf16_bits(kv["k_pool"][:k]); vp = bf16_bits(kv["v_pool"][:k])
+        t0 = time.perf_counter()
+        numerics.decode_step(sk.cfg(), ow, inp["token_ids"].cpu().numpy(), kp, vp, kv["page_table"].cpu().numpy(),
+                             inp["seq_lens"].cpu().numpy(), s.page_size, dtype=np.float32)
+        times[k] = time.perf_counter() - t0
+    per_layer = (times[k2] - times[k1]) / (k2 - k1)
+    fixed = times[k1] - k1 * per_layer
+    est_ms = (fixed + s.n_layers * per_layer) * 1e3
+    return {"value": round(est_ms, 1), "unit": "ms/token", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp32 numpy oracle run cut to {k1} and {k2} of {s.n_layers} layers (weights widened from bf16 "
+                      f"per call, copied per layer from the GPU, copy included); per-layer cost = difference, "
+                      f"extrapolated to {s.n_layers} layers; measured {times[k1]:.1f} s and {times[k2]:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3_8b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--baseline-steps", type=int, default=20)
+    ap.add_argument("--no-baseline", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode step is built and measured on a single MI355X "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import task_graph_runtime_amd as mpk
+
+    s = synth.SHAPES[args.config]
+    print(f"[bench] generating {s.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(s, seed=args.seed, device="cuda")
+    kv = inp["kv"]
+    ids = inp["token_ids"].cuda()
+    lens = inp["seq_lens"].cuda()
+    g = mpk.TGraph(s.cfg(), s.batch, s.page_size)
+    W = mpk.Weights(inp["weights"])
+    KV = mpk.KV(kv["k_pool"], kv["v_pool"], kv["page_table"].cuda())
+    logits = torch.empty((s.batch, s.vocab), device="cuda", dtype=torch.float32)
+    nxt = torch.empty((s.batch,), device="cuda", dtype=torch.int32)
+
+    def mega():
+        g.decode_step(W, ids, KV, lens, logits, nxt)
+
+    print(f"[bench] mega-kernel: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    wall_ms, per = time_steps(mega, args.steps, args.warmup, torch)
+    st = g.status()
+    if st["code"] != 0:
+        raise SystemExit(f"mega-kernel reported {st}")
+    ms = wall_ms / args.steps
+    kern_ms = statistics.mean(per)
+    nbytes = algorithmic_bytes(s, inp["seq_lens"].tolist())
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+
+    base = {}
+    if not args.no_baseline:
+        for mode, hg in (("per_op", False), ("hipgraph", True)):
+            print(f"[bench] baseline {mode}", file=sys.stderr, flush=True)
+            f = (lambda hg=hg: g.decode_step_baseline(W, ids, KV, lens, logits, nxt, use_hipgraph=hg))
+            _, pb = time_steps(f, args.baseline_steps, 3, torch)
+            base[mode] = round(statistics.median(pb), 4)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(s, inp)
+
+    hdr = g.header()["params"]
+    out = {
+        "metric": METRIC, "value": round(ms, 4), "unit": "ms/token", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (random-init bf16 weights, N(0,1) KV)",
+        "config": {"workload": f"{s.name} decode step, batch {s.batch}, "
+                               f"{'ctx ' + str(s.ctx) if s.ctx_range is None else 'ctx U' + str(list(s.ctx_range))}, "
+                               f"page {s.page_size}",
+                   "global_batch": s.batch, "seq_len": int(max(inp['seq_lens'].tolist())) + 1,
+                   "parallelism": "single GPU", "workers": hdr["n_workers"], "sched_waves": hdr["n_sched_waves"],
+                   "s_attn": hdr["s_attn"]},
+        "tb_per_s": round(achieved / 1e3, 3), "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 1),
+        "kernel_ms": {"mean": round(kern_ms, 4), "median": round(statistics.median(per), 4),
+                      "p10": round(sorted(per)[len(per) // 10], 4), "p90": round(sorted(per)[(9 * len(per)) // 10], 4)},
+        "bytes_per_step": nbytes,
+        "baseline_ms": base or None,
+        "speedup_vs_baseline": round(min(base.values()) / kern_ms, 3) if base else None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

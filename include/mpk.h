@@ -1,0 +1,239 @@
+/*
+ * mpk.h -- C ABI of the MI355X (gfx950) decode-step mega-kernel library.
+ *
+ * One transformer decode step of a Qwen3-shaped decoder runs as a single
+ * persistent kernel that executes a task/event graph (tGraph) built on the
+ * host ahead of time.  The method is the one summarised on the page "MPK: A
+ * Compiler and Runtime for Mega-Kernelizing Tensor Programs -- L2":
+ *   - section 2 (Q2): operators become per-tile tasks joined by events; an
+ *     event exists iff a producer's output region overlaps a consumer's input
+ *     region; the graph is fused, normalised and linearised into a compact
+ *     device structure, and an in-kernel runtime of workers (FIFO task queues)
+ *     and schedulers (event queues) runs it with a hybrid JIT/AOT launch policy;
+ *   - section 3, "Target operation, shapes & precision contract": MatMul tasks
+ *     with bf16 inputs/outputs and fp32 accumulation; paged-attention decode
+ *     tasks of data-dependent duration (the JIT ones);
+ *   - section 4, Def 4.1 / Def 4.2, "6 minimum checks", Table 1 and the
+ *     design-space table: fusion, normalisation (<= 1 dependent and <= 1
+ *     triggering event per task), BFS linearisation ([first, last] fan-out),
+ *     scheduler budget of 4 compute units x 4 wavefronts.
+ *
+ * Conventions for every entry point:
+ *   - returns MPK_OK (0) or a negative MPK_ERR_* code and never throws; the
+ *     message of the last failure on the calling thread is mpk_last_error();
+ *   - "device pointer" means memory of the current HIP device, owned by the
+ *     caller unless stated otherwise; "host pointer" means ordinary memory;
+ *   - streams are passed as `void*` holding a hipStream_t (NULL = default
+ *     stream), so this header needs no HIP include;
+ *   - all bf16 data is IEEE bfloat16 (upper half of binary32), matrices are
+ *     row-major [out_features][in_features] (the nn.Linear layout).
+ */
+#ifndef MPK_H
+#define MPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MPK_OK = 0,
+  MPK_ERR_INVALID_ARG = -1, /* null pointer, bad size, config/graph mismatch */
+  MPK_ERR_UNSUPPORTED = -2, /* shape or device outside what the kernels handle */
+  MPK_ERR_HIP = -3,         /* a HIP runtime call failed */
+  MPK_ERR_GRAPH = -4,       /* the task graph has a cycle (cannot happen for the decoder) */
+  MPK_ERR_TIMEOUT = -5,     /* an in-kernel wait exceeded the watchdog; graph is poisoned */
+  MPK_ERR_NOMEM = -6        /* host or device allocation failed */
+};
+
+/* Task types of the decoder tGraph (the order is the program order of one layer). */
+enum {
+  MPK_TASK_EMBED = 0,       /* e[b,:] = E[token_ids[b], :] (fp32)                        */
+  MPK_TASK_ATTN_NORM = 1,   /* r = residual in; h = RMSNorm(r) (bf16)                    */
+  MPK_TASK_QKV = 2,         /* tile of the fused q/k/v projection (group-major columns)  */
+  MPK_TASK_QKNORM_ROPE = 3, /* per (b, kv group): q/k RMSNorm, RoPE, KV-cache append     */
+  MPK_TASK_ATTN = 4,        /* per (b, kv group, split): paged attention partials (JIT)  */
+  MPK_TASK_COMBINE = 5,     /* per (b, kv group): merge split partials (log-sum-exp)     */
+  MPK_TASK_OPROJ = 6,       /* tile of the output projection                             */
+  MPK_TASK_MLP_NORM = 7,    /* s = r + o; h2 = RMSNorm(s)                                */
+  MPK_TASK_GATEUP = 8,      /* tile of gate/up projections with the SwiGLU epilogue      */
+  MPK_TASK_DOWN = 9,        /* tile of the down projection                               */
+  MPK_TASK_FINAL_NORM = 10, /* hf = RMSNorm(s + d) of the last layer                     */
+  MPK_TASK_LMHEAD = 11,     /* tile of the LM head: fp32 logits + per-tile (max, argmax) */
+  MPK_TASK_ARGMAX = 12,     /* next_ids[b] = argmax over tile partials (lowest index)    */
+  MPK_TASK_EMPTY = 13       /* no compute; inserted by normalisation                     */
+};
+enum { MPK_MODE_AOT = 0, MPK_MODE_JIT = 1, MPK_MODE_EMPTY = 2 };
+enum { MPK_EVENT_HAS_JIT = 1, MPK_EVENT_HAS_EMPTY = 2 };
+
+/* Decoder shape.  n_q_heads must be a multiple of n_kv_heads; head_dim is 64
+ * or 128; hidden and ffn are multiples of 8.  RMSNorm is
+ * v / sqrt(mean(v^2) + rms_eps) * gamma; RoPE is rotate-half with angles
+ * pos * rope_theta^(-2i/head_dim). */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, max_seq_len;
+  int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE */
+  int32_t tied_embedding; /* 1: the LM head is the embedding matrix */
+  float rms_eps, rope_theta;
+} mpk_model_cfg;
+
+/* Build parameters; a zero field takes its default (shown).  They are part of
+ * the exported header so that a checker can rebuild the same graph. */
+typedef struct {
+  int32_t n_workers;     /* W worker workgroups (default: compute units - scheduler WGs) */
+  int32_t n_sched_waves; /* scheduler wavefronts, 4 per scheduler WG (default 16)        */
+  int32_t quantum;       /* column quantum of projection tiles (default 1 at B=1, else 16) */
+  int32_t t_qkv, t_o, t_gu, t_down, t_lm; /* tiles per projection (default ~W; t_qkv a
+                                             multiple of n_kv_heads)                    */
+  int32_t s_attn;        /* attention splits per (request, kv group) (default 16 at B=1)  */
+  int32_t host_only;     /* 1: build on the host only (no device work); export still works */
+  int32_t fusion_order;  /* must be 0: Def 4.1 then Def 4.2                               */
+  int32_t aot_policy;    /* must be 0: round-robin over workers in linear order           */
+} mpk_build_params;
+
+typedef struct mpk_tgraph mpk_tgraph; /* opaque; owned by the library */
+
+/* Weights: device pointers to bf16 arrays, owned by the caller.
+ * layer points to a HOST array of n_layers*11 device pointers, per layer in
+ * the order in_norm[H], q[hq*d][H], k[hkv*d][H], v[hkv*d][H], q_norm[d],
+ * k_norm[d], o[H][hq*d], post_norm[H], gate[F][H], up[F][H], down[H][F]
+ * (q_norm/k_norm may be NULL when qk_norm is 0). */
+typedef struct {
+  const void* embed;      /* [vocab][H] */
+  const void* lm_head;    /* [vocab][H]; NULL when tied */
+  const void* final_norm; /* [H] */
+  const void* const* layer;
+} mpk_weights;
+
+/* Paged KV cache (device, caller-owned).  k_pool/v_pool are bf16
+ * [n_layers][n_pages][n_kv_heads][page_size][head_dim]; token p of request b
+ * lives at slot p % page_size of page page_table[b*max_pages_per_seq + p/page_size].
+ * Entries beyond a request's pages must still be valid page ids (they are
+ * never read). */
+typedef struct {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* page_table; /* device, int32 [batch][max_pages_per_seq] */
+  int32_t n_pages;
+  int32_t max_pages_per_seq;
+} mpk_kv;
+
+typedef struct {
+  int32_t n_tasks, n_events, root, end;
+  int32_t n_fused, n_empty, n_rewrites, n_aot;
+  int32_t batch, page_size;
+  mpk_build_params params; /* with every default resolved */
+} mpk_tgraph_header;
+
+/* Host copies of the linearised graph (task index = linear position).  The
+ * arrays are allocated by the library and owned by the caller, who releases
+ * them with mpk_free_host_view.  task_coords is [n_tasks][3]; task_orig is
+ * the program-order id, or -1-k for the k-th empty task; task_worker is -1
+ * for JIT and empty tasks. */
+typedef struct {
+  mpk_tgraph_header header;
+  uint8_t* task_type;
+  uint8_t* task_mode;
+  int16_t* task_layer;
+  uint16_t* task_coords;
+  int32_t* task_orig;
+  int32_t* task_dep;
+  int32_t* task_trig;
+  int16_t* task_worker;
+  uint32_t* event_counts;
+  int32_t* event_first;
+  int32_t* event_last;
+  uint8_t* event_flags;
+  uint32_t* aot_offsets; /* [n_workers + 1] */
+  uint32_t* aot_tasks;   /* [n_aot] */
+} mpk_tgraph_host_view;
+
+/* Generic canonicalisation input (test entry): a task and its boxes. */
+typedef struct {
+  int32_t type, layer, c0, c1, c2;
+} mpk_task_spec;
+typedef struct {
+  int32_t task, is_out, tensor;
+  int32_t lo[4], hi[4]; /* half-open box; unused dims 0..1 */
+} mpk_region;
+
+/* In-kernel status of the last decode step on a graph. */
+typedef struct {
+  int32_t code;   /* MPK_OK or MPK_ERR_TIMEOUT */
+  int32_t wg;     /* workgroup that reported it */
+  int32_t task;   /* task it was about to run, or -1 */
+  int32_t event;  /* event it was waiting on, or -1 */
+  uint32_t counter, target;
+} mpk_status_word;
+
+/* Build the tGraph of one decode step of `cfg` at batch `batch` (1..16) with
+ * KV pages of `page_size` tokens (16, 32 or 64): decomposition into tile
+ * tasks, overlap dependencies, Def 4.1 then Def 4.2 event fusion,
+ * normalisation, Kahn-BFS linearisation, JIT/AOT classification, round-robin
+ * AOT placement (MPK summary page, sections 2 and 4).  Allocates the device
+ * graph, its event counters, queues and activation buffers on the current
+ * device.  *out receives a library-owned handle (mpk_destroy_tgraph). */
+int mpk_build_tgraph(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, mpk_tgraph** out);
+
+/* Same, with explicit build parameters (NULL = defaults). */
+int mpk_build_tgraph_ex(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size,
+                        const mpk_build_params* params, mpk_tgraph** out);
+
+/* Resolved header of a built graph. */
+int mpk_tgraph_info(const mpk_tgraph* g, mpk_tgraph_header* out);
+
+/* Host copies of every index array of the graph (see mpk_tgraph_host_view). */
+int mpk_tgraph_export(const mpk_tgraph* g, mpk_tgraph_host_view* out);
+
+/* Test entry: run the canonicalisation pipeline (overlap edges, fusion,
+ * normalisation, linearisation, classification, placement on n_workers) on
+ * arbitrary tasks and boxes.  Host only; tasks of type MPK_TASK_ATTN are JIT. */
+int mpk_build_generic(const mpk_task_spec* tasks, int32_t n_tasks, const mpk_region* regions,
+                      int32_t n_regions, int32_t n_workers, mpk_tgraph_host_view* out);
+
+void mpk_free_host_view(mpk_tgraph_host_view* v);
+
+/* One decode step as ONE persistent-kernel launch on `stream` (asynchronous).
+ * token_ids[B], seq_lens[B] (tokens already cached; the new token is at
+ * position seq_lens[b]) are device int32; logits is device fp32 [B][vocab];
+ * next_ids is device int32 [B] (argmax, lowest index on ties).  The step
+ * writes the new token's k and v into the cache slot of position seq_lens[b]
+ * and does not change seq_lens.  Calls on one graph must be ordered on one
+ * stream.  A previous watchdog timeout makes the kernel exit at once; read it
+ * with mpk_get_status. */
+int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+                    const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream);
+
+/* The same task bodies launched kernel-per-operator in stream order (the
+ * barrier baseline): one kernel per operator with one workgroup per task.
+ * use_hipgraph = 1 captures the launches once into a hipGraph (re-captured
+ * when a pointer changes) and replays it. */
+int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+                             const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream,
+                             int32_t use_hipgraph);
+
+/* Copy intermediate tensor `tensor` of the last step to host memory `dst`
+ * (`bytes` must equal its size).  Ids: 0 e[B][H] fp32, 1 hf[B][H] bf16,
+ * 3 pmax[B][t_lm] (fp32 value, int32 index pairs); per layer l, 5 + 13*l + k
+ * with k = 0 r fp32, 1 h bf16, 2 qkv bf16 (group-major), 3 q fp32, 6 attention
+ * partials fp32, 7 attn bf16, 8 o bf16, 9 s fp32, 10 h2 bf16, 11 a bf16,
+ * 12 d bf16 (all [B][...]).  Synchronises the device. */
+int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes);
+
+/* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it). */
+int mpk_set_watchdog(mpk_tgraph* g, uint64_t timeout_ns);
+
+/* Synchronises the stream of the last step and reports its in-kernel status. */
+int mpk_get_status(mpk_tgraph* g, mpk_status_word* out);
+
+void mpk_destroy_tgraph(mpk_tgraph* g);
+
+/* Thread-local message describing the last non-zero status ("" if none). */
+const char* mpk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MPK_H */

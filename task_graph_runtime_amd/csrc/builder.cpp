@@ -1,0 +1,328 @@
+// Host-side tGraph builder (see builder.h for the method and its sources).
+#include "builder.h"
+
+#include <algorithm>
+#include <array>
+#include <deque>
+#include <map>
+
+namespace mpk {
+
+namespace {
+
+Box box(int32_t tensor, std::initializer_list<int32_t> lo, std::initializer_list<int32_t> hi) {
+  Box b;
+  b.tensor = tensor;
+  for (int i = 0; i < 4; ++i) { b.lo[i] = 0; b.hi[i] = 1; }
+  int i = 0;
+  for (int32_t v : lo) b.lo[i++] = v;
+  i = 0;
+  for (int32_t v : hi) b.hi[i++] = v;
+  return b;
+}
+
+bool overlaps(const Box& a, const Box& b) {
+  if (a.tensor != b.tensor) return false;
+  for (int i = 0; i < 4; ++i)
+    if (!(a.lo[i] < b.hi[i] && b.lo[i] < a.hi[i])) return false;
+  return true;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build_params* in, int32_t n_cus,
+                   Params* out, std::string* err) {
+  auto bad = [&](const char* m) { *err = m; return (int)MPK_ERR_INVALID_ARG; };
+  auto uns = [&](const char* m) { *err = m; return (int)MPK_ERR_UNSUPPORTED; };
+  if (c.n_layers < 1 || c.hidden < 8 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.ffn < 8 || c.vocab < 1 ||
+      c.max_seq_len < 1)
+    return bad("model config: sizes must be positive");
+  if (c.n_q_heads % c.n_kv_heads) return bad("model config: n_q_heads must be a multiple of n_kv_heads");
+  if (c.head_dim != 64 && c.head_dim != 128) return uns("head_dim must be 64 or 128");
+  if (c.hidden % 8 || c.ffn % 8) return uns("hidden and ffn must be multiples of 8");
+  if (!(c.rms_eps > 0.f) || !(c.rope_theta > 0.f)) return bad("rms_eps and rope_theta must be positive");
+  if (c.qk_norm != 0 && c.qk_norm != 1) return bad("qk_norm must be 0 or 1");
+  if (c.tied_embedding != 0 && c.tied_embedding != 1) return bad("tied_embedding must be 0 or 1");
+  if (c.n_q_heads / c.n_kv_heads > 16) return uns("more than 16 query heads per kv head");
+  if (B < 1 || B > 16) return uns("batch must be in 1..16");
+  if (P != 16 && P != 32 && P != 64) return uns("page_size must be 16, 32 or 64");
+  mpk_build_params z = {};
+  const mpk_build_params& p = in ? *in : z;
+  if (p.fusion_order != 0) return uns("only fusion order 0 (Def 4.1 then Def 4.2) is implemented");
+  if (p.aot_policy != 0) return uns("only AOT policy 0 (round-robin in linear order) is implemented");
+  Params r;
+  r.S_sched = p.n_sched_waves > 0 ? p.n_sched_waves : 16;
+  int32_t sched_wgs = (r.S_sched + 3) / 4;
+  r.W = p.n_workers > 0 ? p.n_workers : n_cus - sched_wgs;
+  if (r.W < 1) return bad("no worker workgroups left");
+  r.q = p.quantum > 0 ? p.quantum : (B == 1 ? 1 : 16);
+  const int64_t G = c.n_q_heads / c.n_kv_heads, d = c.head_dim, Sg = (G + 2) * d;
+  const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hkv = c.n_kv_heads;
+  if (p.t_qkv > 0) {
+    if (p.t_qkv % hkv) return bad("t_qkv must be a multiple of n_kv_heads");
+    r.T_qkv = p.t_qkv;
+  } else {
+    int64_t tpg = std::max<int64_t>(1, std::min<int64_t>(r.W / hkv, cdiv(Sg, r.q)));
+    r.T_qkv = (int32_t)(tpg * hkv);
+  }
+  auto dflt = [&](int32_t v, int64_t N) { return v > 0 ? v : (int32_t)std::min<int64_t>(r.W, cdiv(N, r.q)); };
+  r.T_o = dflt(p.t_o, H);
+  r.T_gu = dflt(p.t_gu, F);
+  r.T_down = dflt(p.t_down, H);
+  r.T_lm = dflt(p.t_lm, V);
+  int64_t max_pages = cdiv(c.max_seq_len, P);
+  if (p.s_attn > 0) {
+    r.S_attn = p.s_attn;
+  } else {
+    int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, cdiv(2 * r.W, (int64_t)B * hkv)));
+    r.S_attn = (int32_t)std::min<int64_t>(s, max_pages);
+  }
+  if (r.T_qkv / hkv > cdiv(Sg, r.q)) return bad("t_qkv: more tiles per kv group than column quanta");
+  struct { int64_t T, N, rows_per_col; const char* name; } ops[] = {
+      {r.T_qkv / hkv, Sg, 1, "t_qkv"}, {r.T_o, H, 1, "t_o"}, {r.T_gu, F, 2, "t_gu"},
+      {r.T_down, H, 1, "t_down"}, {r.T_lm, V, 1, "t_lm"}};
+  for (auto& o : ops) {
+    if (o.T < 1 || o.T > cdiv(o.N, r.q)) { *err = std::string(o.name) + ": tile count out of range"; return MPK_ERR_INVALID_ARG; }
+    if (o.T > 65535) { *err = std::string(o.name) + ": more than 65535 tiles"; return MPK_ERR_INVALID_ARG; }
+    int64_t widest = r.q * cdiv(cdiv(o.N, r.q), o.T);
+    if (widest * o.rows_per_col * B > 16384) {
+      *err = std::string(o.name) + ": tile too wide (columns x batch must stay within 16384 accumulators)";
+      return MPK_ERR_UNSUPPORTED;
+    }
+  }
+  if (r.S_attn < 1 || r.S_attn > 65535) return bad("s_attn out of range");
+  *out = r;
+  return MPK_OK;
+}
+
+void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<TaskDef>* tasks_out) {
+  std::vector<TaskDef>& tasks = *tasks_out;
+  tasks.clear();
+  const int32_t L = c.n_layers, H = c.hidden, hq = c.n_q_heads, hkv = c.n_kv_heads, d = c.head_dim;
+  const int32_t F = c.ffn, V = c.vocab, S = p.S_attn, G = hq / hkv, Sg = (G + 2) * d, maxs = c.max_seq_len;
+  auto add = [&](int32_t type, int32_t layer, int32_t c0, int32_t c1, int32_t c2, std::vector<Box> ins,
+                 std::vector<Box> outs) {
+    TaskDef t;
+    t.type = type; t.layer = layer; t.c[0] = c0; t.c[1] = c1; t.c[2] = c2;
+    t.ins = std::move(ins); t.outs = std::move(outs);
+    tasks.push_back(std::move(t));
+  };
+  add(MPK_TASK_EMBED, -1, 0, 0, 0, {}, {box(T_E, {0, 0}, {B, H})});
+  for (int32_t l = 0; l < L; ++l) {
+    auto t = [&](int32_t k) { return layer_tensor(l, k); };
+    std::vector<Box> ins;
+    if (l == 0) ins = {box(T_E, {0, 0}, {B, H})};
+    else ins = {box(layer_tensor(l - 1, L_S), {0, 0}, {B, H}), box(layer_tensor(l - 1, L_D), {0, 0}, {B, H})};
+    add(MPK_TASK_ATTN_NORM, l, 0, 0, 0, ins, {box(t(L_R), {0, 0}, {B, H}), box(t(L_H), {0, 0}, {B, H})});
+    const int32_t tpg = p.T_qkv / hkv;
+    for (int32_t n = 0; n < p.T_qkv; ++n) {
+      int32_t g = n / tpg, j = n % tpg, lo, hi;
+      tile_range(Sg, p.q, tpg, j, &lo, &hi);
+      add(MPK_TASK_QKV, l, n, 0, 0, {box(t(L_H), {0, 0}, {B, H})}, {box(t(L_QKV), {0, g * Sg + lo}, {B, g * Sg + hi})});
+    }
+    for (int32_t b = 0; b < B; ++b)
+      for (int32_t g = 0; g < hkv; ++g)
+        add(MPK_TASK_QKNORM_ROPE, l, b, g, 0, {box(t(L_QKV), {b, g * Sg}, {b + 1, (g + 1) * Sg})},
+            {box(t(L_Q), {b, g * G * d}, {b + 1, (g + 1) * G * d}), box(t(L_KC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d}),
+             box(t(L_VC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d})});
+    for (int32_t b = 0; b < B; ++b)
+      for (int32_t g = 0; g < hkv; ++g)
+        for (int32_t s = 0; s < S; ++s)
+          add(MPK_TASK_ATTN, l, b, g, s,
+              {box(t(L_Q), {b, g * G * d}, {b + 1, (g + 1) * G * d}), box(t(L_KC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d}),
+               box(t(L_VC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d})},
+              {box(t(L_PART), {b, g, s, 0}, {b + 1, g + 1, s + 1, G * (d + 2)})});
+    for (int32_t b = 0; b < B; ++b)
+      for (int32_t g = 0; g < hkv; ++g)
+        add(MPK_TASK_COMBINE, l, b, g, 0, {box(t(L_PART), {b, g, 0, 0}, {b + 1, g + 1, S, G * (d + 2)})},
+            {box(t(L_ATTN), {b, g * G * d}, {b + 1, (g + 1) * G * d})});
+    for (int32_t n = 0; n < p.T_o; ++n) {
+      int32_t lo, hi;
+      tile_range(H, p.q, p.T_o, n, &lo, &hi);
+      add(MPK_TASK_OPROJ, l, n, 0, 0, {box(t(L_ATTN), {0, 0}, {B, hq * d})}, {box(t(L_O), {0, lo}, {B, hi})});
+    }
+    add(MPK_TASK_MLP_NORM, l, 0, 0, 0, {box(t(L_R), {0, 0}, {B, H}), box(t(L_O), {0, 0}, {B, H})},
+        {box(t(L_S), {0, 0}, {B, H}), box(t(L_H2), {0, 0}, {B, H})});
+    for (int32_t n = 0; n < p.T_gu; ++n) {
+      int32_t lo, hi;
+      tile_range(F, p.q, p.T_gu, n, &lo, &hi);
+      add(MPK_TASK_GATEUP, l, n, 0, 0, {box(t(L_H2), {0, 0}, {B, H})}, {box(t(L_A), {0, lo}, {B, hi})});
+    }
+    for (int32_t n = 0; n < p.T_down; ++n) {
+      int32_t lo, hi;
+      tile_range(H, p.q, p.T_down, n, &lo, &hi);
+      add(MPK_TASK_DOWN, l, n, 0, 0, {box(t(L_A), {0, 0}, {B, F})}, {box(t(L_D), {0, lo}, {B, hi})});
+    }
+  }
+  add(MPK_TASK_FINAL_NORM, -1, 0, 0, 0,
+      {box(layer_tensor(L - 1, L_S), {0, 0}, {B, H}), box(layer_tensor(L - 1, L_D), {0, 0}, {B, H})},
+      {box(T_HF, {0, 0}, {B, H})});
+  for (int32_t n = 0; n < p.T_lm; ++n) {
+    int32_t lo, hi;
+    tile_range(V, p.q, p.T_lm, n, &lo, &hi);
+    add(MPK_TASK_LMHEAD, -1, n, 0, 0, {box(T_HF, {0, 0}, {B, H})},
+        {box(T_LOGITS, {0, lo}, {B, hi}), box(T_PMAX, {0, n, 0}, {B, n + 1, 2})});
+  }
+  add(MPK_TASK_ARGMAX, -1, 0, 0, 0, {box(T_PMAX, {0, 0, 0}, {B, p.T_lm, 2})}, {box(T_NEXT, {0}, {B})});
+}
+
+int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, Graph* out, std::string* err) {
+  const int32_t N = (int32_t)tasks.size();
+  if (W < 1) { *err = "n_workers must be positive"; return MPK_ERR_INVALID_ARG; }
+
+  // ---- overlap dependencies: per tensor, every (out box, in box) pair with producer < consumer
+  struct Ref { int32_t task; const Box* b; };
+  std::map<int32_t, std::vector<Ref>> outs, ins;
+  for (int32_t i = 0; i < N; ++i) {
+    for (const Box& b : tasks[i].outs) outs[b.tensor].push_back({i, &b});
+    for (const Box& b : tasks[i].ins) ins[b.tensor].push_back({i, &b});
+  }
+  std::vector<std::vector<int32_t>> P(N);
+  for (auto& kv : ins) {
+    auto it = outs.find(kv.first);
+    if (it == outs.end()) continue;
+    for (const Ref& c : kv.second)
+      for (const Ref& p : it->second)
+        if (p.task < c.task && overlaps(*p.b, *c.b)) P[c.task].push_back(p.task);
+  }
+  for (auto& v : P) {
+    std::sort(v.begin(), v.end());
+    v.erase(std::unique(v.begin(), v.end()), v.end());
+  }
+
+  // ---- Def 4.1: one event per consumer carrying all of its producers;
+  //      Def 4.2: events with the same producer set merge (consumers unite).
+  std::map<std::vector<int32_t>, std::vector<int32_t>> groups;
+  for (int32_t c = 0; c < N; ++c)
+    if (!P[c].empty()) groups[P[c]].push_back(c);
+  std::vector<std::vector<int32_t>> ev_in, ev_out;
+  {
+    std::vector<std::pair<std::vector<int32_t>, std::vector<int32_t>>> fused(groups.begin(), groups.end());
+    std::sort(fused.begin(), fused.end(), [](const auto& a, const auto& b) { return a.second[0] < b.second[0]; });
+    for (auto& f : fused) { ev_in.push_back(f.first); ev_out.push_back(f.second); }
+  }
+  const int32_t n_fused = (int32_t)ev_in.size();
+  std::vector<int32_t> dep(N, -1), trig(N, -1);
+  for (int32_t e = 0; e < n_fused; ++e)
+    for (int32_t c : ev_out[e]) dep[c] = e;
+  std::vector<std::vector<int32_t>> trigs_of(N);
+  for (int32_t e = 0; e < n_fused; ++e)
+    for (int32_t p : ev_in[e]) trigs_of[p].push_back(e);
+
+  // ---- normalisation: a task triggering k >= 2 events gets one new event e'
+  //      and k empty tasks, empty i waiting on e' and triggering event i.
+  std::vector<int32_t> ttype(N), tlayer(N), torig(N);
+  std::vector<std::array<int32_t, 3>> tcoords(N);
+  for (int32_t i = 0; i < N; ++i) {
+    ttype[i] = tasks[i].type; tlayer[i] = tasks[i].layer; torig[i] = i;
+    tcoords[i] = {tasks[i].c[0], tasks[i].c[1], tasks[i].c[2]};
+  }
+  int32_t n_empty = 0;
+  for (int32_t t = 0; t < N; ++t) {
+    const auto& tr = trigs_of[t];
+    if (tr.size() >= 2) {
+      int32_t ep = (int32_t)ev_in.size();
+      ev_in.push_back({t});
+      ev_out.push_back({});
+      for (size_t i = 0; i < tr.size(); ++i) {
+        int32_t T = (int32_t)ttype.size();
+        ttype.push_back(MPK_TASK_EMPTY); tlayer.push_back(tlayer[t]);
+        tcoords.push_back({(int32_t)i, 0, 0}); torig.push_back(-1 - n_empty);
+        ++n_empty;
+        dep.push_back(ep); trig.push_back(tr[i]);
+        ev_out[ep].push_back(T);
+        for (int32_t& x : ev_in[tr[i]]) if (x == t) x = T;
+      }
+      trig[t] = ep;
+    } else if (tr.size() == 1) {
+      trig[t] = tr[0];
+    }
+  }
+  const int32_t NT = (int32_t)ttype.size();
+  const int32_t root = (int32_t)ev_in.size();
+  ev_in.push_back({}); ev_out.push_back({});
+  const int32_t end = (int32_t)ev_in.size();
+  ev_in.push_back({}); ev_out.push_back({});
+  for (int32_t t = 0; t < NT; ++t) {
+    if (dep[t] < 0) { dep[t] = root; ev_out[root].push_back(t); }
+    if (trig[t] < 0) { trig[t] = end; ev_in[end].push_back(t); }
+  }
+  const int32_t NE = (int32_t)ev_in.size();
+
+  // ---- Kahn-BFS linearisation: an event is enqueued when its last producer
+  //      is placed; a dequeued event places its consumers consecutively.
+  std::vector<int32_t> indeg(NE), new_ev(NE, -1), new_task(NT, -1), first(NE, 0), last(NE, 0);
+  for (int32_t e = 0; e < NE; ++e) indeg[e] = (int32_t)ev_in[e].size();
+  std::deque<int32_t> q{root};
+  int32_t ne = 0, nt = 0;
+  while (!q.empty()) {
+    int32_t e = q.front();
+    q.pop_front();
+    new_ev[e] = ne++;
+    first[e] = nt;
+    std::vector<int32_t> o = ev_out[e];
+    std::sort(o.begin(), o.end());
+    for (int32_t t : o) {
+      new_task[t] = nt++;
+      int32_t f = trig[t];
+      if (--indeg[f] == 0) q.push_back(f);
+    }
+    last[e] = nt - 1;
+  }
+  if (nt != NT || ne != NE) { *err = "tGraph has a cycle"; return MPK_ERR_GRAPH; }
+
+  Graph& g = *out;
+  g = Graph();
+  g.NT = NT; g.NE = NE; g.root = new_ev[root]; g.end = new_ev[end];
+  g.n_fused = n_fused; g.n_empty = n_empty; g.n_rewrites = NE - 2 - n_fused;
+  std::vector<int32_t> order(NT), eorder(NE);
+  for (int32_t t = 0; t < NT; ++t) order[new_task[t]] = t;
+  for (int32_t e = 0; e < NE; ++e) eorder[new_ev[e]] = e;
+  auto mode_of = [](int32_t type) {
+    return type == MPK_TASK_EMPTY ? MPK_MODE_EMPTY : type == MPK_TASK_ATTN ? MPK_MODE_JIT : MPK_MODE_AOT;
+  };
+  g.task_type.resize(NT); g.task_mode.resize(NT); g.task_layer.resize(NT); g.task_coords.resize(3 * (size_t)NT);
+  g.task_orig.resize(NT); g.task_dep.resize(NT); g.task_trig.resize(NT); g.task_worker.assign(NT, -1);
+  for (int32_t i = 0; i < NT; ++i) {
+    int32_t t = order[i];
+    g.task_type[i] = (uint8_t)ttype[t];
+    g.task_mode[i] = (uint8_t)mode_of(ttype[t]);
+    g.task_layer[i] = (int16_t)tlayer[t];
+    for (int k = 0; k < 3; ++k) g.task_coords[3 * (size_t)i + k] = (uint16_t)tcoords[t][k];
+    g.task_orig[i] = torig[t];
+    g.task_dep[i] = new_ev[dep[t]];
+    g.task_trig[i] = new_ev[trig[t]];
+  }
+  g.event_counts.resize(NE); g.event_first.resize(NE); g.event_last.resize(NE); g.event_flags.assign(NE, 0);
+  for (int32_t i = 0; i < NE; ++i) {
+    int32_t e = eorder[i];
+    g.event_counts[i] = (uint32_t)ev_in[e].size();
+    g.event_first[i] = first[e];
+    g.event_last[i] = last[e];
+    for (int32_t t : ev_out[e]) {
+      int m = mode_of(ttype[t]);
+      if (m == MPK_MODE_JIT) g.event_flags[i] |= MPK_EVENT_HAS_JIT;
+      if (m == MPK_MODE_EMPTY) g.event_flags[i] |= MPK_EVENT_HAS_EMPTY;
+    }
+  }
+  // ---- AOT placement: round-robin over workers in linear order
+  std::vector<std::vector<uint32_t>> lists(W);
+  int64_t k = 0;
+  for (int32_t i = 0; i < NT; ++i) {
+    if (g.task_mode[i] != MPK_MODE_AOT) continue;
+    int32_t w = (int32_t)(k % W);
+    g.task_worker[i] = (int16_t)w;
+    lists[w].push_back((uint32_t)i);
+    ++k;
+  }
+  g.aot_offsets.assign(W + 1, 0);
+  for (int32_t w = 0; w < W; ++w) {
+    g.aot_offsets[w + 1] = g.aot_offsets[w] + (uint32_t)lists[w].size();
+    g.aot_tasks.insert(g.aot_tasks.end(), lists[w].begin(), lists[w].end());
+  }
+  return MPK_OK;
+}
+
+}  // namespace mpk

@@ -1,0 +1,78 @@
+// Host-side tGraph builder: operator decomposition into tile tasks, overlap
+// dependencies, event fusion, normalisation, BFS linearisation, JIT/AOT
+// classification and AOT placement.  Plain C++17, no HIP: it runs (and is
+// tested) without a GPU.
+//
+// Method: "MPK: A Compiler and Runtime for Mega-Kernelizing Tensor Programs
+// -- L2", section 2 (Q2), section 4 (Def 4.1, Def 4.2, the "6 minimum
+// checks", design-space table) and section 7 ("Empty tasks as
+// degree-reduction glue"); dependency rule from the author's HN comment
+// (item 2: an edge iff the producer's outputs overlap the consumer's inputs).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "mpk.h"
+
+namespace mpk {
+
+struct Box {
+  int32_t tensor;
+  int32_t lo[4];
+  int32_t hi[4];
+};
+
+struct TaskDef {
+  int32_t type = 0, layer = -1;
+  int32_t c[3] = {0, 0, 0};
+  std::vector<Box> ins, outs;
+};
+
+// Resolved build parameters.
+struct Params {
+  int32_t W = 1, S_sched = 16, q = 1;
+  int32_t T_qkv = 1, T_o = 1, T_gu = 1, T_down = 1, T_lm = 1, S_attn = 1;
+};
+
+// The linearised graph (task index = linear position), as exported.
+struct Graph {
+  int32_t NT = 0, NE = 0, root = 0, end = 0, n_fused = 0, n_empty = 0, n_rewrites = 0;
+  std::vector<uint8_t> task_type, task_mode;
+  std::vector<int16_t> task_layer;
+  std::vector<uint16_t> task_coords;  // [NT][3]
+  std::vector<int32_t> task_orig, task_dep, task_trig;
+  std::vector<int16_t> task_worker;
+  std::vector<uint32_t> event_counts;
+  std::vector<int32_t> event_first, event_last;
+  std::vector<uint8_t> event_flags;
+  std::vector<uint32_t> aot_offsets, aot_tasks;
+};
+
+// Tensor ids of the decoder: 5 shared, then 13 per layer.
+enum { T_E = 0, T_HF = 1, T_LOGITS = 2, T_PMAX = 3, T_NEXT = 4 };
+enum { L_R = 0, L_H, L_QKV, L_Q, L_KC, L_VC, L_PART, L_ATTN, L_O, L_S, L_H2, L_A, L_D, L_COUNT };
+inline int32_t layer_tensor(int32_t l, int32_t k) { return 5 + 13 * l + k; }
+
+// Balanced tile n of T over N columns on a quantum of q columns.
+inline void tile_range(int64_t N, int64_t q, int64_t T, int64_t n, int32_t* lo, int32_t* hi) {
+  int64_t U = (N + q - 1) / q;
+  int64_t a = q * (n * U / T), b = q * ((n + 1) * U / T);
+  *lo = (int32_t)a;
+  *hi = (int32_t)(b < N ? b : N);
+}
+
+// Validate cfg/batch/page size and resolve defaults; `n_cus` is the compute
+// unit count used for the default worker count.  Returns MPK_OK or an error
+// with a message in `err`.
+int resolve_params(const mpk_model_cfg& cfg, int32_t B, int32_t P, const mpk_build_params* in, int32_t n_cus,
+                   Params* out, std::string* err);
+
+// Program-order tasks of one decode step with their input/output boxes.
+void decompose(const mpk_model_cfg& cfg, int32_t B, const Params& p, std::vector<TaskDef>* tasks);
+
+// Canonicalisation pipeline on arbitrary tasks; MPK_ERR_GRAPH on a cycle.
+int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, Graph* g, std::string* err);
+
+}  // namespace mpk

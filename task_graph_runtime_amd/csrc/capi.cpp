@@ -1,0 +1,579 @@
+// C ABI of the decode-step mega-kernel library (declared in include/mpk.h):
+// graph build and upload, the persistent-kernel step, the kernel-per-operator
+// baseline, export for the checker, status and intermediate-tensor readback.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "builder.h"
+#include "mpk.h"
+#include "rt.h"
+
+namespace mpk {
+hipError_t launch_megakernel(const KArgs& a, int grid, hipStream_t stream);
+hipError_t launch_baseline_op(const KArgs& a, const int32_t* list, int count, hipStream_t stream);
+}  // namespace mpk
+
+using namespace mpk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MPK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+#define HIPCHK(x)                                  \
+  do {                                             \
+    hipError_t e_ = (x);                           \
+    if (e_ != hipSuccess) return hip_fail(e_, #x); \
+  } while (0)
+
+uint32_t next_pow2(uint64_t x) {
+  uint64_t p = 1;
+  while (p < x) p <<= 1;
+  return (uint32_t)p;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+}  // namespace
+
+struct mpk_tgraph {
+  mpk_model_cfg cfg{};
+  int32_t B = 0, P = 0;
+  Params prm;
+  mpk_build_params resolved{};
+  bool host_only = false;
+  Graph g;
+
+  int device = 0, n_cus = 0, grid = 0, n_sched_wgs = 0, n_sched = 0;
+  double wall_khz = 100000.0;
+  uint64_t timeout_ns = 2000000000ull;
+  uint32_t epoch = 0;
+
+  std::vector<DevTask> h_tasks;
+  void* d_graph = nullptr;  // tasks, events, aot offsets, aot tasks
+  DevTask* d_tasks = nullptr;
+  DevEvent* d_events = nullptr;
+  uint32_t* d_aot_off = nullptr;
+  uint32_t* d_aot_tasks = nullptr;
+  void* d_rt = nullptr;     // counters, rings, state, status
+  uint32_t* d_ev_cnt = nullptr;
+  unsigned long long* d_sched_ring = nullptr;
+  uint32_t* d_sched_tail = nullptr;
+  unsigned long long* d_jit_ring = nullptr;
+  uint32_t* d_state = nullptr;
+  StatusWord* d_status = nullptr;
+  uint32_t sched_cap = 0, jit_cap = 0;
+
+  void* d_act = nullptr;
+  KArgs base{};             // arguments that do not change between steps
+  struct TensorRef { void* p; int64_t bytes; };
+  std::vector<TensorRef> tensors;  // indexed by tensor id (null when caller-owned)
+
+  const uint16_t** d_wl = nullptr;
+  std::vector<const void*> h_wl;
+
+  int32_t* d_lists = nullptr;
+  std::vector<std::pair<int32_t, int32_t>> ops;  // (offset, count) per operator, program order
+  hipStream_t cap_stream = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  std::vector<uintptr_t> gkey;
+  hipStream_t last_stream = nullptr;
+};
+
+namespace {
+
+void fill_descriptors(mpk_tgraph* t) {
+  const Graph& g = t->g;
+  const Params& p = t->prm;
+  const mpk_model_cfg& c = t->cfg;
+  const int32_t G = c.n_q_heads / c.n_kv_heads, Sg = (G + 2) * c.head_dim, tpg = p.T_qkv / c.n_kv_heads;
+  t->h_tasks.assign(g.NT, DevTask{});
+  for (int32_t i = 0; i < g.NT; ++i) {
+    DevTask& d = t->h_tasks[i];
+    d.type = g.task_type[i];
+    d.mode = g.task_mode[i];
+    d.layer = g.task_layer[i];
+    d.dep = g.task_dep[i];
+    d.trig = g.task_trig[i];
+    const int32_t c0 = g.task_coords[3 * (size_t)i], c1 = g.task_coords[3 * (size_t)i + 1],
+                  c2 = g.task_coords[3 * (size_t)i + 2];
+    int32_t lo = 0, hi = 0;
+    switch (d.type) {
+      case MPK_TASK_QKV: {
+        int32_t gg = c0 / tpg, j = c0 % tpg;
+        tile_range(Sg, p.q, tpg, j, &lo, &hi);
+        d.a0 = gg * Sg + lo; d.a1 = gg * Sg + hi; d.a2 = c0;
+        break;
+      }
+      case MPK_TASK_OPROJ: tile_range(c.hidden, p.q, p.T_o, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_GATEUP: tile_range(c.ffn, p.q, p.T_gu, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_DOWN: tile_range(c.hidden, p.q, p.T_down, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_LMHEAD: tile_range(c.vocab, p.q, p.T_lm, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      default: d.a0 = c0; d.a1 = c1; d.a2 = c2; break;
+    }
+  }
+}
+
+// The runtime resolves empty tasks inline one level deep: an event with empty
+// consumers has only empty consumers, whose own events have none.
+int check_runtime_shape(const Graph& g) {
+  for (int32_t e = 0; e < g.NE; ++e) {
+    if (!(g.event_flags[e] & MPK_EVENT_HAS_EMPTY)) continue;
+    for (int32_t t = g.event_first[e]; t <= g.event_last[e]; ++t) {
+      if (g.task_type[t] != MPK_TASK_EMPTY) return fail(MPK_ERR_GRAPH, "event mixes empty and real consumers");
+      if (g.event_flags[g.task_trig[t]] & MPK_EVENT_HAS_EMPTY) return fail(MPK_ERR_GRAPH, "chained empty tasks");
+    }
+  }
+  return MPK_OK;
+}
+
+void build_op_lists(mpk_tgraph* t, std::vector<int32_t>* flat) {
+  const Graph& g = t->g;
+  const int32_t L = t->cfg.n_layers, n_ops = 4 + 9 * L;
+  std::vector<std::vector<int32_t>> lists(n_ops);
+  static const int per_layer_idx[] = {-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, -1, -1, -1, -1};
+  for (int32_t i = 0; i < g.NT; ++i) {
+    int ty = g.task_type[i], l = g.task_layer[i], k;
+    if (ty == MPK_TASK_EMPTY) continue;
+    if (ty == MPK_TASK_EMBED) k = 0;
+    else if (ty == MPK_TASK_FINAL_NORM) k = 1 + 9 * L;
+    else if (ty == MPK_TASK_LMHEAD) k = 2 + 9 * L;
+    else if (ty == MPK_TASK_ARGMAX) k = 3 + 9 * L;
+    else k = 1 + 9 * l + per_layer_idx[ty];
+    lists[k].push_back(i);
+  }
+  t->ops.clear();
+  flat->clear();
+  for (auto& v : lists) {
+    t->ops.push_back({(int32_t)flat->size(), (int32_t)v.size()});
+    flat->insert(flat->end(), v.begin(), v.end());
+  }
+}
+
+int upload(mpk_tgraph* t) {
+  const Graph& g = t->g;
+  HIPCHK(hipGetDevice(&t->device));
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, t->device));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MPK_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", kernels are built for gfx950");
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, t->device) == hipSuccess && khz > 0)
+    t->wall_khz = khz;
+  t->n_cus = prop.multiProcessorCount;
+  t->n_sched_wgs = (t->prm.S_sched + 3) / 4;
+  t->n_sched = std::min(t->prm.S_sched, t->prm.W);
+  t->grid = t->n_sched_wgs + t->prm.W;
+  if (t->grid > t->n_cus)
+    return fail(MPK_ERR_INVALID_ARG, "workers + scheduler workgroups exceed the compute units");
+
+  fill_descriptors(t);
+  // graph arrays
+  const int64_t o_tasks = 0, o_events = align256(o_tasks + (int64_t)g.NT * sizeof(DevTask));
+  const int64_t o_off = align256(o_events + (int64_t)g.NE * sizeof(DevEvent));
+  const int64_t o_aot = align256(o_off + (int64_t)g.aot_offsets.size() * 4);
+  std::vector<int32_t> flat;
+  build_op_lists(t, &flat);
+  const int64_t o_lists = align256(o_aot + (int64_t)std::max<size_t>(1, g.aot_tasks.size()) * 4);
+  const int64_t o_wl = align256(o_lists + (int64_t)std::max<size_t>(1, flat.size()) * 4);
+  const int64_t graph_bytes = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
+  HIPCHK(hipMalloc(&t->d_graph, graph_bytes));
+  char* gb = (char*)t->d_graph;
+  std::vector<DevEvent> ev(g.NE);
+  for (int32_t e = 0; e < g.NE; ++e) ev[e] = DevEvent{g.event_counts[e], g.event_first[e], g.event_last[e], g.event_flags[e]};
+  t->d_tasks = (DevTask*)(gb + o_tasks);
+  t->d_events = (DevEvent*)(gb + o_events);
+  t->d_aot_off = (uint32_t*)(gb + o_off);
+  t->d_aot_tasks = (uint32_t*)(gb + o_aot);
+  t->d_lists = (int32_t*)(gb + o_lists);
+  t->d_wl = (const uint16_t**)(gb + o_wl);
+  HIPCHK(hipMemcpy(t->d_tasks, t->h_tasks.data(), (size_t)g.NT * sizeof(DevTask), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(t->d_events, ev.data(), (size_t)g.NE * sizeof(DevEvent), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(t->d_aot_off, g.aot_offsets.data(), g.aot_offsets.size() * 4, hipMemcpyHostToDevice));
+  if (!g.aot_tasks.empty())
+    HIPCHK(hipMemcpy(t->d_aot_tasks, g.aot_tasks.data(), g.aot_tasks.size() * 4, hipMemcpyHostToDevice));
+  if (!flat.empty()) HIPCHK(hipMemcpy(t->d_lists, flat.data(), flat.size() * 4, hipMemcpyHostToDevice));
+
+  // runtime: counters, rings, state, status
+  int64_t n_jit_tasks = 0, n_jit_events = 0;
+  for (int32_t i = 0; i < g.NT; ++i) n_jit_tasks += g.task_mode[i] == MPK_MODE_JIT;
+  for (int32_t e = 0; e < g.NE; ++e) n_jit_events += (g.event_flags[e] & MPK_EVENT_HAS_JIT) != 0;
+  t->sched_cap = next_pow2((uint64_t)n_jit_events + 1);
+  t->jit_cap = next_pow2((uint64_t)n_jit_tasks + 1);
+  const int32_t W = t->prm.W, S = t->n_sched;
+  const int64_t r_cnt = 0, r_sring = align256(r_cnt + (int64_t)g.NE * 4);
+  const int64_t r_stail = align256(r_sring + (int64_t)S * t->sched_cap * 8);
+  const int64_t r_jring = align256(r_stail + (int64_t)S * 4);
+  const int64_t r_state = align256(r_jring + (int64_t)W * t->jit_cap * 8);
+  const int64_t r_status = align256(r_state + (int64_t)(2 * W + 2 * S) * 4);
+  const int64_t rt_bytes = align256(r_status + (int64_t)sizeof(StatusWord));
+  HIPCHK(hipMalloc(&t->d_rt, rt_bytes));
+  HIPCHK(hipMemset(t->d_rt, 0, rt_bytes));
+  char* rb = (char*)t->d_rt;
+  t->d_ev_cnt = (uint32_t*)(rb + r_cnt);
+  t->d_sched_ring = (unsigned long long*)(rb + r_sring);
+  t->d_sched_tail = (uint32_t*)(rb + r_stail);
+  t->d_jit_ring = (unsigned long long*)(rb + r_jring);
+  t->d_state = (uint32_t*)(rb + r_state);
+  t->d_status = (StatusWord*)(rb + r_status);
+
+  // activations
+  const mpk_model_cfg& c = t->cfg;
+  const int64_t B = t->B, H = c.hidden, L = c.n_layers, hq = c.n_q_heads, hkv = c.n_kv_heads, d = c.head_dim;
+  const int64_t G = hq / hkv, Sg = (G + 2) * d, F = c.ffn, S_at = t->prm.S_attn;
+  KArgs& a = t->base;
+  a.st_bh = B * H; a.st_qkv = B * hkv * Sg; a.st_q = B * hq * d; a.st_part = B * hkv * S_at * G * (d + 2);
+  a.st_a = B * F;
+  struct Item { int id; int64_t bytes; };
+  std::vector<Item> items = {{T_E, B * H * 4}, {T_HF, B * H * 2}, {T_PMAX, B * (int64_t)t->prm.T_lm * 8}};
+  const int64_t per_layer_bytes[L_COUNT] = {a.st_bh * 4, a.st_bh * 2, a.st_qkv * 2, a.st_q * 4, 0, 0,
+                                            a.st_part * 4, a.st_q * 2, a.st_bh * 2, a.st_bh * 4,
+                                            a.st_bh * 2, a.st_a * 2, a.st_bh * 2};
+  // one contiguous [L][...] block per per-layer tensor kind
+  int64_t off = 0;
+  std::vector<int64_t> shared_off(5, -1), kind_off(L_COUNT, -1);
+  for (auto& it : items) { shared_off[it.id] = off; off = align256(off + it.bytes); }
+  for (int k = 0; k < L_COUNT; ++k) {
+    if (!per_layer_bytes[k]) continue;
+    kind_off[k] = off;
+    off = align256(off + per_layer_bytes[k] * L);
+  }
+  HIPCHK(hipMalloc(&t->d_act, off));
+  HIPCHK(hipMemset(t->d_act, 0, off));
+  char* ab = (char*)t->d_act;
+  a.e = (float*)(ab + shared_off[T_E]);
+  a.hf = (uint16_t*)(ab + shared_off[T_HF]);
+  a.pmax = (PMax*)(ab + shared_off[T_PMAX]);
+  a.r = (float*)(ab + kind_off[L_R]);
+  a.h = (uint16_t*)(ab + kind_off[L_H]);
+  a.qkv = (uint16_t*)(ab + kind_off[L_QKV]);
+  a.q = (float*)(ab + kind_off[L_Q]);
+  a.part = (float*)(ab + kind_off[L_PART]);
+  a.attn = (uint16_t*)(ab + kind_off[L_ATTN]);
+  a.o = (uint16_t*)(ab + kind_off[L_O]);
+  a.s = (float*)(ab + kind_off[L_S]);
+  a.h2 = (uint16_t*)(ab + kind_off[L_H2]);
+  a.a = (uint16_t*)(ab + kind_off[L_A]);
+  a.dn = (uint16_t*)(ab + kind_off[L_D]);
+  t->tensors.assign(5 + 13 * (size_t)L, {nullptr, 0});
+  for (auto& it : items) t->tensors[it.id] = {ab + shared_off[it.id], it.bytes};
+  for (int64_t l = 0; l < L; ++l)
+    for (int k = 0; k < L_COUNT; ++k)
+      if (per_layer_bytes[k]) t->tensors[layer_tensor((int32_t)l, k)] = {ab + kind_off[k] + l * per_layer_bytes[k], per_layer_bytes[k]};
+
+  a.tasks = t->d_tasks; a.events = t->d_events; a.aot_off = t->d_aot_off; a.aot_tasks = t->d_aot_tasks;
+  a.ev_cnt = t->d_ev_cnt; a.sched_ring = t->d_sched_ring; a.sched_tail = t->d_sched_tail; a.jit_ring = t->d_jit_ring;
+  a.state = t->d_state; a.sched_cap = t->sched_cap; a.jit_cap = t->jit_cap;
+  a.n_workers = W; a.n_sched = S; a.n_sched_wgs = t->n_sched_wgs;
+  a.root_event = g.root; a.end_event = g.end;
+  a.status = t->d_status;
+  a.L = c.n_layers; a.H = c.hidden; a.hq = c.n_q_heads; a.hkv = c.n_kv_heads; a.d = c.head_dim; a.F = c.ffn;
+  a.V = c.vocab; a.G = (int32_t)G; a.Sg = (int32_t)Sg; a.B = t->B; a.P = t->P; a.S_attn = t->prm.S_attn;
+  a.T_lm = t->prm.T_lm; a.qk_norm = c.qk_norm; a.max_seq = c.max_seq_len; a.eps = c.rms_eps; a.theta = c.rope_theta;
+  a.wl = t->d_wl;
+  return MPK_OK;
+}
+
+void free_tgraph(mpk_tgraph* t) {
+  if (!t) return;
+  if (t->gexec) (void)hipGraphExecDestroy(t->gexec);
+  if (t->cap_stream) (void)hipStreamDestroy(t->cap_stream);
+  if (t->d_graph) (void)hipFree(t->d_graph);
+  if (t->d_rt) (void)hipFree(t->d_rt);
+  if (t->d_act) (void)hipFree(t->d_act);
+  delete t;
+}
+
+int export_graph(const Graph& g, const mpk_tgraph_header& hdr, mpk_tgraph_host_view* out) {
+  std::memset(out, 0, sizeof(*out));
+  out->header = hdr;
+  auto dup = [](const void* src, size_t bytes) -> void* {
+    void* p = std::malloc(bytes ? bytes : 1);
+    if (p && bytes) std::memcpy(p, src, bytes);
+    return p;
+  };
+  out->task_type = (uint8_t*)dup(g.task_type.data(), g.task_type.size());
+  out->task_mode = (uint8_t*)dup(g.task_mode.data(), g.task_mode.size());
+  out->task_layer = (int16_t*)dup(g.task_layer.data(), g.task_layer.size() * 2);
+  out->task_coords = (uint16_t*)dup(g.task_coords.data(), g.task_coords.size() * 2);
+  out->task_orig = (int32_t*)dup(g.task_orig.data(), g.task_orig.size() * 4);
+  out->task_dep = (int32_t*)dup(g.task_dep.data(), g.task_dep.size() * 4);
+  out->task_trig = (int32_t*)dup(g.task_trig.data(), g.task_trig.size() * 4);
+  out->task_worker = (int16_t*)dup(g.task_worker.data(), g.task_worker.size() * 2);
+  out->event_counts = (uint32_t*)dup(g.event_counts.data(), g.event_counts.size() * 4);
+  out->event_first = (int32_t*)dup(g.event_first.data(), g.event_first.size() * 4);
+  out->event_last = (int32_t*)dup(g.event_last.data(), g.event_last.size() * 4);
+  out->event_flags = (uint8_t*)dup(g.event_flags.data(), g.event_flags.size());
+  out->aot_offsets = (uint32_t*)dup(g.aot_offsets.data(), g.aot_offsets.size() * 4);
+  out->aot_tasks = (uint32_t*)dup(g.aot_tasks.data(), g.aot_tasks.size() * 4);
+  if (!out->task_type || !out->task_mode || !out->task_layer || !out->task_coords || !out->task_orig ||
+      !out->task_dep || !out->task_trig || !out->task_worker || !out->event_counts || !out->event_first ||
+      !out->event_last || !out->event_flags || !out->aot_offsets || !out->aot_tasks) {
+    mpk_free_host_view(out);
+    return fail(MPK_ERR_NOMEM, "host allocation failed");
+  }
+  return MPK_OK;
+}
+
+mpk_tgraph_header make_header(const mpk_tgraph* t) {
+  mpk_tgraph_header h{};
+  const Graph& g = t->g;
+  h.n_tasks = g.NT; h.n_events = g.NE; h.root = g.root; h.end = g.end;
+  h.n_fused = g.n_fused; h.n_empty = g.n_empty; h.n_rewrites = g.n_rewrites; h.n_aot = (int32_t)g.aot_tasks.size();
+  h.batch = t->B; h.page_size = t->P; h.params = t->resolved;
+  return h;
+}
+
+// Fill the per-step arguments; uploads the weight-pointer table when it changed.
+int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+              const int32_t* seq_lens, float* logits, int32_t* next_ids, hipStream_t stream, KArgs* out) {
+  if (!t || !w || !kv || !token_ids || !seq_lens || !logits || !next_ids)
+    return fail(MPK_ERR_INVALID_ARG, "null argument");
+  if (t->host_only) return fail(MPK_ERR_INVALID_ARG, "graph was built host-only");
+  const mpk_model_cfg& c = t->cfg;
+  if (!w->embed || !w->final_norm || !w->layer || (!c.tied_embedding && !w->lm_head))
+    return fail(MPK_ERR_INVALID_ARG, "missing weight pointer");
+  if (!kv->k_pool || !kv->v_pool || !kv->page_table || kv->n_pages < 1 || kv->max_pages_per_seq < 1)
+    return fail(MPK_ERR_INVALID_ARG, "bad KV cache descriptor");
+  std::vector<const void*> wl(w->layer, w->layer + (size_t)c.n_layers * LAYER_PTRS);
+  for (int32_t l = 0; l < c.n_layers; ++l)
+    for (int k = 0; k < LAYER_PTRS; ++k) {
+      const void* p = wl[(size_t)l * LAYER_PTRS + k];
+      bool optional = (k == W_Q_NORM || k == W_K_NORM) && !c.qk_norm;
+      if (!p && !optional) return fail(MPK_ERR_INVALID_ARG, "missing layer weight pointer");
+      if (((uintptr_t)p & 15) != 0) return fail(MPK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+    }
+  if (((uintptr_t)w->embed & 15) || ((uintptr_t)w->lm_head & 15) || ((uintptr_t)kv->k_pool & 15) ||
+      ((uintptr_t)kv->v_pool & 15))
+    return fail(MPK_ERR_INVALID_ARG, "weights and KV pools must be 16-byte aligned");
+  if (wl != t->h_wl) {
+    if (t->last_stream) HIPCHK(hipStreamSynchronize(t->last_stream));
+    HIPCHK(hipStreamSynchronize(stream));
+    HIPCHK(hipMemcpy(t->d_wl, wl.data(), wl.size() * sizeof(void*), hipMemcpyHostToDevice));
+    t->h_wl = wl;
+  }
+  KArgs a = t->base;
+  a.embed = (const uint16_t*)w->embed;
+  a.lm_head = c.tied_embedding ? nullptr : (const uint16_t*)w->lm_head;
+  a.final_norm = (const uint16_t*)w->final_norm;
+  a.k_pool = (uint16_t*)kv->k_pool;
+  a.v_pool = (uint16_t*)kv->v_pool;
+  a.page_table = kv->page_table;
+  a.n_pages = kv->n_pages;
+  a.max_pages = kv->max_pages_per_seq;
+  a.token_ids = token_ids;
+  a.seq_lens = seq_lens;
+  a.logits = logits;
+  a.next_ids = next_ids;
+  a.timeout_ticks = (uint64_t)((double)t->timeout_ns * t->wall_khz / 1e6);
+  if (a.timeout_ticks < 1) a.timeout_ticks = 1;
+  *out = a;
+  return MPK_OK;
+}
+
+int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const mpk_build_params* params,
+               mpk_tgraph** out) {
+  if (!cfg || !out) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  const bool host_only = params && params->host_only;
+  int n_cus = 256;
+  if (!host_only) {
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    HIPCHK(hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev));
+  }
+  Params prm;
+  std::string err;
+  int rc = resolve_params(*cfg, batch, page_size, params, n_cus, &prm, &err);
+  if (rc) return fail(rc, err);
+  if (cfg->hidden > kMaxHidden) return fail(MPK_ERR_UNSUPPORTED, "hidden larger than 8192");
+  if (cfg->n_q_heads / cfg->n_kv_heads > 8) return fail(MPK_ERR_UNSUPPORTED, "more than 8 query heads per kv head");
+  mpk_tgraph* t = new (std::nothrow) mpk_tgraph();
+  if (!t) return fail(MPK_ERR_NOMEM, "host allocation failed");
+  t->cfg = *cfg; t->B = batch; t->P = page_size; t->prm = prm; t->host_only = host_only;
+  mpk_build_params r{};
+  r.n_workers = prm.W; r.n_sched_waves = prm.S_sched; r.quantum = prm.q; r.t_qkv = prm.T_qkv; r.t_o = prm.T_o;
+  r.t_gu = prm.T_gu; r.t_down = prm.T_down; r.t_lm = prm.T_lm; r.s_attn = prm.S_attn; r.host_only = host_only;
+  t->resolved = r;
+  std::vector<TaskDef> tasks;
+  decompose(*cfg, batch, prm, &tasks);
+  rc = canonicalize(tasks, prm.W, &t->g, &err);
+  if (rc) { free_tgraph(t); return fail(rc, err); }
+  rc = check_runtime_shape(t->g);
+  if (rc) { free_tgraph(t); return rc; }
+  if (!host_only) {
+    rc = upload(t);
+    if (rc) { std::string m = g_err; free_tgraph(t); return fail(rc, m); }
+  }
+  *out = t;
+  return MPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mpk_last_error(void) { return g_err.c_str(); }
+
+int mpk_build_tgraph(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, mpk_tgraph** out) {
+  return build_impl(cfg, batch, page_size, nullptr, out);
+}
+
+int mpk_build_tgraph_ex(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const mpk_build_params* params,
+                        mpk_tgraph** out) {
+  return build_impl(cfg, batch, page_size, params, out);
+}
+
+int mpk_tgraph_info(const mpk_tgraph* g, mpk_tgraph_header* out) {
+  if (!g || !out) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  *out = make_header(g);
+  return MPK_OK;
+}
+
+int mpk_tgraph_export(const mpk_tgraph* g, mpk_tgraph_host_view* out) {
+  if (!g || !out) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  return export_graph(g->g, make_header(g), out);
+}
+
+int mpk_build_generic(const mpk_task_spec* specs, int32_t n_tasks, const mpk_region* regions, int32_t n_regions,
+                      int32_t n_workers, mpk_tgraph_host_view* out) {
+  if (!out || n_tasks < 0 || n_regions < 0 || (n_tasks && !specs) || (n_regions && !regions))
+    return fail(MPK_ERR_INVALID_ARG, "bad argument");
+  std::vector<TaskDef> tasks(n_tasks);
+  for (int32_t i = 0; i < n_tasks; ++i) {
+    if (specs[i].type < 0 || specs[i].type >= MPK_TASK_EMPTY) return fail(MPK_ERR_INVALID_ARG, "bad task type");
+    tasks[i].type = specs[i].type; tasks[i].layer = specs[i].layer;
+    tasks[i].c[0] = specs[i].c0; tasks[i].c[1] = specs[i].c1; tasks[i].c[2] = specs[i].c2;
+  }
+  for (int32_t i = 0; i < n_regions; ++i) {
+    const mpk_region& r = regions[i];
+    if (r.task < 0 || r.task >= n_tasks) return fail(MPK_ERR_INVALID_ARG, "region names a missing task");
+    Box b;
+    b.tensor = r.tensor;
+    for (int k = 0; k < 4; ++k) { b.lo[k] = r.lo[k]; b.hi[k] = r.hi[k]; }
+    (r.is_out ? tasks[r.task].outs : tasks[r.task].ins).push_back(b);
+  }
+  Graph g;
+  std::string err;
+  int rc = canonicalize(tasks, n_workers, &g, &err);
+  if (rc) return fail(rc, err);
+  mpk_tgraph_header h{};
+  h.n_tasks = g.NT; h.n_events = g.NE; h.root = g.root; h.end = g.end; h.n_fused = g.n_fused;
+  h.n_empty = g.n_empty; h.n_rewrites = g.n_rewrites; h.n_aot = (int32_t)g.aot_tasks.size();
+  h.params.n_workers = n_workers; h.params.host_only = 1;
+  return export_graph(g, h, out);
+}
+
+void mpk_free_host_view(mpk_tgraph_host_view* v) {
+  if (!v) return;
+  void* ptrs[] = {v->task_type, v->task_mode, v->task_layer, v->task_coords, v->task_orig, v->task_dep, v->task_trig,
+                  v->task_worker, v->event_counts, v->event_first, v->event_last, v->event_flags, v->aot_offsets,
+                  v->aot_tasks};
+  for (void* p : ptrs) std::free(p);
+  std::memset(v, 0, sizeof(*v));
+}
+
+int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+                    const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  KArgs a;
+  int rc = step_args(g, w, token_ids, kv, seq_lens, logits, next_ids, s, &a);
+  if (rc) return rc;
+  a.epoch = ++g->epoch;
+  hipError_t e = launch_megakernel(a, g->grid, s);
+  if (e != hipSuccess) { --g->epoch; return hip_fail(e, "mega-kernel launch"); }
+  g->last_stream = s;
+  return MPK_OK;
+}
+
+int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+                             const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream,
+                             int32_t use_hipgraph) {
+  hipStream_t s = (hipStream_t)stream;
+  KArgs a;
+  int rc = step_args(g, w, token_ids, kv, seq_lens, logits, next_ids, s, &a);
+  if (rc) return rc;
+  a.epoch = g->epoch;
+  g->last_stream = s;
+  if (!use_hipgraph) {
+    for (auto& op : g->ops) {
+      if (!op.second) continue;
+      hipError_t e = launch_baseline_op(a, g->d_lists + op.first, op.second, s);
+      if (e != hipSuccess) return hip_fail(e, "baseline launch");
+    }
+    return MPK_OK;
+  }
+  std::vector<uintptr_t> key = {(uintptr_t)a.embed, (uintptr_t)a.lm_head, (uintptr_t)a.final_norm,
+                                (uintptr_t)a.k_pool, (uintptr_t)a.v_pool, (uintptr_t)a.page_table,
+                                (uintptr_t)a.n_pages, (uintptr_t)a.max_pages, (uintptr_t)a.token_ids,
+                                (uintptr_t)a.seq_lens, (uintptr_t)a.logits, (uintptr_t)a.next_ids};
+  for (auto p : g->h_wl) key.push_back((uintptr_t)p);
+  if (!g->gexec || key != g->gkey) {
+    if (g->gexec) { (void)hipGraphExecDestroy(g->gexec); g->gexec = nullptr; }
+    if (!g->cap_stream) HIPCHK(hipStreamCreateWithFlags(&g->cap_stream, hipStreamNonBlocking));
+    HIPCHK(hipStreamBeginCapture(g->cap_stream, hipStreamCaptureModeThreadLocal));
+    for (auto& op : g->ops) {
+      if (!op.second) continue;
+      hipError_t e = launch_baseline_op(a, g->d_lists + op.first, op.second, g->cap_stream);
+      if (e != hipSuccess) {
+        hipGraph_t dummy;
+        (void)hipStreamEndCapture(g->cap_stream, &dummy);
+        return hip_fail(e, "baseline capture");
+      }
+    }
+    hipGraph_t graph;
+    HIPCHK(hipStreamEndCapture(g->cap_stream, &graph));
+    hipError_t e = hipGraphInstantiate(&g->gexec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) { g->gexec = nullptr; return hip_fail(e, "hipGraphInstantiate"); }
+    g->gkey = key;
+  }
+  HIPCHK(hipGraphLaunch(g->gexec, s));
+  return MPK_OK;
+}
+
+int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes) {
+  if (!g || !dst) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  if (g->host_only) return fail(MPK_ERR_INVALID_ARG, "graph was built host-only");
+  if (tensor < 0 || tensor >= (int32_t)g->tensors.size() || !g->tensors[tensor].p)
+    return fail(MPK_ERR_INVALID_ARG, "tensor id names no library-owned buffer");
+  if ((int64_t)bytes != g->tensors[tensor].bytes) return fail(MPK_ERR_INVALID_ARG, "byte count does not match tensor");
+  HIPCHK(hipDeviceSynchronize());
+  HIPCHK(hipMemcpy(dst, g->tensors[tensor].p, bytes, hipMemcpyDeviceToHost));
+  return MPK_OK;
+}
+
+int mpk_set_watchdog(mpk_tgraph* g, uint64_t timeout_ns) {
+  if (!g) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  g->timeout_ns = timeout_ns ? timeout_ns : 2000000000ull;
+  return MPK_OK;
+}
+
+int mpk_get_status(mpk_tgraph* g, mpk_status_word* out) {
+  if (!g || !out) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  std::memset(out, 0, sizeof(*out));
+  if (g->host_only) return MPK_OK;
+  if (g->last_stream) HIPCHK(hipStreamSynchronize(g->last_stream));
+  else HIPCHK(hipDeviceSynchronize());
+  StatusWord s;
+  HIPCHK(hipMemcpy(&s, g->d_status, sizeof(s), hipMemcpyDeviceToHost));
+  out->code = s.code; out->wg = s.wg; out->task = s.task; out->event = s.event; out->counter = s.counter;
+  out->target = s.target;
+  return MPK_OK;
+}
+
+void mpk_destroy_tgraph(mpk_tgraph* g) { free_tgraph(g); }
+
+}  // extern "C"

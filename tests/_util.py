@@ -10,33 +10,40 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+def host_f32(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> exact fp32 numpy copy (widened on the tensor's device)."""
+    return t.detach().float().cpu().numpy()
+
+
 class LazyLayers:
     """Per-layer weights copied to the host only when the oracle asks for them."""
 
-    def __init__(self, layers):
+    def __init__(self, layers, conv):
         self._layers = layers
+        self._conv = conv
 
     def __len__(self):
         return len(self._layers)
 
     def __getitem__(self, l):
-        return {k: bf16_bits(v) for k, v in self._layers[l].items()}
+        return {k: self._conv(v) for k, v in self._layers[l].items()}
 
 
-def oracle_weights(w: dict, lazy: bool = False) -> dict:
-    layers = LazyLayers(w["layers"]) if lazy else [
-        {k: bf16_bits(v) for k, v in lw.items()} for lw in w["layers"]]
-    return {"embed": bf16_bits(w["embed"]), "final_norm": bf16_bits(w["final_norm"]),
-            "lm_head": None if w["lm_head"] is None else bf16_bits(w["lm_head"]), "layers": layers}
+def oracle_weights(w: dict, lazy: bool = False, widen_on_device: bool = False) -> dict:
+    conv = host_f32 if widen_on_device else bf16_bits
+    layers = LazyLayers(w["layers"], conv) if lazy else [
+        {k: conv(v) for k, v in lw.items()} for lw in w["layers"]]
+    return {"embed": bf16_bits(w["embed"]), "final_norm": conv(w["final_norm"]),
+            "lm_head": None if w["lm_head"] is None else conv(w["lm_head"]), "layers": layers}
 
 
-def run_oracle(inp: dict, dtype=np.float32, capture=None, lazy=False):
+def run_oracle(inp: dict, dtype=np.float32, capture=None, lazy=False, widen_on_device=False):
     from oracle import numerics
     s = inp["shape"]
     kv = inp["kv"]
-    return numerics.decode_step(s.cfg(), oracle_weights(inp["weights"], lazy=lazy),
-                                inp["token_ids"].numpy(), bf16_bits(kv["k_pool"]), bf16_bits(kv["v_pool"]),
-                                kv["page_table"].numpy(), inp["seq_lens"].numpy(), s.page_size,
+    return numerics.decode_step(s.cfg(), oracle_weights(inp["weights"], lazy=lazy, widen_on_device=widen_on_device),
+                                inp["token_ids"].cpu().numpy(), bf16_bits(kv["k_pool"]), bf16_bits(kv["v_pool"]),
+                                kv["page_table"].cpu().numpy(), inp["seq_lens"].cpu().numpy(), s.page_size,
                                 dtype=dtype, capture=capture)
 
 

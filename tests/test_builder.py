@@ -1,0 +1,137 @@
+"""The C++ tGraph builder (through the C ABI, host only) against the oracle spec,
+bit for bit on every exported index array, plus the C ABI surface (CPU only)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, HealthCheck
+
+import synth
+import task_graph_runtime_amd as mpk
+from oracle import tgraph as tg
+from tests.test_tgraph_oracle import programs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ARRAYS = ["task_type", "task_mode", "task_layer", "task_coords", "task_orig", "task_dep", "task_trig",
+          "task_worker", "event_counts", "event_first", "event_last", "event_flags", "aot_offsets", "aot_tasks"]
+
+
+def assert_same(ref, got):
+    for k in ARRAYS:
+        assert ref[k].dtype == got[k].dtype, k
+        assert np.array_equal(ref[k], got[k]), k
+    assert ref["header"] == got["header"]
+
+
+def both(shape, B, W, q=None, S=None, **over):
+    s = shape
+    hkv = s.n_kv_heads
+    q = q if q is not None else (1 if B == 1 else 16)
+    prm = tg.Params(W=W, q=q, S_attn=S or 4, **over)
+    for f, N in (("T_o", s.hidden), ("T_gu", s.ffn), ("T_down", s.hidden), ("T_lm", s.vocab)):
+        if f not in over:
+            setattr(prm, f, min(W, -(-N // q)))
+    if "T_qkv" not in over:
+        Sg = (s.n_q_heads // hkv + 2) * s.head_dim
+        prm.T_qkv = max(1, min(W // hkv, -(-Sg // q))) * hkv
+    ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
+    params = dict(n_workers=W, quantum=q, t_qkv=prm.T_qkv, t_o=prm.T_o, t_gu=prm.T_gu, t_down=prm.T_down,
+                  t_lm=prm.T_lm, s_attn=prm.S_attn)
+    got = mpk.TGraph(s.cfg(), B, s.page_size, params, host_only=True).export()
+    return ref, got, tasks
+
+
+def test_tiny_worked_example_bit_exact():
+    s = synth.SHAPES["tiny"]
+    ref, got, tasks = both(s, 1, 8, q=64, S=4, T_qkv=8, T_o=4, T_gu=11, T_down=4, T_lm=16)
+    assert_same(ref, got)
+    assert got["header"]["NT"] == 109 and got["header"]["NE"] == 33
+    tg.check_semantics(got, tasks, closure=True)
+
+
+@pytest.mark.parametrize("name,B,W,S,layers", [
+    ("tiny", 1, 8, 4, 2), ("tiny", 5, 13, 3, 2), ("tiny", 16, 252, 2, 2),
+    ("qwen3_0p6b", 1, 252, 16, 2), ("qwen3_8b", 1, 252, 16, 1), ("qwen3_8b_b16", 16, 252, 4, 1),
+    ("qwen3_32b", 1, 252, 16, 1)])
+def test_layer_cuts_bit_exact(name, B, W, S, layers):
+    s = synth.SHAPES[name].with_(n_layers=layers)
+    ref, got, tasks = both(s, B, W, S=S)
+    assert_same(ref, got)
+    tg.check_semantics(got, tasks, closure=(len(tasks) < 3000))
+
+
+@pytest.mark.parametrize("name", ["qwen3_0p6b", "qwen3_8b", "qwen3_8b_b16"])
+def test_full_graph_bit_exact(name):
+    s = synth.SHAPES[name]
+    ref, got, _ = both(s, s.batch, 252, S=16 if s.batch == 1 else 4)
+    assert_same(ref, got)
+    tg.check_semantics(got, None)
+
+
+def test_default_params_resolve_as_documented():
+    s = synth.SHAPES["qwen3_8b"]
+    h = mpk.TGraph(s.cfg(), 1, 64, {}, host_only=True).header()
+    p = h["params"]
+    assert p["n_workers"] == 252 and p["n_sched_waves"] == 16 and p["quantum"] == 1
+    assert p["t_qkv"] == 248 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 252 and p["s_attn"] == 16
+    h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
+    assert h16["quantum"] == 16 and h16["s_attn"] == 4
+
+
+@settings(max_examples=120, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(programs())
+def test_generic_entry_matches_spec(prog):
+    specs, regions, W = prog
+    tasks = tg.generic_tasks(specs, regions)
+    ref = tg.canonicalize(tasks, W)
+    got = mpk.build_generic(specs, regions, W)
+    assert_same(ref, got)
+
+
+# ------------------------------------------------------------------ C ABI surface
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "mpk.h")).read()
+    return sorted(set(re.findall(r"\b(mpk_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.CDLL(os.path.join(ROOT, "task_graph_runtime_amd", "libmpk.so"))
+    syms = header_symbols()
+    assert len(syms) >= 13
+    for name in syms:
+        assert hasattr(L, name), name
+    assert set(syms) == set(mpk.SIGNATURES)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=96), -2), (dict(n_q_heads=5), -1), (dict(hidden=260), -2), (dict(qk_norm=2), -1)])
+def test_bad_config_rejected(over, code):
+    c = mpk.model_cfg(synth.SHAPES["tiny"].cfg())
+    for k, v in over.items():
+        setattr(c, k, v)
+    with pytest.raises(mpk.MpkError) as e:
+        mpk.TGraph(c, 1, 16, {}, host_only=True)
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("B,P,params,code", [
+    (0, 16, {}, -2), (17, 16, {}, -2), (1, 24, {}, -2), (1, 16, dict(t_qkv=3), -1),
+    (1, 16, dict(fusion_order=1), -2), (1, 16, dict(t_o=100000), -1)])
+def test_bad_build_args_rejected(B, P, params, code):
+    with pytest.raises(mpk.MpkError) as e:
+        mpk.TGraph(synth.SHAPES["tiny"].cfg(), B, P, params, host_only=True)
+    assert e.value.code == code
+
+
+def test_host_only_graph_refuses_to_run():
+    g = mpk.TGraph(synth.SHAPES["tiny"].cfg(), 1, 16, {}, host_only=True)
+    w = mpk.mpk_weights()
+    rc = mpk.lib().mpk_decode_step(g.h, C.byref(w), None, None, None, None, None, None)
+    assert rc == -1
+
+
+def test_generic_entry_rejects_bad_regions():
+    with pytest.raises(mpk.MpkError):
+        mpk.build_generic([(2, 0, 0, 0, 0)], [(5, 1, 0, (0, 0, 0, 0), (1, 1, 1, 1))], 1)
