@@ -51,7 +51,7 @@ enum {
 /* Task types of the decoder tGraph (the order is the program order of one layer). */
 enum {
   MPK_TASK_EMBED = 0,       /* e[b,:] = E[token_ids[b], :] (fp32)                        */
-  MPK_TASK_ATTN_NORM = 1,   /* r = residual in; h = RMSNorm(r) (bf16)                    */
+  MPK_TASK_ATTN_NORM = 1,   /* r = residual in; h = RMSNorm(r) (fp32)                    */
   MPK_TASK_QKV = 2,         /* tile of the fused q/k/v projection (group-major columns)  */
   MPK_TASK_QKNORM_ROPE = 3, /* per (b, kv group): q/k RMSNorm, RoPE, KV-cache append     */
   MPK_TASK_ATTN = 4,        /* per (b, kv group, split): paged attention partials (JIT)  */
@@ -215,11 +215,12 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
                              int32_t use_hipgraph);
 
 /* Copy intermediate tensor `tensor` of the last step to host memory `dst`
- * (`bytes` must equal its size).  Ids: 0 e[B][H] fp32, 1 hf[B][H] bf16,
- * 3 pmax[B][t_lm] (fp32 value, int32 index pairs); per layer l, 5 + 13*l + k
- * with k = 0 r fp32, 1 h bf16, 2 qkv bf16 (group-major), 3 q fp32, 6 attention
- * partials fp32, 7 attn bf16, 8 o bf16, 9 s fp32, 10 h2 bf16, 11 a bf16,
- * 12 d bf16 (all [B][...]).  Synchronises the device. */
+ * (`bytes` must equal its size).  All are fp32 [B][...]: ids 0 e[B][H],
+ * 1 hf[B][H], 3 pmax[B][t_lm] (fp32 value, int32 index pairs); per layer l,
+ * 5 + 13*l + k with k = 0 r, 1 h, 2 qkv (group-major: per kv group its query
+ * heads, key head, value head), 3 q (after norm and RoPE), 6 attention
+ * partials [B][kv][s_attn][G][2 + head_dim] (max, sum, output), 7 attn,
+ * 8 o, 9 s, 10 h2, 11 a, 12 d.  Synchronises the device. */
 int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes);
 
 /* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it). */

@@ -237,10 +237,10 @@ int upload(mpk_tgraph* t) {
   a.st_bh = B * H; a.st_qkv = B * hkv * Sg; a.st_q = B * hq * d; a.st_part = B * hkv * S_at * G * (d + 2);
   a.st_a = B * F;
   struct Item { int id; int64_t bytes; };
-  std::vector<Item> items = {{T_E, B * H * 4}, {T_HF, B * H * 2}, {T_PMAX, B * (int64_t)t->prm.T_lm * 8}};
-  const int64_t per_layer_bytes[L_COUNT] = {a.st_bh * 4, a.st_bh * 2, a.st_qkv * 2, a.st_q * 4, 0, 0,
-                                            a.st_part * 4, a.st_q * 2, a.st_bh * 2, a.st_bh * 4,
-                                            a.st_bh * 2, a.st_a * 2, a.st_bh * 2};
+  std::vector<Item> items = {{T_E, B * H * 4}, {T_HF, B * H * 4}, {T_PMAX, B * (int64_t)t->prm.T_lm * 8}};
+  const int64_t per_layer_bytes[L_COUNT] = {a.st_bh * 4, a.st_bh * 4, a.st_qkv * 4, a.st_q * 4, 0, 0,
+                                            a.st_part * 4, a.st_q * 4, a.st_bh * 4, a.st_bh * 4,
+                                            a.st_bh * 4, a.st_a * 4, a.st_bh * 4};
   // one contiguous [L][...] block per per-layer tensor kind
   int64_t off = 0;
   std::vector<int64_t> shared_off(5, -1), kind_off(L_COUNT, -1);
@@ -254,19 +254,19 @@ int upload(mpk_tgraph* t) {
   HIPCHK(hipMemset(t->d_act, 0, off));
   char* ab = (char*)t->d_act;
   a.e = (float*)(ab + shared_off[T_E]);
-  a.hf = (uint16_t*)(ab + shared_off[T_HF]);
+  a.hf = (float*)(ab + shared_off[T_HF]);
   a.pmax = (PMax*)(ab + shared_off[T_PMAX]);
   a.r = (float*)(ab + kind_off[L_R]);
-  a.h = (uint16_t*)(ab + kind_off[L_H]);
-  a.qkv = (uint16_t*)(ab + kind_off[L_QKV]);
+  a.h = (float*)(ab + kind_off[L_H]);
+  a.qkv = (float*)(ab + kind_off[L_QKV]);
   a.q = (float*)(ab + kind_off[L_Q]);
   a.part = (float*)(ab + kind_off[L_PART]);
-  a.attn = (uint16_t*)(ab + kind_off[L_ATTN]);
-  a.o = (uint16_t*)(ab + kind_off[L_O]);
+  a.attn = (float*)(ab + kind_off[L_ATTN]);
+  a.o = (float*)(ab + kind_off[L_O]);
   a.s = (float*)(ab + kind_off[L_S]);
-  a.h2 = (uint16_t*)(ab + kind_off[L_H2]);
-  a.a = (uint16_t*)(ab + kind_off[L_A]);
-  a.dn = (uint16_t*)(ab + kind_off[L_D]);
+  a.h2 = (float*)(ab + kind_off[L_H2]);
+  a.a = (float*)(ab + kind_off[L_A]);
+  a.dn = (float*)(ab + kind_off[L_D]);
   t->tensors.assign(5 + 13 * (size_t)L, {nullptr, 0});
   for (auto& it : items) t->tensors[it.id] = {ab + shared_off[it.id], it.bytes};
   for (int64_t l = 0; l < L; ++l)

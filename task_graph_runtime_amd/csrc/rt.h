@@ -86,11 +86,12 @@ struct KArgs {
   float* logits;
   int32_t* next_ids;
   // activations; per-layer tensors are [L][...] with the strides below (elements)
+  // (all fp32: only the weights and the KV cache, the caller's formats, are bf16)
   float* e;
-  uint16_t* hf;
+  float* hf;
   PMax* pmax;
-  float* r;  uint16_t* h;  uint16_t* qkv;  float* q;  float* part;  uint16_t* attn;
-  uint16_t* o;  float* s;  uint16_t* h2;  uint16_t* a;  uint16_t* dn;
+  float* r;  float* h;  float* qkv;  float* q;  float* part;  float* attn;
+  float* o;  float* s;  float* h2;  float* a;  float* dn;
   int64_t st_bh, st_qkv, st_q, st_part, st_a;
 };
 

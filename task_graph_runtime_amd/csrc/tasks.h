@@ -3,8 +3,10 @@
 // kernel-per-operator baseline run the same functions.
 //
 // Operations (MPK summary page, section 3 "Target operation, shapes &
-// precision contract"): projection tiles read bf16 weights and activations
-// and accumulate in fp32, storing bf16 (fp32 logits for the LM head);
+// precision contract"): projection tiles read bf16 weights and accumulate in
+// fp32.  Activations passed between tasks stay fp32 (the page's bf16 task
+// outputs, compounded over 28-64 layers, drift past the 2e-2 logit bound
+// against the fp32 forward); only weights and the KV cache are bf16;
 // attention is paged decode attention of one new query per request against
 // its KV pages.  The decoder layer around them is the Qwen3 layer (RMSNorm,
 // per-head q/k RMSNorm, rotate-half RoPE, GQA, SwiGLU).
@@ -35,11 +37,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
-  acc = fmaf(bflo(w.x), bflo(x.x), acc); acc = fmaf(bfhi(w.x), bfhi(x.x), acc);
-  acc = fmaf(bflo(w.y), bflo(x.y), acc); acc = fmaf(bfhi(w.y), bfhi(x.y), acc);
-  acc = fmaf(bflo(w.z), bflo(x.z), acc); acc = fmaf(bfhi(w.z), bfhi(x.z), acc);
-  acc = fmaf(bflo(w.w), bflo(x.w), acc); acc = fmaf(bfhi(w.w), bfhi(x.w), acc);
+__device__ __forceinline__ float4 ldf4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// 8 bf16 weights (one 16-byte load) times 8 fp32 activations, fp32 accumulate.
+__device__ __forceinline__ float dot8(uint4 w, float4 x0, float4 x1, float acc) {
+  acc = fmaf(bflo(w.x), x0.x, acc); acc = fmaf(bfhi(w.x), x0.y, acc);
+  acc = fmaf(bflo(w.y), x0.z, acc); acc = fmaf(bfhi(w.y), x0.w, acc);
+  acc = fmaf(bflo(w.z), x1.x, acc); acc = fmaf(bfhi(w.z), x1.y, acc);
+  acc = fmaf(bflo(w.w), x1.z, acc); acc = fmaf(bfhi(w.w), x1.w, acc);
   return acc;
 }
 
@@ -113,9 +118,9 @@ __device__ void embed_task(const KArgs& a) {
 }
 
 // ------------------------------------------------------------------ residual add + RMSNorm
-// out32 = in32 + in16 (fp32, optional); out16 = RMSNorm(out32) * gamma (bf16).
-__device__ void norm_task(const KArgs& a, const float* in32, const uint16_t* in16, float* out32,
-                          const uint16_t* gamma, uint16_t* out16, float* red) {
+// res = x + y (y optional), stored when `res` is given; out = RMSNorm(res) * gamma.
+__device__ void norm_task(const KArgs& a, const float* x, const float* y, float* res, const uint16_t* gamma,
+                          float* out, float* red) {
   const int H = a.H;
   for (int b = 0; b < a.B; ++b) {
     float v[kMaxHidden / kThreads];
@@ -125,11 +130,11 @@ __device__ void norm_task(const KArgs& a, const float* in32, const uint16_t* in1
       int i = threadIdx.x + j * kThreads;
       v[j] = 0.f;
       if (i < H) {
-        float x = in32[(int64_t)b * H + i];
-        if (in16) x += bf2f(in16[(int64_t)b * H + i]);
-        v[j] = x;
-        ss = fmaf(x, x, ss);
-        if (out32) out32[(int64_t)b * H + i] = x;
+        float t = x[(int64_t)b * H + i];
+        if (y) t += y[(int64_t)b * H + i];
+        v[j] = t;
+        ss = fmaf(t, t, ss);
+        if (res) res[(int64_t)b * H + i] = t;
       }
     }
     ss = block_sum(ss, red);
@@ -137,7 +142,7 @@ __device__ void norm_task(const KArgs& a, const float* in32, const uint16_t* in1
 #pragma unroll
     for (int j = 0; j < kMaxHidden / kThreads; ++j) {
       int i = threadIdx.x + j * kThreads;
-      if (i < H) out16[(int64_t)b * H + i] = f2bf(v[j] * inv * bf2f(gamma[i]));
+      if (i < H) out[(int64_t)b * H + i] = v[j] * inv * bf2f(gamma[i]);
     }
   }
 }
@@ -178,7 +183,7 @@ __device__ void gemv_task(const KArgs& a, const DevTask& t, float* acc, float* r
   const int type = t.type, l = t.layer, lo = t.a0, hi = t.a1;
   const int B = a.B;
   int K, rpc = 1;
-  const uint16_t* x;
+  const float* x;
   switch (type) {
     case MPK_TASK_QKV: K = a.H; x = a.h + (int64_t)l * a.st_bh; break;
     case MPK_TASK_OPROJ: K = a.hq * a.d; x = a.attn + (int64_t)l * a.st_q; break;
@@ -210,18 +215,19 @@ __device__ void gemv_task(const KArgs& a, const DevTask& t, float* acc, float* r
     }
   };
   for (int s0 = s_beg; s0 < s_end; s0 += U) {
-    uint4 wv[U], xv[U];
+    uint4 wv[U];
+    float4 xa[U], xb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u;
       wv[u] = make_uint4(0, 0, 0, 0);
-      xv[u] = make_uint4(0, 0, 0, 0);
+      xa[u] = xb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (s < s_end) {
         const int r = s / nseg;
         const int k = (s - r * nseg) * 512 + lane * 8;
         if (k < K) {
           wv[u] = ld16(gemv_row(a, type, l, lo, r) + k);
-          if (BT == 1) xv[u] = ld16(x + k);
+          if (BT == 1) { xa[u] = ldf4(x + k); xb[u] = ldf4(x + k + 4); }
         }
       }
     }
@@ -237,11 +243,14 @@ __device__ void gemv_task(const KArgs& a, const DevTask& t, float* acc, float* r
         }
         if (k < K) {
           if (BT == 1) {
-            av[0] = dot8(wv[u], xv[u], av[0]);
+            av[0] = dot8(wv[u], xa[u], xb[u], av[0]);
           } else {
 #pragma unroll
             for (int b = 0; b < BT; ++b)
-              if (b < B) av[b] = dot8(wv[u], ld16(x + (int64_t)b * K + k), av[b]);
+              if (b < B) {
+                const float* xr = x + (int64_t)b * K + k;
+                av[b] = dot8(wv[u], ldf4(xr), ldf4(xr + 4), av[b]);
+              }
           }
         }
       }
@@ -254,28 +263,28 @@ __device__ void gemv_task(const KArgs& a, const DevTask& t, float* acc, float* r
   switch (type) {
     case MPK_TASK_QKV: {
       const int ld = a.hkv * a.Sg;
-      uint16_t* out = a.qkv + (int64_t)l * a.st_qkv;
+      float* out = a.qkv + (int64_t)l * a.st_qkv;
       for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
-        out[(int64_t)b * ld + lo + c] = f2bf(acc[c * B + b]);
+        out[(int64_t)b * ld + lo + c] = acc[c * B + b];
       }
       break;
     }
     case MPK_TASK_OPROJ:
     case MPK_TASK_DOWN: {
-      uint16_t* out = (type == MPK_TASK_OPROJ ? a.o : a.dn) + (int64_t)l * a.st_bh;
+      float* out = (type == MPK_TASK_OPROJ ? a.o : a.dn) + (int64_t)l * a.st_bh;
       for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
-        out[(int64_t)b * a.H + lo + c] = f2bf(acc[c * B + b]);
+        out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
       }
       break;
     }
     case MPK_TASK_GATEUP: {
-      uint16_t* out = a.a + (int64_t)l * a.st_a;
+      float* out = a.a + (int64_t)l * a.st_a;
       for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         float g = acc[(2 * c) * B + b], u = acc[(2 * c + 1) * B + b];
-        out[(int64_t)b * a.F + lo + c] = f2bf(g / (1.0f + expf(-g)) * u);
+        out[(int64_t)b * a.F + lo + c] = g / (1.0f + expf(-g)) * u;
       }
       break;
     }
@@ -325,7 +334,7 @@ __device__ void rope_task(const KArgs& a, const DevTask& t) {
   if (!(pid >= 0 && pid < a.n_pages)) ok = false;
   if (!ok && threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, (uint32_t)pid);
   const int64_t slot = ok ? ((((int64_t)l * a.n_pages + pid) * a.hkv + g) * a.P + (Lb % a.P)) * d : 0;
-  const uint16_t* src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
+  const float* src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
   const uint16_t* const* W = a.wl + (int64_t)l * LAYER_PTRS;
   const bool act = lane < half;
   // angle of pair `lane`: L_b * theta^(-2*lane/d), in double
@@ -336,12 +345,12 @@ __device__ void rope_task(const KArgs& a, const DevTask& t) {
     sn = (float)sin(ang);
   }
   for (int hh = w; hh < G + 2; hh += kWaves) {
-    float x0 = act ? bf2f(src[hh * d + lane]) : 0.f;
-    float x1 = act ? bf2f(src[hh * d + lane + half]) : 0.f;
-    if (hh == G + 1) {  // value head: bf16 copy into the cache
+    float x0 = act ? src[hh * d + lane] : 0.f;
+    float x1 = act ? src[hh * d + lane + half] : 0.f;
+    if (hh == G + 1) {  // value head: rounded into the bf16 cache
       if (act && ok) {
-        a.v_pool[slot + lane] = src[hh * d + lane];
-        a.v_pool[slot + lane + half] = src[hh * d + lane + half];
+        a.v_pool[slot + lane] = f2bf(x0);
+        a.v_pool[slot + lane + half] = f2bf(x1);
       }
       continue;
     }
@@ -503,7 +512,7 @@ __device__ void attn_task(const KArgs& a, const DevTask& t, float* lds) {
 __device__ void combine_task(const KArgs& a, const DevTask& t) {
   const int b = t.a0, g = t.a1, l = t.layer, G = a.G, D = a.d, S = a.S_attn;
   const float* part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)(G * (D + 2));
-  uint16_t* out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
+  float* out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
     const int h = e / D, dd = e - h * D;
     float M = -INFINITY;
@@ -517,7 +526,7 @@ __device__ void combine_task(const KArgs& a, const DevTask& t) {
         O = fmaf(p[2 + dd], f, O);
       }
     }
-    out[h * D + dd] = f2bf(L > 0.f ? O / L : 0.f);
+    out[h * D + dd] = L > 0.f ? O / L : 0.f;
   }
 }
 

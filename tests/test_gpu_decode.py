@@ -80,7 +80,8 @@ def check_cache(inp, cap):
             for pool, name in ((kv["k_pool"], "k_new"), (kv["v_pool"], "v_new")):
                 got = pool[l, pid, :, Lb % P, :].float().cpu().numpy()
                 want = bf16_round(cap[l][name][b])
-                np.testing.assert_allclose(got, want, rtol=1.6e-2, atol=1e-3, err_msg=f"{name} l={l} b={b}")
+                # same bound as the logits: both sides round to bf16 from slightly different fp32 values
+                np.testing.assert_allclose(got, want, rtol=RTOL, atol=ATOL, err_msg=f"{name} l={l} b={b}")
 
 
 TINY = synth.SHAPES["tiny"]
@@ -111,28 +112,26 @@ def test_tiny_intermediates_layer_by_layer():
     hq, hkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
     G = hq // hkv
 
-    def bf(x):
-        return (x.astype(np.uint32) << 16).view(np.float32)
     np.testing.assert_allclose(g.read_tensor(0, (B, H), np.float32), cap["embed"], rtol=0, atol=0)
     for l in range(s.n_layers):
         t = lambda k: 5 + 13 * l + k
         c = cap[l]
         np.testing.assert_allclose(g.read_tensor(t(0), (B, H), np.float32), c["r"], rtol=2e-2, atol=2e-2)
-        np.testing.assert_allclose(bf(g.read_tensor(t(1), (B, H), np.uint16)), c["h"], rtol=2e-2, atol=2e-2)
-        qkv = bf(g.read_tensor(t(2), (B, hkv, (G + 2) * d), np.uint16))
+        np.testing.assert_allclose(g.read_tensor(t(1), (B, H), np.float32), c["h"], rtol=2e-2, atol=2e-2)
+        qkv = g.read_tensor(t(2), (B, hkv, (G + 2) * d), np.float32)
         # oracle qkv is [q heads | k heads | v heads]; the library's is group-major
         oq = c["qkv"][:, :hq * d].reshape(B, hkv, G * d)
         ok = c["qkv"][:, hq * d:(hq + hkv) * d].reshape(B, hkv, d)
         ov = c["qkv"][:, (hq + hkv) * d:].reshape(B, hkv, d)
         np.testing.assert_allclose(qkv, np.concatenate([oq, ok, ov], axis=2), rtol=3e-2, atol=3e-2)
         np.testing.assert_allclose(g.read_tensor(t(3), (B, hq * d), np.float32), c["q"], rtol=3e-2, atol=3e-2)
-        np.testing.assert_allclose(bf(g.read_tensor(t(7), (B, hq * d), np.uint16)), c["attn"], rtol=3e-2, atol=3e-2)
-        np.testing.assert_allclose(bf(g.read_tensor(t(8), (B, H), np.uint16)), c["o"], rtol=3e-2, atol=3e-2)
+        np.testing.assert_allclose(g.read_tensor(t(7), (B, hq * d), np.float32), c["attn"], rtol=3e-2, atol=3e-2)
+        np.testing.assert_allclose(g.read_tensor(t(8), (B, H), np.float32), c["o"], rtol=3e-2, atol=3e-2)
         np.testing.assert_allclose(g.read_tensor(t(9), (B, H), np.float32), c["s"], rtol=3e-2, atol=3e-2)
-        np.testing.assert_allclose(bf(g.read_tensor(t(10), (B, H), np.uint16)), c["h2"], rtol=3e-2, atol=3e-2)
-        np.testing.assert_allclose(bf(g.read_tensor(t(11), (B, F), np.uint16)), c["a"], rtol=3e-2, atol=3e-2)
-        np.testing.assert_allclose(bf(g.read_tensor(t(12), (B, H), np.uint16)), c["d"], rtol=3e-2, atol=3e-2)
-    np.testing.assert_allclose(bf(g.read_tensor(1, (B, H), np.uint16)), cap["hf"], rtol=3e-2, atol=3e-2)
+        np.testing.assert_allclose(g.read_tensor(t(10), (B, H), np.float32), c["h2"], rtol=3e-2, atol=3e-2)
+        np.testing.assert_allclose(g.read_tensor(t(11), (B, F), np.float32), c["a"], rtol=3e-2, atol=3e-2)
+        np.testing.assert_allclose(g.read_tensor(t(12), (B, H), np.float32), c["d"], rtol=3e-2, atol=3e-2)
+    np.testing.assert_allclose(g.read_tensor(1, (B, H), np.float32), cap["hf"], rtol=3e-2, atol=3e-2)
 
 
 @pytest.mark.parametrize("B,lens", [
@@ -224,13 +223,16 @@ def _full(name, seed=0, modes=("mega",), lazy=False):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(300)
 def test_qwen3_0p6b_shape():
     _full("qwen3_0p6b", modes=("mega", "base"))
 
 
+@pytest.mark.timeout(600)
 def test_qwen3_8b_shape():
     _full("qwen3_8b", modes=("mega", "graph"), lazy=True)
 
 
+@pytest.mark.timeout(600)
 def test_qwen3_8b_batch16_shape():
     _full("qwen3_8b_b16", modes=("mega",), lazy=True)
