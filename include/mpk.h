@@ -223,6 +223,33 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
  * 8 o, 9 s, 10 h2, 11 a, 12 d.  Synchronises the device. */
 int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes);
 
+/* Per-task trace of the persistent kernel: times are the GPU's constant-rate
+ * wall clock (ticks; ticks_per_us is reported by mpk_read_trace). */
+typedef struct {
+  int32_t task;     /* linear task index */
+  int32_t worker;   /* worker that ran it */
+  uint64_t t_wait;  /* the worker started looking for this task */
+  uint64_t t_start; /* its dependent event had fired / it was taken from the JIT ring */
+  uint64_t t_end;   /* its body finished (before its triggering event is advanced) */
+} mpk_trace_record;
+
+/* Turn tracing of mpk_decode_step on (1) or off (0).  Allocates (frees) a
+ * device buffer of one record per task; each step overwrites it. */
+int mpk_set_trace(mpk_tgraph* g, int32_t enable);
+
+/* Copy the records of the last traced step to host memory `out` (room for
+ * `capacity` records), grouped by worker in execution order.  *count
+ * receives the number written; *ticks_per_us the clock rate.  Synchronises. */
+int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32_t* count, double* ticks_per_us);
+
+/* Body micro-benchmark: runs the listed tasks (linear indices, host array of
+ * n) one after another in a single workgroup, each `reps` times, on the
+ * arguments and buffers of the last mpk_decode_step call (no events are
+ * waited on or advanced), and writes each task's mean duration in clock
+ * ticks to ticks[n] (host).  Synchronises. */
+int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, uint64_t* ticks,
+                   double* ticks_per_us);
+
 /* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it). */
 int mpk_set_watchdog(mpk_tgraph* g, uint64_t timeout_ns);
 

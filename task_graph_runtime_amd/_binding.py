@@ -78,6 +78,11 @@ class mpk_status_word(C.Structure):
                 ("counter", C.c_uint32), ("target", C.c_uint32)]
 
 
+class mpk_trace_record(C.Structure):
+    _fields_ = [("task", C.c_int32), ("worker", C.c_int32), ("t_wait", C.c_uint64), ("t_start", C.c_uint64),
+                ("t_end", C.c_uint64)]
+
+
 # symbol -> (restype, argtypes); the list every test checks against the header
 SIGNATURES = {
     "mpk_build_tgraph": (C.c_int, [C.POINTER(mpk_model_cfg), C.c_int32, C.c_int32, C.POINTER(C.c_void_p)]),
@@ -94,6 +99,11 @@ SIGNATURES = {
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32]),
     "mpk_read_tensor": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t]),
     "mpk_set_watchdog": (C.c_int, [C.c_void_p, C.c_uint64]),
+    "mpk_set_trace": (C.c_int, [C.c_void_p, C.c_int32]),
+    "mpk_read_trace": (C.c_int, [C.c_void_p, C.POINTER(mpk_trace_record), C.c_int32, C.POINTER(C.c_int32),
+                                 C.POINTER(C.c_double)]),
+    "mpk_time_tasks": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.POINTER(C.c_uint64),
+                                 C.POINTER(C.c_double)]),
     "mpk_get_status": (C.c_int, [C.c_void_p, C.POINTER(mpk_status_word)]),
     "mpk_destroy_tgraph": (None, [C.c_void_p]),
     "mpk_last_error": (C.c_char_p, []),
@@ -255,6 +265,30 @@ class TGraph:
         out = np.empty(shape, dtype=dtype)
         _check(lib().mpk_read_tensor(self.h, int(tensor), out.ctypes.data_as(C.c_void_p), out.nbytes))
         return out
+
+    def set_trace(self, enable: bool = True):
+        _check(lib().mpk_set_trace(self.h, int(bool(enable))))
+
+    def read_trace(self) -> tuple:
+        """Records of the last traced step as a numpy structured array, and ticks/us."""
+        cap = self.header()["n_tasks"] + 16
+        buf = (mpk_trace_record * cap)()
+        n = C.c_int32()
+        tpu = C.c_double()
+        _check(lib().mpk_read_trace(self.h, buf, cap, C.byref(n), C.byref(tpu)))
+        dt = np.dtype([("task", np.int32), ("worker", np.int32), ("t_wait", np.uint64), ("t_start", np.uint64),
+                       ("t_end", np.uint64)])
+        arr = np.frombuffer(bytes(buf), dtype=dt, count=cap)[: n.value].copy()
+        return arr, tpu.value
+
+    def time_tasks(self, tasks, reps: int = 5) -> np.ndarray:
+        """Mean duration (us) of each listed task run alone in one workgroup."""
+        n = len(tasks)
+        T = (C.c_int32 * n)(*[int(t) for t in tasks])
+        out = (C.c_uint64 * n)()
+        tpu = C.c_double()
+        _check(lib().mpk_time_tasks(self.h, T, n, int(reps), out, C.byref(tpu)))
+        return np.array(list(out), dtype=np.float64) / tpu.value
 
     def set_watchdog(self, ns: int):
         _check(lib().mpk_set_watchdog(self.h, int(ns)))

@@ -30,6 +30,11 @@ bool overlaps(const Box& a, const Box& b) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Kernel-side capacities (LDS budget of one workgroup).
+constexpr int64_t kMaxTileAcc = 8192;     // fp32 accumulators of one projection tile
+constexpr int64_t kMaxStagedK = 26624;    // batch-1 activation vector staged in LDS
+constexpr int64_t kMaxSplitPages = 4096;  // page ids staged per attention split
+
 }  // namespace
 
 int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build_params* in, int32_t n_cus,
@@ -67,11 +72,19 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
     int64_t tpg = std::max<int64_t>(1, std::min<int64_t>(r.W / hkv, cdiv(Sg, r.q)));
     r.T_qkv = (int32_t)(tpg * hkv);
   }
-  auto dflt = [&](int32_t v, int64_t N) { return v > 0 ? v : (int32_t)std::min<int64_t>(r.W, cdiv(N, r.q)); };
-  r.T_o = dflt(p.t_o, H);
-  r.T_gu = dflt(p.t_gu, F);
-  r.T_down = dflt(p.t_down, H);
-  r.T_lm = dflt(p.t_lm, V);
+  // default: one tile per worker, more (in steps of W) while a tile's
+  // accumulators (columns x rows per column x batch) exceed the LDS budget
+  auto dflt = [&](int32_t v, int64_t N, int64_t rpc) {
+    if (v > 0) return v;
+    const int64_t U = cdiv(N, r.q);
+    int64_t T = std::min<int64_t>(r.W, U);
+    while (T < U && r.q * cdiv(U, T) * rpc * B > kMaxTileAcc) T = std::min<int64_t>(U, T + r.W);
+    return (int32_t)T;
+  };
+  r.T_o = dflt(p.t_o, H, 1);
+  r.T_gu = dflt(p.t_gu, F, 2);
+  r.T_down = dflt(p.t_down, H, 1);
+  r.T_lm = dflt(p.t_lm, V, 1);
   int64_t max_pages = cdiv(c.max_seq_len, P);
   if (p.s_attn > 0) {
     r.S_attn = p.s_attn;
@@ -87,12 +100,15 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
     if (o.T < 1 || o.T > cdiv(o.N, r.q)) { *err = std::string(o.name) + ": tile count out of range"; return MPK_ERR_INVALID_ARG; }
     if (o.T > 65535) { *err = std::string(o.name) + ": more than 65535 tiles"; return MPK_ERR_INVALID_ARG; }
     int64_t widest = r.q * cdiv(cdiv(o.N, r.q), o.T);
-    if (widest * o.rows_per_col * B > 16384) {
-      *err = std::string(o.name) + ": tile too wide (columns x batch must stay within 16384 accumulators)";
+    if (widest * o.rows_per_col * B > kMaxTileAcc) {
+      *err = std::string(o.name) + ": tile too wide (columns x rows x batch must stay within 8192 accumulators)";
       return MPK_ERR_UNSUPPORTED;
     }
   }
   if (r.S_attn < 1 || r.S_attn > 65535) return bad("s_attn out of range");
+  if (max_pages > kMaxSplitPages) return uns("max_seq_len / page_size above 4096 pages");
+  if (B == 1 && std::max<int64_t>(std::max<int64_t>(H, F), (int64_t)c.n_q_heads * d) > kMaxStagedK)
+    return uns("a projection input longer than 26624 elements");
   *out = r;
   return MPK_OK;
 }

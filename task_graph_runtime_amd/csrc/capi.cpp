@@ -1,9 +1,10 @@
 // C ABI of the decode-step mega-kernel library (declared in include/mpk.h):
 // graph build and upload, the persistent-kernel step, the kernel-per-operator
 // baseline, export for the checker, status and intermediate-tensor readback.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -15,8 +16,9 @@
 #include "rt.h"
 
 namespace mpk {
-hipError_t launch_megakernel(const KArgs& a, int grid, hipStream_t stream);
-hipError_t launch_baseline_op(const KArgs& a, const int32_t* list, int count, hipStream_t stream);
+hipError_t launch_megakernel(const KArgs* d_args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
+hipError_t launch_baseline_op(const KArgs* d_args, const int32_t* list, int count, hipStream_t stream);
+hipError_t launch_time_task(const KArgs* d_args, int task, unsigned long long* out, hipStream_t stream);
 }  // namespace mpk
 
 using namespace mpk;
@@ -78,6 +80,11 @@ struct mpk_tgraph {
 
   void* d_act = nullptr;
   KArgs base{};             // arguments that do not change between steps
+  KArgs* d_args = nullptr;  // device copy read by the kernels
+  KArgs* h_stage = nullptr; // pinned staging of the device copy
+  hipEvent_t args_ev = nullptr;
+  KArgs uploaded{};
+  bool args_valid = false;
   struct TensorRef { void* p; int64_t bytes; };
   std::vector<TensorRef> tensors;  // indexed by tensor id (null when caller-owned)
 
@@ -90,6 +97,8 @@ struct mpk_tgraph {
   hipGraphExec_t gexec = nullptr;
   std::vector<uintptr_t> gkey;
   hipStream_t last_stream = nullptr;
+  void* d_trace = nullptr;  // trace records + counts
+  int32_t trace_cap = 0;
 };
 
 namespace {
@@ -188,7 +197,9 @@ int upload(mpk_tgraph* t) {
   build_op_lists(t, &flat);
   const int64_t o_lists = align256(o_aot + (int64_t)std::max<size_t>(1, g.aot_tasks.size()) * 4);
   const int64_t o_wl = align256(o_lists + (int64_t)std::max<size_t>(1, flat.size()) * 4);
-  const int64_t graph_bytes = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
+  const int64_t o_args = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
+  const int64_t o_freq = align256(o_args + (int64_t)sizeof(KArgs));
+  const int64_t graph_bytes = align256(o_freq + (int64_t)t->cfg.head_dim / 2 * 8);
   HIPCHK(hipMalloc(&t->d_graph, graph_bytes));
   char* gb = (char*)t->d_graph;
   std::vector<DevEvent> ev(g.NE);
@@ -199,6 +210,16 @@ int upload(mpk_tgraph* t) {
   t->d_aot_tasks = (uint32_t*)(gb + o_aot);
   t->d_lists = (int32_t*)(gb + o_lists);
   t->d_wl = (const uint16_t**)(gb + o_wl);
+  t->d_args = (KArgs*)(gb + o_args);
+  {
+    std::vector<double> inv(t->cfg.head_dim / 2);
+    for (size_t i = 0; i < inv.size(); ++i)
+      inv[i] = std::pow((double)t->cfg.rope_theta, -2.0 * (double)i / (double)t->cfg.head_dim);
+    HIPCHK(hipMemcpy(gb + o_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice));
+    t->base.inv_freq = (const double*)(gb + o_freq);
+  }
+  HIPCHK(hipHostMalloc((void**)&t->h_stage, sizeof(KArgs), hipHostMallocDefault));
+  HIPCHK(hipEventCreateWithFlags(&t->args_ev, hipEventDisableTiming));
   HIPCHK(hipMemcpy(t->d_tasks, t->h_tasks.data(), (size_t)g.NT * sizeof(DevTask), hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(t->d_events, ev.data(), (size_t)g.NE * sizeof(DevEvent), hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(t->d_aot_off, g.aot_offsets.data(), g.aot_offsets.size() * 4, hipMemcpyHostToDevice));
@@ -288,11 +309,17 @@ int upload(mpk_tgraph* t) {
 
 void free_tgraph(mpk_tgraph* t) {
   if (!t) return;
+  if (t->args_ev) {
+    (void)hipEventSynchronize(t->args_ev);
+    (void)hipEventDestroy(t->args_ev);
+  }
+  if (t->h_stage) (void)hipHostFree(t->h_stage);
   if (t->gexec) (void)hipGraphExecDestroy(t->gexec);
   if (t->cap_stream) (void)hipStreamDestroy(t->cap_stream);
   if (t->d_graph) (void)hipFree(t->d_graph);
   if (t->d_rt) (void)hipFree(t->d_rt);
   if (t->d_act) (void)hipFree(t->d_act);
+  if (t->d_trace) (void)hipFree(t->d_trace);
   delete t;
 }
 
@@ -377,10 +404,22 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   a.seq_lens = seq_lens;
   a.logits = logits;
   a.next_ids = next_ids;
-  a.timeout_ticks = (uint64_t)((double)t->timeout_ns * t->wall_khz / 1e6);
-  if (a.timeout_ticks < 1) a.timeout_ticks = 1;
   *out = a;
+  // refresh the device copy of the arguments when a caller pointer changed
+  if (!t->args_valid || std::memcmp(&a, &t->uploaded, sizeof(KArgs)) != 0) {
+    HIPCHK(hipEventSynchronize(t->args_ev));   // the staging buffer is free again
+    std::memcpy(t->h_stage, &a, sizeof(KArgs));
+    HIPCHK(hipMemcpyAsync(t->d_args, t->h_stage, sizeof(KArgs), hipMemcpyHostToDevice, stream));
+    HIPCHK(hipEventRecord(t->args_ev, stream));
+    t->uploaded = a;
+    t->args_valid = true;
+  }
   return MPK_OK;
+}
+
+uint64_t timeout_ticks(const mpk_tgraph* t) {
+  uint64_t v = (uint64_t)((double)t->timeout_ns * t->wall_khz / 1e6);
+  return v < 1 ? 1 : v;
 }
 
 int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const mpk_build_params* params,
@@ -491,8 +530,8 @@ int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_id
   KArgs a;
   int rc = step_args(g, w, token_ids, kv, seq_lens, logits, next_ids, s, &a);
   if (rc) return rc;
-  a.epoch = ++g->epoch;
-  hipError_t e = launch_megakernel(a, g->grid, s);
+  const uint32_t epoch = ++g->epoch;
+  hipError_t e = launch_megakernel(g->d_args, epoch, timeout_ticks(g), g->grid, s);
   if (e != hipSuccess) { --g->epoch; return hip_fail(e, "mega-kernel launch"); }
   g->last_stream = s;
   return MPK_OK;
@@ -505,12 +544,11 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
   KArgs a;
   int rc = step_args(g, w, token_ids, kv, seq_lens, logits, next_ids, s, &a);
   if (rc) return rc;
-  a.epoch = g->epoch;
   g->last_stream = s;
   if (!use_hipgraph) {
     for (auto& op : g->ops) {
       if (!op.second) continue;
-      hipError_t e = launch_baseline_op(a, g->d_lists + op.first, op.second, s);
+      hipError_t e = launch_baseline_op(g->d_args, g->d_lists + op.first, op.second, s);
       if (e != hipSuccess) return hip_fail(e, "baseline launch");
     }
     return MPK_OK;
@@ -526,7 +564,7 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
     HIPCHK(hipStreamBeginCapture(g->cap_stream, hipStreamCaptureModeThreadLocal));
     for (auto& op : g->ops) {
       if (!op.second) continue;
-      hipError_t e = launch_baseline_op(a, g->d_lists + op.first, op.second, g->cap_stream);
+      hipError_t e = launch_baseline_op(g->d_args, g->d_lists + op.first, op.second, g->cap_stream);
       if (e != hipSuccess) {
         hipGraph_t dummy;
         (void)hipStreamEndCapture(g->cap_stream, &dummy);
@@ -571,6 +609,78 @@ int mpk_get_status(mpk_tgraph* g, mpk_status_word* out) {
   HIPCHK(hipMemcpy(&s, g->d_status, sizeof(s), hipMemcpyDeviceToHost));
   out->code = s.code; out->wg = s.wg; out->task = s.task; out->event = s.event; out->counter = s.counter;
   out->target = s.target;
+  return MPK_OK;
+}
+
+int mpk_set_trace(mpk_tgraph* g, int32_t enable) {
+  if (!g) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  if (g->host_only) return fail(MPK_ERR_INVALID_ARG, "graph was built host-only");
+  if (g->last_stream) HIPCHK(hipStreamSynchronize(g->last_stream));
+  HIPCHK(hipDeviceSynchronize());
+  if (g->d_trace) { HIPCHK(hipFree(g->d_trace)); g->d_trace = nullptr; }
+  g->base.trace = nullptr; g->base.trace_count = nullptr; g->base.trace_cap = 0;
+  if (enable) {
+    // a worker runs at most its AOT list plus every JIT task of a step
+    int32_t max_aot = 0, n_jit = 0;
+    for (int32_t w = 0; w < g->prm.W; ++w)
+      max_aot = std::max<int32_t>(max_aot, (int32_t)(g->g.aot_offsets[w + 1] - g->g.aot_offsets[w]));
+    for (int32_t i = 0; i < g->g.NT; ++i) n_jit += g->g.task_mode[i] == MPK_MODE_JIT;
+    g->trace_cap = max_aot + n_jit;
+    const int64_t rec_bytes = align256((int64_t)g->prm.W * g->trace_cap * (int64_t)sizeof(TraceRec));
+    HIPCHK(hipMalloc(&g->d_trace, rec_bytes + (int64_t)g->prm.W * 4));
+    HIPCHK(hipMemset(g->d_trace, 0, rec_bytes + (int64_t)g->prm.W * 4));
+    g->base.trace = (TraceRec*)g->d_trace;
+    g->base.trace_count = (uint32_t*)((char*)g->d_trace + rec_bytes);
+    g->base.trace_cap = g->trace_cap;
+  }
+  return MPK_OK;
+}
+
+int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32_t* count, double* ticks_per_us) {
+  if (!g || !count || (capacity > 0 && !out)) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  if (!g->d_trace) return fail(MPK_ERR_INVALID_ARG, "tracing is off");
+  if (g->last_stream) HIPCHK(hipStreamSynchronize(g->last_stream));
+  HIPCHK(hipDeviceSynchronize());
+  const int32_t W = g->prm.W;
+  std::vector<uint32_t> cnt(W);
+  HIPCHK(hipMemcpy(cnt.data(), g->base.trace_count, (size_t)W * 4, hipMemcpyDeviceToHost));
+  std::vector<TraceRec> recs((size_t)W * g->trace_cap);
+  HIPCHK(hipMemcpy(recs.data(), g->base.trace, recs.size() * sizeof(TraceRec), hipMemcpyDeviceToHost));
+  int32_t n = 0;
+  for (int32_t w = 0; w < W; ++w)
+    for (uint32_t k = 0; k < std::min<uint32_t>(cnt[w], (uint32_t)g->trace_cap); ++k) {
+      if (n < capacity) {
+        const TraceRec& r = recs[(size_t)w * g->trace_cap + k];
+        out[n] = mpk_trace_record{r.task, r.worker, r.t_wait, r.t_start, r.t_end};
+      }
+      ++n;
+    }
+  *count = std::min(n, capacity);
+  if (ticks_per_us) *ticks_per_us = g->wall_khz / 1000.0;
+  return n > capacity ? fail(MPK_ERR_INVALID_ARG, "capacity too small") : MPK_OK;
+}
+
+int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, uint64_t* ticks,
+                   double* ticks_per_us) {
+  if (!g || !tasks || !ticks || n < 1 || reps < 1) return fail(MPK_ERR_INVALID_ARG, "bad argument");
+  if (g->host_only || !g->args_valid) return fail(MPK_ERR_INVALID_ARG, "run mpk_decode_step on this graph first");
+  for (int32_t i = 0; i < n; ++i)
+    if (tasks[i] < 0 || tasks[i] >= g->g.NT) return fail(MPK_ERR_INVALID_ARG, "task index out of range");
+  HIPCHK(hipDeviceSynchronize());
+  void* buf = nullptr;
+  HIPCHK(hipMalloc(&buf, (size_t)n * 12));
+  int32_t* d_list = (int32_t*)buf;
+  unsigned long long* d_out = (unsigned long long*)((char*)buf + (size_t)n * 4);
+  (void)d_list;
+  hipError_t e = hipMemset(d_out, 0, (size_t)n * 8);
+  for (int32_t i = 0; i < n && e == hipSuccess; ++i)
+    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) e = launch_time_task(g->d_args, tasks[i], d_out + i, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(ticks, d_out, (size_t)n * 8, hipMemcpyDeviceToHost);
+  for (int32_t i = 0; i < n && e == hipSuccess; ++i) ticks[i] /= (uint64_t)reps;
+  (void)hipFree(buf);
+  if (e != hipSuccess) return hip_fail(e, "mpk_time_tasks");
+  if (ticks_per_us) *ticks_per_us = g->wall_khz / 1000.0;
   return MPK_OK;
 }
 

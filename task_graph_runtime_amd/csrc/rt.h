@@ -40,6 +40,12 @@ struct PMax {
 enum { LAYER_PTRS = 11 };
 enum { W_IN_NORM = 0, W_Q, W_K, W_V, W_Q_NORM, W_K_NORM, W_O, W_POST_NORM, W_GATE, W_UP, W_DOWN };
 
+// One trace record (layout of mpk_trace_record).
+struct TraceRec {
+  int32_t task, worker;
+  uint64_t t_wait, t_start, t_end;
+};
+
 // Status word written by the kernel (layout of mpk_status_word).
 struct StatusWord {
   int32_t code, wg, task, event;
@@ -51,47 +57,71 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBatch = 16;
 constexpr int kMaxHidden = 8192;
 
+// Device pointers of the argument block are typed as global-address-space
+// pointers in device code (same 64-bit layout as the host's plain pointers),
+// so that every access through them is a global -- not a flat -- memory
+// instruction: flat loads also count against the LDS wait counter.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MPK_GLOBAL __attribute__((address_space(1)))
+#else
+#define MPK_GLOBAL
+#endif
+
+// Kernel arguments.  One copy lives in device memory per graph (refreshed
+// only when a caller pointer changes); the kernels receive its address, the
+// step's epoch and the watchdog limit.
 struct KArgs {
   // graph
-  const DevTask* tasks;
-  const DevEvent* events;
-  const uint32_t* aot_off;
-  const uint32_t* aot_tasks;
-  uint32_t* ev_cnt;                 // monotonic event counters (target counts * epoch)
-  unsigned long long* sched_ring;   // [n_sched][sched_cap] (seq << 32 | event)
-  uint32_t* sched_tail;             // [n_sched] producer reservation counters
-  unsigned long long* jit_ring;     // [n_workers][jit_cap] (seq << 32 | task)
-  uint32_t* state;                  // persistent runtime state, see megakernel.hip
+  MPK_GLOBAL const DevTask* tasks;
+  MPK_GLOBAL const DevEvent* events;
+  MPK_GLOBAL const uint32_t* aot_off;
+  MPK_GLOBAL const uint32_t* aot_tasks;
+  MPK_GLOBAL uint32_t* ev_cnt;                 // monotonic event counters (target counts * epoch)
+  MPK_GLOBAL unsigned long long* sched_ring;   // [n_sched][sched_cap] (seq << 32 | event)
+  MPK_GLOBAL uint32_t* sched_tail;             // [n_sched] producer reservation counters
+  MPK_GLOBAL unsigned long long* jit_ring;     // [n_workers][jit_cap] (seq << 32 | task)
+  MPK_GLOBAL uint32_t* state;                  // persistent runtime state, see megakernel.hip
   uint32_t sched_cap, jit_cap;
   int32_t n_workers, n_sched, n_sched_wgs;
   int32_t root_event, end_event;
-  uint32_t epoch;
-  uint64_t timeout_ticks;
-  StatusWord* status;
+  MPK_GLOBAL StatusWord* status;
+  MPK_GLOBAL TraceRec* trace;                  // null: tracing off; else [n_workers][trace_cap]
+  MPK_GLOBAL uint32_t* trace_count;            // [n_workers] records written in the last step
+  int32_t trace_cap;
   // model
   int32_t L, H, hq, hkv, d, F, V, G, Sg, B, P, S_attn, T_lm, qk_norm, max_seq, max_pages, n_pages;
   float eps, theta;
+  MPK_GLOBAL const double* inv_freq;           // [head_dim / 2]: theta^(-2i/head_dim), fp64
   // weights (bf16 bits)
-  const uint16_t* const* wl;        // device array [L * LAYER_PTRS]
-  const uint16_t* embed;
-  const uint16_t* lm_head;
-  const uint16_t* final_norm;
+  MPK_GLOBAL const uint16_t* MPK_GLOBAL const* wl;   // device array [L * LAYER_PTRS]
+  MPK_GLOBAL const uint16_t* embed;
+  MPK_GLOBAL const uint16_t* lm_head;
+  MPK_GLOBAL const uint16_t* final_norm;
   // KV cache
-  uint16_t* k_pool;
-  uint16_t* v_pool;
-  const int32_t* page_table;
+  MPK_GLOBAL uint16_t* k_pool;
+  MPK_GLOBAL uint16_t* v_pool;
+  MPK_GLOBAL const int32_t* page_table;
   // io
-  const int32_t* token_ids;
-  const int32_t* seq_lens;
-  float* logits;
-  int32_t* next_ids;
+  MPK_GLOBAL const int32_t* token_ids;
+  MPK_GLOBAL const int32_t* seq_lens;
+  MPK_GLOBAL float* logits;
+  MPK_GLOBAL int32_t* next_ids;
   // activations; per-layer tensors are [L][...] with the strides below (elements)
   // (all fp32: only the weights and the KV cache, the caller's formats, are bf16)
-  float* e;
-  float* hf;
-  PMax* pmax;
-  float* r;  float* h;  float* qkv;  float* q;  float* part;  float* attn;
-  float* o;  float* s;  float* h2;  float* a;  float* dn;
+  MPK_GLOBAL float* e;
+  MPK_GLOBAL float* hf;
+  MPK_GLOBAL PMax* pmax;
+  MPK_GLOBAL float* r;
+  MPK_GLOBAL float* h;
+  MPK_GLOBAL float* qkv;
+  MPK_GLOBAL float* q;
+  MPK_GLOBAL float* part;
+  MPK_GLOBAL float* attn;
+  MPK_GLOBAL float* o;
+  MPK_GLOBAL float* s;
+  MPK_GLOBAL float* h2;
+  MPK_GLOBAL float* a;
+  MPK_GLOBAL float* dn;
   int64_t st_bh, st_qkv, st_q, st_part, st_a;
 };
 

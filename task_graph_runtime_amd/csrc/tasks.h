@@ -6,8 +6,8 @@
 // precision contract"): projection tiles read bf16 weights and accumulate in
 // fp32.  Activations passed between tasks stay fp32 (the page's bf16 task
 // outputs, compounded over 28-64 layers, drift past the 2e-2 logit bound
-// against the fp32 forward); only weights and the KV cache are bf16;
-// attention is paged decode attention of one new query per request against
+// against the fp32 forward); only weights and the KV cache are bf16.
+// Attention is paged decode attention of one new query per request against
 // its KV pages.  The decoder layer around them is the Qwen3 layer (RMSNorm,
 // per-head q/k RMSNorm, rotate-half RoPE, GQA, SwiGLU).
 #pragma once
@@ -16,11 +16,15 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "mpk.h"
 #include "rt.h"
 
 namespace mpk {
+
+template <typename T>
+using gptr = MPK_GLOBAL T*;
 
 // ------------------------------------------------------------------ helpers
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
@@ -35,9 +39,20 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// Vector load of type T through a global pointer of element type P.
+template <typename T, typename P>
+__device__ __forceinline__ T ldg(MPK_GLOBAL const P* p) {
+  return *reinterpret_cast<MPK_GLOBAL const T*>(p);
+}
 
-__device__ __forceinline__ float4 ldf4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+// Element i of p[0..n) or `dflt` when i >= n (n >= 1).  The load itself is
+// unconditional (from a clamped index): a load under a branch makes the
+// compiler wait for it before the join, serialising round trips.
+template <typename T>
+__device__ __forceinline__ T ld_or(MPK_GLOBAL const T* p, int64_t i, int64_t n, T dflt) {
+  const T v = p[i < n ? i : n - 1];
+  return i < n ? v : dflt;
+}
 
 // 8 bf16 weights (one 16-byte load) times 8 fp32 activations, fp32 accumulate.
 __device__ __forceinline__ float dot8(uint4 w, float4 x0, float4 x1, float acc) {
@@ -67,15 +82,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += __shfl_xor(v, 32);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x140>(v));
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
 
 // Sum over the workgroup; `red` is kWaves floats of LDS.  All threads call it.
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -93,8 +99,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // First in-kernel error wins; later ones are dropped.
 __device__ __forceinline__ void report(const KArgs& a, int32_t code, int32_t task, int32_t event, uint32_t counter,
                                        uint32_t target) {
-  int32_t prev = atomicCAS(&a.status->code, 0, code);
-  if (prev == 0) {
+  int32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(&a.status->code, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
     a.status->wg = (int32_t)blockIdx.x;
     a.status->task = task;
     a.status->event = event;
@@ -104,45 +111,69 @@ __device__ __forceinline__ void report(const KArgs& a, int32_t code, int32_t tas
   }
 }
 
+// LDS layout of a workgroup (one per compute unit).
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kLdsX = 0;                       // staged activation vector (fp32), batch 1
+constexpr int kLdsXFloats = 26624;             // 104 KB: the widest K of the supported shapes
+constexpr int kLdsAcc = kLdsXFloats * 4;       // projection accumulators
+constexpr int kLdsAccFloats = 8192;            // 32 KB
+constexpr int kLdsMisc = kLdsAcc + kLdsAccFloats * 4;   // 24 KB: page ids, control, reduction scratch
+constexpr int kLdsCtl = kLdsMisc + 16384;      // runtime control words
+constexpr int kLdsRed = kLdsBytes - 256;       // 64 words of reduction scratch
+constexpr int kMaxSplitPages = 4096;           // page ids staged per attention split
+
+// The workgroup's LDS, shared by the runtime loop and every task body.
+__shared__ __attribute__((aligned(16))) char g_lds[kLdsBytes];
+
 // ------------------------------------------------------------------ embedding
-__device__ void embed_task(const KArgs& a) {
+__device__ __forceinline__ void embed_task(const KArgs& a) {
   for (int b = 0; b < a.B; ++b) {
     int id = a.token_ids[b];
     if (id < 0 || id >= a.V) {
       if (threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)id, (uint32_t)a.V);
       id = 0;
     }
-    const uint16_t* row = a.embed + (int64_t)id * a.H;
+    gptr<const uint16_t> row = a.embed + (int64_t)id * a.H;
     for (int i = threadIdx.x; i < a.H; i += kThreads) a.e[(int64_t)b * a.H + i] = bf2f(row[i]);
   }
 }
 
 // ------------------------------------------------------------------ residual add + RMSNorm
 // res = x + y (y optional), stored when `res` is given; out = RMSNorm(res) * gamma.
-__device__ void norm_task(const KArgs& a, const float* x, const float* y, float* res, const uint16_t* gamma,
-                          float* out, float* red) {
+// All loads of a row are issued before any store.
+__device__ __forceinline__ void norm_task(const KArgs& a, gptr<const float> __restrict__ x,
+                                          gptr<const float> __restrict__ y, gptr<float> __restrict__ res,
+                                          gptr<const uint16_t> __restrict__ gamma, gptr<float> __restrict__ out,
+                                          float* red) {
+  constexpr int J = kMaxHidden / kThreads;
   const int H = a.H;
   for (int b = 0; b < a.B; ++b) {
-    float v[kMaxHidden / kThreads];
-    float ss = 0.f;
+    float v[J], gm[J];
 #pragma unroll
-    for (int j = 0; j < kMaxHidden / kThreads; ++j) {
-      int i = threadIdx.x + j * kThreads;
-      v[j] = 0.f;
-      if (i < H) {
-        float t = x[(int64_t)b * H + i];
-        if (y) t += y[(int64_t)b * H + i];
-        v[j] = t;
-        ss = fmaf(t, t, ss);
-        if (res) res[(int64_t)b * H + i] = t;
+    for (int j = 0; j < J; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      v[j] = ld_or(x + (int64_t)b * H, i, H, 0.f);
+      gm[j] = bf2f(ld_or(gamma, i, H, (uint16_t)0));
+    }
+    if (y) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        v[j] += ld_or(y + (int64_t)b * H, i, H, 0.f);
       }
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) ss = fmaf(v[j], v[j], ss);
     ss = block_sum(ss, red);
     const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
 #pragma unroll
-    for (int j = 0; j < kMaxHidden / kThreads; ++j) {
-      int i = threadIdx.x + j * kThreads;
-      if (i < H) out[(int64_t)b * H + i] = v[j] * inv * bf2f(gamma[i]);
+    for (int j = 0; j < J; ++j) {
+      const int i = threadIdx.x + j * kThreads;
+      if (i < H) {
+        if (res) res[(int64_t)b * H + i] = v[j];
+        out[(int64_t)b * H + i] = v[j] * inv * gm[j];
+      }
     }
   }
 }
@@ -150,10 +181,10 @@ __device__ void norm_task(const KArgs& a, const float* x, const float* y, float*
 // ------------------------------------------------------------------ projection tiles
 // Row r of the tile's weight rows (output columns [lo, hi); gate/up tiles
 // interleave gate row and up row of each column).
-__device__ __forceinline__ const uint16_t* gemv_row(const KArgs& a, int type, int l, int lo, int r) {
+__device__ __forceinline__ gptr<const uint16_t> gemv_row(const KArgs& a, int type, int l, int lo, int r) {
   switch (type) {
     case MPK_TASK_QKV: {
-      const uint16_t* const* W = a.wl + (int64_t)l * LAYER_PTRS;
+      gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)l * LAYER_PTRS;
       const int col = lo + r, g = col / a.Sg, Gd = a.G * a.d;
       int off = col - g * a.Sg;
       if (off < Gd) return W[W_Q] + (int64_t)(g * Gd + off) * a.H;
@@ -173,97 +204,50 @@ __device__ __forceinline__ const uint16_t* gemv_row(const KArgs& a, int type, in
   }
 }
 
-// y[b, n] = sum_k x[b, k] W[n, k] for the tile's columns.  The tile's weight
-// rows are cut into 1 KB segments (64 lanes x 8 bf16, 16-byte loads); each
-// wavefront streams a contiguous run of segments, keeps one fp32 partial per
-// batch row, reduces it across the wavefront when the row changes and adds it
-// into an LDS accumulator.  BT = 1 (batch 1) or kMaxBatch (batch 2..16).
-template <int BT>
-__device__ void gemv_task(const KArgs& a, const DevTask& t, float* acc, float* red) {
-  const int type = t.type, l = t.layer, lo = t.a0, hi = t.a1;
-  const int B = a.B;
-  int K, rpc = 1;
-  const float* x;
-  switch (type) {
-    case MPK_TASK_QKV: K = a.H; x = a.h + (int64_t)l * a.st_bh; break;
-    case MPK_TASK_OPROJ: K = a.hq * a.d; x = a.attn + (int64_t)l * a.st_q; break;
-    case MPK_TASK_GATEUP: K = a.H; x = a.h2 + (int64_t)l * a.st_bh; rpc = 2; break;
-    case MPK_TASK_DOWN: K = a.F; x = a.a + (int64_t)l * a.st_a; break;
-    default: K = a.H; x = a.hf; break;
+struct GemvOp {
+  int K, rpc;
+  gptr<const float> x;
+};
+__device__ __forceinline__ GemvOp gemv_op(const KArgs& a, const DevTask& t) {
+  const int l = t.layer;
+  switch (t.type) {
+    case MPK_TASK_QKV: return {a.H, 1, a.h + (int64_t)l * a.st_bh};
+    case MPK_TASK_OPROJ: return {a.hq * a.d, 1, a.attn + (int64_t)l * a.st_q};
+    case MPK_TASK_GATEUP: return {a.H, 2, a.h2 + (int64_t)l * a.st_bh};
+    case MPK_TASK_DOWN: return {a.F, 1, a.a + (int64_t)l * a.st_a};
+    default: return {a.H, 1, a.hf};
   }
-  const int ncol = hi - lo, nrows = ncol * rpc;
-  for (int i = threadIdx.x; i < nrows * B; i += kThreads) acc[i] = 0.f;
-  __syncthreads();
+}
 
-  const int nseg = (K + 511) >> 9;
-  const int S = nrows * nseg;
+// Position in a tile's weight rows, advanced one 1 KB segment (64 lanes x 8
+// bf16) at a time without a division per segment.
+struct SegWalk {
+  gptr<const uint16_t> row;
+  int r, ks;
+};
+__device__ __forceinline__ SegWalk seg_start(const KArgs& a, const DevTask& t, int nseg, int s) {
+  SegWalk w;
+  w.r = s / nseg;
+  w.ks = s - w.r * nseg;
+  w.row = gemv_row(a, t.type, t.layer, t.a0, w.r);
+  return w;
+}
+__device__ __forceinline__ void seg_next(const KArgs& a, const DevTask& t, int nseg, SegWalk& w) {
+  if (++w.ks == nseg) {
+    w.ks = 0;
+    ++w.r;
+    w.row = gemv_row(a, t.type, t.layer, t.a0, w.r);
+  }
+}
+
+// Epilogue of a projection tile from the LDS accumulators acc[row][B].
+__device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, const float* acc, float* red) {
+  const int type = t.type, l = t.layer, lo = t.a0, ncol = t.a1 - t.a0, B = a.B;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s_beg = (int)((int64_t)S * w / kWaves), s_end = (int)((int64_t)S * (w + 1) / kWaves);
-  constexpr int U = (BT == 1) ? 8 : 4;
-  float av[BT];
-#pragma unroll
-  for (int b = 0; b < BT; ++b) av[b] = 0.f;
-  int cur = -1;
-  auto flush = [&]() {
-#pragma unroll
-    for (int b = 0; b < BT; ++b) {
-      if (b < B) {
-        float v = wave_sum(av[b]);
-        if (lane == 0) atomicAdd(&acc[cur * B + b], v);
-      }
-      av[b] = 0.f;
-    }
-  };
-  for (int s0 = s_beg; s0 < s_end; s0 += U) {
-    uint4 wv[U];
-    float4 xa[U], xb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u;
-      wv[u] = make_uint4(0, 0, 0, 0);
-      xa[u] = xb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s < s_end) {
-        const int r = s / nseg;
-        const int k = (s - r * nseg) * 512 + lane * 8;
-        if (k < K) {
-          wv[u] = ld16(gemv_row(a, type, l, lo, r) + k);
-          if (BT == 1) { xa[u] = ldf4(x + k); xb[u] = ldf4(x + k + 4); }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u;
-      if (s < s_end) {
-        const int r = s / nseg;
-        const int k = (s - r * nseg) * 512 + lane * 8;
-        if (r != cur) {
-          if (cur >= 0) flush();
-          cur = r;
-        }
-        if (k < K) {
-          if (BT == 1) {
-            av[0] = dot8(wv[u], xa[u], xb[u], av[0]);
-          } else {
-#pragma unroll
-            for (int b = 0; b < BT; ++b)
-              if (b < B) {
-                const float* xr = x + (int64_t)b * K + k;
-                av[b] = dot8(wv[u], ldf4(xr), ldf4(xr + 4), av[b]);
-              }
-          }
-        }
-      }
-    }
-  }
-  if (cur >= 0) flush();
-  __syncthreads();
-
-  // epilogue
   switch (type) {
     case MPK_TASK_QKV: {
       const int ld = a.hkv * a.Sg;
-      float* out = a.qkv + (int64_t)l * a.st_qkv;
+      gptr<float> out = a.qkv + (int64_t)l * a.st_qkv;
       for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         out[(int64_t)b * ld + lo + c] = acc[c * B + b];
@@ -272,15 +256,15 @@ __device__ void gemv_task(const KArgs& a, const DevTask& t, float* acc, float* r
     }
     case MPK_TASK_OPROJ:
     case MPK_TASK_DOWN: {
-      float* out = (type == MPK_TASK_OPROJ ? a.o : a.dn) + (int64_t)l * a.st_bh;
+      gptr<float> out = (type == MPK_TASK_OPROJ ? a.o : a.dn) + (int64_t)l * a.st_bh;
       for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
       }
       break;
     }
-    case MPK_TASK_GATEUP: {
-      float* out = a.a + (int64_t)l * a.st_a;
+    case MPK_TASK_GATEUP: {  // SwiGLU: silu(gate) * up
+      gptr<float> out = a.a + (int64_t)l * a.st_a;
       for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         float g = acc[(2 * c) * B + b], u = acc[(2 * c + 1) * B + b];
@@ -321,32 +305,194 @@ __device__ void gemv_task(const KArgs& a, const DevTask& t, float* acc, float* r
   }
 }
 
+// Batch-1 projection tile: y[n] = sum_k x[k] W[n, k] for the tile's columns.
+// The tile's weight rows are cut into 1 KB segments (64 lanes x 8 bf16, one
+// 16-byte load per lane); wavefront w streams the contiguous run of segments
+// [S w / 8, S (w+1) / 8) through two register buffers of D segments (the
+// loads of one buffer are in flight while the other is consumed), keeps one
+// fp32 partial for the current row, and on a row change reduces it across
+// the wavefront (DPP + lane swaps) into the row's LDS accumulator.  The first
+// buffer's loads are issued before x is staged in LDS (fp32), so both round
+// trips overlap.  Loads are issued unconditionally -- past the end they
+// repeat the last segment -- so the wait counts stay static.
+template <int D>
+__device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, char* lds) {
+  const GemvOp op = gemv_op(a, t);
+  const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc;
+  float* xs = reinterpret_cast<float*>(lds + kLdsX);
+  float* acc = reinterpret_cast<float*>(lds + kLdsAcc);
+  float* red = reinterpret_cast<float*>(lds + kLdsRed);
+  const int nseg = (K + 511) >> 9, S = nrows * nseg;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
+  const int kl = lane * 8;
+  SegWalk ld = seg_start(a, t, nseg, s_beg < S ? s_beg : S - 1);
+  int issued = 0;
+  uint4 b0[D], b1[D];
+  auto issue = [&](uint4 (&b)[D]) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int k = min(ld.ks * 512 + kl, K - 8);
+      b[u] = ldg<uint4>(ld.row + k);
+      if (issued + 1 < total) seg_next(a, t, nseg, ld);
+      ++issued;
+    }
+  };
+  if (total > 0) issue(b0);
+  for (int i = threadIdx.x; i < nrows; i += kThreads) acc[i] = 0.f;
+  {
+    // stage x: every load of the vector is issued before the LDS stores
+    constexpr int XU = (kLdsXFloats / 4 + kThreads - 1) / kThreads;
+    float4 xv[XU];
+    const int n4 = K >> 2;
+    gptr<const float4> x4 = reinterpret_cast<gptr<const float4>>(op.x);
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int i = (int)threadIdx.x + u * kThreads;
+      if (u * kThreads < n4) xv[u] = x4[min(i, n4 - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int i = (int)threadIdx.x + u * kThreads;
+      if (u * kThreads < n4 && i < n4) reinterpret_cast<float4*>(xs)[i] = xv[u];
+    }
+  }
+  __syncthreads();
+  if (total > 0) {
+    int cr = s_beg / nseg, cks = s_beg - cr * nseg;  // consumer position
+    int done = 0, cur = cr;
+    float accv = 0.f;
+    auto consume = [&](const uint4 (&b)[D]) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        if (done < total) {
+          if (cr != cur) {
+            const float v = wave_sum(accv);
+            if (lane == 0) atomicAdd(&acc[cur], v);
+            accv = 0.f;
+            cur = cr;
+          }
+          const int k = cks * 512 + kl;
+          if (k < K) {
+            const float4* xp = reinterpret_cast<const float4*>(xs + k);
+            accv = dot8(b[u], xp[0], xp[1], accv);
+          }
+          if (++cks == nseg) { cks = 0; ++cr; }
+          ++done;
+        }
+      }
+    };
+    while (true) {
+      issue(b1);
+      consume(b0);
+      if (done >= total) break;
+      issue(b0);
+      consume(b1);
+      if (done >= total) break;
+    }
+    const float v = wave_sum(accv);
+    if (lane == 0) atomicAdd(&acc[cur], v);
+  }
+  __syncthreads();
+  gemv_epilogue(a, t, acc, red);
+}
+
+// Batch 2..16 projection tile (VALU): same segment walk, x read from global
+// memory (L2-resident), one fp32 partial per request.
+__device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, char* lds) {
+  constexpr int U = 4;
+  const GemvOp op = gemv_op(a, t);
+  const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc, B = a.B;
+  float* acc = reinterpret_cast<float*>(lds + kLdsAcc);
+  float* red = reinterpret_cast<float*>(lds + kLdsRed);
+  for (int i = threadIdx.x; i < nrows * B; i += kThreads) acc[i] = 0.f;
+  __syncthreads();
+  const int nseg = (K + 511) >> 9, S = nrows * nseg;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
+  if (total > 0) {
+    SegWalk ld = seg_start(a, t, nseg, s_beg);
+    int cur = ld.r, done = 0;
+    float av[kMaxBatch];
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) av[b] = 0.f;
+    while (done < total) {
+      uint4 wv[U];
+      int rr[U], kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        rr[u] = ld.r;
+        kk[u] = ld.ks * 512 + lane * 8;
+        wv[u] = ldg<uint4>(ld.row + min(kk[u], K - 8));
+        if (done + u + 1 < total) seg_next(a, t, nseg, ld);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (done < total) {
+          if (rr[u] != cur) {
+#pragma unroll
+            for (int b = 0; b < kMaxBatch; ++b) {
+              if (b < B) {
+                const float v = wave_sum(av[b]);
+                if (lane == 0) atomicAdd(&acc[cur * B + b], v);
+              }
+              av[b] = 0.f;
+            }
+            cur = rr[u];
+          }
+          if (kk[u] < K) {
+#pragma unroll
+            for (int b = 0; b < kMaxBatch; ++b)
+              if (b < B) {
+                gptr<const float> xr = op.x + (int64_t)b * K + kk[u];
+                av[b] = dot8(wv[u], ldg<float4>(xr), ldg<float4>(xr + 4), av[b]);
+              }
+          }
+          ++done;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b)
+      if (b < B) {
+        const float v = wave_sum(av[b]);
+        if (lane == 0) atomicAdd(&acc[cur * B + b], v);
+      }
+  }
+  __syncthreads();
+  gemv_epilogue(a, t, acc, red);
+}
+
 // ------------------------------------------------------------------ q/k RMSNorm + RoPE + KV append
 // Task (b, g): the G query heads and the key head of kv group g get per-head
 // RMSNorm (qk_norm) and rotate-half RoPE at position L_b; q goes to the q
-// buffer (fp32), k and v to cache slot L_b of request b.
-__device__ void rope_task(const KArgs& a, const DevTask& t) {
+// buffer (fp32), k and v to cache slot L_b of request b (bf16).
+__device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t) {
   const int b = t.a0, g = t.a1, l = t.layer, d = a.d, half = d >> 1, G = a.G;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int Lb = a.seq_lens[b];
   bool ok = Lb >= 0 && Lb < a.max_seq && Lb / a.P < a.max_pages;
-  int pid = ok ? a.page_table[(int64_t)b * a.max_pages + Lb / a.P] : 0;
+  const int pid = ok ? a.page_table[(int64_t)b * a.max_pages + Lb / a.P] : 0;
   if (!(pid >= 0 && pid < a.n_pages)) ok = false;
   if (!ok && threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, (uint32_t)pid);
   const int64_t slot = ok ? ((((int64_t)l * a.n_pages + pid) * a.hkv + g) * a.P + (Lb % a.P)) * d : 0;
-  const float* src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
-  const uint16_t* const* W = a.wl + (int64_t)l * LAYER_PTRS;
+  gptr<const float> src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
+  gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)l * LAYER_PTRS;
   const bool act = lane < half;
-  // angle of pair `lane`: L_b * theta^(-2*lane/d), in double
+  // angle of pair `lane`: L_b * theta^(-2*lane/d); the product and its
+  // reduction to [-pi, pi] are done in fp64 (inverse frequencies are computed
+  // on the host in fp64), cos/sin of the reduced angle in fp32
   float cs = 1.f, sn = 0.f;
   if (act) {
-    double ang = (double)(ok ? Lb : 0) * pow((double)a.theta, -2.0 * (double)lane / (double)d);
-    cs = (float)cos(ang);
-    sn = (float)sin(ang);
+    const double ang = (double)(ok ? Lb : 0) * a.inv_freq[lane];
+    const double two_pi = 6.283185307179586476925286766559;
+    const float red_ang = (float)(ang - two_pi * rint(ang / two_pi));
+    sincosf(red_ang, &sn, &cs);
   }
   for (int hh = w; hh < G + 2; hh += kWaves) {
-    float x0 = act ? src[hh * d + lane] : 0.f;
-    float x1 = act ? src[hh * d + lane + half] : 0.f;
+    const float s0 = src[hh * d + min(lane, half - 1)], s1 = src[hh * d + min(lane, half - 1) + half];
+    float x0 = act ? s0 : 0.f;
+    float x1 = act ? s1 : 0.f;
     if (hh == G + 1) {  // value head: rounded into the bf16 cache
       if (act && ok) {
         a.v_pool[slot + lane] = f2bf(x0);
@@ -355,19 +501,19 @@ __device__ void rope_task(const KArgs& a, const DevTask& t) {
       continue;
     }
     if (a.qk_norm) {
-      float ss = wave_sum(x0 * x0 + x1 * x1);
-      float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
-      const uint16_t* gam = W[hh < G ? W_Q_NORM : W_K_NORM];
-      if (act) {
-        x0 = x0 * inv * bf2f(gam[lane]);
-        x1 = x1 * inv * bf2f(gam[lane + half]);
-      }
+      gptr<const uint16_t> gam = W[hh < G ? W_Q_NORM : W_K_NORM];
+      const int lc = min(lane, half - 1);
+      const float g0 = act ? bf2f(gam[lc]) : 0.f, g1 = act ? bf2f(gam[lc + half]) : 0.f;
+      const float ss = wave_sum(x0 * x0 + x1 * x1);
+      const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
+      x0 = x0 * inv * g0;
+      x1 = x1 * inv * g1;
     }
-    float y0 = x0 * cs - x1 * sn;
-    float y1 = x1 * cs + x0 * sn;
+    const float y0 = x0 * cs - x1 * sn;
+    const float y1 = x1 * cs + x0 * sn;
     if (act) {
       if (hh < G) {
-        float* qo = a.q + (int64_t)l * a.st_q + (int64_t)b * a.hq * d + (int64_t)(g * G + hh) * d;
+        gptr<float> qo = a.q + (int64_t)l * a.st_q + (int64_t)b * a.hq * d + (int64_t)(g * G + hh) * d;
         qo[lane] = y0;
         qo[lane + half] = y1;
       } else if (ok) {
@@ -380,17 +526,24 @@ __device__ void rope_task(const KArgs& a, const DevTask& t) {
 
 // ------------------------------------------------------------------ paged attention, one split
 // Task (b, g, s): pages [floor(s n_b / S), floor((s+1) n_b / S)) of request b,
-// n_b = ceil((L_b + 1) / P); all G query heads of kv group g.  Each 16-lane
-// row of a wavefront owns every 32nd token of the split (lane i of the row
-// holds dims [8i, 8i+8) of d=128, or 4 dims of d=64), keeps an online-softmax
-// state (max m, sum l, o[d]) per head, and the 32 row states are merged with
-// the log-sum-exp rule at the end.  Output: per head (m, l, o[d]) in fp32.
-template <int D>
-__device__ void attn_task(const KArgs& a, const DevTask& t, float* lds) {
-  constexpr int DPL = D / 16;  // dims per lane
-  constexpr int GM = 8;        // max query heads per kv head
+// n_b = ceil((L_b + 1) / P); all G query heads of kv group g.  Each row of R
+// lanes of a wavefront owns every (8 * 64 / R)-th token of the split (lane i
+// of the row holds dims [i D/R, (i+1) D/R): one coalesced key row and value
+// row per token), keeps an online-softmax state (max m, sum l, o[d]) per
+// head, and the row states are merged with the log-sum-exp rule at the end.
+// R = 16 when G <= 4, 32 for G <= 8 (64 registers of q and o either way).
+// Key/value rows are double-buffered in registers (the next token's loads
+// are in flight while the current one is processed; loads past the split's
+// end repeat its last token so the wait counts stay static); the split's
+// page ids are staged in LDS first.  Output: per head (m, l, o[d]) in fp32.
+template <int D, int R, int GM>
+__device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char* lds) {
+  constexpr int DPL = D / R;            // dims per lane
+  constexpr int RPW = 64 / R;           // rows per wavefront
+  constexpr int TPI = kWaves * RPW;     // tokens per iteration of the workgroup
+  using KV = typename std::conditional<DPL == 8, uint4, typename std::conditional<DPL == 4, uint2, uint32_t>::type>::type;
   const int b = t.a0, g = t.a1, s = t.a2, l = t.layer, G = a.G, P = a.P;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, row = lane >> 4, lr = lane & 15;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, row = lane / R, lr = lane % R;
   const int Lb = a.seq_lens[b];
   const bool ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
   if (!ok && threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, 0u);
@@ -399,39 +552,48 @@ __device__ void attn_task(const KArgs& a, const DevTask& t, float* lds) {
   const int j0 = (int)((int64_t)s * nb / a.S_attn), j1 = (int)((int64_t)(s + 1) * nb / a.S_attn);
   const int t0 = j0 * P, t1 = min(j1 * P, ntok);
 
+  int* pids = reinterpret_cast<int*>(lds + kLdsMisc);   // page ids of pages j0..j1-1
+  for (int j = j0 + (int)threadIdx.x; j < j1; j += kThreads) {
+    int pid = a.page_table[(int64_t)b * a.max_pages + j];
+    if (pid < 0 || pid >= a.n_pages) {
+      report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)pid, (uint32_t)a.n_pages);
+      pid = -1;
+    }
+    pids[j - j0] = pid;
+  }
   const float scale = 1.0f / sqrtf((float)D);
   float qv[GM][DPL], ov[GM][DPL], m[GM], lsum[GM];
-  const float* qsrc = a.q + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
+  gptr<const float> qsrc = a.q + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
     m[h] = -INFINITY;
     lsum[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
-      qv[h][i] = h < G ? qsrc[h * D + lr * DPL + i] * scale : 0.f;
+      const float qx = qsrc[min(h, G - 1) * D + lr * DPL + i];
+      qv[h][i] = h < G ? qx * scale : 0.f;
       ov[h][i] = 0.f;
     }
   }
-  const int64_t head_base = ((int64_t)l * a.n_pages * a.hkv + g) * P * D;  // + pid * hkv * P * D
-  for (int tok = t0 + w * 4 + row; tok < t1; tok += 32) {
-    int pid = a.page_table[(int64_t)b * a.max_pages + tok / P];
-    if (pid < 0 || pid >= a.n_pages) {
-      report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)pid, (uint32_t)a.n_pages);
-      continue;
-    }
-    const int64_t off = head_base + (int64_t)pid * a.hkv * P * D + (int64_t)(tok % P) * D + lr * DPL;
+  __syncthreads();
+  gptr<const uint16_t> kbase = a.k_pool + ((int64_t)l * a.n_pages * a.hkv + g) * P * D + lr * DPL;
+  gptr<const uint16_t> vbase = a.v_pool + ((int64_t)l * a.n_pages * a.hkv + g) * P * D + lr * DPL;
+  const int64_t page_stride = (int64_t)a.hkv * P * D;
+  // offset of token `tok`, clamped into the split (a bad page reads page 0 and is not used)
+  auto offs = [&](int tok) -> int64_t {
+    tok = min(tok, t1 - 1);
+    const int pid = pids[tok / P - j0];
+    return (int64_t)(pid >= 0 ? pid : 0) * page_stride + (int64_t)(tok % P) * D;
+  };
+  auto good = [&](int tok) { return tok < t1 && pids[tok / P - j0] >= 0; };
+  auto process = [&](const KV& kc, const KV& vc) {
     float kf[DPL], vf[DPL];
-    if constexpr (DPL == 8) {
-      uint4 kk = ld16(a.k_pool + off), vv = ld16(a.v_pool + off);
-      kf[0] = bflo(kk.x); kf[1] = bfhi(kk.x); kf[2] = bflo(kk.y); kf[3] = bfhi(kk.y);
-      kf[4] = bflo(kk.z); kf[5] = bfhi(kk.z); kf[6] = bflo(kk.w); kf[7] = bfhi(kk.w);
-      vf[0] = bflo(vv.x); vf[1] = bfhi(vv.x); vf[2] = bflo(vv.y); vf[3] = bfhi(vv.y);
-      vf[4] = bflo(vv.z); vf[5] = bfhi(vv.z); vf[6] = bflo(vv.w); vf[7] = bfhi(vv.w);
-    } else {
-      uint2 kk = *reinterpret_cast<const uint2*>(a.k_pool + off);
-      uint2 vv = *reinterpret_cast<const uint2*>(a.v_pool + off);
-      kf[0] = bflo(kk.x); kf[1] = bfhi(kk.x); kf[2] = bflo(kk.y); kf[3] = bfhi(kk.y);
-      vf[0] = bflo(vv.x); vf[1] = bfhi(vv.x); vf[2] = bflo(vv.y); vf[3] = bfhi(vv.y);
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kc);
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vc);
+#pragma unroll
+    for (int i = 0; i < DPL / 2; ++i) {
+      kf[2 * i] = bflo(kw[i]); kf[2 * i + 1] = bfhi(kw[i]);
+      vf[2 * i] = bflo(vw[i]); vf[2 * i + 1] = bfhi(vw[i]);
     }
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
@@ -440,26 +602,47 @@ __device__ void attn_task(const KArgs& a, const DevTask& t, float* lds) {
 #pragma unroll
         for (int i = 0; i < DPL; ++i) p = fmaf(qv[h][i], kf[i], p);
         p = row_sum(p);
+        if (R == 32) p += __shfl_xor(p, 16);
         const float mn = fmaxf(m[h], p);
-        const float al = expf(m[h] - mn);
-        const float e = expf(p - mn);
+        const float al = __expf(m[h] - mn);
+        const float e = __expf(p - mn);
         lsum[h] = fmaf(lsum[h], al, e);
 #pragma unroll
         for (int i = 0; i < DPL; ++i) ov[h][i] = fmaf(ov[h][i], al, e * vf[i]);
         m[h] = mn;
       }
     }
+  };
+  if (t1 > t0) {
+    // `it` is the wavefront's first token of the iteration: uniform over the wavefront
+    const int base = t0 + w * RPW;
+    int tok = base + row;
+    KV k0, v0, k1, v1;
+    int64_t o = offs(tok);
+    k0 = ldg<KV>(kbase + o);
+    v0 = ldg<KV>(vbase + o);
+    for (int it = base; it < t1; it += 2 * TPI, tok += 2 * TPI) {
+      o = offs(tok + TPI);
+      k1 = ldg<KV>(kbase + o);
+      v1 = ldg<KV>(vbase + o);
+      if (good(tok)) process(k0, v0);
+      if (it + TPI >= t1) break;
+      o = offs(tok + 2 * TPI);
+      k0 = ldg<KV>(kbase + o);
+      v0 = ldg<KV>(vbase + o);
+      if (good(tok + TPI)) process(k1, v1);
+    }
   }
-  // merge the four row states of the wavefront (lanes lr, lr+16, lr+32, lr+48)
+  // merge the row states of the wavefront (lanes lr, lr+R, ...)
 #pragma unroll
-  for (int msk = 16; msk <= 32; msk <<= 1) {
+  for (int msk = R; msk <= 32; msk <<= 1) {
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       if (h < G) {
         const float m2 = __shfl_xor(m[h], msk), l2 = __shfl_xor(lsum[h], msk);
         const float mn = fmaxf(m[h], m2);
-        const float a1 = (m[h] == -INFINITY) ? 0.f : expf(m[h] - mn);
-        const float a2 = (m2 == -INFINITY) ? 0.f : expf(m2 - mn);
+        const float a1 = (m[h] == -INFINITY) ? 0.f : __expf(m[h] - mn);
+        const float a2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - mn);
         lsum[h] = lsum[h] * a1 + l2 * a2;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) {
@@ -471,7 +654,7 @@ __device__ void attn_task(const KArgs& a, const DevTask& t, float* lds) {
     }
   }
   // merge the wavefronts through LDS: per wave, per head: m, l, o[D]
-  float* st = lds;  // [kWaves][G][D + 2]
+  float* st = reinterpret_cast<float*>(lds);  // [kWaves][G][D + 2]
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
@@ -484,18 +667,20 @@ __device__ void attn_task(const KArgs& a, const DevTask& t, float* lds) {
     }
   }
   __syncthreads();
-  float* out = a.part + (int64_t)l * a.st_part +
-               (((int64_t)b * a.hkv + g) * a.S_attn + s) * (int64_t)(G * (D + 2));
+  gptr<float> out = a.part + (int64_t)l * a.st_part +
+                    (((int64_t)b * a.hkv + g) * a.S_attn + s) * (int64_t)(G * (D + 2));
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
     const int h = e / D, dd = e - h * D;
     float M = -INFINITY;
+#pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, st[(ww * G + h) * (D + 2)]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
+#pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
         const float* p = st + (ww * G + h) * (D + 2);
         if (p[0] != -INFINITY) {
-          const float f = expf(p[0] - M);
+          const float f = __expf(p[0] - M);
           L = fmaf(p[1], f, L);
           O = fmaf(p[2 + dd], f, O);
         }
@@ -509,61 +694,102 @@ __device__ void attn_task(const KArgs& a, const DevTask& t, float* lds) {
 
 // ------------------------------------------------------------------ split combine
 // Task (b, g): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}, M = max_s m_s.
-__device__ void combine_task(const KArgs& a, const DevTask& t) {
+// The S partial records are staged in LDS first (all loads in flight at once).
+__device__ __forceinline__ void combine_task(const KArgs& a, const DevTask& t, char* lds) {
   const int b = t.a0, g = t.a1, l = t.layer, G = a.G, D = a.d, S = a.S_attn;
-  const float* part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)(G * (D + 2));
-  float* out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
+  const int rec = G * (D + 2);
+  gptr<const float> part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)rec;
+  gptr<float> out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
+  float* st = reinterpret_cast<float*>(lds);
+  const int n = S * rec;
+  const bool staged = n <= kLdsXFloats;
+  if (staged) {
+    constexpr int U = 8;
+    for (int i0 = 0; i0 < n; i0 += U * kThreads) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_or(part, i0 + u * kThreads + (int)threadIdx.x, n, 0.f);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kThreads + (int)threadIdx.x;
+        if (i < n) st[i] = v[u];
+      }
+    }
+    __syncthreads();
+  }
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
     const int h = e / D, dd = e - h * D;
+    auto at = [&](int s_, int k) {
+      return staged ? st[s_ * rec + h * (D + 2) + k] : part[(int64_t)s_ * rec + h * (D + 2) + k];
+    };
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part[(int64_t)s * G * (D + 2) + h * (D + 2)]);
+    for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, at(s_, 0));
     float L = 0.f, O = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* p = part + (int64_t)s * G * (D + 2) + h * (D + 2);
-      if (p[0] != -INFINITY) {
-        const float f = expf(p[0] - M);
-        L = fmaf(p[1], f, L);
-        O = fmaf(p[2 + dd], f, O);
+    for (int s_ = 0; s_ < S; ++s_) {
+      const float ms = at(s_, 0);
+      if (ms != -INFINITY) {
+        const float f = __expf(ms - M);
+        L = fmaf(at(s_, 1), f, L);
+        O = fmaf(at(s_, 2 + dd), f, O);
       }
     }
     out[h * D + dd] = L > 0.f ? O / L : 0.f;
   }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ final argmax
-__device__ void argmax_task(const KArgs& a) {
-  const int b = threadIdx.x;
-  if (b < a.B) {
+// next_ids[b] = argmax over the LM-head tile partials; ties -> lowest index.
+__device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
+  float* red = reinterpret_cast<float*>(lds + kLdsRed);
+  int* redi = reinterpret_cast<int*>(red + kWaves);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int b = 0; b < a.B; ++b) {
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int n = 0; n < a.T_lm; ++n) {
-      PMax p = a.pmax[b * a.T_lm + n];
+    for (int n = threadIdx.x; n < a.T_lm; n += kThreads) {
+      const PMax p = a.pmax[b * a.T_lm + n];
       if (p.v > bv || (p.v == bv && p.i < bi)) { bv = p.v; bi = p.i; }
     }
-    a.next_ids[b] = (bi == INT_MAX) ? 0 : bi;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float ov = __shfl_xor(bv, m);
+      const int oi = __shfl_xor(bi, m);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) { red[w] = bv; redi[w] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int i = 1; i < kWaves; ++i)
+        if (red[i] > bv || (red[i] == bv && redi[i] < bi)) { bv = red[i]; bi = redi[i]; }
+      a.next_ids[b] = (bi == INT_MAX) ? 0 : bi;
+    }
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ dispatch
-constexpr int kLdsBytes = 96 * 1024;  // > 80 KB so only one workgroup fits a compute unit
-
-__device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, char* lds) {
-  float* f = reinterpret_cast<float*>(lds);
-  float* red = f + (kLdsBytes / 4 - 64);  // reduction scratch at the top
+// Runs task `task` with the whole workgroup.
+__device__ __forceinline__ void run_task(gptr<const KArgs> ap, int task) {
+  const KArgs a = *ap;
+  const DevTask t = a.tasks[task];
+  char* lds = g_lds;
+  float* red = reinterpret_cast<float*>(lds + kLdsRed);
   const int l = t.layer;
+  gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)(l < 0 ? 0 : l) * LAYER_PTRS;
   switch (t.type) {
     case MPK_TASK_EMBED:
       embed_task(a);
       break;
     case MPK_TASK_ATTN_NORM:
-      if (l == 0) norm_task(a, a.e, nullptr, a.r, a.wl[W_IN_NORM], a.h, red);
+      if (l == 0) norm_task(a, a.e, nullptr, a.r, W[W_IN_NORM], a.h, red);
       else
         norm_task(a, a.s + (int64_t)(l - 1) * a.st_bh, a.dn + (int64_t)(l - 1) * a.st_bh, a.r + (int64_t)l * a.st_bh,
-                  a.wl[(int64_t)l * LAYER_PTRS + W_IN_NORM], a.h + (int64_t)l * a.st_bh, red);
+                  W[W_IN_NORM], a.h + (int64_t)l * a.st_bh, red);
       break;
     case MPK_TASK_MLP_NORM:
       norm_task(a, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_bh, a.s + (int64_t)l * a.st_bh,
-                a.wl[(int64_t)l * LAYER_PTRS + W_POST_NORM], a.h2 + (int64_t)l * a.st_bh, red);
+                W[W_POST_NORM], a.h2 + (int64_t)l * a.st_bh, red);
       break;
     case MPK_TASK_FINAL_NORM:
       norm_task(a, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_bh, nullptr, a.final_norm,
@@ -574,21 +800,25 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, char*
     case MPK_TASK_GATEUP:
     case MPK_TASK_DOWN:
     case MPK_TASK_LMHEAD:
-      if (a.B == 1) gemv_task<1>(a, t, f, red);
-      else gemv_task<kMaxBatch>(a, t, f, red);
+      if (a.B == 1) gemv_b1<8>(a, t, lds);
+      else gemv_bn(a, t, lds);
       break;
     case MPK_TASK_QKNORM_ROPE:
       rope_task(a, t);
       break;
     case MPK_TASK_ATTN:
-      if (a.d == 128) attn_task<128>(a, t, f);
-      else attn_task<64>(a, t, f);
+      if (a.d == 128) {
+        if (a.G <= 4) attn_task<128, 16, 4>(a, t, lds);
+        else attn_task<128, 32, 8>(a, t, lds);
+      } else {
+        attn_task<64, 16, 8>(a, t, lds);
+      }
       break;
     case MPK_TASK_COMBINE:
-      combine_task(a, t);
+      combine_task(a, t, lds);
       break;
     case MPK_TASK_ARGMAX:
-      argmax_task(a);
+      argmax_task(a, lds);
       break;
     default:
       break;

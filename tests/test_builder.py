@@ -26,21 +26,22 @@ def assert_same(ref, got):
 
 
 def both(shape, B, W, q=None, S=None, **over):
+    """Build the same graph with the C++ builder (defaults resolved by the
+    library, overrides applied) and with the oracle spec (params read back
+    from the library's header)."""
     s = shape
-    hkv = s.n_kv_heads
-    q = q if q is not None else (1 if B == 1 else 16)
-    prm = tg.Params(W=W, q=q, S_attn=S or 4, **over)
-    for f, N in (("T_o", s.hidden), ("T_gu", s.ffn), ("T_down", s.hidden), ("T_lm", s.vocab)):
-        if f not in over:
-            setattr(prm, f, min(W, -(-N // q)))
-    if "T_qkv" not in over:
-        Sg = (s.n_q_heads // hkv + 2) * s.head_dim
-        prm.T_qkv = max(1, min(W // hkv, -(-Sg // q))) * hkv
+    names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm")
+    params = dict(n_workers=W, s_attn=S or 4)
+    if q is not None:
+        params["quantum"] = q
+    for k, v in over.items():
+        params[names[k]] = v
+    g = mpk.TGraph(s.cfg(), B, s.page_size, params, host_only=True)
+    p = g.header()["params"]
+    prm = tg.Params(W=p["n_workers"], S_sched=p["n_sched_waves"], q=p["quantum"], T_qkv=p["t_qkv"], T_o=p["t_o"],
+                    T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"])
     ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
-    params = dict(n_workers=W, quantum=q, t_qkv=prm.T_qkv, t_o=prm.T_o, t_gu=prm.T_gu, t_down=prm.T_down,
-                  t_lm=prm.T_lm, s_attn=prm.S_attn)
-    got = mpk.TGraph(s.cfg(), B, s.page_size, params, host_only=True).export()
-    return ref, got, tasks
+    return ref, g.export(), tasks
 
 
 def test_tiny_worked_example_bit_exact():
@@ -78,6 +79,8 @@ def test_default_params_resolve_as_documented():
     assert p["t_qkv"] == 248 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 252 and p["s_attn"] == 16
     h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
     assert h16["quantum"] == 16 and h16["s_attn"] == 4
+    # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
+    assert h16["t_lm"] == 504 and h16["t_gu"] == 252
 
 
 @settings(max_examples=120, deadline=None, suppress_health_check=[HealthCheck.too_slow])

@@ -236,3 +236,40 @@ def test_qwen3_8b_shape():
 @pytest.mark.timeout(600)
 def test_qwen3_8b_batch16_shape():
     _full("qwen3_8b_b16", modes=("mega",), lazy=True)
+
+
+def test_trace_happens_before_every_wait():
+    """Trace-based check of the runtime: every task starts after every task it
+    waits for (through empty tasks) has finished, and every non-empty task runs
+    exactly once per step."""
+    say("trace happens-before")
+    s = TINY.with_(batch=3, ctx_range=(20, 200), ctx=0)
+    inp = device_inputs(s, seed=9)
+    r = Runner(inp)
+    r.g.set_trace(True)
+    r.run("mega")
+    r.run("mega")
+    rec, tpu = r.g.read_trace()
+    ex = r.g.export()
+    NT = len(ex["task_type"])
+    real = np.nonzero(ex["task_type"] != mpk._binding.TASK_EMPTY)[0]
+    assert sorted(rec["task"].tolist()) == real.tolist()
+    assert np.all(rec["t_wait"] <= rec["t_start"]) and np.all(rec["t_start"] <= rec["t_end"])
+    start = np.zeros(NT, np.uint64); end = np.zeros(NT, np.uint64)
+    start[rec["task"]] = rec["t_start"]; end[rec["task"]] = rec["t_end"]
+    prods = {}
+    for t in range(NT):
+        prods.setdefault(int(ex["task_trig"][t]), []).append(t)
+
+    def real_producers(e):
+        out = []
+        for p in prods.get(e, []):
+            if ex["task_type"][p] == mpk._binding.TASK_EMPTY:
+                out += real_producers(int(ex["task_dep"][p]))
+            else:
+                out.append(p)
+        return out
+    for c in real:
+        for p in real_producers(int(ex["task_dep"][c])):
+            assert end[p] <= start[c], (p, c)
+    r.g.set_trace(False)
