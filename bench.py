@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--baseline-steps", type=int, default=20)
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the step, run a plain device copy of this many MiB three times (a known-size "
+                         "kernel for scaling the HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode step is built and measured on a single MI355X "
@@ -138,6 +141,15 @@ def main():
             f = (lambda hg=hg: g.decode_step_baseline(W, ids, KV, lens, logits, nxt, use_hipgraph=hg))
             _, pb = time_steps(f, args.baseline_steps, 3, torch)
             base[mode] = round(statistics.median(pb), 4)
+
+    if args.calib_copy_mib > 0:
+        n = (args.calib_copy_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu:

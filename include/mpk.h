@@ -83,7 +83,8 @@ typedef struct {
  * the exported header so that a checker can rebuild the same graph. */
 typedef struct {
   int32_t n_workers;     /* W worker workgroups (default: compute units - scheduler WGs) */
-  int32_t n_sched_waves; /* scheduler wavefronts, 4 per scheduler WG (default 16)        */
+  int32_t n_sched_waves; /* scheduler wavefronts, 4 per scheduler WG (default 16); each  */
+                         /* serves at most 64 workers (checked when the graph uploads)   */
   int32_t quantum;       /* column quantum of projection tiles (default 1 at B=1, else 16) */
   int32_t t_qkv, t_o, t_gu, t_down, t_lm; /* tiles per projection (default ~W; t_qkv a
                                              multiple of n_kv_heads)                    */
@@ -231,6 +232,7 @@ typedef struct {
   uint64_t t_wait;  /* the worker started looking for this task */
   uint64_t t_start; /* its dependent event had fired / it was taken from the JIT ring */
   uint64_t t_end;   /* its body finished (before its triggering event is advanced) */
+  uint64_t t_done;  /* its triggering event had been advanced (release + add returned) */
 } mpk_trace_record;
 
 /* Turn tracing of mpk_decode_step on (1) or off (0).  Allocates (frees) a

@@ -80,7 +80,7 @@ class mpk_status_word(C.Structure):
 
 class mpk_trace_record(C.Structure):
     _fields_ = [("task", C.c_int32), ("worker", C.c_int32), ("t_wait", C.c_uint64), ("t_start", C.c_uint64),
-                ("t_end", C.c_uint64)]
+                ("t_end", C.c_uint64), ("t_done", C.c_uint64)]
 
 
 # symbol -> (restype, argtypes); the list every test checks against the header
@@ -277,7 +277,7 @@ class TGraph:
         tpu = C.c_double()
         _check(lib().mpk_read_trace(self.h, buf, cap, C.byref(n), C.byref(tpu)))
         dt = np.dtype([("task", np.int32), ("worker", np.int32), ("t_wait", np.uint64), ("t_start", np.uint64),
-                       ("t_end", np.uint64)])
+                       ("t_end", np.uint64), ("t_done", np.uint64)])
         arr = np.frombuffer(bytes(buf), dtype=dt, count=cap)[: n.value].copy()
         return arr, tpu.value
 

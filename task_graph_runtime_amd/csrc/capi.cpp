@@ -16,9 +16,9 @@
 #include "rt.h"
 
 namespace mpk {
-hipError_t launch_megakernel(const KArgs* d_args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
-hipError_t launch_baseline_op(const KArgs* d_args, const int32_t* list, int count, hipStream_t stream);
-hipError_t launch_time_task(const KArgs* d_args, int task, unsigned long long* out, hipStream_t stream);
+hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
+hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count, hipStream_t stream);
+hipError_t launch_time_task(const KArgs& args, int task, unsigned long long* out, hipStream_t stream);
 }  // namespace mpk
 
 using namespace mpk;
@@ -68,7 +68,8 @@ struct mpk_tgraph {
   DevTask* d_tasks = nullptr;
   DevEvent* d_events = nullptr;
   uint32_t* d_aot_off = nullptr;
-  uint32_t* d_aot_tasks = nullptr;
+  AotEntry* d_aot_desc = nullptr;
+  std::vector<AotEntry> h_aot;  // host copy; its weight pointers follow the last step's weights
   void* d_rt = nullptr;     // counters, rings, state, status
   uint32_t* d_ev_cnt = nullptr;
   unsigned long long* d_sched_ring = nullptr;
@@ -80,10 +81,7 @@ struct mpk_tgraph {
 
   void* d_act = nullptr;
   KArgs base{};             // arguments that do not change between steps
-  KArgs* d_args = nullptr;  // device copy read by the kernels
-  KArgs* h_stage = nullptr; // pinned staging of the device copy
-  hipEvent_t args_ev = nullptr;
-  KArgs uploaded{};
+  KArgs last{};             // arguments of the last step (kernel arguments are passed by value)
   bool args_valid = false;
   struct TensorRef { void* p; int64_t bytes; };
   std::vector<TensorRef> tensors;  // indexed by tensor id (null when caller-owned)
@@ -116,6 +114,8 @@ void fill_descriptors(mpk_tgraph* t) {
     d.layer = g.task_layer[i];
     d.dep = g.task_dep[i];
     d.trig = g.task_trig[i];
+    d.id = i;
+    d.dep_counts = g.event_counts[d.dep];
     const int32_t c0 = g.task_coords[3 * (size_t)i], c1 = g.task_coords[3 * (size_t)i + 1],
                   c2 = g.task_coords[3 * (size_t)i + 2];
     int32_t lo = 0, hi = 0;
@@ -187,6 +187,8 @@ int upload(mpk_tgraph* t) {
   t->grid = t->n_sched_wgs + t->prm.W;
   if (t->grid > t->n_cus)
     return fail(MPK_ERR_INVALID_ARG, "workers + scheduler workgroups exceed the compute units");
+  if ((t->prm.W + t->n_sched - 1) / t->n_sched > 64)
+    return fail(MPK_ERR_INVALID_ARG, "more than 64 workers per scheduler wavefront");
 
   fill_descriptors(t);
   // graph arrays
@@ -195,10 +197,10 @@ int upload(mpk_tgraph* t) {
   const int64_t o_aot = align256(o_off + (int64_t)g.aot_offsets.size() * 4);
   std::vector<int32_t> flat;
   build_op_lists(t, &flat);
-  const int64_t o_lists = align256(o_aot + (int64_t)std::max<size_t>(1, g.aot_tasks.size()) * 4);
+  // (+1: a worker with an empty list still reads one descriptor)
+  const int64_t o_lists = align256(o_aot + (int64_t)(g.aot_tasks.size() + 1) * sizeof(AotEntry));
   const int64_t o_wl = align256(o_lists + (int64_t)std::max<size_t>(1, flat.size()) * 4);
-  const int64_t o_args = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
-  const int64_t o_freq = align256(o_args + (int64_t)sizeof(KArgs));
+  const int64_t o_freq = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
   const int64_t graph_bytes = align256(o_freq + (int64_t)t->cfg.head_dim / 2 * 8);
   HIPCHK(hipMalloc(&t->d_graph, graph_bytes));
   char* gb = (char*)t->d_graph;
@@ -207,10 +209,9 @@ int upload(mpk_tgraph* t) {
   t->d_tasks = (DevTask*)(gb + o_tasks);
   t->d_events = (DevEvent*)(gb + o_events);
   t->d_aot_off = (uint32_t*)(gb + o_off);
-  t->d_aot_tasks = (uint32_t*)(gb + o_aot);
+  t->d_aot_desc = (AotEntry*)(gb + o_aot);
   t->d_lists = (int32_t*)(gb + o_lists);
   t->d_wl = (const uint16_t**)(gb + o_wl);
-  t->d_args = (KArgs*)(gb + o_args);
   {
     std::vector<double> inv(t->cfg.head_dim / 2);
     for (size_t i = 0; i < inv.size(); ++i)
@@ -218,13 +219,13 @@ int upload(mpk_tgraph* t) {
     HIPCHK(hipMemcpy(gb + o_freq, inv.data(), inv.size() * 8, hipMemcpyHostToDevice));
     t->base.inv_freq = (const double*)(gb + o_freq);
   }
-  HIPCHK(hipHostMalloc((void**)&t->h_stage, sizeof(KArgs), hipHostMallocDefault));
-  HIPCHK(hipEventCreateWithFlags(&t->args_ev, hipEventDisableTiming));
   HIPCHK(hipMemcpy(t->d_tasks, t->h_tasks.data(), (size_t)g.NT * sizeof(DevTask), hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(t->d_events, ev.data(), (size_t)g.NE * sizeof(DevEvent), hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(t->d_aot_off, g.aot_offsets.data(), g.aot_offsets.size() * 4, hipMemcpyHostToDevice));
-  if (!g.aot_tasks.empty())
-    HIPCHK(hipMemcpy(t->d_aot_tasks, g.aot_tasks.data(), g.aot_tasks.size() * 4, hipMemcpyHostToDevice));
+  // AOT entries (weight pointers are filled in by the first step)
+  t->h_aot.assign(g.aot_tasks.size() + 1, AotEntry{});
+  for (size_t k = 0; k < g.aot_tasks.size(); ++k) t->h_aot[k].t = t->h_tasks[g.aot_tasks[k]];
+  HIPCHK(hipMemcpy(t->d_aot_desc, t->h_aot.data(), t->h_aot.size() * sizeof(AotEntry), hipMemcpyHostToDevice));
   if (!flat.empty()) HIPCHK(hipMemcpy(t->d_lists, flat.data(), flat.size() * 4, hipMemcpyHostToDevice));
 
   // runtime: counters, rings, state, status
@@ -294,7 +295,7 @@ int upload(mpk_tgraph* t) {
     for (int k = 0; k < L_COUNT; ++k)
       if (per_layer_bytes[k]) t->tensors[layer_tensor((int32_t)l, k)] = {ab + kind_off[k] + l * per_layer_bytes[k], per_layer_bytes[k]};
 
-  a.tasks = t->d_tasks; a.events = t->d_events; a.aot_off = t->d_aot_off; a.aot_tasks = t->d_aot_tasks;
+  a.tasks = t->d_tasks; a.events = t->d_events; a.aot_off = t->d_aot_off; a.aot_desc = t->d_aot_desc;
   a.ev_cnt = t->d_ev_cnt; a.sched_ring = t->d_sched_ring; a.sched_tail = t->d_sched_tail; a.jit_ring = t->d_jit_ring;
   a.state = t->d_state; a.sched_cap = t->sched_cap; a.jit_cap = t->jit_cap;
   a.n_workers = W; a.n_sched = S; a.n_sched_wgs = t->n_sched_wgs;
@@ -309,11 +310,6 @@ int upload(mpk_tgraph* t) {
 
 void free_tgraph(mpk_tgraph* t) {
   if (!t) return;
-  if (t->args_ev) {
-    (void)hipEventSynchronize(t->args_ev);
-    (void)hipEventDestroy(t->args_ev);
-  }
-  if (t->h_stage) (void)hipHostFree(t->h_stage);
   if (t->gexec) (void)hipGraphExecDestroy(t->gexec);
   if (t->cap_stream) (void)hipStreamDestroy(t->cap_stream);
   if (t->d_graph) (void)hipFree(t->d_graph);
@@ -363,7 +359,28 @@ mpk_tgraph_header make_header(const mpk_tgraph* t) {
   return h;
 }
 
-// Fill the per-step arguments; uploads the weight-pointer table when it changed.
+// Weight base pointers of a task (the device's task_ptrs, on the host).
+TaskPtrs host_task_ptrs(const DevTask& d, const std::vector<const void*>& wl, const void* lm, const void* fnorm) {
+  TaskPtrs r{};
+  const size_t base = (size_t)(d.layer < 0 ? 0 : d.layer) * LAYER_PTRS;
+  auto W = [&](int k) { return (const uint16_t*)wl[base + k]; };
+  switch (d.type) {
+    case MPK_TASK_QKV: r.p0 = W(W_Q); r.p1 = W(W_K); r.p2 = W(W_V); break;
+    case MPK_TASK_OPROJ: r.p0 = W(W_O); break;
+    case MPK_TASK_GATEUP: r.p0 = W(W_GATE); r.p1 = W(W_UP); break;
+    case MPK_TASK_DOWN: r.p0 = W(W_DOWN); break;
+    case MPK_TASK_LMHEAD: r.p0 = (const uint16_t*)lm; break;
+    case MPK_TASK_ATTN_NORM: r.p0 = W(W_IN_NORM); break;
+    case MPK_TASK_MLP_NORM: r.p0 = W(W_POST_NORM); break;
+    case MPK_TASK_FINAL_NORM: r.p0 = (const uint16_t*)fnorm; break;
+    case MPK_TASK_QKNORM_ROPE: r.p0 = W(W_Q_NORM); r.p1 = W(W_K_NORM); break;
+    default: break;
+  }
+  return r;
+}
+
+// Fill the per-step arguments; when the weights changed, uploads the
+// weight-pointer table and the AOT entries' resolved pointers.
 int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
               const int32_t* seq_lens, float* logits, int32_t* next_ids, hipStream_t stream, KArgs* out) {
   if (!t || !w || !kv || !token_ids || !seq_lens || !logits || !next_ids)
@@ -385,11 +402,17 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   if (((uintptr_t)w->embed & 15) || ((uintptr_t)w->lm_head & 15) || ((uintptr_t)kv->k_pool & 15) ||
       ((uintptr_t)kv->v_pool & 15))
     return fail(MPK_ERR_INVALID_ARG, "weights and KV pools must be 16-byte aligned");
-  if (wl != t->h_wl) {
+  const void* lm = c.tied_embedding ? w->embed : w->lm_head;
+  std::vector<const void*> key = wl;
+  key.push_back(lm);
+  key.push_back(w->final_norm);
+  if (key != t->h_wl) {
     if (t->last_stream) HIPCHK(hipStreamSynchronize(t->last_stream));
     HIPCHK(hipStreamSynchronize(stream));
     HIPCHK(hipMemcpy(t->d_wl, wl.data(), wl.size() * sizeof(void*), hipMemcpyHostToDevice));
-    t->h_wl = wl;
+    for (size_t k = 0; k + 1 < t->h_aot.size(); ++k) t->h_aot[k].w = host_task_ptrs(t->h_aot[k].t, wl, lm, w->final_norm);
+    HIPCHK(hipMemcpy(t->d_aot_desc, t->h_aot.data(), t->h_aot.size() * sizeof(AotEntry), hipMemcpyHostToDevice));
+    t->h_wl = key;
   }
   KArgs a = t->base;
   a.embed = (const uint16_t*)w->embed;
@@ -405,15 +428,8 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   a.logits = logits;
   a.next_ids = next_ids;
   *out = a;
-  // refresh the device copy of the arguments when a caller pointer changed
-  if (!t->args_valid || std::memcmp(&a, &t->uploaded, sizeof(KArgs)) != 0) {
-    HIPCHK(hipEventSynchronize(t->args_ev));   // the staging buffer is free again
-    std::memcpy(t->h_stage, &a, sizeof(KArgs));
-    HIPCHK(hipMemcpyAsync(t->d_args, t->h_stage, sizeof(KArgs), hipMemcpyHostToDevice, stream));
-    HIPCHK(hipEventRecord(t->args_ev, stream));
-    t->uploaded = a;
-    t->args_valid = true;
-  }
+  t->last = a;
+  t->args_valid = true;
   return MPK_OK;
 }
 
@@ -531,7 +547,7 @@ int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_id
   int rc = step_args(g, w, token_ids, kv, seq_lens, logits, next_ids, s, &a);
   if (rc) return rc;
   const uint32_t epoch = ++g->epoch;
-  hipError_t e = launch_megakernel(g->d_args, epoch, timeout_ticks(g), g->grid, s);
+  hipError_t e = launch_megakernel(a, epoch, timeout_ticks(g), g->grid, s);
   if (e != hipSuccess) { --g->epoch; return hip_fail(e, "mega-kernel launch"); }
   g->last_stream = s;
   return MPK_OK;
@@ -548,7 +564,7 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
   if (!use_hipgraph) {
     for (auto& op : g->ops) {
       if (!op.second) continue;
-      hipError_t e = launch_baseline_op(g->d_args, g->d_lists + op.first, op.second, s);
+      hipError_t e = launch_baseline_op(a, g->d_lists + op.first, op.second, s);
       if (e != hipSuccess) return hip_fail(e, "baseline launch");
     }
     return MPK_OK;
@@ -564,7 +580,7 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
     HIPCHK(hipStreamBeginCapture(g->cap_stream, hipStreamCaptureModeThreadLocal));
     for (auto& op : g->ops) {
       if (!op.second) continue;
-      hipError_t e = launch_baseline_op(g->d_args, g->d_lists + op.first, op.second, g->cap_stream);
+      hipError_t e = launch_baseline_op(a, g->d_lists + op.first, op.second, g->cap_stream);
       if (e != hipSuccess) {
         hipGraph_t dummy;
         (void)hipStreamEndCapture(g->cap_stream, &dummy);
@@ -651,7 +667,7 @@ int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32
     for (uint32_t k = 0; k < std::min<uint32_t>(cnt[w], (uint32_t)g->trace_cap); ++k) {
       if (n < capacity) {
         const TraceRec& r = recs[(size_t)w * g->trace_cap + k];
-        out[n] = mpk_trace_record{r.task, r.worker, r.t_wait, r.t_start, r.t_end};
+        out[n] = mpk_trace_record{r.task, r.worker, r.t_wait, r.t_start, r.t_end, r.t_done};
       }
       ++n;
     }
@@ -668,13 +684,11 @@ int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps,
     if (tasks[i] < 0 || tasks[i] >= g->g.NT) return fail(MPK_ERR_INVALID_ARG, "task index out of range");
   HIPCHK(hipDeviceSynchronize());
   void* buf = nullptr;
-  HIPCHK(hipMalloc(&buf, (size_t)n * 12));
-  int32_t* d_list = (int32_t*)buf;
-  unsigned long long* d_out = (unsigned long long*)((char*)buf + (size_t)n * 4);
-  (void)d_list;
+  HIPCHK(hipMalloc(&buf, (size_t)n * 8));
+  unsigned long long* d_out = (unsigned long long*)buf;
   hipError_t e = hipMemset(d_out, 0, (size_t)n * 8);
   for (int32_t i = 0; i < n && e == hipSuccess; ++i)
-    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) e = launch_time_task(g->d_args, tasks[i], d_out + i, nullptr);
+    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) e = launch_time_task(g->last, tasks[i], d_out + i, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(ticks, d_out, (size_t)n * 8, hipMemcpyDeviceToHost);
   for (int32_t i = 0; i < n && e == hipSuccess; ++i) ticks[i] /= (uint64_t)reps;

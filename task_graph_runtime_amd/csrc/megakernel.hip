@@ -21,6 +21,13 @@ namespace mpk {
 
 namespace {
 
+// Kernel arguments live in the constant kernel-argument segment.
+#if defined(__HIP_DEVICE_COMPILE__)
+using kptr = const __attribute__((address_space(4))) KArgs*;
+#else
+using kptr = const KArgs*;
+#endif
+
 __device__ __forceinline__ uint32_t ld_relaxed(gptr<const uint32_t> p) {
   return __hip_atomic_load(const_cast<gptr<uint32_t>>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -51,54 +58,125 @@ __device__ __forceinline__ void push_event(const KArgs& a, int e) {
                ((unsigned long long)(pos + 1) << 32) | (uint32_t)e);
 }
 
-// One trigger of event e by the calling thread (after the producer's writes
-// are complete for the whole workgroup).  If this add fires the event, its
-// empty consumers are resolved here (each triggers its own event) and JIT
-// consumers are handed to a scheduler.
-__device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e) {
-  const uint32_t old = __hip_atomic_fetch_add(&a.ev_cnt[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  const DevEvent ev = a.events[e];
+// One trigger of event e by wavefront 0 of a workgroup whose writes for the
+// trigger are complete (after a barrier).  Lane 0 advances the counter; if
+// this add fires the event, its empty consumers are resolved here, one lane
+// each (each empty task advances its own event: one release fence covers
+// them all), and the fired events with JIT consumers are handed to their
+// scheduler.
+__device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e, const DevEvent& ev) {
+  const int lane = threadIdx.x & 63;
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(&a.ev_cnt[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
   if (old + 1u != ev.counts * epoch) return;
   acquire_fence();
   if (ev.flags & MPK_EVENT_HAS_EMPTY) {
-    for (int t = ev.first; t <= ev.last; ++t) {
-      const int f = a.tasks[t].trig;
-      const uint32_t o2 = __hip_atomic_fetch_add(&a.ev_cnt[f], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      const DevEvent fe = a.events[f];
-      if (o2 + 1u == fe.counts * epoch && (fe.flags & MPK_EVENT_HAS_JIT)) push_event(a, f);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int t0 = ev.first; t0 <= ev.last; t0 += 64) {
+      const int t = t0 + lane;
+      if (t <= ev.last) {
+        const int f = a.tasks[t].trig;
+        const uint32_t o2 = __hip_atomic_fetch_add(&a.ev_cnt[f], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const DevEvent fe = a.events[f];
+        if (o2 + 1u == fe.counts * epoch && (fe.flags & MPK_EVENT_HAS_JIT)) {
+          acquire_fence();
+          push_event(a, f);
+        }
+      }
     }
   }
-  if (ev.flags & MPK_EVENT_HAS_JIT) push_event(a, e);
+  if ((ev.flags & MPK_EVENT_HAS_JIT) && lane == 0) push_event(a, e);
 }
 
 enum { CMD_EXIT = 0, CMD_JIT = 1, CMD_AOT = 2 };
 
-__device__ __forceinline__ void worker_loop(gptr<const KArgs> ap, uint32_t epoch, uint64_t timeout, int w) {
-  const KArgs a = *ap;
+// Constant records fetched ahead of use: lanes 0..N-1 of each wavefront load
+// one dword each (a vector load: its wait lands where the record is first
+// used, not at the next LDS wait as a scalar load's would), and the record is
+// rebuilt in scalar registers from the lanes.
+template <int N>
+__device__ __forceinline__ uint32_t fetch_words(gptr<const uint32_t> p) {
+  return p[threadIdx.x & (N - 1)];
+}
+__device__ __forceinline__ uint32_t word(uint32_t v, int k) { return (uint32_t)__builtin_amdgcn_readlane((int)v, k); }
+template <typename T>
+__device__ __forceinline__ gptr<const T> ptr_words(uint32_t v, int k) {
+  return reinterpret_cast<gptr<const T>>(((uint64_t)word(v, k + 1) << 32) | word(v, k));
+}
+// (field by field, so that the records stay in registers)
+__device__ __forceinline__ DevTask unpack_task(uint32_t v) {
+  DevTask t;
+  const uint32_t w0 = word(v, 0);
+  t.type = (uint8_t)w0;
+  t.mode = (uint8_t)(w0 >> 8);
+  t.layer = (int16_t)(w0 >> 16);
+  t.dep = (int32_t)word(v, 1);
+  t.trig = (int32_t)word(v, 2);
+  t.a0 = (int32_t)word(v, 3);
+  t.a1 = (int32_t)word(v, 4);
+  t.a2 = (int32_t)word(v, 5);
+  t.id = (int32_t)word(v, 6);
+  t.dep_counts = word(v, 7);
+  return t;
+}
+__device__ __forceinline__ TaskPtrs unpack_ptrs(uint32_t v) {
+  TaskPtrs p;
+  p.p0 = ptr_words<uint16_t>(v, 8);
+  p.p1 = ptr_words<uint16_t>(v, 10);
+  p.p2 = ptr_words<uint16_t>(v, 12);
+  return p;
+}
+__device__ __forceinline__ DevEvent unpack_event(uint32_t v) {
+  DevEvent e;
+  e.counts = word(v, 0);
+  e.first = (int32_t)word(v, 1);
+  e.last = (int32_t)word(v, 2);
+  e.flags = word(v, 3);
+  return e;
+}
+
+// A worker.  It holds the descriptor of its next AOT task in registers (the
+// per-worker descriptor copies are constant, so the following one is fetched
+// while the current task runs); thread 0 waits for either a JIT task or the
+// next AOT task's event, the workgroup runs the task, and wavefront 0 advances
+// the task's triggering event.
+__device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t timeout, int w) {
+  const KArgs a0 = *kp;
   int& s_cmd = reinterpret_cast<int*>(g_lds + kLdsCtl)[0];
   int& s_task = reinterpret_cast<int*>(g_lds + kLdsCtl)[1];
   const int tid = threadIdx.x;
   uint32_t jit_head = 0;
-  if (tid == 0) jit_head = st_jit_head(a)[w];
-  int i = (int)a.aot_off[w];
-  const int iend = (int)a.aot_off[w + 1];
-  const uint32_t end_target = a.events[a.end_event].counts * epoch;
-  gptr<const unsigned long long> ring = a.jit_ring + (int64_t)w * a.jit_cap;
-  gptr<TraceRec> trace = a.trace ? a.trace + (int64_t)w * a.trace_cap : nullptr;
+  if (tid == 0) jit_head = st_jit_head(a0)[w];
+  const uint32_t aot0 = a0.aot_off[w];
+  const int n_aot = (int)(a0.aot_off[w + 1] - aot0);
+  gptr<const AotEntry> aot = a0.aot_desc + aot0;
+  int i = 0;
+  // the next AOT entry, in flight (a worker with no AOT task reads its
+  // neighbour's first entry and never uses it)
+  uint32_t nxt_v = fetch_words<16>(reinterpret_cast<gptr<const uint32_t>>(aot));
+  const uint32_t end_target = a0.events[a0.end_event].counts * epoch;
+  gptr<const unsigned long long> ring = a0.jit_ring + (int64_t)w * a0.jit_cap;
+  gptr<TraceRec> trace = a0.trace ? a0.trace + (int64_t)w * a0.trace_cap : nullptr;
+  const int trace_cap = a0.trace_cap;
   int n_trace = 0;
   uint64_t t_wait = 0, t_start = 0;
   while (true) {
+    // the arguments are re-read (constant cache) in every iteration rather
+    // than held in registers across it
+    kptr ap = kp;
+    asm volatile("" : "+s"(ap));
+    const KArgs a = *ap;
+    // dependent event, its trigger count and the id of the next AOT task
+    const int nxt_dep = (int)word(nxt_v, 1);
+    const int nxt_id = (int)word(nxt_v, 6);
+    const uint32_t nxt_counts = word(nxt_v, 7);
     if (tid == 0) {
       int cmd = CMD_EXIT, task = -1;
       const long long t0 = wall_clock64();
       t_wait = (uint64_t)t0;
-      int dep = -1;
-      uint32_t target = 0, cnt = 0;
-      if (i < iend) {
-        task = (int)a.aot_tasks[i];
-        dep = a.tasks[task].dep;
-        target = a.events[dep].counts * epoch;
-      }
+      const uint32_t target = nxt_counts * epoch;
+      uint32_t cnt = 0;
       while (true) {
         const unsigned long long slot = ld_relaxed64(&ring[jit_head & (a.jit_cap - 1)]);
         if ((uint32_t)(slot >> 32) == jit_head + 1u) {
@@ -107,8 +185,8 @@ __device__ __forceinline__ void worker_loop(gptr<const KArgs> ap, uint32_t epoch
           cmd = CMD_JIT;
           break;
         }
-        if (i < iend) {
-          cnt = ld_relaxed(&a.ev_cnt[dep]);
+        if (i < n_aot) {
+          cnt = ld_relaxed(&a.ev_cnt[nxt_dep]);
           if (reached(cnt, target)) { cmd = CMD_AOT; break; }
         } else if (reached(ld_relaxed(&a.ev_cnt[a.end_event]), end_target)) {
           cmd = CMD_EXIT;
@@ -116,8 +194,8 @@ __device__ __forceinline__ void worker_loop(gptr<const KArgs> ap, uint32_t epoch
         }
         if (ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code)) != 0u) { cmd = CMD_EXIT; break; }
         if ((uint64_t)(wall_clock64() - t0) > timeout) {
-          report(a, MPK_ERR_TIMEOUT, task, i < iend ? dep : a.end_event, i < iend ? cnt : 0u,
-                 i < iend ? target : end_target);
+          report(a, MPK_ERR_TIMEOUT, i < n_aot ? nxt_id : -1, i < n_aot ? nxt_dep : a.end_event,
+                 i < n_aot ? cnt : 0u, i < n_aot ? target : end_target);
           cmd = CMD_EXIT;
           break;
         }
@@ -129,31 +207,56 @@ __device__ __forceinline__ void worker_loop(gptr<const KArgs> ap, uint32_t epoch
       s_task = task;
     }
     __syncthreads();
-    const int cmd = s_cmd, task = s_task;
+    const int cmd = __builtin_amdgcn_readfirstlane(s_cmd), jtask = __builtin_amdgcn_readfirstlane(s_task);
     __syncthreads();
     if (cmd == CMD_EXIT) break;
-    run_task(ap, task);
-    __syncthreads();
-    if (tid == 0) {
-      if (trace && n_trace < a.trace_cap)
-        trace[n_trace++] = TraceRec{task, w, t_wait, t_start, (uint64_t)wall_clock64()};
-      trigger(a, epoch, a.tasks[task].trig);
+    // the task as an AOT entry spread over lanes 0..15 (a JIT task's
+    // descriptor with null weight pointers: JIT tasks are attention tasks)
+    uint32_t cur_v;
+    if (cmd == CMD_AOT) {
+      cur_v = nxt_v;
+      ++i;
+      nxt_v = fetch_words<16>(reinterpret_cast<gptr<const uint32_t>>(aot + (i < n_aot ? i : n_aot - 1)));
+    } else {
+      const uint32_t v = fetch_words<8>(reinterpret_cast<gptr<const uint32_t>>(a.tasks + jtask));
+      cur_v = (threadIdx.x & 15) < 8 ? v : 0u;
     }
-    if (cmd == CMD_AOT) ++i;
+    const DevTask t = unpack_task(cur_v);
+    const TaskPtrs P = unpack_ptrs(cur_v);
+    // the triggering event's record, in flight while the task runs
+    const uint32_t ev_v = fetch_words<4>(reinterpret_cast<gptr<const uint32_t>>(a.events + t.trig));
+    run_task(a, t, P);
+    __syncthreads();
+    if (tid < 64) {
+      const uint64_t t_end = (uint64_t)wall_clock64();
+      trigger(a, epoch, t.trig, unpack_event(ev_v));
+      if (tid == 0 && trace && n_trace < trace_cap)
+        trace[n_trace++] = TraceRec{t.id, w, t_wait, t_start, t_end, (uint64_t)wall_clock64()};
+    }
   }
   if (tid == 0) {
-    st_jit_head(a)[w] = jit_head;
-    if (trace) a.trace_count[w] = (uint32_t)n_trace;
+    st_jit_head(a0)[w] = jit_head;
+    if (trace) a0.trace_count[w] = (uint32_t)n_trace;
   }
 }
 
-// One scheduler per wavefront (lane 0 does the work).
+// One scheduler per wavefront.  Scheduler s serves workers s, s + S, s + 2S,
+// ... (n_sub <= 64 of them); lane x keeps the JIT ring tail of its x-th
+// worker in a register.  A popped event's JIT tasks are dealt round-robin
+// (a running cursor over the sub-workers) in rounds of n_sub tasks: in one
+// round every lane writes the slot of its own worker, so a round costs one
+// store per lane in parallel.  One release fence before the rounds orders
+// the slot stores after everything the scheduler has acquired (the workers
+// read the slots relaxed and then fence-acquire).
 __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, uint64_t timeout, int s) {
-  if ((threadIdx.x & 63) != 0) return;
-  uint32_t head = st_sched_head(a)[s], rr = st_sched_rr(a)[s];
+  const int lane = threadIdx.x & 63;
   const int n_sub = (a.n_workers - s + a.n_sched - 1) / a.n_sched;
   gptr<uint32_t> tails = st_jit_tail(a);
+  const int my_w = s + lane * a.n_sched;
+  uint32_t my_tail = lane < n_sub ? tails[my_w] : 0u;
+  uint32_t head = st_sched_head(a)[s], rr = st_sched_rr(a)[s];
   gptr<const unsigned long long> ring = a.sched_ring + (int64_t)s * a.sched_cap;
+  gptr<unsigned long long> my_ring = a.jit_ring + (int64_t)(lane < n_sub ? my_w : 0) * a.jit_cap;
   const uint32_t end_target = a.events[a.end_event].counts * epoch;
   long long t0 = wall_clock64();
   while (true) {
@@ -163,35 +266,44 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
       const int e = (int)(uint32_t)slot;
       ++head;
       const DevEvent ev = a.events[e];
-      for (int t = ev.first; t <= ev.last; ++t) {
-        const int w = s + (int)(rr % (uint32_t)n_sub) * a.n_sched;
-        ++rr;
-        const uint32_t tail = tails[w];
-        st_release64(&a.jit_ring[(int64_t)w * a.jit_cap + (tail & (a.jit_cap - 1))],
-                     ((unsigned long long)(tail + 1u) << 32) | (uint32_t)t);
-        tails[w] = tail + 1u;
+      const int k = ev.last - ev.first + 1;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      for (int base = 0; base < k; base += n_sub) {
+        // task base + j goes to sub-worker (rr + base + j) mod n_sub
+        const int r0 = (int)((rr + (uint32_t)base) % (uint32_t)n_sub);
+        const int j = base + (lane - r0 + n_sub) % n_sub;
+        if (lane < n_sub && j < k) {
+          __hip_atomic_store(&my_ring[my_tail & (a.jit_cap - 1)],
+                             ((unsigned long long)(my_tail + 1u) << 32) | (uint32_t)(ev.first + j),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ++my_tail;
+        }
       }
+      rr += (uint32_t)k;
       t0 = wall_clock64();
       continue;
     }
     if (reached(ld_relaxed(&a.ev_cnt[a.end_event]), end_target)) break;
     if (ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code)) != 0u) break;
     if ((uint64_t)(wall_clock64() - t0) > timeout) {
-      report(a, MPK_ERR_TIMEOUT, -1, a.end_event, 0u, end_target);
+      if (lane == 0) report(a, MPK_ERR_TIMEOUT, -1, a.end_event, 0u, end_target);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  st_sched_head(a)[s] = head;
-  st_sched_rr(a)[s] = rr;
+  if (lane < n_sub) tails[my_w] = my_tail;
+  if (lane == 0) {
+    st_sched_head(a)[s] = head;
+    st_sched_rr(a)[s] = rr;
+  }
 }
 
 }  // namespace
 
-__global__ void __launch_bounds__(kThreads) mpk_megakernel(const KArgs* __restrict__ args, uint32_t epoch,
-                                                            uint64_t timeout) {
-  gptr<const KArgs> ap = (gptr<const KArgs>)(args);
-  const KArgs a = *ap;
+__global__ void __launch_bounds__(kThreads) mpk_megakernel(const KArgs args, uint32_t epoch, uint64_t timeout) {
+  // `args` is the first kernel argument: it starts the kernel-argument segment
+  const kptr kp = (kptr)(__builtin_amdgcn_kernarg_segment_ptr());
+  const KArgs a = args;
   if (ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code)) != 0u) return;  // poisoned graph
   const int wg = blockIdx.x;
   if (wg < a.n_sched_wgs) {
@@ -200,37 +312,41 @@ __global__ void __launch_bounds__(kThreads) mpk_megakernel(const KArgs* __restri
     return;
   }
   const int w = wg - a.n_sched_wgs;
-  if (w < a.n_workers) worker_loop(ap, epoch, timeout, w);
+  if (w < a.n_workers) worker_loop(kp, epoch, timeout, w);
 }
 
 // Kernel-per-operator baseline: workgroup i runs task list[i], no events.
-__global__ void __launch_bounds__(kThreads) mpk_baseline_op(const KArgs* __restrict__ ap, const int32_t* list) {
-  run_task((gptr<const KArgs>)(ap), list[blockIdx.x]);
+__global__ void __launch_bounds__(kThreads) mpk_baseline_op(const KArgs a, const int32_t* list) {
+  const DevTask t = a.tasks[list[blockIdx.x]];
+  run_task(a, t, task_ptrs(a, t));
 }
 
 // Body timing: one workgroup runs one task and adds its wall-clock ticks to *out.
-__global__ void __launch_bounds__(kThreads) mpk_time_task_kernel(const KArgs* __restrict__ ap, int task,
+__global__ void __launch_bounds__(kThreads) mpk_time_task_kernel(const KArgs a, int task,
                                                                   unsigned long long* out) {
+  const DevTask t = a.tasks[task];
+  const TaskPtrs P = task_ptrs(a, t);
   __syncthreads();
   const unsigned long long t0 = wall_clock64();
-  run_task((gptr<const KArgs>)(ap), task);
+  run_task(a, t, P);
   __syncthreads();
   if (threadIdx.x == 0) *out += wall_clock64() - t0;
 }
 
-hipError_t launch_time_task(const KArgs* d_args, int task, unsigned long long* out, hipStream_t stream) {
-  hipLaunchKernelGGL(mpk_time_task_kernel, dim3(1), dim3(kThreads), 0, stream, d_args, task, out);
+hipError_t launch_time_task(const KArgs& args, int task, unsigned long long* out, hipStream_t stream) {
+  hipLaunchKernelGGL(mpk_time_task_kernel, dim3(1), dim3(kThreads), 0, stream, args, task, out);
   return hipGetLastError();
 }
 
-hipError_t launch_megakernel(const KArgs* d_args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream) {
-  void* args[] = {&d_args, &epoch, &timeout};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mpk_megakernel), dim3(grid), dim3(kThreads),
-                                    args, 0, stream);
+hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream) {
+  KArgs a = args;
+  void* p[] = {&a, &epoch, &timeout};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mpk_megakernel), dim3(grid), dim3(kThreads), p,
+                                    0, stream);
 }
 
-hipError_t launch_baseline_op(const KArgs* d_args, const int32_t* list, int count, hipStream_t stream) {
-  hipLaunchKernelGGL(mpk_baseline_op, dim3(count), dim3(kThreads), 0, stream, d_args, list);
+hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count, hipStream_t stream) {
+  hipLaunchKernelGGL(mpk_baseline_op, dim3(count), dim3(kThreads), 0, stream, args, list);
   return hipGetLastError();
 }
 

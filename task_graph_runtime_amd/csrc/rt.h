@@ -5,21 +5,55 @@
 
 #include <cstdint>
 
+// Device pointers of the argument block and of the records below are typed
+// as global-address-space pointers in device code (same 64-bit layout as the
+// host's plain pointers), so that every access through them is a global --
+// not a flat -- memory instruction: flat loads also count against the LDS
+// wait counter.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MPK_GLOBAL __attribute__((address_space(1)))
+#else
+#define MPK_GLOBAL
+#endif
+
 namespace mpk {
 
 // One linearised task, 32 bytes (two 16-byte loads / one s_load_dwordx8).
-// a0..a3 are the task's operands: projection tiles (a0, a1) = output column
+// a0..a2 are the task's operands: projection tiles (a0, a1) = output column
 // range, a2 = tile index; per-request tasks a0 = b, a1 = kv group, a2 = split.
+// id is the task's own linear index and dep_counts the trigger count of its
+// dependent event, so that a worker holding the descriptor needs no further
+// load before it can wait.
 struct alignas(16) DevTask {
   uint8_t type;
   uint8_t mode;
   int16_t layer;
   int32_t dep;
   int32_t trig;
-  int32_t a0, a1, a2, a3;
-  int32_t rsv;
+  int32_t a0, a1, a2;
+  int32_t id;
+  uint32_t dep_counts;
 };
 static_assert(sizeof(DevTask) == 32, "DevTask must be 32 bytes");
+
+// Weight base pointers a task reads (resolved from the per-layer pointer
+// table): QKV q/k/v, GATEUP gate/up, other projections and the LM head p0,
+// norms their gain p0, q/k norm + RoPE the q and k gains p0, p1.
+struct TaskPtrs {
+  MPK_GLOBAL const uint16_t* p0;
+  MPK_GLOBAL const uint16_t* p1;
+  MPK_GLOBAL const uint16_t* p2;
+};
+
+// One entry of a worker's ahead-of-time list: the task's descriptor and its
+// resolved weight pointers (refreshed by the host when the weights change),
+// 64 bytes.
+struct alignas(64) AotEntry {
+  DevTask t;
+  TaskPtrs w;
+  uint64_t pad;
+};
+static_assert(sizeof(AotEntry) == 64, "AotEntry must be 64 bytes");
 
 // One linearised event: fires when `counts` triggers arrive (per step);
 // its dependent tasks are [first, last].
@@ -43,7 +77,7 @@ enum { W_IN_NORM = 0, W_Q, W_K, W_V, W_Q_NORM, W_K_NORM, W_O, W_POST_NORM, W_GAT
 // One trace record (layout of mpk_trace_record).
 struct TraceRec {
   int32_t task, worker;
-  uint64_t t_wait, t_start, t_end;
+  uint64_t t_wait, t_start, t_end, t_done;
 };
 
 // Status word written by the kernel (layout of mpk_status_word).
@@ -57,15 +91,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBatch = 16;
 constexpr int kMaxHidden = 8192;
 
-// Device pointers of the argument block are typed as global-address-space
-// pointers in device code (same 64-bit layout as the host's plain pointers),
-// so that every access through them is a global -- not a flat -- memory
-// instruction: flat loads also count against the LDS wait counter.
-#if defined(__HIP_DEVICE_COMPILE__)
-#define MPK_GLOBAL __attribute__((address_space(1)))
-#else
-#define MPK_GLOBAL
-#endif
 
 // Kernel arguments.  One copy lives in device memory per graph (refreshed
 // only when a caller pointer changes); the kernels receive its address, the
@@ -74,8 +99,8 @@ struct KArgs {
   // graph
   MPK_GLOBAL const DevTask* tasks;
   MPK_GLOBAL const DevEvent* events;
-  MPK_GLOBAL const uint32_t* aot_off;
-  MPK_GLOBAL const uint32_t* aot_tasks;
+  MPK_GLOBAL const uint32_t* aot_off;          // [n_workers + 1] offsets into aot_desc
+  MPK_GLOBAL const AotEntry* aot_desc;         // per worker, its AOT tasks in FIFO order
   MPK_GLOBAL uint32_t* ev_cnt;                 // monotonic event counters (target counts * epoch)
   MPK_GLOBAL unsigned long long* sched_ring;   // [n_sched][sched_cap] (seq << 32 | event)
   MPK_GLOBAL uint32_t* sched_tail;             // [n_sched] producer reservation counters

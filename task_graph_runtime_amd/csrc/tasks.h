@@ -178,29 +178,55 @@ __device__ __forceinline__ void norm_task(const KArgs& a, gptr<const float> __re
   }
 }
 
+// ------------------------------------------------------------------ weight pointers
+// The weight base pointers of task t (see TaskPtrs), read from the per-layer
+// pointer table; all loads are issued together.
+__device__ __forceinline__ TaskPtrs task_ptrs(const KArgs& a, const DevTask& t) {
+  TaskPtrs r{};
+  gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)(t.layer < 0 ? 0 : t.layer) * LAYER_PTRS;
+  switch (t.type) {
+    case MPK_TASK_QKV: r.p0 = W[W_Q]; r.p1 = W[W_K]; r.p2 = W[W_V]; break;
+    case MPK_TASK_OPROJ: r.p0 = W[W_O]; break;
+    case MPK_TASK_GATEUP: r.p0 = W[W_GATE]; r.p1 = W[W_UP]; break;
+    case MPK_TASK_DOWN: r.p0 = W[W_DOWN]; break;
+    case MPK_TASK_LMHEAD: r.p0 = a.lm_head ? a.lm_head : a.embed; break;
+    case MPK_TASK_ATTN_NORM: r.p0 = W[W_IN_NORM]; break;
+    case MPK_TASK_MLP_NORM: r.p0 = W[W_POST_NORM]; break;
+    case MPK_TASK_FINAL_NORM: r.p0 = a.final_norm; break;
+    case MPK_TASK_QKNORM_ROPE: r.p0 = W[W_Q_NORM]; r.p1 = W[W_K_NORM]; break;
+    default: break;
+  }
+  return r;
+}
+
 // ------------------------------------------------------------------ projection tiles
 // Row r of the tile's weight rows (output columns [lo, hi); gate/up tiles
-// interleave gate row and up row of each column).
-__device__ __forceinline__ gptr<const uint16_t> gemv_row(const KArgs& a, int type, int l, int lo, int r) {
+// interleave gate row and up row of each column), from the task's weight
+// base pointers: pure arithmetic, no memory access.
+__device__ __forceinline__ gptr<const uint16_t> gemv_row(const KArgs& a, int type, const TaskPtrs& P, int lo,
+                                                         int r) {
   switch (type) {
     case MPK_TASK_QKV: {
-      gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)l * LAYER_PTRS;
       const int col = lo + r, g = col / a.Sg, Gd = a.G * a.d;
       int off = col - g * a.Sg;
-      if (off < Gd) return W[W_Q] + (int64_t)(g * Gd + off) * a.H;
+      if (off < Gd) return P.p0 + (int64_t)(g * Gd + off) * a.H;
       off -= Gd;
-      if (off < a.d) return W[W_K] + (int64_t)(g * a.d + off) * a.H;
+      if (off < a.d) return P.p1 + (int64_t)(g * a.d + off) * a.H;
       off -= a.d;
-      return W[W_V] + (int64_t)(g * a.d + off) * a.H;
+      return P.p2 + (int64_t)(g * a.d + off) * a.H;
     }
     case MPK_TASK_OPROJ:
-      return a.wl[(int64_t)l * LAYER_PTRS + W_O] + (int64_t)(lo + r) * (a.hq * a.d);
-    case MPK_TASK_GATEUP:
-      return a.wl[(int64_t)l * LAYER_PTRS + ((r & 1) ? W_UP : W_GATE)] + (int64_t)(lo + (r >> 1)) * a.H;
+      return P.p0 + (int64_t)(lo + r) * (a.hq * a.d);
+    case MPK_TASK_GATEUP: {
+      // (select between the two pointer values, not between the fields:
+      // a conditional of two lvalues selects an address and keeps P in memory)
+      gptr<const uint16_t> gate = P.p0, up = P.p1;
+      return ((r & 1) ? up : gate) + (int64_t)(lo + (r >> 1)) * a.H;
+    }
     case MPK_TASK_DOWN:
-      return a.wl[(int64_t)l * LAYER_PTRS + W_DOWN] + (int64_t)(lo + r) * a.F;
+      return P.p0 + (int64_t)(lo + r) * a.F;
     default:
-      return (a.lm_head ? a.lm_head : a.embed) + (int64_t)(lo + r) * a.H;
+      return P.p0 + (int64_t)(lo + r) * a.H;
   }
 }
 
@@ -225,18 +251,18 @@ struct SegWalk {
   gptr<const uint16_t> row;
   int r, ks;
 };
-__device__ __forceinline__ SegWalk seg_start(const KArgs& a, const DevTask& t, int nseg, int s) {
+__device__ __forceinline__ SegWalk seg_start(const KArgs& a, const DevTask& t, const TaskPtrs& P, int nseg, int s) {
   SegWalk w;
   w.r = s / nseg;
   w.ks = s - w.r * nseg;
-  w.row = gemv_row(a, t.type, t.layer, t.a0, w.r);
+  w.row = gemv_row(a, t.type, P, t.a0, w.r);
   return w;
 }
-__device__ __forceinline__ void seg_next(const KArgs& a, const DevTask& t, int nseg, SegWalk& w) {
+__device__ __forceinline__ void seg_next(const KArgs& a, const DevTask& t, const TaskPtrs& P, int nseg, SegWalk& w) {
   if (++w.ks == nseg) {
     w.ks = 0;
     ++w.r;
-    w.row = gemv_row(a, t.type, t.layer, t.a0, w.r);
+    w.row = gemv_row(a, t.type, P, t.a0, w.r);
   }
 }
 
@@ -254,9 +280,16 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       }
       break;
     }
-    case MPK_TASK_OPROJ:
+    case MPK_TASK_OPROJ: {
+      gptr<float> out = a.o + (int64_t)l * a.st_bh;
+      for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
+        int b = i / ncol, c = i - b * ncol;
+        out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
+      }
+      break;
+    }
     case MPK_TASK_DOWN: {
-      gptr<float> out = (type == MPK_TASK_OPROJ ? a.o : a.dn) + (int64_t)l * a.st_bh;
+      gptr<float> out = a.dn + (int64_t)l * a.st_bh;
       for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
@@ -316,7 +349,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
 // trips overlap.  Loads are issued unconditionally -- past the end they
 // repeat the last segment -- so the wait counts stay static.
 template <int D>
-__device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, char* lds) {
+__device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
   const GemvOp op = gemv_op(a, t);
   const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc;
   float* xs = reinterpret_cast<float*>(lds + kLdsX);
@@ -326,7 +359,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, char* 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
   const int kl = lane * 8;
-  SegWalk ld = seg_start(a, t, nseg, s_beg < S ? s_beg : S - 1);
+  SegWalk ld = seg_start(a, t, P, nseg, s_beg < S ? s_beg : S - 1);
   int issued = 0;
   uint4 b0[D], b1[D];
   auto issue = [&](uint4 (&b)[D]) {
@@ -334,27 +367,27 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, char* 
     for (int u = 0; u < D; ++u) {
       const int k = min(ld.ks * 512 + kl, K - 8);
       b[u] = ldg<uint4>(ld.row + k);
-      if (issued + 1 < total) seg_next(a, t, nseg, ld);
+      if (issued + 1 < total) seg_next(a, t, P, nseg, ld);
       ++issued;
     }
   };
   if (total > 0) issue(b0);
   for (int i = threadIdx.x; i < nrows; i += kThreads) acc[i] = 0.f;
   {
-    // stage x: every load of the vector is issued before the LDS stores
-    constexpr int XU = (kLdsXFloats / 4 + kThreads - 1) / kThreads;
-    float4 xv[XU];
+    // stage x in chunks of 8 float4 per thread: the chunk's loads are all
+    // issued (from clamped indices) before its LDS stores
     const int n4 = K >> 2;
     gptr<const float4> x4 = reinterpret_cast<gptr<const float4>>(op.x);
+    float4* xs4 = reinterpret_cast<float4*>(xs);
+    for (int base = 0; base < n4; base += 8 * kThreads) {
+      float4 xv[8];
 #pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int i = (int)threadIdx.x + u * kThreads;
-      if (u * kThreads < n4) xv[u] = x4[min(i, n4 - 1)];
-    }
+      for (int u = 0; u < 8; ++u) xv[u] = x4[min(base + u * kThreads + (int)threadIdx.x, n4 - 1)];
 #pragma unroll
-    for (int u = 0; u < XU; ++u) {
-      const int i = (int)threadIdx.x + u * kThreads;
-      if (u * kThreads < n4 && i < n4) reinterpret_cast<float4*>(xs)[i] = xv[u];
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kThreads + (int)threadIdx.x;
+        if (i < n4) xs4[i] = xv[u];
+      }
     }
   }
   __syncthreads();
@@ -399,7 +432,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, char* 
 
 // Batch 2..16 projection tile (VALU): same segment walk, x read from global
 // memory (L2-resident), one fp32 partial per request.
-__device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, char* lds) {
+__device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
   constexpr int U = 4;
   const GemvOp op = gemv_op(a, t);
   const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc, B = a.B;
@@ -411,7 +444,7 @@ __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, char* 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
   if (total > 0) {
-    SegWalk ld = seg_start(a, t, nseg, s_beg);
+    SegWalk ld = seg_start(a, t, P, nseg, s_beg);
     int cur = ld.r, done = 0;
     float av[kMaxBatch];
 #pragma unroll
@@ -424,7 +457,7 @@ __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, char* 
         rr[u] = ld.r;
         kk[u] = ld.ks * 512 + lane * 8;
         wv[u] = ldg<uint4>(ld.row + min(kk[u], K - 8));
-        if (done + u + 1 < total) seg_next(a, t, nseg, ld);
+        if (done + u + 1 < total) seg_next(a, t, P, nseg, ld);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -467,7 +500,7 @@ __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, char* 
 // Task (b, g): the G query heads and the key head of kv group g get per-head
 // RMSNorm (qk_norm) and rotate-half RoPE at position L_b; q goes to the q
 // buffer (fp32), k and v to cache slot L_b of request b (bf16).
-__device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t) {
+__device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t, const TaskPtrs& P) {
   const int b = t.a0, g = t.a1, l = t.layer, d = a.d, half = d >> 1, G = a.G;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int Lb = a.seq_lens[b];
@@ -477,7 +510,6 @@ __device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t) {
   if (!ok && threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, (uint32_t)pid);
   const int64_t slot = ok ? ((((int64_t)l * a.n_pages + pid) * a.hkv + g) * a.P + (Lb % a.P)) * d : 0;
   gptr<const float> src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
-  gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)l * LAYER_PTRS;
   const bool act = lane < half;
   // angle of pair `lane`: L_b * theta^(-2*lane/d); the product and its
   // reduction to [-pi, pi] are done in fp64 (inverse frequencies are computed
@@ -501,7 +533,8 @@ __device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t) {
       continue;
     }
     if (a.qk_norm) {
-      gptr<const uint16_t> gam = W[hh < G ? W_Q_NORM : W_K_NORM];
+      gptr<const uint16_t> gq = P.p0, gk = P.p1;
+      gptr<const uint16_t> gam = hh < G ? gq : gk;
       const int lc = min(lane, half - 1);
       const float g0 = act ? bf2f(gam[lc]) : 0.f, g1 = act ? bf2f(gam[lc + half]) : 0.f;
       const float ss = wave_sum(x0 * x0 + x1 * x1);
@@ -770,41 +803,39 @@ __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
 
 // ------------------------------------------------------------------ dispatch
 // Runs task `task` with the whole workgroup.
-__device__ __forceinline__ void run_task(gptr<const KArgs> ap, int task) {
-  const KArgs a = *ap;
-  const DevTask t = a.tasks[task];
+// Task t with its resolved weight pointers P (task_ptrs).
+__device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const TaskPtrs& P) {
   char* lds = g_lds;
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
   const int l = t.layer;
-  gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)(l < 0 ? 0 : l) * LAYER_PTRS;
   switch (t.type) {
     case MPK_TASK_EMBED:
       embed_task(a);
       break;
     case MPK_TASK_ATTN_NORM:
-      if (l == 0) norm_task(a, a.e, nullptr, a.r, W[W_IN_NORM], a.h, red);
+      if (l == 0) norm_task(a, a.e, nullptr, a.r, P.p0, a.h, red);
       else
         norm_task(a, a.s + (int64_t)(l - 1) * a.st_bh, a.dn + (int64_t)(l - 1) * a.st_bh, a.r + (int64_t)l * a.st_bh,
-                  W[W_IN_NORM], a.h + (int64_t)l * a.st_bh, red);
+                  P.p0, a.h + (int64_t)l * a.st_bh, red);
       break;
     case MPK_TASK_MLP_NORM:
       norm_task(a, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_bh, a.s + (int64_t)l * a.st_bh,
-                W[W_POST_NORM], a.h2 + (int64_t)l * a.st_bh, red);
+                P.p0, a.h2 + (int64_t)l * a.st_bh, red);
       break;
     case MPK_TASK_FINAL_NORM:
-      norm_task(a, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_bh, nullptr, a.final_norm,
-                a.hf, red);
+      norm_task(a, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_bh, nullptr, P.p0, a.hf,
+                red);
       break;
     case MPK_TASK_QKV:
     case MPK_TASK_OPROJ:
     case MPK_TASK_GATEUP:
     case MPK_TASK_DOWN:
     case MPK_TASK_LMHEAD:
-      if (a.B == 1) gemv_b1<8>(a, t, lds);
-      else gemv_bn(a, t, lds);
+      if (a.B == 1) gemv_b1<8>(a, t, P, lds);
+      else gemv_bn(a, t, P, lds);
       break;
     case MPK_TASK_QKNORM_ROPE:
-      rope_task(a, t);
+      rope_task(a, t, P);
       break;
     case MPK_TASK_ATTN:
       if (a.d == 128) {
