@@ -35,6 +35,29 @@ def algorithmic_bytes(s, seq_lens) -> int:
     return 2 * (w + len(seq_lens) * H + kv)
 
 
+DEVICE_SOURCES = ("task_graph_runtime_amd/csrc/megakernel.hip", "task_graph_runtime_amd/csrc/tasks.h",
+                  "task_graph_runtime_amd/csrc/rt.h")
+TRAFFIC_FILE = "profiles/megakernel_{config}_traffic.txt"
+
+
+def measured_traffic(config: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    workload, or None when there is none or the device sources have changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(config=config.replace("qwen3_8b", "qwen3_8b_b1")))
+    if not os.path.exists(path):
+        return None
+    kv = dict(line.strip().split("=", 1) for line in open(path) if "=" in line and " " not in line.strip())
+    h = hashlib.sha256()
+    for src in DEVICE_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None
+    return int(kv["traffic_bytes"])
+
+
 def time_steps(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -174,7 +197,7 @@ def main():
         "baseline_ms": base or None,
         "speedup_vs_baseline": round(min(base.values()) / kern_ms, 3) if base else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
