@@ -83,8 +83,9 @@ typedef struct {
  * the exported header so that a checker can rebuild the same graph. */
 typedef struct {
   int32_t n_workers;     /* W worker workgroups (default: compute units - scheduler WGs) */
-  int32_t n_sched_waves; /* scheduler wavefronts, 4 per scheduler WG (default 16); each  */
-                         /* serves at most 64 workers (checked when the graph uploads)   */
+  int32_t n_sched_waves; /* scheduler wavefronts, 4 per scheduler WG (default: the largest */
+                         /* S <= 16 dividing the worker count; 14 on 256 compute units);  */
+                         /* each serves at most 64 workers (checked when the graph uploads) */
   int32_t quantum;       /* column quantum of projection tiles (default 1 at B=1, else 16) */
   int32_t t_qkv, t_o, t_gu, t_down, t_lm; /* tiles per projection (default ~W; t_qkv a
                                              multiple of n_kv_heads)                    */
@@ -233,6 +234,11 @@ typedef struct {
   uint64_t t_start; /* its dependent event had fired / it was taken from the JIT ring */
   uint64_t t_end;   /* its body finished (before its triggering event is advanced) */
   uint64_t t_done;  /* its triggering event had been advanced (release + add returned) */
+  uint64_t t_mark[2]; /* two points inside the body, 0 where the body has none:
+                         projection tiles: x staged / weight stream done;
+                         attention: page ids and q staged / key loop done;
+                         norms: inputs summed / reduction done;
+                         combine: partials staged / merged; q/k norm + RoPE: inputs read */
 } mpk_trace_record;
 
 /* Turn tracing of mpk_decode_step on (1) or off (0).  Allocates (frees) a
@@ -248,8 +254,10 @@ int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32
  * n) one after another in a single workgroup, each `reps` times, on the
  * arguments and buffers of the last mpk_decode_step call (no events are
  * waited on or advanced), and writes each task's mean duration in clock
- * ticks to ticks[n] (host).  Synchronises. */
-int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, uint64_t* ticks,
+ * ticks to ticks[n] (host).  cold = 1 invalidates the device-scope caches of
+ * the workgroup's die (an agent-scope acquire) right before each run, as a
+ * task started by the persistent kernel sees them.  Synchronises. */
+int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, int32_t cold, uint64_t* ticks,
                    double* ticks_per_us);
 
 /* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it). */

@@ -80,7 +80,7 @@ class mpk_status_word(C.Structure):
 
 class mpk_trace_record(C.Structure):
     _fields_ = [("task", C.c_int32), ("worker", C.c_int32), ("t_wait", C.c_uint64), ("t_start", C.c_uint64),
-                ("t_end", C.c_uint64), ("t_done", C.c_uint64)]
+                ("t_end", C.c_uint64), ("t_done", C.c_uint64), ("t_mark", C.c_uint64 * 2)]
 
 
 # symbol -> (restype, argtypes); the list every test checks against the header
@@ -102,7 +102,7 @@ SIGNATURES = {
     "mpk_set_trace": (C.c_int, [C.c_void_p, C.c_int32]),
     "mpk_read_trace": (C.c_int, [C.c_void_p, C.POINTER(mpk_trace_record), C.c_int32, C.POINTER(C.c_int32),
                                  C.POINTER(C.c_double)]),
-    "mpk_time_tasks": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.POINTER(C.c_uint64),
+    "mpk_time_tasks": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_uint64),
                                  C.POINTER(C.c_double)]),
     "mpk_get_status": (C.c_int, [C.c_void_p, C.POINTER(mpk_status_word)]),
     "mpk_destroy_tgraph": (None, [C.c_void_p]),
@@ -277,17 +277,18 @@ class TGraph:
         tpu = C.c_double()
         _check(lib().mpk_read_trace(self.h, buf, cap, C.byref(n), C.byref(tpu)))
         dt = np.dtype([("task", np.int32), ("worker", np.int32), ("t_wait", np.uint64), ("t_start", np.uint64),
-                       ("t_end", np.uint64), ("t_done", np.uint64)])
+                       ("t_end", np.uint64), ("t_done", np.uint64), ("t_mark", np.uint64, (2,))])
         arr = np.frombuffer(bytes(buf), dtype=dt, count=cap)[: n.value].copy()
         return arr, tpu.value
 
-    def time_tasks(self, tasks, reps: int = 5) -> np.ndarray:
-        """Mean duration (us) of each listed task run alone in one workgroup."""
+    def time_tasks(self, tasks, reps: int = 5, cold: bool = False) -> np.ndarray:
+        """Mean duration (us) of each listed task run alone in one workgroup
+        (cold: caches of its die invalidated before each run)."""
         n = len(tasks)
         T = (C.c_int32 * n)(*[int(t) for t in tasks])
         out = (C.c_uint64 * n)()
         tpu = C.c_double()
-        _check(lib().mpk_time_tasks(self.h, T, n, int(reps), out, C.byref(tpu)))
+        _check(lib().mpk_time_tasks(self.h, T, n, int(reps), int(bool(cold)), out, C.byref(tpu)))
         return np.array(list(out), dtype=np.float64) / tpu.value
 
     def set_watchdog(self, ns: int):

@@ -58,9 +58,18 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   if (p.fusion_order != 0) return uns("only fusion order 0 (Def 4.1 then Def 4.2) is implemented");
   if (p.aot_policy != 0) return uns("only AOT policy 0 (round-robin in linear order) is implemented");
   Params r;
-  r.S_sched = p.n_sched_waves > 0 ? p.n_sched_waves : 16;
-  int32_t sched_wgs = (r.S_sched + 3) / 4;
-  r.W = p.n_workers > 0 ? p.n_workers : n_cus - sched_wgs;
+  // default scheduler count: the largest S <= 16 that divides the worker
+  // count, so that every scheduler deals over the same number of workers
+  // (an event's JIT tasks go to one scheduler's workers)
+  auto workers_for = [&](int32_t S) { return p.n_workers > 0 ? p.n_workers : n_cus - (S + 3) / 4; };
+  if (p.n_sched_waves > 0) {
+    r.S_sched = p.n_sched_waves;
+  } else {
+    r.S_sched = 1;
+    for (int32_t S = 16; S >= 1; --S)
+      if (workers_for(S) > 0 && workers_for(S) % S == 0) { r.S_sched = S; break; }
+  }
+  r.W = workers_for(r.S_sched);
   if (r.W < 1) return bad("no worker workgroups left");
   r.q = p.quantum > 0 ? p.quantum : (B == 1 ? 1 : 16);
   const int64_t G = c.n_q_heads / c.n_kv_heads, d = c.head_dim, Sg = (G + 2) * d;

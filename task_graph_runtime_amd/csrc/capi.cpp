@@ -18,7 +18,7 @@
 namespace mpk {
 hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
 hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count, hipStream_t stream);
-hipError_t launch_time_task(const KArgs& args, int task, unsigned long long* out, hipStream_t stream);
+hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream);
 }  // namespace mpk
 
 using namespace mpk;
@@ -415,6 +415,8 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
     t->h_wl = key;
   }
   KArgs a = t->base;
+  a.poll_sleep = 1;
+  if (const char* ps = std::getenv("MPK_POLL_SLEEP")) a.poll_sleep = std::atoi(ps);   // (experiment)
   a.embed = (const uint16_t*)w->embed;
   a.lm_head = c.tied_embedding ? nullptr : (const uint16_t*)w->lm_head;
   a.final_norm = (const uint16_t*)w->final_norm;
@@ -667,7 +669,7 @@ int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32
     for (uint32_t k = 0; k < std::min<uint32_t>(cnt[w], (uint32_t)g->trace_cap); ++k) {
       if (n < capacity) {
         const TraceRec& r = recs[(size_t)w * g->trace_cap + k];
-        out[n] = mpk_trace_record{r.task, r.worker, r.t_wait, r.t_start, r.t_end, r.t_done};
+        out[n] = mpk_trace_record{r.task, r.worker, r.t_wait, r.t_start, r.t_end, r.t_done, {r.t_mark[0], r.t_mark[1]}};
       }
       ++n;
     }
@@ -676,7 +678,7 @@ int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32
   return n > capacity ? fail(MPK_ERR_INVALID_ARG, "capacity too small") : MPK_OK;
 }
 
-int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, uint64_t* ticks,
+int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, int32_t cold, uint64_t* ticks,
                    double* ticks_per_us) {
   if (!g || !tasks || !ticks || n < 1 || reps < 1) return fail(MPK_ERR_INVALID_ARG, "bad argument");
   if (g->host_only || !g->args_valid) return fail(MPK_ERR_INVALID_ARG, "run mpk_decode_step on this graph first");
@@ -688,7 +690,7 @@ int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps,
   unsigned long long* d_out = (unsigned long long*)buf;
   hipError_t e = hipMemset(d_out, 0, (size_t)n * 8);
   for (int32_t i = 0; i < n && e == hipSuccess; ++i)
-    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) e = launch_time_task(g->last, tasks[i], d_out + i, nullptr);
+    for (int32_t r = 0; r < reps && e == hipSuccess; ++r) e = launch_time_task(g->last, tasks[i], cold != 0, d_out + i, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(ticks, d_out, (size_t)n * 8, hipMemcpyDeviceToHost);
   for (int32_t i = 0; i < n && e == hipSuccess; ++i) ticks[i] /= (uint64_t)reps;

@@ -199,7 +199,7 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
           cmd = CMD_EXIT;
           break;
         }
-        __builtin_amdgcn_s_sleep(1);
+        for (int z = 0; z < a.poll_sleep; ++z) __builtin_amdgcn_s_sleep(1);
       }
       if (cmd != CMD_EXIT) acquire_fence();
       t_start = (uint64_t)wall_clock64();
@@ -223,6 +223,10 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
     }
     const DevTask t = unpack_task(cur_v);
     const TaskPtrs P = unpack_ptrs(cur_v);
+    if (trace && tid == 0) {
+      reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[0] = 0;
+      reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[1] = 0;
+    }
     // the triggering event's record, in flight while the task runs
     const uint32_t ev_v = fetch_words<4>(reinterpret_cast<gptr<const uint32_t>>(a.events + t.trig));
     run_task(a, t, P);
@@ -230,8 +234,10 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
     if (tid < 64) {
       const uint64_t t_end = (uint64_t)wall_clock64();
       trigger(a, epoch, t.trig, unpack_event(ev_v));
-      if (tid == 0 && trace && n_trace < trace_cap)
-        trace[n_trace++] = TraceRec{t.id, w, t_wait, t_start, t_end, (uint64_t)wall_clock64()};
+      if (tid == 0 && trace && n_trace < trace_cap) {
+        const unsigned long long* mk = reinterpret_cast<const unsigned long long*>(g_lds + kLdsMarks);
+        trace[n_trace++] = TraceRec{t.id, w, t_wait, t_start, t_end, (uint64_t)wall_clock64(), {mk[0], mk[1]}};
+      }
     }
   }
   if (tid == 0) {
@@ -322,19 +328,20 @@ __global__ void __launch_bounds__(kThreads) mpk_baseline_op(const KArgs a, const
 }
 
 // Body timing: one workgroup runs one task and adds its wall-clock ticks to *out.
-__global__ void __launch_bounds__(kThreads) mpk_time_task_kernel(const KArgs a, int task,
+__global__ void __launch_bounds__(kThreads) mpk_time_task_kernel(const KArgs a, int task, int cold,
                                                                   unsigned long long* out) {
   const DevTask t = a.tasks[task];
   const TaskPtrs P = task_ptrs(a, t);
   __syncthreads();
+  if (cold) acquire_fence();
   const unsigned long long t0 = wall_clock64();
   run_task(a, t, P);
   __syncthreads();
   if (threadIdx.x == 0) *out += wall_clock64() - t0;
 }
 
-hipError_t launch_time_task(const KArgs& args, int task, unsigned long long* out, hipStream_t stream) {
-  hipLaunchKernelGGL(mpk_time_task_kernel, dim3(1), dim3(kThreads), 0, stream, args, task, out);
+hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream) {
+  hipLaunchKernelGGL(mpk_time_task_kernel, dim3(1), dim3(kThreads), 0, stream, args, task, cold ? 1 : 0, out);
   return hipGetLastError();
 }
 

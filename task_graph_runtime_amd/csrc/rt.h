@@ -78,6 +78,7 @@ enum { W_IN_NORM = 0, W_Q, W_K, W_V, W_Q_NORM, W_K_NORM, W_O, W_POST_NORM, W_GAT
 struct TraceRec {
   int32_t task, worker;
   uint64_t t_wait, t_start, t_end, t_done;
+  uint64_t t_mark[2];
 };
 
 // Status word written by the kernel (layout of mpk_status_word).
@@ -109,6 +110,7 @@ struct KArgs {
   uint32_t sched_cap, jit_cap;
   int32_t n_workers, n_sched, n_sched_wgs;
   int32_t root_event, end_event;
+  int32_t poll_sleep;                          // s_sleep(1) periods between two polls of a waiting worker
   MPK_GLOBAL StatusWord* status;
   MPK_GLOBAL TraceRec* trace;                  // null: tracing off; else [n_workers][trace_cap]
   MPK_GLOBAL uint32_t* trace_count;            // [n_workers] records written in the last step

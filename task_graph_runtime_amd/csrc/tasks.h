@@ -27,6 +27,17 @@ template <typename T>
 using gptr = MPK_GLOBAL T*;
 
 // ------------------------------------------------------------------ helpers
+// The calling thread's index in the workgroup, re-derived at each use.  The
+// persistent kernel runs the task bodies inside its worker loop; an index
+// the compiler can see is loop-invariant gets every per-thread address built
+// from it hoisted out of the loop and held in registers across all tasks,
+// which starves the bodies of registers and serialises their loads.
+__device__ __forceinline__ int tidx() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -85,9 +96,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Sum over the workgroup; `red` is kWaves floats of LDS.  All threads call it.
 __device__ __forceinline__ float block_sum(float v, float* red) {
+  const int tid0 = tidx();
   v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  const int w = tid0 >> 6;
+  if ((tid0 & 63) == 0) red[w] = v;
   __syncthreads();
   float t = 0.f;
 #pragma unroll
@@ -125,56 +137,96 @@ constexpr int kMaxSplitPages = 4096;           // page ids staged per attention 
 // The workgroup's LDS, shared by the runtime loop and every task body.
 __shared__ __attribute__((aligned(16))) char g_lds[kLdsBytes];
 
+// Trace marks: when tracing, thread 0 stamps two points inside a task body
+// into the control area (the worker copies them into the task's record).
+constexpr int kLdsMarks = kLdsCtl + 16;
+__device__ __forceinline__ void mark(const KArgs& a, int k) {
+  const int tid0 = tidx();
+  if (a.trace && tid0 == 0) reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[k] = wall_clock64();
+}
+
+// ------------------------------------------------------------------ staging into LDS
+// Direct global -> LDS loads: every load of a staged vector is issued back to
+// back and none of the data passes through registers, so the copy costs one
+// memory round trip whatever the surrounding register pressure.  Wavefront
+// w copies chunks w, w + 8, ... of 64 lanes x U bytes (U = 16 or 4); units
+// past n re-read the last unit into the tail of the last chunk, so dst needs
+// room for n rounded up to whole chunks.  src and dst are U-byte aligned.
+// The copy is complete after lds_stage_wait().
+using lds_void = __attribute__((address_space(3))) void*;
+template <int U>
+__device__ __forceinline__ void lds_stage(gptr<const void> src, char* dst, int n, int tid) {
+  static_assert(U == 16 || U == 4, "16- or 4-byte units");
+  using unit = typename std::conditional<U == 16, uint4, uint32_t>::type;
+  const int w = tid >> 6, lane = tid & 63;
+  gptr<const unit> su = reinterpret_cast<gptr<const unit>>(src);
+  for (int c = w; c * 64 < n; c += kWaves) {
+    const int u = min(c * 64 + lane, n - 1);
+    __builtin_amdgcn_global_load_lds(su + u, (lds_void)(dst + c * 64 * U), U, 0, 0);
+  }
+}
+__device__ __forceinline__ void lds_stage_wait() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+// bytes of LDS a staged copy of `bytes` occupies (whole 1 KB chunks)
+__device__ __forceinline__ int lds_chunks(int bytes) { return (bytes + 1023) & ~1023; }
+
 // ------------------------------------------------------------------ embedding
 __device__ __forceinline__ void embed_task(const KArgs& a) {
+  const int tid0 = tidx();
   for (int b = 0; b < a.B; ++b) {
     int id = a.token_ids[b];
     if (id < 0 || id >= a.V) {
-      if (threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)id, (uint32_t)a.V);
+      if (tid0 == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)id, (uint32_t)a.V);
       id = 0;
     }
     gptr<const uint16_t> row = a.embed + (int64_t)id * a.H;
-    for (int i = threadIdx.x; i < a.H; i += kThreads) a.e[(int64_t)b * a.H + i] = bf2f(row[i]);
+    for (int i = tid0; i < a.H; i += kThreads) a.e[(int64_t)b * a.H + i] = bf2f(row[i]);
   }
 }
 
 // ------------------------------------------------------------------ residual add + RMSNorm
 // res = x + y (y optional), stored when `res` is given; out = RMSNorm(res) * gamma.
-// All loads of a row are issued before any store.
+// gamma and the input rows are staged in LDS with direct loads (all rows at
+// once when they fit, else one row at a time).
 __device__ __forceinline__ void norm_task(const KArgs& a, gptr<const float> __restrict__ x,
                                           gptr<const float> __restrict__ y, gptr<float> __restrict__ res,
                                           gptr<const uint16_t> __restrict__ gamma, gptr<float> __restrict__ out,
-                                          float* red) {
-  constexpr int J = kMaxHidden / kThreads;
-  const int H = a.H;
-  for (int b = 0; b < a.B; ++b) {
-    float v[J], gm[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int i = threadIdx.x + j * kThreads;
-      v[j] = ld_or(x + (int64_t)b * H, i, H, 0.f);
-      gm[j] = bf2f(ld_or(gamma, i, H, (uint16_t)0));
+                                          char* lds, float* red) {
+  const int tid0 = tidx();
+  const int H = a.H, B = a.B;
+  const int hb = lds_chunks(H * 4), gb = lds_chunks(H * 2);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds + kLdsX);
+  char* xsl = lds + kLdsX + gb;
+  const int rows = (B * 2 * hb + gb <= kLdsXFloats * 4) ? B : 1;
+  lds_stage<16>(gamma, lds + kLdsX, H / 8, tid0);
+  for (int b0 = 0; b0 < B; b0 += rows) {
+    const int nr = min(rows, B - b0);
+    for (int r = 0; r < nr; ++r) {
+      lds_stage<16>(x + (int64_t)(b0 + r) * H, xsl + (2 * r) * hb, H / 4, tid0);
+      if (y) lds_stage<16>(y + (int64_t)(b0 + r) * H, xsl + (2 * r + 1) * hb, H / 4, tid0);
     }
-    if (y) {
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int i = threadIdx.x + j * kThreads;
-        v[j] += ld_or(y + (int64_t)b * H, i, H, 0.f);
+    lds_stage_wait();
+    mark(a, 0);
+    for (int r = 0; r < nr; ++r) {
+      const float* xr = reinterpret_cast<const float*>(xsl + (2 * r) * hb);
+      const float* yr = reinterpret_cast<const float*>(xsl + (2 * r + 1) * hb);
+      float ss = 0.f;
+      for (int i = tid0; i < H; i += kThreads) {
+        const float v = y ? xr[i] + yr[i] : xr[i];
+        ss = fmaf(v, v, ss);
+      }
+      ss = block_sum(ss, red);
+      mark(a, 1);
+      const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+      for (int i = tid0; i < H; i += kThreads) {
+        const float v = y ? xr[i] + yr[i] : xr[i];
+        if (res) res[(int64_t)(b0 + r) * H + i] = v;
+        out[(int64_t)(b0 + r) * H + i] = v * inv * bf2f(gs[i]);
       }
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) ss = fmaf(v[j], v[j], ss);
-    ss = block_sum(ss, red);
-    const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int i = threadIdx.x + j * kThreads;
-      if (i < H) {
-        if (res) res[(int64_t)b * H + i] = v[j];
-        out[(int64_t)b * H + i] = v[j] * inv * gm[j];
-      }
-    }
+    __syncthreads();   // the staging area is refilled by the next group of rows
   }
 }
 
@@ -268,13 +320,14 @@ __device__ __forceinline__ void seg_next(const KArgs& a, const DevTask& t, const
 
 // Epilogue of a projection tile from the LDS accumulators acc[row][B].
 __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, const float* acc, float* red) {
+  const int tid0 = tidx();
   const int type = t.type, l = t.layer, lo = t.a0, ncol = t.a1 - t.a0, B = a.B;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = tid0 >> 6, lane = tid0 & 63;
   switch (type) {
     case MPK_TASK_QKV: {
       const int ld = a.hkv * a.Sg;
       gptr<float> out = a.qkv + (int64_t)l * a.st_qkv;
-      for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
+      for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         out[(int64_t)b * ld + lo + c] = acc[c * B + b];
       }
@@ -282,7 +335,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
     }
     case MPK_TASK_OPROJ: {
       gptr<float> out = a.o + (int64_t)l * a.st_bh;
-      for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
+      for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
       }
@@ -290,7 +343,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
     }
     case MPK_TASK_DOWN: {
       gptr<float> out = a.dn + (int64_t)l * a.st_bh;
-      for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
+      for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
       }
@@ -298,7 +351,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
     }
     case MPK_TASK_GATEUP: {  // SwiGLU: silu(gate) * up
       gptr<float> out = a.a + (int64_t)l * a.st_a;
-      for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
+      for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         float g = acc[(2 * c) * B + b], u = acc[(2 * c + 1) * B + b];
         out[(int64_t)b * a.F + lo + c] = g / (1.0f + expf(-g)) * u;
@@ -306,7 +359,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       break;
     }
     default: {  // LM head: fp32 logits and the tile's (max, argmax) per request
-      for (int i = threadIdx.x; i < ncol * B; i += kThreads) {
+      for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         a.logits[(int64_t)b * a.V + lo + c] = acc[c * B + b];
       }
@@ -314,7 +367,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       for (int b = 0; b < B; ++b) {
         float bv = -INFINITY;
         int bi = INT_MAX;
-        for (int c = threadIdx.x; c < ncol; c += kThreads) {
+        for (int c = tid0; c < ncol; c += kThreads) {
           float v = acc[c * B + b];
           if (v > bv) { bv = v; bi = lo + c; }   // increasing c: first max kept
         }
@@ -326,7 +379,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
         }
         if (lane == 0) { red[w] = bv; redi[w] = bi; }
         __syncthreads();
-        if (threadIdx.x == 0) {
+        if (tid0 == 0) {
           for (int i = 1; i < kWaves; ++i)
             if (red[i] > bv || (red[i] == bv && redi[i] < bi)) { bv = red[i]; bi = redi[i]; }
           a.pmax[b * a.T_lm + t.a2] = PMax{bv, bi};
@@ -350,13 +403,14 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
 // repeat the last segment -- so the wait counts stay static.
 template <int D>
 __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
+  const int tid0 = tidx();
   const GemvOp op = gemv_op(a, t);
   const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc;
   float* xs = reinterpret_cast<float*>(lds + kLdsX);
   float* acc = reinterpret_cast<float*>(lds + kLdsAcc);
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
   const int nseg = (K + 511) >> 9, S = nrows * nseg;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = tid0 >> 6, lane = tid0 & 63;
   const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
   const int kl = lane * 8;
   SegWalk ld = seg_start(a, t, P, nseg, s_beg < S ? s_beg : S - 1);
@@ -372,25 +426,11 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
     }
   };
   if (total > 0) issue(b0);
-  for (int i = threadIdx.x; i < nrows; i += kThreads) acc[i] = 0.f;
-  {
-    // stage x in chunks of 8 float4 per thread: the chunk's loads are all
-    // issued (from clamped indices) before its LDS stores
-    const int n4 = K >> 2;
-    gptr<const float4> x4 = reinterpret_cast<gptr<const float4>>(op.x);
-    float4* xs4 = reinterpret_cast<float4*>(xs);
-    for (int base = 0; base < n4; base += 8 * kThreads) {
-      float4 xv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) xv[u] = x4[min(base + u * kThreads + (int)threadIdx.x, n4 - 1)];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kThreads + (int)threadIdx.x;
-        if (i < n4) xs4[i] = xv[u];
-      }
-    }
-  }
-  __syncthreads();
+  for (int i = tid0; i < nrows; i += kThreads) acc[i] = 0.f;
+  // stage x (fp32) in LDS with direct loads, behind the first weight buffer
+  lds_stage<16>(op.x, reinterpret_cast<char*>(xs), K / 4, tid0);
+  lds_stage_wait();
+  mark(a, 0);
   if (total > 0) {
     int cr = s_beg / nseg, cks = s_beg - cr * nseg;  // consumer position
     int done = 0, cur = cr;
@@ -426,6 +466,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
     const float v = wave_sum(accv);
     if (lane == 0) atomicAdd(&acc[cur], v);
   }
+  mark(a, 1);
   __syncthreads();
   gemv_epilogue(a, t, acc, red);
 }
@@ -433,15 +474,16 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
 // Batch 2..16 projection tile (VALU): same segment walk, x read from global
 // memory (L2-resident), one fp32 partial per request.
 __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
+  const int tid0 = tidx();
   constexpr int U = 4;
   const GemvOp op = gemv_op(a, t);
   const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc, B = a.B;
   float* acc = reinterpret_cast<float*>(lds + kLdsAcc);
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
-  for (int i = threadIdx.x; i < nrows * B; i += kThreads) acc[i] = 0.f;
+  for (int i = tid0; i < nrows * B; i += kThreads) acc[i] = 0.f;
   __syncthreads();
   const int nseg = (K + 511) >> 9, S = nrows * nseg;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = tid0 >> 6, lane = tid0 & 63;
   const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
   if (total > 0) {
     SegWalk ld = seg_start(a, t, P, nseg, s_beg);
@@ -501,13 +543,14 @@ __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, const 
 // RMSNorm (qk_norm) and rotate-half RoPE at position L_b; q goes to the q
 // buffer (fp32), k and v to cache slot L_b of request b (bf16).
 __device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t, const TaskPtrs& P) {
+  const int tid0 = tidx();
   const int b = t.a0, g = t.a1, l = t.layer, d = a.d, half = d >> 1, G = a.G;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = tid0 >> 6, lane = tid0 & 63;
   const int Lb = a.seq_lens[b];
   bool ok = Lb >= 0 && Lb < a.max_seq && Lb / a.P < a.max_pages;
   const int pid = ok ? a.page_table[(int64_t)b * a.max_pages + Lb / a.P] : 0;
   if (!(pid >= 0 && pid < a.n_pages)) ok = false;
-  if (!ok && threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, (uint32_t)pid);
+  if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, (uint32_t)pid);
   const int64_t slot = ok ? ((((int64_t)l * a.n_pages + pid) * a.hkv + g) * a.P + (Lb % a.P)) * d : 0;
   gptr<const float> src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
   const bool act = lane < half;
@@ -521,6 +564,7 @@ __device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t, cons
     const float red_ang = (float)(ang - two_pi * rint(ang / two_pi));
     sincosf(red_ang, &sn, &cs);
   }
+  mark(a, 0);
   for (int hh = w; hh < G + 2; hh += kWaves) {
     const float s0 = src[hh * d + min(lane, half - 1)], s1 = src[hh * d + min(lane, half - 1) + half];
     float x0 = act ? s0 : 0.f;
@@ -571,22 +615,23 @@ __device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t, cons
 // page ids are staged in LDS first.  Output: per head (m, l, o[d]) in fp32.
 template <int D, int R, int GM>
 __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char* lds) {
+  const int tid0 = tidx();
   constexpr int DPL = D / R;            // dims per lane
   constexpr int RPW = 64 / R;           // rows per wavefront
   constexpr int TPI = kWaves * RPW;     // tokens per iteration of the workgroup
   using KV = typename std::conditional<DPL == 8, uint4, typename std::conditional<DPL == 4, uint2, uint32_t>::type>::type;
   const int b = t.a0, g = t.a1, s = t.a2, l = t.layer, G = a.G, P = a.P;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, row = lane / R, lr = lane % R;
+  const int w = tid0 >> 6, lane = tid0 & 63, row = lane / R, lr = lane % R;
   const int Lb = a.seq_lens[b];
   const bool ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
-  if (!ok && threadIdx.x == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, 0u);
+  if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, 0u);
   const int ntok = ok ? Lb + 1 : 0;
   const int nb = (ntok + P - 1) / P;
   const int j0 = (int)((int64_t)s * nb / a.S_attn), j1 = (int)((int64_t)(s + 1) * nb / a.S_attn);
   const int t0 = j0 * P, t1 = min(j1 * P, ntok);
 
   int* pids = reinterpret_cast<int*>(lds + kLdsMisc);   // page ids of pages j0..j1-1
-  for (int j = j0 + (int)threadIdx.x; j < j1; j += kThreads) {
+  for (int j = j0 + tid0; j < j1; j += kThreads) {
     int pid = a.page_table[(int64_t)b * a.max_pages + j];
     if (pid < 0 || pid >= a.n_pages) {
       report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)pid, (uint32_t)a.n_pages);
@@ -609,6 +654,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char
     }
   }
   __syncthreads();
+  mark(a, 0);
   gptr<const uint16_t> kbase = a.k_pool + ((int64_t)l * a.n_pages * a.hkv + g) * P * D + lr * DPL;
   gptr<const uint16_t> vbase = a.v_pool + ((int64_t)l * a.n_pages * a.hkv + g) * P * D + lr * DPL;
   const int64_t page_stride = (int64_t)a.hkv * P * D;
@@ -666,6 +712,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char
       if (good(tok + TPI)) process(k1, v1);
     }
   }
+  mark(a, 1);
   // merge the row states of the wavefront (lanes lr, lr+R, ...)
 #pragma unroll
   for (int msk = R; msk <= 32; msk <<= 1) {
@@ -702,7 +749,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char
   __syncthreads();
   gptr<float> out = a.part + (int64_t)l * a.st_part +
                     (((int64_t)b * a.hkv + g) * a.S_attn + s) * (int64_t)(G * (D + 2));
-  for (int e = threadIdx.x; e < G * D; e += kThreads) {
+  for (int e = tid0; e < G * D; e += kThreads) {
     const int h = e / D, dd = e - h * D;
     float M = -INFINITY;
 #pragma unroll
@@ -729,58 +776,54 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char
 // Task (b, g): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}, M = max_s m_s.
 // The S partial records are staged in LDS first (all loads in flight at once).
 __device__ __forceinline__ void combine_task(const KArgs& a, const DevTask& t, char* lds) {
+  const int tid0 = tidx();
   const int b = t.a0, g = t.a1, l = t.layer, G = a.G, D = a.d, S = a.S_attn;
   const int rec = G * (D + 2);
   gptr<const float> part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)rec;
   gptr<float> out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
   float* st = reinterpret_cast<float*>(lds);
   const int n = S * rec;
-  const bool staged = n <= kLdsXFloats;
+  const bool staged = ((n + 63) & ~63) <= kLdsXFloats;
   if (staged) {
-    constexpr int U = 8;
-    for (int i0 = 0; i0 < n; i0 += U * kThreads) {
-      float v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ld_or(part, i0 + u * kThreads + (int)threadIdx.x, n, 0.f);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * kThreads + (int)threadIdx.x;
-        if (i < n) st[i] = v[u];
-      }
-    }
-    __syncthreads();
+    lds_stage<4>(part, reinterpret_cast<char*>(st), n, tid0);
+    lds_stage_wait();
   }
-  for (int e = threadIdx.x; e < G * D; e += kThreads) {
-    const int h = e / D, dd = e - h * D;
-    auto at = [&](int s_, int k) {
-      return staged ? st[s_ * rec + h * (D + 2) + k] : part[(int64_t)s_ * rec + h * (D + 2) + k];
-    };
-    float M = -INFINITY;
-    for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, at(s_, 0));
-    float L = 0.f, O = 0.f;
-    for (int s_ = 0; s_ < S; ++s_) {
-      const float ms = at(s_, 0);
-      if (ms != -INFINITY) {
-        const float f = __expf(ms - M);
-        L = fmaf(at(s_, 1), f, L);
-        O = fmaf(at(s_, 2 + dd), f, O);
+  mark(a, 0);
+  auto merge = [&](auto at) {
+    for (int e = tid0; e < G * D; e += kThreads) {
+      const int h = e / D, dd = e - h * D;
+      float M = -INFINITY;
+      for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, at(s_ * rec + h * (D + 2)));
+      float L = 0.f, O = 0.f;
+      for (int s_ = 0; s_ < S; ++s_) {
+        const int r0 = s_ * rec + h * (D + 2);
+        const float ms = at(r0);
+        if (ms != -INFINITY) {
+          const float f = __expf(ms - M);
+          L = fmaf(at(r0 + 1), f, L);
+          O = fmaf(at(r0 + 2 + dd), f, O);
+        }
       }
+      out[h * D + dd] = L > 0.f ? O / L : 0.f;
     }
-    out[h * D + dd] = L > 0.f ? O / L : 0.f;
-  }
+  };
+  if (staged) merge([&](int i) { return st[i]; });
+  else merge([&](int i) { return part[i]; });
+  mark(a, 1);
   __syncthreads();
 }
 
 // ------------------------------------------------------------------ final argmax
 // next_ids[b] = argmax over the LM-head tile partials; ties -> lowest index.
 __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
+  const int tid0 = tidx();
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
   int* redi = reinterpret_cast<int*>(red + kWaves);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = tid0 >> 6, lane = tid0 & 63;
   for (int b = 0; b < a.B; ++b) {
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int n = threadIdx.x; n < a.T_lm; n += kThreads) {
+    for (int n = tid0; n < a.T_lm; n += kThreads) {
       const PMax p = a.pmax[b * a.T_lm + n];
       if (p.v > bv || (p.v == bv && p.i < bi)) { bv = p.v; bi = p.i; }
     }
@@ -792,7 +835,7 @@ __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
     }
     if (lane == 0) { red[w] = bv; redi[w] = bi; }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid0 == 0) {
       for (int i = 1; i < kWaves; ++i)
         if (red[i] > bv || (red[i] == bv && redi[i] < bi)) { bv = red[i]; bi = redi[i]; }
       a.next_ids[b] = (bi == INT_MAX) ? 0 : bi;
@@ -813,18 +856,18 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
       embed_task(a);
       break;
     case MPK_TASK_ATTN_NORM:
-      if (l == 0) norm_task(a, a.e, nullptr, a.r, P.p0, a.h, red);
+      if (l == 0) norm_task(a, a.e, nullptr, a.r, P.p0, a.h, lds, red);
       else
         norm_task(a, a.s + (int64_t)(l - 1) * a.st_bh, a.dn + (int64_t)(l - 1) * a.st_bh, a.r + (int64_t)l * a.st_bh,
-                  P.p0, a.h + (int64_t)l * a.st_bh, red);
+                  P.p0, a.h + (int64_t)l * a.st_bh, lds, red);
       break;
     case MPK_TASK_MLP_NORM:
       norm_task(a, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_bh, a.s + (int64_t)l * a.st_bh,
-                P.p0, a.h2 + (int64_t)l * a.st_bh, red);
+                P.p0, a.h2 + (int64_t)l * a.st_bh, lds, red);
       break;
     case MPK_TASK_FINAL_NORM:
       norm_task(a, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_bh, nullptr, P.p0, a.hf,
-                red);
+                lds, red);
       break;
     case MPK_TASK_QKV:
     case MPK_TASK_OPROJ:

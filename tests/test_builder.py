@@ -75,7 +75,8 @@ def test_default_params_resolve_as_documented():
     s = synth.SHAPES["qwen3_8b"]
     h = mpk.TGraph(s.cfg(), 1, 64, {}, host_only=True).header()
     p = h["params"]
-    assert p["n_workers"] == 252 and p["n_sched_waves"] == 16 and p["quantum"] == 1
+    # 14 scheduler wavefronts (4 workgroups) leave 252 workers, 18 per scheduler
+    assert p["n_workers"] == 252 and p["n_sched_waves"] == 14 and p["quantum"] == 1
     assert p["t_qkv"] == 248 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 252 and p["s_attn"] == 16
     h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
     assert h16["quantum"] == 16 and h16["s_attn"] == 4
