@@ -48,14 +48,21 @@ enum {
   MPK_ERR_NOMEM = -6        /* host or device allocation failed */
 };
 
-/* Task types of the decoder tGraph (the order is the program order of one layer). */
+/* Task types of the decoder tGraph (the order is the program order of one layer).
+ * At batch 1 the residual add + RMSNorm of the layer run inside the QKV,
+ * GATEUP and LMHEAD tiles (and the embedding gather inside the layer-0 QKV
+ * tiles), so EMBED and the *_NORM tasks appear at batch > 1 only.  Ids 3 and 5
+ * are not emitted for the decoder: q/k RMSNorm + RoPE + the KV append and the
+ * split combine run inside the ATTN tasks. */
 enum {
   MPK_TASK_EMBED = 0,       /* e[b,:] = E[token_ids[b], :] (fp32)                        */
   MPK_TASK_ATTN_NORM = 1,   /* r = residual in; h = RMSNorm(r) (fp32)                    */
   MPK_TASK_QKV = 2,         /* tile of the fused q/k/v projection (group-major columns)  */
-  MPK_TASK_QKNORM_ROPE = 3, /* per (b, kv group): q/k RMSNorm, RoPE, KV-cache append     */
-  MPK_TASK_ATTN = 4,        /* per (b, kv group, split): paged attention partials (JIT)  */
-  MPK_TASK_COMBINE = 5,     /* per (b, kv group): merge split partials (log-sum-exp)     */
+  MPK_TASK_QKNORM_ROPE = 3, /* (reserved)                                                */
+  MPK_TASK_ATTN = 4,        /* per (b, kv group, split): q/k norm, RoPE, paged attention */
+                            /* partials (JIT); the last split of (b, g) appends the new  */
+                            /* k/v, the last one to finish merges the partials           */
+  MPK_TASK_COMBINE = 5,     /* (reserved)                                                */
   MPK_TASK_OPROJ = 6,       /* tile of the output projection                             */
   MPK_TASK_MLP_NORM = 7,    /* s = r + o; h2 = RMSNorm(s)                                */
   MPK_TASK_GATEUP = 8,      /* tile of gate/up projections with the SwiGLU epilogue      */
@@ -217,12 +224,14 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
                              int32_t use_hipgraph);
 
 /* Copy intermediate tensor `tensor` of the last step to host memory `dst`
- * (`bytes` must equal its size).  All are fp32 [B][...]: ids 0 e[B][H],
- * 1 hf[B][H], 3 pmax[B][t_lm] (fp32 value, int32 index pairs); per layer l,
- * 5 + 13*l + k with k = 0 r, 1 h, 2 qkv (group-major: per kv group its query
- * heads, key head, value head), 3 q (after norm and RoPE), 6 attention
- * partials [B][kv][s_attn][G][2 + head_dim] (max, sum, output), 7 attn,
- * 8 o, 9 s, 10 h2, 11 a, 12 d.  Synchronises the device. */
+ * (`bytes` must equal its size).  All are fp32 [B][...]: ids 3 pmax[B][t_lm]
+ * (fp32 value, int32 index pairs); per layer l, 5 + 13*l + k with k = 0 r
+ * (residual into the layer), 2 qkv (raw projection, group-major: per kv group
+ * its query heads, key head, value head), 6 attention partials
+ * [B][kv][s_attn][G][2 + head_dim] (max, sum, output), 7 attn, 8 o, 9 s
+ * (residual after attention), 11 a, 12 d; at batch > 1 also 0 e[B][H],
+ * 1 hf[B][H], and per layer k = 1 h, 10 h2 (the normalised inputs).
+ * Synchronises the device. */
 int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes);
 
 /* Per-task trace of the persistent kernel: times are the GPU's constant-rate
@@ -235,10 +244,9 @@ typedef struct {
   uint64_t t_end;   /* its body finished (before its triggering event is advanced) */
   uint64_t t_done;  /* its triggering event had been advanced (release + add returned) */
   uint64_t t_mark[2]; /* two points inside the body, 0 where the body has none:
-                         projection tiles: x staged / weight stream done;
-                         attention: page ids and q staged / key loop done;
-                         norms: inputs summed / reduction done;
-                         combine: partials staged / merged; q/k norm + RoPE: inputs read */
+                         projection tiles: x staged (and normalised) / weight stream done;
+                         attention: q normalised and rotated / key loop done;
+                         norms: inputs summed / reduction done */
 } mpk_trace_record;
 
 /* Turn tracing of mpk_decode_step on (1) or off (0).  Allocates (frees) a

@@ -32,8 +32,15 @@ tiles ``[q*floor(n*U/T), min(N, q*floor((n+1)*U/T)))`` with ``U = ceil(N/q)``.
 The fused q/k/v projection writes its columns group-major -- for kv group
 ``g``: its ``G`` query heads, then its key head, then its value head -- and
 is tiled within each group (``T_qkv / n_kv_heads`` tiles per group), so each
-q/k-norm + RoPE task reads one contiguous column block produced by the tiles
-of its own group and no projection tile feeds two groups.
+attention split reads one contiguous column block produced by the tiles of
+its own group and no projection tile feeds two groups.
+
+Operator fusion (a choice of this build, not of the pages; the rewrites
+below apply unchanged to whatever tasks the decomposition emits): q/k
+RMSNorm + RoPE, the KV-cache append and the split combine run inside the
+attention tasks, and at batch 1 the residual add + RMSNorm run inside the
+projection tiles that consume them (``fused_norm``).  Type ids 3
+(QKNORM_ROPE) and 5 (COMBINE) are therefore never emitted for the decoder.
 """
 from __future__ import annotations
 
@@ -42,7 +49,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-# task types
+# task types (3 and 5 are kept as ids for the generic entry; the decoder emits neither)
 EMBED, ATTN_NORM, QKV, QKNORM_ROPE, ATTN, COMBINE, OPROJ, MLP_NORM, GATEUP, DOWN, FINAL_NORM, LMHEAD, ARGMAX, \
     EMPTY = range(14)
 TYPE_NAMES = ["EMBED", "ATTN_NORM", "QKV", "QKNORM_ROPE", "ATTN", "COMBINE", "OPROJ", "MLP_NORM", "GATEUP", "DOWN",
@@ -83,70 +90,91 @@ def _box(tensor, lo, hi):
     return (tensor, lo, hi)
 
 
+def fused_norm(B):
+    """Whether RMSNorm runs inside the projection tiles that consume it.
+
+    At batch 1 every projection tile stages its whole input vector on chip, so
+    the residual add and RMSNorm are recomputed by each consuming tile (a
+    prologue) instead of running as a task of their own; the first tile of
+    the consuming projection also stores the residual for later layers.  At
+    batch > 1 the norms stay tasks (ATTN_NORM, MLP_NORM, FINAL_NORM) and the
+    embedding an EMBED task.
+    """
+    return B == 1
+
+
 def decompose(cfg, B, P, prm: Params):
     """Operators -> tasks with their input/output boxes, in program order.
 
     Returns a list of dicts ``{type, layer, coords, ins, outs}``; a box is
     ``(tensor_id, lo[4], hi[4])`` (half-open).
+
+    Per layer: [ATTN_NORM] QKV tiles, ATTN(b, g, s) [JIT], OPROJ tiles,
+    [MLP_NORM] GATEUP tiles, DOWN tiles; then [FINAL_NORM] LMHEAD tiles and
+    ARGMAX (bracketed tasks only at batch > 1, see ``fused_norm``).  An
+    attention split also applies q/k RMSNorm and RoPE to its query heads, the
+    last split of (b, g) appends the new key/value to the cache, and the last
+    split of (b, g) to finish merges the S partials into the attention output
+    (so every split of (b, g) declares that output).
     """
     L = cfg["n_layers"]; H = cfg["hidden"]; hq = cfg["n_q_heads"]; hkv = cfg["n_kv_heads"]; d = cfg["head_dim"]
     F = cfg["ffn"]; V = cfg["vocab"]; S = prm.S_attn
     G = hq // hkv
     Sg = (G + 2) * d          # qkv columns of one kv group: G q heads, then k, then v
     maxs = cfg["max_seq_len"]
+    fused = fused_norm(B)
     tasks = []
 
     def add(tp, layer, coords, ins, outs):
         c = tuple(coords) + (0,) * (3 - len(coords))
         tasks.append(dict(type=tp, layer=layer, coords=c, ins=ins, outs=outs))
 
-    add(EMBED, -1, (), [], [_box(T_E, (0, 0), (B, H))])
+    full = lambda tn, n: _box(tn, (0, 0), (B, n))
+    if not fused:
+        add(EMBED, -1, (), [], [full(T_E, H)])
     for l in range(L):
         t = lambda k: layer_tensor(l, k)
-        if l == 0:
-            ins = [_box(T_E, (0, 0), (B, H))]
-        else:
-            ins = [_box(layer_tensor(l - 1, L_S), (0, 0), (B, H)), _box(layer_tensor(l - 1, L_D), (0, 0), (B, H))]
-        add(ATTN_NORM, l, (), ins, [_box(t(L_R), (0, 0), (B, H)), _box(t(L_H), (0, 0), (B, H))])
+        prev = [] if l == 0 else [full(layer_tensor(l - 1, L_S), H), full(layer_tensor(l - 1, L_D), H)]
+        if not fused:
+            add(ATTN_NORM, l, (), prev if l else [full(T_E, H)], [full(t(L_R), H), full(t(L_H), H)])
         tpg = prm.T_qkv // hkv
         for n in range(prm.T_qkv):
             g, j = divmod(n, tpg)
             lo, hi = tile_range(Sg, prm.q, tpg, j)
-            add(QKV, l, (n,), [_box(t(L_H), (0, 0), (B, H))], [_box(t(L_QKV), (0, g * Sg + lo), (B, g * Sg + hi))])
-        for b in range(B):
-            for g in range(hkv):
-                ins = [_box(t(L_QKV), (b, g * Sg), (b + 1, (g + 1) * Sg))]
-                outs = [_box(t(L_Q), (b, g * G * d), (b + 1, (g + 1) * G * d)),
-                        _box(t(L_KC), (b, 0, g, 0), (b + 1, maxs, g + 1, d)),
-                        _box(t(L_VC), (b, 0, g, 0), (b + 1, maxs, g + 1, d))]
-                add(QKNORM_ROPE, l, (b, g), ins, outs)
+            outs = [_box(t(L_QKV), (0, g * Sg + lo), (B, g * Sg + hi))]
+            if fused and n == 0:
+                outs.append(full(t(L_R), H))
+            add(QKV, l, (n,), prev if fused else [full(t(L_H), H)], outs)
         for b in range(B):
             for g in range(hkv):
                 for s in range(S):
-                    ins = [_box(t(L_Q), (b, g * G * d), (b + 1, (g + 1) * G * d)),
-                           _box(t(L_KC), (b, 0, g, 0), (b + 1, maxs, g + 1, d)),
-                           _box(t(L_VC), (b, 0, g, 0), (b + 1, maxs, g + 1, d))]
-                    add(ATTN, l, (b, g, s), ins, [_box(t(L_PART), (b, g, s, 0), (b + 1, g + 1, s + 1, G * (d + 2)))])
-        for b in range(B):
-            for g in range(hkv):
-                add(COMBINE, l, (b, g), [_box(t(L_PART), (b, g, 0, 0), (b + 1, g + 1, S, G * (d + 2)))],
-                    [_box(t(L_ATTN), (b, g * G * d), (b + 1, (g + 1) * G * d))])
+                    outs = [_box(t(L_PART), (b, g, s, 0), (b + 1, g + 1, s + 1, G * (d + 2))),
+                            _box(t(L_ATTN), (b, g * G * d), (b + 1, (g + 1) * G * d))]
+                    if s == S - 1:
+                        outs += [_box(t(L_KC), (b, 0, g, 0), (b + 1, maxs, g + 1, d)),
+                                 _box(t(L_VC), (b, 0, g, 0), (b + 1, maxs, g + 1, d))]
+                    add(ATTN, l, (b, g, s), [_box(t(L_QKV), (b, g * Sg), (b + 1, (g + 1) * Sg))], outs)
         for n in range(prm.T_o):
             lo, hi = tile_range(H, prm.q, prm.T_o, n)
-            add(OPROJ, l, (n,), [_box(t(L_ATTN), (0, 0), (B, hq * d))], [_box(t(L_O), (0, lo), (B, hi))])
-        add(MLP_NORM, l, (), [_box(t(L_R), (0, 0), (B, H)), _box(t(L_O), (0, 0), (B, H))],
-            [_box(t(L_S), (0, 0), (B, H)), _box(t(L_H2), (0, 0), (B, H))])
+            add(OPROJ, l, (n,), [full(t(L_ATTN), hq * d)], [_box(t(L_O), (0, lo), (B, hi))])
+        mid = [full(t(L_R), H), full(t(L_O), H)]
+        if not fused:
+            add(MLP_NORM, l, (), mid, [full(t(L_S), H), full(t(L_H2), H)])
         for n in range(prm.T_gu):
             lo, hi = tile_range(F, prm.q, prm.T_gu, n)
-            add(GATEUP, l, (n,), [_box(t(L_H2), (0, 0), (B, H))], [_box(t(L_A), (0, lo), (B, hi))])
+            outs = [_box(t(L_A), (0, lo), (B, hi))]
+            if fused and n == 0:
+                outs.append(full(t(L_S), H))
+            add(GATEUP, l, (n,), mid if fused else [full(t(L_H2), H)], outs)
         for n in range(prm.T_down):
             lo, hi = tile_range(H, prm.q, prm.T_down, n)
-            add(DOWN, l, (n,), [_box(t(L_A), (0, 0), (B, F))], [_box(t(L_D), (0, lo), (B, hi))])
-    add(FINAL_NORM, -1, (), [_box(layer_tensor(L - 1, L_S), (0, 0), (B, H)),
-                             _box(layer_tensor(L - 1, L_D), (0, 0), (B, H))], [_box(T_HF, (0, 0), (B, H))])
+            add(DOWN, l, (n,), [full(t(L_A), F)], [_box(t(L_D), (0, lo), (B, hi))])
+    last = [full(layer_tensor(L - 1, L_S), H), full(layer_tensor(L - 1, L_D), H)]
+    if not fused:
+        add(FINAL_NORM, -1, (), last, [full(T_HF, H)])
     for n in range(prm.T_lm):
         lo, hi = tile_range(V, prm.q, prm.T_lm, n)
-        add(LMHEAD, -1, (n,), [_box(T_HF, (0, 0), (B, H))],
+        add(LMHEAD, -1, (n,), last if fused else [full(T_HF, H)],
             [_box(T_LOGITS, (0, lo), (B, hi)), _box(T_PMAX, (0, n, 0), (B, n + 1, 2))])
     add(ARGMAX, -1, (), [_box(T_PMAX, (0, 0, 0), (B, prm.T_lm, 2))], [_box(T_NEXT, (0,), (B,))])
     return tasks

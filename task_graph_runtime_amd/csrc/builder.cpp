@@ -127,6 +127,7 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
   tasks.clear();
   const int32_t L = c.n_layers, H = c.hidden, hq = c.n_q_heads, hkv = c.n_kv_heads, d = c.head_dim;
   const int32_t F = c.ffn, V = c.vocab, S = p.S_attn, G = hq / hkv, Sg = (G + 2) * d, maxs = c.max_seq_len;
+  const bool fused = fused_norm(B);
   auto add = [&](int32_t type, int32_t layer, int32_t c0, int32_t c1, int32_t c2, std::vector<Box> ins,
                  std::vector<Box> outs) {
     TaskDef t;
@@ -134,60 +135,59 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
     t.ins = std::move(ins); t.outs = std::move(outs);
     tasks.push_back(std::move(t));
   };
-  add(MPK_TASK_EMBED, -1, 0, 0, 0, {}, {box(T_E, {0, 0}, {B, H})});
+  auto full = [&](int32_t tensor, int32_t n) { return box(tensor, {0, 0}, {B, n}); };
+  if (!fused) add(MPK_TASK_EMBED, -1, 0, 0, 0, {}, {full(T_E, H)});
   for (int32_t l = 0; l < L; ++l) {
     auto t = [&](int32_t k) { return layer_tensor(l, k); };
-    std::vector<Box> ins;
-    if (l == 0) ins = {box(T_E, {0, 0}, {B, H})};
-    else ins = {box(layer_tensor(l - 1, L_S), {0, 0}, {B, H}), box(layer_tensor(l - 1, L_D), {0, 0}, {B, H})};
-    add(MPK_TASK_ATTN_NORM, l, 0, 0, 0, ins, {box(t(L_R), {0, 0}, {B, H}), box(t(L_H), {0, 0}, {B, H})});
+    std::vector<Box> prev;
+    if (l > 0) prev = {full(layer_tensor(l - 1, L_S), H), full(layer_tensor(l - 1, L_D), H)};
+    if (!fused)
+      add(MPK_TASK_ATTN_NORM, l, 0, 0, 0, l ? prev : std::vector<Box>{full(T_E, H)}, {full(t(L_R), H), full(t(L_H), H)});
     const int32_t tpg = p.T_qkv / hkv;
     for (int32_t n = 0; n < p.T_qkv; ++n) {
       int32_t g = n / tpg, j = n % tpg, lo, hi;
       tile_range(Sg, p.q, tpg, j, &lo, &hi);
-      add(MPK_TASK_QKV, l, n, 0, 0, {box(t(L_H), {0, 0}, {B, H})}, {box(t(L_QKV), {0, g * Sg + lo}, {B, g * Sg + hi})});
+      std::vector<Box> outs = {box(t(L_QKV), {0, g * Sg + lo}, {B, g * Sg + hi})};
+      if (fused && n == 0) outs.push_back(full(t(L_R), H));
+      add(MPK_TASK_QKV, l, n, 0, 0, fused ? prev : std::vector<Box>{full(t(L_H), H)}, outs);
     }
     for (int32_t b = 0; b < B; ++b)
       for (int32_t g = 0; g < hkv; ++g)
-        add(MPK_TASK_QKNORM_ROPE, l, b, g, 0, {box(t(L_QKV), {b, g * Sg}, {b + 1, (g + 1) * Sg})},
-            {box(t(L_Q), {b, g * G * d}, {b + 1, (g + 1) * G * d}), box(t(L_KC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d}),
-             box(t(L_VC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d})});
-    for (int32_t b = 0; b < B; ++b)
-      for (int32_t g = 0; g < hkv; ++g)
-        for (int32_t s = 0; s < S; ++s)
-          add(MPK_TASK_ATTN, l, b, g, s,
-              {box(t(L_Q), {b, g * G * d}, {b + 1, (g + 1) * G * d}), box(t(L_KC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d}),
-               box(t(L_VC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d})},
-              {box(t(L_PART), {b, g, s, 0}, {b + 1, g + 1, s + 1, G * (d + 2)})});
-    for (int32_t b = 0; b < B; ++b)
-      for (int32_t g = 0; g < hkv; ++g)
-        add(MPK_TASK_COMBINE, l, b, g, 0, {box(t(L_PART), {b, g, 0, 0}, {b + 1, g + 1, S, G * (d + 2)})},
-            {box(t(L_ATTN), {b, g * G * d}, {b + 1, (g + 1) * G * d})});
+        for (int32_t s = 0; s < S; ++s) {
+          std::vector<Box> outs = {box(t(L_PART), {b, g, s, 0}, {b + 1, g + 1, s + 1, G * (d + 2)}),
+                                   box(t(L_ATTN), {b, g * G * d}, {b + 1, (g + 1) * G * d})};
+          if (s == S - 1) {
+            outs.push_back(box(t(L_KC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d}));
+            outs.push_back(box(t(L_VC), {b, 0, g, 0}, {b + 1, maxs, g + 1, d}));
+          }
+          add(MPK_TASK_ATTN, l, b, g, s, {box(t(L_QKV), {b, g * Sg}, {b + 1, (g + 1) * Sg})}, outs);
+        }
     for (int32_t n = 0; n < p.T_o; ++n) {
       int32_t lo, hi;
       tile_range(H, p.q, p.T_o, n, &lo, &hi);
-      add(MPK_TASK_OPROJ, l, n, 0, 0, {box(t(L_ATTN), {0, 0}, {B, hq * d})}, {box(t(L_O), {0, lo}, {B, hi})});
+      add(MPK_TASK_OPROJ, l, n, 0, 0, {full(t(L_ATTN), hq * d)}, {box(t(L_O), {0, lo}, {B, hi})});
     }
-    add(MPK_TASK_MLP_NORM, l, 0, 0, 0, {box(t(L_R), {0, 0}, {B, H}), box(t(L_O), {0, 0}, {B, H})},
-        {box(t(L_S), {0, 0}, {B, H}), box(t(L_H2), {0, 0}, {B, H})});
+    const std::vector<Box> mid = {full(t(L_R), H), full(t(L_O), H)};
+    if (!fused) add(MPK_TASK_MLP_NORM, l, 0, 0, 0, mid, {full(t(L_S), H), full(t(L_H2), H)});
     for (int32_t n = 0; n < p.T_gu; ++n) {
       int32_t lo, hi;
       tile_range(F, p.q, p.T_gu, n, &lo, &hi);
-      add(MPK_TASK_GATEUP, l, n, 0, 0, {box(t(L_H2), {0, 0}, {B, H})}, {box(t(L_A), {0, lo}, {B, hi})});
+      std::vector<Box> outs = {box(t(L_A), {0, lo}, {B, hi})};
+      if (fused && n == 0) outs.push_back(full(t(L_S), H));
+      add(MPK_TASK_GATEUP, l, n, 0, 0, fused ? mid : std::vector<Box>{full(t(L_H2), H)}, outs);
     }
     for (int32_t n = 0; n < p.T_down; ++n) {
       int32_t lo, hi;
       tile_range(H, p.q, p.T_down, n, &lo, &hi);
-      add(MPK_TASK_DOWN, l, n, 0, 0, {box(t(L_A), {0, 0}, {B, F})}, {box(t(L_D), {0, lo}, {B, hi})});
+      add(MPK_TASK_DOWN, l, n, 0, 0, {full(t(L_A), F)}, {box(t(L_D), {0, lo}, {B, hi})});
     }
   }
-  add(MPK_TASK_FINAL_NORM, -1, 0, 0, 0,
-      {box(layer_tensor(L - 1, L_S), {0, 0}, {B, H}), box(layer_tensor(L - 1, L_D), {0, 0}, {B, H})},
-      {box(T_HF, {0, 0}, {B, H})});
+  const std::vector<Box> last = {full(layer_tensor(L - 1, L_S), H), full(layer_tensor(L - 1, L_D), H)};
+  if (!fused) add(MPK_TASK_FINAL_NORM, -1, 0, 0, 0, last, {full(T_HF, H)});
   for (int32_t n = 0; n < p.T_lm; ++n) {
     int32_t lo, hi;
     tile_range(V, p.q, p.T_lm, n, &lo, &hi);
-    add(MPK_TASK_LMHEAD, -1, n, 0, 0, {box(T_HF, {0, 0}, {B, H})},
+    add(MPK_TASK_LMHEAD, -1, n, 0, 0, fused ? last : std::vector<Box>{full(T_HF, H)},
         {box(T_LOGITS, {0, lo}, {B, hi}), box(T_PMAX, {0, n, 0}, {B, n + 1, 2})});
   }
   add(MPK_TASK_ARGMAX, -1, 0, 0, 0, {box(T_PMAX, {0, 0, 0}, {B, p.T_lm, 2})}, {box(T_NEXT, {0}, {B})});

@@ -69,7 +69,17 @@ inline void tile_range(int64_t N, int64_t q, int64_t T, int64_t n, int32_t* lo, 
 int resolve_params(const mpk_model_cfg& cfg, int32_t B, int32_t P, const mpk_build_params* in, int32_t n_cus,
                    Params* out, std::string* err);
 
+// Whether the residual add + RMSNorm run inside the projection tiles that
+// consume them (batch 1: every tile stages its whole input vector on chip),
+// instead of as ATTN_NORM / MLP_NORM / FINAL_NORM tasks (and EMBED).
+inline bool fused_norm(int32_t B) { return B == 1; }
+
 // Program-order tasks of one decode step with their input/output boxes.
+// Per layer: [ATTN_NORM] QKV tiles, ATTN(b, g, s) (JIT; also q/k RMSNorm +
+// RoPE, the KV append in split S-1, and the split combine by the last split
+// of (b, g) to finish), OPROJ tiles, [MLP_NORM] GATEUP tiles, DOWN tiles;
+// then [FINAL_NORM] LMHEAD tiles, ARGMAX.  At batch 1 (fused_norm) the first
+// QKV tile also stores the residual r, the first GATEUP tile the residual s.
 void decompose(const mpk_model_cfg& cfg, int32_t B, const Params& p, std::vector<TaskDef>* tasks);
 
 // Canonicalisation pipeline on arbitrary tasks; MPK_ERR_GRAPH on a cycle.

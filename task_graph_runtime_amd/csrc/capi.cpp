@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <map>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -77,6 +78,8 @@ struct mpk_tgraph {
   unsigned long long* d_jit_ring = nullptr;
   uint32_t* d_state = nullptr;
   StatusWord* d_status = nullptr;
+  uint32_t* d_arrive = nullptr;  // attention split arrivals (0 between steps)
+  int64_t arrive_bytes = 0;
   uint32_t sched_cap = 0, jit_cap = 0;
 
   void* d_act = nullptr;
@@ -148,27 +151,63 @@ int check_runtime_shape(const Graph& g) {
   return MPK_OK;
 }
 
+// Kernel-per-operator lists for the baseline: one operator per (layer, task
+// type), in the program order of its tasks; a list holds its tasks in linear
+// order.
 void build_op_lists(mpk_tgraph* t, std::vector<int32_t>* flat) {
   const Graph& g = t->g;
-  const int32_t L = t->cfg.n_layers, n_ops = 4 + 9 * L;
-  std::vector<std::vector<int32_t>> lists(n_ops);
-  static const int per_layer_idx[] = {-1, 0, 1, 2, 3, 4, 5, 6, 7, 8, -1, -1, -1, -1};
+  std::map<std::pair<int32_t, int32_t>, size_t> idx;
+  std::vector<std::pair<int32_t, std::vector<int32_t>>> lists;  // (first program-order id, tasks)
   for (int32_t i = 0; i < g.NT; ++i) {
-    int ty = g.task_type[i], l = g.task_layer[i], k;
+    const int32_t ty = g.task_type[i];
     if (ty == MPK_TASK_EMPTY) continue;
-    if (ty == MPK_TASK_EMBED) k = 0;
-    else if (ty == MPK_TASK_FINAL_NORM) k = 1 + 9 * L;
-    else if (ty == MPK_TASK_LMHEAD) k = 2 + 9 * L;
-    else if (ty == MPK_TASK_ARGMAX) k = 3 + 9 * L;
-    else k = 1 + 9 * l + per_layer_idx[ty];
-    lists[k].push_back(i);
+    const auto key = std::make_pair((int32_t)g.task_layer[i], ty);
+    auto it = idx.find(key);
+    if (it == idx.end()) {
+      it = idx.emplace(key, lists.size()).first;
+      lists.push_back({g.task_orig[i], {}});
+    }
+    auto& L = lists[it->second];
+    L.first = std::min(L.first, g.task_orig[i]);
+    L.second.push_back(i);
   }
+  std::sort(lists.begin(), lists.end(), [](const auto& a, const auto& b) { return a.first < b.first; });
   t->ops.clear();
   flat->clear();
   for (auto& v : lists) {
-    t->ops.push_back({(int32_t)flat->size(), (int32_t)v.size()});
-    flat->insert(flat->end(), v.begin(), v.end());
+    t->ops.push_back({(int32_t)flat->size(), (int32_t)v.second.size()});
+    flat->insert(flat->end(), v.second.begin(), v.second.end());
   }
+}
+
+// LDS layout of a workgroup (KArgs::lds_*): staging area, projection
+// accumulators, the weight pre-load area (batch 1) and the page ids of an
+// attention split under the runtime's control words at the top.
+int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KArgs* a) {
+  auto chunks = [](int64_t b) { return (b + 1023) & ~(int64_t)1023; };
+  const int64_t H = c.hidden, F = c.ffn, d = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, G = hq / hkv;
+  const bool fused = fused_norm(B);
+  int64_t stage = fused ? std::max({chunks(H * 4), chunks(hq * d * 4), chunks(F * 4), 2 * chunks(H * 4) + chunks(H * 2)})
+                        : chunks(H * 2) + 2 * chunks(H * 4);   // a norm task's gain and one row pair
+  // attention: wavefront merge states, raw q/k/v row, processed heads
+  stage = std::max(stage, chunks(kWaves * G * (d + 2) * 4) + 2 * chunks((G + 2) * d * 4));
+  // the split combine stages its records when they fit in 64 KB (else it reads them from global memory)
+  const int64_t comb = ((p.S_attn * G * (d + 2) + 63) & ~(int64_t)63) * 4;
+  if (comb <= 64 * 1024) stage = std::max(stage, comb);
+  // accumulators: the widest projection tile, rows per column x batch
+  const int64_t tpg = p.T_qkv / hkv, Sg = (G + 2) * d;
+  auto widest = [&](int64_t N, int64_t T) { return p.q * ((((N + p.q - 1) / p.q) + T - 1) / T); };
+  const int64_t acc = chunks(4 * B * std::max({widest(Sg, tpg), widest(H, p.T_o), 2 * widest(F, p.T_gu),
+                                               widest(H, p.T_down), widest(c.vocab, p.T_lm)}));
+  const int64_t max_pages = std::min<int64_t>((c.max_seq_len + P - 1) / P, 4096);
+  const int64_t pid = kLdsBytes - kLdsTop - chunks(4 * max_pages);
+  const int64_t pf = stage + acc;
+  if (pf > pid) return fail(MPK_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
+  a->lds_acc = (int32_t)stage;
+  a->lds_pf = (int32_t)pf;
+  a->lds_pid = (int32_t)pid;
+  a->pf_segs = fused ? (int32_t)std::min<int64_t>(kMaxPfSegs, (pid - pf) / (kPfWaves * 1024)) : 0;
+  return MPK_OK;
 }
 
 int upload(mpk_tgraph* t) {
@@ -240,7 +279,9 @@ int upload(mpk_tgraph* t) {
   const int64_t r_jring = align256(r_stail + (int64_t)S * 4);
   const int64_t r_state = align256(r_jring + (int64_t)W * t->jit_cap * 8);
   const int64_t r_status = align256(r_state + (int64_t)(2 * W + 2 * S) * 4);
-  const int64_t rt_bytes = align256(r_status + (int64_t)sizeof(StatusWord));
+  const int64_t r_arrive = align256(r_status + (int64_t)sizeof(StatusWord));
+  const int64_t rt_bytes =
+      align256(r_arrive + (int64_t)t->cfg.n_layers * t->B * t->cfg.n_kv_heads * 4);
   HIPCHK(hipMalloc(&t->d_rt, rt_bytes));
   HIPCHK(hipMemset(t->d_rt, 0, rt_bytes));
   char* rb = (char*)t->d_rt;
@@ -250,6 +291,8 @@ int upload(mpk_tgraph* t) {
   t->d_jit_ring = (unsigned long long*)(rb + r_jring);
   t->d_state = (uint32_t*)(rb + r_state);
   t->d_status = (StatusWord*)(rb + r_status);
+  t->d_arrive = (uint32_t*)(rb + r_arrive);
+  t->arrive_bytes = rt_bytes - r_arrive;
 
   // activations
   const mpk_model_cfg& c = t->cfg;
@@ -258,11 +301,15 @@ int upload(mpk_tgraph* t) {
   KArgs& a = t->base;
   a.st_bh = B * H; a.st_qkv = B * hkv * Sg; a.st_q = B * hq * d; a.st_part = B * hkv * S_at * G * (d + 2);
   a.st_a = B * F;
+  // batch > 1 only (norm tasks): e, hf, h, h2
+  const bool fused = fused_norm(t->B);
   struct Item { int id; int64_t bytes; };
-  std::vector<Item> items = {{T_E, B * H * 4}, {T_HF, B * H * 4}, {T_PMAX, B * (int64_t)t->prm.T_lm * 8}};
-  const int64_t per_layer_bytes[L_COUNT] = {a.st_bh * 4, a.st_bh * 4, a.st_qkv * 4, a.st_q * 4, 0, 0,
+  std::vector<Item> items = {{T_PMAX, B * (int64_t)t->prm.T_lm * 8}};
+  if (!fused) items.insert(items.begin(), {{T_E, B * H * 4}, {T_HF, B * H * 4}});
+  const int64_t nf = fused ? 0 : 1;
+  const int64_t per_layer_bytes[L_COUNT] = {a.st_bh * 4, nf * a.st_bh * 4, a.st_qkv * 4, 0, 0, 0,
                                             a.st_part * 4, a.st_q * 4, a.st_bh * 4, a.st_bh * 4,
-                                            a.st_bh * 4, a.st_a * 4, a.st_bh * 4};
+                                            nf * a.st_bh * 4, a.st_a * 4, a.st_bh * 4};
   // one contiguous [L][...] block per per-layer tensor kind
   int64_t off = 0;
   std::vector<int64_t> shared_off(5, -1), kind_off(L_COUNT, -1);
@@ -275,20 +322,21 @@ int upload(mpk_tgraph* t) {
   HIPCHK(hipMalloc(&t->d_act, off));
   HIPCHK(hipMemset(t->d_act, 0, off));
   char* ab = (char*)t->d_act;
-  a.e = (float*)(ab + shared_off[T_E]);
-  a.hf = (float*)(ab + shared_off[T_HF]);
-  a.pmax = (PMax*)(ab + shared_off[T_PMAX]);
-  a.r = (float*)(ab + kind_off[L_R]);
-  a.h = (float*)(ab + kind_off[L_H]);
-  a.qkv = (float*)(ab + kind_off[L_QKV]);
-  a.q = (float*)(ab + kind_off[L_Q]);
-  a.part = (float*)(ab + kind_off[L_PART]);
-  a.attn = (float*)(ab + kind_off[L_ATTN]);
-  a.o = (float*)(ab + kind_off[L_O]);
-  a.s = (float*)(ab + kind_off[L_S]);
-  a.h2 = (float*)(ab + kind_off[L_H2]);
-  a.a = (float*)(ab + kind_off[L_A]);
-  a.dn = (float*)(ab + kind_off[L_D]);
+  auto shared = [&](int id) { return shared_off[id] < 0 ? nullptr : (float*)(ab + shared_off[id]); };
+  auto kind = [&](int k) { return kind_off[k] < 0 ? nullptr : (float*)(ab + kind_off[k]); };
+  a.e = shared(T_E);
+  a.hf = shared(T_HF);
+  a.pmax = (PMax*)shared(T_PMAX);
+  a.r = kind(L_R);
+  a.h = kind(L_H);
+  a.qkv = kind(L_QKV);
+  a.part = kind(L_PART);
+  a.attn = kind(L_ATTN);
+  a.o = kind(L_O);
+  a.s = kind(L_S);
+  a.h2 = kind(L_H2);
+  a.a = kind(L_A);
+  a.dn = kind(L_D);
   t->tensors.assign(5 + 13 * (size_t)L, {nullptr, 0});
   for (auto& it : items) t->tensors[it.id] = {ab + shared_off[it.id], it.bytes};
   for (int64_t l = 0; l < L; ++l)
@@ -305,7 +353,9 @@ int upload(mpk_tgraph* t) {
   a.V = c.vocab; a.G = (int32_t)G; a.Sg = (int32_t)Sg; a.B = t->B; a.P = t->P; a.S_attn = t->prm.S_attn;
   a.T_lm = t->prm.T_lm; a.qk_norm = c.qk_norm; a.max_seq = c.max_seq_len; a.eps = c.rms_eps; a.theta = c.rope_theta;
   a.wl = t->d_wl;
-  return MPK_OK;
+  a.arrive = t->d_arrive;
+  a.gemv_d = 4;
+  return lds_layout(c, t->B, t->P, t->prm, &a);
 }
 
 void free_tgraph(mpk_tgraph* t) {
@@ -365,15 +415,15 @@ TaskPtrs host_task_ptrs(const DevTask& d, const std::vector<const void*>& wl, co
   const size_t base = (size_t)(d.layer < 0 ? 0 : d.layer) * LAYER_PTRS;
   auto W = [&](int k) { return (const uint16_t*)wl[base + k]; };
   switch (d.type) {
-    case MPK_TASK_QKV: r.p0 = W(W_Q); r.p1 = W(W_K); r.p2 = W(W_V); break;
+    case MPK_TASK_QKV: r.p0 = W(W_Q); r.p1 = W(W_K); r.p2 = W(W_V); r.p3 = W(W_IN_NORM); break;
     case MPK_TASK_OPROJ: r.p0 = W(W_O); break;
-    case MPK_TASK_GATEUP: r.p0 = W(W_GATE); r.p1 = W(W_UP); break;
+    case MPK_TASK_GATEUP: r.p0 = W(W_GATE); r.p1 = W(W_UP); r.p3 = W(W_POST_NORM); break;
     case MPK_TASK_DOWN: r.p0 = W(W_DOWN); break;
-    case MPK_TASK_LMHEAD: r.p0 = (const uint16_t*)lm; break;
+    case MPK_TASK_LMHEAD: r.p0 = (const uint16_t*)lm; r.p3 = (const uint16_t*)fnorm; break;
     case MPK_TASK_ATTN_NORM: r.p0 = W(W_IN_NORM); break;
     case MPK_TASK_MLP_NORM: r.p0 = W(W_POST_NORM); break;
     case MPK_TASK_FINAL_NORM: r.p0 = (const uint16_t*)fnorm; break;
-    case MPK_TASK_QKNORM_ROPE: r.p0 = W(W_Q_NORM); r.p1 = W(W_K_NORM); break;
+    case MPK_TASK_ATTN: r.p0 = W(W_Q_NORM); r.p1 = W(W_K_NORM); break;
     default: break;
   }
   return r;
@@ -417,6 +467,8 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   KArgs a = t->base;
   a.poll_sleep = 1;
   if (const char* ps = std::getenv("MPK_POLL_SLEEP")) a.poll_sleep = std::atoi(ps);   // (experiment)
+  if (const char* ps = std::getenv("MPK_PF_SEGS")) a.pf_segs = std::min(a.pf_segs, std::atoi(ps));   // (experiment)
+  if (const char* ps = std::getenv("MPK_GEMV_D")) a.gemv_d = std::atoi(ps);   // (experiment)
   a.embed = (const uint16_t*)w->embed;
   a.lm_head = c.tied_embedding ? nullptr : (const uint16_t*)w->lm_head;
   a.final_norm = (const uint16_t*)w->final_norm;
@@ -693,6 +745,9 @@ int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps,
     for (int32_t r = 0; r < reps && e == hipSuccess; ++r) e = launch_time_task(g->last, tasks[i], cold != 0, d_out + i, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(ticks, d_out, (size_t)n * 8, hipMemcpyDeviceToHost);
+  // timed attention splits counted arrivals outside a step: back to 0 for the next step
+  if (e == hipSuccess) e = hipMemset(g->d_arrive, 0, (size_t)g->arrive_bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   for (int32_t i = 0; i < n && e == hipSuccess; ++i) ticks[i] /= (uint64_t)reps;
   (void)hipFree(buf);
   if (e != hipSuccess) return hip_fail(e, "mpk_time_tasks");

@@ -34,10 +34,10 @@ __device__ __forceinline__ uint32_t ld_relaxed(gptr<const uint32_t> p) {
 __device__ __forceinline__ unsigned long long ld_relaxed64(gptr<const unsigned long long> p) {
   return __hip_atomic_load(const_cast<gptr<unsigned long long>>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_release64(gptr<unsigned long long> p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_relaxed64(gptr<unsigned long long> p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 
 __device__ __forceinline__ bool reached(uint32_t cnt, uint32_t target) { return (int32_t)(cnt - target) >= 0; }
 
@@ -54,35 +54,31 @@ __device__ __forceinline__ gptr<uint32_t> st_jit_tail(const KArgs& a) { return a
 __device__ __forceinline__ void push_event(const KArgs& a, int e) {
   const int s = e % a.n_sched;
   const uint32_t pos = __hip_atomic_fetch_add(&a.sched_tail[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  st_release64(&a.sched_ring[(int64_t)s * a.sched_cap + (pos & (a.sched_cap - 1))],
+  st_relaxed64(&a.sched_ring[(int64_t)s * a.sched_cap + (pos & (a.sched_cap - 1))],
                ((unsigned long long)(pos + 1) << 32) | (uint32_t)e);
 }
 
-// One trigger of event e by wavefront 0 of a workgroup whose writes for the
-// trigger are complete (after a barrier).  Lane 0 advances the counter; if
-// this add fires the event, its empty consumers are resolved here, one lane
-// each (each empty task advances its own event: one release fence covers
-// them all), and the fired events with JIT consumers are handed to their
-// scheduler.
+// One trigger of event e by wavefront 0 of a workgroup whose stores for the
+// trigger are complete (every wavefront waited for them before a barrier).
+// Lane 0 advances the counter; if this add fires the event, its empty
+// consumers are resolved here, one lane each (each empty task advances its
+// own event), and the fired events with JIT consumers are handed to their
+// scheduler.  No cache maintenance is needed: the data the events guard is
+// accessed agent-coherently (see tasks.h), the counters atomically.
 __device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e, const DevEvent& ev) {
   const int lane = threadIdx.x & 63;
   uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(&a.ev_cnt[e], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = __hip_atomic_fetch_add(&a.ev_cnt[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
   if (old + 1u != ev.counts * epoch) return;
-  acquire_fence();
   if (ev.flags & MPK_EVENT_HAS_EMPTY) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     for (int t0 = ev.first; t0 <= ev.last; t0 += 64) {
       const int t = t0 + lane;
       if (t <= ev.last) {
         const int f = a.tasks[t].trig;
         const uint32_t o2 = __hip_atomic_fetch_add(&a.ev_cnt[f], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const DevEvent fe = a.events[f];
-        if (o2 + 1u == fe.counts * epoch && (fe.flags & MPK_EVENT_HAS_JIT)) {
-          acquire_fence();
-          push_event(a, f);
-        }
+        if (o2 + 1u == fe.counts * epoch && (fe.flags & MPK_EVENT_HAS_JIT)) push_event(a, f);
       }
     }
   }
@@ -125,6 +121,7 @@ __device__ __forceinline__ TaskPtrs unpack_ptrs(uint32_t v) {
   p.p0 = ptr_words<uint16_t>(v, 8);
   p.p1 = ptr_words<uint16_t>(v, 10);
   p.p2 = ptr_words<uint16_t>(v, 12);
+  p.p3 = ptr_words<uint16_t>(v, 14);
   return p;
 }
 __device__ __forceinline__ DevEvent unpack_event(uint32_t v) {
@@ -140,7 +137,10 @@ __device__ __forceinline__ DevEvent unpack_event(uint32_t v) {
 // per-worker descriptor copies are constant, so the following one is fetched
 // while the current task runs); thread 0 waits for either a JIT task or the
 // next AOT task's event, the workgroup runs the task, and wavefront 0 advances
-// the task's triggering event.
+// the task's triggering event.  Meanwhile wavefronts 1..7 issue the weight
+// pre-load of the next AOT task when it is a batch-1 projection tile
+// (gemv_preload), so its first weight bytes stream in while the worker
+// triggers, waits and runs JIT tasks.
 __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t timeout, int w) {
   const KArgs a0 = *kp;
   int& s_cmd = reinterpret_cast<int*>(g_lds + kLdsCtl)[0];
@@ -161,6 +161,16 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
   const int trace_cap = a0.trace_cap;
   int n_trace = 0;
   uint64_t t_wait = 0, t_start = 0;
+  // index of the AOT task whose weight pre-load has been issued (-1: none)
+  int pre_i = -1;
+  auto preload_next = [&](const KArgs& a) {
+    if (a.pf_segs > 0 && i < n_aot && pre_i != i) {
+      const DevTask nt = unpack_task(nxt_v);
+      if (is_gemv(nt.type) && tid >= 64) gemv_preload(a, nt, unpack_ptrs(nxt_v), g_lds);
+      pre_i = i;
+    }
+  };
+  preload_next(a0);
   while (true) {
     // the arguments are re-read (constant cache) in every iteration rather
     // than held in registers across it
@@ -177,22 +187,23 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
       t_wait = (uint64_t)t0;
       const uint32_t target = nxt_counts * epoch;
       uint32_t cnt = 0;
+      const bool has_aot = i < n_aot;
+      gptr<const uint32_t> cnt_p = &a.ev_cnt[has_aot ? nxt_dep : a.end_event];
+      const uint32_t cnt_target = has_aot ? target : end_target;
       while (true) {
+        // one round trip per poll: the JIT slot, the counter and the status
+        // word are loaded together and checked afterwards
         const unsigned long long slot = ld_relaxed64(&ring[jit_head & (a.jit_cap - 1)]);
+        cnt = ld_relaxed(cnt_p);
+        const uint32_t status = ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code));
         if ((uint32_t)(slot >> 32) == jit_head + 1u) {
           task = (int)(uint32_t)slot;
           ++jit_head;
           cmd = CMD_JIT;
           break;
         }
-        if (i < n_aot) {
-          cnt = ld_relaxed(&a.ev_cnt[nxt_dep]);
-          if (reached(cnt, target)) { cmd = CMD_AOT; break; }
-        } else if (reached(ld_relaxed(&a.ev_cnt[a.end_event]), end_target)) {
-          cmd = CMD_EXIT;
-          break;
-        }
-        if (ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code)) != 0u) { cmd = CMD_EXIT; break; }
+        if (reached(cnt, cnt_target)) { cmd = has_aot ? CMD_AOT : CMD_EXIT; break; }
+        if (status != 0u) { cmd = CMD_EXIT; break; }
         if ((uint64_t)(wall_clock64() - t0) > timeout) {
           report(a, MPK_ERR_TIMEOUT, i < n_aot ? nxt_id : -1, i < n_aot ? nxt_dep : a.end_event,
                  i < n_aot ? cnt : 0u, i < n_aot ? target : end_target);
@@ -201,7 +212,6 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
         }
         for (int z = 0; z < a.poll_sleep; ++z) __builtin_amdgcn_s_sleep(1);
       }
-      if (cmd != CMD_EXIT) acquire_fence();
       t_start = (uint64_t)wall_clock64();
       s_cmd = cmd;
       s_task = task;
@@ -213,8 +223,10 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
     // the task as an AOT entry spread over lanes 0..15 (a JIT task's
     // descriptor with null weight pointers: JIT tasks are attention tasks)
     uint32_t cur_v;
+    bool pre = false;
     if (cmd == CMD_AOT) {
       cur_v = nxt_v;
+      pre = pre_i == i;
       ++i;
       nxt_v = fetch_words<16>(reinterpret_cast<gptr<const uint32_t>>(aot + (i < n_aot ? i : n_aot - 1)));
     } else {
@@ -222,14 +234,16 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
       cur_v = (threadIdx.x & 15) < 8 ? v : 0u;
     }
     const DevTask t = unpack_task(cur_v);
-    const TaskPtrs P = unpack_ptrs(cur_v);
+    // (a JIT task -- attention -- reads its gains through the pointer table)
+    const TaskPtrs P = cmd == CMD_AOT ? unpack_ptrs(cur_v) : task_ptrs(a, t);
     if (trace && tid == 0) {
       reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[0] = 0;
       reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[1] = 0;
     }
     // the triggering event's record, in flight while the task runs
     const uint32_t ev_v = fetch_words<4>(reinterpret_cast<gptr<const uint32_t>>(a.events + t.trig));
-    run_task(a, t, P);
+    run_task(a, t, P, pre);
+    wait_vm<0>();   // the task's stores are complete before its event advances
     __syncthreads();
     if (tid < 64) {
       const uint64_t t_end = (uint64_t)wall_clock64();
@@ -239,6 +253,7 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
         trace[n_trace++] = TraceRec{t.id, w, t_wait, t_start, t_end, (uint64_t)wall_clock64(), {mk[0], mk[1]}};
       }
     }
+    preload_next(a);
   }
   if (tid == 0) {
     st_jit_head(a0)[w] = jit_head;
@@ -251,9 +266,8 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
 // worker in a register.  A popped event's JIT tasks are dealt round-robin
 // (a running cursor over the sub-workers) in rounds of n_sub tasks: in one
 // round every lane writes the slot of its own worker, so a round costs one
-// store per lane in parallel.  One release fence before the rounds orders
-// the slot stores after everything the scheduler has acquired (the workers
-// read the slots relaxed and then fence-acquire).
+// store per lane in parallel.  Ring slots are written and read with relaxed
+// agent-scope atomics.
 __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, uint64_t timeout, int s) {
   const int lane = threadIdx.x & 63;
   const int n_sub = (a.n_workers - s + a.n_sched - 1) / a.n_sched;
@@ -267,13 +281,13 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
   long long t0 = wall_clock64();
   while (true) {
     const unsigned long long slot = ld_relaxed64(&ring[head & (a.sched_cap - 1)]);
+    const uint32_t end_cnt = ld_relaxed(&a.ev_cnt[a.end_event]);
+    const uint32_t status = ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code));
     if ((uint32_t)(slot >> 32) == head + 1u) {
-      acquire_fence();
       const int e = (int)(uint32_t)slot;
       ++head;
       const DevEvent ev = a.events[e];
       const int k = ev.last - ev.first + 1;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       for (int base = 0; base < k; base += n_sub) {
         // task base + j goes to sub-worker (rr + base + j) mod n_sub
         const int r0 = (int)((rr + (uint32_t)base) % (uint32_t)n_sub);
@@ -289,8 +303,8 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
       t0 = wall_clock64();
       continue;
     }
-    if (reached(ld_relaxed(&a.ev_cnt[a.end_event]), end_target)) break;
-    if (ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code)) != 0u) break;
+    if (reached(end_cnt, end_target)) break;
+    if (status != 0u) break;
     if ((uint64_t)(wall_clock64() - t0) > timeout) {
       if (lane == 0) report(a, MPK_ERR_TIMEOUT, -1, a.end_event, 0u, end_target);
       break;
@@ -321,10 +335,16 @@ __global__ void __launch_bounds__(kThreads) mpk_megakernel(const KArgs args, uin
   if (w < a.n_workers) worker_loop(kp, epoch, timeout, w);
 }
 
-// Kernel-per-operator baseline: workgroup i runs task list[i], no events.
+// Kernel-per-operator baseline: workgroup i runs task list[i], no events (a
+// projection tile issues its weight pre-load first, as in the persistent
+// kernel).  A poisoned graph runs nothing.
 __global__ void __launch_bounds__(kThreads) mpk_baseline_op(const KArgs a, const int32_t* list) {
+  if (ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code)) != 0u) return;
   const DevTask t = a.tasks[list[blockIdx.x]];
-  run_task(a, t, task_ptrs(a, t));
+  const TaskPtrs P = task_ptrs(a, t);
+  const bool pre = a.pf_segs > 0 && is_gemv(t.type);
+  if (pre) gemv_preload(a, t, P, g_lds);
+  run_task(a, t, P, pre);
 }
 
 // Body timing: one workgroup runs one task and adds its wall-clock ticks to *out.
@@ -333,7 +353,7 @@ __global__ void __launch_bounds__(kThreads) mpk_time_task_kernel(const KArgs a, 
   const DevTask t = a.tasks[task];
   const TaskPtrs P = task_ptrs(a, t);
   __syncthreads();
-  if (cold) acquire_fence();
+  if (cold) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // cold caches, as after a fenced wait
   const unsigned long long t0 = wall_clock64();
   run_task(a, t, P);
   __syncthreads();

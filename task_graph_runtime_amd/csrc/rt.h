@@ -37,12 +37,14 @@ struct alignas(16) DevTask {
 static_assert(sizeof(DevTask) == 32, "DevTask must be 32 bytes");
 
 // Weight base pointers a task reads (resolved from the per-layer pointer
-// table): QKV q/k/v, GATEUP gate/up, other projections and the LM head p0,
-// norms their gain p0, q/k norm + RoPE the q and k gains p0, p1.
+// table): QKV q/k/v, GATEUP gate/up, other projections and the LM head p0;
+// p3 the gain of the RMSNorm a batch-1 QKV / GATEUP / LM-head tile applies to
+// its input; norm tasks their gain p0; attention the q and k gains p0, p1.
 struct TaskPtrs {
   MPK_GLOBAL const uint16_t* p0;
   MPK_GLOBAL const uint16_t* p1;
   MPK_GLOBAL const uint16_t* p2;
+  MPK_GLOBAL const uint16_t* p3;
 };
 
 // One entry of a worker's ahead-of-time list: the task's descriptor and its
@@ -51,7 +53,6 @@ struct TaskPtrs {
 struct alignas(64) AotEntry {
   DevTask t;
   TaskPtrs w;
-  uint64_t pad;
 };
 static_assert(sizeof(AotEntry) == 64, "AotEntry must be 64 bytes");
 
@@ -89,6 +90,13 @@ struct StatusWord {
 
 constexpr int kThreads = 512;   // threads per workgroup (8 wavefronts)
 constexpr int kWaves = kThreads / 64;
+// LDS of a workgroup: the whole 160 KB of a compute unit.  The top kLdsTop
+// bytes hold the runtime's control words and reduction scratch; the rest is
+// laid out per graph by the host (KArgs::lds_*).
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kLdsTop = 512;
+constexpr int kPfWaves = kWaves - 1;   // wavefronts that pre-load weights (all but the polling one)
+constexpr int kMaxPfSegs = 16;         // pre-loaded 1 KB segments per wavefront, at most
 constexpr int kMaxBatch = 16;
 constexpr int kMaxHidden = 8192;
 
@@ -111,6 +119,13 @@ struct KArgs {
   int32_t n_workers, n_sched, n_sched_wgs;
   int32_t root_event, end_event;
   int32_t poll_sleep;                          // s_sleep(1) periods between two polls of a waiting worker
+  // per-graph LDS layout (bytes): the staging area [0, lds_acc) (activation
+  // vectors, attention merge and combine records), projection accumulators
+  // [lds_acc, lds_pf), the weight pre-load area of pf_segs 1 KB segments for
+  // each of the kPfWaves pre-loading wavefronts at lds_pf (pf_segs = 0: no
+  // pre-load), and an attention split's page ids at lds_pid
+  int32_t lds_acc, lds_pf, pf_segs, lds_pid;
+  int32_t gemv_d;                              // batch-1 projection: segments per register buffer (4 or 8)
   MPK_GLOBAL StatusWord* status;
   MPK_GLOBAL TraceRec* trace;                  // null: tracing off; else [n_workers][trace_cap]
   MPK_GLOBAL uint32_t* trace_count;            // [n_workers] records written in the last step
@@ -135,13 +150,13 @@ struct KArgs {
   MPK_GLOBAL int32_t* next_ids;
   // activations; per-layer tensors are [L][...] with the strides below (elements)
   // (all fp32: only the weights and the KV cache, the caller's formats, are bf16)
+  // (e, hf, h and h2 exist at batch > 1 only, where the norms are tasks)
   MPK_GLOBAL float* e;
   MPK_GLOBAL float* hf;
   MPK_GLOBAL PMax* pmax;
   MPK_GLOBAL float* r;
   MPK_GLOBAL float* h;
   MPK_GLOBAL float* qkv;
-  MPK_GLOBAL float* q;
   MPK_GLOBAL float* part;
   MPK_GLOBAL float* attn;
   MPK_GLOBAL float* o;
@@ -150,6 +165,10 @@ struct KArgs {
   MPK_GLOBAL float* a;
   MPK_GLOBAL float* dn;
   int64_t st_bh, st_qkv, st_q, st_part, st_a;
+  // split arrivals per (layer, request, kv group): the attention split that
+  // brings one to S_attn is the last of its (b, g), merges the partials and
+  // resets it to 0, so it is 0 between steps
+  MPK_GLOBAL uint32_t* arrive;
 };
 
 }  // namespace mpk

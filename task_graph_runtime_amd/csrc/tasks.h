@@ -10,6 +10,12 @@
 // Attention is paged decode attention of one new query per request against
 // its KV pages.  The decoder layer around them is the Qwen3 layer (RMSNorm,
 // per-head q/k RMSNorm, rotate-half RoPE, GQA, SwiGLU).
+//
+// Fused bodies (fewer dependency levels per layer): an attention split also
+// applies q/k RMSNorm + RoPE to its heads, the last split of (b, g) appends
+// the new key/value to the cache, and the last split of (b, g) to finish
+// merges the splits' partials; at batch 1 a QKV / GATEUP / LM-head tile
+// computes the residual add + RMSNorm of its input itself.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,6 +62,50 @@ __device__ __forceinline__ T ldg(MPK_GLOBAL const P* p) {
   return *reinterpret_cast<MPK_GLOBAL const T*>(p);
 }
 
+// ------------------------------------------------------------------ task-to-task data
+// Activations pass between tasks, and so between compute units on different
+// XCDs, whose L2 caches are not coherent with each other.  Instead of
+// release/acquire fences -- a write-back or invalidation of the whole L2 of
+// the XCD, which the 32 compute units of an XCD serialise on -- every access
+// to task-to-task data is agent-coherent by itself (scope bit sc1): stores go
+// through to the device's point of coherence, loads read it.  A producer
+// waits for its stores to complete (s_waitcnt) before it advances an event
+// counter, and a consumer loads the data only after it has seen the counter,
+// so the data it reads is the producer's.  Weights, constant graph records
+// and the KV cache written in earlier steps are read with ordinary cached
+// loads.
+constexpr int kCohAux = 16;   // cache-policy operand of a direct global -> LDS load: sc1
+__device__ __forceinline__ void st_coh(MPK_GLOBAL float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<MPK_GLOBAL uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(MPK_GLOBAL const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<MPK_GLOBAL uint32_t*>(const_cast<MPK_GLOBAL float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// 16-byte buffer load at byte offset `off` of base[0, bytes) (base is
+// wavefront-uniform; a load past `bytes` returns 0 and touches no memory);
+// Coh: agent-coherent (sc1).
+template <bool Coh>
+__device__ __forceinline__ uint4 ld16(MPK_GLOBAL const void* base, int off, int bytes) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(reinterpret_cast<const void*>(base)), 0, bytes, 0x00020000);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, Coh ? kCohAux : 0));
+}
+// Agent-coherent load of p[i..i+4) of the n-element array p.
+__device__ __forceinline__ float4 ld4_coh(MPK_GLOBAL const float* base, int i, int n) {
+  return __builtin_bit_cast(float4, ld16<true>(base, i * 4, n * 4));
+}
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (loads complete in issue order).  Through the builtin, so the
+// compiler's own wait insertion sees it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Element i of p[0..n) or `dflt` when i >= n (n >= 1).  The load itself is
 // unconditional (from a clamped index): a load under a branch makes the
 // compiler wait for it before the join, serialising round trips.
@@ -87,6 +137,14 @@ __device__ __forceinline__ float row_sum(float v) {
   v += dpp<0x140>(v);
   return v;
 }
+// Sum over the wavefront, as a wavefront-uniform value (row sums by DPP, then
+// the four row totals read out of lanes 0, 16, 32, 48).
+__device__ __forceinline__ float wave_total(float v) {
+  v = row_sum(v);
+  const int iv = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) + __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) + __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
+}
 __device__ __forceinline__ float wave_sum(float v) {
   v = row_sum(v);
   v += __shfl_xor(v, 16);
@@ -94,17 +152,31 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Workgroup barrier for LDS data only: the wavefront's LDS operations are
+// complete, its vector-memory loads may stay in flight.  (__syncthreads also
+// orders global memory at workgroup scope, and after direct global -> LDS
+// loads the compiler makes it wait for every outstanding load, which would
+// drain the weight buffers in flight.)  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void bar_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Sum over the workgroup; `red` is kWaves floats of LDS.  All threads call it.
+template <bool LdsOnly = false>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int tid0 = tidx();
   v = wave_sum(v);
   const int w = tid0 >> 6;
   if ((tid0 & 63) == 0) red[w] = v;
-  __syncthreads();
+  if (LdsOnly) bar_lds(); else __syncthreads();
   float t = 0.f;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) t += red[i];
-  __syncthreads();
+  if (LdsOnly) bar_lds(); else __syncthreads();
   return t;
 }
 
@@ -123,14 +195,10 @@ __device__ __forceinline__ void report(const KArgs& a, int32_t code, int32_t tas
   }
 }
 
-// LDS layout of a workgroup (one per compute unit).
-constexpr int kLdsBytes = 160 * 1024;
-constexpr int kLdsX = 0;                       // staged activation vector (fp32), batch 1
-constexpr int kLdsXFloats = 26624;             // 104 KB: the widest K of the supported shapes
-constexpr int kLdsAcc = kLdsXFloats * 4;       // projection accumulators
-constexpr int kLdsAccFloats = 8192;            // 32 KB
-constexpr int kLdsMisc = kLdsAcc + kLdsAccFloats * 4;   // 24 KB: page ids, control, reduction scratch
-constexpr int kLdsCtl = kLdsMisc + 16384;      // runtime control words
+// LDS of a workgroup (one per compute unit): [0, kLdsCtl) is laid out per
+// graph by the host (KArgs::lds_*); the top kLdsTop bytes hold the runtime's
+// control words, the trace marks and 64 words of reduction scratch.
+constexpr int kLdsCtl = kLdsBytes - kLdsTop;   // runtime control words
 constexpr int kLdsRed = kLdsBytes - 256;       // 64 words of reduction scratch
 constexpr int kMaxSplitPages = 4096;           // page ids staged per attention split
 
@@ -154,7 +222,8 @@ __device__ __forceinline__ void mark(const KArgs& a, int k) {
 // room for n rounded up to whole chunks.  src and dst are U-byte aligned.
 // The copy is complete after lds_stage_wait().
 using lds_void = __attribute__((address_space(3))) void*;
-template <int U>
+// Coh: the source is task-to-task data (agent-coherent loads).
+template <int U, bool Coh = false>
 __device__ __forceinline__ void lds_stage(gptr<const void> src, char* dst, int n, int tid) {
   static_assert(U == 16 || U == 4, "16- or 4-byte units");
   using unit = typename std::conditional<U == 16, uint4, uint32_t>::type;
@@ -162,7 +231,7 @@ __device__ __forceinline__ void lds_stage(gptr<const void> src, char* dst, int n
   gptr<const unit> su = reinterpret_cast<gptr<const unit>>(src);
   for (int c = w; c * 64 < n; c += kWaves) {
     const int u = min(c * 64 + lane, n - 1);
-    __builtin_amdgcn_global_load_lds(su + u, (lds_void)(dst + c * 64 * U), U, 0, 0);
+    __builtin_amdgcn_global_load_lds(su + u, (lds_void)(dst + c * 64 * U), U, 0, Coh ? kCohAux : 0);
   }
 }
 __device__ __forceinline__ void lds_stage_wait() {
@@ -182,7 +251,7 @@ __device__ __forceinline__ void embed_task(const KArgs& a) {
       id = 0;
     }
     gptr<const uint16_t> row = a.embed + (int64_t)id * a.H;
-    for (int i = tid0; i < a.H; i += kThreads) a.e[(int64_t)b * a.H + i] = bf2f(row[i]);
+    for (int i = tid0; i < a.H; i += kThreads) st_coh(a.e + (int64_t)b * a.H + i, bf2f(row[i]));
   }
 }
 
@@ -197,15 +266,15 @@ __device__ __forceinline__ void norm_task(const KArgs& a, gptr<const float> __re
   const int tid0 = tidx();
   const int H = a.H, B = a.B;
   const int hb = lds_chunks(H * 4), gb = lds_chunks(H * 2);
-  const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds + kLdsX);
-  char* xsl = lds + kLdsX + gb;
-  const int rows = (B * 2 * hb + gb <= kLdsXFloats * 4) ? B : 1;
-  lds_stage<16>(gamma, lds + kLdsX, H / 8, tid0);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds);
+  char* xsl = lds + gb;
+  const int rows = (B * 2 * hb + gb <= a.lds_acc) ? B : 1;
+  lds_stage<16>(gamma, lds, H / 8, tid0);
   for (int b0 = 0; b0 < B; b0 += rows) {
     const int nr = min(rows, B - b0);
     for (int r = 0; r < nr; ++r) {
-      lds_stage<16>(x + (int64_t)(b0 + r) * H, xsl + (2 * r) * hb, H / 4, tid0);
-      if (y) lds_stage<16>(y + (int64_t)(b0 + r) * H, xsl + (2 * r + 1) * hb, H / 4, tid0);
+      lds_stage<16, true>(x + (int64_t)(b0 + r) * H, xsl + (2 * r) * hb, H / 4, tid0);
+      if (y) lds_stage<16, true>(y + (int64_t)(b0 + r) * H, xsl + (2 * r + 1) * hb, H / 4, tid0);
     }
     lds_stage_wait();
     mark(a, 0);
@@ -222,8 +291,8 @@ __device__ __forceinline__ void norm_task(const KArgs& a, gptr<const float> __re
       const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
       for (int i = tid0; i < H; i += kThreads) {
         const float v = y ? xr[i] + yr[i] : xr[i];
-        if (res) res[(int64_t)(b0 + r) * H + i] = v;
-        out[(int64_t)(b0 + r) * H + i] = v * inv * bf2f(gs[i]);
+        if (res) st_coh(res + (int64_t)(b0 + r) * H + i, v);
+        st_coh(out + (int64_t)(b0 + r) * H + i, v * inv * bf2f(gs[i]));
       }
     }
     __syncthreads();   // the staging area is refilled by the next group of rows
@@ -237,15 +306,15 @@ __device__ __forceinline__ TaskPtrs task_ptrs(const KArgs& a, const DevTask& t) 
   TaskPtrs r{};
   gptr<const gptr<const uint16_t>> W = a.wl + (int64_t)(t.layer < 0 ? 0 : t.layer) * LAYER_PTRS;
   switch (t.type) {
-    case MPK_TASK_QKV: r.p0 = W[W_Q]; r.p1 = W[W_K]; r.p2 = W[W_V]; break;
+    case MPK_TASK_QKV: r.p0 = W[W_Q]; r.p1 = W[W_K]; r.p2 = W[W_V]; r.p3 = W[W_IN_NORM]; break;
     case MPK_TASK_OPROJ: r.p0 = W[W_O]; break;
-    case MPK_TASK_GATEUP: r.p0 = W[W_GATE]; r.p1 = W[W_UP]; break;
+    case MPK_TASK_GATEUP: r.p0 = W[W_GATE]; r.p1 = W[W_UP]; r.p3 = W[W_POST_NORM]; break;
     case MPK_TASK_DOWN: r.p0 = W[W_DOWN]; break;
-    case MPK_TASK_LMHEAD: r.p0 = a.lm_head ? a.lm_head : a.embed; break;
+    case MPK_TASK_LMHEAD: r.p0 = a.lm_head ? a.lm_head : a.embed; r.p3 = a.final_norm; break;
     case MPK_TASK_ATTN_NORM: r.p0 = W[W_IN_NORM]; break;
     case MPK_TASK_MLP_NORM: r.p0 = W[W_POST_NORM]; break;
     case MPK_TASK_FINAL_NORM: r.p0 = a.final_norm; break;
-    case MPK_TASK_QKNORM_ROPE: r.p0 = W[W_Q_NORM]; r.p1 = W[W_K_NORM]; break;
+    case MPK_TASK_ATTN: r.p0 = W[W_Q_NORM]; r.p1 = W[W_K_NORM]; break;
     default: break;
   }
   return r;
@@ -329,7 +398,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       gptr<float> out = a.qkv + (int64_t)l * a.st_qkv;
       for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
-        out[(int64_t)b * ld + lo + c] = acc[c * B + b];
+        st_coh(out + (int64_t)b * ld + lo + c, acc[c * B + b]);
       }
       break;
     }
@@ -337,7 +406,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       gptr<float> out = a.o + (int64_t)l * a.st_bh;
       for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
-        out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
+        st_coh(out + (int64_t)b * a.H + lo + c, acc[c * B + b]);
       }
       break;
     }
@@ -345,7 +414,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       gptr<float> out = a.dn + (int64_t)l * a.st_bh;
       for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
-        out[(int64_t)b * a.H + lo + c] = acc[c * B + b];
+        st_coh(out + (int64_t)b * a.H + lo + c, acc[c * B + b]);
       }
       break;
     }
@@ -354,7 +423,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         float g = acc[(2 * c) * B + b], u = acc[(2 * c + 1) * B + b];
-        out[(int64_t)b * a.F + lo + c] = g / (1.0f + expf(-g)) * u;
+        st_coh(out + (int64_t)b * a.F + lo + c, g / (1.0f + expf(-g)) * u);
       }
       break;
     }
@@ -382,7 +451,9 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
         if (tid0 == 0) {
           for (int i = 1; i < kWaves; ++i)
             if (red[i] > bv || (red[i] == bv && redi[i] < bi)) { bv = red[i]; bi = redi[i]; }
-          a.pmax[b * a.T_lm + t.a2] = PMax{bv, bi};
+          __hip_atomic_store(reinterpret_cast<MPK_GLOBAL unsigned long long*>(a.pmax + b * a.T_lm + t.a2),
+                             ((unsigned long long)(uint32_t)bi << 32) | __float_as_uint(bv), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
       }
@@ -391,81 +462,302 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
   }
 }
 
-// Batch-1 projection tile: y[n] = sum_k x[k] W[n, k] for the tile's columns.
-// The tile's weight rows are cut into 1 KB segments (64 lanes x 8 bf16, one
-// 16-byte load per lane); wavefront w streams the contiguous run of segments
-// [S w / 8, S (w+1) / 8) through two register buffers of D segments (the
-// loads of one buffer are in flight while the other is consumed), keeps one
-// fp32 partial for the current row, and on a row change reduces it across
-// the wavefront (DPP + lane swaps) into the row's LDS accumulator.  The first
-// buffer's loads are issued before x is staged in LDS (fp32), so both round
-// trips overlap.  Loads are issued unconditionally -- past the end they
-// repeat the last segment -- so the wait counts stay static.
-template <int D>
-__device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
+// Segments of a batch-1 projection tile: its rows x ceil(K / 512) weight
+// segments of 1 KB (64 lanes x 8 bf16), numbered row by row.  With pre-load
+// (pre), the first P0 = min(S, 7 pf_segs) segments are the pre-loaded prefix:
+// wavefront w >= 1 holds [pb, pe) = [P0 (w-1) / 7, P0 w / 7) in its LDS
+// pre-load area, filled before the tile's event fired (wavefront 0 polls for
+// events and pre-loads nothing: its poll would wait behind the loads).  The
+// other segments [P0, S) are streamed from HBM in chunks of D segments,
+// handed out dynamically (gemv_b1).
+struct GemvTile {
+  int K, nrows, nseg, S, P0, pb, pe;
+};
+__device__ __forceinline__ GemvTile gemv_tile(const KArgs& a, const DevTask& t, int w, bool pre) {
+  GemvTile r;
+  r.K = t.type == MPK_TASK_OPROJ ? a.hq * a.d : t.type == MPK_TASK_DOWN ? a.F : a.H;
+  r.nrows = (t.a1 - t.a0) * (t.type == MPK_TASK_GATEUP ? 2 : 1);
+  r.nseg = (r.K + 511) >> 9;
+  r.S = r.nrows * r.nseg;
+  r.P0 = (pre && a.pf_segs > 0) ? min(r.S, kPfWaves * min(a.pf_segs, kMaxPfSegs)) : 0;
+  r.pb = w ? (int)((int64_t)r.P0 * (w - 1) / kPfWaves) : 0;
+  r.pe = w ? (int)((int64_t)r.P0 * w / kPfWaves) : 0;
+  return r;
+}
+__device__ __forceinline__ char* pf_slot(const KArgs& a, char* lds, int w, int j) {
+  return lds + a.lds_pf + ((w - 1) * min(a.pf_segs, kMaxPfSegs) + j) * 1024;
+}
+__device__ __forceinline__ bool is_gemv(int type) {
+  return type == MPK_TASK_QKV || type == MPK_TASK_OPROJ || type == MPK_TASK_GATEUP || type == MPK_TASK_DOWN ||
+         type == MPK_TASK_LMHEAD;
+}
+
+// Weight pre-load of a batch-1 projection tile (MPK summary section 5,
+// techniques inventory: cross-task pipelining): each pre-loading wavefront
+// loads its segments [pb, pe) of the tile and writes them to its LDS
+// pre-load area, before the tile's event has fired (the worker calls it
+// right after its previous task).  Wavefront 0 returns at once.  (Through
+// registers, not direct global -> LDS loads: a direct load still counted as
+// outstanding makes the compiler drain every load in flight before each
+// later LDS access, which would serialise the weight streams.)
+__device__ __forceinline__ void gemv_preload(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
   const int tid0 = tidx();
-  const GemvOp op = gemv_op(a, t);
-  const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc;
-  float* xs = reinterpret_cast<float*>(lds + kLdsX);
-  float* acc = reinterpret_cast<float*>(lds + kLdsAcc);
-  float* red = reinterpret_cast<float*>(lds + kLdsRed);
-  const int nseg = (K + 511) >> 9, S = nrows * nseg;
   const int w = tid0 >> 6, lane = tid0 & 63;
-  const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
+  const GemvTile r = gemv_tile(a, t, w, true);
+  const int n = r.pe - r.pb;
+  if (n <= 0) return;
+  SegWalk sw = seg_start(a, t, P, r.nseg, r.pb);
+  uint4 v[kMaxPfSegs];
+#pragma unroll
+  for (int j = 0; j < kMaxPfSegs; ++j) {
+    const int k = min(sw.ks * 512 + lane * 8, r.K - 8);
+    v[j] = ldg<uint4>(sw.row + k);
+    if (r.pb + j + 1 < r.pe) seg_next(a, t, P, r.nseg, sw);
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxPfSegs; ++j)
+    if (j < n) *reinterpret_cast<uint4*>(pf_slot(a, lds, w, j) + lane * 16) = v[j];
+}
+
+// Input vector of a batch-1 projection tile, staged in LDS as fp32 at offset
+// 0.  OPROJ and DOWN take theirs as is (attention output, SwiGLU output);
+// QKV, GATEUP and the LM head apply the residual add + RMSNorm of the layer
+// first:  v = E[token] (QKV of layer 0), s_{l-1} + d_{l-1} (QKV of layer l),
+// r_l + o_l (GATEUP), s_{L-1} + d_{L-1} (LM head);
+// x = v / sqrt(mean(v^2) + eps) * gamma.  Tile 0 of QKV / GATEUP also
+// stores v: the residual r_l / s_l that later layers add to.
+// xs_issue stages the inputs in LDS with direct global -> LDS loads
+// (agent-coherent for task-to-task data); xs_finish, once they have landed,
+// computes x in place.
+struct XSrc {
+  gptr<const float> v1, v2;     // fp32 summands (v2 may be null)
+  gptr<const uint16_t> emb;     // bf16 embedding row instead of v1 (layer-0 QKV)
+  gptr<float> res;              // where to store v, or null
+  bool norm;
+};
+__device__ __forceinline__ XSrc gemv_xsrc(const KArgs& a, const DevTask& t, const TaskPtrs& P) {
+  const int l = t.layer;
+  XSrc x{nullptr, nullptr, nullptr, nullptr, true};
+  switch (t.type) {
+    case MPK_TASK_QKV:
+      if (l == 0) {
+        int id = a.token_ids[0];
+        if (id < 0 || id >= a.V) {
+          if (tidx() == 0) report(a, MPK_ERR_INVALID_ARG, t.id, -1, (uint32_t)id, (uint32_t)a.V);
+          id = 0;
+        }
+        x.emb = a.embed + (int64_t)id * a.H;
+      } else {
+        x.v1 = a.s + (int64_t)(l - 1) * a.st_bh;
+        x.v2 = a.dn + (int64_t)(l - 1) * a.st_bh;
+      }
+      if (t.a2 == 0) x.res = a.r + (int64_t)l * a.st_bh;
+      break;
+    case MPK_TASK_GATEUP:
+      x.v1 = a.r + (int64_t)l * a.st_bh;
+      x.v2 = a.o + (int64_t)l * a.st_bh;
+      if (t.a2 == 0) x.res = a.s + (int64_t)l * a.st_bh;
+      break;
+    case MPK_TASK_LMHEAD:
+      x.v1 = a.s + (int64_t)(a.L - 1) * a.st_bh;
+      x.v2 = a.dn + (int64_t)(a.L - 1) * a.st_bh;
+      break;
+    case MPK_TASK_OPROJ:
+      x.v1 = a.attn + (int64_t)l * a.st_q;
+      x.norm = false;
+      break;
+    default:  // DOWN
+      x.v1 = a.a + (int64_t)l * a.st_a;
+      x.norm = false;
+      break;
+  }
+  return x;
+}
+__device__ __forceinline__ void xs_issue(const KArgs& a, const XSrc& x, int K, const TaskPtrs& P, char* lds) {
+  const int tid0 = tidx();
+  if (!x.norm) {
+    lds_stage<16, true>(x.v1, lds, K / 4, tid0);
+    return;
+  }
+  const int H = a.H, hb = lds_chunks(H * 4);
+  if (x.emb) lds_stage<16>(x.emb, lds + hb, H / 8, tid0);
+  else lds_stage<16, true>(x.v1, lds, H / 4, tid0);
+  if (x.v2) lds_stage<16, true>(x.v2, lds + hb, H / 4, tid0);
+  lds_stage<16>(P.p3, lds + 2 * hb, H / 8, tid0);
+}
+__device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* lds, float* red) {
+  if (!x.norm) return;
+  const int tid0 = tidx();
+  const int H = a.H, hb = lds_chunks(H * 4);
+  float* xs = reinterpret_cast<float*>(lds);
+  const float* x2 = reinterpret_cast<const float*>(lds + hb);
+  const uint16_t* e16 = reinterpret_cast<const uint16_t*>(lds + hb);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds + 2 * hb);
+  constexpr int NV = kMaxHidden / kThreads;
+  float v[NV];
+  if (x.emb) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = bf2f(e16[min(tid0 + j * kThreads, H - 1)]);
+  } else if (x.v2) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = min(tid0 + j * kThreads, H - 1);
+      v[j] = xs[i] + x2[i];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = xs[min(tid0 + j * kThreads, H - 1)];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    if (tid0 + j * kThreads < H) ss = fmaf(v[j], v[j], ss);
+  ss = block_sum<true>(ss, red);
+  const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = tid0 + j * kThreads;
+    if (i < H) {
+      xs[i] = v[j] * inv * bf2f(gs[i]);
+      if (x.res) st_coh(x.res + i, v[j]);
+    }
+  }
+  bar_lds();
+}
+
+// Batch-1 projection tile: y[n] = sum_k x[k] W[n, k] for the tile's columns.
+// Each wavefront first consumes its pre-loaded segments (gemv_tile), then
+// streams chunks of D segments through two register buffers (the loads of
+// one chunk are in flight while the other is consumed).  The streamed part
+// [P0, S) is cut into nch chunks: the first 8 n_st are static -- wavefront w
+// takes the contiguous run [w n_st, (w+1) n_st) -- and the rest, the tail, is
+// claimed chunk by chunk from an LDS counter, so that wavefronts served
+// faster by the memory system take more of it and all finish together.  A
+// lane takes 8 weights per segment (one 16-byte load) against x staged in LDS
+// (fp32) and keeps one fp32 partial, reduced across the wavefront into the
+// row's LDS accumulator when the row changes.  The staging loads of x go out
+// first and the first chunk's loads right behind them, so both round trips
+// overlap; the wait for x leaves that chunk in flight.  Loads past the tile's
+// last segment repeat it, so the wait counts stay static.
+template <int D>
+__device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds, bool pre) {
+  const int tid0 = tidx();
+  const int lane = tid0 & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // (wavefront-uniform: scalar control flow)
+  const GemvTile r = gemv_tile(a, t, w, pre);
+  const int K = r.K, nrows = r.nrows, nseg = r.nseg, S = r.S, P0 = r.P0;
+  const int nch = (S - P0 + D - 1) / D;            // streamed chunks
+  // static chunks per wavefront (a run of at least 2, or none)
+  const int n_st = nch / kWaves - 2 >= 2 ? nch / kWaves - 2 : 0;
+  const float inv_nseg = 1.0f / (float)nseg;
+  float* xs = reinterpret_cast<float*>(lds);
+  float* acc = reinterpret_cast<float*>(lds + a.lds_acc);
+  float* red = reinterpret_cast<float*>(lds + kLdsRed);
+  int* ctr = reinterpret_cast<int*>(lds + kLdsCtl) + 3;   // tail chunks claimed so far
   const int kl = lane * 8;
-  SegWalk ld = seg_start(a, t, P, nseg, s_beg < S ? s_beg : S - 1);
-  int issued = 0;
+  const XSrc xsrc = gemv_xsrc(a, t, P);
+  xs_issue(a, xsrc, K, P, lds);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);   // the staging loads stay ahead of the weight loads (counted waits)
+  // segment s -> (row, segment within the row) without an integer division
+  auto split = [&](int s0, int& row, int& ks) {
+    row = (int)(((float)s0 + 0.5f) * inv_nseg);
+    ks = s0 - row * nseg;
+  };
   uint4 b0[D], b1[D];
-  auto issue = [&](uint4 (&b)[D]) {
+  // (a chunk past the last one re-reads the last: issues and consumes stay
+  // unconditional, so the compiler can tell which buffer's loads are the
+  // older ones and places exact waits)
+  auto issue = [&](uint4 (&b)[D], int c) {
+    const int s0 = P0 + min(c, nch - 1) * D;
+    SegWalk ld;
+    split(s0, ld.r, ld.ks);
+    ld.row = gemv_row(a, t.type, P, t.a0, ld.r);
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int k = min(ld.ks * 512 + kl, K - 8);
       b[u] = ldg<uint4>(ld.row + k);
-      if (issued + 1 < total) seg_next(a, t, P, nseg, ld);
-      ++issued;
+      if (s0 + u + 1 < S) seg_next(a, t, P, nseg, ld);
     }
   };
-  if (total > 0) issue(b0);
-  for (int i = tid0; i < nrows; i += kThreads) acc[i] = 0.f;
-  // stage x (fp32) in LDS with direct loads, behind the first weight buffer
-  lds_stage<16>(op.x, reinterpret_cast<char*>(xs), K / 4, tid0);
-  lds_stage_wait();
-  mark(a, 0);
-  if (total > 0) {
-    int cr = s_beg / nseg, cks = s_beg - cr * nseg;  // consumer position
-    int done = 0, cur = cr;
-    float accv = 0.f;
-    auto consume = [&](const uint4 (&b)[D]) {
-#pragma unroll
-      for (int u = 0; u < D; ++u) {
-        if (done < total) {
-          if (cr != cur) {
-            const float v = wave_sum(accv);
-            if (lane == 0) atomicAdd(&acc[cur], v);
-            accv = 0.f;
-            cur = cr;
-          }
-          const int k = cks * 512 + kl;
-          if (k < K) {
-            const float4* xp = reinterpret_cast<const float4*>(xs + k);
-            accv = dot8(b[u], xp[0], xp[1], accv);
-          }
-          if (++cks == nseg) { cks = 0; ++cr; }
-          ++done;
-        }
-      }
-    };
-    while (true) {
-      issue(b1);
-      consume(b0);
-      if (done >= total) break;
-      issue(b0);
-      consume(b1);
-      if (done >= total) break;
+  // fp32 partial of the current row, reduced into its accumulator on a change
+  int cur = -1;
+  float accv = 0.f;
+  auto flush = [&]() {
+    const float v = wave_total(accv);
+    if (lane == 0 && cur >= 0) atomicAdd(&acc[cur], v);
+    accv = 0.f;
+  };
+  // segment (row, ks) of weights wv; a segment past the tile (valid false)
+  // adds nothing
+  auto eat = [&](const uint4& wv, int row, int ks, bool valid) {
+    if (valid && row != cur) {
+      flush();
+      cur = row;
     }
-    const float v = wave_sum(accv);
-    if (lane == 0) atomicAdd(&acc[cur], v);
+    const int k = min(ks * 512 + kl, K - 8);
+    const float4* xp = reinterpret_cast<const float4*>(xs + k);
+    const float d = dot8(wv, xp[0], xp[1], 0.f);
+    accv += (valid && ks * 512 + kl < K) ? d : 0.f;
+  };
+  auto consume = [&](const uint4 (&b)[D], int c) {
+    const int s0 = P0 + c * D;
+    int row, ks;
+    split(min(s0, S - 1), row, ks);
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const bool valid = s0 + u < S;
+      eat(b[u], row, ks, valid);
+      if (valid && ++ks == nseg) { ks = 0; ++row; }
+    }
+  };
+  // the wavefront's chunk sequence: its static run, then claimed tail chunks.
+  // Its first two chunks are fixed -- the start of its static run, or tail
+  // chunks w and w + 8 when there is none -- so both buffers are in flight
+  // before the counter is set up; claims continue after those.
+  int st_i = 2;
+  auto next_chunk = [&]() {
+    if (st_i < n_st) return w * n_st + st_i++;
+    int c = 0;
+    if (lane == 0) c = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return kWaves * n_st + (n_st > 0 ? 0 : 2 * kWaves) + __builtin_amdgcn_readfirstlane(c);
+  };
+  int c0 = n_st > 0 ? w * n_st : w;
+  int c1 = n_st > 0 ? w * n_st + 1 : w + kWaves;
+  if (nch > 0) {   // behind the loads of x: the round trips overlap
+    issue(b0, c0);
+    issue(b1, c1);
   }
+  for (int i = tid0; i < nrows; i += kThreads) acc[i] = 0.f;
+  if (tid0 == 0) *ctr = 0;
+  if (nch > 0) wait_vm<2 * D>();   // the staging landed; both chunks may still be in flight
+  else wait_vm<0>();
+  bar_lds();
+  xs_finish(a, xsrc, lds, red);
+  mark(a, 0);
+  if (r.pe > r.pb) {   // the pre-loaded prefix
+    int row, ks;
+    split(r.pb, row, ks);
+    for (int j = 0; j < r.pe - r.pb; ++j) {
+      eat(*reinterpret_cast<const uint4*>(pf_slot(a, lds, w, j) + lane * 16), row, ks, true);
+      if (++ks == nseg) { ks = 0; ++row; }
+    }
+  }
+  // both buffers stay in flight: consume the older chunk, then refill its
+  // buffer; chunk numbers only grow, so once the older pending chunk is past
+  // the end, so is the other
+  if (nch > 0) {
+    while (c0 < nch) {
+      consume(b0, c0);
+      c0 = next_chunk();
+      issue(b0, c0);
+      if (c1 >= nch) break;
+      consume(b1, c1);
+      c1 = next_chunk();
+      issue(b1, c1);
+    }
+  }
+  flush();
   mark(a, 1);
   __syncthreads();
   gemv_epilogue(a, t, acc, red);
@@ -478,7 +770,7 @@ __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, const 
   constexpr int U = 4;
   const GemvOp op = gemv_op(a, t);
   const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc, B = a.B;
-  float* acc = reinterpret_cast<float*>(lds + kLdsAcc);
+  float* acc = reinterpret_cast<float*>(lds + a.lds_acc);
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
   for (int i = tid0; i < nrows * B; i += kThreads) acc[i] = 0.f;
   __syncthreads();
@@ -519,8 +811,8 @@ __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, const 
 #pragma unroll
             for (int b = 0; b < kMaxBatch; ++b)
               if (b < B) {
-                gptr<const float> xr = op.x + (int64_t)b * K + kk[u];
-                av[b] = dot8(wv[u], ldg<float4>(xr), ldg<float4>(xr + 4), av[b]);
+                gptr<const float> xr = op.x + (int64_t)b * K;
+                av[b] = dot8(wv[u], ld4_coh(xr, kk[u], K), ld4_coh(xr, kk[u] + 4, K), av[b]);
               }
           }
           ++done;
@@ -538,142 +830,184 @@ __device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, const 
   gemv_epilogue(a, t, acc, red);
 }
 
-// ------------------------------------------------------------------ q/k RMSNorm + RoPE + KV append
-// Task (b, g): the G query heads and the key head of kv group g get per-head
-// RMSNorm (qk_norm) and rotate-half RoPE at position L_b; q goes to the q
-// buffer (fp32), k and v to cache slot L_b of request b (bf16).
-__device__ __forceinline__ void rope_task(const KArgs& a, const DevTask& t, const TaskPtrs& P) {
+// ------------------------------------------------------------------ paged attention, one split
+// Merge of the S_attn partial records (m, l, o[D]) of (b, g) into the
+// attention output: o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M},
+// M = max_s m_s (empty splits carry m = -inf, l = 0).  Run by the split that
+// finishes last.  The records are staged in LDS first when they fit.
+__device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g, char* lds) {
   const int tid0 = tidx();
-  const int b = t.a0, g = t.a1, l = t.layer, d = a.d, half = d >> 1, G = a.G;
-  const int w = tid0 >> 6, lane = tid0 & 63;
-  const int Lb = a.seq_lens[b];
-  bool ok = Lb >= 0 && Lb < a.max_seq && Lb / a.P < a.max_pages;
-  const int pid = ok ? a.page_table[(int64_t)b * a.max_pages + Lb / a.P] : 0;
-  if (!(pid >= 0 && pid < a.n_pages)) ok = false;
-  if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, (uint32_t)pid);
-  const int64_t slot = ok ? ((((int64_t)l * a.n_pages + pid) * a.hkv + g) * a.P + (Lb % a.P)) * d : 0;
-  gptr<const float> src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
-  const bool act = lane < half;
-  // angle of pair `lane`: L_b * theta^(-2*lane/d); the product and its
-  // reduction to [-pi, pi] are done in fp64 (inverse frequencies are computed
-  // on the host in fp64), cos/sin of the reduced angle in fp32
-  float cs = 1.f, sn = 0.f;
-  if (act) {
-    const double ang = (double)(ok ? Lb : 0) * a.inv_freq[lane];
-    const double two_pi = 6.283185307179586476925286766559;
-    const float red_ang = (float)(ang - two_pi * rint(ang / two_pi));
-    sincosf(red_ang, &sn, &cs);
+  const int G = a.G, D = a.d, S = a.S_attn;
+  const int rec = G * (D + 2);
+  gptr<const float> part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)rec;
+  gptr<float> out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
+  float* st = reinterpret_cast<float*>(lds);
+  const int n = S * rec;
+  const bool staged = ((n + 63) & ~63) * 4 <= a.lds_acc;
+  if (staged) {
+    lds_stage<4, true>(part, reinterpret_cast<char*>(st), n, tid0);
+    lds_stage_wait();
   }
-  mark(a, 0);
-  for (int hh = w; hh < G + 2; hh += kWaves) {
-    const float s0 = src[hh * d + min(lane, half - 1)], s1 = src[hh * d + min(lane, half - 1) + half];
-    float x0 = act ? s0 : 0.f;
-    float x1 = act ? s1 : 0.f;
-    if (hh == G + 1) {  // value head: rounded into the bf16 cache
-      if (act && ok) {
-        a.v_pool[slot + lane] = f2bf(x0);
-        a.v_pool[slot + lane + half] = f2bf(x1);
+  auto merge = [&](auto at) {
+    for (int e = tid0; e < G * D; e += kThreads) {
+      const int h = e / D, dd = e - h * D;
+      float M = -INFINITY;
+      for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, at(s_ * rec + h * (D + 2)));
+      float L = 0.f, O = 0.f;
+      for (int s_ = 0; s_ < S; ++s_) {
+        const int r0 = s_ * rec + h * (D + 2);
+        const float ms = at(r0);
+        if (ms != -INFINITY) {
+          const float f = __expf(ms - M);
+          L = fmaf(at(r0 + 1), f, L);
+          O = fmaf(at(r0 + 2 + dd), f, O);
+        }
       }
-      continue;
+      st_coh(out + h * D + dd, L > 0.f ? O / L : 0.f);
     }
-    if (a.qk_norm) {
-      gptr<const uint16_t> gq = P.p0, gk = P.p1;
-      gptr<const uint16_t> gam = hh < G ? gq : gk;
-      const int lc = min(lane, half - 1);
-      const float g0 = act ? bf2f(gam[lc]) : 0.f, g1 = act ? bf2f(gam[lc + half]) : 0.f;
-      const float ss = wave_sum(x0 * x0 + x1 * x1);
-      const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
-      x0 = x0 * inv * g0;
-      x1 = x1 * inv * g1;
-    }
-    const float y0 = x0 * cs - x1 * sn;
-    const float y1 = x1 * cs + x0 * sn;
-    if (act) {
-      if (hh < G) {
-        gptr<float> qo = a.q + (int64_t)l * a.st_q + (int64_t)b * a.hq * d + (int64_t)(g * G + hh) * d;
-        qo[lane] = y0;
-        qo[lane + half] = y1;
-      } else if (ok) {
-        a.k_pool[slot + lane] = f2bf(y0);
-        a.k_pool[slot + lane + half] = f2bf(y1);
-      }
-    }
-  }
+  };
+  if (staged) merge([&](int i) { return st[i]; });
+  else merge([&](int i) { return ld_coh(part + i); });
 }
 
-// ------------------------------------------------------------------ paged attention, one split
-// Task (b, g, s): pages [floor(s n_b / S), floor((s+1) n_b / S)) of request b,
-// n_b = ceil((L_b + 1) / P); all G query heads of kv group g.  Each row of R
-// lanes of a wavefront owns every (8 * 64 / R)-th token of the split (lane i
-// of the row holds dims [i D/R, (i+1) D/R): one coalesced key row and value
-// row per token), keeps an online-softmax state (max m, sum l, o[d]) per
-// head, and the row states are merged with the log-sum-exp rule at the end.
-// R = 16 when G <= 4, 32 for G <= 8 (64 registers of q and o either way).
-// Key/value rows are double-buffered in registers (the next token's loads
-// are in flight while the current one is processed; loads past the split's
-// end repeat its last token so the wait counts stay static); the split's
-// page ids are staged in LDS first.  Output: per head (m, l, o[d]) in fp32.
+// Task (b, g, s): decode attention of request b's new query against pages
+// [floor(s n_b / S), floor((s+1) n_b / S)) of its n_b = ceil((L_b + 1) / P)
+// pages, for all G query heads of kv group g.
+//  1. The group's raw q/k/v projection row (fp32) is staged in LDS; each of
+//     its G query heads and its key head gets per-head RMSNorm (qk_norm) and
+//     rotate-half RoPE at position L_b (angle L_b theta^(-2i/d), product and
+//     reduction to [-pi, pi] in fp64, cos/sin in fp32).  The last split
+//     (s = S-1, the one holding position L_b) writes the new key and value to
+//     cache slot L_b in bf16 and attends to them in fp32 as they are.
+//  2. Cached tokens: each row of R lanes of a wavefront owns every
+//     (8 * 64 / R)-th token of the split (lane i of the row holds dims
+//     [i D/R, (i+1) D/R): one coalesced key row and value row per token) and
+//     keeps an online-softmax state (max m, sum l, o[d]) per head; key/value
+//     rows are double-buffered in registers (loads past the split's end
+//     repeat its last token so the wait counts stay static).  R = 16 when
+//     G <= 4, 32 for G <= 8.  Row, wavefront and workgroup states merge with
+//     the log-sum-exp rule into the split's partial (m, l, o[d]) per head.
+//  3. The split adds itself to the (layer, b, g) arrival counter; the one
+//     that completes it merges all S partials into the attention output
+//     (attn_combine) and resets the counter.
 template <int D, int R, int GM>
-__device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char* lds) {
+__device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, const TaskPtrs& Pw, char* lds) {
   const int tid0 = tidx();
   constexpr int DPL = D / R;            // dims per lane
   constexpr int RPW = 64 / R;           // rows per wavefront
   constexpr int TPI = kWaves * RPW;     // tokens per iteration of the workgroup
+  constexpr int HALF = D / 2;
   using KV = typename std::conditional<DPL == 8, uint4, typename std::conditional<DPL == 4, uint2, uint32_t>::type>::type;
   const int b = t.a0, g = t.a1, s = t.a2, l = t.layer, G = a.G, P = a.P;
   const int w = tid0 >> 6, lane = tid0 & 63, row = lane / R, lr = lane % R;
+  const bool last_split = s == a.S_attn - 1;
+  // LDS: wavefront merge states [kWaves][G][D + 2] at 0, the raw q/k/v row at
+  // o_raw, the processed heads [G + 2][D] (G query heads scaled by 1/sqrt(D),
+  // the new key, the new value) at o_qk
+  const int o_raw = lds_chunks(kWaves * G * (D + 2) * 4);
+  const int o_qk = o_raw + lds_chunks((G + 2) * D * 4);
+  float* raw = reinterpret_cast<float*>(lds + o_raw);
+  float* qk = reinterpret_cast<float*>(lds + o_qk);
+  gptr<const float> src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
+  // (through registers: see gemv_preload)
+  const int nraw = (G + 2) * D;
+  float4 rv[(10 * 128 + 4 * kThreads - 1) / (4 * kThreads)];
+#pragma unroll
+  for (int j = 0; j < (int)(sizeof(rv) / sizeof(rv[0])); ++j) rv[j] = ld4_coh(src, (tid0 + j * kThreads) * 4, nraw);
+
   const int Lb = a.seq_lens[b];
   const bool ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
-  if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)Lb, 0u);
+  if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, t.id, -1, (uint32_t)Lb, 0u);
   const int ntok = ok ? Lb + 1 : 0;
   const int nb = (ntok + P - 1) / P;
   const int j0 = (int)((int64_t)s * nb / a.S_attn), j1 = (int)((int64_t)(s + 1) * nb / a.S_attn);
   const int t0 = j0 * P, t1 = min(j1 * P, ntok);
-
-  int* pids = reinterpret_cast<int*>(lds + kLdsMisc);   // page ids of pages j0..j1-1
+  const int tc1 = min(t1, ntok - 1);    // cached tokens of the split: [t0, tc1)
+  int* pids = reinterpret_cast<int*>(lds + a.lds_pid);   // page ids of pages j0..j1-1
   for (int j = j0 + tid0; j < j1; j += kThreads) {
     int pid = a.page_table[(int64_t)b * a.max_pages + j];
     if (pid < 0 || pid >= a.n_pages) {
-      report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)pid, (uint32_t)a.n_pages);
+      report(a, MPK_ERR_INVALID_ARG, t.id, -1, (uint32_t)pid, (uint32_t)a.n_pages);
       pid = -1;
     }
     pids[j - j0] = pid;
   }
+  const bool act = lane < HALF;
+  const int lc = min(lane, HALF - 1);
+  float cs = 1.f, sn = 0.f;
+  if (act) {
+    const double ang = (double)(ok ? Lb : 0) * a.inv_freq[lc];
+    const double two_pi = 6.283185307179586476925286766559;
+    const float red_ang = (float)(ang - two_pi * rint(ang / two_pi));
+    sincosf(red_ang, &sn, &cs);
+  }
+  float g0q = 1.f, g1q = 1.f, g0k = 1.f, g1k = 1.f;
+  if (a.qk_norm) {
+    gptr<const uint16_t> gq = Pw.p0, gk = Pw.p1;
+    g0q = bf2f(gq[lc]); g1q = bf2f(gq[lc + HALF]);
+    g0k = bf2f(gk[lc]); g1k = bf2f(gk[lc + HALF]);
+  }
+#pragma unroll
+  for (int j = 0; j < (int)(sizeof(rv) / sizeof(rv[0])); ++j) {
+    const int i = (tid0 + j * kThreads) * 4;
+    if (i < nraw) *reinterpret_cast<float4*>(raw + i) = rv[j];
+  }
+  __syncthreads();   // raw row staged, page ids written
   const float scale = 1.0f / sqrtf((float)D);
+  for (int hh = w; hh < G + 2; hh += kWaves) {
+    float x0 = act ? raw[hh * D + lc] : 0.f, x1 = act ? raw[hh * D + lc + HALF] : 0.f;
+    if (hh <= G) {   // query heads and the key head: q/k RMSNorm, RoPE
+      if (a.qk_norm) {
+        const float ss = wave_sum(x0 * x0 + x1 * x1);
+        const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+        x0 = x0 * inv * (hh < G ? g0q : g0k);
+        x1 = x1 * inv * (hh < G ? g1q : g1k);
+      }
+      const float y0 = x0 * cs - x1 * sn;
+      const float y1 = x1 * cs + x0 * sn;
+      const float f = hh < G ? scale : 1.f;
+      x0 = y0 * f;
+      x1 = y1 * f;
+    }
+    if (act) {
+      qk[hh * D + lane] = x0;
+      qk[hh * D + lane + HALF] = x1;
+    }
+    if (hh >= G && last_split && ok && act) {   // append the new key / value to the cache
+      const int pid = pids[Lb / P - j0];
+      if (pid >= 0) {
+        gptr<uint16_t> pool = hh == G ? a.k_pool : a.v_pool;
+        const int64_t slot = ((((int64_t)l * a.n_pages + pid) * a.hkv + g) * P + (Lb % P)) * D;
+        pool[slot + lane] = f2bf(x0);
+        pool[slot + lane + HALF] = f2bf(x1);
+      }
+    }
+  }
+  __syncthreads();
   float qv[GM][DPL], ov[GM][DPL], m[GM], lsum[GM];
-  gptr<const float> qsrc = a.q + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
     m[h] = -INFINITY;
     lsum[h] = 0.f;
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
-      const float qx = qsrc[min(h, G - 1) * D + lr * DPL + i];
-      qv[h][i] = h < G ? qx * scale : 0.f;
+      const float qx = qk[min(h, G - 1) * D + lr * DPL + i];
+      qv[h][i] = h < G ? qx : 0.f;
       ov[h][i] = 0.f;
     }
   }
-  __syncthreads();
   mark(a, 0);
   gptr<const uint16_t> kbase = a.k_pool + ((int64_t)l * a.n_pages * a.hkv + g) * P * D + lr * DPL;
   gptr<const uint16_t> vbase = a.v_pool + ((int64_t)l * a.n_pages * a.hkv + g) * P * D + lr * DPL;
   const int64_t page_stride = (int64_t)a.hkv * P * D;
-  // offset of token `tok`, clamped into the split (a bad page reads page 0 and is not used)
+  // offset of cached token `tok`, clamped into the split (a bad page reads page 0 and is not used)
   auto offs = [&](int tok) -> int64_t {
-    tok = min(tok, t1 - 1);
+    tok = min(tok, tc1 - 1);
     const int pid = pids[tok / P - j0];
     return (int64_t)(pid >= 0 ? pid : 0) * page_stride + (int64_t)(tok % P) * D;
   };
-  auto good = [&](int tok) { return tok < t1 && pids[tok / P - j0] >= 0; };
-  auto process = [&](const KV& kc, const KV& vc) {
-    float kf[DPL], vf[DPL];
-    const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kc);
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vc);
-#pragma unroll
-    for (int i = 0; i < DPL / 2; ++i) {
-      kf[2 * i] = bflo(kw[i]); kf[2 * i + 1] = bfhi(kw[i]);
-      vf[2 * i] = bflo(vw[i]); vf[2 * i + 1] = bfhi(vw[i]);
-    }
+  auto good = [&](int tok) { return tok < tc1 && pids[tok / P - j0] >= 0; };
+  auto process = [&](const float (&kf)[DPL], const float (&vf)[DPL]) {
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       if (h < G) {
@@ -692,25 +1026,44 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char
       }
     }
   };
-  if (t1 > t0) {
-    // `it` is the wavefront's first token of the iteration: uniform over the wavefront
-    const int base = t0 + w * RPW;
+  auto process_bf = [&](const KV& kc, const KV& vc) {
+    float kf[DPL], vf[DPL];
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kc);
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vc);
+#pragma unroll
+    for (int i = 0; i < DPL / 2; ++i) {
+      kf[2 * i] = bflo(kw[i]); kf[2 * i + 1] = bfhi(kw[i]);
+      vf[2 * i] = bflo(vw[i]); vf[2 * i + 1] = bfhi(vw[i]);
+    }
+    process(kf, vf);
+  };
+  if (tc1 > t0) {
+    const int base = t0 + w * RPW;   // the wavefront's first token of each iteration (uniform)
     int tok = base + row;
     KV k0, v0, k1, v1;
     int64_t o = offs(tok);
     k0 = ldg<KV>(kbase + o);
     v0 = ldg<KV>(vbase + o);
-    for (int it = base; it < t1; it += 2 * TPI, tok += 2 * TPI) {
+    for (int it = base; it < tc1; it += 2 * TPI, tok += 2 * TPI) {
       o = offs(tok + TPI);
       k1 = ldg<KV>(kbase + o);
       v1 = ldg<KV>(vbase + o);
-      if (good(tok)) process(k0, v0);
-      if (it + TPI >= t1) break;
+      if (good(tok)) process_bf(k0, v0);
+      if (it + TPI >= tc1) break;
       o = offs(tok + 2 * TPI);
       k0 = ldg<KV>(kbase + o);
       v0 = ldg<KV>(vbase + o);
-      if (good(tok + TPI)) process(k1, v1);
+      if (good(tok + TPI)) process_bf(k1, v1);
     }
+  }
+  if (last_split && ok && w == 0 && row == 0) {   // the new token, in fp32
+    float kf[DPL], vf[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      kf[i] = qk[G * D + lr * DPL + i];
+      vf[i] = qk[(G + 1) * D + lr * DPL + i];
+    }
+    process(kf, vf);
   }
   mark(a, 1);
   // merge the row states of the wavefront (lanes lr, lr+R, ...)
@@ -766,50 +1119,26 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, char
         }
       }
     }
-    out[h * (D + 2) + 2 + dd] = O;
-    if (dd == 0) { out[h * (D + 2)] = M; out[h * (D + 2) + 1] = L; }
+    st_coh(out + h * (D + 2) + 2 + dd, O);
+    if (dd == 0) {
+      st_coh(out + h * (D + 2), M);
+      st_coh(out + h * (D + 2) + 1, L);
+    }
+  }
+  // arrival: every wavefront's partial stores are complete before the
+  // barrier, so the split that completes the count reads all S partials
+  wait_vm<0>();
+  __syncthreads();
+  int* flag = reinterpret_cast<int*>(lds + kLdsCtl) + 2;
+  if (tid0 == 0) {
+    gptr<uint32_t> ctr = a.arrive + ((int64_t)l * a.B + b) * a.hkv + g;
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old + 1u == (uint32_t)a.S_attn;
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
   }
   __syncthreads();
-}
-
-// ------------------------------------------------------------------ split combine
-// Task (b, g): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}, M = max_s m_s.
-// The S partial records are staged in LDS first (all loads in flight at once).
-__device__ __forceinline__ void combine_task(const KArgs& a, const DevTask& t, char* lds) {
-  const int tid0 = tidx();
-  const int b = t.a0, g = t.a1, l = t.layer, G = a.G, D = a.d, S = a.S_attn;
-  const int rec = G * (D + 2);
-  gptr<const float> part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)rec;
-  gptr<float> out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
-  float* st = reinterpret_cast<float*>(lds);
-  const int n = S * rec;
-  const bool staged = ((n + 63) & ~63) <= kLdsXFloats;
-  if (staged) {
-    lds_stage<4>(part, reinterpret_cast<char*>(st), n, tid0);
-    lds_stage_wait();
-  }
-  mark(a, 0);
-  auto merge = [&](auto at) {
-    for (int e = tid0; e < G * D; e += kThreads) {
-      const int h = e / D, dd = e - h * D;
-      float M = -INFINITY;
-      for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, at(s_ * rec + h * (D + 2)));
-      float L = 0.f, O = 0.f;
-      for (int s_ = 0; s_ < S; ++s_) {
-        const int r0 = s_ * rec + h * (D + 2);
-        const float ms = at(r0);
-        if (ms != -INFINITY) {
-          const float f = __expf(ms - M);
-          L = fmaf(at(r0 + 1), f, L);
-          O = fmaf(at(r0 + 2 + dd), f, O);
-        }
-      }
-      out[h * D + dd] = L > 0.f ? O / L : 0.f;
-    }
-  };
-  if (staged) merge([&](int i) { return st[i]; });
-  else merge([&](int i) { return part[i]; });
-  mark(a, 1);
+  if (__builtin_amdgcn_readfirstlane(*flag)) attn_combine(a, l, b, g, lds);
   __syncthreads();
 }
 
@@ -824,7 +1153,10 @@ __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
     float bv = -INFINITY;
     int bi = INT_MAX;
     for (int n = tid0; n < a.T_lm; n += kThreads) {
-      const PMax p = a.pmax[b * a.T_lm + n];
+      const unsigned long long pv = __hip_atomic_load(
+          reinterpret_cast<MPK_GLOBAL unsigned long long*>(a.pmax + b * a.T_lm + n), __ATOMIC_RELAXED,
+          __HIP_MEMORY_SCOPE_AGENT);
+      const PMax p{__uint_as_float((uint32_t)pv), (int32_t)(pv >> 32)};
       if (p.v > bv || (p.v == bv && p.i < bi)) { bv = p.v; bi = p.i; }
     }
 #pragma unroll
@@ -845,9 +1177,9 @@ __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
 }
 
 // ------------------------------------------------------------------ dispatch
-// Runs task `task` with the whole workgroup.
-// Task t with its resolved weight pointers P (task_ptrs).
-__device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const TaskPtrs& P) {
+// Runs task t, with its resolved weight pointers P (task_ptrs), with the
+// whole workgroup; pre: its weight pre-load (gemv_preload) was issued.
+__device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const TaskPtrs& P, bool pre = false) {
   char* lds = g_lds;
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
   const int l = t.layer;
@@ -874,22 +1206,17 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
     case MPK_TASK_GATEUP:
     case MPK_TASK_DOWN:
     case MPK_TASK_LMHEAD:
-      if (a.B == 1) gemv_b1<8>(a, t, P, lds);
-      else gemv_bn(a, t, P, lds);
-      break;
-    case MPK_TASK_QKNORM_ROPE:
-      rope_task(a, t, P);
+      if (a.B > 1) gemv_bn(a, t, P, lds);
+      else if (a.gemv_d == 4) gemv_b1<4>(a, t, P, lds, pre);
+      else gemv_b1<8>(a, t, P, lds, pre);
       break;
     case MPK_TASK_ATTN:
       if (a.d == 128) {
-        if (a.G <= 4) attn_task<128, 16, 4>(a, t, lds);
-        else attn_task<128, 32, 8>(a, t, lds);
+        if (a.G <= 4) attn_task<128, 16, 4>(a, t, P, lds);
+        else attn_task<128, 32, 8>(a, t, P, lds);
       } else {
-        attn_task<64, 16, 8>(a, t, lds);
+        attn_task<64, 16, 8>(a, t, P, lds);
       }
-      break;
-    case MPK_TASK_COMBINE:
-      combine_task(a, t, lds);
       break;
     case MPK_TASK_ARGMAX:
       argmax_task(a, lds);

@@ -48,7 +48,7 @@ def test_tiny_worked_example_bit_exact():
     s = synth.SHAPES["tiny"]
     ref, got, tasks = both(s, 1, 8, q=64, S=4, T_qkv=8, T_o=4, T_gu=11, T_down=4, T_lm=16)
     assert_same(ref, got)
-    assert got["header"]["NT"] == 109 and got["header"]["NE"] == 33
+    assert got["header"]["NT"] == 95 and got["header"]["NE"] == 19
     tg.check_semantics(got, tasks, closure=True)
 
 

@@ -23,38 +23,62 @@ def tiny():
 def test_tiny_worked_example_sizes():
     g, tasks = tiny()
     h = g["header"]
-    # per layer 41 tasks; 101 originals; 27 fused events; 4 fan-out rewrites
-    assert len(tasks) == 101
-    assert sum(1 for t in tasks if t["layer"] == 0) == 41
-    assert h["n_fused"] == 27 and h["n_rewrites"] == 4 and h["n_empty"] == 8
-    assert h["NT"] == 109 and h["NE"] == 33 and h["root"] == 0 and h["end"] == 32
+    # Hand count (batch 1, so the norms run inside the projection tiles): per layer
+    # 8 QKV + 2 groups x 4 splits ATTN + 4 OPROJ + 11 GATEUP + 4 DOWN = 35 tasks; 2 layers,
+    # 16 LM-head tiles and ARGMAX give 87.  Fused events: layer 0 {2 ATTN groups, OPROJ,
+    # GATEUP, DOWN}, layer 1 the same plus its QKV event, then LM head and ARGMAX = 13.
+    # QKV tile 0 (also stores the residual for GATEUP) and GATEUP tile 0 (also stores the
+    # residual for the next layer / LM head) each feed two events: 4 rewrites, 8 empties.
+    assert len(tasks) == 87
+    assert sum(1 for t in tasks if t["layer"] == 0) == 35
+    assert h["n_fused"] == 13 and h["n_rewrites"] == 4 and h["n_empty"] == 8
+    assert h["NT"] == 95 and h["NE"] == 19 and h["root"] == 0 and h["end"] == 18
 
 
 def test_tiny_worked_example_order_and_counts():
     g, _ = tiny()
     T = tg
     tt = list(g["task_type"])
-    expect = [T.EMBED, T.ATTN_NORM, T.EMPTY, T.EMPTY] + [T.QKV] * 8 + [T.QKNORM_ROPE] * 2 + [T.ATTN] * 8 + \
-        [T.COMBINE] * 2 + [T.OPROJ] * 4 + [T.MLP_NORM]
+    # layer-0 QKV tiles are the sources; the empties of QKV tile 0 follow them
+    expect = [T.QKV] * 8 + [T.EMPTY] * 2 + [T.ATTN] * 8 + [T.OPROJ] * 4 + [T.GATEUP] * 11 + [T.EMPTY] * 2 + \
+        [T.DOWN] * 4 + [T.QKV] * 8
     assert tt[:len(expect)] == expect
     cnt = g["event_counts"]; dep = g["task_dep"]
     c = lambda i: int(cnt[dep[i]])
-    assert c(12) == 4 and c(13) == 4          # q/k-norm+RoPE waits for the 4 projection tiles of its group
-    assert c(22) == 4 and c(23) == 4          # combine waits for its 4 attention splits
-    assert c(24) == 2                         # O projection waits for both combines
-    assert c(28) == 5                         # MLP norm: 4 O tiles + the empty task standing in for ATTN_NORM
-    # the two empty tasks after ATTN_NORM_0 feed, in order, the projection event and the MLP-norm event
-    assert g["task_orig"][2] == -1 and g["task_orig"][3] == -2
-    assert g["event_first"][g["task_trig"][2]] == 4
-    assert g["task_type"][g["event_first"][g["task_trig"][3]]] == T.MLP_NORM
+    assert all(c(i) == 0 for i in range(8))      # root
+    assert c(8) == 1 and c(9) == 1               # e' of QKV tile 0
+    assert all(c(i) == 4 for i in range(10, 18))  # a split waits for the 4 projection tiles of its group
+    assert c(18) == 8                            # O projection waits for all 8 splits (any may combine)
+    assert c(22) == 5                            # GATEUP: 4 O tiles + the empty standing in for QKV tile 0
+    assert c(35) == 11                           # DOWN waits for the 11 gate/up tiles
+    assert c(39) == 5                            # next QKV: 4 DOWN tiles + the empty for GATEUP tile 0
+    # the two empties of QKV tile 0 feed, in order, the group-0 attention event and the GATEUP event
+    assert g["task_orig"][8] == -1 and g["task_orig"][9] == -2
+    # (group 1's event completes with tile 7, before group 0's completes through empty 8, so the
+    # BFS places group 1's splits at 10..13 and group 0's at 14..17)
+    assert g["event_first"][g["task_trig"][8]] == 14
+    assert [tuple(g["task_coords"][i]) for i in (10, 14)] == [(0, 1, 0), (0, 0, 0)]
+    assert g["task_type"][g["event_first"][g["task_trig"][9]]] == T.GATEUP
     # ATTN tasks are JIT, empties EMPTY, all else AOT; the AOT worker is round-robin in linear order
     aot = [i for i in range(len(tt)) if g["task_mode"][i] == T.MODE_AOT]
     assert [int(g["task_worker"][i]) for i in aot] == [k % 8 for k in range(len(aot))]
-    last = [i for i in range(len(tt)) if tt[i] == T.DOWN][-1]
-    assert c(last + 1) == 5 if tt[last + 1] == T.FINAL_NORM else True
+    lm = tt.index(T.LMHEAD)
+    assert c(lm) == 5                            # last DOWN tiles + the empty of the last GATEUP tile 0
     argmax = tt.index(T.ARGMAX)
     assert c(argmax) == 16 and g["event_counts"][g["header"]["end"]] == 1
     tg.check_semantics(g, _, closure=True)
+
+
+def test_tiny_worked_example_batch3_keeps_norm_tasks():
+    g, tasks = tg.build(synth.SHAPES["tiny"].cfg(), 3, 16, TINY_PRM)
+    tt = list(g["task_type"])
+    # EMBED + per layer (ATTN_NORM, 8 QKV, 3 x 2 x 4 ATTN, 4 OPROJ, MLP_NORM, 11 GATEUP, 4 DOWN) = 1 + 2 x 53,
+    # + FINAL_NORM + 16 LM + ARGMAX
+    assert len(tasks) == 1 + 2 * 53 + 18
+    assert tt.count(T_EMPTY := tg.EMPTY) == 8    # ATTN_NORM and MLP_NORM each feed two events
+    assert tt[:4] == [tg.EMBED, tg.ATTN_NORM, T_EMPTY, T_EMPTY]
+    assert tg.QKNORM_ROPE not in tt and tg.COMBINE not in tt
+    tg.check_semantics(g, tasks, closure=True)
 
 
 def test_rewrite_identities():
@@ -90,7 +114,8 @@ def test_full_graph_invariants(name):
     tg.check_semantics(g, None)
     h = g["header"]
     assert h["n_empty"] / h["NT"] < 0.01          # "deep, not wide": under 1% empty tasks
-    assert h["n_empty"] == 4 * s.n_layers          # ATTN_NORM and MLP_NORM fan out to two events per layer
+    # two tasks per layer fan out to two events (the residual keepers at batch 1, the norms otherwise)
+    assert h["n_empty"] == 4 * s.n_layers
 
 
 # ------------------------------------------------------------------ random programs
