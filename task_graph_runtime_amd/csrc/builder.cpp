@@ -98,7 +98,7 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   if (p.s_attn > 0) {
     r.S_attn = p.s_attn;
   } else {
-    int64_t s = std::min<int64_t>(16, std::max<int64_t>(1, cdiv(2 * r.W, (int64_t)B * hkv)));
+    int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, cdiv(2 * r.W, (int64_t)B * hkv)));
     r.S_attn = (int32_t)std::min<int64_t>(s, max_pages);
   }
   if (r.T_qkv / hkv > cdiv(Sg, r.q)) return bad("t_qkv: more tiles per kv group than column quanta");

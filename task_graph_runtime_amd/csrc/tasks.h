@@ -842,11 +842,20 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
   gptr<const float> part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)rec;
   gptr<float> out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
   float* st = reinterpret_cast<float*>(lds);
-  const int n = S * rec;
+  const int n = S * rec;   // (a multiple of 4: rec = G (D + 2) with D even)
   const bool staged = ((n + 63) & ~63) * 4 <= a.lds_acc;
-  if (staged) {
-    lds_stage<4, true>(part, reinterpret_cast<char*>(st), n, tid0);
-    lds_stage_wait();
+  if (staged) {   // staged through registers: all loads in flight at once
+    for (int i0 = 0; i0 < n; i0 += 4 * kThreads * 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = ld4_coh(part, i0 + (tid0 + u * kThreads) * 4, n);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + (tid0 + u * kThreads) * 4;
+        if (i < n) *reinterpret_cast<float4*>(st + i) = v[u];
+      }
+    }
+    __syncthreads();
   }
   auto merge = [&](auto at) {
     for (int e = tid0; e < G * D; e += kThreads) {
