@@ -45,7 +45,7 @@ def measured_traffic(config: str):
     workload, or None when there is none or the device sources have changed
     since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, TRAFFIC_FILE.format(config=config.replace("qwen3_8b", "qwen3_8b_b1")))
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(config={"qwen3_8b": "qwen3_8b_b1"}.get(config, config)))
     if not os.path.exists(path):
         return None
     kv = dict(line.strip().split("=", 1) for line in open(path) if "=" in line and " " not in line.strip())

@@ -98,7 +98,11 @@ def fused_norm(B):
     prologue) instead of running as a task of their own; the first tile of
     the consuming projection also stores the residual for later layers.  At
     batch > 1 the norms stay tasks (ATTN_NORM, MLP_NORM, FINAL_NORM) and the
-    embedding an EMBED task.
+    embedding EMBED tasks, one task per request: coords (b,), output row b.
+    A norm task declares all B rows of its inputs, though it reads row b
+    only: every norm task of an operator then has the same producer set and
+    the B tasks share one event, instead of B events that every producer
+    tile would have to trigger (B rewrites per tile).
     """
     return B == 1
 
@@ -130,13 +134,16 @@ def decompose(cfg, B, P, prm: Params):
         tasks.append(dict(type=tp, layer=layer, coords=c, ins=ins, outs=outs))
 
     full = lambda tn, n: _box(tn, (0, 0), (B, n))
+    row = lambda tn, b, n: _box(tn, (b, 0), (b + 1, n))
     if not fused:
-        add(EMBED, -1, (), [], [full(T_E, H)])
+        for b in range(B):
+            add(EMBED, -1, (b,), [], [row(T_E, b, H)])
     for l in range(L):
         t = lambda k: layer_tensor(l, k)
         prev = [] if l == 0 else [full(layer_tensor(l - 1, L_S), H), full(layer_tensor(l - 1, L_D), H)]
         if not fused:
-            add(ATTN_NORM, l, (), prev if l else [full(T_E, H)], [full(t(L_R), H), full(t(L_H), H)])
+            for b in range(B):
+                add(ATTN_NORM, l, (b,), prev if l else [full(T_E, H)], [row(t(L_R), b, H), row(t(L_H), b, H)])
         tpg = prm.T_qkv // hkv
         for n in range(prm.T_qkv):
             g, j = divmod(n, tpg)
@@ -159,7 +166,8 @@ def decompose(cfg, B, P, prm: Params):
             add(OPROJ, l, (n,), [full(t(L_ATTN), hq * d)], [_box(t(L_O), (0, lo), (B, hi))])
         mid = [full(t(L_R), H), full(t(L_O), H)]
         if not fused:
-            add(MLP_NORM, l, (), mid, [full(t(L_S), H), full(t(L_H2), H)])
+            for b in range(B):
+                add(MLP_NORM, l, (b,), mid, [row(t(L_S), b, H), row(t(L_H2), b, H)])
         for n in range(prm.T_gu):
             lo, hi = tile_range(F, prm.q, prm.T_gu, n)
             outs = [_box(t(L_A), (0, lo), (B, hi))]
@@ -171,7 +179,8 @@ def decompose(cfg, B, P, prm: Params):
             add(DOWN, l, (n,), [full(t(L_A), F)], [_box(t(L_D), (0, lo), (B, hi))])
     last = [full(layer_tensor(L - 1, L_S), H), full(layer_tensor(L - 1, L_D), H)]
     if not fused:
-        add(FINAL_NORM, -1, (), last, [full(T_HF, H)])
+        for b in range(B):
+            add(FINAL_NORM, -1, (b,), last, [row(T_HF, b, H)])
     for n in range(prm.T_lm):
         lo, hi = tile_range(V, prm.q, prm.T_lm, n)
         add(LMHEAD, -1, (n,), last if fused else [full(T_HF, H)],

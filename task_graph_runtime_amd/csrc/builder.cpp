@@ -136,13 +136,20 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
     tasks.push_back(std::move(t));
   };
   auto full = [&](int32_t tensor, int32_t n) { return box(tensor, {0, 0}, {B, n}); };
-  if (!fused) add(MPK_TASK_EMBED, -1, 0, 0, 0, {}, {full(T_E, H)});
+  // batch > 1: one embedding / norm task per request b (coords (b,), output
+  // row b); norm tasks declare all B rows of their inputs so that the B tasks
+  // of an operator share one event
+  auto row = [&](int32_t tensor, int32_t b, int32_t n) { return box(tensor, {b, 0}, {b + 1, n}); };
+  if (!fused)
+    for (int32_t b = 0; b < B; ++b) add(MPK_TASK_EMBED, -1, b, 0, 0, {}, {row(T_E, b, H)});
   for (int32_t l = 0; l < L; ++l) {
     auto t = [&](int32_t k) { return layer_tensor(l, k); };
     std::vector<Box> prev;
     if (l > 0) prev = {full(layer_tensor(l - 1, L_S), H), full(layer_tensor(l - 1, L_D), H)};
     if (!fused)
-      add(MPK_TASK_ATTN_NORM, l, 0, 0, 0, l ? prev : std::vector<Box>{full(T_E, H)}, {full(t(L_R), H), full(t(L_H), H)});
+      for (int32_t b = 0; b < B; ++b)
+        add(MPK_TASK_ATTN_NORM, l, b, 0, 0, l ? prev : std::vector<Box>{full(T_E, H)},
+            {row(t(L_R), b, H), row(t(L_H), b, H)});
     const int32_t tpg = p.T_qkv / hkv;
     for (int32_t n = 0; n < p.T_qkv; ++n) {
       int32_t g = n / tpg, j = n % tpg, lo, hi;
@@ -168,7 +175,8 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
       add(MPK_TASK_OPROJ, l, n, 0, 0, {full(t(L_ATTN), hq * d)}, {box(t(L_O), {0, lo}, {B, hi})});
     }
     const std::vector<Box> mid = {full(t(L_R), H), full(t(L_O), H)};
-    if (!fused) add(MPK_TASK_MLP_NORM, l, 0, 0, 0, mid, {full(t(L_S), H), full(t(L_H2), H)});
+    if (!fused)
+      for (int32_t b = 0; b < B; ++b) add(MPK_TASK_MLP_NORM, l, b, 0, 0, mid, {row(t(L_S), b, H), row(t(L_H2), b, H)});
     for (int32_t n = 0; n < p.T_gu; ++n) {
       int32_t lo, hi;
       tile_range(F, p.q, p.T_gu, n, &lo, &hi);
@@ -183,7 +191,8 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
     }
   }
   const std::vector<Box> last = {full(layer_tensor(L - 1, L_S), H), full(layer_tensor(L - 1, L_D), H)};
-  if (!fused) add(MPK_TASK_FINAL_NORM, -1, 0, 0, 0, last, {full(T_HF, H)});
+  if (!fused)
+    for (int32_t b = 0; b < B; ++b) add(MPK_TASK_FINAL_NORM, -1, b, 0, 0, last, {row(T_HF, b, H)});
   for (int32_t n = 0; n < p.T_lm; ++n) {
     int32_t lo, hi;
     tile_range(V, p.q, p.T_lm, n, &lo, &hi);

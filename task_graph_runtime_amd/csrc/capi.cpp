@@ -241,10 +241,27 @@ int upload(mpk_tgraph* t) {
   const int64_t o_wl = align256(o_lists + (int64_t)std::max<size_t>(1, flat.size()) * 4);
   const int64_t o_freq = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
   const int64_t graph_bytes = align256(o_freq + (int64_t)t->cfg.head_dim / 2 * 8);
+  // A JIT event's tasks are dealt in chunks of (workers / schedulers) tasks,
+  // one chunk per scheduler ring entry, to consecutive schedulers from a
+  // starting one; the starting schedulers follow a running cursor over all
+  // chunks in event order, so the chunks of events that fire together land
+  // on different schedulers (and so on different workers).  The device copy
+  // of the event keeps its starting scheduler in flags bits 16..31.
+  std::vector<DevEvent> ev(g.NE);
+  const int32_t chunk = std::max<int32_t>(1, t->prm.W / t->n_sched);
+  int64_t n_entries = 0;
+  if (g.NE >= (1 << kJitEventBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 2^20 events");
+  for (int32_t e = 0; e < g.NE; ++e) {
+    ev[e] = DevEvent{g.event_counts[e], g.event_first[e], g.event_last[e], g.event_flags[e]};
+    if (g.event_flags[e] & MPK_EVENT_HAS_JIT) {
+      const int64_t n_ch = (g.event_last[e] - g.event_first[e] + chunk) / chunk;
+      if (n_ch > (1 << kJitChunkBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 4096 JIT chunks in one event");
+      ev[e].flags |= (uint32_t)(n_entries % t->n_sched) << 16;
+      n_entries += n_ch;
+    }
+  }
   HIPCHK(hipMalloc(&t->d_graph, graph_bytes));
   char* gb = (char*)t->d_graph;
-  std::vector<DevEvent> ev(g.NE);
-  for (int32_t e = 0; e < g.NE; ++e) ev[e] = DevEvent{g.event_counts[e], g.event_first[e], g.event_last[e], g.event_flags[e]};
   t->d_tasks = (DevTask*)(gb + o_tasks);
   t->d_events = (DevEvent*)(gb + o_events);
   t->d_aot_off = (uint32_t*)(gb + o_off);
@@ -268,10 +285,9 @@ int upload(mpk_tgraph* t) {
   if (!flat.empty()) HIPCHK(hipMemcpy(t->d_lists, flat.data(), flat.size() * 4, hipMemcpyHostToDevice));
 
   // runtime: counters, rings, state, status
-  int64_t n_jit_tasks = 0, n_jit_events = 0;
+  int64_t n_jit_tasks = 0;
   for (int32_t i = 0; i < g.NT; ++i) n_jit_tasks += g.task_mode[i] == MPK_MODE_JIT;
-  for (int32_t e = 0; e < g.NE; ++e) n_jit_events += (g.event_flags[e] & MPK_EVENT_HAS_JIT) != 0;
-  t->sched_cap = next_pow2((uint64_t)n_jit_events + 1);
+  t->sched_cap = next_pow2((uint64_t)n_entries + 1);   // every ring entry of a step fits in any one ring
   t->jit_cap = next_pow2((uint64_t)n_jit_tasks + 1);
   const int32_t W = t->prm.W, S = t->n_sched;
   const int64_t r_cnt = 0, r_sring = align256(r_cnt + (int64_t)g.NE * 4);

@@ -10,10 +10,11 @@
 // global counters advanced by atomic adds; an event fires when its counter
 // reaches counts * epoch (counters are never reset: each step raises the
 // target).  The agent whose add fires an event resolves the event's empty
-// consumers on the spot and, if the event has JIT consumers, appends it to
-// the ring of scheduler (event mod n_sched).  A scheduler pops its ring and
-// deals the event's JIT tasks round-robin onto the JIT rings of its workers
-// (workers w with w mod n_sched == its index).  Everything exits when the end
+// consumers on the spot and, if the event has JIT consumers, appends its
+// tasks, in chunks of (workers / schedulers), to the rings of consecutive
+// schedulers.  A scheduler pops its ring and deals a chunk's tasks
+// round-robin onto the JIT rings of its workers (workers w with
+// w mod n_sched == its index).  Everything exits when the end
 // event fires; every wait has a watchdog so that the grid always drains.
 #include "tasks.h"
 
@@ -51,11 +52,19 @@ __device__ __forceinline__ gptr<uint32_t> st_sched_head(const KArgs& a) { return
 __device__ __forceinline__ gptr<uint32_t> st_sched_rr(const KArgs& a) { return a.state + a.n_workers + a.n_sched; }
 __device__ __forceinline__ gptr<uint32_t> st_jit_tail(const KArgs& a) { return a.state + a.n_workers + 2 * a.n_sched; }
 
-__device__ __forceinline__ void push_event(const KArgs& a, int e) {
-  const int s = e % a.n_sched;
+// A fired JIT event is handed over in chunks of (workers / schedulers) of
+// its tasks, chunk c to scheduler (s0 + c) mod n_sched, where s0 is the
+// event's starting scheduler (flags bits 16..31, set by the host so that the
+// chunks of events firing together spread over all schedulers).
+__device__ __forceinline__ int jit_chunk(const KArgs& a) { return max(1, a.n_workers / a.n_sched); }
+__device__ __forceinline__ int jit_chunks(const KArgs& a, const DevEvent& ev) {
+  return (ev.last - ev.first + jit_chunk(a)) / jit_chunk(a);
+}
+__device__ __forceinline__ void push_chunk(const KArgs& a, int e, const DevEvent& ev, int c) {
+  const int s = (int)(((ev.flags >> 16) + (uint32_t)c) % (uint32_t)a.n_sched);
   const uint32_t pos = __hip_atomic_fetch_add(&a.sched_tail[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   st_relaxed64(&a.sched_ring[(int64_t)s * a.sched_cap + (pos & (a.sched_cap - 1))],
-               ((unsigned long long)(pos + 1) << 32) | (uint32_t)e);
+               ((unsigned long long)(pos + 1) << 32) | ((uint32_t)c << kJitEventBits) | (uint32_t)e);
 }
 
 // One trigger of event e by wavefront 0 of a workgroup whose stores for the
@@ -78,11 +87,13 @@ __device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e, c
         const int f = a.tasks[t].trig;
         const uint32_t o2 = __hip_atomic_fetch_add(&a.ev_cnt[f], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const DevEvent fe = a.events[f];
-        if (o2 + 1u == fe.counts * epoch && (fe.flags & MPK_EVENT_HAS_JIT)) push_event(a, f);
+        if (o2 + 1u == fe.counts * epoch && (fe.flags & MPK_EVENT_HAS_JIT))
+          for (int c = 0; c < jit_chunks(a, fe); ++c) push_chunk(a, f, fe, c);
       }
     }
   }
-  if ((ev.flags & MPK_EVENT_HAS_JIT) && lane == 0) push_event(a, e);
+  if (ev.flags & MPK_EVENT_HAS_JIT)
+    for (int c = lane; c < jit_chunks(a, ev); c += 64) push_chunk(a, e, ev, c);
 }
 
 enum { CMD_EXIT = 0, CMD_JIT = 1, CMD_AOT = 2 };
@@ -284,17 +295,19 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
     const uint32_t end_cnt = ld_relaxed(&a.ev_cnt[a.end_event]);
     const uint32_t status = ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code));
     if ((uint32_t)(slot >> 32) == head + 1u) {
-      const int e = (int)(uint32_t)slot;
+      const int e = (int)((uint32_t)slot & ((1u << kJitEventBits) - 1u));
+      const int c = (int)((uint32_t)slot >> kJitEventBits);
       ++head;
       const DevEvent ev = a.events[e];
-      const int k = ev.last - ev.first + 1;
+      const int first = ev.first + c * jit_chunk(a);
+      const int k = min(ev.last - first + 1, jit_chunk(a));
       for (int base = 0; base < k; base += n_sub) {
         // task base + j goes to sub-worker (rr + base + j) mod n_sub
         const int r0 = (int)((rr + (uint32_t)base) % (uint32_t)n_sub);
         const int j = base + (lane - r0 + n_sub) % n_sub;
         if (lane < n_sub && j < k) {
           __hip_atomic_store(&my_ring[my_tail & (a.jit_cap - 1)],
-                             ((unsigned long long)(my_tail + 1u) << 32) | (uint32_t)(ev.first + j),
+                             ((unsigned long long)(my_tail + 1u) << 32) | (uint32_t)(first + j),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ++my_tail;
         }

@@ -66,6 +66,9 @@ struct alignas(16) DevEvent {
 };
 static_assert(sizeof(DevEvent) == 16, "DevEvent must be 16 bytes");
 
+// Scheduler ring entry: seq << 32 | chunk << 20 | event (see the megakernel).
+constexpr int kJitEventBits = 20, kJitChunkBits = 12;
+
 // Per-(request, LM-head tile) partial argmax.
 struct PMax {
   float v;

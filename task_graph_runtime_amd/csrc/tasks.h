@@ -242,60 +242,51 @@ __device__ __forceinline__ void lds_stage_wait() {
 __device__ __forceinline__ int lds_chunks(int bytes) { return (bytes + 1023) & ~1023; }
 
 // ------------------------------------------------------------------ embedding
-__device__ __forceinline__ void embed_task(const KArgs& a) {
+// Row b of the embedding table for request b's token (batch > 1; at batch 1
+// the layer-0 QKV tiles gather it themselves).
+__device__ __forceinline__ void embed_task(const KArgs& a, int b) {
   const int tid0 = tidx();
-  for (int b = 0; b < a.B; ++b) {
-    int id = a.token_ids[b];
-    if (id < 0 || id >= a.V) {
-      if (tid0 == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)id, (uint32_t)a.V);
-      id = 0;
-    }
-    gptr<const uint16_t> row = a.embed + (int64_t)id * a.H;
-    for (int i = tid0; i < a.H; i += kThreads) st_coh(a.e + (int64_t)b * a.H + i, bf2f(row[i]));
+  int id = a.token_ids[b];
+  if (id < 0 || id >= a.V) {
+    if (tid0 == 0) report(a, MPK_ERR_INVALID_ARG, -1, -1, (uint32_t)id, (uint32_t)a.V);
+    id = 0;
   }
+  gptr<const uint16_t> row = a.embed + (int64_t)id * a.H;
+  for (int i = tid0; i < a.H; i += kThreads) st_coh(a.e + (int64_t)b * a.H + i, bf2f(row[i]));
 }
 
 // ------------------------------------------------------------------ residual add + RMSNorm
-// res = x + y (y optional), stored when `res` is given; out = RMSNorm(res) * gamma.
-// gamma and the input rows are staged in LDS with direct loads (all rows at
-// once when they fit, else one row at a time).
-__device__ __forceinline__ void norm_task(const KArgs& a, gptr<const float> __restrict__ x,
+// Row b: res = x + y (y optional), stored when `res` is given;
+// out = RMSNorm(res) * gamma.  gamma and the input rows are staged in LDS
+// with direct loads.
+__device__ __forceinline__ void norm_task(const KArgs& a, int b, gptr<const float> __restrict__ x,
                                           gptr<const float> __restrict__ y, gptr<float> __restrict__ res,
                                           gptr<const uint16_t> __restrict__ gamma, gptr<float> __restrict__ out,
                                           char* lds, float* red) {
   const int tid0 = tidx();
-  const int H = a.H, B = a.B;
+  const int H = a.H;
   const int hb = lds_chunks(H * 4), gb = lds_chunks(H * 2);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds);
-  char* xsl = lds + gb;
-  const int rows = (B * 2 * hb + gb <= a.lds_acc) ? B : 1;
+  const float* xr = reinterpret_cast<const float*>(lds + gb);
+  const float* yr = reinterpret_cast<const float*>(lds + gb + hb);
+  const int64_t off = (int64_t)b * H;
   lds_stage<16>(gamma, lds, H / 8, tid0);
-  for (int b0 = 0; b0 < B; b0 += rows) {
-    const int nr = min(rows, B - b0);
-    for (int r = 0; r < nr; ++r) {
-      lds_stage<16, true>(x + (int64_t)(b0 + r) * H, xsl + (2 * r) * hb, H / 4, tid0);
-      if (y) lds_stage<16, true>(y + (int64_t)(b0 + r) * H, xsl + (2 * r + 1) * hb, H / 4, tid0);
-    }
-    lds_stage_wait();
-    mark(a, 0);
-    for (int r = 0; r < nr; ++r) {
-      const float* xr = reinterpret_cast<const float*>(xsl + (2 * r) * hb);
-      const float* yr = reinterpret_cast<const float*>(xsl + (2 * r + 1) * hb);
-      float ss = 0.f;
-      for (int i = tid0; i < H; i += kThreads) {
-        const float v = y ? xr[i] + yr[i] : xr[i];
-        ss = fmaf(v, v, ss);
-      }
-      ss = block_sum(ss, red);
-      mark(a, 1);
-      const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
-      for (int i = tid0; i < H; i += kThreads) {
-        const float v = y ? xr[i] + yr[i] : xr[i];
-        if (res) st_coh(res + (int64_t)(b0 + r) * H + i, v);
-        st_coh(out + (int64_t)(b0 + r) * H + i, v * inv * bf2f(gs[i]));
-      }
-    }
-    __syncthreads();   // the staging area is refilled by the next group of rows
+  lds_stage<16, true>(x + off, lds + gb, H / 4, tid0);
+  if (y) lds_stage<16, true>(y + off, lds + gb + hb, H / 4, tid0);
+  lds_stage_wait();
+  mark(a, 0);
+  float ss = 0.f;
+  for (int i = tid0; i < H; i += kThreads) {
+    const float v = y ? xr[i] + yr[i] : xr[i];
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum(ss, red);
+  mark(a, 1);
+  const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+  for (int i = tid0; i < H; i += kThreads) {
+    const float v = y ? xr[i] + yr[i] : xr[i];
+    if (res) st_coh(res + off + i, v);
+    st_coh(out + off + i, v * inv * bf2f(gs[i]));
   }
 }
 
@@ -763,68 +754,143 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
   gemv_epilogue(a, t, acc, red);
 }
 
-// Batch 2..16 projection tile (VALU): same segment walk, x read from global
-// memory (L2-resident), one fp32 partial per request.
-__device__ __forceinline__ void gemv_bn(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
+// ------------------------------------------------------------------ projection tile, batch 2..16 (MFMA)
+// With B requests the tile is a dense contraction Y[b][n] = sum_k W[n][k]
+// X[b][k] (K2 MatMul task of the MPK summary page, batch 16 sits in its
+// memory-bound regime), computed with v_mfma_f32_16x16x32_bf16:
+//   A = 16 weight rows x 32 k, lane l holding row l % 16 at k 8 (l / 16) .. +7
+//       (one 16-byte load straight from the weight row);
+//   B = X^T, lane l holding request l % 16 at the same 8 k;
+//   D = 16 rows x 16 requests, lane l holding rows 4 (l / 16) + r, request l % 16.
+// The fp32 activations enter as two bf16 operands, hi = bf16(x) and
+// lo = bf16(x - hi); the weights are exact bf16, so every product is exact
+// in fp32 and x keeps about 16 significant bits (activations between tasks
+// are fp32: bf16 rounding at every task drifts past the logit bound).
+// Wavefront w takes k-steps [w nks / 8, (w + 1) nks / 8) (32 k per step) of
+// every 16-row block, in passes over NRB row blocks with NRB accumulators in
+// registers.  A pass walks the wavefront's k range in groups of KG steps:
+// the group's x slice is converted once for all NRB blocks, and while the
+// group multiplies, the next group's weights (NRB x KG x 1 KB) and x are in
+// flight; the last group is peeled so that every load in the loop is
+// unconditional and the compiler's waits count exactly.  At the end of a
+// pass the partials go to the LDS accumulators acc[row][B] (ds_add).  Rows
+// past the tile and requests past B are computed on clamped rows and dropped;
+// k-steps past the wavefront's range see x = 0.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// (a, b) -> packed bf16 hi = (bf16(a), bf16(b)) and lo = bf16 of the remainders.
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
+}
+struct XOp {
+  bf16x8 hi, lo;
+};
+__device__ __forceinline__ XOp x_operand(float4 x0, float4 x1) {
+  uint4 h, l;
+  split_bf16(x0.x, x0.y, h.x, l.x);
+  split_bf16(x0.z, x0.w, h.y, l.y);
+  split_bf16(x1.x, x1.y, h.z, l.z);
+  split_bf16(x1.z, x1.w, h.w, l.w);
+  return {__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, l)};
+}
+
+// One pass: row blocks [rb0, rb0 + NRB) over the wavefront's k-steps [ks0, ks1).
+template <int NRB, int KG>
+__device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
+                                          float* acc, int nrows, int rb0, int ks0, int ks1) {
+  const int lane = tidx() & 63, li = lane & 15, lg = lane >> 4;
+  const int K = op.K, B = a.B;
+  const int nkg = (ks1 - ks0 + KG - 1) / KG;
+  const int klast = min((ks1 - 1) * 32 + lg * 8, K - 8);   // the lane's last k in range
+  const int xoff = min(li, B - 1) * K;                      // x row of the lane's request
+  gptr<const uint16_t> rows[NRB];
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) rows[r] = gemv_row(a, t.type, P, t.a0, min((rb0 + r) * 16 + li, nrows - 1));
+  uint4 wv[NRB][KG];
+  float4 xr[2 * KG];
+  XOp xo[KG];
+  f32x4 c[NRB];
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) c[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  auto kof = [&](int kg, int j) { return min((ks0 + kg * KG + j) * 32 + lg * 8, klast); };
+  auto wload = [&](int kg, int r) {
+#pragma unroll
+    for (int j = 0; j < KG; ++j) wv[r][j] = ldg<uint4>(rows[r] + kof(kg, j));
+  };
+  auto xload = [&](int kg) {
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      xr[2 * j] = ld4_coh(op.x, xoff + kof(kg, j), B * K);
+      xr[2 * j + 1] = ld4_coh(op.x, xoff + kof(kg, j) + 4, B * K);
+    }
+  };
+  auto xconvert = [&](int kg) {
+    const float4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const bool in = ks0 + kg * KG + j < ks1;
+      xo[j] = x_operand(in ? xr[2 * j] : z, in ? xr[2 * j + 1] : z);
+    }
+  };
+  auto mul = [&](int r) {
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const bf16x8 w = __builtin_bit_cast(bf16x8, wv[r][j]);
+      c[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xo[j].hi, c[r], 0, 0, 0);
+      c[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, xo[j].lo, c[r], 0, 0, 0);
+    }
+  };
+  xload(0);
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) wload(0, r);
+  for (int kg = 0; kg + 1 < nkg; ++kg) {
+    xconvert(kg);
+    xload(kg + 1);
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) {
+      mul(r);
+      wload(kg + 1, r);
+    }
+  }
+  xconvert(nkg - 1);
+#pragma unroll
+  for (int r = 0; r < NRB; ++r) mul(r);
+#pragma unroll
+  for (int r = 0; r < NRB; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (rb0 + r) * 16 + lg * 4 + i;
+      if (li < B && row < nrows) atomicAdd(&acc[row * B + li], c[r][i]);
+    }
+}
+
+template <int NRB, int KG>
+__device__ __forceinline__ void mfma_passes(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
+                                            float* acc, int nrows, int nrb, int ks0, int ks1) {
+  for (int rb0 = 0; rb0 < nrb; rb0 += NRB) mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, ks0, ks1);
+}
+
+__device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
   const int tid0 = tidx();
-  constexpr int U = 4;
   const GemvOp op = gemv_op(a, t);
   const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc, B = a.B;
   float* acc = reinterpret_cast<float*>(lds + a.lds_acc);
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
   for (int i = tid0; i < nrows * B; i += kThreads) acc[i] = 0.f;
   __syncthreads();
-  const int nseg = (K + 511) >> 9, S = nrows * nseg;
-  const int w = tid0 >> 6, lane = tid0 & 63;
-  const int s_beg = (int)((int64_t)S * w / kWaves), total = (int)((int64_t)S * (w + 1) / kWaves) - s_beg;
-  if (total > 0) {
-    SegWalk ld = seg_start(a, t, P, nseg, s_beg);
-    int cur = ld.r, done = 0;
-    float av[kMaxBatch];
-#pragma unroll
-    for (int b = 0; b < kMaxBatch; ++b) av[b] = 0.f;
-    while (done < total) {
-      uint4 wv[U];
-      int rr[U], kk[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        rr[u] = ld.r;
-        kk[u] = ld.ks * 512 + lane * 8;
-        wv[u] = ldg<uint4>(ld.row + min(kk[u], K - 8));
-        if (done + u + 1 < total) seg_next(a, t, P, nseg, ld);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (done < total) {
-          if (rr[u] != cur) {
-#pragma unroll
-            for (int b = 0; b < kMaxBatch; ++b) {
-              if (b < B) {
-                const float v = wave_sum(av[b]);
-                if (lane == 0) atomicAdd(&acc[cur * B + b], v);
-              }
-              av[b] = 0.f;
-            }
-            cur = rr[u];
-          }
-          if (kk[u] < K) {
-#pragma unroll
-            for (int b = 0; b < kMaxBatch; ++b)
-              if (b < B) {
-                gptr<const float> xr = op.x + (int64_t)b * K;
-                av[b] = dot8(wv[u], ld4_coh(xr, kk[u], K), ld4_coh(xr, kk[u] + 4, K), av[b]);
-              }
-          }
-          ++done;
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kMaxBatch; ++b)
-      if (b < B) {
-        const float v = wave_sum(av[b]);
-        if (lane == 0) atomicAdd(&acc[cur * B + b], v);
-      }
+  const int w = tid0 >> 6;
+  const int nks = (K + 31) >> 5, nrb = (nrows + 15) >> 4;
+  const int ks0 = nks * w / kWaves, ks1 = nks * (w + 1) / kWaves;
+  // weights in flight per wavefront: NRB x KG KB
+  if (ks1 > ks0) {
+    if (nrb <= 2) mfma_passes<2, 4>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
+    else if (nrb <= 4) mfma_passes<4, 4>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
+    else mfma_passes<8, 2>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
   }
   __syncthreads();
   gemv_epilogue(a, t, acc, red);
@@ -1194,28 +1260,28 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
   const int l = t.layer;
   switch (t.type) {
     case MPK_TASK_EMBED:
-      embed_task(a);
+      embed_task(a, t.a0);
       break;
     case MPK_TASK_ATTN_NORM:
-      if (l == 0) norm_task(a, a.e, nullptr, a.r, P.p0, a.h, lds, red);
+      if (l == 0) norm_task(a, t.a0, a.e, nullptr, a.r, P.p0, a.h, lds, red);
       else
-        norm_task(a, a.s + (int64_t)(l - 1) * a.st_bh, a.dn + (int64_t)(l - 1) * a.st_bh, a.r + (int64_t)l * a.st_bh,
-                  P.p0, a.h + (int64_t)l * a.st_bh, lds, red);
+        norm_task(a, t.a0, a.s + (int64_t)(l - 1) * a.st_bh, a.dn + (int64_t)(l - 1) * a.st_bh,
+                  a.r + (int64_t)l * a.st_bh, P.p0, a.h + (int64_t)l * a.st_bh, lds, red);
       break;
     case MPK_TASK_MLP_NORM:
-      norm_task(a, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_bh, a.s + (int64_t)l * a.st_bh,
+      norm_task(a, t.a0, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_bh, a.s + (int64_t)l * a.st_bh,
                 P.p0, a.h2 + (int64_t)l * a.st_bh, lds, red);
       break;
     case MPK_TASK_FINAL_NORM:
-      norm_task(a, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_bh, nullptr, P.p0, a.hf,
-                lds, red);
+      norm_task(a, t.a0, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_bh, nullptr, P.p0,
+                a.hf, lds, red);
       break;
     case MPK_TASK_QKV:
     case MPK_TASK_OPROJ:
     case MPK_TASK_GATEUP:
     case MPK_TASK_DOWN:
     case MPK_TASK_LMHEAD:
-      if (a.B > 1) gemv_bn(a, t, P, lds);
+      if (a.B > 1) gemv_mfma(a, t, P, lds);
       else if (a.gemv_d == 4) gemv_b1<4>(a, t, P, lds, pre);
       else gemv_b1<8>(a, t, P, lds, pre);
       break;

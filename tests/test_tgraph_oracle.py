@@ -72,11 +72,22 @@ def test_tiny_worked_example_order_and_counts():
 def test_tiny_worked_example_batch3_keeps_norm_tasks():
     g, tasks = tg.build(synth.SHAPES["tiny"].cfg(), 3, 16, TINY_PRM)
     tt = list(g["task_type"])
-    # EMBED + per layer (ATTN_NORM, 8 QKV, 3 x 2 x 4 ATTN, 4 OPROJ, MLP_NORM, 11 GATEUP, 4 DOWN) = 1 + 2 x 53,
-    # + FINAL_NORM + 16 LM + ARGMAX
-    assert len(tasks) == 1 + 2 * 53 + 18
-    assert tt.count(T_EMPTY := tg.EMPTY) == 8    # ATTN_NORM and MLP_NORM each feed two events
-    assert tt[:4] == [tg.EMBED, tg.ATTN_NORM, T_EMPTY, T_EMPTY]
+    T_EMPTY = tg.EMPTY
+    # Hand count: 3 EMBED (one per request) + per layer (3 ATTN_NORM, 8 QKV, 3 x 2 x 4 ATTN, 4 OPROJ,
+    # 3 MLP_NORM, 11 GATEUP, 4 DOWN) = 3 + 2 x 57, + 3 FINAL_NORM + 16 LM + ARGMAX = 137.
+    assert len(tasks) == 137
+    assert [tuple(t["coords"]) for t in tasks if t["type"] == tg.ATTN_NORM][:3] == [(0, 0, 0), (1, 0, 0), (2, 0, 0)]
+    # Each norm task feeds two events: the next projection's (all B norm tasks) and the next norm's
+    # (all B norm tasks + the projection tiles after them): 2 x (3 + 3) rewrites, 2 empties each.
+    # Fused events per layer: [ATTN_NORM], QKV, 2 attention groups, OPROJ, MLP_NORM, GATEUP, DOWN = 8;
+    # then FINAL_NORM, LM head, ARGMAX: 19.
+    h = g["header"]
+    assert h["n_rewrites"] == 12 and h["n_empty"] == 24 and tt.count(T_EMPTY) == 24 and h["n_fused"] == 19
+    assert h["NT"] == 137 + 24 and h["NE"] == 19 + 12 + 2
+    assert tt[:12] == [tg.EMBED] * 3 + [tg.ATTN_NORM] * 3 + [T_EMPTY] * 6
+    cnt = g["event_counts"]; dep = g["task_dep"]
+    assert all(int(cnt[dep[i]]) == 3 for i in range(3, 6))   # every layer-0 norm waits for the 3 embeddings
+    assert int(cnt[dep[12]]) == 3 and tt[12] == tg.QKV         # QKV waits for the 3 norms (via their empties)
     assert tg.QKNORM_ROPE not in tt and tg.COMBINE not in tt
     tg.check_semantics(g, tasks, closure=True)
 
@@ -113,9 +124,11 @@ def test_full_graph_invariants(name):
     g, _ = tg.build(s.cfg(), s.batch, s.page_size, prm)
     tg.check_semantics(g, None)
     h = g["header"]
-    assert h["n_empty"] / h["NT"] < 0.01          # "deep, not wide": under 1% empty tasks
-    # two tasks per layer fan out to two events (the residual keepers at batch 1, the norms otherwise)
-    assert h["n_empty"] == 4 * s.n_layers
+    # two tasks per layer (the residual keepers) fan out to two events at batch 1, the 2 B norm
+    # tasks per layer at batch B > 1; each such task gets two empties
+    per_layer = 2 if s.batch == 1 else 2 * s.batch
+    assert h["n_empty"] == 2 * per_layer * s.n_layers
+    assert h["n_empty"] / h["NT"] < (0.01 if s.batch == 1 else 0.05)   # "deep, not wide"
 
 
 # ------------------------------------------------------------------ random programs
