@@ -41,6 +41,17 @@ RMSNorm + RoPE, the KV-cache append and the split combine run inside the
 attention tasks, and at batch 1 the residual add + RMSNorm run inside the
 projection tiles that consume them (``fused_norm``).  Type ids 3
 (QKNORM_ROPE) and 5 (COMBINE) are therefore never emitted for the decoder.
+
+Attention slots (a choice of this build): kv group ``g`` has ``M = B * S``
+attention tasks, task ``(b, g, s)`` being slot ``j = b*S + s`` of the group.
+Which request a slot serves is decided when the step runs, from the
+sequence lengths, so that every slot gets about the same number of pages
+(a request with more cached tokens gets more splits).  A slot may therefore
+serve any request of its group, and every attention task declares the whole
+group: all B rows of the group's q/k/v columns as input; the group's partial
+records, attention output and cache rows of all B requests as outputs.  The
+events are the same as with per-request boxes (the group's projection tiles
+cover all B rows, and the O projection reads every group).
 """
 from __future__ import annotations
 
@@ -117,9 +128,10 @@ def decompose(cfg, B, P, prm: Params):
     [MLP_NORM] GATEUP tiles, DOWN tiles; then [FINAL_NORM] LMHEAD tiles and
     ARGMAX (bracketed tasks only at batch > 1, see ``fused_norm``).  An
     attention split also applies q/k RMSNorm and RoPE to its query heads, the
-    last split of (b, g) appends the new key/value to the cache, and the last
-    split of (b, g) to finish merges the S partials into the attention output
-    (so every split of (b, g) declares that output).
+    last split of a request appends the new key/value to the cache, and the
+    last split of a request to finish merges the request's partials into the
+    attention output (attention tasks declare their whole kv group, see the
+    module docstring on slots).
     """
     L = cfg["n_layers"]; H = cfg["hidden"]; hq = cfg["n_q_heads"]; hkv = cfg["n_kv_heads"]; d = cfg["head_dim"]
     F = cfg["ffn"]; V = cfg["vocab"]; S = prm.S_attn
@@ -155,12 +167,11 @@ def decompose(cfg, B, P, prm: Params):
         for b in range(B):
             for g in range(hkv):
                 for s in range(S):
-                    outs = [_box(t(L_PART), (b, g, s, 0), (b + 1, g + 1, s + 1, G * (d + 2))),
-                            _box(t(L_ATTN), (b, g * G * d), (b + 1, (g + 1) * G * d))]
-                    if s == S - 1:
-                        outs += [_box(t(L_KC), (b, 0, g, 0), (b + 1, maxs, g + 1, d)),
-                                 _box(t(L_VC), (b, 0, g, 0), (b + 1, maxs, g + 1, d))]
-                    add(ATTN, l, (b, g, s), [_box(t(L_QKV), (b, g * Sg), (b + 1, (g + 1) * Sg))], outs)
+                    outs = [_box(t(L_PART), (0, g, 0, 0), (B, g + 1, S, G * (d + 2))),
+                            _box(t(L_ATTN), (0, g * G * d), (B, (g + 1) * G * d)),
+                            _box(t(L_KC), (0, 0, g, 0), (B, maxs, g + 1, d)),
+                            _box(t(L_VC), (0, 0, g, 0), (B, maxs, g + 1, d))]
+                    add(ATTN, l, (b, g, s), [_box(t(L_QKV), (0, g * Sg), (B, (g + 1) * Sg))], outs)
         for n in range(prm.T_o):
             lo, hi = tile_range(H, prm.q, prm.T_o, n)
             add(OPROJ, l, (n,), [full(t(L_ATTN), hq * d)], [_box(t(L_O), (0, lo), (B, hi))])

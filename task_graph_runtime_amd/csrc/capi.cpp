@@ -191,9 +191,11 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
                         : chunks(H * 2) + 2 * chunks(H * 4);   // a norm task's gain and one row pair
   // attention: wavefront merge states, raw q/k/v row, processed heads
   stage = std::max(stage, chunks(kWaves * G * (d + 2) * 4) + 2 * chunks((G + 2) * d * 4));
-  // the split combine stages its records when they fit in 64 KB (else it reads them from global memory)
-  const int64_t comb = ((p.S_attn * G * (d + 2) + 63) & ~(int64_t)63) * 4;
-  if (comb <= 64 * 1024) stage = std::max(stage, comb);
+  // the split combine stages a request's records when they fit in 96 KB (else it reads them from
+  // global memory); a request gets at most B (S - 1) + 1 slots
+  const int64_t max_split = (int64_t)B * (p.S_attn - 1) + 1;
+  const int64_t comb = ((max_split * G * (d + 2) + 63) & ~(int64_t)63) * 4;
+  if (comb <= 96 * 1024) stage = std::max(stage, comb);
   // accumulators: the widest projection tile, rows per column x batch
   const int64_t tpg = p.T_qkv / hkv, Sg = (G + 2) * d;
   auto widest = [&](int64_t N, int64_t T) { return p.q * ((((N + p.q - 1) / p.q) + T - 1) / T); };
@@ -370,7 +372,6 @@ int upload(mpk_tgraph* t) {
   a.T_lm = t->prm.T_lm; a.qk_norm = c.qk_norm; a.max_seq = c.max_seq_len; a.eps = c.rms_eps; a.theta = c.rope_theta;
   a.wl = t->d_wl;
   a.arrive = t->d_arrive;
-  a.gemv_d = 4;
   return lds_layout(c, t->B, t->P, t->prm, &a);
 }
 
@@ -482,9 +483,6 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   }
   KArgs a = t->base;
   a.poll_sleep = 1;
-  if (const char* ps = std::getenv("MPK_POLL_SLEEP")) a.poll_sleep = std::atoi(ps);   // (experiment)
-  if (const char* ps = std::getenv("MPK_PF_SEGS")) a.pf_segs = std::min(a.pf_segs, std::atoi(ps));   // (experiment)
-  if (const char* ps = std::getenv("MPK_GEMV_D")) a.gemv_d = std::atoi(ps);   // (experiment)
   a.embed = (const uint16_t*)w->embed;
   a.lm_head = c.tied_embedding ? nullptr : (const uint16_t*)w->lm_head;
   a.final_norm = (const uint16_t*)w->final_norm;

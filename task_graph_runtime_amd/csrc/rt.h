@@ -128,7 +128,6 @@ struct KArgs {
   // each of the kPfWaves pre-loading wavefronts at lds_pf (pf_segs = 0: no
   // pre-load), and an attention split's page ids at lds_pid
   int32_t lds_acc, lds_pf, pf_segs, lds_pid;
-  int32_t gemv_d;                              // batch-1 projection: segments per register buffer (4 or 8)
   MPK_GLOBAL StatusWord* status;
   MPK_GLOBAL TraceRec* trace;                  // null: tracing off; else [n_workers][trace_cap]
   MPK_GLOBAL uint32_t* trace_count;            // [n_workers] records written in the last step

@@ -897,15 +897,61 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
 }
 
 // ------------------------------------------------------------------ paged attention, one split
-// Merge of the S_attn partial records (m, l, o[D]) of (b, g) into the
-// attention output: o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M},
-// M = max_s m_s (empty splits carry m = -inf, l = 0).  Run by the split that
-// finishes last.  The records are staged in LDS first when they fit.
-__device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g, char* lds) {
+// Attention slots.  Kv group g has M = B S_attn attention tasks; task
+// (b, g, s) is slot j = b S_attn + s.  When the step runs, request b gets
+// n_b = 1 + floor((M - B) pages_b / total) consecutive slots
+// (pages_b = ceil((L_b + 1) / P), total = their sum; a request with an
+// invalid length counts 0 pages), in request order; slots past the last
+// request's are idle, and splits past a request's pages are empty.  At batch
+// 1 that is all S_attn slots.  Every task computes the same allocation from
+// the B sequence lengths, so the splits of a long request are as short as
+// those of a short one and the group's tasks take about the same time.
+struct AttnSlot {
+  int b, s, n, start;   // request (-1: idle slot), its split, its split count, its first slot
+};
+__device__ __forceinline__ int attn_pages(const KArgs& a, int L) {
+  return (L >= 0 && L < a.max_seq && L / a.P < a.max_pages) ? (L + a.P) / a.P : 0;
+}
+// (one request per lane of the first 16: one vector load of the lengths, a
+// butterfly sum, a scan of the split counts and a ballot; the result is
+// wavefront-uniform)
+// one: batch 1, return {0, j, 0, 0} without loading anything (the caller
+// knows the split count, S_attn).
+__device__ __forceinline__ AttnSlot attn_slot(const KArgs& a, int j, bool one) {
+  const int lane = tidx() & 63, B = a.B, M = B * a.S_attn;
+  if (one) return AttnSlot{0, j, 0, 0};
+  const int L = a.seq_lens[min(lane, B - 1)];
+  const int pg = lane < B ? attn_pages(a, L) : 0;
+  int total = pg;
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) total += __shfl_xor(total, m, 16);
+  const int n = lane < B ? 1 + (int)((int64_t)(M - B) * pg / max(total, 1)) : 0;
+  int incl = n;
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+    const int v = __shfl_up(incl, d, 16);
+    if ((lane & 15) >= d) incl += v;
+  }
+  const int start = incl - n;
+  const unsigned long long mine = __ballot(lane < B && j >= start && j < incl);
+  if (mine == 0ull) return AttnSlot{-1, 0, 0, 0};
+  const int src = __ffsll((long long)mine) - 1;
+  const int st = __builtin_amdgcn_readfirstlane(__shfl(start, src));
+  return AttnSlot{src, j - st, __builtin_amdgcn_readfirstlane(__shfl(n, src)), st};
+}
+
+// Merge of the n partial records (m, l, o[D]) of a request, in slots
+// [start, start + n) of kv group g, into its attention output (row b):
+// o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}, M = max_s m_s (empty
+// splits carry m = -inf, l = 0).  Run by the split that finishes last.  The
+// records are staged in LDS first when they fit.
+__device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g, int start, int n_split,
+                                             char* lds) {
   const int tid0 = tidx();
-  const int G = a.G, D = a.d, S = a.S_attn;
+  const int G = a.G, D = a.d, S = n_split;
   const int rec = G * (D + 2);
-  gptr<const float> part = a.part + (int64_t)l * a.st_part + ((int64_t)b * a.hkv + g) * S * (int64_t)rec;
+  gptr<const float> part =
+      a.part + (int64_t)l * a.st_part + ((int64_t)g * a.B * a.S_attn + start) * (int64_t)rec;
   gptr<float> out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
   float* st = reinterpret_cast<float*>(lds);
   const int n = S * rec;   // (a multiple of 4: rec = G (D + 2) with D even)
@@ -945,9 +991,10 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
   else merge([&](int i) { return ld_coh(part + i); });
 }
 
-// Task (b, g, s): decode attention of request b's new query against pages
+// Task of slot j of kv group g, serving split s of the S splits of request b
+// (attn_slot): decode attention of request b's new query against pages
 // [floor(s n_b / S), floor((s+1) n_b / S)) of its n_b = ceil((L_b + 1) / P)
-// pages, for all G query heads of kv group g.
+// pages, for all G query heads of kv group g.  An idle slot does nothing.
 //  1. The group's raw q/k/v projection row (fp32) is staged in LDS; each of
 //     its G query heads and its key head gets per-head RMSNorm (qk_norm) and
 //     rotate-half RoPE at position L_b (angle L_b theta^(-2i/d), product and
@@ -962,8 +1009,9 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
 //     repeat its last token so the wait counts stay static).  R = 16 when
 //     G <= 4, 32 for G <= 8.  Row, wavefront and workgroup states merge with
 //     the log-sum-exp rule into the split's partial (m, l, o[d]) per head.
-//  3. The split adds itself to the (layer, b, g) arrival counter; the one
-//     that completes it merges all S partials into the attention output
+//  3. The split writes its partial to slot j, then adds itself to the
+//     (layer, b, g) arrival counter; the one that completes it (S arrivals)
+//     merges the request's S partials into the attention output
 //     (attn_combine) and resets the counter.
 template <int D, int R, int GM>
 __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, const TaskPtrs& Pw, char* lds) {
@@ -973,9 +1021,13 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
   constexpr int TPI = kWaves * RPW;     // tokens per iteration of the workgroup
   constexpr int HALF = D / 2;
   using KV = typename std::conditional<DPL == 8, uint4, typename std::conditional<DPL == 4, uint2, uint32_t>::type>::type;
-  const int b = t.a0, g = t.a1, s = t.a2, l = t.layer, G = a.G, P = a.P;
+  const int slot = t.a0 * a.S_attn + t.a2, g = t.a1, l = t.layer, G = a.G, P = a.P;
+  // at batch 1 the request is known (b = 0, s = slot), so the q/k/v row loads
+  // go out before the split count, which needs the length, is known
+  AttnSlot sl = attn_slot(a, slot, a.B == 1);
+  if (sl.b < 0) return;
+  const int b = sl.b, s = sl.s;
   const int w = tid0 >> 6, lane = tid0 & 63, row = lane / R, lr = lane % R;
-  const bool last_split = s == a.S_attn - 1;
   // LDS: wavefront merge states [kWaves][G][D + 2] at 0, the raw q/k/v row at
   // o_raw, the processed heads [G + 2][D] (G query heads scaled by 1/sqrt(D),
   // the new key, the new value) at o_qk
@@ -992,10 +1044,13 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
 
   const int Lb = a.seq_lens[b];
   const bool ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
-  if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, t.id, -1, (uint32_t)Lb, 0u);
   const int ntok = ok ? Lb + 1 : 0;
   const int nb = (ntok + P - 1) / P;
-  const int j0 = (int)((int64_t)s * nb / a.S_attn), j1 = (int)((int64_t)(s + 1) * nb / a.S_attn);
+  // at batch 1, attn_slot's allocation for one request: min(pages, S_attn) splits, at least 1
+  const int S = a.B == 1 ? a.S_attn : sl.n;   // (attn_slot's allocation for one request)
+  const bool last_split = s == S - 1;
+  if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, t.id, -1, (uint32_t)Lb, 0u);
+  const int j0 = (int)((int64_t)s * nb / S), j1 = (int)((int64_t)(s + 1) * nb / S);
   const int t0 = j0 * P, t1 = min(j1 * P, ntok);
   const int tc1 = min(t1, ntok - 1);    // cached tokens of the split: [t0, tc1)
   int* pids = reinterpret_cast<int*>(lds + a.lds_pid);   // page ids of pages j0..j1-1
@@ -1175,8 +1230,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
     }
   }
   __syncthreads();
-  gptr<float> out = a.part + (int64_t)l * a.st_part +
-                    (((int64_t)b * a.hkv + g) * a.S_attn + s) * (int64_t)(G * (D + 2));
+  gptr<float> out = a.part + (int64_t)l * a.st_part + ((int64_t)g * a.B * a.S_attn + slot) * (int64_t)(G * (D + 2));
   for (int e = tid0; e < G * D; e += kThreads) {
     const int h = e / D, dd = e - h * D;
     float M = -INFINITY;
@@ -1208,12 +1262,12 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
   if (tid0 == 0) {
     gptr<uint32_t> ctr = a.arrive + ((int64_t)l * a.B + b) * a.hkv + g;
     const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old + 1u == (uint32_t)a.S_attn;
+    const int last = old + 1u == (uint32_t)S;
     if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
   __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(*flag)) attn_combine(a, l, b, g, lds);
+  if (__builtin_amdgcn_readfirstlane(*flag)) attn_combine(a, l, b, g, sl.start, S, lds);
   __syncthreads();
 }
 
@@ -1282,8 +1336,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
     case MPK_TASK_DOWN:
     case MPK_TASK_LMHEAD:
       if (a.B > 1) gemv_mfma(a, t, P, lds);
-      else if (a.gemv_d == 4) gemv_b1<4>(a, t, P, lds, pre);
-      else gemv_b1<8>(a, t, P, lds, pre);
+      else gemv_b1<4>(a, t, P, lds, pre);
       break;
     case MPK_TASK_ATTN:
       if (a.d == 128) {

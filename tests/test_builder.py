@@ -79,7 +79,7 @@ def test_default_params_resolve_as_documented():
     assert p["n_workers"] == 252 and p["n_sched_waves"] == 14 and p["quantum"] == 1
     assert p["t_qkv"] == 248 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 252 and p["s_attn"] == 8
     h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
-    assert h16["quantum"] == 16 and h16["s_attn"] == 4
+    assert h16["quantum"] == 16 and h16["s_attn"] == 3   # floor(2 x 252 / (16 x 8)) slots per request
     # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
     assert h16["t_lm"] == 504 and h16["t_gu"] == 252
 
