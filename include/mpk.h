@@ -103,6 +103,10 @@ typedef struct {
   int32_t host_only;     /* 1: build on the host only (no device work); export still works */
   int32_t fusion_order;  /* must be 0: Def 4.1 then Def 4.2                               */
   int32_t aot_policy;    /* must be 0: round-robin over workers in linear order           */
+  int32_t attn_jit;      /* attention tasks: 0 default (JIT at batch > 1, where the splits */
+                         /* of an event differ in cost with the requests' lengths; AOT at */
+                         /* batch 1, where they are equal), 1 JIT, 2 AOT; the exported    */
+                         /* header holds the resolved value (1 or 2)                      */
 } mpk_build_params;
 
 typedef struct mpk_tgraph mpk_tgraph; /* opaque; owned by the library */

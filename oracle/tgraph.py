@@ -18,7 +18,10 @@ Mega-Kernelizing Tensor Programs -- L2"):
 * section 4 check 4 (Alg 1): BFS linearisation places the dependent tasks of
   each dequeued event consecutively, so fan-out is a ``[first, last]`` range;
 * section 4, design-space table: JIT for data-dependent attention, AOT for
-  the rest.
+  the rest.  Which attention counts as data-dependent is a parameter
+  (``Params.jit_attn``); the library's default makes it JIT at batch > 1,
+  where an event's splits serve requests of different lengths, and AOT at
+  batch 1, where every split of the step has the same pages.
 The HN comment (item 2) fixes the dependency rule: B depends on A iff A
 produces any element B consumes.
 
@@ -88,6 +91,7 @@ class Params:
     T_down: int = 1
     T_lm: int = 1
     S_attn: int = 1
+    jit_attn: bool = True   # attention tasks JIT (else AOT)
 
 
 def tile_range(N, q, T, n):
@@ -224,7 +228,7 @@ def producer_sets(tasks):
     return P
 
 
-def canonicalize(tasks, W):
+def canonicalize(tasks, W, jit_attn=True):
     """Fusion (Def 4.1 then 4.2), normalisation, Kahn-BFS linearisation,
     classification and AOT placement.  Returns the exported arrays (dict)."""
     N = len(tasks)
@@ -307,7 +311,7 @@ def canonicalize(tasks, W):
 
     order = sorted(range(NT), key=lambda t: new_task[t])
     eorder = sorted(range(NE), key=lambda e: new_ev[e])
-    mode = {EMPTY: MODE_EMPTY, ATTN: MODE_JIT}
+    mode = {EMPTY: MODE_EMPTY, ATTN: MODE_JIT if jit_attn else MODE_AOT}
     out = {
         "task_type": np.array([ttype[t] for t in order], dtype=np.uint8),
         "task_mode": np.array([mode.get(ttype[t], MODE_AOT) for t in order], dtype=np.uint8),
@@ -348,7 +352,7 @@ def canonicalize(tasks, W):
 def build(cfg, B, P, prm: Params):
     """The whole spec for a decoder: decompose, then canonicalise."""
     tasks = decompose(cfg, B, P, prm)
-    return canonicalize(tasks, prm.W), tasks
+    return canonicalize(tasks, prm.W, prm.jit_attn), tasks
 
 
 # ----------------------------------------------------------------------------- checker
@@ -388,7 +392,9 @@ def check_semantics(g, tasks=None, closure=True):
     assert np.all(maxprod[dep] < np.arange(NT))
     # degree-1 structure and modes
     tt = g["task_type"]; md = g["task_mode"]
-    assert np.all((md == MODE_JIT) == (tt == ATTN)) and np.all((md == MODE_EMPTY) == (tt == EMPTY))
+    # JIT tasks are attention tasks, all of one mode (JIT or AOT); EMPTY exactly the empties
+    assert np.all((md != MODE_JIT) | (tt == ATTN)) and np.all((md == MODE_EMPTY) == (tt == EMPTY))
+    assert len(set(md[tt == ATTN].tolist())) <= 1
     for e in range(NE):
         cons = md[first[e]:last[e] + 1]
         f = (FLAG_HAS_JIT if np.any(cons == MODE_JIT) else 0) | (FLAG_HAS_EMPTY if np.any(cons == MODE_EMPTY) else 0)

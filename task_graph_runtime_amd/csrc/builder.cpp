@@ -57,6 +57,7 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   const mpk_build_params& p = in ? *in : z;
   if (p.fusion_order != 0) return uns("only fusion order 0 (Def 4.1 then Def 4.2) is implemented");
   if (p.aot_policy != 0) return uns("only AOT policy 0 (round-robin in linear order) is implemented");
+  if (p.attn_jit < 0 || p.attn_jit > 2) return bad("attn_jit must be 0, 1 or 2");
   Params r;
   // default scheduler count: the largest S <= 16 that divides the worker
   // count, so that every scheduler deals over the same number of workers
@@ -102,6 +103,9 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
     int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, 2 * r.W / ((int64_t)B * hkv)));
     r.S_attn = (int32_t)std::min<int64_t>(s, max_pages);
   }
+  // hybrid policy: attention JIT where its tasks' costs vary at run time
+  // (batch > 1: per-request lengths), AOT at batch 1 (equal splits)
+  r.jit_attn = p.attn_jit == 1 || (p.attn_jit == 0 && B > 1);
   if (r.T_qkv / hkv > cdiv(Sg, r.q)) return bad("t_qkv: more tiles per kv group than column quanta");
   struct { int64_t T, N, rows_per_col; const char* name; } ops[] = {
       {r.T_qkv / hkv, Sg, 1, "t_qkv"}, {r.T_o, H, 1, "t_o"}, {r.T_gu, F, 2, "t_gu"},
@@ -204,7 +208,7 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
   add(MPK_TASK_ARGMAX, -1, 0, 0, 0, {box(T_PMAX, {0, 0, 0}, {B, p.T_lm, 2})}, {box(T_NEXT, {0}, {B})});
 }
 
-int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, Graph* out, std::string* err) {
+int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, bool jit_attn, Graph* out, std::string* err) {
   const int32_t N = (int32_t)tasks.size();
   if (W < 1) { *err = "n_workers must be positive"; return MPK_ERR_INVALID_ARG; }
 
@@ -316,8 +320,8 @@ int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, Graph* out, std::
   std::vector<int32_t> order(NT), eorder(NE);
   for (int32_t t = 0; t < NT; ++t) order[new_task[t]] = t;
   for (int32_t e = 0; e < NE; ++e) eorder[new_ev[e]] = e;
-  auto mode_of = [](int32_t type) {
-    return type == MPK_TASK_EMPTY ? MPK_MODE_EMPTY : type == MPK_TASK_ATTN ? MPK_MODE_JIT : MPK_MODE_AOT;
+  auto mode_of = [jit_attn](int32_t type) {
+    return type == MPK_TASK_EMPTY ? MPK_MODE_EMPTY : type == MPK_TASK_ATTN && jit_attn ? MPK_MODE_JIT : MPK_MODE_AOT;
   };
   g.task_type.resize(NT); g.task_mode.resize(NT); g.task_layer.resize(NT); g.task_coords.resize(3 * (size_t)NT);
   g.task_orig.resize(NT); g.task_dep.resize(NT); g.task_trig.resize(NT); g.task_worker.assign(NT, -1);

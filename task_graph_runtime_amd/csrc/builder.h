@@ -34,6 +34,7 @@ struct TaskDef {
 struct Params {
   int32_t W = 1, S_sched = 16, q = 1;
   int32_t T_qkv = 1, T_o = 1, T_gu = 1, T_down = 1, T_lm = 1, S_attn = 1;
+  bool jit_attn = true;   // attention tasks JIT (else AOT)
 };
 
 // The linearised graph (task index = linear position), as exported.
@@ -83,6 +84,6 @@ inline bool fused_norm(int32_t B) { return B == 1; }
 void decompose(const mpk_model_cfg& cfg, int32_t B, const Params& p, std::vector<TaskDef>* tasks);
 
 // Canonicalisation pipeline on arbitrary tasks; MPK_ERR_GRAPH on a cycle.
-int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, Graph* g, std::string* err);
+int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, bool jit_attn, Graph* g, std::string* err);
 
 }  // namespace mpk

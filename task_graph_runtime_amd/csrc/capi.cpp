@@ -529,10 +529,11 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   mpk_build_params r{};
   r.n_workers = prm.W; r.n_sched_waves = prm.S_sched; r.quantum = prm.q; r.t_qkv = prm.T_qkv; r.t_o = prm.T_o;
   r.t_gu = prm.T_gu; r.t_down = prm.T_down; r.t_lm = prm.T_lm; r.s_attn = prm.S_attn; r.host_only = host_only;
+  r.attn_jit = prm.jit_attn ? 1 : 2;
   t->resolved = r;
   std::vector<TaskDef> tasks;
   decompose(*cfg, batch, prm, &tasks);
-  rc = canonicalize(tasks, prm.W, &t->g, &err);
+  rc = canonicalize(tasks, prm.W, prm.jit_attn, &t->g, &err);
   if (rc) { free_tgraph(t); return fail(rc, err); }
   rc = check_runtime_shape(t->g);
   if (rc) { free_tgraph(t); return rc; }
@@ -590,12 +591,12 @@ int mpk_build_generic(const mpk_task_spec* specs, int32_t n_tasks, const mpk_reg
   }
   Graph g;
   std::string err;
-  int rc = canonicalize(tasks, n_workers, &g, &err);
+  int rc = canonicalize(tasks, n_workers, true, &g, &err);
   if (rc) return fail(rc, err);
   mpk_tgraph_header h{};
   h.n_tasks = g.NT; h.n_events = g.NE; h.root = g.root; h.end = g.end; h.n_fused = g.n_fused;
   h.n_empty = g.n_empty; h.n_rewrites = g.n_rewrites; h.n_aot = (int32_t)g.aot_tasks.size();
-  h.params.n_workers = n_workers; h.params.host_only = 1;
+  h.params.n_workers = n_workers; h.params.host_only = 1; h.params.attn_jit = 1;
   return export_graph(g, h, out);
 }
 

@@ -31,7 +31,7 @@ def both(shape, B, W, q=None, S=None, **over):
     from the library's header)."""
     s = shape
     names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm")
-    params = dict(n_workers=W, s_attn=S or 4)
+    params = dict(n_workers=W, s_attn=S or 4, attn_jit=over.pop("attn_jit", 0))
     if q is not None:
         params["quantum"] = q
     for k, v in over.items():
@@ -39,16 +39,33 @@ def both(shape, B, W, q=None, S=None, **over):
     g = mpk.TGraph(s.cfg(), B, s.page_size, params, host_only=True)
     p = g.header()["params"]
     prm = tg.Params(W=p["n_workers"], S_sched=p["n_sched_waves"], q=p["quantum"], T_qkv=p["t_qkv"], T_o=p["t_o"],
-                    T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"])
+                    T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"],
+                    jit_attn=p["attn_jit"] == 1)
     ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
-    return ref, g.export(), tasks
+    got = g.export()
+    got["params"] = p
+    return ref, got, tasks
 
 
-def test_tiny_worked_example_bit_exact():
+@pytest.mark.parametrize("attn_jit", [0, 1, 2])
+def test_tiny_worked_example_bit_exact(attn_jit):
     s = synth.SHAPES["tiny"]
-    ref, got, tasks = both(s, 1, 8, q=64, S=4, T_qkv=8, T_o=4, T_gu=11, T_down=4, T_lm=16)
+    ref, got, tasks = both(s, 1, 8, q=64, S=4, T_qkv=8, T_o=4, T_gu=11, T_down=4, T_lm=16, attn_jit=attn_jit)
     assert_same(ref, got)
     assert got["header"]["NT"] == 95 and got["header"]["NE"] == 19
+    # default at batch 1: attention AOT
+    assert got["params"]["attn_jit"] == (1 if attn_jit == 1 else 2)
+    n_jit = int(np.sum(got["task_mode"] == tg.MODE_JIT))
+    assert n_jit == (16 if attn_jit == 1 else 0)
+    tg.check_semantics(got, tasks, closure=True)
+
+
+@pytest.mark.parametrize("B,attn_jit,resolved", [(2, 0, 1), (2, 2, 2), (16, 0, 1)])
+def test_attention_policy_at_batch_above_one(B, attn_jit, resolved):
+    s = synth.SHAPES["tiny"].with_(n_layers=1)
+    ref, got, tasks = both(s, B, 13, S=2, attn_jit=attn_jit)
+    assert_same(ref, got)
+    assert got["params"]["attn_jit"] == resolved
     tg.check_semantics(got, tasks, closure=True)
 
 

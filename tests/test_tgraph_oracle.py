@@ -92,6 +92,20 @@ def test_tiny_worked_example_batch3_keeps_norm_tasks():
     tg.check_semantics(g, tasks, closure=True)
 
 
+def test_tiny_worked_example_aot_attention():
+    # the same graph with attention placed ahead of time: identical tasks and events, no JIT flag,
+    # and the round-robin placement now runs over the attention tasks too
+    from dataclasses import replace
+    g, _ = tiny()
+    ga, tasks = tg.build(synth.SHAPES["tiny"].cfg(), 1, 16, replace(TINY_PRM, jit_attn=False))
+    for k in ("task_type", "task_dep", "task_trig", "event_counts", "event_first", "event_last"):
+        assert np.array_equal(g[k], ga[k]), k
+    assert not np.any(ga["task_mode"] == tg.MODE_JIT) and not np.any(ga["event_flags"] & tg.FLAG_HAS_JIT)
+    aot = [i for i in range(len(ga["task_type"])) if ga["task_mode"][i] == tg.MODE_AOT]
+    assert len(aot) == 87 and [int(ga["task_worker"][i]) for i in aot] == [k % 8 for k in range(87)]
+    tg.check_semantics(ga, tasks, closure=True)
+
+
 def test_rewrite_identities():
     g, tasks = tiny()
     P = tg.producer_sets(tasks)
