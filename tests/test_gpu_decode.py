@@ -141,6 +141,20 @@ def test_tiny_intermediates_layer_by_layer(B):
     check_cache(inp, cap)
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_tiny_eight_query_heads_per_group(B):
+    """The G = 8 attention body (32 lanes per key row, as at the 32B shape) on a
+    small decoder: 16 q heads over 2 kv heads of 128 dims."""
+    s = TINY.with_(n_q_heads=16, n_kv_heads=2, head_dim=128, qk_norm=True, batch=B, ctx_range=(30, 250), ctx=0)
+    say("tiny G=8", B)
+    inp = device_inputs(s, seed=21 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    logits, nxt = Runner(inp).run("mega")
+    check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+
+
 @pytest.mark.parametrize("B,lens", [
     (3, [0, 15, 16]),              # empty context; new token ends a page; new token opens a page
     (4, [1, 31, 100, 255]),        # 255 = max_seq_len - 1: the last slot
@@ -243,6 +257,11 @@ def test_qwen3_8b_shape():
 @pytest.mark.timeout(600)
 def test_qwen3_8b_batch16_shape():
     _full("qwen3_8b_b16", modes=("mega",), lazy=True)
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_32b_shape():
+    _full("qwen3_32b", modes=("mega",), lazy=True)
 
 
 def test_trace_happens_before_every_wait():
