@@ -92,9 +92,10 @@ typedef struct {
  * the exported header so that a checker can rebuild the same graph. */
 typedef struct {
   int32_t n_workers;     /* W worker workgroups (default: compute units - scheduler WGs) */
-  int32_t n_sched_waves; /* scheduler wavefronts, 4 per scheduler WG (default: the largest */
-                         /* S <= 16 dividing the worker count; 14 on 256 compute units);  */
-                         /* each serves at most 64 workers (checked when the graph uploads) */
+  int32_t n_sched_waves; /* scheduler wavefronts, 4 per scheduler WG (default: none when  */
+                         /* no task is JIT, so every compute unit is a worker; else the   */
+                         /* largest S <= 16 dividing the worker count, 14 on 256 compute  */
+                         /* units); each serves at most 64 workers (checked at upload)    */
   int32_t quantum;       /* column quantum of projection tiles (default 1 at B=1, else 16) */
   int32_t t_qkv, t_o, t_gu, t_down, t_lm; /* tiles per projection (default ~W; t_qkv a
                                              multiple of n_kv_heads)                    */

@@ -59,12 +59,17 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   if (p.aot_policy != 0) return uns("only AOT policy 0 (round-robin in linear order) is implemented");
   if (p.attn_jit < 0 || p.attn_jit > 2) return bad("attn_jit must be 0, 1 or 2");
   Params r;
-  // default scheduler count: the largest S <= 16 that divides the worker
-  // count, so that every scheduler deals over the same number of workers
-  // (an event's JIT tasks go to one scheduler's workers)
+  // hybrid policy: attention JIT where its tasks' costs vary at run time
+  // (batch > 1: per-request lengths), AOT at batch 1 (equal splits)
+  r.jit_attn = p.attn_jit == 1 || (p.attn_jit == 0 && B > 1);
+  // default scheduler count: none when nothing is JIT (every compute unit
+  // is a worker), else the largest S <= 16 that divides the worker count, so
+  // that every scheduler deals over the same number of workers
   auto workers_for = [&](int32_t S) { return p.n_workers > 0 ? p.n_workers : n_cus - (S + 3) / 4; };
   if (p.n_sched_waves > 0) {
     r.S_sched = p.n_sched_waves;
+  } else if (!r.jit_attn) {
+    r.S_sched = 0;
   } else {
     r.S_sched = 1;
     for (int32_t S = 16; S >= 1; --S)
@@ -103,9 +108,6 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
     int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, 2 * r.W / ((int64_t)B * hkv)));
     r.S_attn = (int32_t)std::min<int64_t>(s, max_pages);
   }
-  // hybrid policy: attention JIT where its tasks' costs vary at run time
-  // (batch > 1: per-request lengths), AOT at batch 1 (equal splits)
-  r.jit_attn = p.attn_jit == 1 || (p.attn_jit == 0 && B > 1);
   if (r.T_qkv / hkv > cdiv(Sg, r.q)) return bad("t_qkv: more tiles per kv group than column quanta");
   struct { int64_t T, N, rows_per_col; const char* name; } ops[] = {
       {r.T_qkv / hkv, Sg, 1, "t_qkv"}, {r.T_o, H, 1, "t_o"}, {r.T_gu, F, 2, "t_gu"},

@@ -228,7 +228,9 @@ int upload(mpk_tgraph* t) {
   t->grid = t->n_sched_wgs + t->prm.W;
   if (t->grid > t->n_cus)
     return fail(MPK_ERR_INVALID_ARG, "workers + scheduler workgroups exceed the compute units");
-  if ((t->prm.W + t->n_sched - 1) / t->n_sched > 64)
+  if (t->n_sched == 0 && std::count(g.task_mode.begin(), g.task_mode.end(), (uint8_t)MPK_MODE_JIT) > 0)
+    return fail(MPK_ERR_INVALID_ARG, "JIT tasks need at least one scheduler wavefront");
+  if (t->n_sched > 0 && (t->prm.W + t->n_sched - 1) / t->n_sched > 64)
     return fail(MPK_ERR_INVALID_ARG, "more than 64 workers per scheduler wavefront");
 
   fill_descriptors(t);
@@ -250,7 +252,7 @@ int upload(mpk_tgraph* t) {
   // on different schedulers (and so on different workers).  The device copy
   // of the event keeps its starting scheduler in flags bits 16..31.
   std::vector<DevEvent> ev(g.NE);
-  const int32_t chunk = std::max<int32_t>(1, t->prm.W / t->n_sched);
+  const int32_t chunk = std::max<int32_t>(1, t->prm.W / std::max(1, t->n_sched));
   int64_t n_entries = 0;
   if (g.NE >= (1 << kJitEventBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 2^20 events");
   for (int32_t e = 0; e < g.NE; ++e) {

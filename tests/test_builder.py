@@ -92,10 +92,12 @@ def test_default_params_resolve_as_documented():
     s = synth.SHAPES["qwen3_8b"]
     h = mpk.TGraph(s.cfg(), 1, 64, {}, host_only=True).header()
     p = h["params"]
-    # 14 scheduler wavefronts (4 workgroups) leave 252 workers, 18 per scheduler
-    assert p["n_workers"] == 252 and p["n_sched_waves"] == 14 and p["quantum"] == 1
-    assert p["t_qkv"] == 248 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 252 and p["s_attn"] == 8
+    # batch 1: attention is AOT, nothing is JIT, so no scheduler workgroups: 256 workers
+    assert p["n_workers"] == 256 and p["n_sched_waves"] == 0 and p["quantum"] == 1 and p["attn_jit"] == 2
+    assert p["t_qkv"] == 256 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 256 and p["s_attn"] == 8
     h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
+    # batch 16: JIT attention; 14 scheduler wavefronts (4 workgroups) leave 252 workers, 18 per scheduler
+    assert h16["n_workers"] == 252 and h16["n_sched_waves"] == 14 and h16["attn_jit"] == 1
     assert h16["quantum"] == 16 and h16["s_attn"] == 3   # floor(2 x 252 / (16 x 8)) slots per request
     # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
     assert h16["t_lm"] == 504 and h16["t_gu"] == 252
