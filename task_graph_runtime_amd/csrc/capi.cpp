@@ -65,6 +65,8 @@ struct mpk_tgraph {
   uint32_t epoch = 0;
 
   std::vector<DevTask> h_tasks;
+  std::vector<uint32_t> dev_counts;   // device event counts (two-level events: non-empty sub-counters)
+  std::vector<uint16_t> quota;        // [NE][kEvSub] arrivals per sub-counter and step
   void* d_graph = nullptr;  // tasks, events, aot offsets, aot tasks
   DevTask* d_tasks = nullptr;
   DevEvent* d_events = nullptr;
@@ -73,6 +75,8 @@ struct mpk_tgraph {
   std::vector<AotEntry> h_aot;  // host copy; its weight pointers follow the last step's weights
   void* d_rt = nullptr;     // counters, rings, state, status
   uint32_t* d_ev_cnt = nullptr;
+  uint32_t* d_ev_sub = nullptr;
+  uint16_t* d_ev_quota = nullptr;
   unsigned long long* d_sched_ring = nullptr;
   uint32_t* d_sched_tail = nullptr;
   unsigned long long* d_jit_ring = nullptr;
@@ -104,6 +108,31 @@ struct mpk_tgraph {
 
 namespace {
 
+// Two-level events (see rt.h): per event, the arrivals of each sub-counter
+// (producer t counts on sub-counter t mod kEvSub) and the device count.
+int two_level_events(mpk_tgraph* t) {
+  const Graph& g = t->g;
+  t->dev_counts.assign(g.event_counts.begin(), g.event_counts.end());
+  std::vector<uint32_t> q((size_t)g.NE * kEvSub, 0);
+  for (int32_t i = 0; i < g.NT; ++i)
+    if (g.task_trig[i] >= 0) ++q[(size_t)g.task_trig[i] * kEvSub + (i % kEvSub)];
+  t->quota.assign(q.size(), 0);
+  for (int32_t e = 0; e < g.NE; ++e) {
+    if (g.event_counts[e] < kTwoLevelMin) continue;
+    uint32_t nnz = 0, sum = 0;
+    for (int k = 0; k < kEvSub; ++k) {
+      const uint32_t v = q[(size_t)e * kEvSub + k];
+      if (v > 65535) return fail(MPK_ERR_UNSUPPORTED, "more than 65535 producers on one event sub-counter");
+      t->quota[(size_t)e * kEvSub + k] = (uint16_t)v;
+      nnz += v > 0;
+      sum += v;
+    }
+    if (sum != g.event_counts[e]) return fail(MPK_ERR_GRAPH, "event count differs from its producers");
+    t->dev_counts[e] = nnz;
+  }
+  return MPK_OK;
+}
+
 void fill_descriptors(mpk_tgraph* t) {
   const Graph& g = t->g;
   const Params& p = t->prm;
@@ -118,7 +147,7 @@ void fill_descriptors(mpk_tgraph* t) {
     d.dep = g.task_dep[i];
     d.trig = g.task_trig[i];
     d.id = i;
-    d.dep_counts = g.event_counts[d.dep];
+    d.dep_counts = t->dev_counts[d.dep];
     const int32_t c0 = g.task_coords[3 * (size_t)i], c1 = g.task_coords[3 * (size_t)i + 1],
                   c2 = g.task_coords[3 * (size_t)i + 2];
     int32_t lo = 0, hi = 0;
@@ -233,6 +262,7 @@ int upload(mpk_tgraph* t) {
   if (t->n_sched > 0 && (t->prm.W + t->n_sched - 1) / t->n_sched > 64)
     return fail(MPK_ERR_INVALID_ARG, "more than 64 workers per scheduler wavefront");
 
+  if (int rc = two_level_events(t)) return rc;
   fill_descriptors(t);
   // graph arrays
   const int64_t o_tasks = 0, o_events = align256(o_tasks + (int64_t)g.NT * sizeof(DevTask));
@@ -244,7 +274,8 @@ int upload(mpk_tgraph* t) {
   const int64_t o_lists = align256(o_aot + (int64_t)(g.aot_tasks.size() + 1) * sizeof(AotEntry));
   const int64_t o_wl = align256(o_lists + (int64_t)std::max<size_t>(1, flat.size()) * 4);
   const int64_t o_freq = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
-  const int64_t graph_bytes = align256(o_freq + (int64_t)t->cfg.head_dim / 2 * 8);
+  const int64_t o_quota = align256(o_freq + (int64_t)t->cfg.head_dim / 2 * 8);
+  const int64_t graph_bytes = align256(o_quota + (int64_t)g.NE * kEvSub * 2);
   // A JIT event's tasks are dealt in chunks of (workers / schedulers) tasks,
   // one chunk per scheduler ring entry, to consecutive schedulers from a
   // starting one; the starting schedulers follow a running cursor over all
@@ -256,7 +287,8 @@ int upload(mpk_tgraph* t) {
   int64_t n_entries = 0;
   if (g.NE >= (1 << kJitEventBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 2^20 events");
   for (int32_t e = 0; e < g.NE; ++e) {
-    ev[e] = DevEvent{g.event_counts[e], g.event_first[e], g.event_last[e], g.event_flags[e]};
+    ev[e] = DevEvent{t->dev_counts[e], g.event_first[e], g.event_last[e], g.event_flags[e]};
+    if (g.event_counts[e] >= kTwoLevelMin) ev[e].flags |= kEvTwoLevel;
     if (g.event_flags[e] & MPK_EVENT_HAS_JIT) {
       const int64_t n_ch = (g.event_last[e] - g.event_first[e] + chunk) / chunk;
       if (n_ch > (1 << kJitChunkBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 4096 JIT chunks in one event");
@@ -281,6 +313,8 @@ int upload(mpk_tgraph* t) {
   }
   HIPCHK(hipMemcpy(t->d_tasks, t->h_tasks.data(), (size_t)g.NT * sizeof(DevTask), hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(t->d_events, ev.data(), (size_t)g.NE * sizeof(DevEvent), hipMemcpyHostToDevice));
+  t->d_ev_quota = (uint16_t*)(gb + o_quota);
+  HIPCHK(hipMemcpy(t->d_ev_quota, t->quota.data(), t->quota.size() * 2, hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(t->d_aot_off, g.aot_offsets.data(), g.aot_offsets.size() * 4, hipMemcpyHostToDevice));
   // AOT entries (weight pointers are filled in by the first step)
   t->h_aot.assign(g.aot_tasks.size() + 1, AotEntry{});
@@ -294,7 +328,8 @@ int upload(mpk_tgraph* t) {
   t->sched_cap = next_pow2((uint64_t)n_entries + 1);   // every ring entry of a step fits in any one ring
   t->jit_cap = next_pow2((uint64_t)n_jit_tasks + 1);
   const int32_t W = t->prm.W, S = t->n_sched;
-  const int64_t r_cnt = 0, r_sring = align256(r_cnt + (int64_t)g.NE * 4);
+  const int64_t r_cnt = 0, r_sub = align256(r_cnt + (int64_t)g.NE * 4);
+  const int64_t r_sring = align256(r_sub + (int64_t)g.NE * kEvSub * 4);
   const int64_t r_stail = align256(r_sring + (int64_t)S * t->sched_cap * 8);
   const int64_t r_jring = align256(r_stail + (int64_t)S * 4);
   const int64_t r_state = align256(r_jring + (int64_t)W * t->jit_cap * 8);
@@ -306,6 +341,7 @@ int upload(mpk_tgraph* t) {
   HIPCHK(hipMemset(t->d_rt, 0, rt_bytes));
   char* rb = (char*)t->d_rt;
   t->d_ev_cnt = (uint32_t*)(rb + r_cnt);
+  t->d_ev_sub = (uint32_t*)(rb + r_sub);
   t->d_sched_ring = (unsigned long long*)(rb + r_sring);
   t->d_sched_tail = (uint32_t*)(rb + r_stail);
   t->d_jit_ring = (unsigned long long*)(rb + r_jring);
@@ -364,7 +400,8 @@ int upload(mpk_tgraph* t) {
       if (per_layer_bytes[k]) t->tensors[layer_tensor((int32_t)l, k)] = {ab + kind_off[k] + l * per_layer_bytes[k], per_layer_bytes[k]};
 
   a.tasks = t->d_tasks; a.events = t->d_events; a.aot_off = t->d_aot_off; a.aot_desc = t->d_aot_desc;
-  a.ev_cnt = t->d_ev_cnt; a.sched_ring = t->d_sched_ring; a.sched_tail = t->d_sched_tail; a.jit_ring = t->d_jit_ring;
+  a.ev_cnt = t->d_ev_cnt; a.ev_sub = t->d_ev_sub; a.ev_quota = t->d_ev_quota;
+  a.sched_ring = t->d_sched_ring; a.sched_tail = t->d_sched_tail; a.jit_ring = t->d_jit_ring;
   a.state = t->d_state; a.sched_cap = t->sched_cap; a.jit_cap = t->jit_cap;
   a.n_workers = W; a.n_sched = S; a.n_sched_wgs = t->n_sched_wgs;
   a.root_event = g.root; a.end_event = g.end;

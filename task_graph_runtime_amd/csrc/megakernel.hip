@@ -67,27 +67,42 @@ __device__ __forceinline__ void push_chunk(const KArgs& a, int e, const DevEvent
                ((unsigned long long)(pos + 1) << 32) | ((uint32_t)c << kJitEventBits) | (uint32_t)e);
 }
 
-// One trigger of event e by wavefront 0 of a workgroup whose stores for the
-// trigger are complete (every wavefront waited for them before a barrier).
-// Lane 0 advances the counter; if this add fires the event, its empty
-// consumers are resolved here, one lane each (each empty task advances its
-// own event), and the fired events with JIT consumers are handed to their
-// scheduler.  No cache maintenance is needed: the data the events guard is
-// accessed agent-coherently (see tasks.h), the counters atomically.
-__device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e, const DevEvent& ev) {
+// One arrival at event e by task `task` (linear index); q: the quota of
+// its sub-counter (task mod kEvSub) when e is two-level (see rt.h).  True
+// when this arrival fires the event.
+__device__ __forceinline__ bool arrive(const KArgs& a, uint32_t epoch, int e, const DevEvent& ev, int task,
+                                       uint32_t q) {
+  if (ev.flags & kEvTwoLevel) {
+    const uint32_t o = __hip_atomic_fetch_add(&a.ev_sub[(int64_t)e * kEvSub + (task & (kEvSub - 1))], 1u,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (o + 1u != q * epoch) return false;
+  }
+  const uint32_t o = __hip_atomic_fetch_add(&a.ev_cnt[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return o + 1u == ev.counts * epoch;
+}
+
+// One trigger of event e by task `task`, run by wavefront 0 of a workgroup
+// whose stores for the trigger are complete (every wavefront waited for them
+// before a barrier); q: its sub-counter quota (arrive).  Lane 0 arrives; if
+// that fires the event, its empty consumers are resolved here, one lane each
+// (each empty task arrives at its own event), and the fired events with JIT
+// consumers are handed to the schedulers.  No cache maintenance is needed:
+// the data the events guard is accessed agent-coherently (see tasks.h), the
+// counters atomically.
+__device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e, const DevEvent& ev, int task,
+                                        uint32_t q) {
   const int lane = threadIdx.x & 63;
-  uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(&a.ev_cnt[e], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  if (old + 1u != ev.counts * epoch) return;
+  int fired = 0;
+  if (lane == 0) fired = arrive(a, epoch, e, ev, task, q);
+  if (!__shfl(fired, 0)) return;
   if (ev.flags & MPK_EVENT_HAS_EMPTY) {
     for (int t0 = ev.first; t0 <= ev.last; t0 += 64) {
       const int t = t0 + lane;
       if (t <= ev.last) {
         const int f = a.tasks[t].trig;
-        const uint32_t o2 = __hip_atomic_fetch_add(&a.ev_cnt[f], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const DevEvent fe = a.events[f];
-        if (o2 + 1u == fe.counts * epoch && (fe.flags & MPK_EVENT_HAS_JIT))
+        const uint32_t qf = (fe.flags & kEvTwoLevel) ? a.ev_quota[(int64_t)f * kEvSub + (t & (kEvSub - 1))] : 0u;
+        if (arrive(a, epoch, f, fe, t, qf) && (fe.flags & MPK_EVENT_HAS_JIT))
           for (int c = 0; c < jit_chunks(a, fe); ++c) push_chunk(a, f, fe, c);
       }
     }
@@ -251,14 +266,16 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
       reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[0] = 0;
       reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[1] = 0;
     }
-    // the triggering event's record, in flight while the task runs
+    // the triggering event's record and the task's sub-counter quota, in
+    // flight while the task runs
     const uint32_t ev_v = fetch_words<4>(reinterpret_cast<gptr<const uint32_t>>(a.events + t.trig));
+    const uint32_t q_v = a.ev_quota[(int64_t)t.trig * kEvSub + (t.id & (kEvSub - 1))];
     run_task(a, t, P, pre);
     wait_vm<0>();   // the task's stores are complete before its event advances
     __syncthreads();
     if (tid < 64) {
       const uint64_t t_end = (uint64_t)wall_clock64();
-      trigger(a, epoch, t.trig, unpack_event(ev_v));
+      trigger(a, epoch, t.trig, unpack_event(ev_v), t.id, q_v);
       if (tid == 0 && trace && n_trace < trace_cap) {
         const unsigned long long* mk = reinterpret_cast<const unsigned long long*>(g_lds + kLdsMarks);
         trace[n_trace++] = TraceRec{t.id, w, t_wait, t_start, t_end, (uint64_t)wall_clock64(), {mk[0], mk[1]}};

@@ -66,6 +66,19 @@ struct alignas(16) DevEvent {
 };
 static_assert(sizeof(DevEvent) == 16, "DevEvent must be 16 bytes");
 
+// Two-level events.  An event with at least kTwoLevelMin producers counts
+// its arrivals on kEvSub sub-counters first (the producer with linear index
+// t adds to sub-counter t mod kEvSub); the arrival that completes a
+// sub-counter's quota adds 1 to the event counter, which then needs one
+// arrival per non-empty sub-counter.  Simultaneous returning atomics on one
+// address serialise (256 at once: 1.6 us mean, 3 us worst, against 0.35 us
+// on distinct addresses), and a projection's tiles finish close together.
+// The device copy of such an event carries kEvTwoLevel in its flags and the
+// number of non-empty sub-counters as its count.
+constexpr int kEvSub = 8;
+constexpr uint32_t kTwoLevelMin = 32;
+constexpr uint32_t kEvTwoLevel = 4;
+
 // Scheduler ring entry: seq << 32 | chunk << 20 | event (see the megakernel).
 constexpr int kJitEventBits = 20, kJitChunkBits = 12;
 
@@ -114,6 +127,8 @@ struct KArgs {
   MPK_GLOBAL const uint32_t* aot_off;          // [n_workers + 1] offsets into aot_desc
   MPK_GLOBAL const AotEntry* aot_desc;         // per worker, its AOT tasks in FIFO order
   MPK_GLOBAL uint32_t* ev_cnt;                 // monotonic event counters (target counts * epoch)
+  MPK_GLOBAL uint32_t* ev_sub;                 // [NE][kEvSub] sub-counters of two-level events
+  MPK_GLOBAL const uint16_t* ev_quota;         // [NE][kEvSub] arrivals per sub-counter and step
   MPK_GLOBAL unsigned long long* sched_ring;   // [n_sched][sched_cap] (seq << 32 | event)
   MPK_GLOBAL uint32_t* sched_tail;             // [n_sched] producer reservation counters
   MPK_GLOBAL unsigned long long* jit_ring;     // [n_workers][jit_cap] (seq << 32 | task)
