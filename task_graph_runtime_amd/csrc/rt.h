@@ -76,7 +76,7 @@ static_assert(sizeof(DevEvent) == 16, "DevEvent must be 16 bytes");
 // The device copy of such an event carries kEvTwoLevel in its flags and the
 // number of non-empty sub-counters as its count.
 constexpr int kEvSub = 8;
-constexpr uint32_t kTwoLevelMin = 32;
+constexpr uint32_t kTwoLevelMin = 64;
 constexpr uint32_t kEvTwoLevel = 4;
 
 // Scheduler ring entry: seq << 32 | chunk << 20 | event (see the megakernel).
