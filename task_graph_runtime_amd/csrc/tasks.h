@@ -517,11 +517,14 @@ __device__ __forceinline__ void gemv_preload(const KArgs& a, const DevTask& t, c
 // r_l + o_l (GATEUP), s_{L-1} + d_{L-1} (LM head);
 // x = v / sqrt(mean(v^2) + eps) * gamma.  Tile 0 of QKV / GATEUP also
 // stores v: the residual r_l / s_l that later layers add to.
-// xs_issue stages the inputs in LDS with direct global -> LDS loads
-// (agent-coherent for task-to-task data); xs_finish, once they have landed,
-// computes x in place.
+// xs_issue stages the inputs: the residual summands and the gain of a
+// norm tile past layer 0 into registers (thread i holds elements
+// [8 (i + 512 j), +8), 16-byte loads all in flight at once: direct-to-LDS
+// loads keep few requests in flight per compute unit), everything else into
+// LDS with direct global -> LDS loads (agent-coherent for task-to-task
+// data); xs_finish, once they have landed, computes x into LDS.
 struct XSrc {
-  gptr<const float> v1, v2;     // fp32 summands (v2 may be null)
+  gptr<const float> v1, v2;     // fp32 summands (v2 null only with emb or without norm)
   gptr<const uint16_t> emb;     // bf16 embedding row instead of v1 (layer-0 QKV)
   gptr<float> res;              // where to store v, or null
   bool norm;
@@ -564,41 +567,83 @@ __device__ __forceinline__ XSrc gemv_xsrc(const KArgs& a, const DevTask& t, cons
   }
   return x;
 }
-__device__ __forceinline__ void xs_issue(const KArgs& a, const XSrc& x, int K, const TaskPtrs& P, char* lds) {
+constexpr int kXsIt = kMaxHidden / (8 * kThreads);
+struct XRegs {
+  float4 v1[2 * kXsIt], v2[2 * kXsIt];
+  uint4 g[kXsIt];
+};
+__device__ __forceinline__ void xs_issue(const KArgs& a, const XSrc& x, int K, const TaskPtrs& P, char* lds,
+                                         XRegs& xr) {
   const int tid0 = tidx();
   if (!x.norm) {
     lds_stage<16, true>(x.v1, lds, K / 4, tid0);
     return;
   }
   const int H = a.H, hb = lds_chunks(H * 4);
-  if (x.emb) lds_stage<16>(x.emb, lds + hb, H / 8, tid0);
-  else lds_stage<16, true>(x.v1, lds, H / 4, tid0);
-  if (x.v2) lds_stage<16, true>(x.v2, lds + hb, H / 4, tid0);
-  lds_stage<16>(P.p3, lds + 2 * hb, H / 8, tid0);
+  if (x.emb) {
+    lds_stage<16>(x.emb, lds + hb, H / 8, tid0);
+    lds_stage<16>(P.p3, lds + 2 * hb, H / 8, tid0);
+    return;
+  }
+  // (past H the buffer loads return 0)
+#pragma unroll
+  for (int j = 0; j < kXsIt; ++j) {
+    const int e = (tid0 + j * kThreads) * 8;
+    xr.v1[2 * j] = ld4_coh(x.v1, e, H);
+    xr.v1[2 * j + 1] = ld4_coh(x.v1, e + 4, H);
+    xr.v2[2 * j] = ld4_coh(x.v2, e, H);
+    xr.v2[2 * j + 1] = ld4_coh(x.v2, e + 4, H);
+    xr.g[j] = ld16<false>(P.p3, e * 2, H * 2);
+  }
 }
-__device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* lds, float* red) {
+__device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* lds, float* red, const XRegs& xr) {
   if (!x.norm) return;
   const int tid0 = tidx();
   const int H = a.H, hb = lds_chunks(H * 4);
   float* xs = reinterpret_cast<float*>(lds);
-  const float* x2 = reinterpret_cast<const float*>(lds + hb);
+  if (!x.emb) {
+    float v[8 * kXsIt];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2 * kXsIt; ++j) {
+      v[4 * j] = xr.v1[j].x + xr.v2[j].x;
+      v[4 * j + 1] = xr.v1[j].y + xr.v2[j].y;
+      v[4 * j + 2] = xr.v1[j].z + xr.v2[j].z;
+      v[4 * j + 3] = xr.v1[j].w + xr.v2[j].w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ss = fmaf(v[4 * j + u], v[4 * j + u], ss);
+    }
+    ss = block_sum<true>(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
+#pragma unroll
+    for (int j = 0; j < kXsIt; ++j) {
+      const int e = (tid0 + j * kThreads) * 8;
+      if (e < H) {
+        const uint32_t gw[4] = {xr.g[j].x, xr.g[j].y, xr.g[j].z, xr.g[j].w};
+        float o[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          o[2 * u] = v[8 * j + 2 * u] * inv * bflo(gw[u]);
+          o[2 * u + 1] = v[8 * j + 2 * u + 1] * inv * bfhi(gw[u]);
+        }
+        *reinterpret_cast<float4*>(xs + e) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(xs + e + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        if (x.res) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) st_coh(x.res + e + u, v[8 * j + u]);
+        }
+      }
+    }
+    bar_lds();
+    return;
+  }
+  // layer 0: the embedding row and the gain, staged in LDS
   const uint16_t* e16 = reinterpret_cast<const uint16_t*>(lds + hb);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds + 2 * hb);
   constexpr int NV = kMaxHidden / kThreads;
   float v[NV];
-  if (x.emb) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = bf2f(e16[min(tid0 + j * kThreads, H - 1)]);
-  } else if (x.v2) {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int i = min(tid0 + j * kThreads, H - 1);
-      v[j] = xs[i] + x2[i];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = xs[min(tid0 + j * kThreads, H - 1)];
-  }
+  for (int j = 0; j < NV; ++j) v[j] = bf2f(e16[min(tid0 + j * kThreads, H - 1)]);
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -647,7 +692,8 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
   int* ctr = reinterpret_cast<int*>(lds + kLdsCtl) + 3;   // tail chunks claimed so far
   const int kl = lane * 8;
   const XSrc xsrc = gemv_xsrc(a, t, P);
-  xs_issue(a, xsrc, K, P, lds);
+  XRegs xr;
+  xs_issue(a, xsrc, K, P, lds, xr);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);   // the staging loads stay ahead of the weight loads (counted waits)
   // segment s -> (row, segment within the row) without an integer division
@@ -724,7 +770,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
   if (nch > 0) wait_vm<2 * D>();   // the staging landed; both chunks may still be in flight
   else wait_vm<0>();
   bar_lds();
-  xs_finish(a, xsrc, lds, red);
+  xs_finish(a, xsrc, lds, red, xr);
   mark(a, 0);
   if (r.pe > r.pb) {   // the pre-loaded prefix
     int row, ks;
