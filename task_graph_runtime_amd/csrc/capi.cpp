@@ -289,6 +289,11 @@ int upload(mpk_tgraph* t) {
   for (int32_t e = 0; e < g.NE; ++e) {
     ev[e] = DevEvent{t->dev_counts[e], g.event_first[e], g.event_last[e], g.event_flags[e]};
     if (g.event_counts[e] >= kTwoLevelMin) ev[e].flags |= kEvTwoLevel;
+    if (g.event_counts[e] == 1 && g.event_last[e] >= g.event_first[e]) {
+      bool all_empty = true;
+      for (int32_t i = g.event_first[e]; i <= g.event_last[e]; ++i) all_empty &= g.task_mode[i] == MPK_MODE_EMPTY;
+      if (all_empty) ev[e].flags |= kEvSole;
+    }
     if (g.event_flags[e] & MPK_EVENT_HAS_JIT) {
       const int64_t n_ch = (g.event_last[e] - g.event_first[e] + chunk) / chunk;
       if (n_ch > (1 << kJitChunkBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 4096 JIT chunks in one event");

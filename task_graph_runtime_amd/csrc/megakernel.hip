@@ -72,6 +72,7 @@ __device__ __forceinline__ void push_chunk(const KArgs& a, int e, const DevEvent
 // when this arrival fires the event.
 __device__ __forceinline__ bool arrive(const KArgs& a, uint32_t epoch, int e, const DevEvent& ev, int task,
                                        uint32_t q) {
+  if (ev.flags & kEvSole) return true;
   if (ev.flags & kEvTwoLevel) {
     const uint32_t o = __hip_atomic_fetch_add(&a.ev_sub[(int64_t)e * kEvSub + (task & (kEvSub - 1))], 1u,
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

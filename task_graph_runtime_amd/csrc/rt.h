@@ -78,6 +78,10 @@ static_assert(sizeof(DevEvent) == 16, "DevEvent must be 16 bytes");
 constexpr int kEvSub = 8;
 constexpr uint32_t kTwoLevelMin = 64;
 constexpr uint32_t kEvTwoLevel = 4;
+// An event with one producer whose consumers are all EMPTY tasks (the e' of
+// a normalisation rewrite): its one arrival always fires it and nothing polls
+// its counter, so the arrival takes no atomic.
+constexpr uint32_t kEvSole = 8;
 
 // Scheduler ring entry: seq << 32 | chunk << 20 | event (see the megakernel).
 constexpr int kJitEventBits = 20, kJitChunkBits = 12;
