@@ -59,7 +59,7 @@ enum {
   MPK_TASK_ATTN_NORM = 1,   /* r = residual in; h = RMSNorm(r) (fp32)                    */
   MPK_TASK_QKV = 2,         /* tile of the fused q/k/v projection (group-major columns)  */
   MPK_TASK_QKNORM_ROPE = 3, /* (reserved)                                                */
-  MPK_TASK_ATTN = 4,        /* slot b*s_attn + s of a kv group (JIT): serves one split of */
+  MPK_TASK_ATTN = 4,        /* slot j of a kv group's s_attn slots: serves one split of   */
                             /* one request, chosen at run time so that the group's slots */
                             /* get equal page counts; q/k norm, RoPE, paged attention    */
                             /* partial; a request's last split appends the new k/v, the  */
@@ -99,8 +99,9 @@ typedef struct {
   int32_t quantum;       /* column quantum of projection tiles (default 1 at B=1, else 16) */
   int32_t t_qkv, t_o, t_gu, t_down, t_lm; /* tiles per projection (default ~W; t_qkv a
                                              multiple of n_kv_heads)                    */
-  int32_t s_attn;        /* attention slots per (request, kv group) (default             */
-                         /* min(8, 2 W / (B n_kv_heads)), at least 1 and at most the pages) */
+  int32_t s_attn;        /* attention slots per kv group, at least the batch (default:   */
+                         /* batch 1: min(8, 2 W / n_kv_heads, pages), the splits; batch > */
+                         /* 1: max(B, min(W / n_kv_heads, B pages)), one task per worker) */
   int32_t host_only;     /* 1: build on the host only (no device work); export still works */
   int32_t fusion_order;  /* must be 0: Def 4.1 then Def 4.2                               */
   int32_t aot_policy;    /* must be 0: round-robin over workers in linear order           */
@@ -236,7 +237,7 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
  * (fp32 value, int32 index pairs); per layer l, 5 + 13*l + k with k = 0 r
  * (residual into the layer), 2 qkv (raw projection, group-major: per kv group
  * its query heads, key head, value head), 6 attention partials
- * [kv][B * s_attn][G][2 + head_dim] (per kv group and slot: max, sum, output;
+ * [kv][s_attn][G][2 + head_dim] (per kv group and slot: max, sum, output;
  * a request's splits occupy consecutive slots), 7 attn, 8 o, 9 s
  * (residual after attention), 11 a, 12 d; at batch > 1 also 0 e[B][H],
  * 1 hf[B][H], and per layer k = 1 h, 10 h2 (the normalised inputs).

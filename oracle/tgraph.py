@@ -45,11 +45,12 @@ attention tasks, and at batch 1 the residual add + RMSNorm run inside the
 projection tiles that consume them (``fused_norm``).  Type ids 3
 (QKNORM_ROPE) and 5 (COMBINE) are therefore never emitted for the decoder.
 
-Attention slots (a choice of this build): kv group ``g`` has ``M = B * S``
-attention tasks, task ``(b, g, s)`` being slot ``j = b*S + s`` of the group.
-Which request a slot serves is decided when the step runs, from the
-sequence lengths, so that every slot gets about the same number of pages
-(a request with more cached tokens gets more splits).  A slot may therefore
+Attention slots (a choice of this build): kv group ``g`` has ``M = S_attn``
+attention tasks, task ``(j, g)`` being slot ``j`` of the group (at batch 1
+the slots are the request's splits).  Which request a slot serves is decided
+when the step runs, from the sequence lengths, so that every slot gets
+about the same number of pages (a request with more cached tokens gets more
+splits); ``M >= B`` gives every request at least one.  A slot may therefore
 serve any request of its group, and every attention task declares the whole
 group: all B rows of the group's q/k/v columns as input; the group's partial
 records, attention output and cache rows of all B requests as outputs.  The
@@ -128,7 +129,7 @@ def decompose(cfg, B, P, prm: Params):
     Returns a list of dicts ``{type, layer, coords, ins, outs}``; a box is
     ``(tensor_id, lo[4], hi[4])`` (half-open).
 
-    Per layer: [ATTN_NORM] QKV tiles, ATTN(b, g, s) [JIT], OPROJ tiles,
+    Per layer: [ATTN_NORM] QKV tiles, ATTN(j, g) [JIT], OPROJ tiles,
     [MLP_NORM] GATEUP tiles, DOWN tiles; then [FINAL_NORM] LMHEAD tiles and
     ARGMAX (bracketed tasks only at batch > 1, see ``fused_norm``).  An
     attention split also applies q/k RMSNorm and RoPE to its query heads, the
@@ -168,14 +169,13 @@ def decompose(cfg, B, P, prm: Params):
             if fused and n == 0:
                 outs.append(full(t(L_R), H))
             add(QKV, l, (n,), prev if fused else [full(t(L_H), H)], outs)
-        for b in range(B):
-            for g in range(hkv):
-                for s in range(S):
-                    outs = [_box(t(L_PART), (0, g, 0, 0), (B, g + 1, S, G * (d + 2))),
-                            _box(t(L_ATTN), (0, g * G * d), (B, (g + 1) * G * d)),
-                            _box(t(L_KC), (0, 0, g, 0), (B, maxs, g + 1, d)),
-                            _box(t(L_VC), (0, 0, g, 0), (B, maxs, g + 1, d))]
-                    add(ATTN, l, (b, g, s), [_box(t(L_QKV), (0, g * Sg), (B, (g + 1) * Sg))], outs)
+        for g in range(hkv):
+            for j in range(S):
+                outs = [_box(t(L_PART), (0, g, 0, 0), (1, g + 1, S, G * (d + 2))),
+                        _box(t(L_ATTN), (0, g * G * d), (B, (g + 1) * G * d)),
+                        _box(t(L_KC), (0, 0, g, 0), (B, maxs, g + 1, d)),
+                        _box(t(L_VC), (0, 0, g, 0), (B, maxs, g + 1, d))]
+                add(ATTN, l, (j, g), [_box(t(L_QKV), (0, g * Sg), (B, (g + 1) * Sg))], outs)
         for n in range(prm.T_o):
             lo, hi = tile_range(H, prm.q, prm.T_o, n)
             add(OPROJ, l, (n,), [full(t(L_ATTN), hq * d)], [_box(t(L_O), (0, lo), (B, hi))])

@@ -101,10 +101,16 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   r.T_down = dflt(p.t_down, H, 1);
   r.T_lm = dflt(p.t_lm, V, 1);
   int64_t max_pages = cdiv(c.max_seq_len, P);
+  // S_attn = M, the attention slots of a kv group (dealt to the requests by
+  // page count when the step runs); at batch 1 they are the splits
   if (p.s_attn > 0) {
     r.S_attn = p.s_attn;
+    if (r.S_attn < B) return bad("s_attn: fewer attention slots per kv group than requests");
+  } else if (B > 1) {
+    // one attention task per worker, at most one slot per page of each request
+    r.S_attn = (int32_t)std::max<int64_t>(B, std::min<int64_t>(r.W / hkv, (int64_t)B * max_pages));
   } else {
-    // at most two attention tasks per worker: 2 W / (B hkv) slots per request, at most 8
+    // at most two attention tasks per worker (2 W / hkv splits), at most 8
     int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, 2 * r.W / ((int64_t)B * hkv)));
     r.S_attn = (int32_t)std::min<int64_t>(s, max_pages);
   }
@@ -165,18 +171,17 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
       if (fused && n == 0) outs.push_back(full(t(L_R), H));
       add(MPK_TASK_QKV, l, n, 0, 0, fused ? prev : std::vector<Box>{full(t(L_H), H)}, outs);
     }
-    // attention task (b, g, s) is slot b*S + s of kv group g; the request a
-    // slot serves is decided at run time from the sequence lengths, so every
-    // task declares its whole group (all B rows)
-    for (int32_t b = 0; b < B; ++b)
-      for (int32_t g = 0; g < hkv; ++g)
-        for (int32_t s = 0; s < S; ++s) {
-          std::vector<Box> outs = {box(t(L_PART), {0, g, 0, 0}, {B, g + 1, S, G * (d + 2)}),
-                                   box(t(L_ATTN), {0, g * G * d}, {B, (g + 1) * G * d}),
-                                   box(t(L_KC), {0, 0, g, 0}, {B, maxs, g + 1, d}),
-                                   box(t(L_VC), {0, 0, g, 0}, {B, maxs, g + 1, d})};
-          add(MPK_TASK_ATTN, l, b, g, s, {box(t(L_QKV), {0, g * Sg}, {B, (g + 1) * Sg})}, outs);
-        }
+    // attention task (j, g) is slot j of kv group g; the request a slot
+    // serves is decided at run time from the sequence lengths, so every task
+    // declares its whole group (all B rows)
+    for (int32_t g = 0; g < hkv; ++g)
+      for (int32_t s = 0; s < S; ++s) {
+        std::vector<Box> outs = {box(t(L_PART), {0, g, 0, 0}, {1, g + 1, S, G * (d + 2)}),
+                                 box(t(L_ATTN), {0, g * G * d}, {B, (g + 1) * G * d}),
+                                 box(t(L_KC), {0, 0, g, 0}, {B, maxs, g + 1, d}),
+                                 box(t(L_VC), {0, 0, g, 0}, {B, maxs, g + 1, d})};
+        add(MPK_TASK_ATTN, l, s, g, 0, {box(t(L_QKV), {0, g * Sg}, {B, (g + 1) * Sg})}, outs);
+      }
     for (int32_t n = 0; n < p.T_o; ++n) {
       int32_t lo, hi;
       tile_range(H, p.q, p.T_o, n, &lo, &hi);

@@ -221,8 +221,8 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
   // attention: wavefront merge states, raw q/k/v row, processed heads
   stage = std::max(stage, chunks(kWaves * G * (d + 2) * 4) + 2 * chunks((G + 2) * d * 4));
   // the split combine stages a request's records when they fit in 96 KB (else it reads them from
-  // global memory); a request gets at most B (S - 1) + 1 slots
-  const int64_t max_split = (int64_t)B * (p.S_attn - 1) + 1;
+  // global memory); a request gets at most M - B + 1 of the M slots
+  const int64_t max_split = (int64_t)p.S_attn - B + 1;
   const int64_t comb = ((max_split * G * (d + 2) + 63) & ~(int64_t)63) * 4;
   if (comb <= 96 * 1024) stage = std::max(stage, comb);
   // accumulators: the widest projection tile, rows per column x batch
@@ -261,6 +261,8 @@ int upload(mpk_tgraph* t) {
     return fail(MPK_ERR_INVALID_ARG, "JIT tasks need at least one scheduler wavefront");
   if (t->n_sched > 0 && (t->prm.W + t->n_sched - 1) / t->n_sched > 64)
     return fail(MPK_ERR_INVALID_ARG, "more than 64 workers per scheduler wavefront");
+  if (t->n_sched > 0 && t->prm.W % t->n_sched != 0)
+    return fail(MPK_ERR_INVALID_ARG, "the worker count must be a multiple of the scheduler wavefronts");
 
   if (int rc = two_level_events(t)) return rc;
   fill_descriptors(t);
@@ -276,14 +278,15 @@ int upload(mpk_tgraph* t) {
   const int64_t o_freq = align256(o_wl + (int64_t)t->cfg.n_layers * LAYER_PTRS * 8);
   const int64_t o_quota = align256(o_freq + (int64_t)t->cfg.head_dim / 2 * 8);
   const int64_t graph_bytes = align256(o_quota + (int64_t)g.NE * kEvSub * 2);
-  // A JIT event's tasks are dealt in chunks of (workers / schedulers) tasks,
-  // one chunk per scheduler ring entry, to consecutive schedulers from a
-  // starting one; the starting schedulers follow a running cursor over all
-  // chunks in event order, so the chunks of events that fire together land
-  // on different schedulers (and so on different workers).  The device copy
-  // of the event keeps its starting scheduler in flags bits 16..31.
+  // JIT placement by worker position (see the mega-kernel): the tasks of a
+  // JIT event take consecutive positions from the running count of JIT
+  // tasks in event order (mod W), so events that fire together fill the
+  // workers one task each before any worker gets a second.  The device copy
+  // of the event keeps its start position in flags bits 16..31; one
+  // scheduler ring entry per scheduler segment the positions cross.
   std::vector<DevEvent> ev(g.NE);
-  const int32_t chunk = std::max<int32_t>(1, t->prm.W / std::max(1, t->n_sched));
+  const int64_t Wp = t->prm.W, n_sub = Wp / std::max(1, t->n_sched);
+  int64_t pos = 0;   // running JIT task count, the next event's start position
   int64_t n_entries = 0;
   if (g.NE >= (1 << kJitEventBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 2^20 events");
   for (int32_t e = 0; e < g.NE; ++e) {
@@ -295,10 +298,12 @@ int upload(mpk_tgraph* t) {
       if (all_empty) ev[e].flags |= kEvSole;
     }
     if (g.event_flags[e] & MPK_EVENT_HAS_JIT) {
-      const int64_t n_ch = (g.event_last[e] - g.event_first[e] + chunk) / chunk;
+      const int64_t k = g.event_last[e] - g.event_first[e] + 1, P = pos % Wp;
+      const int64_t n_ch = (P + k - 1) / n_sub - P / n_sub + 1;
       if (n_ch > (1 << kJitChunkBits)) return fail(MPK_ERR_UNSUPPORTED, "more than 4096 JIT chunks in one event");
-      ev[e].flags |= (uint32_t)(n_entries % t->n_sched) << 16;
+      ev[e].flags |= (uint32_t)P << 16;
       n_entries += n_ch;
+      pos += k;
     }
   }
   HIPCHK(hipMalloc(&t->d_graph, graph_bytes));
@@ -338,7 +343,7 @@ int upload(mpk_tgraph* t) {
   const int64_t r_stail = align256(r_sring + (int64_t)S * t->sched_cap * 8);
   const int64_t r_jring = align256(r_stail + (int64_t)S * 4);
   const int64_t r_state = align256(r_jring + (int64_t)W * t->jit_cap * 8);
-  const int64_t r_status = align256(r_state + (int64_t)(2 * W + 2 * S) * 4);
+  const int64_t r_status = align256(r_state + (int64_t)(2 * W + S) * 4);
   const int64_t r_arrive = align256(r_status + (int64_t)sizeof(StatusWord));
   const int64_t rt_bytes =
       align256(r_arrive + (int64_t)t->cfg.n_layers * t->B * t->cfg.n_kv_heads * 4);
@@ -360,7 +365,7 @@ int upload(mpk_tgraph* t) {
   const int64_t B = t->B, H = c.hidden, L = c.n_layers, hq = c.n_q_heads, hkv = c.n_kv_heads, d = c.head_dim;
   const int64_t G = hq / hkv, Sg = (G + 2) * d, F = c.ffn, S_at = t->prm.S_attn;
   KArgs& a = t->base;
-  a.st_bh = B * H; a.st_qkv = B * hkv * Sg; a.st_q = B * hq * d; a.st_part = B * hkv * S_at * G * (d + 2);
+  a.st_bh = B * H; a.st_qkv = B * hkv * Sg; a.st_q = B * hq * d; a.st_part = hkv * S_at * G * (d + 2);
   a.st_a = B * F;
   // batch > 1 only (norm tasks): e, hf, h, h2
   const bool fused = fused_norm(t->B);

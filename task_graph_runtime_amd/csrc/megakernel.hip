@@ -11,10 +11,11 @@
 // reaches counts * epoch (counters are never reset: each step raises the
 // target).  The agent whose add fires an event resolves the event's empty
 // consumers on the spot and, if the event has JIT consumers, appends its
-// tasks, in chunks of (workers / schedulers), to the rings of consecutive
-// schedulers.  A scheduler pops its ring and deals a chunk's tasks
-// round-robin onto the JIT rings of its workers (workers w with
-// w mod n_sched == its index).  Everything exits when the end
+// tasks, one chunk per scheduler segment of worker positions they take, to
+// the rings of consecutive schedulers.  A scheduler pops its ring and writes
+// a chunk's tasks onto the JIT rings of the workers at their positions (its
+// workers are those w with w mod n_sched == its index).  Everything exits
+// when the end
 // event fires; every wait has a watchdog so that the grid always drains.
 #include "tasks.h"
 
@@ -45,23 +46,28 @@ __device__ __forceinline__ bool reached(uint32_t cnt, uint32_t target) { return 
 // Persistent runtime state (device words, kept across steps):
 //   [0, W)            JIT ring head of each worker
 //   [W, W+S)          event ring head of each scheduler
-//   [W+S, W+2S)       round-robin cursor of each scheduler
-//   [W+2S, 2W+2S)     JIT ring tail of each worker (written by its scheduler)
+//   [W+S, 2W+S)       JIT ring tail of each worker (written by its scheduler)
 __device__ __forceinline__ gptr<uint32_t> st_jit_head(const KArgs& a) { return a.state; }
 __device__ __forceinline__ gptr<uint32_t> st_sched_head(const KArgs& a) { return a.state + a.n_workers; }
-__device__ __forceinline__ gptr<uint32_t> st_sched_rr(const KArgs& a) { return a.state + a.n_workers + a.n_sched; }
-__device__ __forceinline__ gptr<uint32_t> st_jit_tail(const KArgs& a) { return a.state + a.n_workers + 2 * a.n_sched; }
+__device__ __forceinline__ gptr<uint32_t> st_jit_tail(const KArgs& a) { return a.state + a.n_workers + a.n_sched; }
 
-// A fired JIT event is handed over in chunks of (workers / schedulers) of
-// its tasks, chunk c to scheduler (s0 + c) mod n_sched, where s0 is the
-// event's starting scheduler (flags bits 16..31, set by the host so that the
-// chunks of events firing together spread over all schedulers).
-__device__ __forceinline__ int jit_chunk(const KArgs& a) { return max(1, a.n_workers / a.n_sched); }
+// JIT placement by worker position.  Position p in [0, W) is worker
+// (p / n_sub) + S (p mod n_sub), the (p mod n_sub)-th worker of scheduler
+// p / n_sub (n_sub = W / S).  The tasks of JIT event e take consecutive
+// positions from its start P_e (flags bits 16..31; the host sets P_e to the
+// running count of JIT tasks in event order, mod W, so the events of a
+// layer, which fire together, fill the workers one task each before any
+// worker gets a second).  The event is handed over as one chunk per
+// scheduler segment its positions cross: chunk c to scheduler
+// (P_e / n_sub + c) mod S, which writes each of the chunk's tasks into the
+// ring of the worker at its position.
+__device__ __forceinline__ int jit_sub(const KArgs& a) { return a.n_workers / a.n_sched; }
 __device__ __forceinline__ int jit_chunks(const KArgs& a, const DevEvent& ev) {
-  return (ev.last - ev.first + jit_chunk(a)) / jit_chunk(a);
+  const int P = (int)(ev.flags >> 16), n = jit_sub(a);
+  return (P + ev.last - ev.first) / n - P / n + 1;
 }
 __device__ __forceinline__ void push_chunk(const KArgs& a, int e, const DevEvent& ev, int c) {
-  const int s = (int)(((ev.flags >> 16) + (uint32_t)c) % (uint32_t)a.n_sched);
+  const int s = (int)(((ev.flags >> 16) / (uint32_t)jit_sub(a) + (uint32_t)c) % (uint32_t)a.n_sched);
   const uint32_t pos = __hip_atomic_fetch_add(&a.sched_tail[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   st_relaxed64(&a.sched_ring[(int64_t)s * a.sched_cap + (pos & (a.sched_cap - 1))],
                ((unsigned long long)(pos + 1) << 32) | ((uint32_t)c << kJitEventBits) | (uint32_t)e);
@@ -291,19 +297,18 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
 }
 
 // One scheduler per wavefront.  Scheduler s serves workers s, s + S, s + 2S,
-// ... (n_sub <= 64 of them); lane x keeps the JIT ring tail of its x-th
-// worker in a register.  A popped event's JIT tasks are dealt round-robin
-// (a running cursor over the sub-workers) in rounds of n_sub tasks: in one
-// round every lane writes the slot of its own worker, so a round costs one
-// store per lane in parallel.  Ring slots are written and read with relaxed
-// agent-scope atomics.
+// ... (n_sub = W / S <= 64 of them); lane x keeps the JIT ring tail of its
+// x-th worker in a register.  A popped chunk's tasks sit at distinct
+// positions of the scheduler's segment (see push_chunk), so each lane writes
+// at most one slot, all lanes in parallel.  Ring slots are written and read
+// with relaxed agent-scope atomics.
 __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, uint64_t timeout, int s) {
   const int lane = threadIdx.x & 63;
-  const int n_sub = (a.n_workers - s + a.n_sched - 1) / a.n_sched;
+  const int n_sub = jit_sub(a);
   gptr<uint32_t> tails = st_jit_tail(a);
   const int my_w = s + lane * a.n_sched;
   uint32_t my_tail = lane < n_sub ? tails[my_w] : 0u;
-  uint32_t head = st_sched_head(a)[s], rr = st_sched_rr(a)[s];
+  uint32_t head = st_sched_head(a)[s];
   gptr<const unsigned long long> ring = a.sched_ring + (int64_t)s * a.sched_cap;
   gptr<unsigned long long> my_ring = a.jit_ring + (int64_t)(lane < n_sub ? my_w : 0) * a.jit_cap;
   const uint32_t end_target = a.events[a.end_event].counts * epoch;
@@ -317,20 +322,16 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
       const int c = (int)((uint32_t)slot >> kJitEventBits);
       ++head;
       const DevEvent ev = a.events[e];
-      const int first = ev.first + c * jit_chunk(a);
-      const int k = min(ev.last - first + 1, jit_chunk(a));
-      for (int base = 0; base < k; base += n_sub) {
-        // task base + j goes to sub-worker (rr + base + j) mod n_sub
-        const int r0 = (int)((rr + (uint32_t)base) % (uint32_t)n_sub);
-        const int j = base + (lane - r0 + n_sub) % n_sub;
-        if (lane < n_sub && j < k) {
-          __hip_atomic_store(&my_ring[my_tail & (a.jit_cap - 1)],
-                             ((unsigned long long)(my_tail + 1u) << 32) | (uint32_t)(first + j),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ++my_tail;
-        }
+      // the chunk's positions (unwrapped): [u0, u1) within one segment
+      const int P = (int)(ev.flags >> 16), seg = P / n_sub + c;
+      const int u0 = max(P, seg * n_sub), u1 = min(P + ev.last - ev.first + 1, (seg + 1) * n_sub);
+      const int u = seg * n_sub + lane;   // this lane's position in the segment
+      if (lane < n_sub && u >= u0 && u < u1) {
+        __hip_atomic_store(&my_ring[my_tail & (a.jit_cap - 1)],
+                           ((unsigned long long)(my_tail + 1u) << 32) | (uint32_t)(ev.first + (u - P)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++my_tail;
       }
-      rr += (uint32_t)k;
       t0 = wall_clock64();
       continue;
     }
@@ -343,10 +344,7 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
     __builtin_amdgcn_s_sleep(2);
   }
   if (lane < n_sub) tails[my_w] = my_tail;
-  if (lane == 0) {
-    st_sched_head(a)[s] = head;
-    st_sched_rr(a)[s] = rr;
-  }
+  if (lane == 0) st_sched_head(a)[s] = head;
 }
 
 }  // namespace

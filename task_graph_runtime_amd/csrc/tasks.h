@@ -943,15 +943,15 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
 }
 
 // ------------------------------------------------------------------ paged attention, one split
-// Attention slots.  Kv group g has M = B S_attn attention tasks; task
-// (b, g, s) is slot j = b S_attn + s.  When the step runs, request b gets
-// n_b = 1 + floor((M - B) pages_b / total) consecutive slots
-// (pages_b = ceil((L_b + 1) / P), total = their sum; a request with an
-// invalid length counts 0 pages), in request order; slots past the last
-// request's are idle, and splits past a request's pages are empty.  At batch
-// 1 that is all S_attn slots.  Every task computes the same allocation from
-// the B sequence lengths, so the splits of a long request are as short as
-// those of a short one and the group's tasks take about the same time.
+// Attention slots.  Kv group g has M = S_attn attention tasks; task (j, g)
+// is slot j (M >= B).  When the step runs, request b gets
+// n_b = max(1, ceil(pages_b / T)) consecutive slots, in request order, with
+// T the smallest split size (in pages) for which sum_b n_b <= M
+// (pages_b = ceil((L_b + 1) / P); a request with an invalid length counts 0
+// pages); slots past the last request's are idle.  At batch 1 the request
+// takes all S_attn slots (splits past its pages are empty).  Every task
+// computes the same allocation from the B sequence lengths, so no split is
+// longer than T pages however the lengths differ.
 struct AttnSlot {
   int b, s, n, start;   // request (-1: idle slot), its split, its split count, its first slot
 };
@@ -964,14 +964,27 @@ __device__ __forceinline__ int attn_pages(const KArgs& a, int L) {
 // one: batch 1, return {0, j, 0, 0} without loading anything (the caller
 // knows the split count, S_attn).
 __device__ __forceinline__ AttnSlot attn_slot(const KArgs& a, int j, bool one) {
-  const int lane = tidx() & 63, B = a.B, M = B * a.S_attn;
+  const int lane = tidx() & 63, B = a.B, M = a.S_attn;
   if (one) return AttnSlot{0, j, 0, 0};
   const int L = a.seq_lens[min(lane, B - 1)];
   const int pg = lane < B ? attn_pages(a, L) : 0;
-  int total = pg;
+  // T: binary search over [1, max pages] (T = max pages always fits: B <= M)
+  int mx = pg;
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) total += __shfl_xor(total, m, 16);
-  const int n = lane < B ? 1 + (int)((int64_t)(M - B) * pg / max(total, 1)) : 0;
+  for (int m = 1; m < 16; m <<= 1) mx = max(mx, __shfl_xor(mx, m, 16));
+  auto splits = [&](int T) {   // sum_b max(1, ceil(pages_b / T)), wavefront-uniform (lanes 0..15)
+    int c = lane < B ? max(1, (pg + T - 1) / T) : 0;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) c += __shfl_xor(c, m, 16);
+    return __builtin_amdgcn_readfirstlane(c);
+  };
+  int lo = 1, hi = max(__builtin_amdgcn_readfirstlane(mx), 1);
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    if (splits(mid) <= M) hi = mid;
+    else lo = mid + 1;
+  }
+  const int n = lane < B ? max(1, (pg + lo - 1) / lo) : 0;
   int incl = n;
 #pragma unroll
   for (int d = 1; d < 16; d <<= 1) {
@@ -997,7 +1010,7 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
   const int G = a.G, D = a.d, S = n_split;
   const int rec = G * (D + 2);
   gptr<const float> part =
-      a.part + (int64_t)l * a.st_part + ((int64_t)g * a.B * a.S_attn + start) * (int64_t)rec;
+      a.part + (int64_t)l * a.st_part + ((int64_t)g * a.S_attn + start) * (int64_t)rec;
   gptr<float> out = a.attn + (int64_t)l * a.st_q + (int64_t)b * a.hq * D + (int64_t)g * G * D;
   float* st = reinterpret_cast<float*>(lds);
   const int n = S * rec;   // (a multiple of 4: rec = G (D + 2) with D even)
@@ -1067,7 +1080,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
   constexpr int TPI = kWaves * RPW;     // tokens per iteration of the workgroup
   constexpr int HALF = D / 2;
   using KV = typename std::conditional<DPL == 8, uint4, typename std::conditional<DPL == 4, uint2, uint32_t>::type>::type;
-  const int slot = t.a0 * a.S_attn + t.a2, g = t.a1, l = t.layer, G = a.G, P = a.P;
+  const int slot = t.a0, g = t.a1, l = t.layer, G = a.G, P = a.P;
   // at batch 1 the request is known (b = 0, s = slot), so the q/k/v row loads
   // go out before the split count, which needs the length, is known
   AttnSlot sl = attn_slot(a, slot, a.B == 1);
@@ -1276,7 +1289,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
     }
   }
   __syncthreads();
-  gptr<float> out = a.part + (int64_t)l * a.st_part + ((int64_t)g * a.B * a.S_attn + slot) * (int64_t)(G * (D + 2));
+  gptr<float> out = a.part + (int64_t)l * a.st_part + ((int64_t)g * a.S_attn + slot) * (int64_t)(G * (D + 2));
   for (int e = tid0; e < G * D; e += kThreads) {
     const int h = e / D, dd = e - h * D;
     float M = -INFINITY;

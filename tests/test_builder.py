@@ -31,7 +31,7 @@ def both(shape, B, W, q=None, S=None, **over):
     from the library's header)."""
     s = shape
     names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm")
-    params = dict(n_workers=W, s_attn=S or 4, attn_jit=over.pop("attn_jit", 0))
+    params = dict(n_workers=W, s_attn=S or max(4, B), attn_jit=over.pop("attn_jit", 0))
     if q is not None:
         params["quantum"] = q
     for k, v in over.items():
@@ -63,15 +63,15 @@ def test_tiny_worked_example_bit_exact(attn_jit):
 @pytest.mark.parametrize("B,attn_jit,resolved", [(2, 0, 1), (2, 2, 2), (16, 0, 1)])
 def test_attention_policy_at_batch_above_one(B, attn_jit, resolved):
     s = synth.SHAPES["tiny"].with_(n_layers=1)
-    ref, got, tasks = both(s, B, 13, S=2, attn_jit=attn_jit)
+    ref, got, tasks = both(s, B, 13, S=max(2, B), attn_jit=attn_jit)
     assert_same(ref, got)
     assert got["params"]["attn_jit"] == resolved
     tg.check_semantics(got, tasks, closure=True)
 
 
 @pytest.mark.parametrize("name,B,W,S,layers", [
-    ("tiny", 1, 8, 4, 2), ("tiny", 5, 13, 3, 2), ("tiny", 16, 252, 2, 2),
-    ("qwen3_0p6b", 1, 252, 16, 2), ("qwen3_8b", 1, 252, 16, 1), ("qwen3_8b_b16", 16, 252, 4, 1),
+    ("tiny", 1, 8, 4, 2), ("tiny", 5, 13, 7, 2), ("tiny", 16, 252, 20, 2),
+    ("qwen3_0p6b", 1, 252, 16, 2), ("qwen3_8b", 1, 252, 16, 1), ("qwen3_8b_b16", 16, 252, 31, 1),
     ("qwen3_32b", 1, 252, 16, 1)])
 def test_layer_cuts_bit_exact(name, B, W, S, layers):
     s = synth.SHAPES[name].with_(n_layers=layers)
@@ -83,7 +83,7 @@ def test_layer_cuts_bit_exact(name, B, W, S, layers):
 @pytest.mark.parametrize("name", ["qwen3_0p6b", "qwen3_8b", "qwen3_8b_b16"])
 def test_full_graph_bit_exact(name):
     s = synth.SHAPES[name]
-    ref, got, _ = both(s, s.batch, 252, S=16 if s.batch == 1 else 4)
+    ref, got, _ = both(s, s.batch, 252, S=16 if s.batch == 1 else 31)
     assert_same(ref, got)
     tg.check_semantics(got, None)
 
@@ -98,7 +98,8 @@ def test_default_params_resolve_as_documented():
     h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
     # batch 16: JIT attention; 14 scheduler wavefronts (4 workgroups) leave 252 workers, 18 per scheduler
     assert h16["n_workers"] == 252 and h16["n_sched_waves"] == 14 and h16["attn_jit"] == 1
-    assert h16["quantum"] == 16 and h16["s_attn"] == 3   # floor(2 x 252 / (16 x 8)) slots per request
+    # one attention task per worker: floor(252 / 8) = 31 slots per kv group, dealt to the 16 requests by pages
+    assert h16["quantum"] == 16 and h16["s_attn"] == 31
     # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
     assert h16["t_lm"] == 504 and h16["t_gu"] == 252
 

@@ -174,7 +174,7 @@ def test_tiny_ragged(B, lens, mode):
 
 @pytest.mark.parametrize("params", [
     dict(n_workers=8, quantum=64, t_qkv=8, t_o=4, t_gu=11, t_down=4, t_lm=16, s_attn=4),   # the worked example
-    dict(n_workers=3, n_sched_waves=4, s_attn=1),                                             # few workers, one split
+    dict(n_workers=3, n_sched_waves=4, s_attn=2),                                             # few workers, one split each
     dict(n_workers=200, s_attn=9, t_lm=1000, quantum=1),                                      # many tiles, odd split
 ])
 def test_tiny_build_params(params):
