@@ -897,10 +897,15 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
   for (int kg = 0; kg + 1 < nkg; ++kg) {
     xconvert(kg);
     xload(kg + 1);
+    // (block by block: the next group's weights of block r go out as soon as
+    // block r's products are issued, so they are in flight during the other
+    // blocks' products; the compiler would otherwise sink every load below
+    // the last product and expose a full round trip per group)
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
       mul(r);
       wload(kg + 1, r);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   xconvert(nkg - 1);
