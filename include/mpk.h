@@ -105,6 +105,13 @@ typedef struct {
   int32_t host_only;     /* 1: build on the host only (no device work); export still works */
   int32_t fusion_order;  /* must be 0: Def 4.1 then Def 4.2                               */
   int32_t aot_policy;    /* must be 0: round-robin over workers in linear order           */
+  int32_t k_qkv, k_o, k_down; /* k-splits of the q/k/v, O and down projections: tile n   */
+                              /* is column tile n / k over k range n % k (ranges on a    */
+                              /* quantum of 32; at most one range per 32 elements), each */
+                              /* range writing its own plane of partial sums; t_qkv must */
+                              /* be a multiple of n_kv_heads x k_qkv, t_o of k_o, t_down */
+                              /* of k_down (default 2, 4, 4 at batch > 1; 1 at batch 1,  */
+                              /* the only value allowed there)                           */
   int32_t attn_jit;      /* attention tasks: 0 default (JIT at batch > 1, where the splits */
                          /* of an event differ in cost with the requests' lengths; AOT at */
                          /* batch 1, where they are equal), 1 JIT, 2 AOT; the exported    */
@@ -236,10 +243,11 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
  * (`bytes` must equal its size).  All are fp32 [B][...]: ids 3 pmax[B][t_lm]
  * (fp32 value, int32 index pairs); per layer l, 5 + 13*l + k with k = 0 r
  * (residual into the layer), 2 qkv (raw projection, group-major: per kv group
- * its query heads, key head, value head), 6 attention partials
+ * its query heads, key head, value head; k_qkv planes [k_qkv][B][...] whose
+ * sum is the projection), 6 attention partials
  * [kv][s_attn][G][2 + head_dim] (per kv group and slot: max, sum, output;
- * a request's splits occupy consecutive slots), 7 attn, 8 o, 9 s
- * (residual after attention), 11 a, 12 d; at batch > 1 also 0 e[B][H],
+ * a request's splits occupy consecutive slots), 7 attn, 8 o (k_o planes), 9 s
+ * (residual after attention), 11 a, 12 d (k_down planes); at batch > 1 also 0 e[B][H],
  * 1 hf[B][H], and per layer k = 1 h, 10 h2 (the normalised inputs).
  * Synchronises the device. */
 int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes);

@@ -38,6 +38,15 @@ is tiled within each group (``T_qkv / n_kv_heads`` tiles per group), so each
 attention split reads one contiguous column block produced by the tiles of
 its own group and no projection tile feeds two groups.
 
+K-split (batch > 1, a choice of this build): the q/k/v, O and down
+projections cut their input dimension into ``K_qkv``, ``K_o``, ``K_down``
+ranges (on a quantum of 32), and tile ``n`` of a projection is column tile
+``n // K`` over k-range ``n % K``.  Each k-range writes its own plane of
+partial sums (``[plane][b][column]``), and every reader of those outputs
+(attention splits, norm tasks) adds the planes.  A tile then reads only its
+k-range of the activations, which at batch 16 are as many bytes as the
+weights of a 16-row tile.  At batch 1 every K is 1.
+
 Operator fusion (a choice of this build, not of the pages; the rewrites
 below apply unchanged to whatever tasks the decomposition emits): q/k
 RMSNorm + RoPE, the KV-cache append and the split combine run inside the
@@ -93,6 +102,9 @@ class Params:
     T_lm: int = 1
     S_attn: int = 1
     jit_attn: bool = True   # attention tasks JIT (else AOT)
+    K_qkv: int = 1          # k-splits of the q/k/v, O and down projections (batch > 1)
+    K_o: int = 1
+    K_down: int = 1
 
 
 def tile_range(N, q, T, n):
@@ -152,34 +164,42 @@ def decompose(cfg, B, P, prm: Params):
 
     full = lambda tn, n: _box(tn, (0, 0), (B, n))
     row = lambda tn, b, n: _box(tn, (b, 0), (b + 1, n))
+    # q/k/v, O and down outputs have one plane of partial sums per k-split:
+    # [plane][b][column]; their readers take all planes
+    planes = lambda tn, ks, n: _box(tn, (0, 0, 0), (ks, B, n))
+    Kq, Ko, Kd = prm.K_qkv, prm.K_o, prm.K_down
     if not fused:
         for b in range(B):
             add(EMBED, -1, (b,), [], [row(T_E, b, H)])
     for l in range(L):
         t = lambda k: layer_tensor(l, k)
-        prev = [] if l == 0 else [full(layer_tensor(l - 1, L_S), H), full(layer_tensor(l - 1, L_D), H)]
+        prev = [] if l == 0 else [full(layer_tensor(l - 1, L_S), H), planes(layer_tensor(l - 1, L_D), Kd, H)]
         if not fused:
             for b in range(B):
                 add(ATTN_NORM, l, (b,), prev if l else [full(T_E, H)], [row(t(L_R), b, H), row(t(L_H), b, H)])
         tpg = prm.T_qkv // hkv
         for n in range(prm.T_qkv):
-            g, j = divmod(n, tpg)
-            lo, hi = tile_range(Sg, prm.q, tpg, j)
-            outs = [_box(t(L_QKV), (0, g * Sg + lo), (B, g * Sg + hi))]
+            g, r = divmod(n, tpg)
+            j, ks = divmod(r, Kq)
+            lo, hi = tile_range(Sg, prm.q, tpg // Kq, j)
+            klo, khi = tile_range(H, 32, Kq, ks)
+            outs = [_box(t(L_QKV), (ks, 0, g * Sg + lo), (ks + 1, B, g * Sg + hi))]
             if fused and n == 0:
                 outs.append(full(t(L_R), H))
-            add(QKV, l, (n,), prev if fused else [full(t(L_H), H)], outs)
+            add(QKV, l, (n,), prev if fused else [_box(t(L_H), (0, klo), (B, khi))], outs)
         for g in range(hkv):
             for j in range(S):
                 outs = [_box(t(L_PART), (0, g, 0, 0), (1, g + 1, S, G * (d + 2))),
                         _box(t(L_ATTN), (0, g * G * d), (B, (g + 1) * G * d)),
                         _box(t(L_KC), (0, 0, g, 0), (B, maxs, g + 1, d)),
                         _box(t(L_VC), (0, 0, g, 0), (B, maxs, g + 1, d))]
-                add(ATTN, l, (j, g), [_box(t(L_QKV), (0, g * Sg), (B, (g + 1) * Sg))], outs)
+                add(ATTN, l, (j, g), [_box(t(L_QKV), (0, 0, g * Sg), (Kq, B, (g + 1) * Sg))], outs)
         for n in range(prm.T_o):
-            lo, hi = tile_range(H, prm.q, prm.T_o, n)
-            add(OPROJ, l, (n,), [full(t(L_ATTN), hq * d)], [_box(t(L_O), (0, lo), (B, hi))])
-        mid = [full(t(L_R), H), full(t(L_O), H)]
+            c, ks = divmod(n, Ko)
+            lo, hi = tile_range(H, prm.q, prm.T_o // Ko, c)
+            klo, khi = tile_range(hq * d, 32, Ko, ks)
+            add(OPROJ, l, (n,), [_box(t(L_ATTN), (0, klo), (B, khi))], [_box(t(L_O), (ks, 0, lo), (ks + 1, B, hi))])
+        mid = [full(t(L_R), H), planes(t(L_O), Ko, H)]
         if not fused:
             for b in range(B):
                 add(MLP_NORM, l, (b,), mid, [row(t(L_S), b, H), row(t(L_H2), b, H)])
@@ -190,9 +210,11 @@ def decompose(cfg, B, P, prm: Params):
                 outs.append(full(t(L_S), H))
             add(GATEUP, l, (n,), mid if fused else [full(t(L_H2), H)], outs)
         for n in range(prm.T_down):
-            lo, hi = tile_range(H, prm.q, prm.T_down, n)
-            add(DOWN, l, (n,), [full(t(L_A), F)], [_box(t(L_D), (0, lo), (B, hi))])
-    last = [full(layer_tensor(L - 1, L_S), H), full(layer_tensor(L - 1, L_D), H)]
+            c, ks = divmod(n, Kd)
+            lo, hi = tile_range(H, prm.q, prm.T_down // Kd, c)
+            klo, khi = tile_range(F, 32, Kd, ks)
+            add(DOWN, l, (n,), [_box(t(L_A), (0, klo), (B, khi))], [_box(t(L_D), (ks, 0, lo), (ks + 1, B, hi))])
+    last = [full(layer_tensor(L - 1, L_S), H), planes(layer_tensor(L - 1, L_D), Kd, H)]
     if not fused:
         for b in range(B):
             add(FINAL_NORM, -1, (b,), last, [row(T_HF, b, H)])

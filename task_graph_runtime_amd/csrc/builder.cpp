@@ -80,26 +80,38 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   r.q = p.quantum > 0 ? p.quantum : (B == 1 ? 1 : 16);
   const int64_t G = c.n_q_heads / c.n_kv_heads, d = c.head_dim, Sg = (G + 2) * d;
   const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hkv = c.n_kv_heads;
+  // k-splits: at batch > 1 a tile's activation slice costs 4 B per k and
+  // request (fp32), as much as 16 rows of bf16 weights; splitting k shrinks
+  // it while the column tiles grow to keep one tile per worker
+  r.K_qkv = p.k_qkv > 0 ? p.k_qkv : (B > 1 ? 2 : 1);
+  r.K_o = p.k_o > 0 ? p.k_o : (B > 1 ? 4 : 1);
+  r.K_down = p.k_down > 0 ? p.k_down : (B > 1 ? 4 : 1);
+  if (B == 1 && (r.K_qkv != 1 || r.K_o != 1 || r.K_down != 1))
+    return uns("k-splits need batch > 1 (a batch-1 tile stages its whole input)");
+  if (r.K_qkv > cdiv(H, 32) || r.K_o > cdiv((int64_t)c.n_q_heads * d, 32) || r.K_down > cdiv(F, 32))
+    return bad("a k-split finer than 32 elements");
   if (p.t_qkv > 0) {
-    if (p.t_qkv % hkv) return bad("t_qkv must be a multiple of n_kv_heads");
+    if (p.t_qkv % (hkv * r.K_qkv)) return bad("t_qkv must be a multiple of n_kv_heads x k_qkv");
     r.T_qkv = p.t_qkv;
   } else {
-    int64_t tpg = std::max<int64_t>(1, std::min<int64_t>(r.W / hkv, cdiv(Sg, r.q)));
-    r.T_qkv = (int32_t)(tpg * hkv);
+    int64_t tpg = std::max<int64_t>(1, std::min<int64_t>(r.W / (hkv * r.K_qkv), cdiv(Sg, r.q)));
+    r.T_qkv = (int32_t)(tpg * hkv * r.K_qkv);
   }
-  // default: one tile per worker, more (in steps of W) while a tile's
-  // accumulators (columns x rows per column x batch) exceed the LDS budget
-  auto dflt = [&](int32_t v, int64_t N, int64_t rpc) {
-    if (v > 0) return v;
-    const int64_t U = cdiv(N, r.q);
-    int64_t T = std::min<int64_t>(r.W, U);
-    while (T < U && r.q * cdiv(U, T) * rpc * B > kMaxTileAcc) T = std::min<int64_t>(U, T + r.W);
-    return (int32_t)T;
+  // default: one tile per worker (W / K column tiles x K k-ranges), more
+  // column tiles (in steps of W / K) while a tile's accumulators (columns x
+  // rows per column x batch) exceed the LDS budget
+  auto dflt = [&](int32_t v, int64_t N, int64_t rpc, int64_t K) {
+    if (v > 0) return v % K ? -1 : v;
+    const int64_t U = cdiv(N, r.q), Wk = std::max<int64_t>(1, r.W / K);
+    int64_t T = std::min<int64_t>(Wk, U);
+    while (T < U && r.q * cdiv(U, T) * rpc * B > kMaxTileAcc) T = std::min<int64_t>(U, T + Wk);
+    return (int32_t)(T * K);
   };
-  r.T_o = dflt(p.t_o, H, 1);
-  r.T_gu = dflt(p.t_gu, F, 2);
-  r.T_down = dflt(p.t_down, H, 1);
-  r.T_lm = dflt(p.t_lm, V, 1);
+  r.T_o = dflt(p.t_o, H, 1, r.K_o);
+  r.T_gu = dflt(p.t_gu, F, 2, 1);
+  r.T_down = dflt(p.t_down, H, 1, r.K_down);
+  r.T_lm = dflt(p.t_lm, V, 1, 1);
+  if (r.T_o < 0 || r.T_down < 0) return bad("t_o / t_down must be multiples of k_o / k_down");
   int64_t max_pages = cdiv(c.max_seq_len, P);
   // S_attn = M, the attention slots of a kv group (dealt to the requests by
   // page count when the step runs); at batch 1 they are the splits
@@ -114,10 +126,11 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
     int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, 2 * r.W / ((int64_t)B * hkv)));
     r.S_attn = (int32_t)std::min<int64_t>(s, max_pages);
   }
-  if (r.T_qkv / hkv > cdiv(Sg, r.q)) return bad("t_qkv: more tiles per kv group than column quanta");
+  if (r.T_qkv / (hkv * r.K_qkv) > cdiv(Sg, r.q)) return bad("t_qkv: more tiles per kv group than column quanta");
+  // (column tiles per operator)
   struct { int64_t T, N, rows_per_col; const char* name; } ops[] = {
-      {r.T_qkv / hkv, Sg, 1, "t_qkv"}, {r.T_o, H, 1, "t_o"}, {r.T_gu, F, 2, "t_gu"},
-      {r.T_down, H, 1, "t_down"}, {r.T_lm, V, 1, "t_lm"}};
+      {r.T_qkv / (hkv * r.K_qkv), Sg, 1, "t_qkv"}, {r.T_o / r.K_o, H, 1, "t_o"}, {r.T_gu, F, 2, "t_gu"},
+      {r.T_down / r.K_down, H, 1, "t_down"}, {r.T_lm, V, 1, "t_lm"}};
   for (auto& o : ops) {
     if (o.T < 1 || o.T > cdiv(o.N, r.q)) { *err = std::string(o.name) + ": tile count out of range"; return MPK_ERR_INVALID_ARG; }
     if (o.T > 65535) { *err = std::string(o.name) + ": more than 65535 tiles"; return MPK_ERR_INVALID_ARG; }
@@ -153,23 +166,30 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
   // row b); norm tasks declare all B rows of their inputs so that the B tasks
   // of an operator share one event
   auto row = [&](int32_t tensor, int32_t b, int32_t n) { return box(tensor, {b, 0}, {b + 1, n}); };
+  // q/k/v, O and down outputs: one plane of partial sums per k-range,
+  // [plane][b][column]; their readers take all planes
+  auto planes = [&](int32_t tensor, int32_t k, int32_t n) { return box(tensor, {0, 0, 0}, {k, B, n}); };
+  const int32_t Kq = p.K_qkv, Ko = p.K_o, Kd = p.K_down;
   if (!fused)
     for (int32_t b = 0; b < B; ++b) add(MPK_TASK_EMBED, -1, b, 0, 0, {}, {row(T_E, b, H)});
   for (int32_t l = 0; l < L; ++l) {
     auto t = [&](int32_t k) { return layer_tensor(l, k); };
     std::vector<Box> prev;
-    if (l > 0) prev = {full(layer_tensor(l - 1, L_S), H), full(layer_tensor(l - 1, L_D), H)};
+    if (l > 0) prev = {full(layer_tensor(l - 1, L_S), H), planes(layer_tensor(l - 1, L_D), Kd, H)};
     if (!fused)
       for (int32_t b = 0; b < B; ++b)
         add(MPK_TASK_ATTN_NORM, l, b, 0, 0, l ? prev : std::vector<Box>{full(T_E, H)},
             {row(t(L_R), b, H), row(t(L_H), b, H)});
+    // tile n: kv group n / tpg, column tile (n mod tpg) / Kq, k-range n mod Kq
     const int32_t tpg = p.T_qkv / hkv;
     for (int32_t n = 0; n < p.T_qkv; ++n) {
-      int32_t g = n / tpg, j = n % tpg, lo, hi;
-      tile_range(Sg, p.q, tpg, j, &lo, &hi);
-      std::vector<Box> outs = {box(t(L_QKV), {0, g * Sg + lo}, {B, g * Sg + hi})};
+      const int32_t g = n / tpg, j = (n % tpg) / Kq, ks = n % Kq;
+      int32_t lo, hi, klo, khi;
+      tile_range(Sg, p.q, tpg / Kq, j, &lo, &hi);
+      tile_range(H, 32, Kq, ks, &klo, &khi);
+      std::vector<Box> outs = {box(t(L_QKV), {ks, 0, g * Sg + lo}, {ks + 1, B, g * Sg + hi})};
       if (fused && n == 0) outs.push_back(full(t(L_R), H));
-      add(MPK_TASK_QKV, l, n, 0, 0, fused ? prev : std::vector<Box>{full(t(L_H), H)}, outs);
+      add(MPK_TASK_QKV, l, n, 0, 0, fused ? prev : std::vector<Box>{box(t(L_H), {0, klo}, {B, khi})}, outs);
     }
     // attention task (j, g) is slot j of kv group g; the request a slot
     // serves is decided at run time from the sequence lengths, so every task
@@ -180,14 +200,16 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
                                  box(t(L_ATTN), {0, g * G * d}, {B, (g + 1) * G * d}),
                                  box(t(L_KC), {0, 0, g, 0}, {B, maxs, g + 1, d}),
                                  box(t(L_VC), {0, 0, g, 0}, {B, maxs, g + 1, d})};
-        add(MPK_TASK_ATTN, l, s, g, 0, {box(t(L_QKV), {0, g * Sg}, {B, (g + 1) * Sg})}, outs);
+        add(MPK_TASK_ATTN, l, s, g, 0, {box(t(L_QKV), {0, 0, g * Sg}, {Kq, B, (g + 1) * Sg})}, outs);
       }
-    for (int32_t n = 0; n < p.T_o; ++n) {
-      int32_t lo, hi;
-      tile_range(H, p.q, p.T_o, n, &lo, &hi);
-      add(MPK_TASK_OPROJ, l, n, 0, 0, {full(t(L_ATTN), hq * d)}, {box(t(L_O), {0, lo}, {B, hi})});
+    for (int32_t n = 0; n < p.T_o; ++n) {   // column tile n / Ko, k-range n mod Ko
+      int32_t lo, hi, klo, khi;
+      tile_range(H, p.q, p.T_o / Ko, n / Ko, &lo, &hi);
+      tile_range(hq * d, 32, Ko, n % Ko, &klo, &khi);
+      add(MPK_TASK_OPROJ, l, n, 0, 0, {box(t(L_ATTN), {0, klo}, {B, khi})},
+          {box(t(L_O), {n % Ko, 0, lo}, {n % Ko + 1, B, hi})});
     }
-    const std::vector<Box> mid = {full(t(L_R), H), full(t(L_O), H)};
+    const std::vector<Box> mid = {full(t(L_R), H), planes(t(L_O), Ko, H)};
     if (!fused)
       for (int32_t b = 0; b < B; ++b) add(MPK_TASK_MLP_NORM, l, b, 0, 0, mid, {row(t(L_S), b, H), row(t(L_H2), b, H)});
     for (int32_t n = 0; n < p.T_gu; ++n) {
@@ -197,13 +219,15 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
       if (fused && n == 0) outs.push_back(full(t(L_S), H));
       add(MPK_TASK_GATEUP, l, n, 0, 0, fused ? mid : std::vector<Box>{full(t(L_H2), H)}, outs);
     }
-    for (int32_t n = 0; n < p.T_down; ++n) {
-      int32_t lo, hi;
-      tile_range(H, p.q, p.T_down, n, &lo, &hi);
-      add(MPK_TASK_DOWN, l, n, 0, 0, {full(t(L_A), F)}, {box(t(L_D), {0, lo}, {B, hi})});
+    for (int32_t n = 0; n < p.T_down; ++n) {   // column tile n / Kd, k-range n mod Kd
+      int32_t lo, hi, klo, khi;
+      tile_range(H, p.q, p.T_down / Kd, n / Kd, &lo, &hi);
+      tile_range(F, 32, Kd, n % Kd, &klo, &khi);
+      add(MPK_TASK_DOWN, l, n, 0, 0, {box(t(L_A), {0, klo}, {B, khi})},
+          {box(t(L_D), {n % Kd, 0, lo}, {n % Kd + 1, B, hi})});
     }
   }
-  const std::vector<Box> last = {full(layer_tensor(L - 1, L_S), H), full(layer_tensor(L - 1, L_D), H)};
+  const std::vector<Box> last = {full(layer_tensor(L - 1, L_S), H), planes(layer_tensor(L - 1, L_D), Kd, H)};
   if (!fused)
     for (int32_t b = 0; b < B; ++b) add(MPK_TASK_FINAL_NORM, -1, b, 0, 0, last, {row(T_HF, b, H)});
   for (int32_t n = 0; n < p.T_lm; ++n) {

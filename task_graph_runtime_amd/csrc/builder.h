@@ -35,6 +35,7 @@ struct Params {
   int32_t W = 1, S_sched = 16, q = 1;
   int32_t T_qkv = 1, T_o = 1, T_gu = 1, T_down = 1, T_lm = 1, S_attn = 1;
   bool jit_attn = true;   // attention tasks JIT (else AOT)
+  int32_t K_qkv = 1, K_o = 1, K_down = 1;   // k-splits (batch > 1)
 };
 
 // The linearised graph (task index = linear position), as exported.

@@ -152,16 +152,23 @@ void fill_descriptors(mpk_tgraph* t) {
                   c2 = g.task_coords[3 * (size_t)i + 2];
     int32_t lo = 0, hi = 0;
     switch (d.type) {
+      // (projection tile n of a k-split into K ranges: column tile n / K,
+      // k range n % K, which the device derives from a2 = n)
       case MPK_TASK_QKV: {
-        int32_t gg = c0 / tpg, j = c0 % tpg;
-        tile_range(Sg, p.q, tpg, j, &lo, &hi);
+        int32_t gg = c0 / tpg, j = (c0 % tpg) / p.K_qkv;
+        tile_range(Sg, p.q, tpg / p.K_qkv, j, &lo, &hi);
         d.a0 = gg * Sg + lo; d.a1 = gg * Sg + hi; d.a2 = c0;
         break;
       }
-      case MPK_TASK_OPROJ: tile_range(c.hidden, p.q, p.T_o, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_OPROJ:
+        tile_range(c.hidden, p.q, p.T_o / p.K_o, c0 / p.K_o, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0;
+        break;
       case MPK_TASK_GATEUP: tile_range(c.ffn, p.q, p.T_gu, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
-      case MPK_TASK_DOWN: tile_range(c.hidden, p.q, p.T_down, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_DOWN:
+        tile_range(c.hidden, p.q, p.T_down / p.K_down, c0 / p.K_down, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0;
+        break;
       case MPK_TASK_LMHEAD: tile_range(c.vocab, p.q, p.T_lm, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_ATTN: d.a0 = c0; d.a1 = c1; d.a2 = p.K_qkv; break;
       default: d.a0 = c0; d.a1 = c1; d.a2 = c2; break;
     }
   }
@@ -217,7 +224,8 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
   const int64_t H = c.hidden, F = c.ffn, d = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, G = hq / hkv;
   const bool fused = fused_norm(B);
   int64_t stage = fused ? std::max({chunks(H * 4), chunks(hq * d * 4), chunks(F * 4), 2 * chunks(H * 4) + chunks(H * 2)})
-                        : chunks(H * 2) + 2 * chunks(H * 4);   // a norm task's gain and one row pair
+                        : chunks(H * 2) + (1 + std::max(p.K_o, p.K_down)) * chunks(H * 4);
+  // (batch > 1: a norm task's gain, its residual row and the k-split planes it adds)
   // attention: wavefront merge states, raw q/k/v row, processed heads
   stage = std::max(stage, chunks(kWaves * G * (d + 2) * 4) + 2 * chunks((G + 2) * d * 4));
   // the split combine stages a request's records when they fit in 96 KB (else it reads them from
@@ -228,8 +236,9 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
   // accumulators: the widest projection tile, rows per column x batch
   const int64_t tpg = p.T_qkv / hkv, Sg = (G + 2) * d;
   auto widest = [&](int64_t N, int64_t T) { return p.q * ((((N + p.q - 1) / p.q) + T - 1) / T); };
-  const int64_t acc = chunks(4 * B * std::max({widest(Sg, tpg), widest(H, p.T_o), 2 * widest(F, p.T_gu),
-                                               widest(H, p.T_down), widest(c.vocab, p.T_lm)}));
+  const int64_t acc = chunks(4 * B * std::max({widest(Sg, tpg / p.K_qkv), widest(H, p.T_o / p.K_o),
+                                               2 * widest(F, p.T_gu), widest(H, p.T_down / p.K_down),
+                                               widest(c.vocab, p.T_lm)}));
   const int64_t max_pages = std::min<int64_t>((c.max_seq_len + P - 1) / P, 4096);
   const int64_t pid = kLdsBytes - kLdsTop - chunks(4 * max_pages);
   const int64_t pf = stage + acc;
@@ -365,8 +374,11 @@ int upload(mpk_tgraph* t) {
   const int64_t B = t->B, H = c.hidden, L = c.n_layers, hq = c.n_q_heads, hkv = c.n_kv_heads, d = c.head_dim;
   const int64_t G = hq / hkv, Sg = (G + 2) * d, F = c.ffn, S_at = t->prm.S_attn;
   KArgs& a = t->base;
-  a.st_bh = B * H; a.st_qkv = B * hkv * Sg; a.st_q = B * hq * d; a.st_part = hkv * S_at * G * (d + 2);
+  a.st_bh = B * H; a.st_q = B * hq * d; a.st_part = hkv * S_at * G * (d + 2);
   a.st_a = B * F;
+  // k-split projections write K planes [K][B][...] whose sum is the output
+  a.Kq = t->prm.K_qkv; a.Ko = t->prm.K_o; a.Kd = t->prm.K_down;
+  a.st_qkv = a.Kq * B * hkv * Sg; a.st_o = a.Ko * a.st_bh; a.st_dn = a.Kd * a.st_bh;
   // batch > 1 only (norm tasks): e, hf, h, h2
   const bool fused = fused_norm(t->B);
   struct Item { int id; int64_t bytes; };
@@ -374,8 +386,8 @@ int upload(mpk_tgraph* t) {
   if (!fused) items.insert(items.begin(), {{T_E, B * H * 4}, {T_HF, B * H * 4}});
   const int64_t nf = fused ? 0 : 1;
   const int64_t per_layer_bytes[L_COUNT] = {a.st_bh * 4, nf * a.st_bh * 4, a.st_qkv * 4, 0, 0, 0,
-                                            a.st_part * 4, a.st_q * 4, a.st_bh * 4, a.st_bh * 4,
-                                            nf * a.st_bh * 4, a.st_a * 4, a.st_bh * 4};
+                                            a.st_part * 4, a.st_q * 4, a.st_o * 4, a.st_bh * 4,
+                                            nf * a.st_bh * 4, a.st_a * 4, a.st_dn * 4};
   // one contiguous [L][...] block per per-layer tensor kind
   int64_t off = 0;
   std::vector<int64_t> shared_off(5, -1), kind_off(L_COUNT, -1);
@@ -579,6 +591,7 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   r.n_workers = prm.W; r.n_sched_waves = prm.S_sched; r.quantum = prm.q; r.t_qkv = prm.T_qkv; r.t_o = prm.T_o;
   r.t_gu = prm.T_gu; r.t_down = prm.T_down; r.t_lm = prm.T_lm; r.s_attn = prm.S_attn; r.host_only = host_only;
   r.attn_jit = prm.jit_attn ? 1 : 2;
+  r.k_qkv = prm.K_qkv; r.k_o = prm.K_o; r.k_down = prm.K_down;
   t->resolved = r;
   std::vector<TaskDef> tasks;
   decompose(*cfg, batch, prm, &tasks);

@@ -20,7 +20,9 @@ namespace mpk {
 
 // One linearised task, 32 bytes (two 16-byte loads / one s_load_dwordx8).
 // a0..a2 are the task's operands: projection tiles (a0, a1) = output column
-// range, a2 = tile index; per-request tasks a0 = b, a1 = kv group, a2 = split.
+// range, a2 = tile index (under a k-split into K ranges, k range a2 % K);
+// attention a0 = slot, a1 = kv group, a2 = the q/k/v projection's plane
+// count; per-request norms and the embedding a0 = b.
 // id is the task's own linear index and dep_counts the trigger count of its
 // dependent event, so that a worker holding the descriptor needs no further
 // load before it can wait.
@@ -185,7 +187,10 @@ struct KArgs {
   MPK_GLOBAL float* h2;
   MPK_GLOBAL float* a;
   MPK_GLOBAL float* dn;
-  int64_t st_bh, st_qkv, st_q, st_part, st_a;
+  int64_t st_bh, st_qkv, st_q, st_part, st_a, st_o, st_dn;
+  // k-split of the QKV, O and down projections at batch > 1: qkv, o and dn
+  // hold Kq, Ko and Kd planes of [B][...] each, the output is their sum
+  int32_t Kq, Ko, Kd;
   // split arrivals per (layer, request, kv group): the attention split that
   // brings one to S_attn is the last of its (b, g), merges the partials and
   // resets it to 0, so it is 0 between steps

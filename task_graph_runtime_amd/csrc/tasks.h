@@ -256,11 +256,11 @@ __device__ __forceinline__ void embed_task(const KArgs& a, int b) {
 }
 
 // ------------------------------------------------------------------ residual add + RMSNorm
-// Row b: res = x + y (y optional), stored when `res` is given;
-// out = RMSNorm(res) * gamma.  gamma and the input rows are staged in LDS
-// with direct loads.
+// Row b: res = x + y, with y the sum of ny planes [ny][B][H] (ny = 0: no y),
+// stored when `res` is given; out = RMSNorm(res) * gamma.  gamma and the
+// input rows are staged in LDS with direct loads.
 __device__ __forceinline__ void norm_task(const KArgs& a, int b, gptr<const float> __restrict__ x,
-                                          gptr<const float> __restrict__ y, gptr<float> __restrict__ res,
+                                          gptr<const float> __restrict__ y, int ny, gptr<float> __restrict__ res,
                                           gptr<const uint16_t> __restrict__ gamma, gptr<float> __restrict__ out,
                                           char* lds, float* red) {
   const int tid0 = tidx();
@@ -268,23 +268,26 @@ __device__ __forceinline__ void norm_task(const KArgs& a, int b, gptr<const floa
   const int hb = lds_chunks(H * 4), gb = lds_chunks(H * 2);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(lds);
   const float* xr = reinterpret_cast<const float*>(lds + gb);
-  const float* yr = reinterpret_cast<const float*>(lds + gb + hb);
   const int64_t off = (int64_t)b * H;
   lds_stage<16>(gamma, lds, H / 8, tid0);
   lds_stage<16, true>(x + off, lds + gb, H / 4, tid0);
-  if (y) lds_stage<16, true>(y + off, lds + gb + hb, H / 4, tid0);
+  for (int p = 0; p < ny; ++p) lds_stage<16, true>(y + p * a.st_bh + off, lds + gb + hb * (1 + p), H / 4, tid0);
   lds_stage_wait();
   mark(a, 0);
+  // the row in place: xr = x + sum of the planes, each element by the thread that reads it again
+  float* xw = reinterpret_cast<float*>(lds + gb);
   float ss = 0.f;
   for (int i = tid0; i < H; i += kThreads) {
-    const float v = y ? xr[i] + yr[i] : xr[i];
+    float v = xr[i];
+    for (int p = 0; p < ny; ++p) v += xr[i + (1 + p) * (hb / 4)];
+    xw[i] = v;
     ss = fmaf(v, v, ss);
   }
   ss = block_sum(ss, red);
   mark(a, 1);
   const float inv = 1.0f / sqrtf(ss / (float)H + a.eps);
   for (int i = tid0; i < H; i += kThreads) {
-    const float v = y ? xr[i] + yr[i] : xr[i];
+    const float v = xr[i];
     if (res) st_coh(res + off + i, v);
     st_coh(out + off + i, v * inv * bf2f(gs[i]));
   }
@@ -378,15 +381,21 @@ __device__ __forceinline__ void seg_next(const KArgs& a, const DevTask& t, const
   }
 }
 
-// Epilogue of a projection tile from the LDS accumulators acc[row][B].
-__device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, const float* acc, float* red) {
+// k range of projection tile n under a split of its contraction into K
+// ranges: n % K (the plane its partial sums go to); K = 1: 0.
+__device__ __forceinline__ int ksplit_part(int K, int n) { return K == 1 ? 0 : n % K; }
+
+// Epilogue of a projection tile from the LDS accumulators acc[row][B]; the
+// q/k/v, O and down tiles write k-split plane `plane` (0 at batch 1).
+__device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, const float* acc, float* red,
+                                              int plane) {
   const int tid0 = tidx();
   const int type = t.type, l = t.layer, lo = t.a0, ncol = t.a1 - t.a0, B = a.B;
   const int w = tid0 >> 6, lane = tid0 & 63;
   switch (type) {
     case MPK_TASK_QKV: {
       const int ld = a.hkv * a.Sg;
-      gptr<float> out = a.qkv + (int64_t)l * a.st_qkv;
+      gptr<float> out = a.qkv + (int64_t)l * a.st_qkv + (int64_t)plane * B * ld;
       for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         st_coh(out + (int64_t)b * ld + lo + c, acc[c * B + b]);
@@ -394,7 +403,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       break;
     }
     case MPK_TASK_OPROJ: {
-      gptr<float> out = a.o + (int64_t)l * a.st_bh;
+      gptr<float> out = a.o + (int64_t)l * a.st_o + (int64_t)plane * a.st_bh;
       for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         st_coh(out + (int64_t)b * a.H + lo + c, acc[c * B + b]);
@@ -402,7 +411,7 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
       break;
     }
     case MPK_TASK_DOWN: {
-      gptr<float> out = a.dn + (int64_t)l * a.st_bh;
+      gptr<float> out = a.dn + (int64_t)l * a.st_dn + (int64_t)plane * a.st_bh;
       for (int i = tid0; i < ncol * B; i += kThreads) {
         int b = i / ncol, c = i - b * ncol;
         st_coh(out + (int64_t)b * a.H + lo + c, acc[c * B + b]);
@@ -543,18 +552,18 @@ __device__ __forceinline__ XSrc gemv_xsrc(const KArgs& a, const DevTask& t, cons
         x.emb = a.embed + (int64_t)id * a.H;
       } else {
         x.v1 = a.s + (int64_t)(l - 1) * a.st_bh;
-        x.v2 = a.dn + (int64_t)(l - 1) * a.st_bh;
+        x.v2 = a.dn + (int64_t)(l - 1) * a.st_dn;
       }
       if (t.a2 == 0) x.res = a.r + (int64_t)l * a.st_bh;
       break;
     case MPK_TASK_GATEUP:
       x.v1 = a.r + (int64_t)l * a.st_bh;
-      x.v2 = a.o + (int64_t)l * a.st_bh;
+      x.v2 = a.o + (int64_t)l * a.st_o;
       if (t.a2 == 0) x.res = a.s + (int64_t)l * a.st_bh;
       break;
     case MPK_TASK_LMHEAD:
       x.v1 = a.s + (int64_t)(a.L - 1) * a.st_bh;
-      x.v2 = a.dn + (int64_t)(a.L - 1) * a.st_bh;
+      x.v2 = a.dn + (int64_t)(a.L - 1) * a.st_dn;
       break;
     case MPK_TASK_OPROJ:
       x.v1 = a.attn + (int64_t)l * a.st_q;
@@ -797,7 +806,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
   flush();
   mark(a, 1);
   __syncthreads();
-  gemv_epilogue(a, t, acc, red);
+  gemv_epilogue(a, t, acc, red, 0);
 }
 
 // ------------------------------------------------------------------ projection tile, batch 2..16 (MFMA)
@@ -935,8 +944,13 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
   for (int i = tid0; i < nrows * B; i += kThreads) acc[i] = 0.f;
   __syncthreads();
   const int w = tid0 >> 6;
-  const int nks = (K + 31) >> 5, nrb = (nrows + 15) >> 4;
-  const int ks0 = nks * w / kWaves, ks1 = nks * (w + 1) / kWaves;
+  const int nrb = (nrows + 15) >> 4;
+  // the tile's k range (a split of the contraction into ks ranges, on a
+  // quantum of one 32-k step) and the wavefront's share of it
+  const int ks = t.type == MPK_TASK_QKV ? a.Kq : t.type == MPK_TASK_OPROJ ? a.Ko : t.type == MPK_TASK_DOWN ? a.Kd : 1;
+  const int U = (K + 31) >> 5, kr = ksplit_part(ks, t.a2);
+  const int kb = kr * U / ks, nks = (kr + 1) * U / ks - kb;
+  const int ks0 = kb + nks * w / kWaves, ks1 = kb + nks * (w + 1) / kWaves;
   // weights in flight per wavefront: NRB x KG KB
   if (ks1 > ks0) {
     if (nrb <= 2) mfma_passes<2, 4>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
@@ -944,7 +958,7 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
     else mfma_passes<8, 2>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
   }
   __syncthreads();
-  gemv_epilogue(a, t, acc, red);
+  gemv_epilogue(a, t, acc, red, kr);
 }
 
 // ------------------------------------------------------------------ paged attention, one split
@@ -1100,11 +1114,20 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
   float* raw = reinterpret_cast<float*>(lds + o_raw);
   float* qk = reinterpret_cast<float*>(lds + o_qk);
   gptr<const float> src = a.qkv + (int64_t)l * a.st_qkv + (int64_t)b * a.hkv * a.Sg + (int64_t)g * a.Sg;
-  // (through registers: see gemv_preload)
+  // (through registers: see gemv_preload; the row is the sum of the
+  // projection's t.a2 k-split planes)
   const int nraw = (G + 2) * D;
   float4 rv[(10 * 128 + 4 * kThreads - 1) / (4 * kThreads)];
 #pragma unroll
   for (int j = 0; j < (int)(sizeof(rv) / sizeof(rv[0])); ++j) rv[j] = ld4_coh(src, (tid0 + j * kThreads) * 4, nraw);
+  for (int p = 1; p < t.a2; ++p) {
+    gptr<const float> sp = src + (int64_t)p * a.B * a.hkv * a.Sg;
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(rv) / sizeof(rv[0])); ++j) {
+      const float4 v = ld4_coh(sp, (tid0 + j * kThreads) * 4, nraw);
+      rv[j].x += v.x; rv[j].y += v.y; rv[j].z += v.z; rv[j].w += v.w;
+    }
+  }
 
   const int Lb = a.seq_lens[b];
   const bool ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
@@ -1381,18 +1404,18 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
       embed_task(a, t.a0);
       break;
     case MPK_TASK_ATTN_NORM:
-      if (l == 0) norm_task(a, t.a0, a.e, nullptr, a.r, P.p0, a.h, lds, red);
+      if (l == 0) norm_task(a, t.a0, a.e, nullptr, 0, a.r, P.p0, a.h, lds, red);
       else
-        norm_task(a, t.a0, a.s + (int64_t)(l - 1) * a.st_bh, a.dn + (int64_t)(l - 1) * a.st_bh,
+        norm_task(a, t.a0, a.s + (int64_t)(l - 1) * a.st_bh, a.dn + (int64_t)(l - 1) * a.st_dn, a.Kd,
                   a.r + (int64_t)l * a.st_bh, P.p0, a.h + (int64_t)l * a.st_bh, lds, red);
       break;
     case MPK_TASK_MLP_NORM:
-      norm_task(a, t.a0, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_bh, a.s + (int64_t)l * a.st_bh,
+      norm_task(a, t.a0, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_o, a.Ko, a.s + (int64_t)l * a.st_bh,
                 P.p0, a.h2 + (int64_t)l * a.st_bh, lds, red);
       break;
     case MPK_TASK_FINAL_NORM:
-      norm_task(a, t.a0, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_bh, nullptr, P.p0,
-                a.hf, lds, red);
+      norm_task(a, t.a0, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_dn, a.Kd, nullptr,
+                P.p0, a.hf, lds, red);
       break;
     case MPK_TASK_QKV:
     case MPK_TASK_OPROJ:

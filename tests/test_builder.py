@@ -30,7 +30,8 @@ def both(shape, B, W, q=None, S=None, **over):
     library, overrides applied) and with the oracle spec (params read back
     from the library's header)."""
     s = shape
-    names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm")
+    names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm", K_qkv="k_qkv", K_o="k_o",
+                 K_down="k_down")
     params = dict(n_workers=W, s_attn=S or max(4, B), attn_jit=over.pop("attn_jit", 0))
     if q is not None:
         params["quantum"] = q
@@ -40,7 +41,7 @@ def both(shape, B, W, q=None, S=None, **over):
     p = g.header()["params"]
     prm = tg.Params(W=p["n_workers"], S_sched=p["n_sched_waves"], q=p["quantum"], T_qkv=p["t_qkv"], T_o=p["t_o"],
                     T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"],
-                    jit_attn=p["attn_jit"] == 1)
+                    jit_attn=p["attn_jit"] == 1, K_qkv=p["k_qkv"], K_o=p["k_o"], K_down=p["k_down"])
     ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
     got = g.export()
     got["params"] = p
@@ -67,6 +68,28 @@ def test_attention_policy_at_batch_above_one(B, attn_jit, resolved):
     assert_same(ref, got)
     assert got["params"]["attn_jit"] == resolved
     tg.check_semantics(got, tasks, closure=True)
+
+
+@pytest.mark.parametrize("K", [(1, 1, 1), (3, 2, 4), (2, 5, 3)])
+def test_k_split_bit_exact(K):
+    """Projections split along their contraction (batch > 1): tile n is column
+    tile n / K over k range n % K, its output one of K planes that the
+    consumers read whole."""
+    s = synth.SHAPES["tiny"]
+    ref, got, tasks = both(s, 3, 13, S=4, K_qkv=K[0], K_o=K[1], K_down=K[2])
+    assert_same(ref, got)
+    p = got["params"]
+    assert (p["k_qkv"], p["k_o"], p["k_down"]) == K
+    assert p["t_qkv"] % (s.n_kv_heads * K[0]) == 0 and p["t_o"] % K[1] == 0 and p["t_down"] % K[2] == 0
+    tg.check_semantics(got, tasks, closure=True)
+
+
+@pytest.mark.parametrize("B,over", [(1, dict(k_qkv=2)), (1, dict(k_down=2)), (2, dict(k_o=1000)),
+                                    (2, dict(k_qkv=2, t_qkv=6))])
+def test_bad_k_split_rejected(B, over):
+    s = synth.SHAPES["tiny"]
+    with pytest.raises(mpk.MpkError):
+        mpk.TGraph(s.cfg(), B, s.page_size, dict(n_workers=13, s_attn=4) | over, host_only=True)
 
 
 @pytest.mark.parametrize("name,B,W,S,layers", [
@@ -102,6 +125,10 @@ def test_default_params_resolve_as_documented():
     assert h16["quantum"] == 16 and h16["s_attn"] == 31
     # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
     assert h16["t_lm"] == 504 and h16["t_gu"] == 252
+    # the q/k/v, output and down projections split their contraction 2, 4 and 4 ways
+    assert (h16["k_qkv"], h16["k_o"], h16["k_down"]) == (2, 4, 4)
+    assert h16["t_qkv"] == 240 and h16["t_o"] == h16["t_down"] == 252
+    assert (p["k_qkv"], p["k_o"], p["k_down"]) == (1, 1, 1)
 
 
 @settings(max_examples=120, deadline=None, suppress_health_check=[HealthCheck.too_slow])

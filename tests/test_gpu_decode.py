@@ -115,8 +115,11 @@ def test_tiny_intermediates_layer_by_layer(B):
     H, F = s.hidden, s.ffn
     hq, hkv, d = s.n_q_heads, s.n_kv_heads, s.head_dim
     G = hq // hkv
-
+    # q/k/v, output and down projections: the sum of their k-split planes
+    p = g.header()["params"]
+    Kq, Ko, Kd = p["k_qkv"], p["k_o"], p["k_down"]
     if B > 1:
+        assert (Kq, Ko, Kd) != (1, 1, 1)
         np.testing.assert_allclose(g.read_tensor(0, (B, H), np.float32), cap["embed"], rtol=0, atol=0)
     for l in range(s.n_layers):
         t = lambda k: 5 + 13 * l + k
@@ -125,19 +128,37 @@ def test_tiny_intermediates_layer_by_layer(B):
         if B > 1:
             np.testing.assert_allclose(g.read_tensor(t(1), (B, H), np.float32), c["h"], rtol=2e-2, atol=2e-2)
             np.testing.assert_allclose(g.read_tensor(t(10), (B, H), np.float32), c["h2"], rtol=3e-2, atol=3e-2)
-        qkv = g.read_tensor(t(2), (B, hkv, (G + 2) * d), np.float32)
+        qkv = g.read_tensor(t(2), (Kq, B, hkv, (G + 2) * d), np.float32).sum(axis=0)
         # oracle qkv is [q heads | k heads | v heads]; the library's is group-major
         oq = c["qkv"][:, :hq * d].reshape(B, hkv, G * d)
         ok = c["qkv"][:, hq * d:(hq + hkv) * d].reshape(B, hkv, d)
         ov = c["qkv"][:, (hq + hkv) * d:].reshape(B, hkv, d)
         np.testing.assert_allclose(qkv, np.concatenate([oq, ok, ov], axis=2), rtol=3e-2, atol=3e-2)
         np.testing.assert_allclose(g.read_tensor(t(7), (B, hq * d), np.float32), c["attn"], rtol=3e-2, atol=3e-2)
-        np.testing.assert_allclose(g.read_tensor(t(8), (B, H), np.float32), c["o"], rtol=3e-2, atol=3e-2)
+        np.testing.assert_allclose(g.read_tensor(t(8), (Ko, B, H), np.float32).sum(axis=0), c["o"], rtol=3e-2,
+                                   atol=3e-2)
         np.testing.assert_allclose(g.read_tensor(t(9), (B, H), np.float32), c["s"], rtol=3e-2, atol=3e-2)
         np.testing.assert_allclose(g.read_tensor(t(11), (B, F), np.float32), c["a"], rtol=3e-2, atol=3e-2)
-        np.testing.assert_allclose(g.read_tensor(t(12), (B, H), np.float32), c["d"], rtol=3e-2, atol=3e-2)
+        np.testing.assert_allclose(g.read_tensor(t(12), (Kd, B, H), np.float32).sum(axis=0), c["d"], rtol=3e-2,
+                                   atol=3e-2)
     if B > 1:
         np.testing.assert_allclose(g.read_tensor(1, (B, H), np.float32), cap["hf"], rtol=3e-2, atol=3e-2)
+    check_cache(inp, cap)
+
+
+@pytest.mark.parametrize("K", [(1, 1, 1), (3, 2, 4), (2, 5, 3)])
+@pytest.mark.parametrize("mode", ["mega", "base"])
+def test_tiny_k_split(K, mode):
+    """Batch 3 with the q/k/v, output and down projections split along their
+    contraction into K ranges (the readers add the planes)."""
+    s = TINY.with_(batch=3, ctx_range=(3, 120), ctx=0)
+    say("tiny k-split", K, mode)
+    inp = device_inputs(s, seed=31, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    r = Runner(inp, dict(k_qkv=K[0], k_o=K[1], k_down=K[2]))
+    logits, nxt = r.run(mode)
+    check(logits, nxt, ref, ref_next)
     check_cache(inp, cap)
 
 
