@@ -110,8 +110,9 @@ typedef struct {
                               /* quantum of 32; at most one range per 32 elements), each */
                               /* range writing its own plane of partial sums; t_qkv must */
                               /* be a multiple of n_kv_heads x k_qkv, t_o of k_o, t_down */
-                              /* of k_down (default 2, 4, 4 at batch > 1; 1 at batch 1,  */
-                              /* the only value allowed there)                           */
+                              /* of k_down (default 1, 3, 3 at batch > 1 -- 1 where a    */
+                              /* given t_o / t_down is not a multiple of 3; 1 at batch  */
+                              /* 1, the only value allowed there)                        */
   int32_t attn_jit;      /* attention tasks: 0 default (JIT at batch > 1, where the splits */
                          /* of an event differ in cost with the requests' lengths; AOT at */
                          /* batch 1, where they are equal), 1 JIT, 2 AOT; the exported    */

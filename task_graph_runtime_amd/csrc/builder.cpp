@@ -82,10 +82,13 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   const int64_t H = c.hidden, F = c.ffn, V = c.vocab, hkv = c.n_kv_heads;
   // k-splits: at batch > 1 a tile's activation slice costs 4 B per k and
   // request (fp32), as much as 16 rows of bf16 weights; splitting k shrinks
-  // it while the column tiles grow to keep one tile per worker
-  r.K_qkv = p.k_qkv > 0 ? p.k_qkv : (B > 1 ? 2 : 1);
-  r.K_o = p.k_o > 0 ? p.k_o : (B > 1 ? 4 : 1);
-  r.K_down = p.k_down > 0 ? p.k_down : (B > 1 ? 4 : 1);
+  // it while the column tiles grow to keep one tile per worker (defaults:
+  // the fastest of a sweep at the 8B shape, batch 16; the q/k/v projection's
+  // narrow column tiles gain nothing from it; a tile count given without its
+  // k-split keeps the default only if it divides)
+  r.K_qkv = p.k_qkv > 0 ? p.k_qkv : 1;
+  r.K_o = p.k_o > 0 ? p.k_o : (B > 1 && (p.t_o <= 0 || p.t_o % 3 == 0) ? 3 : 1);
+  r.K_down = p.k_down > 0 ? p.k_down : (B > 1 && (p.t_down <= 0 || p.t_down % 3 == 0) ? 3 : 1);
   if (B == 1 && (r.K_qkv != 1 || r.K_o != 1 || r.K_down != 1))
     return uns("k-splits need batch > 1 (a batch-1 tile stages its whole input)");
   if (r.K_qkv > cdiv(H, 32) || r.K_o > cdiv((int64_t)c.n_q_heads * d, 32) || r.K_down > cdiv(F, 32))

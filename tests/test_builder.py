@@ -84,6 +84,13 @@ def test_k_split_bit_exact(K):
     tg.check_semantics(got, tasks, closure=True)
 
 
+def test_k_split_default_yields_to_a_given_tile_count():
+    s = synth.SHAPES["tiny"]
+    p = mpk.TGraph(s.cfg(), 3, s.page_size, dict(n_workers=13, s_attn=4, t_o=4, t_down=6), host_only=True)
+    p = p.header()["params"]
+    assert (p["k_o"], p["k_down"], p["t_o"], p["t_down"]) == (1, 3, 4, 6)
+
+
 @pytest.mark.parametrize("B,over", [(1, dict(k_qkv=2)), (1, dict(k_down=2)), (2, dict(k_o=1000)),
                                     (2, dict(k_qkv=2, t_qkv=6))])
 def test_bad_k_split_rejected(B, over):
@@ -125,9 +132,9 @@ def test_default_params_resolve_as_documented():
     assert h16["quantum"] == 16 and h16["s_attn"] == 31
     # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
     assert h16["t_lm"] == 504 and h16["t_gu"] == 252
-    # the q/k/v, output and down projections split their contraction 2, 4 and 4 ways
-    assert (h16["k_qkv"], h16["k_o"], h16["k_down"]) == (2, 4, 4)
-    assert h16["t_qkv"] == 240 and h16["t_o"] == h16["t_down"] == 252
+    # the output and down projections split their contraction 3 ways
+    assert (h16["k_qkv"], h16["k_o"], h16["k_down"]) == (1, 3, 3)
+    assert h16["t_qkv"] == 248 and h16["t_o"] == h16["t_down"] == 252
     assert (p["k_qkv"], p["k_o"], p["k_down"]) == (1, 1, 1)
 
 
