@@ -880,8 +880,8 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
   auto xload = [&](int kg) {
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
-      xr[2 * j] = ld4_coh(op.x, xoff + kof(kg, j), B * K);
-      xr[2 * j + 1] = ld4_coh(op.x, xoff + kof(kg, j) + 4, B * K);
+      xr[2 * j] = __builtin_bit_cast(float4, ld16<false>(op.x, (xoff + kof(kg, j)) * 4, B * K * 4));
+      xr[2 * j + 1] = __builtin_bit_cast(float4, ld16<false>(op.x, (xoff + kof(kg, j) + 4) * 4, B * K * 4));
     }
   };
   auto xconvert = [&](int kg) {
@@ -951,8 +951,20 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
   const int U = (K + 31) >> 5, kr = ksplit_part(ks, t.a2);
   const int kb = kr * U / ks, nks = (kr + 1) * U / ks - kb;
   const int ks0 = kb + nks * w / kWaves, ks1 = kb + nks * (w + 1) / kWaves;
-  // weights in flight per wavefront: NRB x KG KB
+  // The input rows are task-to-task data, read here with ordinary (L2-
+  // cached) loads rather than agent-coherent ones, so that the tiles on one
+  // XCD share one fetch per line instead of one each.  No L2 can hold a
+  // stale copy: each input is written once per step, by agent-coherent
+  // stores that are complete before this tile's event fires, and nothing
+  // reads it earlier in the step, so no L2 fetched it before the event
+  // (copies from earlier steps are gone: a kernel launch starts with no
+  // stale cached lines, as stream order across launches requires).  A line
+  // that gate/up tiles on two XCDs share (the down projection's input) holds
+  // in the writer's L2 only the bytes that XCD wrote -- a write does not
+  // fill the line -- so the read fetches the line, whose other bytes the
+  // other tile's write-through stores have reached.
   if (ks1 > ks0) {
+    // weights in flight per wavefront: NRB x KG KB
     if (nrb <= 2) mfma_passes<2, 4>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
     else if (nrb <= 4) mfma_passes<4, 4>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
     else mfma_passes<8, 2>(a, t, P, op, acc, nrows, nrb, ks0, ks1);

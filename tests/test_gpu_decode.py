@@ -221,6 +221,26 @@ def test_tiny_repeated_steps_are_stable():
         np.testing.assert_allclose(o, outs[0], rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("B", [1, 3, 16])
+def test_tiny_alternating_inputs(B):
+    """Steps of one graph alternate between two token sets: each step matches
+    its own oracle, so nothing a step reads is left over from the step before
+    (task-to-task data that projection tiles read through the L2)."""
+    s = TINY.with_(batch=B, ctx_range=(3, 120), ctx=0)
+    say("tiny alternating inputs", B)
+    inp = device_inputs(s, seed=41 + B, gamma="uniform")
+    ids = [inp["token_ids"].clone(), (inp["token_ids"] * 7 + 13) % s.vocab]
+    refs = []
+    for t in ids:
+        inp["token_ids"] = t
+        refs.append(run_oracle(inp))
+    r = Runner(inp)
+    for k in [0, 1, 0, 1, 1, 0]:
+        r.inp["token_ids_dev"].copy_(ids[k].to(r.inp["token_ids_dev"].dtype).cuda())
+        logits, nxt = r.run("mega")
+        check(logits, nxt, *refs[k])
+
+
 def test_watchdog_reports_timeout_and_poisons():
     say("watchdog")
     inp = device_inputs(TINY, seed=1)
