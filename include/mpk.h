@@ -113,10 +113,15 @@ typedef struct {
                               /* of k_down (default 1, 3, 3 at batch > 1 -- 1 where a    */
                               /* given t_o / t_down is not a multiple of 3; 1 at batch  */
                               /* 1, the only value allowed there)                        */
-  int32_t attn_jit;      /* attention tasks: 0 default (JIT at batch > 1, where the splits */
-                         /* of an event differ in cost with the requests' lengths; AOT at */
-                         /* batch 1, where they are equal), 1 JIT, 2 AOT; the exported    */
-                         /* header holds the resolved value (1 or 2)                      */
+  int32_t attn_jit;      /* scheduling policy: 0 default (every task AOT: an attention     */
+                         /* task sizes its split from the lengths at run time, so static  */
+                         /* placement is balanced), 1 the hybrid policy (attention JIT,  */
+                         /* the rest AOT), 2 every task AOT, 3 every non-empty task JIT  */
+                         /* but the root event's consumers, which no trigger hands over; */
+                         /* the exported header holds the resolved value (1, 2 or 3)      */
+  int32_t weight_preload; /* 0 default (on), 1 on, 2 off: batch-1 projection tiles load   */
+                          /* their first weight segments before their event fires (the   */
+                          /* cross-task pipelining ablation); the header holds 1 or 2    */
 } mpk_build_params;
 
 typedef struct mpk_tgraph mpk_tgraph; /* opaque; owned by the library */

@@ -21,7 +21,9 @@ Mega-Kernelizing Tensor Programs -- L2"):
   the rest.  Which attention counts as data-dependent is a parameter
   (``Params.jit_attn``); the library's default makes it JIT at batch > 1,
   where an event's splits serve requests of different lengths, and AOT at
-  batch 1, where every split of the step has the same pages.
+  batch 1, where every split of the step has the same pages.  The two ends
+  of the design space, every task AOT and every task JIT
+  (``Params.jit_all``), are the scheduling ablation.
 The HN comment (item 2) fixes the dependency rule: B depends on A iff A
 produces any element B consumes.
 
@@ -102,6 +104,7 @@ class Params:
     T_lm: int = 1
     S_attn: int = 1
     jit_attn: bool = True   # attention tasks JIT (else AOT)
+    jit_all: bool = False   # every non-empty task JIT
     K_qkv: int = 1          # k-splits of the q/k/v, O and down projections (batch > 1)
     K_o: int = 1
     K_down: int = 1
@@ -250,7 +253,7 @@ def producer_sets(tasks):
     return P
 
 
-def canonicalize(tasks, W, jit_attn=True):
+def canonicalize(tasks, W, jit_attn=True, jit_all=False):
     """Fusion (Def 4.1 then 4.2), normalisation, Kahn-BFS linearisation,
     classification and AOT placement.  Returns the exported arrays (dict)."""
     N = len(tasks)
@@ -333,10 +336,18 @@ def canonicalize(tasks, W, jit_attn=True):
 
     order = sorted(range(NT), key=lambda t: new_task[t])
     eorder = sorted(range(NE), key=lambda e: new_ev[e])
-    mode = {EMPTY: MODE_EMPTY, ATTN: MODE_JIT if jit_attn else MODE_AOT}
+    # JIT tasks are handed over when their event fires; the root event is
+    # never triggered, so its consumers stay AOT under every policy
+    mode = {EMPTY: MODE_EMPTY, ATTN: MODE_JIT if jit_attn or jit_all else MODE_AOT}
+    other = MODE_JIT if jit_all else MODE_AOT
+
+    def mode_of(t):
+        m = mode.get(ttype[t], other)
+        return MODE_AOT if m == MODE_JIT and dep[t] == root else m
+
     out = {
         "task_type": np.array([ttype[t] for t in order], dtype=np.uint8),
-        "task_mode": np.array([mode.get(ttype[t], MODE_AOT) for t in order], dtype=np.uint8),
+        "task_mode": np.array([mode_of(t) for t in order], dtype=np.uint8),
         "task_layer": np.array([tlayer[t] for t in order], dtype=np.int16),
         "task_coords": np.array([tcoords[t] for t in order], dtype=np.uint16).reshape(NT, 3),
         "task_orig": np.array([torig[t] for t in order], dtype=np.int32),
@@ -349,7 +360,7 @@ def canonicalize(tasks, W, jit_attn=True):
     flags = np.zeros(NE, dtype=np.uint8)
     for e in range(NE):
         for t in ev_out[e]:
-            m = mode.get(ttype[t], MODE_AOT)
+            m = mode_of(t)
             if m == MODE_JIT:
                 flags[new_ev[e]] |= FLAG_HAS_JIT
             elif m == MODE_EMPTY:
@@ -374,7 +385,7 @@ def canonicalize(tasks, W, jit_attn=True):
 def build(cfg, B, P, prm: Params):
     """The whole spec for a decoder: decompose, then canonicalise."""
     tasks = decompose(cfg, B, P, prm)
-    return canonicalize(tasks, prm.W, prm.jit_attn), tasks
+    return canonicalize(tasks, prm.W, prm.jit_attn, prm.jit_all), tasks
 
 
 # ----------------------------------------------------------------------------- checker
@@ -414,9 +425,14 @@ def check_semantics(g, tasks=None, closure=True):
     assert np.all(maxprod[dep] < np.arange(NT))
     # degree-1 structure and modes
     tt = g["task_type"]; md = g["task_mode"]
-    # JIT tasks are attention tasks, all of one mode (JIT or AOT); EMPTY exactly the empties
-    assert np.all((md != MODE_JIT) | (tt == ATTN)) and np.all((md == MODE_EMPTY) == (tt == EMPTY))
-    assert len(set(md[tt == ATTN].tolist())) <= 1
+    # EMPTY exactly the empties; the root's consumers AOT; either JIT tasks
+    # are attention tasks, all of one mode (JIT or AOT), or every other
+    # non-empty task is JIT
+    assert np.all((md == MODE_EMPTY) == (tt == EMPTY)) and np.all(md[dep == root] != MODE_JIT)
+    if np.any((md == MODE_JIT) & (tt != ATTN)):
+        assert np.all(md[(tt != EMPTY) & (dep != root)] == MODE_JIT)
+    else:
+        assert len(set(md[(tt == ATTN) & (dep != root)].tolist())) <= 1
     for e in range(NE):
         cons = md[first[e]:last[e] + 1]
         f = (FLAG_HAS_JIT if np.any(cons == MODE_JIT) else 0) | (FLAG_HAS_EMPTY if np.any(cons == MODE_EMPTY) else 0)

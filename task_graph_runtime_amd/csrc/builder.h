@@ -34,7 +34,9 @@ struct TaskDef {
 struct Params {
   int32_t W = 1, S_sched = 16, q = 1;
   int32_t T_qkv = 1, T_o = 1, T_gu = 1, T_down = 1, T_lm = 1, S_attn = 1;
-  bool jit_attn = true;   // attention tasks JIT (else AOT)
+  bool jit_attn = true;
+  bool jit_all = false;   // every non-empty task JIT (scheduling ablation)
+  bool preload = true;    // weight pre-load of the next AOT projection tile   // attention tasks JIT (else AOT)
   int32_t K_qkv = 1, K_o = 1, K_down = 1;   // k-splits (batch > 1)
 };
 
@@ -85,6 +87,7 @@ inline bool fused_norm(int32_t B) { return B == 1; }
 void decompose(const mpk_model_cfg& cfg, int32_t B, const Params& p, std::vector<TaskDef>* tasks);
 
 // Canonicalisation pipeline on arbitrary tasks; MPK_ERR_GRAPH on a cycle.
-int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, bool jit_attn, Graph* g, std::string* err);
+// jit: 0 every non-empty task AOT, 1 attention JIT, 2 every non-empty task JIT
+int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, int jit, Graph* g, std::string* err);
 
 }  // namespace mpk

@@ -246,7 +246,7 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
   a->lds_acc = (int32_t)stage;
   a->lds_pf = (int32_t)pf;
   a->lds_pid = (int32_t)pid;
-  a->pf_segs = fused ? (int32_t)std::min<int64_t>(kMaxPfSegs, (pid - pf) / (kPfWaves * 1024)) : 0;
+  a->pf_segs = fused && p.preload ? (int32_t)std::min<int64_t>(kMaxPfSegs, (pid - pf) / (kPfWaves * 1024)) : 0;
   return MPK_OK;
 }
 
@@ -590,12 +590,13 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   mpk_build_params r{};
   r.n_workers = prm.W; r.n_sched_waves = prm.S_sched; r.quantum = prm.q; r.t_qkv = prm.T_qkv; r.t_o = prm.T_o;
   r.t_gu = prm.T_gu; r.t_down = prm.T_down; r.t_lm = prm.T_lm; r.s_attn = prm.S_attn; r.host_only = host_only;
-  r.attn_jit = prm.jit_attn ? 1 : 2;
+  r.attn_jit = prm.jit_all ? 3 : prm.jit_attn ? 1 : 2;
+  r.weight_preload = prm.preload ? 1 : 2;
   r.k_qkv = prm.K_qkv; r.k_o = prm.K_o; r.k_down = prm.K_down;
   t->resolved = r;
   std::vector<TaskDef> tasks;
   decompose(*cfg, batch, prm, &tasks);
-  rc = canonicalize(tasks, prm.W, prm.jit_attn, &t->g, &err);
+  rc = canonicalize(tasks, prm.W, prm.jit_all ? 2 : prm.jit_attn ? 1 : 0, &t->g, &err);
   if (rc) { free_tgraph(t); return fail(rc, err); }
   rc = check_runtime_shape(t->g);
   if (rc) { free_tgraph(t); return rc; }
@@ -653,7 +654,7 @@ int mpk_build_generic(const mpk_task_spec* specs, int32_t n_tasks, const mpk_reg
   }
   Graph g;
   std::string err;
-  int rc = canonicalize(tasks, n_workers, true, &g, &err);
+  int rc = canonicalize(tasks, n_workers, 1, &g, &err);
   if (rc) return fail(rc, err);
   mpk_tgraph_header h{};
   h.n_tasks = g.NT; h.n_events = g.NE; h.root = g.root; h.end = g.end; h.n_fused = g.n_fused;

@@ -254,7 +254,7 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
     __syncthreads();
     if (cmd == CMD_EXIT) break;
     // the task as an AOT entry spread over lanes 0..15 (a JIT task's
-    // descriptor with null weight pointers: JIT tasks are attention tasks)
+    // descriptor, whose weight pointers are resolved below)
     uint32_t cur_v;
     bool pre = false;
     if (cmd == CMD_AOT) {
@@ -267,7 +267,7 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
       cur_v = (threadIdx.x & 15) < 8 ? v : 0u;
     }
     const DevTask t = unpack_task(cur_v);
-    // (a JIT task -- attention -- reads its gains through the pointer table)
+    // (a JIT task resolves its weight pointers through the layer pointer table)
     const TaskPtrs P = cmd == CMD_AOT ? unpack_ptrs(cur_v) : task_ptrs(a, t);
     if (trace && tid == 0) {
       reinterpret_cast<unsigned long long*>(g_lds + kLdsMarks)[0] = 0;

@@ -41,7 +41,8 @@ def both(shape, B, W, q=None, S=None, **over):
     p = g.header()["params"]
     prm = tg.Params(W=p["n_workers"], S_sched=p["n_sched_waves"], q=p["quantum"], T_qkv=p["t_qkv"], T_o=p["t_o"],
                     T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"],
-                    jit_attn=p["attn_jit"] == 1, K_qkv=p["k_qkv"], K_o=p["k_o"], K_down=p["k_down"])
+                    jit_attn=p["attn_jit"] == 1, jit_all=p["attn_jit"] == 3, K_qkv=p["k_qkv"], K_o=p["k_o"],
+                    K_down=p["k_down"])
     ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
     got = g.export()
     got["params"] = p
@@ -61,7 +62,8 @@ def test_tiny_worked_example_bit_exact(attn_jit):
     tg.check_semantics(got, tasks, closure=True)
 
 
-@pytest.mark.parametrize("B,attn_jit,resolved", [(2, 0, 1), (2, 2, 2), (16, 0, 1)])
+@pytest.mark.parametrize("B,attn_jit,resolved", [(2, 0, 2), (2, 1, 1), (2, 2, 2), (16, 0, 2), (16, 1, 1), (1, 3, 3),
+                                                  (3, 3, 3)])
 def test_attention_policy_at_batch_above_one(B, attn_jit, resolved):
     s = synth.SHAPES["tiny"].with_(n_layers=1)
     ref, got, tasks = both(s, B, 13, S=max(2, B), attn_jit=attn_jit)
@@ -82,6 +84,31 @@ def test_k_split_bit_exact(K):
     assert (p["k_qkv"], p["k_o"], p["k_down"]) == K
     assert p["t_qkv"] % (s.n_kv_heads * K[0]) == 0 and p["t_o"] % K[1] == 0 and p["t_down"] % K[2] == 0
     tg.check_semantics(got, tasks, closure=True)
+
+
+def test_all_jit_policy():
+    """attn_jit = 3: every non-empty task JIT but the root's consumers (nothing
+    triggers the root event, so nothing would hand them over), so schedulers
+    exist at batch 1 too."""
+    s = synth.SHAPES["tiny"]
+    ref, got, tasks = both(s, 1, 12, S=4, attn_jit=3)
+    assert_same(ref, got)
+    md, tt, dep = got["task_mode"], got["task_type"], got["task_dep"]
+    root = got["header"]["root"]
+    assert np.all(md[(tt != tg.EMPTY) & (dep != root)] == tg.MODE_JIT)
+    assert np.all(md[dep == root] == tg.MODE_AOT) and got["aot_offsets"][-1] == np.sum(dep == root)
+    assert np.all(tt[dep == root] == tg.QKV)   # the layer-0 projection tiles (batch 1)
+    assert got["params"]["n_sched_waves"] > 0
+    tg.check_semantics(got, tasks, closure=True)
+
+
+def test_weight_preload_switch():
+    s = synth.SHAPES["tiny"]
+    for v, want in ((0, 1), (1, 1), (2, 2)):
+        p = mpk.TGraph(s.cfg(), 1, s.page_size, dict(weight_preload=v), host_only=True).header()["params"]
+        assert p["weight_preload"] == want
+    with pytest.raises(mpk.MpkError):
+        mpk.TGraph(s.cfg(), 1, s.page_size, dict(weight_preload=3), host_only=True)
 
 
 def test_k_split_default_yields_to_a_given_tile_count():
@@ -126,15 +153,18 @@ def test_default_params_resolve_as_documented():
     assert p["n_workers"] == 256 and p["n_sched_waves"] == 0 and p["quantum"] == 1 and p["attn_jit"] == 2
     assert p["t_qkv"] == 256 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 256 and p["s_attn"] == 8
     h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
-    # batch 16: JIT attention; 14 scheduler wavefronts (4 workgroups) leave 252 workers, 18 per scheduler
-    assert h16["n_workers"] == 252 and h16["n_sched_waves"] == 14 and h16["attn_jit"] == 1
-    # one attention task per worker: floor(252 / 8) = 31 slots per kv group, dealt to the 16 requests by pages
-    assert h16["quantum"] == 16 and h16["s_attn"] == 31
+    # batch 16: every task AOT by default too, so no scheduler workgroups: 256 workers
+    assert h16["n_workers"] == 256 and h16["n_sched_waves"] == 0 and h16["attn_jit"] == 2
+    # one attention task per worker: 256 / 8 = 32 slots per kv group, dealt to the 16 requests by pages
+    assert h16["quantum"] == 16 and h16["s_attn"] == 32
     # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
-    assert h16["t_lm"] == 504 and h16["t_gu"] == 252
-    # the output and down projections split their contraction 3 ways
+    assert h16["t_lm"] == 512 and h16["t_gu"] == 256
+    # the output and down projections split their contraction 3 ways (85 column tiles x 3)
     assert (h16["k_qkv"], h16["k_o"], h16["k_down"]) == (1, 3, 3)
-    assert h16["t_qkv"] == 248 and h16["t_o"] == h16["t_down"] == 252
+    assert h16["t_qkv"] == 256 and h16["t_o"] == h16["t_down"] == 255
+    # the hybrid policy (attention JIT): 14 scheduler wavefronts (4 workgroups) leave 252 workers
+    hj = mpk.TGraph(s.cfg(), 16, 64, dict(attn_jit=1), host_only=True).header()["params"]
+    assert hj["n_workers"] == 252 and hj["n_sched_waves"] == 14 and hj["attn_jit"] == 1 and hj["s_attn"] == 31
     assert (p["k_qkv"], p["k_o"], p["k_down"]) == (1, 1, 1)
 
 

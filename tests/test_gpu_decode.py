@@ -163,6 +163,21 @@ def test_tiny_k_split(K, mode):
 
 
 @pytest.mark.parametrize("B", [1, 3])
+@pytest.mark.parametrize("params", [dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2)])
+def test_tiny_scheduling_ablations(B, params):
+    """The ablation builds: every task JIT, attention JIT, and no weight
+    pre-load, each against the oracle."""
+    s = TINY.with_(batch=B, ctx_range=(3, 120), ctx=0)
+    say("tiny ablation", B, params)
+    inp = device_inputs(s, seed=51 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    logits, nxt = Runner(inp, params).run("mega")
+    check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+
+
+@pytest.mark.parametrize("B", [1, 3])
 def test_tiny_eight_query_heads_per_group(B):
     """The G = 8 attention body (32 lanes per key row, as at the 32B shape) on a
     small decoder: 16 q heads over 2 kv heads of 128 dims."""
@@ -268,7 +283,7 @@ def test_bad_token_id_reported_not_faulting():
 
 
 # ------------------------------------------------------------------ real shapes
-def _full(name, seed=0, modes=("mega",), lazy=False):
+def _full(name, seed=0, modes=("mega",), lazy=False, builds=()):
     s = synth.SHAPES[name]
     say(name, "generate")
     inp = device_inputs(s, seed=seed)
@@ -280,8 +295,15 @@ def _full(name, seed=0, modes=("mega",), lazy=False):
         say(name, mode)
         logits, nxt = r.run(mode)
         errs[mode] = check(logits, nxt, ref, ref_next)
+    del r
+    for params in builds:   # other build parameters, mega-kernel
+        say(name, params)
+        r = Runner(inp, params)
+        logits, nxt = r.run("mega")
+        errs[str(params)] = check(logits, nxt, ref, ref_next)
+        del r
     say(name, "max |d|", errs)
-    del r, inp
+    del inp
     torch.cuda.empty_cache()
 
 
@@ -292,12 +314,14 @@ def test_qwen3_0p6b_shape():
 
 @pytest.mark.timeout(600)
 def test_qwen3_8b_shape():
-    _full("qwen3_8b", modes=("mega", "graph"), lazy=True)
+    # (with the scheduling and pre-load ablation builds that the measurements compare)
+    _full("qwen3_8b", modes=("mega", "graph"), lazy=True, builds=(dict(attn_jit=3), dict(weight_preload=2)))
 
 
 @pytest.mark.timeout(600)
 def test_qwen3_8b_batch16_shape():
-    _full("qwen3_8b_b16", modes=("mega",), lazy=True)
+    # (default AOT attention, and the hybrid policy's JIT attention)
+    _full("qwen3_8b_b16", modes=("mega",), lazy=True, builds=(dict(attn_jit=1),))
 
 
 @pytest.mark.timeout(900)
