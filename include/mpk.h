@@ -122,6 +122,10 @@ typedef struct {
   int32_t weight_preload; /* 0 default (on), 1 on, 2 off: batch-1 projection tiles load   */
                           /* their first weight segments before their event fires (the   */
                           /* cross-task pipelining ablation); the header holds 1 or 2    */
+  int32_t coarse_events;  /* 0 default (fine-grained events), 1 the operator-level graph: */
+                          /* an attention split waits for every q/k/v tile, not only its */
+                          /* own kv group's (every other operator already waits for the  */
+                          /* whole previous one) -- the pages' coarse-graph ablation     */
 } mpk_build_params;
 
 typedef struct mpk_tgraph mpk_tgraph; /* opaque; owned by the library */

@@ -105,6 +105,7 @@ class Params:
     S_attn: int = 1
     jit_attn: bool = True   # attention tasks JIT (else AOT)
     jit_all: bool = False   # every non-empty task JIT
+    coarse: bool = False    # operator-level graph: attention waits for every q/k/v tile
     K_qkv: int = 1          # k-splits of the q/k/v, O and down projections (batch > 1)
     K_o: int = 1
     K_down: int = 1
@@ -196,7 +197,11 @@ def decompose(cfg, B, P, prm: Params):
                         _box(t(L_ATTN), (0, g * G * d), (B, (g + 1) * G * d)),
                         _box(t(L_KC), (0, 0, g, 0), (B, maxs, g + 1, d)),
                         _box(t(L_VC), (0, 0, g, 0), (B, maxs, g + 1, d))]
-                add(ATTN, l, (j, g), [_box(t(L_QKV), (0, 0, g * Sg), (Kq, B, (g + 1) * Sg))], outs)
+                # (coarse: the operator-level graph of the pages' ablation, a task
+                # waits for the whole previous operator)
+                qin = (_box(t(L_QKV), (0, 0, 0), (Kq, B, hkv * Sg)) if prm.coarse
+                       else _box(t(L_QKV), (0, 0, g * Sg), (Kq, B, (g + 1) * Sg)))
+                add(ATTN, l, (j, g), [qin], outs)
         for n in range(prm.T_o):
             c, ks = divmod(n, Ko)
             lo, hi = tile_range(H, prm.q, prm.T_o // Ko, c)

@@ -68,6 +68,8 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   r.jit_all = p.attn_jit == 3;
   r.jit_attn = r.jit_all || p.attn_jit == 1;
   r.preload = p.weight_preload != 2;
+  if (p.coarse_events < 0 || p.coarse_events > 1) return bad("coarse_events must be 0 or 1");
+  r.coarse = p.coarse_events == 1;
   // default scheduler count: none when nothing is JIT (every compute unit
   // is a worker), else the largest S <= 16 that divides the worker count, so
   // that every scheduler deals over the same number of workers
@@ -209,7 +211,12 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
                                  box(t(L_ATTN), {0, g * G * d}, {B, (g + 1) * G * d}),
                                  box(t(L_KC), {0, 0, g, 0}, {B, maxs, g + 1, d}),
                                  box(t(L_VC), {0, 0, g, 0}, {B, maxs, g + 1, d})};
-        add(MPK_TASK_ATTN, l, s, g, 0, {box(t(L_QKV), {0, 0, g * Sg}, {Kq, B, (g + 1) * Sg})}, outs);
+        // (coarse: the operator-level graph, where a task waits for the whole
+        // previous operator; only attention's per-group input differs)
+        add(MPK_TASK_ATTN, l, s, g, 0,
+            {p.coarse ? box(t(L_QKV), {0, 0, 0}, {Kq, B, hkv * Sg})
+                      : box(t(L_QKV), {0, 0, g * Sg}, {Kq, B, (g + 1) * Sg})},
+            outs);
       }
     for (int32_t n = 0; n < p.T_o; ++n) {   // column tile n / Ko, k-range n mod Ko
       int32_t lo, hi, klo, khi;

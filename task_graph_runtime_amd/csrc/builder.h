@@ -34,9 +34,10 @@ struct TaskDef {
 struct Params {
   int32_t W = 1, S_sched = 16, q = 1;
   int32_t T_qkv = 1, T_o = 1, T_gu = 1, T_down = 1, T_lm = 1, S_attn = 1;
-  bool jit_attn = true;
+  bool jit_attn = true;   // attention tasks JIT (else AOT)
   bool jit_all = false;   // every non-empty task JIT (scheduling ablation)
-  bool preload = true;    // weight pre-load of the next AOT projection tile   // attention tasks JIT (else AOT)
+  bool preload = true;    // weight pre-load of the next AOT projection tile
+  bool coarse = false;    // operator-level graph: attention waits for all q/k/v tiles
   int32_t K_qkv = 1, K_o = 1, K_down = 1;   // k-splits (batch > 1)
 };
 

@@ -592,6 +592,7 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   r.t_gu = prm.T_gu; r.t_down = prm.T_down; r.t_lm = prm.T_lm; r.s_attn = prm.S_attn; r.host_only = host_only;
   r.attn_jit = prm.jit_all ? 3 : prm.jit_attn ? 1 : 2;
   r.weight_preload = prm.preload ? 1 : 2;
+  r.coarse_events = prm.coarse ? 1 : 0;
   r.k_qkv = prm.K_qkv; r.k_o = prm.K_o; r.k_down = prm.K_down;
   t->resolved = r;
   std::vector<TaskDef> tasks;

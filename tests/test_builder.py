@@ -31,7 +31,7 @@ def both(shape, B, W, q=None, S=None, **over):
     from the library's header)."""
     s = shape
     names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm", K_qkv="k_qkv", K_o="k_o",
-                 K_down="k_down")
+                 K_down="k_down", coarse="coarse_events")
     params = dict(n_workers=W, s_attn=S or max(4, B), attn_jit=over.pop("attn_jit", 0))
     if q is not None:
         params["quantum"] = q
@@ -42,7 +42,7 @@ def both(shape, B, W, q=None, S=None, **over):
     prm = tg.Params(W=p["n_workers"], S_sched=p["n_sched_waves"], q=p["quantum"], T_qkv=p["t_qkv"], T_o=p["t_o"],
                     T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"],
                     jit_attn=p["attn_jit"] == 1, jit_all=p["attn_jit"] == 3, K_qkv=p["k_qkv"], K_o=p["k_o"],
-                    K_down=p["k_down"])
+                    K_down=p["k_down"], coarse=p["coarse_events"] == 1)
     ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
     got = g.export()
     got["params"] = p
@@ -100,6 +100,20 @@ def test_all_jit_policy():
     assert np.all(tt[dep == root] == tg.QKV)   # the layer-0 projection tiles (batch 1)
     assert got["params"]["n_sched_waves"] > 0
     tg.check_semantics(got, tasks, closure=True)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_coarse_operator_level_graph(B):
+    """coarse_events = 1: every attention split waits for every q/k/v tile of
+    its layer (the operator-level graph), so the per-group attention events
+    merge into one."""
+    s = synth.SHAPES["tiny"]
+    ref, got, tasks = both(s, B, 13, S=4, coarse=1)
+    assert_same(ref, got)
+    tg.check_semantics(got, tasks, closure=True)
+    _, fine, _ = both(s, B, 13, S=4)
+    att = lambda g: set(g["task_dep"][g["task_type"] == tg.ATTN].tolist())
+    assert len(att(got)) == s.n_layers and len(att(fine)) == s.n_layers * s.n_kv_heads
 
 
 def test_weight_preload_switch():

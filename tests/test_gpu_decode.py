@@ -163,10 +163,10 @@ def test_tiny_k_split(K, mode):
 
 
 @pytest.mark.parametrize("B", [1, 3])
-@pytest.mark.parametrize("params", [dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2)])
+@pytest.mark.parametrize("params", [dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2), dict(coarse_events=1)])
 def test_tiny_scheduling_ablations(B, params):
-    """The ablation builds: every task JIT, attention JIT, and no weight
-    pre-load, each against the oracle."""
+    """The ablation builds: every task JIT, attention JIT, no weight pre-load
+    and the operator-level graph, each against the oracle."""
     s = TINY.with_(batch=B, ctx_range=(3, 120), ctx=0)
     say("tiny ablation", B, params)
     inp = device_inputs(s, seed=51 + B, gamma="uniform")
@@ -315,7 +315,8 @@ def test_qwen3_0p6b_shape():
 @pytest.mark.timeout(600)
 def test_qwen3_8b_shape():
     # (with the scheduling and pre-load ablation builds that the measurements compare)
-    _full("qwen3_8b", modes=("mega", "graph"), lazy=True, builds=(dict(attn_jit=3), dict(weight_preload=2)))
+    _full("qwen3_8b", modes=("mega", "graph"), lazy=True,
+          builds=(dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2), dict(coarse_events=1)))
 
 
 @pytest.mark.timeout(600)
