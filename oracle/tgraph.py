@@ -14,7 +14,8 @@ Mega-Kernelizing Tensor Programs -- L2"):
   (Def 4.2)": events with equal consumer sets, then equal producer sets, merge;
 * section 4, "6 minimum checks" (check 3) and section 7 ("Empty tasks as
   degree-reduction glue"): normalisation adds one event e' and k empty tasks
-  per fan-out so that every task has <= 1 dependent and <= 1 triggering event;
+  per fan-out (and, for a graph built without fusion, per fan-in) so that
+  every task has <= 1 dependent and <= 1 triggering event;
 * section 4 check 4 (Alg 1): BFS linearisation places the dependent tasks of
   each dequeued event consecutively, so fan-out is a ``[first, last]`` range;
 * section 4, design-space table: JIT for data-dependent attention, AOT for
@@ -105,10 +106,11 @@ class Params:
     S_attn: int = 1
     jit_attn: bool = True   # attention tasks JIT (else AOT)
     jit_all: bool = False   # every non-empty task JIT
-    coarse: bool = False    # operator-level graph: attention waits for every q/k/v tile
+    coarse: bool = False    # operator-level graph: every task waits for the whole previous operator
     K_qkv: int = 1          # k-splits of the q/k/v, O and down projections (batch > 1)
     K_o: int = 1
     K_down: int = 1
+    fusion: int = 0         # 0: Def 4.1 then Def 4.2; 1: no fusion (one event per overlap edge)
 
 
 def tile_range(N, q, T, n):
@@ -190,15 +192,17 @@ def decompose(cfg, B, P, prm: Params):
             outs = [_box(t(L_QKV), (ks, 0, g * Sg + lo), (ks + 1, B, g * Sg + hi))]
             if fused and n == 0:
                 outs.append(full(t(L_R), H))
-            add(QKV, l, (n,), prev if fused else [_box(t(L_H), (0, klo), (B, khi))], outs)
+            # (coarse: the operator-level graph of the pages' ablation, where a task
+            # waits for the whole previous operator, so a k-split tile declares its
+            # whole input row)
+            add(QKV, l, (n,), prev if fused else [full(t(L_H), H) if prm.coarse else _box(t(L_H), (0, klo), (B, khi))],
+                outs)
         for g in range(hkv):
             for j in range(S):
                 outs = [_box(t(L_PART), (0, g, 0, 0), (1, g + 1, S, G * (d + 2))),
                         _box(t(L_ATTN), (0, g * G * d), (B, (g + 1) * G * d)),
                         _box(t(L_KC), (0, 0, g, 0), (B, maxs, g + 1, d)),
                         _box(t(L_VC), (0, 0, g, 0), (B, maxs, g + 1, d))]
-                # (coarse: the operator-level graph of the pages' ablation, a task
-                # waits for the whole previous operator)
                 qin = (_box(t(L_QKV), (0, 0, 0), (Kq, B, hkv * Sg)) if prm.coarse
                        else _box(t(L_QKV), (0, 0, g * Sg), (Kq, B, (g + 1) * Sg)))
                 add(ATTN, l, (j, g), [qin], outs)
@@ -206,7 +210,8 @@ def decompose(cfg, B, P, prm: Params):
             c, ks = divmod(n, Ko)
             lo, hi = tile_range(H, prm.q, prm.T_o // Ko, c)
             klo, khi = tile_range(hq * d, 32, Ko, ks)
-            add(OPROJ, l, (n,), [_box(t(L_ATTN), (0, klo), (B, khi))], [_box(t(L_O), (ks, 0, lo), (ks + 1, B, hi))])
+            oin = full(t(L_ATTN), hq * d) if prm.coarse else _box(t(L_ATTN), (0, klo), (B, khi))
+            add(OPROJ, l, (n,), [oin], [_box(t(L_O), (ks, 0, lo), (ks + 1, B, hi))])
         mid = [full(t(L_R), H), planes(t(L_O), Ko, H)]
         if not fused:
             for b in range(B):
@@ -221,7 +226,8 @@ def decompose(cfg, B, P, prm: Params):
             c, ks = divmod(n, Kd)
             lo, hi = tile_range(H, prm.q, prm.T_down // Kd, c)
             klo, khi = tile_range(F, 32, Kd, ks)
-            add(DOWN, l, (n,), [_box(t(L_A), (0, klo), (B, khi))], [_box(t(L_D), (ks, 0, lo), (ks + 1, B, hi))])
+            din = full(t(L_A), F) if prm.coarse else _box(t(L_A), (0, klo), (B, khi))
+            add(DOWN, l, (n,), [din], [_box(t(L_D), (ks, 0, lo), (ks + 1, B, hi))])
     last = [full(layer_tensor(L - 1, L_S), H), planes(layer_tensor(L - 1, L_D), Kd, H)]
     if not fused:
         for b in range(B):
@@ -258,51 +264,91 @@ def producer_sets(tasks):
     return P
 
 
-def canonicalize(tasks, W, jit_attn=True, jit_all=False):
-    """Fusion (Def 4.1 then 4.2), normalisation, Kahn-BFS linearisation,
-    classification and AOT placement.  Returns the exported arrays (dict)."""
+FUSION_A, FUSION_OFF = 0, 1
+
+
+def canonicalize(tasks, W, jit_attn=True, jit_all=False, fusion=FUSION_A):
+    """Fusion (Def 4.1 then 4.2, or none), normalisation, Kahn-BFS
+    linearisation, classification and AOT placement.  Returns the exported
+    arrays (dict).
+
+    ``fusion=FUSION_OFF`` keeps one event per overlap edge ``(p, c)``
+    (In = {p}, Out = {c}, pre-ordered by ``(c, p)``); a consumer then depends
+    on several events and normalisation needs the fan-in rewrite besides the
+    fan-out one (MPK summary section 4, "6 minimum checks", check 3)."""
     N = len(tasks)
     P = producer_sets(tasks)
 
-    # Def 4.1: one event per consumer with all its producers; Def 4.2: merge equal producer sets.
-    groups = {}
-    for c in range(N):
-        if P[c]:
-            groups.setdefault(frozenset(P[c]), []).append(c)
-    fused = sorted(([sorted(k), sorted(v)] for k, v in groups.items()), key=lambda e: min(e[1]))
-    # fixpoint: Out-sets disjoint, In-sets distinct
-    seen_out = set()
-    for _, o in fused:
-        assert not (seen_out & set(o))
-        seen_out |= set(o)
-    assert len({tuple(i) for i, _ in fused}) == len(fused)
+    if fusion == FUSION_A:
+        # Def 4.1: one event per consumer with all its producers; Def 4.2: merge equal producer sets.
+        groups = {}
+        for c in range(N):
+            if P[c]:
+                groups.setdefault(frozenset(P[c]), []).append(c)
+        fused = sorted(([sorted(k), sorted(v)] for k, v in groups.items()), key=lambda e: min(e[1]))
+        # fixpoint: Out-sets disjoint, In-sets distinct
+        seen_out = set()
+        for _, o in fused:
+            assert not (seen_out & set(o))
+            seen_out |= set(o)
+        assert len({tuple(i) for i, _ in fused}) == len(fused)
+    elif fusion == FUSION_OFF:
+        fused = [[[p], [c]] for c in range(N) for p in sorted(P[c])]
+    else:
+        raise ValueError("fusion must be FUSION_A or FUSION_OFF")
 
     ev_in = [list(i) for i, _ in fused]
     ev_out = [list(o) for _, o in fused]
-    dep = {}
-    trig = {}
+    deps_of = [[] for _ in range(N)]
     for e, o in enumerate(ev_out):
         for c in o:
-            dep[c] = e
+            deps_of[c].append(e)         # in pre-order
     trigs_of = [[] for _ in range(N)]
     for e, i in enumerate(ev_in):
         for p in i:
-            trigs_of[p].append(e)        # already in pre-order (fused is sorted)
+            trigs_of[p].append(e)        # in pre-order
 
+    # normalisation, task by task in original order: a task with k >= 2
+    # dependent events (fan-in, only without fusion) gets a new event e' that
+    # k empty tasks trigger, empty i waiting on the i-th event; a task with
+    # k >= 2 triggering events (fan-out) gets a new event e' that k empty
+    # tasks wait on, empty i triggering the i-th event.  Empty tasks are
+    # numbered after the originals in the order they are made; coords (i, 0)
+    # for a fan-out empty, (i, 1) for a fan-in one.
     ttype = [t["type"] for t in tasks]
     tlayer = [t["layer"] for t in tasks]
     tcoords = [t["coords"] for t in tasks]
     torig = list(range(N))
     n_empty = 0
+    dep = {}
+    trig = {}
+
+    def new_empty(t, i, kind):
+        nonlocal n_empty
+        T = len(ttype)
+        ttype.append(EMPTY); tlayer.append(tlayer[t]); tcoords.append((i, kind, 0))
+        torig.append(-1 - n_empty); n_empty += 1
+        return T
+
     for t in range(N):
+        dl = deps_of[t]
+        if len(dl) >= 2:
+            ep = len(ev_in)
+            ev_in.append([]); ev_out.append([t])
+            for i, e in enumerate(dl):
+                T = new_empty(t, i, 1)
+                dep[T] = e; trig[T] = ep
+                ev_in[ep].append(T)
+                ev_out[e] = [T if x == t else x for x in ev_out[e]]
+            dep[t] = ep
+        elif len(dl) == 1:
+            dep[t] = dl[0]
         tr = trigs_of[t]
         if len(tr) >= 2:
             ep = len(ev_in)
             ev_in.append([t]); ev_out.append([])
             for i, e in enumerate(tr):
-                T = len(ttype)
-                ttype.append(EMPTY); tlayer.append(tlayer[t]); tcoords.append((i, 0, 0))
-                torig.append(-1 - n_empty); n_empty += 1
+                T = new_empty(t, i, 0)
                 dep[T] = ep; trig[T] = e
                 ev_out[ep].append(T)
                 ev_in[e] = [T if x == t else x for x in ev_in[e]]
@@ -390,7 +436,7 @@ def canonicalize(tasks, W, jit_attn=True, jit_all=False):
 def build(cfg, B, P, prm: Params):
     """The whole spec for a decoder: decompose, then canonicalise."""
     tasks = decompose(cfg, B, P, prm)
-    return canonicalize(tasks, prm.W, prm.jit_attn, prm.jit_all), tasks
+    return canonicalize(tasks, prm.W, prm.jit_attn, prm.jit_all, prm.fusion), tasks
 
 
 # ----------------------------------------------------------------------------- checker
@@ -410,47 +456,48 @@ def check_semantics(g, tasks=None, closure=True):
     hdr = g["header"]
     root, end = hdr["root"], hdr["end"]
     dep = g["task_dep"].astype(np.int64); trig = g["task_trig"].astype(np.int64)
-    assert np.all((dep >= 0) & (dep < NE)) and np.all((trig >= 0) & (trig < NE))
-    assert not np.any(dep == end) and not np.any(trig == root)
+    assert np.all((dep >= 0) & (dep < NE)) and np.all((trig >= 0) & (trig < NE)), "event index out of range"
+    assert not np.any(dep == end) and not np.any(trig == root), "a task waits on the end or triggers the root"
     # contiguity
     first = g["event_first"].astype(np.int64); last = g["event_last"].astype(np.int64)
     for e in range(NE):
         idx = np.nonzero(dep == e)[0]
         if len(idx) == 0:
-            assert first[e] == last[e] + 1, e
+            assert first[e] == last[e] + 1, f"contiguity: event {e} has no consumers but range [{first[e]}, {last[e]}]"
         else:
-            assert idx[0] == first[e] and idx[-1] == last[e] and len(idx) == last[e] - first[e] + 1, e
+            assert idx[0] == first[e] and idx[-1] == last[e] and len(idx) == last[e] - first[e] + 1, \
+                f"contiguity: consumers of event {e} are not [first, last]"
     # counts
     cnt = np.bincount(trig, minlength=NE)
-    assert np.array_equal(cnt, g["event_counts"].astype(np.int64))
-    assert g["event_counts"][root] == 0
+    assert np.array_equal(cnt, g["event_counts"].astype(np.int64)), "counts: an event's count differs from its producers"
+    assert g["event_counts"][root] == 0, "counts: the root event has producers"
     # topological: every producer of dep(t) precedes t
     maxprod = np.full(NE, -1, dtype=np.int64)
     np.maximum.at(maxprod, trig, np.arange(NT))
-    assert np.all(maxprod[dep] < np.arange(NT))
+    assert np.all(maxprod[dep] < np.arange(NT)), "topological: a task precedes a producer of its event"
     # degree-1 structure and modes
     tt = g["task_type"]; md = g["task_mode"]
     # EMPTY exactly the empties; the root's consumers AOT; either JIT tasks
     # are attention tasks, all of one mode (JIT or AOT), or every other
     # non-empty task is JIT
-    assert np.all((md == MODE_EMPTY) == (tt == EMPTY)) and np.all(md[dep == root] != MODE_JIT)
+    assert np.all((md == MODE_EMPTY) == (tt == EMPTY)) and np.all(md[dep == root] != MODE_JIT), "modes: empty/JIT modes"
     if np.any((md == MODE_JIT) & (tt != ATTN)):
-        assert np.all(md[(tt != EMPTY) & (dep != root)] == MODE_JIT)
+        assert np.all(md[(tt != EMPTY) & (dep != root)] == MODE_JIT), "modes: mixed JIT policy"
     else:
-        assert len(set(md[(tt == ATTN) & (dep != root)].tolist())) <= 1
+        assert len(set(md[(tt == ATTN) & (dep != root)].tolist())) <= 1, "modes: mixed attention modes"
     for e in range(NE):
         cons = md[first[e]:last[e] + 1]
         f = (FLAG_HAS_JIT if np.any(cons == MODE_JIT) else 0) | (FLAG_HAS_EMPTY if np.any(cons == MODE_EMPTY) else 0)
-        assert g["event_flags"][e] == f
+        assert g["event_flags"][e] == f, f"flags: event {e}"
     # AOT lists
     off = g["aot_offsets"].astype(np.int64); lst = g["aot_tasks"].astype(np.int64)
     W = len(off) - 1
-    assert off[0] == 0 and off[-1] == len(lst) == int(np.sum(md == MODE_AOT))
+    assert off[0] == 0 and off[-1] == len(lst) == int(np.sum(md == MODE_AOT)), "aot: list sizes"
     for w in range(W):
         seg = lst[off[w]:off[w + 1]]
-        assert np.all(np.diff(seg) > 0)
-        assert np.all(g["task_worker"][seg] == w)
-    assert np.all((g["task_worker"] >= 0) == (md == MODE_AOT))
+        assert np.all(np.diff(seg) > 0), f"aot: list of worker {w} not increasing"
+        assert np.all(g["task_worker"][seg] == w), f"aot: task_worker disagrees with list {w}"
+    assert np.all((g["task_worker"] >= 0) == (md == MODE_AOT)), "aot: task_worker on a non-AOT task"
     if tasks is not None and closure:
         _check_closure(g, tasks)
 
@@ -484,7 +531,7 @@ def _check_closure(g, tasks):
         if orig[t] >= 0:
             assert waits[t] == reach[int(orig[t])], f"closure differs at task {t} (orig {orig[t]})"
             seen += 1
-    assert seen == N
+    assert seen == N, "closure: a real task is missing"
 
 
 def generic_tasks(specs, regions):

@@ -187,3 +187,154 @@ def test_random_programs_preserve_every_wait(prog):
     g = tg.canonicalize(tasks, W)
     tg.check_semantics(g, tasks, closure=True)
     assert g["header"]["NT"] == len(tasks) + g["header"]["n_empty"]
+
+
+# ------------------------------------------------------------------ the checker must reject wrong graphs
+# Each case breaks one property that MPK summary section 4 ("6 minimum checks") requires of a
+# canonical tGraph and asserts that check_semantics rejects it, naming the property.
+def _raises(g, tasks, what):
+    with pytest.raises(AssertionError, match=what):
+        tg.check_semantics(g, tasks, closure=tasks is not None)
+
+
+def _copy(g):
+    return {k: (v.copy() if isinstance(v, np.ndarray) else dict(v) if isinstance(v, dict) else v) for k, v in g.items()}
+
+
+def test_checker_rejects_a_dropped_wait():
+    # O-projection tile 0 of layer 0 declares only kv group 0's part of the attention output, so the
+    # graph built from it lets the tile start before group 1's splits: a wait the true boxes need
+    g, tasks = tiny()
+    bad = [dict(t, ins=list(t["ins"])) for t in tasks]
+    k = next(i for i, t in enumerate(bad) if t["type"] == tg.OPROJ and t["layer"] == 0)
+    tn, lo, hi = bad[k]["ins"][0]
+    G_d = 2 * 64                      # tiny: 2 query heads of 64 per kv group
+    bad[k]["ins"][0] = (tn, lo, (hi[0], G_d) + tuple(hi[2:]))
+    gb = tg.canonicalize(bad, TINY_PRM.W, TINY_PRM.jit_attn)
+    tg.check_semantics(gb, bad, closure=True)     # consistent with its own (wrong) boxes
+    _raises(gb, tasks, "closure")
+
+
+def test_checker_rejects_an_added_wait():
+    # the operator-level graph makes every attention split wait for all q/k/v tiles; against the
+    # fine boxes that is a wait no overlap implies
+    from dataclasses import replace
+    _, fine = tiny()
+    gc, coarse = tg.build(synth.SHAPES["tiny"].cfg(), 1, 16, replace(TINY_PRM, coarse=True))
+    tg.check_semantics(gc, coarse, closure=True)
+    _raises(gc, fine, "closure")
+
+
+def test_checker_rejects_a_broken_range():
+    g, tasks = tiny()
+    e = int(np.argmax(g["event_last"] - g["event_first"]))     # an event with several consumers
+    bad = _copy(g)
+    bad["event_last"][e] -= 1
+    _raises(bad, None, "contiguity")
+    bad = _copy(g)
+    bad["event_first"][e] += 1
+    _raises(bad, None, "contiguity")
+
+
+def test_checker_rejects_a_wrong_count():
+    g, tasks = tiny()
+    for e in (int(g["task_dep"][20]), int(g["header"]["end"])):
+        bad = _copy(g)
+        bad["event_counts"][e] += 1
+        _raises(bad, None, "counts")
+
+
+def test_checker_rejects_wrong_flags_and_aot_lists():
+    g, _ = tiny()
+    bad = _copy(g)
+    bad["event_flags"][int(g["task_dep"][8])] ^= tg.FLAG_HAS_EMPTY
+    _raises(bad, None, "flags")
+    bad = _copy(g)
+    lst = bad["aot_tasks"]
+    lst[0], lst[1] = lst[1], lst[0]
+    _raises(bad, None, "aot")
+
+
+def test_checker_rejects_a_non_topological_order():
+    # two tasks: linear task 0 waits on event 1, which linear task 1 triggers; task 1 waits on
+    # the root (event 0), task 0 triggers the end (event 2).  Ranges and counts are consistent;
+    # only the order is wrong.
+    g = {"task_type": np.array([tg.QKV, tg.QKV], np.uint8), "task_mode": np.zeros(2, np.uint8),
+         "task_dep": np.array([1, 0], np.int32), "task_trig": np.array([2, 1], np.int32),
+         "task_worker": np.array([0, 0], np.int16), "event_counts": np.array([0, 1, 1], np.uint32),
+         "event_first": np.array([1, 0, 3], np.int32), "event_last": np.array([1, 0, 2], np.int32),
+         "event_flags": np.zeros(3, np.uint8), "aot_offsets": np.array([0, 2], np.uint32),
+         "aot_tasks": np.array([0, 1], np.uint32), "header": dict(root=0, end=2)}
+    _raises(g, None, "topological")
+    ok = _copy(g)   # the same two tasks in the right order pass
+    ok.update(task_dep=np.array([0, 1], np.int32), task_trig=np.array([1, 2], np.int32),
+              event_first=np.array([0, 1, 2], np.int32), event_last=np.array([0, 1, 1], np.int32))
+    tg.check_semantics(ok)
+
+
+# ------------------------------------------------------------------ top-2 gap
+def test_top2_gap_hand_values():
+    from oracle import numerics as on
+    rows = np.array([[1.0, 3.0, 2.0],        # 3 - 2
+                     [5.0, 5.0, 1.0],        # a tie at the top: 0
+                     [-3.0, -1.0, -2.0],     # negatives: -1 - (-2)
+                     [0.5, 0.5, 0.5],        # all equal: 0
+                     [7.0, -4.0, 2.5]])      # 7 - 2.5
+    np.testing.assert_array_equal(on.top2_gap(rows), [1.0, 0.0, 1.0, 0.0, 4.5])
+    assert on.top2_gap(np.array([2.0, 10.0])) == 8.0
+
+
+# ------------------------------------------------------------------ no fusion: the fan-in rewrite
+def _two_by_two():
+    """Operator A (tiles A0, A1) writes tensor 0; operator B (tiles B0, B1) reads all of it."""
+    specs = [(tg.QKV, 0, 0, 0, 0), (tg.QKV, 0, 1, 0, 0), (tg.OPROJ, 0, 0, 0, 0), (tg.OPROJ, 0, 1, 0, 0)]
+    regions = [(0, 1, 0, (0, 0, 0, 0), (1, 4, 1, 1)), (1, 1, 0, (0, 4, 0, 0), (1, 8, 1, 1)),
+               (2, 0, 0, (0, 0, 0, 0), (1, 8, 1, 1)), (3, 0, 0, (0, 0, 0, 0), (1, 8, 1, 1)),
+               (2, 1, 1, (0, 0, 0, 0), (1, 1, 1, 1)), (3, 1, 1, (0, 1, 0, 0), (1, 2, 1, 1))]
+    return specs, regions
+
+
+def test_fusion_off_hand_example():
+    # Hand derivation.  Fused (Def 4.1 then 4.2): one event {A0, A1} -> {B0, B1}; with root and end
+    # NE = 3, NT = 4.  Without fusion: 4 edge events pre-ordered (B0,A0) (B0,A1) (B1,A0) (B1,A1);
+    # A0 and A1 each fan out to 2 (e' + 2 empties), B0 and B1 each fan in from 2 (e' + 2 empties):
+    # 8 empties, NE = 4 + 4 + 2 = 10.  Empties are numbered A0's two, A1's two (fan-out, coords (i,0)),
+    # then B0's two, B1's two (fan-in, coords (i,1)).  BFS: root -> A0, A1; e'(A0) -> its empties,
+    # which fire (B0,A0), (B1,A0); e'(A1) -> its empties, firing (B0,A1), (B1,A1); those four events
+    # place the fan-in empties of B0, B1, B0, B1; then e'(B0) -> B0, e'(B1) -> B1.
+    specs, regions = _two_by_two()
+    tasks = tg.generic_tasks(specs, regions)
+    gf = tg.canonicalize(tasks, 2)
+    assert (gf["header"]["NT"], gf["header"]["NE"], gf["header"]["n_empty"]) == (4, 3, 0)
+    g = tg.canonicalize(tasks, 2, fusion=tg.FUSION_OFF)
+    h = g["header"]
+    assert (h["NT"], h["NE"], h["n_fused"], h["n_rewrites"], h["n_empty"]) == (12, 10, 4, 4, 8)
+    assert g["task_orig"].tolist() == [0, 1, -1, -2, -3, -4, -5, -7, -6, -8, 2, 3]
+    assert [tuple(c[:2]) for c in g["task_coords"][2:10]] == [(0, 0), (1, 0), (0, 0), (1, 0),
+                                                              (0, 1), (0, 1), (1, 1), (1, 1)]
+    cnt = g["event_counts"][g["task_dep"]]
+    assert cnt.tolist() == [0, 0, 1, 1, 1, 1, 1, 1, 1, 1, 2, 2]   # the fan-in e' of B0 and B1 count 2
+    assert g["event_counts"][h["end"]] == 2
+    tg.check_semantics(g, tasks, closure=True)
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(programs())
+def test_random_programs_without_fusion_preserve_every_wait(prog):
+    specs, regions, W = prog
+    tasks = tg.generic_tasks(specs, regions)
+    g = tg.canonicalize(tasks, W, fusion=tg.FUSION_OFF)
+    tg.check_semantics(g, tasks, closure=True)
+    P = tg.producer_sets(tasks)
+    fan_in = sum(len(p) for p in P if len(p) >= 2)
+    fan_out = sum(n for n in np.bincount([x for p in P for x in p], minlength=len(tasks)) if n >= 2)
+    assert g["header"]["n_empty"] == fan_in + fan_out
+    assert g["header"]["n_fused"] == sum(len(p) for p in P)
+
+
+def test_tiny_decoder_without_fusion():
+    from dataclasses import replace
+    g, tasks = tg.build(synth.SHAPES["tiny"].cfg(), 1, 16, replace(TINY_PRM, fusion=tg.FUSION_OFF))
+    tg.check_semantics(g, tasks, closure=True)
+    gf, _ = tiny()
+    assert g["header"]["n_empty"] > 10 * gf["header"]["n_empty"]   # no fusion: a wide graph
