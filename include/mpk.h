@@ -103,7 +103,10 @@ typedef struct {
                          /* batch 1: min(8, 2 W / n_kv_heads, pages), the splits; batch > */
                          /* 1: max(B, min(W / n_kv_heads, B pages)), one task per worker) */
   int32_t host_only;     /* 1: build on the host only (no device work); export still works */
-  int32_t fusion_order;  /* must be 0: Def 4.1 then Def 4.2                               */
+  int32_t fusion_order;  /* 0 default: successor-set fusion (Def 4.1) then predecessor-set */
+                         /* fusion (Def 4.2); 1 none: one event per overlap edge, so      */
+                         /* normalisation also rewrites fan-ins (an ablation for small     */
+                         /* graphs: the device holds at most 2^20 events)                 */
   int32_t aot_policy;    /* must be 0: round-robin over workers in linear order           */
   int32_t k_qkv, k_o, k_down; /* k-splits of the q/k/v, O and down projections: tile n   */
                               /* is column tile n / k over k range n % k (ranges on a    */
@@ -207,44 +210,99 @@ typedef struct {
  * KV pages of `page_size` tokens (16, 32 or 64): decomposition into tile
  * tasks, overlap dependencies, Def 4.1 then Def 4.2 event fusion,
  * normalisation, Kahn-BFS linearisation, JIT/AOT classification, round-robin
- * AOT placement (MPK summary page, sections 2 and 4).  Allocates the device
- * graph, its event counters, queues and activation buffers on the current
- * device.  *out receives a library-owned handle (mpk_destroy_tgraph). */
+ * AOT placement (MPK summary page, section 2 Q2 and section 4: Def 4.1,
+ * Def 4.2, "6 minimum checks", design-space table; the graph is built once,
+ * ahead of time).  cfg: host pointer, read only.  Allocates the device graph,
+ * its event counters, queues and activation buffers on the current device
+ * (the only allocation of the library besides tracing and mpk_time_tasks).
+ * *out receives a library-owned handle, released with mpk_destroy_tgraph;
+ * on an error *out is NULL and nothing stays allocated.  Errors:
+ * MPK_ERR_INVALID_ARG (null pointer, inconsistent cfg), MPK_ERR_UNSUPPORTED
+ * (shape the kernels do not handle, device not gfx950), MPK_ERR_HIP,
+ * MPK_ERR_NOMEM. */
 int mpk_build_tgraph(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, mpk_tgraph** out);
 
-/* Same, with explicit build parameters (NULL = defaults). */
+/* Same, with explicit build parameters (host pointer, NULL = every default;
+ * see mpk_build_params).  host_only = 1 builds the graph without touching
+ * the device (for mpk_tgraph_export; mpk_decode_step then fails). */
 int mpk_build_tgraph_ex(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size,
                         const mpk_build_params* params, mpk_tgraph** out);
 
-/* Resolved header of a built graph. */
+/* Resolved header of a built graph: task and event counts, root and end
+ * events, fusion and rewrite counts, and every build parameter with its
+ * default resolved (MPK summary page, section 4 notation: a task's dependent
+ * and triggering events, an event's counts and [first, last]).  out: host
+ * pointer, written.  Errors: MPK_ERR_INVALID_ARG on a null pointer. */
 int mpk_tgraph_info(const mpk_tgraph* g, mpk_tgraph_header* out);
 
-/* Host copies of every index array of the graph (see mpk_tgraph_host_view). */
+/* Host copies of every index array of the linearised graph (see
+ * mpk_tgraph_host_view): what a checker compares against its own
+ * construction of the graph (MPK summary page, section 4, "6 minimum
+ * checks": <= 1 dependent and <= 1 triggering event per task, contiguous
+ * [first, last] fan-out).  The arrays are malloc'ed by the library and owned
+ * by the caller, who frees them with mpk_free_host_view.  Errors:
+ * MPK_ERR_INVALID_ARG, MPK_ERR_NOMEM (nothing is left allocated). */
 int mpk_tgraph_export(const mpk_tgraph* g, mpk_tgraph_host_view* out);
 
 /* Test entry: run the canonicalisation pipeline (overlap edges, fusion,
  * normalisation, linearisation, classification, placement on n_workers) on
- * arbitrary tasks and boxes.  Host only; tasks of type MPK_TASK_ATTN are JIT. */
+ * arbitrary tasks and boxes (MPK summary page, section 2 Q2: an event iff a
+ * producer's output region overlaps a consumer's input region; the author's
+ * comments on the blog post, item 2: the same rule).  Host only; tasks of
+ * type MPK_TASK_ATTN are JIT.  tasks[n_tasks], regions[n_regions]: host
+ * arrays, read only; a region names its task by index, is_out 1 for an
+ * output box.  The view is filled as by mpk_tgraph_export.  Same as
+ * mpk_build_generic_ex with n_workers set and every other field 0.
+ * Errors: MPK_ERR_INVALID_ARG (bad task type, region of a missing task),
+ * MPK_ERR_GRAPH (a cycle), MPK_ERR_NOMEM. */
 int mpk_build_generic(const mpk_task_spec* tasks, int32_t n_tasks, const mpk_region* regions,
                       int32_t n_regions, int32_t n_workers, mpk_tgraph_host_view* out);
 
+/* The same with build parameters (host pointer, required): n_workers,
+ * fusion_order and attn_jit are read (attn_jit 0 and 1: attention tasks JIT,
+ * 2: every task AOT, 3: every non-empty task JIT but the root's consumers);
+ * every other field is ignored.  MPK summary page, section 4: Def 4.1 /
+ * Def 4.2 and the "6 minimum checks" (normalisation, fan-out and fan-in
+ * rewrites; contiguous [first, last] fan-out). */
+int mpk_build_generic_ex(const mpk_task_spec* tasks, int32_t n_tasks, const mpk_region* regions,
+                         int32_t n_regions, const mpk_build_params* params, mpk_tgraph_host_view* out);
+
+/* Free the arrays of a host view filled by mpk_tgraph_export or
+ * mpk_build_generic(_ex) and zero the view; NULL and an already freed
+ * (zeroed) view are accepted. */
 void mpk_free_host_view(mpk_tgraph_host_view* v);
 
-/* One decode step as ONE persistent-kernel launch on `stream` (asynchronous).
- * token_ids[B], seq_lens[B] (tokens already cached; the new token is at
- * position seq_lens[b]) are device int32; logits is device fp32 [B][vocab];
- * next_ids is device int32 [B] (argmax, lowest index on ties).  The step
- * writes the new token's k and v into the cache slot of position seq_lens[b]
- * and does not change seq_lens.  Calls on one graph must be ordered on one
- * stream.  A previous watchdog timeout makes the kernel exit at once; read it
- * with mpk_get_status. */
+/* One decode step as ONE persistent-kernel launch on `stream` (asynchronous):
+ * the whole forward of one new token per request, run by the in-kernel
+ * runtime of workers and schedulers over the graph's events (MPK summary
+ * page, section 3 Fig 1: one launch per step instead of one per operator;
+ * section 2 Q2: workers pop FIFO task queues, schedulers consume event
+ * queues; section 4 Table 1 and design-space table: the hybrid JIT/AOT
+ * policy).  w: host pointer to device weight pointers (caller-owned,
+ * bf16, read only); token_ids[B], seq_lens[B] (tokens already cached; the
+ * new token is at position seq_lens[b]) are device int32; logits is device
+ * fp32 [B][vocab]; next_ids is device int32 [B] (argmax, lowest index on
+ * ties).  The step writes the new token's k and v into the cache slot of
+ * position seq_lens[b] (bf16) and does not change seq_lens.  Calls on one
+ * graph must be ordered on one stream.  When the weight pointers differ from
+ * the last call's, the call first synchronises and uploads the resolved
+ * pointers (the steady state makes no host-device copy).  Errors returned
+ * synchronously: MPK_ERR_INVALID_ARG (null or misaligned pointer, host-only
+ * graph), MPK_ERR_HIP (launch failure).  In-kernel failures (watchdog
+ * timeout, a token id outside the vocabulary, a bad page id or cached
+ * length) are reported by mpk_get_status and poison the graph: later steps
+ * exit at once and leave their outputs unwritten. */
 int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
                     const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream);
 
-/* The same task bodies launched kernel-per-operator in stream order (the
- * barrier baseline): one kernel per operator with one workgroup per task.
- * use_hipgraph = 1 captures the launches once into a hipGraph (re-captured
- * when a pointer changes) and replays it. */
+/* The kernel-per-operator baseline the mega-kernel is measured against
+ * (MPK summary page, section 2 Q1: kernel-per-operator execution with a
+ * barrier at every operator boundary; section 2 Q3: the comparison): the
+ * same task bodies, one kernel per operator with one workgroup per task,
+ * launched in stream order with no events.  Arguments, outputs and errors
+ * are those of mpk_decode_step.  use_hipgraph = 1 captures the launches once
+ * into a hipGraph (re-captured when a pointer changes; the first call
+ * creates a capture stream) and replays it. */
 int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
                              const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream,
                              int32_t use_hipgraph);
@@ -259,7 +317,11 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
  * a request's splits occupy consecutive slots), 7 attn, 8 o (k_o planes), 9 s
  * (residual after attention), 11 a, 12 d (k_down planes); at batch > 1 also 0 e[B][H],
  * 1 hf[B][H], and per layer k = 1 h, 10 h2 (the normalised inputs).
- * Synchronises the device. */
+ * The ids are the tensors of the graph's regions (MPK summary page, section
+ * 2 Q2: events are inferred from the regions tasks read and write), so a
+ * test can check every task's output layer by layer.  Synchronises the
+ * device.  Errors: MPK_ERR_INVALID_ARG (no such library-owned tensor, wrong
+ * size, host-only graph), MPK_ERR_HIP. */
 int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes);
 
 /* Per-task trace of the persistent kernel: times are the GPU's constant-rate
@@ -277,34 +339,60 @@ typedef struct {
                          norms: inputs summed / reduction done */
 } mpk_trace_record;
 
-/* Turn tracing of mpk_decode_step on (1) or off (0).  Allocates (frees) a
- * device buffer of one record per task; each step overwrites it. */
+/* Turn tracing of mpk_decode_step on (1) or off (0): each worker records when
+ * it waited for, started and finished each task, which is what the pages'
+ * per-phase analysis of the persistent kernel needs (MPK summary page,
+ * section 4, "% peak / lower-bound derivation": the gap to the bandwidth
+ * bound is scheduling and synchronisation).  Synchronises; allocates (frees)
+ * a library-owned device buffer of one record per task; each step
+ * overwrites it.  Errors: MPK_ERR_INVALID_ARG (host-only graph), MPK_ERR_HIP. */
 int mpk_set_trace(mpk_tgraph* g, int32_t enable);
 
 /* Copy the records of the last traced step to host memory `out` (room for
  * `capacity` records), grouped by worker in execution order.  *count
- * receives the number written; *ticks_per_us the clock rate.  Synchronises. */
+ * receives the number written; *ticks_per_us the clock rate (may be NULL).
+ * Synchronises.  Errors: MPK_ERR_INVALID_ARG (tracing off, capacity too
+ * small: the first `capacity` records are still written), MPK_ERR_HIP. */
 int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32_t* count, double* ticks_per_us);
 
-/* Body micro-benchmark: runs the listed tasks (linear indices, host array of
- * n) one after another in a single workgroup, each `reps` times, on the
- * arguments and buffers of the last mpk_decode_step call (no events are
- * waited on or advanced), and writes each task's mean duration in clock
- * ticks to ticks[n] (host).  cold = 1 invalidates the device-scope caches of
- * the workgroup's die (an agent-scope acquire) right before each run, as a
- * task started by the persistent kernel sees them.  Synchronises. */
+/* Body micro-benchmark and serial execution: runs the listed tasks (linear
+ * indices, host array of n) one after another in a single workgroup, each
+ * `reps` times, on the arguments and buffers of the last mpk_decode_step
+ * call (no events are waited on or advanced), and writes each task's mean
+ * duration in clock ticks to ticks[n] (host).  cold = 1 invalidates the
+ * device-scope caches of the workgroup's die (an agent-scope acquire) right
+ * before each run, as a task started by the persistent kernel sees them.
+ * The per-task cost the pages analyse (MPK summary page, section 4,
+ * design-space table: task granularity).  Allocates and frees a small
+ * device buffer; synchronises.  Errors: MPK_ERR_INVALID_ARG (no step run
+ * yet, index out of range), MPK_ERR_HIP. */
 int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, int32_t cold, uint64_t* ticks,
                    double* ticks_per_us);
 
-/* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it). */
+/* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it):
+ * every wait of a worker or scheduler gives up after it, reports
+ * MPK_ERR_TIMEOUT and poisons the graph, so the persistent grid always
+ * drains (the runtime's forward-progress guard; the pages' runtime has no
+ * such limit).  Takes effect at the next step.  Errors: MPK_ERR_INVALID_ARG. */
 int mpk_set_watchdog(mpk_tgraph* g, uint64_t timeout_ns);
 
-/* Synchronises the stream of the last step and reports its in-kernel status. */
+/* Synchronises the stream of the last step and reports its in-kernel status
+ * (out: host pointer): MPK_OK, MPK_ERR_TIMEOUT (with the workgroup, task,
+ * event, counter and target of the wait that gave up) or
+ * MPK_ERR_INVALID_ARG (a token id outside the vocabulary or a bad page id or
+ * cached length: counter holds the value, target the bound).  A non-zero
+ * code stays: the graph is poisoned until it is destroyed.  Errors of the
+ * call itself: MPK_ERR_INVALID_ARG, MPK_ERR_HIP. */
 int mpk_get_status(mpk_tgraph* g, mpk_status_word* out);
 
+/* Release a graph and everything the library allocated for it (device
+ * graph, counters, queues, activations, trace, captured baseline graph).
+ * Must not be called while a step on it may still run: synchronise the
+ * step's stream first.  NULL is accepted. */
 void mpk_destroy_tgraph(mpk_tgraph* g);
 
-/* Thread-local message describing the last non-zero status ("" if none). */
+/* Thread-local message describing the last non-zero status returned on the
+ * calling thread ("" if none); valid until the thread's next failing call. */
 const char* mpk_last_error(void);
 
 #ifdef __cplusplus

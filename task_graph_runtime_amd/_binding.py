@@ -93,6 +93,8 @@ SIGNATURES = {
     "mpk_tgraph_export": (C.c_int, [C.c_void_p, C.POINTER(mpk_tgraph_host_view)]),
     "mpk_build_generic": (C.c_int, [C.POINTER(mpk_task_spec), C.c_int32, C.POINTER(mpk_region), C.c_int32,
                                     C.c_int32, C.POINTER(mpk_tgraph_host_view)]),
+    "mpk_build_generic_ex": (C.c_int, [C.POINTER(mpk_task_spec), C.c_int32, C.POINTER(mpk_region), C.c_int32,
+                                       C.POINTER(mpk_build_params), C.POINTER(mpk_tgraph_host_view)]),
     "mpk_free_host_view": (None, [C.POINTER(mpk_tgraph_host_view)]),
     "mpk_decode_step": (C.c_int, [C.c_void_p, C.POINTER(mpk_weights), C.c_void_p, C.POINTER(mpk_kv), C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p]),
@@ -165,7 +167,7 @@ def _view_to_dict(v: mpk_tgraph_host_view) -> dict:
     return out
 
 
-def build_generic(specs, regions, n_workers) -> dict:
+def build_generic(specs, regions, n_workers, fusion_order: int = 0, attn_jit: int = 0) -> dict:
     """Canonicalise arbitrary tasks/boxes in the library (host only)."""
     S = (mpk_task_spec * max(1, len(specs)))(*[mpk_task_spec(*map(int, s)) for s in specs])
     R = (mpk_region * max(1, len(regions)))()
@@ -173,8 +175,10 @@ def build_generic(specs, regions, n_workers) -> dict:
         R[i].task, R[i].is_out, R[i].tensor = int(t), int(is_out), int(tn)
         for k in range(4):
             R[i].lo[k], R[i].hi[k] = int(lo[k]), int(hi[k])
+    p = mpk_build_params()
+    p.n_workers, p.fusion_order, p.attn_jit = int(n_workers), int(fusion_order), int(attn_jit)
     v = mpk_tgraph_host_view()
-    _check(lib().mpk_build_generic(S, len(specs), R, len(regions), int(n_workers), C.byref(v)))
+    _check(lib().mpk_build_generic_ex(S, len(specs), R, len(regions), C.byref(p), C.byref(v)))
     try:
         return _view_to_dict(v)
     finally:

@@ -52,10 +52,15 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   if (c.tied_embedding != 0 && c.tied_embedding != 1) return bad("tied_embedding must be 0 or 1");
   if (c.n_q_heads / c.n_kv_heads > 16) return uns("more than 16 query heads per kv head");
   if (B < 1 || B > 16) return uns("batch must be in 1..16");
+  // the matrix-core tiles (batch > 1) walk the contraction in whole 32-element
+  // steps, and a k-split range starts on a 32-element (128-byte) boundary of
+  // the fp32 activation rows, so both inputs of a projection must be whole
+  // steps (the attention output, hq x d, always is)
+  if (B > 1 && (c.hidden % 32 || c.ffn % 32)) return uns("at batch > 1, hidden and ffn must be multiples of 32");
   if (P != 16 && P != 32 && P != 64) return uns("page_size must be 16, 32 or 64");
   mpk_build_params z = {};
   const mpk_build_params& p = in ? *in : z;
-  if (p.fusion_order != 0) return uns("only fusion order 0 (Def 4.1 then Def 4.2) is implemented");
+  if (p.fusion_order < 0 || p.fusion_order > 1) return uns("fusion_order must be 0 (Def 4.1 then Def 4.2) or 1 (none)");
   if (p.aot_policy != 0) return uns("only AOT policy 0 (round-robin in linear order) is implemented");
   if (p.attn_jit < 0 || p.attn_jit > 3) return bad("attn_jit must be 0, 1, 2 or 3");
   if (p.weight_preload < 0 || p.weight_preload > 2) return bad("weight_preload must be 0, 1 or 2");
@@ -70,6 +75,7 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   r.preload = p.weight_preload != 2;
   if (p.coarse_events < 0 || p.coarse_events > 1) return bad("coarse_events must be 0 or 1");
   r.coarse = p.coarse_events == 1;
+  r.fusion = p.fusion_order;
   // default scheduler count: none when nothing is JIT (every compute unit
   // is a worker), else the largest S <= 16 that divides the worker count, so
   // that every scheduler deals over the same number of workers
@@ -200,7 +206,10 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
       tile_range(H, 32, Kq, ks, &klo, &khi);
       std::vector<Box> outs = {box(t(L_QKV), {ks, 0, g * Sg + lo}, {ks + 1, B, g * Sg + hi})};
       if (fused && n == 0) outs.push_back(full(t(L_R), H));
-      add(MPK_TASK_QKV, l, n, 0, 0, fused ? prev : std::vector<Box>{box(t(L_H), {0, klo}, {B, khi})}, outs);
+      // (coarse: the operator-level graph, where a task waits for the whole
+      // previous operator, so a k-split tile declares its whole input row)
+      add(MPK_TASK_QKV, l, n, 0, 0,
+          fused ? prev : std::vector<Box>{p.coarse ? full(t(L_H), H) : box(t(L_H), {0, klo}, {B, khi})}, outs);
     }
     // attention task (j, g) is slot j of kv group g; the request a slot
     // serves is decided at run time from the sequence lengths, so every task
@@ -211,8 +220,6 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
                                  box(t(L_ATTN), {0, g * G * d}, {B, (g + 1) * G * d}),
                                  box(t(L_KC), {0, 0, g, 0}, {B, maxs, g + 1, d}),
                                  box(t(L_VC), {0, 0, g, 0}, {B, maxs, g + 1, d})};
-        // (coarse: the operator-level graph, where a task waits for the whole
-        // previous operator; only attention's per-group input differs)
         add(MPK_TASK_ATTN, l, s, g, 0,
             {p.coarse ? box(t(L_QKV), {0, 0, 0}, {Kq, B, hkv * Sg})
                       : box(t(L_QKV), {0, 0, g * Sg}, {Kq, B, (g + 1) * Sg})},
@@ -222,7 +229,7 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
       int32_t lo, hi, klo, khi;
       tile_range(H, p.q, p.T_o / Ko, n / Ko, &lo, &hi);
       tile_range(hq * d, 32, Ko, n % Ko, &klo, &khi);
-      add(MPK_TASK_OPROJ, l, n, 0, 0, {box(t(L_ATTN), {0, klo}, {B, khi})},
+      add(MPK_TASK_OPROJ, l, n, 0, 0, {p.coarse ? full(t(L_ATTN), hq * d) : box(t(L_ATTN), {0, klo}, {B, khi})},
           {box(t(L_O), {n % Ko, 0, lo}, {n % Ko + 1, B, hi})});
     }
     const std::vector<Box> mid = {full(t(L_R), H), planes(t(L_O), Ko, H)};
@@ -239,7 +246,7 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
       int32_t lo, hi, klo, khi;
       tile_range(H, p.q, p.T_down / Kd, n / Kd, &lo, &hi);
       tile_range(F, 32, Kd, n % Kd, &klo, &khi);
-      add(MPK_TASK_DOWN, l, n, 0, 0, {box(t(L_A), {0, klo}, {B, khi})},
+      add(MPK_TASK_DOWN, l, n, 0, 0, {p.coarse ? full(t(L_A), F) : box(t(L_A), {0, klo}, {B, khi})},
           {box(t(L_D), {n % Kd, 0, lo}, {n % Kd + 1, B, hi})});
     }
   }
@@ -255,9 +262,10 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
   add(MPK_TASK_ARGMAX, -1, 0, 0, 0, {box(T_PMAX, {0, 0, 0}, {B, p.T_lm, 2})}, {box(T_NEXT, {0}, {B})});
 }
 
-int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, int jit, Graph* out, std::string* err) {
+int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, int jit, int fusion, Graph* out, std::string* err) {
   const int32_t N = (int32_t)tasks.size();
   if (W < 1) { *err = "n_workers must be positive"; return MPK_ERR_INVALID_ARG; }
+  if (fusion != 0 && fusion != 1) { *err = "fusion order must be 0 or 1"; return MPK_ERR_UNSUPPORTED; }
 
   // ---- overlap dependencies: per tensor, every (out box, in box) pair with producer < consumer
   struct Ref { int32_t task; const Box* b; };
@@ -279,46 +287,73 @@ int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, int jit, Graph* o
     v.erase(std::unique(v.begin(), v.end()), v.end());
   }
 
-  // ---- Def 4.1: one event per consumer carrying all of its producers;
-  //      Def 4.2: events with the same producer set merge (consumers unite).
-  std::map<std::vector<int32_t>, std::vector<int32_t>> groups;
-  for (int32_t c = 0; c < N; ++c)
-    if (!P[c].empty()) groups[P[c]].push_back(c);
+  // ---- events.  Fusion A: Def 4.1 (one event per consumer carrying all of
+  //      its producers), then Def 4.2 (events with the same producer set
+  //      merge, consumers unite); pre-ordered by their smallest consumer.
+  //      Fusion off: one event per overlap edge (p, c), pre-ordered by (c, p).
   std::vector<std::vector<int32_t>> ev_in, ev_out;
-  {
+  if (fusion == 0) {
+    std::map<std::vector<int32_t>, std::vector<int32_t>> groups;
+    for (int32_t c = 0; c < N; ++c)
+      if (!P[c].empty()) groups[P[c]].push_back(c);
     std::vector<std::pair<std::vector<int32_t>, std::vector<int32_t>>> fused(groups.begin(), groups.end());
     std::sort(fused.begin(), fused.end(), [](const auto& a, const auto& b) { return a.second[0] < b.second[0]; });
     for (auto& f : fused) { ev_in.push_back(f.first); ev_out.push_back(f.second); }
+  } else {
+    for (int32_t c = 0; c < N; ++c)
+      for (int32_t p : P[c]) { ev_in.push_back({p}); ev_out.push_back({c}); }
   }
   const int32_t n_fused = (int32_t)ev_in.size();
-  std::vector<int32_t> dep(N, -1), trig(N, -1);
-  for (int32_t e = 0; e < n_fused; ++e)
-    for (int32_t c : ev_out[e]) dep[c] = e;
-  std::vector<std::vector<int32_t>> trigs_of(N);
-  for (int32_t e = 0; e < n_fused; ++e)
+  std::vector<std::vector<int32_t>> deps_of(N), trigs_of(N);
+  for (int32_t e = 0; e < n_fused; ++e) {
+    for (int32_t c : ev_out[e]) deps_of[c].push_back(e);
     for (int32_t p : ev_in[e]) trigs_of[p].push_back(e);
+  }
 
-  // ---- normalisation: a task triggering k >= 2 events gets one new event e'
-  //      and k empty tasks, empty i waiting on e' and triggering event i.
-  std::vector<int32_t> ttype(N), tlayer(N), torig(N);
+  // ---- normalisation, task by task in program order: k >= 2 dependent
+  //      events (fan-in, only without fusion) -> a new event e' triggered by
+  //      k empty tasks, empty i waiting on the i-th event; k >= 2 triggering
+  //      events (fan-out) -> a new event e' that k empty tasks wait on, empty
+  //      i triggering the i-th event.  Empties are numbered after the
+  //      originals in the order they are made, coords (i, 0) for fan-out and
+  //      (i, 1) for fan-in.
+  std::vector<int32_t> ttype(N), tlayer(N), torig(N), dep(N, -1), trig(N, -1);
   std::vector<std::array<int32_t, 3>> tcoords(N);
   for (int32_t i = 0; i < N; ++i) {
     ttype[i] = tasks[i].type; tlayer[i] = tasks[i].layer; torig[i] = i;
     tcoords[i] = {tasks[i].c[0], tasks[i].c[1], tasks[i].c[2]};
   }
   int32_t n_empty = 0;
+  auto new_empty = [&](int32_t t, int32_t i, int32_t kind) {
+    const int32_t T = (int32_t)ttype.size();
+    ttype.push_back(MPK_TASK_EMPTY); tlayer.push_back(tlayer[t]);
+    tcoords.push_back({i, kind, 0}); torig.push_back(-1 - n_empty);
+    dep.push_back(-1); trig.push_back(-1);
+    ++n_empty;
+    return T;
+  };
   for (int32_t t = 0; t < N; ++t) {
-    const auto& tr = trigs_of[t];
+    const std::vector<int32_t> dl = deps_of[t];
+    if (dl.size() >= 2) {
+      const int32_t ep = (int32_t)ev_in.size();
+      ev_in.push_back({}); ev_out.push_back({t});
+      for (size_t i = 0; i < dl.size(); ++i) {
+        const int32_t T = new_empty(t, (int32_t)i, 1);
+        dep[T] = dl[i]; trig[T] = ep;
+        ev_in[ep].push_back(T);
+        for (int32_t& x : ev_out[dl[i]]) if (x == t) x = T;
+      }
+      dep[t] = ep;
+    } else if (dl.size() == 1) {
+      dep[t] = dl[0];
+    }
+    const std::vector<int32_t> tr = trigs_of[t];
     if (tr.size() >= 2) {
-      int32_t ep = (int32_t)ev_in.size();
-      ev_in.push_back({t});
-      ev_out.push_back({});
+      const int32_t ep = (int32_t)ev_in.size();
+      ev_in.push_back({t}); ev_out.push_back({});
       for (size_t i = 0; i < tr.size(); ++i) {
-        int32_t T = (int32_t)ttype.size();
-        ttype.push_back(MPK_TASK_EMPTY); tlayer.push_back(tlayer[t]);
-        tcoords.push_back({(int32_t)i, 0, 0}); torig.push_back(-1 - n_empty);
-        ++n_empty;
-        dep.push_back(ep); trig.push_back(tr[i]);
+        const int32_t T = new_empty(t, (int32_t)i, 0);
+        dep[T] = ep; trig[T] = tr[i];
         ev_out[ep].push_back(T);
         for (int32_t& x : ev_in[tr[i]]) if (x == t) x = T;
       }

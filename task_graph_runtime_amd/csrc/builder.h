@@ -38,6 +38,7 @@ struct Params {
   bool jit_all = false;   // every non-empty task JIT (scheduling ablation)
   bool preload = true;    // weight pre-load of the next AOT projection tile
   bool coarse = false;    // operator-level graph: attention waits for all q/k/v tiles
+  int32_t fusion = 0;     // 0: Def 4.1 then Def 4.2; 1: none (one event per overlap edge)
   int32_t K_qkv = 1, K_o = 1, K_down = 1;   // k-splits (batch > 1)
 };
 
@@ -88,7 +89,9 @@ inline bool fused_norm(int32_t B) { return B == 1; }
 void decompose(const mpk_model_cfg& cfg, int32_t B, const Params& p, std::vector<TaskDef>* tasks);
 
 // Canonicalisation pipeline on arbitrary tasks; MPK_ERR_GRAPH on a cycle.
-// jit: 0 every non-empty task AOT, 1 attention JIT, 2 every non-empty task JIT
-int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, int jit, Graph* g, std::string* err);
+// jit: 0 every non-empty task AOT, 1 attention JIT, 2 every non-empty task JIT;
+// fusion: 0 Def 4.1 then Def 4.2, 1 none (one event per overlap edge, so
+// normalisation rewrites fan-ins as well as fan-outs)
+int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, int jit, int fusion, Graph* g, std::string* err);
 
 }  // namespace mpk

@@ -174,14 +174,26 @@ void fill_descriptors(mpk_tgraph* t) {
   }
 }
 
-// The runtime resolves empty tasks inline one level deep: an event with empty
-// consumers has only empty consumers, whose own events have none.
+// The runtime resolves empty tasks inline, at most two levels deep (a graph
+// built without fusion chains a fan-out empty into a fan-in empty): an event
+// with empty consumers has only empty consumers, and an empty task's event
+// with empty consumers hands those to empties whose own events have none.
 int check_runtime_shape(const Graph& g) {
+  auto only_empty = [&](int32_t e) {
+    for (int32_t t = g.event_first[e]; t <= g.event_last[e]; ++t)
+      if (g.task_type[t] != MPK_TASK_EMPTY) return false;
+    return true;
+  };
   for (int32_t e = 0; e < g.NE; ++e) {
     if (!(g.event_flags[e] & MPK_EVENT_HAS_EMPTY)) continue;
+    if (!only_empty(e)) return fail(MPK_ERR_GRAPH, "event mixes empty and real consumers");
     for (int32_t t = g.event_first[e]; t <= g.event_last[e]; ++t) {
-      if (g.task_type[t] != MPK_TASK_EMPTY) return fail(MPK_ERR_GRAPH, "event mixes empty and real consumers");
-      if (g.event_flags[g.task_trig[t]] & MPK_EVENT_HAS_EMPTY) return fail(MPK_ERR_GRAPH, "chained empty tasks");
+      const int32_t f = g.task_trig[t];
+      if (!(g.event_flags[f] & MPK_EVENT_HAS_EMPTY)) continue;
+      if (!only_empty(f)) return fail(MPK_ERR_GRAPH, "event mixes empty and real consumers");
+      for (int32_t t2 = g.event_first[f]; t2 <= g.event_last[f]; ++t2)
+        if (g.event_flags[g.task_trig[t2]] & MPK_EVENT_HAS_EMPTY)
+          return fail(MPK_ERR_GRAPH, "empty tasks chained more than two deep");
     }
   }
   return MPK_OK;
@@ -594,10 +606,11 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   r.weight_preload = prm.preload ? 1 : 2;
   r.coarse_events = prm.coarse ? 1 : 0;
   r.k_qkv = prm.K_qkv; r.k_o = prm.K_o; r.k_down = prm.K_down;
+  r.fusion_order = prm.fusion;
   t->resolved = r;
   std::vector<TaskDef> tasks;
   decompose(*cfg, batch, prm, &tasks);
-  rc = canonicalize(tasks, prm.W, prm.jit_all ? 2 : prm.jit_attn ? 1 : 0, &t->g, &err);
+  rc = canonicalize(tasks, prm.W, prm.jit_all ? 2 : prm.jit_attn ? 1 : 0, prm.fusion, &t->g, &err);
   if (rc) { free_tgraph(t); return fail(rc, err); }
   rc = check_runtime_shape(t->g);
   if (rc) { free_tgraph(t); return rc; }
@@ -635,10 +648,13 @@ int mpk_tgraph_export(const mpk_tgraph* g, mpk_tgraph_host_view* out) {
   return export_graph(g->g, make_header(g), out);
 }
 
-int mpk_build_generic(const mpk_task_spec* specs, int32_t n_tasks, const mpk_region* regions, int32_t n_regions,
-                      int32_t n_workers, mpk_tgraph_host_view* out) {
-  if (!out || n_tasks < 0 || n_regions < 0 || (n_tasks && !specs) || (n_regions && !regions))
+int mpk_build_generic_ex(const mpk_task_spec* specs, int32_t n_tasks, const mpk_region* regions, int32_t n_regions,
+                         const mpk_build_params* params, mpk_tgraph_host_view* out) {
+  if (!out || !params || n_tasks < 0 || n_regions < 0 || (n_tasks && !specs) || (n_regions && !regions))
     return fail(MPK_ERR_INVALID_ARG, "bad argument");
+  const int32_t jit = params->attn_jit == 0 || params->attn_jit == 1 ? 1 : params->attn_jit == 2 ? 0
+                      : params->attn_jit == 3 ? 2 : -1;
+  if (jit < 0) return fail(MPK_ERR_INVALID_ARG, "attn_jit must be 0, 1, 2 or 3");
   std::vector<TaskDef> tasks(n_tasks);
   for (int32_t i = 0; i < n_tasks; ++i) {
     if (specs[i].type < 0 || specs[i].type >= MPK_TASK_EMPTY) return fail(MPK_ERR_INVALID_ARG, "bad task type");
@@ -655,13 +671,23 @@ int mpk_build_generic(const mpk_task_spec* specs, int32_t n_tasks, const mpk_reg
   }
   Graph g;
   std::string err;
-  int rc = canonicalize(tasks, n_workers, 1, &g, &err);
+  int rc = canonicalize(tasks, params->n_workers, jit, params->fusion_order, &g, &err);
   if (rc) return fail(rc, err);
   mpk_tgraph_header h{};
   h.n_tasks = g.NT; h.n_events = g.NE; h.root = g.root; h.end = g.end; h.n_fused = g.n_fused;
   h.n_empty = g.n_empty; h.n_rewrites = g.n_rewrites; h.n_aot = (int32_t)g.aot_tasks.size();
-  h.params.n_workers = n_workers; h.params.host_only = 1; h.params.attn_jit = 1;
+  h.params = *params;
+  h.params.host_only = 1;
+  h.params.attn_jit = jit == 1 ? 1 : jit == 0 ? 2 : 3;
   return export_graph(g, h, out);
+}
+
+int mpk_build_generic(const mpk_task_spec* specs, int32_t n_tasks, const mpk_region* regions, int32_t n_regions,
+                      int32_t n_workers, mpk_tgraph_host_view* out) {
+  mpk_build_params p{};
+  p.n_workers = n_workers;
+  p.attn_jit = 1;
+  return mpk_build_generic_ex(specs, n_tasks, regions, n_regions, &p, out);
 }
 
 void mpk_free_host_view(mpk_tgraph_host_view* v) {

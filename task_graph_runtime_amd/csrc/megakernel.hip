@@ -88,14 +88,33 @@ __device__ __forceinline__ bool arrive(const KArgs& a, uint32_t epoch, int e, co
   return o + 1u == ev.counts * epoch;
 }
 
+// The arrival of empty task t (linear index) at its triggering event; when
+// that fires the event, its JIT consumers are handed to the schedulers.
+// True when the arrival fired an event that has empty consumers, whose
+// record is then in *fe_out.
+__device__ __forceinline__ bool arrive_empty(const KArgs& a, uint32_t epoch, int t, int* f_out, DevEvent* fe_out) {
+  const int f = a.tasks[t].trig;
+  const DevEvent fe = a.events[f];
+  const uint32_t qf = (fe.flags & kEvTwoLevel) ? a.ev_quota[(int64_t)f * kEvSub + (t & (kEvSub - 1))] : 0u;
+  if (!arrive(a, epoch, f, fe, t, qf)) return false;
+  if (fe.flags & MPK_EVENT_HAS_JIT)
+    for (int c = 0; c < jit_chunks(a, fe); ++c) push_chunk(a, f, fe, c);
+  *f_out = f;
+  *fe_out = fe;
+  return (fe.flags & MPK_EVENT_HAS_EMPTY) != 0;
+}
+
 // One trigger of event e by task `task`, run by wavefront 0 of a workgroup
 // whose stores for the trigger are complete (every wavefront waited for them
 // before a barrier); q: its sub-counter quota (arrive).  Lane 0 arrives; if
 // that fires the event, its empty consumers are resolved here, one lane each
 // (each empty task arrives at its own event), and the fired events with JIT
-// consumers are handed to the schedulers.  No cache maintenance is needed:
-// the data the events guard is accessed agent-coherently (see tasks.h), the
-// counters atomically.
+// consumers are handed to the schedulers.  An empty task whose arrival fires
+// an event with empty consumers of its own (a graph built without fusion:
+// fan-out empties feeding fan-in empties) resolves those in the same lane,
+// one after another; the host admits no deeper chain.  No cache maintenance
+// is needed: the data the events guard is accessed agent-coherently (see
+// tasks.h), the counters atomically.
 __device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e, const DevEvent& ev, int task,
                                         uint32_t q) {
   const int lane = threadIdx.x & 63;
@@ -105,12 +124,12 @@ __device__ __forceinline__ void trigger(const KArgs& a, uint32_t epoch, int e, c
   if (ev.flags & MPK_EVENT_HAS_EMPTY) {
     for (int t0 = ev.first; t0 <= ev.last; t0 += 64) {
       const int t = t0 + lane;
-      if (t <= ev.last) {
-        const int f = a.tasks[t].trig;
-        const DevEvent fe = a.events[f];
-        const uint32_t qf = (fe.flags & kEvTwoLevel) ? a.ev_quota[(int64_t)f * kEvSub + (t & (kEvSub - 1))] : 0u;
-        if (arrive(a, epoch, f, fe, t, qf) && (fe.flags & MPK_EVENT_HAS_JIT))
-          for (int c = 0; c < jit_chunks(a, fe); ++c) push_chunk(a, f, fe, c);
+      int f;
+      DevEvent fe;
+      if (t <= ev.last && arrive_empty(a, epoch, t, &f, &fe)) {
+        int f2;
+        DevEvent fe2;
+        for (int t2 = fe.first; t2 <= fe.last; ++t2) (void)arrive_empty(a, epoch, t2, &f2, &fe2);
       }
     }
   }

@@ -31,7 +31,7 @@ def both(shape, B, W, q=None, S=None, **over):
     from the library's header)."""
     s = shape
     names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm", K_qkv="k_qkv", K_o="k_o",
-                 K_down="k_down", coarse="coarse_events")
+                 K_down="k_down", coarse="coarse_events", fusion="fusion_order")
     params = dict(n_workers=W, s_attn=S or max(4, B), attn_jit=over.pop("attn_jit", 0))
     if q is not None:
         params["quantum"] = q
@@ -42,7 +42,7 @@ def both(shape, B, W, q=None, S=None, **over):
     prm = tg.Params(W=p["n_workers"], S_sched=p["n_sched_waves"], q=p["quantum"], T_qkv=p["t_qkv"], T_o=p["t_o"],
                     T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"],
                     jit_attn=p["attn_jit"] == 1, jit_all=p["attn_jit"] == 3, K_qkv=p["k_qkv"], K_o=p["k_o"],
-                    K_down=p["k_down"], coarse=p["coarse_events"] == 1)
+                    K_down=p["k_down"], coarse=p["coarse_events"] == 1, fusion=p["fusion_order"])
     ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
     got = g.export()
     got["params"] = p
@@ -104,16 +104,28 @@ def test_all_jit_policy():
 
 @pytest.mark.parametrize("B", [1, 3])
 def test_coarse_operator_level_graph(B):
-    """coarse_events = 1: every attention split waits for every q/k/v tile of
-    its layer (the operator-level graph), so the per-group attention events
-    merge into one."""
+    """coarse_events = 1, the operator-level graph: every task waits for the
+    whole previous operator, so all tiles of one operator (one layer and task
+    type) share one dependent event -- also the k-split O and down tiles at
+    batch > 1, which the fine graph lets wait for their own k-range only."""
     s = synth.SHAPES["tiny"]
     ref, got, tasks = both(s, B, 13, S=4, coarse=1)
     assert_same(ref, got)
     tg.check_semantics(got, tasks, closure=True)
     _, fine, _ = both(s, B, 13, S=4)
+    if B > 1:
+        assert got["params"]["k_o"] == 3 and got["params"]["k_down"] == 3
+
+    def deps(g, ty):
+        real = g["task_type"] == ty
+        return {(int(l), int(d)) for l, d in zip(g["task_layer"][real], g["task_dep"][real])}
+    for ty in (tg.QKV, tg.ATTN, tg.OPROJ, tg.GATEUP, tg.DOWN, tg.LMHEAD):
+        d = deps(got, ty)
+        assert len(d) == len({l for l, _ in d}), tg.TYPE_NAMES[ty]   # one event per operator
     att = lambda g: set(g["task_dep"][g["task_type"] == tg.ATTN].tolist())
     assert len(att(got)) == s.n_layers and len(att(fine)) == s.n_layers * s.n_kv_heads
+    if B > 1:   # fine: the O and down tiles wait per k-range
+        assert len(deps(fine, tg.OPROJ)) == 3 * s.n_layers and len(deps(fine, tg.DOWN)) == 3 * s.n_layers
 
 
 def test_weight_preload_switch():
@@ -192,6 +204,30 @@ def test_generic_entry_matches_spec(prog):
     assert_same(ref, got)
 
 
+@settings(max_examples=120, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(programs())
+def test_generic_entry_without_fusion_matches_spec(prog):
+    """The fan-in rewrite (no fusion) in the C++ builder against the spec, on
+    random programs with misaligned tilings."""
+    specs, regions, W = prog
+    tasks = tg.generic_tasks(specs, regions)
+    ref = tg.canonicalize(tasks, W, fusion=tg.FUSION_OFF)
+    got = mpk.build_generic(specs, regions, W, fusion_order=1)
+    assert_same(ref, got)
+
+
+@pytest.mark.parametrize("B,attn_jit", [(1, 0), (1, 1), (3, 0), (3, 3)])
+def test_decoder_without_fusion_bit_exact(B, attn_jit):
+    s = synth.SHAPES["tiny"]
+    ref, got, tasks = both(s, B, 8, q=64 if B == 1 else 16, S=4, T_qkv=8, T_o=4 if B == 1 else 6, T_gu=11,
+                           T_down=4 if B == 1 else 6, T_lm=16, attn_jit=attn_jit, fusion=1)
+    assert_same(ref, got)
+    assert got["params"]["fusion_order"] == 1
+    tg.check_semantics(got, tasks, closure=True)
+    # the fan-in rewrite is in use: empties waiting on an event that another empty did not fire
+    assert np.any(got["task_coords"][got["task_type"] == tg.EMPTY][:, 1] == 1)
+
+
 # ------------------------------------------------------------------ C ABI surface
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "mpk.h")).read()
@@ -220,7 +256,7 @@ def test_bad_config_rejected(over, code):
 
 @pytest.mark.parametrize("B,P,params,code", [
     (0, 16, {}, -2), (17, 16, {}, -2), (1, 24, {}, -2), (1, 16, dict(t_qkv=3), -1),
-    (1, 16, dict(fusion_order=1), -2), (1, 16, dict(t_o=100000), -1)])
+    (1, 16, dict(fusion_order=2), -2), (1, 16, dict(t_o=100000), -1)])
 def test_bad_build_args_rejected(B, P, params, code):
     with pytest.raises(mpk.MpkError) as e:
         mpk.TGraph(synth.SHAPES["tiny"].cfg(), B, P, params, host_only=True)
@@ -237,3 +273,21 @@ def test_host_only_graph_refuses_to_run():
 def test_generic_entry_rejects_bad_regions():
     with pytest.raises(mpk.MpkError):
         mpk.build_generic([(2, 0, 0, 0, 0)], [(5, 1, 0, (0, 0, 0, 0), (1, 1, 1, 1))], 1)
+
+
+@pytest.mark.parametrize("over", [dict(hidden=264), dict(ffn=712), dict(hidden=264, ffn=712), dict(hidden=280)])
+def test_partial_k_step_shapes_refused_above_batch_one(over):
+    """Batch > 1 runs the projections on the matrix cores in whole 32-element
+    contraction steps, with k-split ranges on 128-byte boundaries of the fp32
+    rows: a hidden or ffn size that is a multiple of 8 but not of 32 is refused
+    there (MPK_ERR_UNSUPPORTED) and still accepted at batch 1, whose tiles take
+    the contraction 8 elements per lane."""
+    c = mpk.model_cfg(synth.SHAPES["tiny"].cfg())
+    for k, v in over.items():
+        setattr(c, k, v)
+    for B in (2, 3, 16):
+        with pytest.raises(mpk.MpkError) as e:
+            mpk.TGraph(c, B, 16, {}, host_only=True)
+        assert e.value.code == -2 and "multiples of 32" in str(e.value)
+    g = mpk.TGraph(c, 1, 16, {}, host_only=True)
+    assert g.header()["n_tasks"] > 0
