@@ -369,6 +369,22 @@ int mpk_read_trace(mpk_tgraph* g, mpk_trace_record* out, int32_t capacity, int32
 int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps, int32_t cold, uint64_t* ticks,
                    double* ticks_per_us);
 
+/* Serial execution, the check that the graph's regions are complete: with
+ * poison = 1 every library-owned activation is first filled with all-ones
+ * bytes (NaN in fp32), then the listed tasks (linear indices, host array of
+ * n) run once each, one after another, in a single workgroup on the
+ * arguments of the last mpk_decode_step call, with no events.  Run in a
+ * topological order of the graph that prefers the ready task latest in
+ * program order, a task executes before every task it does not declare as
+ * a producer, so a region missing from a task's declared inputs leaves it
+ * reading NaN (MPK summary page, section 2 Q2 and section 4 check 1: an
+ * event iff a producer's output region overlaps a consumer's input region,
+ * and no producer-consumer wait may be lost).  Empty tasks in the list do
+ * nothing.  Writes the last step's outputs and KV slots.  Synchronises.
+ * Errors: MPK_ERR_INVALID_ARG (no step run yet, index out of range),
+ * MPK_ERR_HIP. */
+int mpk_run_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t poison);
+
 /* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it):
  * every wait of a worker or scheduler gives up after it, reports
  * MPK_ERR_TIMEOUT and poisons the graph, so the persistent grid always

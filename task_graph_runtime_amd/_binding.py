@@ -107,6 +107,7 @@ SIGNATURES = {
                                  C.POINTER(C.c_double)]),
     "mpk_time_tasks": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_uint64),
                                  C.POINTER(C.c_double)]),
+    "mpk_run_tasks": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32), C.c_int32, C.c_int32]),
     "mpk_get_status": (C.c_int, [C.c_void_p, C.POINTER(mpk_status_word)]),
     "mpk_destroy_tgraph": (None, [C.c_void_p]),
     "mpk_last_error": (C.c_char_p, []),
@@ -295,6 +296,13 @@ class TGraph:
         tpu = C.c_double()
         _check(lib().mpk_time_tasks(self.h, T, n, int(reps), int(bool(cold)), out, C.byref(tpu)))
         return np.array(list(out), dtype=np.float64) / tpu.value
+
+    def run_tasks(self, tasks, poison: bool = True):
+        """Run the listed tasks serially in one workgroup (mpk_run_tasks),
+        after filling every library-owned activation with NaN when poison."""
+        n = len(tasks)
+        T = (C.c_int32 * n)(*[int(t) for t in tasks])
+        _check(lib().mpk_run_tasks(self.h, T, n, int(bool(poison))))
 
     def set_watchdog(self, ns: int):
         _check(lib().mpk_set_watchdog(self.h, int(ns)))

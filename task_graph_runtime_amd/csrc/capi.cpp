@@ -87,6 +87,7 @@ struct mpk_tgraph {
   uint32_t sched_cap = 0, jit_cap = 0;
 
   void* d_act = nullptr;
+  int64_t act_bytes = 0;
   KArgs base{};             // arguments that do not change between steps
   KArgs last{};             // arguments of the last step (kernel arguments are passed by value)
   bool args_valid = false;
@@ -411,6 +412,7 @@ int upload(mpk_tgraph* t) {
   }
   HIPCHK(hipMalloc(&t->d_act, off));
   HIPCHK(hipMemset(t->d_act, 0, off));
+  t->act_bytes = off;
   char* ab = (char*)t->d_act;
   auto shared = [&](int id) { return shared_off[id] < 0 ? nullptr : (float*)(ab + shared_off[id]); };
   auto kind = [&](int k) { return kind_off[k] < 0 ? nullptr : (float*)(ab + kind_off[k]); };
@@ -857,6 +859,27 @@ int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps,
   (void)hipFree(buf);
   if (e != hipSuccess) return hip_fail(e, "mpk_time_tasks");
   if (ticks_per_us) *ticks_per_us = g->wall_khz / 1000.0;
+  return MPK_OK;
+}
+
+int mpk_run_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t poison) {
+  if (!g || !tasks || n < 1) return fail(MPK_ERR_INVALID_ARG, "bad argument");
+  if (g->host_only || !g->args_valid) return fail(MPK_ERR_INVALID_ARG, "run mpk_decode_step on this graph first");
+  for (int32_t i = 0; i < n; ++i)
+    if (tasks[i] < 0 || tasks[i] >= g->g.NT) return fail(MPK_ERR_INVALID_ARG, "task index out of range");
+  HIPCHK(hipDeviceSynchronize());
+  // all-ones bytes: every fp32 activation reads as a NaN, every partial
+  // argmax as (NaN, -1)
+  if (poison) HIPCHK(hipMemset(g->d_act, 0xFF, (size_t)g->act_bytes));
+  HIPCHK(hipMemset(g->d_arrive, 0, (size_t)g->arrive_bytes));
+  void* buf = nullptr;
+  HIPCHK(hipMalloc(&buf, 8));
+  hipError_t e = hipSuccess;
+  for (int32_t i = 0; i < n && e == hipSuccess; ++i)
+    e = launch_time_task(g->last, tasks[i], false, (unsigned long long*)buf, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  (void)hipFree(buf);
+  if (e != hipSuccess) return hip_fail(e, "mpk_run_tasks");
   return MPK_OK;
 }
 

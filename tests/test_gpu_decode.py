@@ -365,3 +365,151 @@ def test_trace_happens_before_every_wait():
         for p in real_producers(int(ex["task_dep"][c])):
             assert end[p] <= start[c], (p, c)
     r.g.set_trace(False)
+
+
+# ------------------------------------------------------------------ region completeness
+def reverse_priority_order(ex):
+    """A topological order of the built graph that always runs, among the
+    ready tasks, the one latest in program order (empty tasks resolve at
+    once).  A task then runs before every task it does not wait for through
+    the graph, so if its declared inputs miss a region some earlier task
+    writes, it runs before that writer and reads the poison."""
+    import heapq
+    dep, trig, cnt = ex["task_dep"], ex["task_trig"], ex["event_counts"]
+    first, last, orig, tt = ex["event_first"], ex["event_last"], ex["task_orig"], ex["task_type"]
+    arrived = np.zeros(len(cnt), np.int64)
+    heap, order = [], []
+
+    def fire(e):
+        for t in range(int(first[e]), int(last[e]) + 1):
+            if tt[t] == mpk._binding.TASK_EMPTY:
+                arrive(int(trig[t]))
+            else:
+                heapq.heappush(heap, (-int(orig[t]), t))
+
+    def arrive(e):
+        arrived[e] += 1
+        if arrived[e] == cnt[e]:
+            fire(e)
+    fire(int(ex["header"]["root"]))
+    while heap:
+        _, t = heapq.heappop(heap)
+        order.append(t)
+        arrive(int(trig[t]))
+    assert len(order) == int(np.sum(tt != mpk._binding.TASK_EMPTY))
+    return order
+
+
+@pytest.mark.parametrize("B,params", [(1, {}), (3, {}), (3, dict(k_qkv=3, k_o=2, k_down=4)),
+                                      (2, dict(attn_jit=1))])
+def test_regions_complete_serial_poisoned(B, params):
+    """Every region a task reads is declared: with all activations NaN, the
+    tasks run one at a time in the reverse-priority order above and the step
+    still matches the oracle (a missing region would be read before its
+    writer ran)."""
+    s = TINY.with_(batch=B, ctx_range=(3, 120), ctx=0)
+    say("regions complete", B, params)
+    inp = device_inputs(s, seed=61 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    r = Runner(inp, params)
+    r.run("mega")                       # sets the step's arguments
+    order = reverse_priority_order(r.g.export())
+    r.logits.fill_(float("nan"))
+    r.next.fill_(-1)
+    r.g.run_tasks(order, poison=True)
+    torch.cuda.synchronize()
+    check(r.logits.cpu().numpy(), r.next.cpu().numpy(), ref, ref_next)
+    check_cache(inp, cap)
+
+
+def test_serial_order_catches_a_missing_region():
+    """The check above is not vacuous: the same serial run in the order that
+    puts the O-projection tiles of layer 0 ahead of the attention splits they
+    read (as a graph missing those regions would allow) produces NaN."""
+    inp = device_inputs(TINY, seed=3)
+    r = Runner(inp)
+    r.run("mega")
+    ex = r.g.export()
+    order = reverse_priority_order(ex)
+    tt, layer = ex["task_type"], ex["task_layer"]
+    o0 = [t for t in order if tt[t] == mpk._binding.TASK_OPROJ and layer[t] == 0]
+    a0 = [t for t in order if tt[t] == mpk._binding.TASK_ATTN and layer[t] == 0]
+    rest = [t for t in order if t not in o0]
+    k = rest.index(a0[0])
+    r.g.run_tasks(rest[:k] + o0 + rest[k:], poison=True)
+    torch.cuda.synchronize()
+    assert np.isnan(r.logits.cpu().numpy()).all()
+
+
+# ------------------------------------------------------------------ shapes off the beaten path
+@pytest.mark.parametrize("B", [1, 3])
+def test_tiny_head_dim_64_with_qk_norm(B):
+    s = TINY.with_(qk_norm=True, batch=B, ctx_range=(3, 200), ctx=0)
+    say("tiny d=64 qk_norm", B)
+    inp = device_inputs(s, seed=71 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    for mode in ("mega", "base"):
+        logits, nxt = Runner(inp).run(mode)
+        check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+
+
+@pytest.mark.parametrize("B,H,F", [(1, 264, 712), (1, 520, 1000), (3, 288, 352), (5, 320, 416)])
+def test_odd_widths(B, H, F):
+    """Widths that are not multiples of the tile and k-step quanta: at batch 1
+    multiples of 8 only (partial 512-element segments), above it multiples of
+    32 but not 64 or 128 (odd k-step counts, uneven k-split ranges)."""
+    s = TINY.with_(hidden=H, ffn=F, batch=B, ctx_range=(3, 150), ctx=0)
+    say("odd widths", B, H, F)
+    inp = device_inputs(s, seed=81 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    for mode in ("mega", "base"):
+        logits, nxt = Runner(inp).run(mode)
+        check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_batch16_alternating_inputs():
+    """Four steps of the 8B batch-16 graph alternating two token sets, each
+    step against its own oracle: the matrix-core tiles read task-to-task
+    inputs through the L2, so nothing of the previous step may survive there."""
+    s = synth.SHAPES["qwen3_8b_b16"]
+    say("8B b16 alternating", "generate")
+    inp = device_inputs(s, seed=5)
+    ids = [inp["token_ids"].clone(), (inp["token_ids"] * 7 + 13) % s.vocab]
+    refs = []
+    for k, t in enumerate(ids):
+        say("8B b16 alternating", "oracle", k)
+        inp["token_ids"] = t
+        refs.append(run_oracle(inp, lazy=True, widen_on_device=True))
+    r = Runner(inp)
+    for i, k in enumerate([0, 1, 0, 1]):
+        say("8B b16 alternating", "step", i, "tokens", k)
+        r.inp["token_ids_dev"].copy_(ids[k].to(r.inp["token_ids_dev"].dtype).cuda())
+        logits, nxt = r.run("mega")
+        check(logits, nxt, *refs[k])
+    del r
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,attn_jit", [(1, 0), (1, 1), (3, 0), (3, 1)])
+def test_tiny_without_fusion(B, attn_jit):
+    """The graph built without event fusion (one event per overlap edge,
+    fan-in and fan-out rewrites, empty tasks two deep) runs to the same
+    result; with attention JIT the fan-in events hand their splits over."""
+    s = TINY.with_(batch=B, ctx_range=(3, 120), ctx=0)
+    say("tiny no fusion", B, attn_jit)
+    inp = device_inputs(s, seed=91 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    params = dict(n_workers=8, quantum=64 if B == 1 else 16, t_qkv=8, t_o=4, t_gu=11, t_down=4, t_lm=16, s_attn=4,
+                  fusion_order=1, attn_jit=attn_jit)
+    r = Runner(inp, params)
+    assert r.g.header()["params"]["fusion_order"] == 1
+    logits, nxt = r.run("mega")
+    check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
