@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--baseline-steps", type=int, default=20)
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--params", default="{}",
+                    help="build parameters (JSON object of mpk_build_params fields, e.g. '{\"s_attn\": 16}') for "
+                         "the ablations; the default build is the one measured")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the step, run a plain device copy of this many MiB three times (a known-size "
                          "kernel for scaling the HBM byte counters of a profiler run)")
@@ -138,7 +141,7 @@ def main():
     kv = inp["kv"]
     ids = inp["token_ids"].cuda()
     lens = inp["seq_lens"].cuda()
-    g = mpk.TGraph(s.cfg(), s.batch, s.page_size)
+    g = mpk.TGraph(s.cfg(), s.batch, s.page_size, json.loads(args.params))
     W = mpk.Weights(inp["weights"])
     KV = mpk.KV(kv["k_pool"], kv["v_pool"], kv["page_table"].cuda())
     logits = torch.empty((s.batch, s.vocab), device="cuda", dtype=torch.float32)

@@ -100,8 +100,9 @@ typedef struct {
   int32_t t_qkv, t_o, t_gu, t_down, t_lm; /* tiles per projection (default ~W; t_qkv a
                                              multiple of n_kv_heads)                    */
   int32_t s_attn;        /* attention slots per kv group, at least the batch (default:   */
-                         /* batch 1: min(8, 2 W / n_kv_heads, pages), the splits; batch > */
-                         /* 1: max(B, min(W / n_kv_heads, B pages)), one task per worker) */
+                         /* batch 1: min(W / n_kv_heads, pages); batch > 1: max(B,       */
+                         /* min(W / n_kv_heads, B pages)): one attention task per worker; */
+                         /* the step deals them to the requests by page count)            */
   int32_t host_only;     /* 1: build on the host only (no device work); export still works */
   int32_t fusion_order;  /* 0 default: successor-set fusion (Def 4.1) then predecessor-set */
                          /* fusion (Def 4.2); 1 none: one event per overlap edge, so      */
@@ -129,6 +130,11 @@ typedef struct {
                           /* an attention split waits for every q/k/v tile, not only its */
                           /* own kv group's (every other operator already waits for the  */
                           /* whole previous one) -- the pages' coarse-graph ablation     */
+  int32_t attn_split_pages; /* at least this many KV pages per attention split when the   */
+                            /* step runs (default 1): a request of p pages takes          */
+                            /* min(slots, ceil(p / this)) splits at batch 1 (and no more  */
+                            /* than the split combine can stage in LDS), and the split    */
+                            /* size of a batch never drops below it                       */
 } mpk_build_params;
 
 typedef struct mpk_tgraph mpk_tgraph; /* opaque; owned by the library */

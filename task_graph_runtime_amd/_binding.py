@@ -36,7 +36,7 @@ class mpk_model_cfg(C.Structure):
 class mpk_build_params(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_workers", "n_sched_waves", "quantum", "t_qkv", "t_o", "t_gu", "t_down",
                                          "t_lm", "s_attn", "host_only", "fusion_order", "aot_policy", "k_qkv", "k_o", "k_down",
-                                         "attn_jit", "weight_preload", "coarse_events")]
+                                         "attn_jit", "weight_preload", "coarse_events", "attn_split_pages")]
 
 
 class mpk_weights(C.Structure):

@@ -76,6 +76,8 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   if (p.coarse_events < 0 || p.coarse_events > 1) return bad("coarse_events must be 0 or 1");
   r.coarse = p.coarse_events == 1;
   r.fusion = p.fusion_order;
+  if (p.attn_split_pages < 0) return bad("attn_split_pages must not be negative");
+  r.split_pages = p.attn_split_pages > 0 ? p.attn_split_pages : 1;
   // default scheduler count: none when nothing is JIT (every compute unit
   // is a worker), else the largest S <= 16 that divides the worker count, so
   // that every scheduler deals over the same number of workers
@@ -139,9 +141,12 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
     // one attention task per worker, at most one slot per page of each request
     r.S_attn = (int32_t)std::max<int64_t>(B, std::min<int64_t>(r.W / hkv, (int64_t)B * max_pages));
   } else {
-    // at most two attention tasks per worker (2 W / hkv splits), at most 8
-    int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, 2 * r.W / ((int64_t)B * hkv)));
-    r.S_attn = (int32_t)std::min<int64_t>(s, max_pages);
+    // one attention task per worker, as at batch > 1: the request's split
+    // count is decided when the step runs (at most one split per page,
+    // attn_split_pages pages at least, and no more than the split combine can
+    // stage), and with W attention tasks every worker runs one task of each
+    // operator of a layer (8B shape: 4.06 against 4.19 ms with 8 slots)
+    r.S_attn = (int32_t)std::max<int64_t>(1, std::min<int64_t>(r.W / hkv, max_pages));
   }
   if (r.T_qkv / (hkv * r.K_qkv) > cdiv(Sg, r.q)) return bad("t_qkv: more tiles per kv group than column quanta");
   // (column tiles per operator)

@@ -39,6 +39,7 @@ struct Params {
   bool preload = true;    // weight pre-load of the next AOT projection tile
   bool coarse = false;    // operator-level graph: attention waits for all q/k/v tiles
   int32_t fusion = 0;     // 0: Def 4.1 then Def 4.2; 1: none (one event per overlap edge)
+  int32_t split_pages = 2;  // minimum KV pages per attention split (run time)
   int32_t K_qkv = 1, K_o = 1, K_down = 1;   // k-splits (batch > 1)
 };
 

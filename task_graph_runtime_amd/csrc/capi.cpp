@@ -242,10 +242,11 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
   // attention: wavefront merge states, raw q/k/v row, processed heads
   stage = std::max(stage, chunks(kWaves * G * (d + 2) * 4) + 2 * chunks((G + 2) * d * 4));
   // the split combine stages a request's records when they fit in 96 KB (else it reads them from
-  // global memory); a request gets at most M - B + 1 of the M slots
+  // global memory); a request gets at most M - B + 1 of the M slots.  At batch 1 the step caps the
+  // request's split count at what the staging area holds, so the area is not grown for it.
   const int64_t max_split = (int64_t)p.S_attn - B + 1;
   const int64_t comb = ((max_split * G * (d + 2) + 63) & ~(int64_t)63) * 4;
-  if (comb <= 96 * 1024) stage = std::max(stage, comb);
+  if (B > 1 && comb <= 96 * 1024) stage = std::max(stage, comb);
   // accumulators: the widest projection tile, rows per column x batch
   const int64_t tpg = p.T_qkv / hkv, Sg = (G + 2) * d;
   auto widest = [&](int64_t N, int64_t T) { return p.q * ((((N + p.q - 1) / p.q) + T - 1) / T); };
@@ -447,6 +448,7 @@ int upload(mpk_tgraph* t) {
   a.T_lm = t->prm.T_lm; a.qk_norm = c.qk_norm; a.max_seq = c.max_seq_len; a.eps = c.rms_eps; a.theta = c.rope_theta;
   a.wl = t->d_wl;
   a.arrive = t->d_arrive;
+  a.attn_min_pages = t->prm.split_pages;
   return lds_layout(c, t->B, t->P, t->prm, &a);
 }
 
@@ -609,6 +611,7 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   r.coarse_events = prm.coarse ? 1 : 0;
   r.k_qkv = prm.K_qkv; r.k_o = prm.K_o; r.k_down = prm.K_down;
   r.fusion_order = prm.fusion;
+  r.attn_split_pages = prm.split_pages;
   t->resolved = r;
   std::vector<TaskDef> tasks;
   decompose(*cfg, batch, prm, &tasks);

@@ -195,6 +195,8 @@ struct KArgs {
   // brings one to S_attn is the last of its (b, g), merges the partials and
   // resets it to 0, so it is 0 between steps
   MPK_GLOBAL uint32_t* arrive;
+  // the smallest split an attention task takes, in KV pages (see attn_slot)
+  int32_t attn_min_pages;
 };
 
 }  // namespace mpk

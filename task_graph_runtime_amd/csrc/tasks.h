@@ -106,6 +106,20 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// 16 bytes of a batch-1 tile's weight stream, loaded non-temporally: every
+// weight byte is read exactly once per step, and a stream that does not
+// displace other lines of the L2 leaves it to the data tasks share (the
+// activation vectors every tile stages, the attention's pages).  On one
+// MI355X the 8B batch-1 step went from 4.03 to 3.86 ms.  (The matrix-core
+// tiles of batch > 1 read each 128-byte weight line as two 64-byte halves in
+// consecutive contraction steps, so their loads keep the line in the L2:
+// non-temporal loads there measured 7.68 against 7.41 ms.)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldw(MPK_GLOBAL const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<MPK_GLOBAL const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Element i of p[0..n) or `dflt` when i >= n (n >= 1).  The load itself is
 // unconditional (from a clamped index): a load under a branch makes the
 // compiler wait for it before the join, serialising round trips.
@@ -511,7 +525,7 @@ __device__ __forceinline__ void gemv_preload(const KArgs& a, const DevTask& t, c
 #pragma unroll
   for (int j = 0; j < kMaxPfSegs; ++j) {
     const int k = min(sw.ks * 512 + lane * 8, r.K - 8);
-    v[j] = ldg<uint4>(sw.row + k);
+    v[j] = ldw(sw.row + k);
     if (r.pb + j + 1 < r.pe) seg_next(a, t, P, r.nseg, sw);
   }
 #pragma unroll
@@ -722,7 +736,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int k = min(ld.ks * 512 + kl, K - 8);
-      b[u] = ldg<uint4>(ld.row + k);
+      b[u] = ldw(ld.row + k);
       if (s0 + u + 1 < S) seg_next(a, t, P, nseg, ld);
     }
   };
@@ -979,8 +993,12 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
 // n_b = max(1, ceil(pages_b / T)) consecutive slots, in request order, with
 // T the smallest split size (in pages) for which sum_b n_b <= M
 // (pages_b = ceil((L_b + 1) / P); a request with an invalid length counts 0
-// pages); slots past the last request's are idle.  At batch 1 the request
-// takes all S_attn slots (splits past its pages are empty).  Every task
+// pages); slots past the last request's are idle.  T is at least Tmin =
+// attn_min_pages: a split shorter than that costs more in its fixed latency
+// (q/k/v row, norm and rotation, partial record, merge) than it saves in key
+// and value streaming.  At batch 1 that makes the request's split count
+// n = min(M, max(1, ceil(pages / Tmin))), so the split count follows the
+// cached length at run time (a graph is built for the longest).  Every task
 // computes the same allocation from the B sequence lengths, so no split is
 // longer than T pages however the lengths differ.
 struct AttnSlot {
@@ -993,7 +1011,7 @@ __device__ __forceinline__ int attn_pages(const KArgs& a, int L) {
 // butterfly sum, a scan of the split counts and a ballot; the result is
 // wavefront-uniform)
 // one: batch 1, return {0, j, 0, 0} without loading anything (the caller
-// knows the split count, S_attn).
+// sizes the splits once it has read the length).
 __device__ __forceinline__ AttnSlot attn_slot(const KArgs& a, int j, bool one) {
   const int lane = tidx() & 63, B = a.B, M = a.S_attn;
   if (one) return AttnSlot{0, j, 0, 0};
@@ -1009,7 +1027,7 @@ __device__ __forceinline__ AttnSlot attn_slot(const KArgs& a, int j, bool one) {
     for (int m = 1; m < 16; m <<= 1) c += __shfl_xor(c, m, 16);
     return __builtin_amdgcn_readfirstlane(c);
   };
-  int lo = 1, hi = max(__builtin_amdgcn_readfirstlane(mx), 1);
+  int lo = a.attn_min_pages, hi = max(__builtin_amdgcn_readfirstlane(mx), lo);
   while (lo < hi) {
     const int mid = (lo + hi) / 2;
     if (splits(mid) <= M) hi = mid;
@@ -1028,6 +1046,12 @@ __device__ __forceinline__ AttnSlot attn_slot(const KArgs& a, int j, bool one) {
   const int src = __ffsll((long long)mine) - 1;
   const int st = __builtin_amdgcn_readfirstlane(__shfl(start, src));
   return AttnSlot{src, j - st, __builtin_amdgcn_readfirstlane(__shfl(n, src)), st};
+}
+
+// The most splits of one request whose partial records the combine stages
+// in LDS (staging area [0, lds_acc), records padded as attn_combine does).
+__device__ __forceinline__ int attn_stage_cap(const KArgs& a) {
+  return max(1, (a.lds_acc / 4 - 63) / (a.G * (a.d + 2)));
 }
 
 // Merge of the n partial records (m, l, o[D]) of a request, in slots
@@ -1145,8 +1169,11 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
   const bool ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
   const int ntok = ok ? Lb + 1 : 0;
   const int nb = (ntok + P - 1) / P;
-  // at batch 1, attn_slot's allocation for one request: min(pages, S_attn) splits, at least 1
-  const int S = a.B == 1 ? a.S_attn : sl.n;   // (attn_slot's allocation for one request)
+  // at batch 1, attn_slot's allocation for one request: min(S_attn, ceil(pages / Tmin)) splits,
+  // at least 1, and no more than the split combine can stage in LDS; a slot past them is idle
+  const int S = a.B == 1 ? max(1, min(min(a.S_attn, attn_stage_cap(a)), (nb + a.attn_min_pages - 1) / a.attn_min_pages))
+                         : sl.n;
+  if (s >= S) return;
   const bool last_split = s == S - 1;
   if (!ok && tid0 == 0) report(a, MPK_ERR_INVALID_ARG, t.id, -1, (uint32_t)Lb, 0u);
   const int j0 = (int)((int64_t)s * nb / S), j1 = (int)((int64_t)(s + 1) * nb / S);

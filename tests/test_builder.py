@@ -177,7 +177,10 @@ def test_default_params_resolve_as_documented():
     p = h["params"]
     # batch 1: attention is AOT, nothing is JIT, so no scheduler workgroups: 256 workers
     assert p["n_workers"] == 256 and p["n_sched_waves"] == 0 and p["quantum"] == 1 and p["attn_jit"] == 2
-    assert p["t_qkv"] == 256 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 256 and p["s_attn"] == 8
+    # one attention task per worker: 256 / 8 = 32 slots per kv group (the step uses as many as the
+    # cached length and the combine's staging allow); at least one page per split
+    assert p["t_qkv"] == 256 and p["t_o"] == p["t_gu"] == p["t_down"] == p["t_lm"] == 256 and p["s_attn"] == 32
+    assert p["attn_split_pages"] == 1
     h16 = mpk.TGraph(s.cfg(), 16, 64, {}, host_only=True).header()["params"]
     # batch 16: every task AOT by default too, so no scheduler workgroups: 256 workers
     assert h16["n_workers"] == 256 and h16["n_sched_waves"] == 0 and h16["attn_jit"] == 2
