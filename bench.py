@@ -35,25 +35,36 @@ def algorithmic_bytes(s, seq_lens) -> int:
     return 2 * (w + len(seq_lens) * H + kv)
 
 
-DEVICE_SOURCES = ("task_graph_runtime_amd/csrc/megakernel.hip", "task_graph_runtime_amd/csrc/tasks.h",
-                  "task_graph_runtime_amd/csrc/rt.h")
+SOURCE_FILES = ("include/mpk.h",)
+SOURCE_DIR = "task_graph_runtime_amd/csrc"
 TRAFFIC_FILE = "profiles/megakernel_{config}_traffic.txt"
 
 
-def measured_traffic(config: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of this
-    workload, or None when there is none or the device sources have changed
-    since the counters were taken."""
+def source_hash(params: dict) -> str:
+    """sha256 over every library source (the C ABI header and all of csrc/)
+    and the graph's resolved build parameters: the HBM-traffic counters of a
+    profile are valid only for the build and graph they were taken on."""
     import hashlib
+    h = hashlib.sha256()
+    files = list(SOURCE_FILES) + sorted(os.path.join(SOURCE_DIR, f) for f in os.listdir(os.path.join(ROOT, SOURCE_DIR))
+                                        if f.endswith((".h", ".cpp", ".hip")))
+    for src in files:
+        h.update(src.encode())
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    h.update(json.dumps(params, sort_keys=True).encode())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    workload, or None when there is none or it was taken on other sources or
+    build parameters."""
     path = os.path.join(ROOT, TRAFFIC_FILE.format(config={"qwen3_8b": "qwen3_8b_b1"}.get(config, config)))
     if not os.path.exists(path):
         return None
     kv = dict(line.strip().split("=", 1) for line in open(path) if "=" in line and " " not in line.strip())
-    h = hashlib.sha256()
-    for src in DEVICE_SOURCES:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    if kv.get("source_sha256") != h.hexdigest():
+    if kv.get("source_sha256") != src_hash:
         return None
     return int(kv["traffic_bytes"])
 
@@ -75,38 +86,42 @@ def time_steps(fn, steps, warmup, torch):
     return wall_ms, per
 
 
-def cpu_baseline(s, inp, budget_layers=(2, 4)):
-    """The oracle, as it stands, on a bounded sample: the step cut to k1 and k2
-    layers (embedding, final norm and LM head included); the per-layer cost is
-    the difference, extrapolated to all layers."""
+def cpu_baseline(s, inp, steps=3):
+    """The oracle, as it stands, timed on the host cores: `steps` full decode
+    steps (fp32 numpy with the installed multithreaded BLAS; every bf16 weight
+    matrix widened to fp32 when it is used, that work included), median.  The
+    weights are copied to host memory once, outside the timed region."""
     import numpy as np
     from oracle import numerics
     from tests._util import oracle_weights, bf16_bits
+    cores = len(os.sched_getaffinity(0))
+    blas, threads = "unknown", cores
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = int(info[0].get("num_threads", cores))
     except Exception:
-        cores = os.cpu_count()
+        pass
+    ram_gib = os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES") / 2**30
     kv = inp["kv"]
-    k1, k2 = budget_layers
-    w = inp["weights"]
-    times = {}
-    for k in (k1, k2):
-        sk = s.with_(n_layers=k)
-        wk = {"embed": w["embed"], "final_norm": w["final_norm"], "lm_head": w["lm_head"], "layers": w["layers"][:k]}
-        ow = oracle_weights(wk, lazy=True)
-        kp = bf16_bits(kv["k_pool"][:k]); vp = bf16_bits(kv["v_pool"][:k])
+    w = oracle_weights(inp["weights"])          # host bf16 bit patterns, copied once
+    kp, vp = bf16_bits(kv["k_pool"]), bf16_bits(kv["v_pool"])
+    args = (inp["token_ids"].cpu().numpy(), kp, vp, kv["page_table"].cpu().numpy(), inp["seq_lens"].cpu().numpy(),
+            s.page_size)
+    times = []
+    for _ in range(steps):
         t0 = time.perf_counter()
-        numerics.decode_step(sk.cfg(), ow, inp["token_ids"].cpu().numpy(), kp, vp, kv["page_table"].cpu().numpy(),
-                             inp["seq_lens"].cpu().numpy(), s.page_size, dtype=np.float32)
-        times[k] = time.perf_counter() - t0
-    per_layer = (times[k2] - times[k1]) / (k2 - k1)
-    fixed = times[k1] - k1 * per_layer
-    est_ms = (fixed + s.n_layers * per_layer) * 1e3
-    return {"value": round(est_ms, 1), "unit": "ms/token", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp32 numpy oracle run cut to {k1} and {k2} of {s.n_layers} layers (weights widened from bf16 "
-                      f"per call, copied per layer from the GPU, copy included); per-layer cost = difference, "
-                      f"extrapolated to {s.n_layers} layers; measured {times[k1]:.1f} s and {times[k2]:.1f} s"}
+        numerics.decode_step(s.cfg(), w, *args, dtype=np.float32)
+        times.append(time.perf_counter() - t0)
+        print(f"[bench] cpu oracle step {len(times)}: {times[-1]:.2f} s", file=sys.stderr, flush=True)
+    del w, kp, vp
+    med = statistics.median(times)
+    return {"value": round(med * 1e3, 1), "unit": "ms/token", "cores": int(threads), "kind": "oracle",
+            "sample": f"median of {steps} full {s.name} decode steps of the fp32 numpy oracle "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s; bf16 weights widened per use, included; "
+                      f"BLAS {blas}, {threads} threads of {cores} cores in the affinity mask, {ram_gib:.0f} GiB RAM)"}
 
 
 def main():
@@ -183,6 +198,8 @@ def main():
         cpu = cpu_baseline(s, inp)
 
     hdr = g.header()["params"]
+    src_hash = source_hash(hdr)
+    print(f"[bench] source hash {src_hash}", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC, "value": round(ms, 4), "unit": "ms/token", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
@@ -200,10 +217,13 @@ def main():
         "baseline_ms": base or None,
         "speedup_vs_baseline": round(min(base.values()) / kern_ms, 3) if base else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config, src_hash)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    # release the graph while the runtime is up (not from a finaliser at interpreter exit)
+    torch.cuda.synchronize()
+    g.close()
 
 
 if __name__ == "__main__":
