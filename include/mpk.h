@@ -301,6 +301,28 @@ void mpk_free_host_view(mpk_tgraph_host_view* v);
 int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
                     const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as mpk_decode_step -- same kernel, same arguments, same outputs --
+ * with its per-call mutable device state (event counters, scheduler and JIT
+ * rings, split arrivals, fp32 activations) in a static device area of the
+ * library (64 MiB, one per GPU the library runs on, held until the process
+ * ends) instead of the graph's own buffers.  The call allocates nothing,
+ * synchronises nothing and copies nothing from the host: it clears the
+ * runtime part of the area with a fill kernel on `stream` and launches the
+ * step there (epoch 1).  The graph's device must be current, and the
+ * weights must be the ones the graph was last bound to by mpk_decode_step
+ * (which uploads their resolved pointers).  Every call on one GPU shares
+ * that GPU's area, which keeps the last call's contents: calls that overlap
+ * on one GPU (other streams, other graphs) race and must be ordered by the
+ * caller.  mpk_read_tensor reads the graph's own buffers, not this area.  The
+ * in-kernel status goes to the graph's status word (mpk_get_status).
+ * Errors: MPK_ERR_UNSUPPORTED when the graph's state exceeds the area (the
+ * message gives both sizes), MPK_ERR_INVALID_ARG (null pointer, host-only
+ * graph, weights not bound, device not current), MPK_ERR_HIP. */
+int mpk_decode_step_noalloc(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+                            const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream);
+
 /* The kernel-per-operator baseline the mega-kernel is measured against
  * (MPK summary page, section 2 Q1: kernel-per-operator execution with a
  * barrier at every operator boundary; section 2 Q3: the comparison): the

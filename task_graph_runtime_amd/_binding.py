@@ -98,6 +98,8 @@ SIGNATURES = {
     "mpk_free_host_view": (None, [C.POINTER(mpk_tgraph_host_view)]),
     "mpk_decode_step": (C.c_int, [C.c_void_p, C.POINTER(mpk_weights), C.c_void_p, C.POINTER(mpk_kv), C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p]),
+    "mpk_decode_step_noalloc": (C.c_int, [C.c_void_p, C.POINTER(mpk_weights), C.c_void_p, C.POINTER(mpk_kv),
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "mpk_decode_step_baseline": (C.c_int, [C.c_void_p, C.POINTER(mpk_weights), C.c_void_p, C.POINTER(mpk_kv),
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32]),
     "mpk_read_tensor": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t]),
@@ -260,6 +262,10 @@ class TGraph:
     def decode_step(self, w: Weights, token_ids, kv: KV, seq_lens, logits, next_ids, stream=None):
         _check(lib().mpk_decode_step(self.h, C.byref(w.s), _ptr(token_ids), C.byref(kv.s), _ptr(seq_lens),
                                      _ptr(logits), _ptr(next_ids), _stream_ptr(stream)))
+
+    def decode_step_noalloc(self, w: Weights, token_ids, kv: KV, seq_lens, logits, next_ids, stream=None):
+        _check(lib().mpk_decode_step_noalloc(self.h, C.byref(w.s), _ptr(token_ids), C.byref(kv.s), _ptr(seq_lens),
+                                             _ptr(logits), _ptr(next_ids), _stream_ptr(stream)))
 
     def decode_step_baseline(self, w: Weights, token_ids, kv: KV, seq_lens, logits, next_ids, stream=None,
                              use_hipgraph: bool = False):

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <map>
 #include <cmath>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -20,20 +21,28 @@ namespace mpk {
 hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
 hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count, hipStream_t stream);
 hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream);
+size_t scratch_capacity();
+hipError_t scratch_address(int device, void** out);
+hipError_t scratch_zero(void* p, size_t bytes, hipStream_t stream);
 }  // namespace mpk
 
 using namespace mpk;
 
 namespace {
 
-thread_local std::string g_err;
+// The message of the last failure on this thread, in a fixed buffer so that
+// reporting an error allocates nothing (the no-allocation step reports
+// through it too).
+thread_local char g_err[512];
 
-int fail(int code, const std::string& msg) {
-  g_err = msg;
+int fail(int code, const char* msg) {
+  std::snprintf(g_err, sizeof(g_err), "%s", msg);
   return code;
 }
+int fail(int code, const std::string& msg) { return fail(code, msg.c_str()); }
 int hip_fail(hipError_t e, const char* what) {
-  return fail(MPK_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  std::snprintf(g_err, sizeof(g_err), "%s: %s", what, hipGetErrorString(e));
+  return MPK_ERR_HIP;
 }
 #define HIPCHK(x)                                  \
   do {                                             \
@@ -84,6 +93,7 @@ struct mpk_tgraph {
   StatusWord* d_status = nullptr;
   uint32_t* d_arrive = nullptr;  // attention split arrivals (0 between steps)
   int64_t arrive_bytes = 0;
+  int64_t rt_bytes = 0;     // runtime arena (counters, rings, state, status, arrivals)
   uint32_t sched_cap = 0, jit_cap = 0;
 
   void* d_act = nullptr;
@@ -370,6 +380,7 @@ int upload(mpk_tgraph* t) {
   const int64_t r_arrive = align256(r_status + (int64_t)sizeof(StatusWord));
   const int64_t rt_bytes =
       align256(r_arrive + (int64_t)t->cfg.n_layers * t->B * t->cfg.n_kv_heads * 4);
+  t->rt_bytes = rt_bytes;
   HIPCHK(hipMalloc(&t->d_rt, rt_bytes));
   HIPCHK(hipMemset(t->d_rt, 0, rt_bytes));
   char* rb = (char*)t->d_rt;
@@ -523,6 +534,9 @@ TaskPtrs host_task_ptrs(const DevTask& d, const std::vector<const void*>& wl, co
   return r;
 }
 
+void fill_args(const mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+               const int32_t* seq_lens, float* logits, int32_t* next_ids, KArgs* out);
+
 // Fill the per-step arguments; when the weights changed, uploads the
 // weight-pointer table and the AOT entries' resolved pointers.
 int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
@@ -558,6 +572,17 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
     HIPCHK(hipMemcpy(t->d_aot_desc, t->h_aot.data(), t->h_aot.size() * sizeof(AotEntry), hipMemcpyHostToDevice));
     t->h_wl = key;
   }
+  fill_args(t, w, token_ids, kv, seq_lens, logits, next_ids, out);
+  t->last = *out;
+  t->args_valid = true;
+  return MPK_OK;
+}
+
+// Arguments of one step from the graph's resolved ones and the caller's
+// pointers (no device work, no allocation).
+void fill_args(const mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+               const int32_t* seq_lens, float* logits, int32_t* next_ids, KArgs* out) {
+  const mpk_model_cfg& c = t->cfg;
   KArgs a = t->base;
   a.poll_sleep = 1;
   a.embed = (const uint16_t*)w->embed;
@@ -573,9 +598,25 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   a.logits = logits;
   a.next_ids = next_ids;
   *out = a;
-  t->last = a;
-  t->args_valid = true;
-  return MPK_OK;
+}
+
+// Whether w holds the weight pointers the graph's descriptors were last
+// resolved against (compared in place: no allocation).
+bool weights_bound(const mpk_tgraph* t, const mpk_weights* w) {
+  const size_t n = (size_t)t->cfg.n_layers * LAYER_PTRS;
+  if (t->h_wl.size() != n + 2) return false;
+  for (size_t i = 0; i < n; ++i)
+    if (w->layer[i] != t->h_wl[i]) return false;
+  const void* lm = t->cfg.tied_embedding ? w->embed : w->lm_head;
+  return lm == t->h_wl[n] && w->final_norm == t->h_wl[n + 1];
+}
+
+// Move a pointer into [from, from + n) to the same offset from `to`.
+template <typename T>
+void rebase(T*& p, const void* from, int64_t n, char* to) {
+  const char* c = reinterpret_cast<const char*>(p);
+  const char* f = reinterpret_cast<const char*>(from);
+  if (p && c >= f && c < f + n) p = reinterpret_cast<T*>(to + (c - f));
 }
 
 uint64_t timeout_ticks(const mpk_tgraph* t) {
@@ -631,7 +672,7 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
 
 extern "C" {
 
-const char* mpk_last_error(void) { return g_err.c_str(); }
+const char* mpk_last_error(void) { return g_err; }
 
 int mpk_build_tgraph(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, mpk_tgraph** out) {
   return build_impl(cfg, batch, page_size, nullptr, out);
@@ -713,6 +754,57 @@ int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_id
   const uint32_t epoch = ++g->epoch;
   hipError_t e = launch_megakernel(a, epoch, timeout_ticks(g), g->grid, s);
   if (e != hipSuccess) { --g->epoch; return hip_fail(e, "mega-kernel launch"); }
+  g->last_stream = s;
+  return MPK_OK;
+}
+
+int mpk_decode_step_noalloc(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
+                            const int32_t* seq_lens, float* logits, int32_t* next_ids, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (!g || !w || !w->layer || !kv || !token_ids || !seq_lens || !logits || !next_ids)
+    return fail(MPK_ERR_INVALID_ARG, "null argument");
+  if (g->host_only) return fail(MPK_ERR_INVALID_ARG, "graph was built host-only");
+  const size_t need = (size_t)g->rt_bytes + (size_t)g->act_bytes;
+  if (need > scratch_capacity()) {
+    std::snprintf(g_err, sizeof(g_err), "the step needs %zu bytes of scratch, more than the %zu of the static area",
+                  need, scratch_capacity());
+    return MPK_ERR_UNSUPPORTED;
+  }
+  if (!weights_bound(g, w))
+    return fail(MPK_ERR_INVALID_ARG, "weights not bound to this graph: run mpk_decode_step once with these weights");
+  if (!kv->k_pool || !kv->v_pool || !kv->page_table || kv->n_pages < 1 || kv->max_pages_per_seq < 1 ||
+      ((uintptr_t)kv->k_pool & 15) || ((uintptr_t)kv->v_pool & 15) || ((uintptr_t)w->embed & 15))
+    return fail(MPK_ERR_INVALID_ARG, "bad KV cache descriptor or embedding pointer");
+  int dev = -1;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev != g->device) return fail(MPK_ERR_INVALID_ARG, "the graph's device is not the current device");
+  void* base = nullptr;
+  hipError_t e = scratch_address(dev, &base);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  KArgs a;
+  fill_args(g, w, token_ids, kv, seq_lens, logits, next_ids, &a);
+  // the runtime arena at the start of the scratch area, the activations right after it
+  // (both blocks keep the graph's own layout; the status word stays the graph's)
+  char* rt = static_cast<char*>(base);
+  char* act = rt + g->rt_bytes;
+  rebase(a.ev_cnt, g->d_rt, g->rt_bytes, rt);
+  rebase(a.ev_sub, g->d_rt, g->rt_bytes, rt);
+  rebase(a.sched_ring, g->d_rt, g->rt_bytes, rt);
+  rebase(a.sched_tail, g->d_rt, g->rt_bytes, rt);
+  rebase(a.jit_ring, g->d_rt, g->rt_bytes, rt);
+  rebase(a.state, g->d_rt, g->rt_bytes, rt);
+  rebase(a.arrive, g->d_rt, g->rt_bytes, rt);
+  for (float** p : {&a.e, &a.hf, &a.r, &a.h, &a.qkv, &a.part, &a.attn, &a.o, &a.s, &a.h2, &a.a, &a.dn})
+    rebase(*p, g->d_act, g->act_bytes, act);
+  rebase(a.pmax, g->d_act, g->act_bytes, act);
+  a.trace = nullptr;
+  a.trace_count = nullptr;
+  a.trace_cap = 0;
+  // counters, rings and arrivals start at zero, so the step runs as epoch 1
+  e = scratch_zero(rt, (size_t)g->rt_bytes, s);
+  if (e != hipSuccess) return hip_fail(e, "scratch clear");
+  e = launch_megakernel(a, 1u, timeout_ticks(g), g->grid, s);
+  if (e != hipSuccess) return hip_fail(e, "mega-kernel launch");
   g->last_stream = s;
   return MPK_OK;
 }
