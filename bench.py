@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--baseline-steps", type=int, default=20)
     ap.add_argument("--no-baseline", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prepared", action="store_true",
+                    help="batch > 1: run the step on weights repacked by mpk_prepare_weights (matrix-core load order)")
     ap.add_argument("--params", default="{}",
                     help="build parameters (JSON object of mpk_build_params fields, e.g. '{\"s_attn\": 16}') for "
                          "the ablations; the default build is the one measured")
@@ -158,6 +160,8 @@ def main():
     lens = inp["seq_lens"].cuda()
     g = mpk.TGraph(s.cfg(), s.batch, s.page_size, json.loads(args.params))
     W = mpk.Weights(inp["weights"])
+    if args.prepared:
+        W = mpk.PreparedWeights(g, W)
     KV = mpk.KV(kv["k_pool"], kv["v_pool"], kv["page_table"].cuda())
     logits = torch.empty((s.batch, s.vocab), device="cuda", dtype=torch.float32)
     nxt = torch.empty((s.batch,), device="cuda", dtype=torch.int32)
@@ -209,7 +213,7 @@ def main():
                                f"page {s.page_size}",
                    "global_batch": s.batch, "seq_len": int(max(inp['seq_lens'].tolist())) + 1,
                    "parallelism": "single GPU", "workers": hdr["n_workers"], "sched_waves": hdr["n_sched_waves"],
-                   "s_attn": hdr["s_attn"]},
+                   "s_attn": hdr["s_attn"], "weights": "prepared" if args.prepared else "row-major"},
         "tb_per_s": round(achieved / 1e3, 3), "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 1),
         "kernel_ms": {"mean": round(kern_ms, 4), "median": round(statistics.median(per), 4),
                       "p10": round(sorted(per)[len(per) // 10], 4), "p90": round(sorted(per)[(9 * len(per)) // 10], 4)},

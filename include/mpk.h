@@ -146,9 +146,11 @@ typedef struct mpk_tgraph mpk_tgraph; /* opaque; owned by the library */
  * (q_norm/k_norm may be NULL when qk_norm is 0). */
 typedef struct {
   const void* embed;      /* [vocab][H] */
-  const void* lm_head;    /* [vocab][H]; NULL when tied */
+  const void* lm_head;    /* [vocab][H]; NULL when tied (layout 0) */
   const void* final_norm; /* [H] */
   const void* const* layer;
+  int32_t layout;         /* 0: the matrices as above (row-major [out][in]);
+                             1: prepared by mpk_prepare_weights for one graph */
 } mpk_weights;
 
 /* Paged KV cache (device, caller-owned).  k_pool/v_pool are bf16
@@ -277,6 +279,36 @@ int mpk_build_generic_ex(const mpk_task_spec* tasks, int32_t n_tasks, const mpk_
  * mpk_build_generic(_ex) and zero the view; NULL and an already freed
  * (zeroed) view are accepted. */
 void mpk_free_host_view(mpk_tgraph_host_view* v);
+
+/* Size in bytes of the device buffer mpk_prepare_weights fills for graph g
+ * (*bytes, host pointer).  Errors: MPK_ERR_INVALID_ARG on a null pointer. */
+int mpk_prepared_weights_bytes(const mpk_tgraph* g, size_t* bytes);
+
+/* One-time repack of the projection weights of a batch > 1 graph into the
+ * order its matrix-core tiles load them (layout 1).  Each q, k, v, o, down and
+ * LM-head matrix [N][K] becomes blocks of 16 rows x 32 k, stored as
+ * [ceil(N/16)][K/32][64][8] bf16 (lane l of a block: row l % 16 at k
+ * 8 (l / 16) .. +7, the A operand of v_mfma_f32_16x16x32_bf16), so that a
+ * wavefront's loads of one block are one contiguous 1 KB; gate and up become
+ * one matrix of 2F interleaved rows (gate row c at 2c, up row c at 2c + 1),
+ * the order of a gate/up tile's rows.  The values are copied bit for bit.
+ * The MatMul task of MPK summary page section 3 ("Target operation, shapes &
+ * precision contract") is an output tile of a GEMM; at batch > 1 this is the
+ * tile's operand layout.  Inputs: `in` (layout 0) as for mpk_decode_step;
+ * `dst`, a caller-owned device buffer of dst_bytes >= the size
+ * mpk_prepared_weights_bytes reports, 256-byte aligned; `packed_layers`, a
+ * caller-owned host array of n_layers x 11 pointers.  Outputs: `packed`
+ * (host) with layout 1, the prepared matrices in dst, the LM head a prepared
+ * copy (also when tied), embedding and norm gains the caller's own, layer =
+ * packed_layers (the gate and up entries both point at the interleaved
+ * matrix).  The copy runs asynchronously on `stream`; `in` must stay valid
+ * until it completes; then `packed` serves every step of this graph and
+ * `dst` must outlive them.  Errors: MPK_ERR_INVALID_ARG (null pointer, buffer
+ * too small or misaligned, `in` not layout 0), MPK_ERR_UNSUPPORTED (batch 1,
+ * whose tiles stream whole rows, or a column quantum not a multiple of 16),
+ * MPK_ERR_HIP. */
+int mpk_prepare_weights(const mpk_tgraph* g, const mpk_weights* in, void* dst, size_t dst_bytes,
+                        const void** packed_layers, mpk_weights* packed, void* stream);
 
 /* One decode step as ONE persistent-kernel launch on `stream` (asynchronous):
  * the whole forward of one new token per request, run by the in-kernel

@@ -41,7 +41,7 @@ class mpk_build_params(C.Structure):
 
 class mpk_weights(C.Structure):
     _fields_ = [("embed", C.c_void_p), ("lm_head", C.c_void_p), ("final_norm", C.c_void_p),
-                ("layer", C.POINTER(C.c_void_p))]
+                ("layer", C.POINTER(C.c_void_p)), ("layout", C.c_int32)]
 
 
 class mpk_kv(C.Structure):
@@ -96,6 +96,9 @@ SIGNATURES = {
     "mpk_build_generic_ex": (C.c_int, [C.POINTER(mpk_task_spec), C.c_int32, C.POINTER(mpk_region), C.c_int32,
                                        C.POINTER(mpk_build_params), C.POINTER(mpk_tgraph_host_view)]),
     "mpk_free_host_view": (None, [C.POINTER(mpk_tgraph_host_view)]),
+    "mpk_prepared_weights_bytes": (C.c_int, [C.c_void_p, C.POINTER(C.c_size_t)]),
+    "mpk_prepare_weights": (C.c_int, [C.c_void_p, C.POINTER(mpk_weights), C.c_void_p, C.c_size_t,
+                                      C.POINTER(C.c_void_p), C.POINTER(mpk_weights), C.c_void_p]),
     "mpk_decode_step": (C.c_int, [C.c_void_p, C.POINTER(mpk_weights), C.c_void_p, C.POINTER(mpk_kv), C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p]),
     "mpk_decode_step_noalloc": (C.c_int, [C.c_void_p, C.POINTER(mpk_weights), C.c_void_p, C.POINTER(mpk_kv),
@@ -201,7 +204,27 @@ class Weights:
         layers = w["layers"]
         self._arr = (C.c_void_p * (len(layers) * 11))(*[int(lw[n].data_ptr()) for lw in layers for n in self.NAMES])
         self.s = mpk_weights(int(w["embed"].data_ptr()), 0 if w.get("lm_head") is None else int(w["lm_head"].data_ptr()),
-                             int(w["final_norm"].data_ptr()), C.cast(self._arr, C.POINTER(C.c_void_p)))
+                             int(w["final_norm"].data_ptr()), C.cast(self._arr, C.POINTER(C.c_void_p)), 0)
+
+
+class PreparedWeights:
+    """Weights of one batch > 1 graph in the matrix-core load order
+    (mpk_prepare_weights): a device buffer (torch uint8 tensor) and the
+    prepared mpk_weights that point into it.  Holds the source weights until
+    the repack has run (the caller's stream is synchronised)."""
+
+    def __init__(self, g: "TGraph", w: Weights, stream=None):
+        import torch
+        n = C.c_size_t()
+        _check(lib().mpk_prepared_weights_bytes(g.h, C.byref(n)))
+        self.buf = torch.empty(max(1, n.value), dtype=torch.uint8, device="cuda")
+        n_layers = g.cfg.n_layers
+        self._arr = (C.c_void_p * (n_layers * 11))()
+        self.s = mpk_weights()
+        _check(lib().mpk_prepare_weights(g.h, C.byref(w.s), C.c_void_p(self.buf.data_ptr()), n.value,
+                                         C.cast(self._arr, C.POINTER(C.c_void_p)), C.byref(self.s), _stream_ptr(stream)))
+        torch.cuda.synchronize()
+        self._keep = w._keep  # the embedding and norm gains are the caller's own
 
 
 class KV:

@@ -21,6 +21,8 @@ namespace mpk {
 hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
 hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count, hipStream_t stream);
 hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream);
+int64_t packed_bytes(int64_t N, int64_t K);
+hipError_t launch_pack(const void* a, const void* b, int64_t N, int64_t K, void* dst, hipStream_t stream);
 size_t scratch_capacity();
 hipError_t scratch_address(int device, void** out);
 hipError_t scratch_zero(void* p, size_t bytes, hipStream_t stream);
@@ -537,6 +539,12 @@ TaskPtrs host_task_ptrs(const DevTask& d, const std::vector<const void*>& wl, co
 void fill_args(const mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
                const int32_t* seq_lens, float* logits, int32_t* next_ids, KArgs* out);
 
+// The LM head's weights: the tied embedding, except for prepared weights,
+// which always carry a prepared copy of their own.
+const void* lm_pointer(const mpk_tgraph* t, const mpk_weights* w) {
+  return (t->cfg.tied_embedding && w->layout != 1) ? w->embed : w->lm_head;
+}
+
 // Fill the per-step arguments; when the weights changed, uploads the
 // weight-pointer table and the AOT entries' resolved pointers.
 int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, const mpk_kv* kv,
@@ -545,7 +553,11 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
     return fail(MPK_ERR_INVALID_ARG, "null argument");
   if (t->host_only) return fail(MPK_ERR_INVALID_ARG, "graph was built host-only");
   const mpk_model_cfg& c = t->cfg;
-  if (!w->embed || !w->final_norm || !w->layer || (!c.tied_embedding && !w->lm_head))
+  if (w->layout != 0 && w->layout != 1) return fail(MPK_ERR_INVALID_ARG, "weights layout must be 0 or 1");
+  const bool packed = w->layout == 1;
+  if (packed && (t->B == 1 || t->prm.q % 16))
+    return fail(MPK_ERR_INVALID_ARG, "prepared weights (layout 1) serve only the batch > 1 graph they were made for");
+  if (!w->embed || !w->final_norm || !w->layer || ((packed || !c.tied_embedding) && !w->lm_head))
     return fail(MPK_ERR_INVALID_ARG, "missing weight pointer");
   if (!kv->k_pool || !kv->v_pool || !kv->page_table || kv->n_pages < 1 || kv->max_pages_per_seq < 1)
     return fail(MPK_ERR_INVALID_ARG, "bad KV cache descriptor");
@@ -560,7 +572,7 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   if (((uintptr_t)w->embed & 15) || ((uintptr_t)w->lm_head & 15) || ((uintptr_t)kv->k_pool & 15) ||
       ((uintptr_t)kv->v_pool & 15))
     return fail(MPK_ERR_INVALID_ARG, "weights and KV pools must be 16-byte aligned");
-  const void* lm = c.tied_embedding ? w->embed : w->lm_head;
+  const void* lm = lm_pointer(t, w);
   std::vector<const void*> key = wl;
   key.push_back(lm);
   key.push_back(w->final_norm);
@@ -586,7 +598,8 @@ void fill_args(const mpk_tgraph* t, const mpk_weights* w, const int32_t* token_i
   KArgs a = t->base;
   a.poll_sleep = 1;
   a.embed = (const uint16_t*)w->embed;
-  a.lm_head = c.tied_embedding ? nullptr : (const uint16_t*)w->lm_head;
+  a.lm_head = (const uint16_t*)lm_pointer(t, w);
+  a.wpacked = w->layout == 1;
   a.final_norm = (const uint16_t*)w->final_norm;
   a.k_pool = (uint16_t*)kv->k_pool;
   a.v_pool = (uint16_t*)kv->v_pool;
@@ -607,8 +620,7 @@ bool weights_bound(const mpk_tgraph* t, const mpk_weights* w) {
   if (t->h_wl.size() != n + 2) return false;
   for (size_t i = 0; i < n; ++i)
     if (w->layer[i] != t->h_wl[i]) return false;
-  const void* lm = t->cfg.tied_embedding ? w->embed : w->lm_head;
-  return lm == t->h_wl[n] && w->final_norm == t->h_wl[n + 1];
+  return lm_pointer(t, w) == t->h_wl[n] && w->final_norm == t->h_wl[n + 1] && (w->layout == 1) == (t->last.wpacked != 0);
 }
 
 // Move a pointer into [from, from + n) to the same offset from `to`.
@@ -755,6 +767,78 @@ int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_id
   hipError_t e = launch_megakernel(a, epoch, timeout_ticks(g), g->grid, s);
   if (e != hipSuccess) { --g->epoch; return hip_fail(e, "mega-kernel launch"); }
   g->last_stream = s;
+  return MPK_OK;
+}
+
+// The matrices of a prepared copy, in order: per layer q, k, v, o, gate/up
+// (interleaved), down; then the LM head.  Each entry: the source(s), rows,
+// contraction length and offset in the buffer.
+struct PackPlan {
+  struct Item { const void* a; const void* b; int64_t N, K, off; int layer, slot; };
+  std::vector<Item> items;
+  int64_t bytes = 0;
+};
+PackPlan pack_plan(const mpk_tgraph* t, const mpk_weights* w) {
+  const mpk_model_cfg& c = t->cfg;
+  const int64_t H = c.hidden, F = c.ffn, hq = c.n_q_heads, hkv = c.n_kv_heads, d = c.head_dim;
+  PackPlan p;
+  auto add = [&](const void* a, const void* b, int64_t N, int64_t K, int layer, int slot) {
+    p.items.push_back({a, b, N, K, p.bytes, layer, slot});
+    p.bytes = align256(p.bytes + packed_bytes(N, K));
+  };
+  for (int l = 0; l < c.n_layers; ++l) {
+    const void* const* L = w ? w->layer + (size_t)l * LAYER_PTRS : nullptr;
+    add(L ? L[W_Q] : nullptr, nullptr, hq * d, H, l, W_Q);
+    add(L ? L[W_K] : nullptr, nullptr, hkv * d, H, l, W_K);
+    add(L ? L[W_V] : nullptr, nullptr, hkv * d, H, l, W_V);
+    add(L ? L[W_O] : nullptr, nullptr, H, hq * d, l, W_O);
+    add(L ? L[W_GATE] : nullptr, L ? L[W_UP] : nullptr, 2 * F, H, l, W_GATE);
+    add(L ? L[W_DOWN] : nullptr, nullptr, H, F, l, W_DOWN);
+  }
+  add(w ? (c.tied_embedding ? w->embed : w->lm_head) : nullptr, nullptr, c.vocab, H, -1, -1);
+  return p;
+}
+
+int mpk_prepared_weights_bytes(const mpk_tgraph* g, size_t* bytes) {
+  if (!g || !bytes) return fail(MPK_ERR_INVALID_ARG, "null argument");
+  *bytes = (size_t)pack_plan(g, nullptr).bytes;
+  return MPK_OK;
+}
+
+int mpk_prepare_weights(const mpk_tgraph* g, const mpk_weights* in, void* dst, size_t dst_bytes,
+                        const void** packed_layers, mpk_weights* packed, void* stream) {
+  if (!g || !in || !dst || !packed_layers || !packed || !in->layer || !in->embed || !in->final_norm)
+    return fail(MPK_ERR_INVALID_ARG, "null argument");
+  if (in->layout != 0) return fail(MPK_ERR_INVALID_ARG, "the input weights must be layout 0");
+  if (g->B == 1) return fail(MPK_ERR_UNSUPPORTED, "batch-1 graphs stream whole weight rows: nothing to prepare");
+  if (g->prm.q % 16) return fail(MPK_ERR_UNSUPPORTED, "prepared weights need a column quantum that is a multiple of 16");
+  if (((uintptr_t)dst & 255) != 0) return fail(MPK_ERR_INVALID_ARG, "dst must be 256-byte aligned");
+  const mpk_model_cfg& c = g->cfg;
+  if (!c.tied_embedding && !in->lm_head) return fail(MPK_ERR_INVALID_ARG, "missing LM head");
+  const PackPlan p = pack_plan(g, in);
+  if ((int64_t)dst_bytes < p.bytes) return fail(MPK_ERR_INVALID_ARG, "dst smaller than mpk_prepared_weights_bytes");
+  for (const auto& it : p.items)
+    if (!it.a || (it.slot == W_GATE && !it.b) || ((uintptr_t)it.a & 15) || ((uintptr_t)it.b & 15))
+      return fail(MPK_ERR_INVALID_ARG, "missing or misaligned weight matrix");
+  hipStream_t s = (hipStream_t)stream;
+  char* base = static_cast<char*>(dst);
+  for (size_t i = 0; i < (size_t)c.n_layers * LAYER_PTRS; ++i) packed_layers[i] = in->layer[i];
+  const void* lm = nullptr;
+  for (const auto& it : p.items) {
+    hipError_t e = launch_pack(it.a, it.b, it.N, it.K, base + it.off, s);
+    if (e != hipSuccess) return hip_fail(e, "weight repack");
+    if (it.layer < 0) {
+      lm = base + it.off;
+    } else {
+      packed_layers[(size_t)it.layer * LAYER_PTRS + it.slot] = base + it.off;
+      if (it.slot == W_GATE) packed_layers[(size_t)it.layer * LAYER_PTRS + W_UP] = base + it.off;
+    }
+  }
+  packed->embed = in->embed;
+  packed->lm_head = lm;
+  packed->final_norm = in->final_norm;
+  packed->layer = packed_layers;
+  packed->layout = 1;
   return MPK_OK;
 }
 

@@ -197,6 +197,9 @@ struct KArgs {
   MPK_GLOBAL uint32_t* arrive;
   // the smallest split an attention task takes, in KV pages (see attn_slot)
   int32_t attn_min_pages;
+  // 1: the projection weights are prepared (matrix-core operand order, see
+  // packed_block in tasks.h; batch > 1 only)
+  int32_t wpacked;
 };
 
 }  // namespace mpk

@@ -868,6 +868,38 @@ __device__ __forceinline__ XOp x_operand(float4 x0, float4 x1) {
   return {__builtin_bit_cast(bf16x8, h), __builtin_bit_cast(bf16x8, l)};
 }
 
+// Prepared weights (mpk_prepare_weights): every projection matrix [N][K] is
+// stored as blocks of 16 rows x 32 k, [ceil(N/16)][K/32][64 lanes][8 bf16],
+// lane l of a block holding row l % 16 at k 8 (l / 16) .. +7 -- the A operand
+// of v_mfma_f32_16x16x32_bf16 as this tile loads it, so a wavefront's 16-byte
+// loads of one k-step cover one contiguous 1 KB instead of sixteen 64-byte
+// halves of lines.  Gate and up are one matrix of 2F interleaved rows (gate
+// row c at 2c, up row c at 2c + 1, the gate/up tile's row order).  The base
+// of the block holding tile row r0 (a multiple of 16) of a tile whose
+// columns start at lo:
+__device__ __forceinline__ gptr<const uint16_t> packed_block(const KArgs& a, int type, const TaskPtrs& P, int lo,
+                                                             int r0) {
+  switch (type) {
+    case MPK_TASK_QKV: {
+      const int col = lo + r0, g = col / a.Sg, Gd = a.G * a.d, ksn = a.H >> 5;
+      int off = col - g * a.Sg;
+      if (off < Gd) return P.p0 + (int64_t)((g * Gd + off) >> 4) * ksn * 512;
+      off -= Gd;
+      if (off < a.d) return P.p1 + (int64_t)((g * a.d + off) >> 4) * ksn * 512;
+      off -= a.d;
+      return P.p2 + (int64_t)((g * a.d + off) >> 4) * ksn * 512;
+    }
+    case MPK_TASK_OPROJ:
+      return P.p0 + (int64_t)((lo + r0) >> 4) * ((a.hq * a.d) >> 5) * 512;
+    case MPK_TASK_GATEUP:
+      return P.p0 + (int64_t)((2 * lo + r0) >> 4) * (a.H >> 5) * 512;
+    case MPK_TASK_DOWN:
+      return P.p0 + (int64_t)((lo + r0) >> 4) * (a.F >> 5) * 512;
+    default:
+      return P.p0 + (int64_t)((lo + r0) >> 4) * (a.H >> 5) * 512;
+  }
+}
+
 // One pass: row blocks [rb0, rb0 + NRB) over the wavefront's k-steps [ks0, ks1).
 template <int NRB, int KG>
 __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
@@ -877,9 +909,12 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
   const int nkg = (ks1 - ks0 + KG - 1) / KG;
   const int klast = min((ks1 - 1) * 32 + lg * 8, K - 8);   // the lane's last k in range
   const int xoff = min(li, B - 1) * K;                      // x row of the lane's request
+  // prepared weights: the lane's 16 bytes of each 1 KB block (rows past the tile read its last block)
   gptr<const uint16_t> rows[NRB];
 #pragma unroll
-  for (int r = 0; r < NRB; ++r) rows[r] = gemv_row(a, t.type, P, t.a0, min((rb0 + r) * 16 + li, nrows - 1));
+  for (int r = 0; r < NRB; ++r)
+    rows[r] = a.wpacked ? packed_block(a, t.type, P, t.a0, min(rb0 + r, (nrows - 1) >> 4) * 16) + lane * 8
+                        : gemv_row(a, t.type, P, t.a0, min((rb0 + r) * 16 + li, nrows - 1));
   uint4 wv[NRB][KG];
   float4 xr[2 * KG];
   XOp xo[KG];
@@ -887,9 +922,11 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
 #pragma unroll
   for (int r = 0; r < NRB; ++r) c[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
   auto kof = [&](int kg, int j) { return min((ks0 + kg * KG + j) * 32 + lg * 8, klast); };
+  // (prepared weights: k-step ks of a block is the 1 KB at ks * 512 elements)
   auto wload = [&](int kg, int r) {
 #pragma unroll
-    for (int j = 0; j < KG; ++j) wv[r][j] = ldg<uint4>(rows[r] + kof(kg, j));
+    for (int j = 0; j < KG; ++j)
+      wv[r][j] = ldg<uint4>(rows[r] + (a.wpacked ? min(ks0 + kg * KG + j, ks1 - 1) * 512 : kof(kg, j)));
   };
   auto xload = [&](int kg) {
 #pragma unroll

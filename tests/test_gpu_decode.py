@@ -513,3 +513,52 @@ def test_tiny_without_fusion(B, attn_jit):
     logits, nxt = r.run("mega")
     check(logits, nxt, ref, ref_next)
     check_cache(inp, cap)
+
+
+# ------------------------------------------------------------------ prepared weights (matrix-core load order)
+@pytest.mark.parametrize("B,params", [(3, {}), (3, dict(k_qkv=3, k_o=2, k_down=4)), (16, {}), (5, dict(attn_jit=1))])
+def test_prepared_weights(B, params):
+    """mpk_prepare_weights copies every projection into 16 x 32 blocks in the
+    matrix-core tile's lane order (gate/up interleaved); the step on the
+    prepared copy matches the oracle and the step on the original weights."""
+    s = TINY.with_(qk_norm=True, batch=B, ctx_range=(3, 200), ctx=0)
+    say("prepared weights", B, params)
+    inp = device_inputs(s, seed=111 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    r = Runner(inp, params)
+    plain, plain_next = r.run("mega")
+    check(plain, plain_next, ref, ref_next)
+    pw = mpk.PreparedWeights(r.g, r.w)
+    assert pw.s.layout == 1
+    r.w = pw
+    for mode in ("mega", "base"):
+        logits, nxt = r.run(mode)
+        check(logits, nxt, ref, ref_next)
+        np.testing.assert_allclose(logits, plain, rtol=1e-4, atol=1e-4)
+    check_cache(inp, cap)
+
+
+def test_prepared_weights_refused_at_batch_one():
+    inp = device_inputs(TINY, seed=120)
+    r = Runner(inp)
+    with pytest.raises(mpk.MpkError) as e:
+        mpk.PreparedWeights(r.g, r.w)
+    assert e.value.code == -2
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_batch16_prepared_weights():
+    s = synth.SHAPES["qwen3_8b_b16"]
+    say("8B b16 prepared", "generate")
+    inp = device_inputs(s, seed=0)
+    say("8B b16 prepared", "oracle")
+    ref, ref_next = run_oracle(inp, lazy=True, widen_on_device=True)
+    r = Runner(inp)
+    r.run("mega")
+    r.w = mpk.PreparedWeights(r.g, r.w)
+    say("8B b16 prepared", "mega")
+    logits, nxt = r.run("mega")
+    say("8B b16 prepared", "max |d|", check(logits, nxt, ref, ref_next))
+    del r
+    torch.cuda.empty_cache()
