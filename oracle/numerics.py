@@ -18,6 +18,11 @@ Programs -- L2"), section 3, "Target operation, shapes & precision contract":
 
 Section 2 (Q1, the regime) and section 4 ("% peak / lower-bound derivation")
 fix the workload: single-token decode of Qwen3-shaped models at batch 1-16.
+Section 5 (Fig 10, techniques inventory: the fused gather-GEMM of MoE
+layers) and the author's comments ("our next step is to support MoE
+models") bring in mixture-of-experts layers; the plainest reading of one is
+the Qwen3-MoE layer (softmax router, top-k experts, weights renormalised over
+them, SwiGLU experts).
 The pages name RMSNorm, RoPE and SwiGLU but do not write the decoder layer
 out.  The plainest reading, the Qwen3 decoder layer, is used:
 
@@ -32,6 +37,9 @@ out.  The plainest reading, the Qwen3 decoder layer, is used:
       x  += concat(o) Wo^T
       h2  = RMSNorm(x; g_post)
       x  += (silu(h2 Wg^T) * (h2 Wu^T)) Wd^T
+            (mixture of experts: x += sum over the token's top-k experts e of
+             w_e (silu(h2 Wg_e^T) * (h2 Wu_e^T)) Wd_e^T, w = softmax(h2 Wr^T)
+             at those experts, renormalised over them -- the Qwen3-MoE layer)
     logits = RMSNorm(x; g_final) Wlm^T   (Wlm = E when tied)
     next   = argmax(logits), lowest index on ties
 
@@ -112,6 +120,49 @@ def swiglu(g, u):
 def gemv(x, W):
     """``y = x W^T`` for ``W[out, in]`` (nn.Linear layout)."""
     return x @ W.T
+
+
+def moe_route(logits, top_k, norm_topk):
+    """Expert routing of each row of router logits ``[B, E]``.
+
+    The probabilities are the softmax over the E experts; a token goes to the
+    ``top_k`` most probable (ties to the lowest expert index), with those
+    probabilities as weights, renormalised to sum to one when ``norm_topk``.
+    Returns ``(ids [B, k], weights [B, k], margin [B])``: ids in decreasing
+    probability, and the margin between the k-th and the (k+1)-th probability
+    (how far the choice is from a tie; inf when k = E)."""
+    p = softmax(logits)
+    B, E = p.shape
+    ids = np.zeros((B, top_k), dtype=np.int64)
+    w = np.zeros((B, top_k), dtype=p.dtype)
+    margin = np.full(B, np.inf)
+    for b in range(B):
+        order = sorted(range(E), key=lambda e: (-p[b, e], e))
+        ids[b] = order[:top_k]
+        w[b] = p[b, ids[b]]
+        if top_k < E:
+            margin[b] = float(p[b, order[top_k - 1]] - p[b, order[top_k]])
+    if norm_topk:
+        w = w / np.sum(w, axis=-1, keepdims=True)
+    return ids, w, margin
+
+
+def moe_ffn(h, router, gate, up, down, top_k, norm_topk, dtype):
+    """Mixture-of-experts SwiGLU FFN of rows ``h [B, H]``: router logits
+    ``h router^T``, routing (``moe_route``), then for each token the sum over
+    its experts e of ``w_e (silu(h gate_e^T) * (h up_e^T)) down_e^T``.
+    ``gate``, ``up``, ``down`` are indexable by expert (``[E][F][H]``,
+    ``[E][F][H]``, ``[E][H][F]``); only the chosen experts are read.
+    Returns ``(out [B, H], logits, ids, weights, margin)``."""
+    logits = gemv(h, widen(router, dtype))
+    ids, w, margin = moe_route(logits, top_k, norm_topk)
+    out = np.zeros_like(h)
+    for b in range(h.shape[0]):
+        for j in range(top_k):
+            e = int(ids[b, j])
+            a = swiglu(gemv(h[b], widen(gate[e], dtype)), gemv(h[b], widen(up[e], dtype)))
+            out[b] += w[b, j] * gemv(a, widen(down[e], dtype))
+    return out, logits, ids, w, margin
 
 
 def argmax_lowest(v):
@@ -197,14 +248,21 @@ def decode_step(cfg, weights, token_ids, k_pool, v_pool, page_table, seq_lens, p
         o = gemv(attn2, widen(Wl["o"], dtype))
         s = r + o
         h2 = rms_norm(s, widen(Wl["post_norm"], dtype), eps)
-        g_ = gemv(h2, widen(Wl["gate"], dtype))
-        u_ = gemv(h2, widen(Wl["up"], dtype))
-        a = swiglu(g_, u_)
-        dn = gemv(a, widen(Wl["down"], dtype))
+        moe = {}
+        if int(cfg.get("n_experts", 0)) > 0:
+            dn, rl, ids, wts, margin = moe_ffn(h2, Wl["router"], Wl["gate"], Wl["up"], Wl["down"],
+                                               int(cfg["top_k"]), bool(cfg.get("norm_topk", True)), dtype)
+            a = None
+            moe = dict(router_logits=rl, expert_ids=ids, expert_weights=wts, route_margin=margin)
+        else:
+            g_ = gemv(h2, widen(Wl["gate"], dtype))
+            u_ = gemv(h2, widen(Wl["up"], dtype))
+            a = swiglu(g_, u_)
+            dn = gemv(a, widen(Wl["down"], dtype))
         x = s + dn
         if capture is not None:
             capture[l] = dict(r=r, h=h, qkv=qkv, q=q.reshape(B, -1), k_new=k, v_new=v,
-                              attn=attn2, o=o, s=s, h2=h2, a=a, d=dn)
+                              attn=attn2, o=o, s=s, h2=h2, a=a, d=dn, **moe)
     hf = rms_norm(x, widen(weights["final_norm"], dtype), eps)
     lm = weights["lm_head"] if weights.get("lm_head") is not None else weights["embed"]
     logits = gemv(hf, widen(lm, dtype))

@@ -10,7 +10,8 @@ Recipe (one generator per tensor, so that any tensor can be re-drawn alone):
 * indices: 0 embedding; ``1 + 11*l + j`` for layer ``l`` and
   ``j`` in (in_norm, q, k, v, q_norm, k_norm, o, post_norm, gate, up, down);
   then final_norm, lm_head, K pool, V pool, page permutation, token ids,
-  cached lengths;
+  cached lengths, and (mixture-of-experts shapes) the router of each layer;
+  an expert shape's gate / up / down are ``[n_experts][...]`` stacks;
 * matrices: fp32 ``randn * 0.02`` rounded to bf16 (round-to-nearest-even);
 * RMSNorm gains: 1 (``gamma="ones"``) or ``U[0.5, 1.5]`` (``gamma="uniform"``);
 * K/V: bf16 ``N(0, 1)`` at cached positions ``< L_b``; every other slot,
@@ -48,6 +49,13 @@ class Shape:
     batch: int
     ctx: int = 0                 # fixed cached length (when ctx_range is None)
     ctx_range: tuple | None = None   # inclusive uniform range of cached lengths
+    # mixture of experts (every layer's FFN when n_experts > 0): n_experts
+    # SwiGLU experts of width moe_ffn, top_k of them per token, their softmax
+    # weights renormalised over the top k when norm_topk
+    n_experts: int = 0
+    top_k: int = 0
+    moe_ffn: int = 0
+    norm_topk: bool = True
 
     def cfg(self) -> dict:
         d = asdict(self)
@@ -72,6 +80,14 @@ SHAPES = {
                           16, ctx_range=(256, 4096)),
     "qwen3_32b": Shape("qwen3_32b", 64, 5120, 64, 8, 128, 25600, 151936, True, False, 1e-6, 1e4, 8192, 64, 1,
                        ctx=4096),
+    # mixture-of-experts decoders: a tiny one, and the Qwen3-30B-A3B shape (48 layers, 128 experts of width
+    # 768, 8 per token) at batch 1 and at batch 16 with ragged contexts
+    "tiny_moe": Shape("tiny_moe", 2, 256, 4, 2, 64, 704, 1024, False, False, 1e-6, 1e4, 256, 16, 1, ctx=128,
+                      n_experts=8, top_k=2, moe_ffn=96),
+    "qwen3_30b_a3b": Shape("qwen3_30b_a3b", 48, 2048, 32, 4, 128, 6144, 151936, True, False, 1e-6, 1e4, 8192, 64, 1,
+                           ctx=1024, n_experts=128, top_k=8, moe_ffn=768),
+    "qwen3_30b_a3b_b16": Shape("qwen3_30b_a3b_b16", 48, 2048, 32, 4, 128, 6144, 151936, True, False, 1e-6, 1e4, 8192,
+                               64, 16, ctx_range=(256, 4096), n_experts=128, top_k=8, moe_ffn=768),
 }
 
 
@@ -103,6 +119,9 @@ def make_weights(s: Shape, seed: int = 0, device="cpu", gamma="ones") -> dict:
     w = {"embed": _mat((V, H), seed, 0, device), "layers": []}
     shapes = {"in_norm": (H,), "q": (hq * d, H), "k": (hkv * d, H), "v": (hkv * d, H), "q_norm": (d,),
               "k_norm": (d,), "o": (H, hq * d), "post_norm": (H,), "gate": (F, H), "up": (F, H), "down": (H, F)}
+    E, Fe = s.n_experts, s.moe_ffn
+    if E:   # expert weights [E][...]; the router [E][H] is drawn after every other tensor (see below)
+        shapes.update(gate=(E, Fe, H), up=(E, Fe, H), down=(E, H, Fe))
     for l in range(s.n_layers):
         lw = {}
         for j, name in enumerate(LAYER_TENSORS):
@@ -115,6 +134,9 @@ def make_weights(s: Shape, seed: int = 0, device="cpu", gamma="ones") -> dict:
     base = n_fixed(s)
     w["final_norm"] = _gain(H, seed, base, device, gamma)
     w["lm_head"] = None if s.tied_embedding else _mat((V, H), seed, base + 1, device)
+    if E:   # router of layer l: tensor n_fixed + 7 + l, after the KV pools, page table, tokens and lengths
+        for l in range(s.n_layers):
+            w["layers"][l]["router"] = _mat((E, H), seed, base + 7 + l, device)
     return w
 
 

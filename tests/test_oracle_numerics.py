@@ -149,6 +149,13 @@ def _hf_model(s, w, arch):
                   tie_word_embeddings=s.tied_embedding, attention_bias=False)
     if arch == "qwen3":
         m = Qwen3ForCausalLM(Qwen3Config(**common, attn_implementation="eager"))
+    elif arch == "qwen3_moe":
+        from transformers import Qwen3MoeConfig, Qwen3MoeForCausalLM
+        cfg = Qwen3MoeConfig(**common, num_experts=s.n_experts, num_experts_per_tok=s.top_k,
+                             moe_intermediate_size=s.moe_ffn, norm_topk_prob=s.norm_topk, decoder_sparse_step=1,
+                             mlp_only_layers=[], attn_implementation="eager")
+        cfg._experts_implementation = "eager"   # the per-expert loop (the grouped-GEMM path has no fp64)
+        m = Qwen3MoeForCausalLM(cfg)
     else:
         m = LlamaForCausalLM(LlamaConfig(**common, mlp_bias=False, attn_implementation="eager"))
     m = m.double().eval()
@@ -169,11 +176,16 @@ def _hf_model(s, w, arch):
             L.input_layernorm.weight.copy_(f(lw["in_norm"]))
             L.self_attn.q_proj.weight.copy_(f(lw["q"])); L.self_attn.k_proj.weight.copy_(f(lw["k"]))
             L.self_attn.v_proj.weight.copy_(f(lw["v"])); L.self_attn.o_proj.weight.copy_(f(lw["o"]))
-            if arch == "qwen3":
+            if arch in ("qwen3", "qwen3_moe"):
                 L.self_attn.q_norm.weight.copy_(f(lw["q_norm"])); L.self_attn.k_norm.weight.copy_(f(lw["k_norm"]))
             L.post_attention_layernorm.weight.copy_(f(lw["post_norm"]))
-            L.mlp.gate_proj.weight.copy_(f(lw["gate"])); L.mlp.up_proj.weight.copy_(f(lw["up"]))
-            L.mlp.down_proj.weight.copy_(f(lw["down"]))
+            if arch == "qwen3_moe":   # router [E][H]; experts: gate and up stacked [E][2F][H], down [E][H][F]
+                L.mlp.gate.weight.copy_(f(lw["router"]))
+                L.mlp.experts.gate_up_proj.copy_(torch.cat([f(lw["gate"]), f(lw["up"])], dim=1))
+                L.mlp.experts.down_proj.copy_(f(lw["down"]))
+            else:
+                L.mlp.gate_proj.weight.copy_(f(lw["gate"])); L.mlp.up_proj.weight.copy_(f(lw["up"]))
+                L.mlp.down_proj.weight.copy_(f(lw["down"]))
         m.model.norm.weight.copy_(f(w["final_norm"]))
         if not s.tied_embedding:
             m.lm_head.weight.copy_(f(w["lm_head"]))
@@ -206,6 +218,8 @@ SMALL_QK = synth.Shape("small_qk", 2, 128, 4, 2, 32, 192, 300, True, False, 1e-6
     (SMALL_QK, "qwen3", "uniform"),
     (SMALL_QK.with_(tied_embedding=True, rope_theta=1e6), "qwen3", "uniform"),
     (synth.SHAPES["tiny"].with_(batch=2, ctx_range=(5, 140), ctx=0), "llama", "uniform"),
+    (SMALL_QK.with_(n_experts=6, top_k=2, moe_ffn=48), "qwen3_moe", "uniform"),
+    (SMALL_QK.with_(n_experts=5, top_k=3, moe_ffn=40, norm_topk=False, batch=2), "qwen3_moe", "ones"),
 ])
 def test_decode_step_matches_transformers(shape, arch, gamma):
     inp = synth.make_inputs(shape, seed=3, gamma=gamma)
@@ -235,3 +249,44 @@ def test_oracle_never_reads_poisoned_slots():
     assert torch.isnan(inp["kv"]["k_pool"].float()).any()
     logits, _ = run_oracle(inp)
     assert np.all(np.isfinite(logits))
+
+
+# ---------------------------------------------------------------- mixture of experts
+def test_moe_route_hand_values():
+    # probabilities 0.1, 0.2, 0.3, 0.4 (logits ln 1 .. ln 4): the top 2 are experts 3 and 2
+    lg = np.log(np.array([[1.0, 2.0, 3.0, 4.0]]))
+    ids, w, margin = on.moe_route(lg, 2, True)
+    assert ids.tolist() == [[3, 2]]
+    np.testing.assert_allclose(w, [[0.4 / 0.7, 0.3 / 0.7]], rtol=1e-12)
+    np.testing.assert_allclose(margin, [0.1], rtol=1e-12)
+    ids, w, _ = on.moe_route(lg, 2, False)
+    np.testing.assert_allclose(w, [[0.4, 0.3]], rtol=1e-12)
+    # a tie at the cut goes to the lower expert index; top-k = E has no margin
+    ids, w, margin = on.moe_route(np.array([[0.0, 1.0, 1.0, 0.0]]), 1, True)
+    assert ids.tolist() == [[1]] and margin[0] == 0.0 and w[0, 0] == 1.0
+    _, _, margin = on.moe_route(lg, 4, True)
+    assert margin[0] == np.inf
+
+
+def test_single_expert_moe_is_the_dense_ffn():
+    # one expert chosen with weight 1: exactly the SwiGLU FFN of that expert
+    H, F = 16, 24
+    h = RNG.standard_normal((3, H))
+    g, u, dn = (RNG.standard_normal(sh) * 0.2 for sh in ((1, F, H), (1, F, H), (1, H, F)))
+    out, _, ids, w, _ = on.moe_ffn(h, RNG.standard_normal((1, H)), g, u, dn, 1, True, np.float64)
+    dense = np.stack([on.gemv(on.swiglu(on.gemv(x, g[0]), on.gemv(x, u[0])), dn[0]) for x in h])
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    np.testing.assert_array_equal(out, dense)
+
+
+def test_moe_reads_only_the_chosen_experts():
+    # experts outside each token's top k are NaN: a finite result shows none was used
+    H, F, E = 8, 12, 6
+    h = RNG.standard_normal((2, H))
+    router = RNG.standard_normal((E, H))
+    ids, _, _ = on.moe_route(on.gemv(h, router), 2, True)
+    g, u, dn = (np.full(sh, np.nan) for sh in ((E, F, H), (E, F, H), (E, H, F)))
+    for e in set(ids.ravel().tolist()):
+        g[e], u[e], dn[e] = (RNG.standard_normal(x.shape[1:]) for x in (g, u, dn))
+    out, *_ = on.moe_ffn(h, router, g, u, dn, 2, True, np.float64)
+    assert np.all(np.isfinite(out))
