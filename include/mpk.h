@@ -72,7 +72,16 @@ enum {
   MPK_TASK_FINAL_NORM = 10, /* hf = RMSNorm(s + d) of the last layer                     */
   MPK_TASK_LMHEAD = 11,     /* tile of the LM head: fp32 logits + per-tile (max, argmax) */
   MPK_TASK_ARGMAX = 12,     /* next_ids[b] = argmax over tile partials (lowest index)    */
-  MPK_TASK_EMPTY = 13       /* no compute; inserted by normalisation                     */
+  MPK_TASK_EMPTY = 13,      /* no compute; inserted by normalisation                     */
+  /* mixture-of-experts layers (n_experts > 0) in place of GATEUP / DOWN:      */
+  MPK_TASK_ROUTER = 14,     /* tile of the router: logits [B][E]; at batch 1 also the     */
+                            /* residual add + RMSNorm (tile 0 stores s and h2 and zeroes  */
+                            /* d, which the down tiles add to; at batch > 1 MLP_NORM does) */
+  MPK_TASK_EXPERT_GU = 15,  /* tile of expert slot s (the s-th distinct expert the batch  */
+                            /* chose): gate/up of its tokens' rows, SwiGLU; tile 0 writes */
+                            /* the slot's route record (expert, tokens, weights)          */
+  MPK_TASK_EXPERT_DOWN = 16 /* tile of slot s: down projection, adds weight x output of   */
+                            /* each of the slot's tokens into the layer's output          */
 };
 enum { MPK_MODE_AOT = 0, MPK_MODE_JIT = 1, MPK_MODE_EMPTY = 2 };
 enum { MPK_EVENT_HAS_JIT = 1, MPK_EVENT_HAS_EMPTY = 2 };
@@ -86,6 +95,12 @@ typedef struct {
   int32_t qk_norm;        /* 1: per-head RMSNorm of q and k before RoPE */
   int32_t tied_embedding; /* 1: the LM head is the embedding matrix */
   float rms_eps, rope_theta;
+  /* mixture of experts (0 experts: a dense SwiGLU FFN of width ffn in every
+   * layer).  With n_experts = E > 0 every layer's FFN is E SwiGLU experts of
+   * width moe_ffn: router logits h Wr^T, softmax over the experts, the top_k
+   * most probable (ties to the lower index) weighted by their probabilities,
+   * renormalised over the top_k when norm_topk = 1.  E <= 256, top_k <= 16. */
+  int32_t n_experts, top_k, moe_ffn, norm_topk;
 } mpk_model_cfg;
 
 /* Build parameters; a zero field takes its default (shown).  They are part of
@@ -114,9 +129,11 @@ typedef struct {
                               /* quantum of 32; at most one range per 32 elements), each */
                               /* range writing its own plane of partial sums; t_qkv must */
                               /* be a multiple of n_kv_heads x k_qkv, t_o of k_o, t_down */
-                              /* of k_down (default 1, 3, 3 at batch > 1 -- 1 where a    */
-                              /* given t_o / t_down is not a multiple of 3; 1 at batch  */
-                              /* 1, the only value allowed there)                        */
+                              /* of k_down (default at batch > 1: 1; the largest of 4, 3, */
+                              /* 2 dividing n_kv_heads, so that a range holds whole kv   */
+                              /* groups; 3 -- 1 with experts -- each yielding to a given */
+                              /* t_o / t_down it does not divide; 1 at batch 1, the only */
+                              /* value allowed there)                                    */
   int32_t attn_jit;      /* scheduling policy: 0 default (every task AOT: an attention     */
                          /* task sizes its split from the lengths at run time, so static  */
                          /* placement is balanced), 1 the hybrid policy (attention JIT,  */
@@ -130,6 +147,11 @@ typedef struct {
                           /* an attention split waits for every q/k/v tile, not only its */
                           /* own kv group's (every other operator already waits for the  */
                           /* whole previous one) -- the pages' coarse-graph ablation     */
+  int32_t t_router, t_egu, t_edown; /* mixture of experts: router tiles (default min(E,   */
+                                    /* W / 8) on the column quantum), gate/up and down    */
+                                    /* tiles per expert slot (default about W / slots, more */
+                                    /* while a tile's accumulators exceed the LDS budget); */
+                                    /* a layer has min(E, B x top_k) expert slots          */
   int32_t attn_split_pages; /* at least this many KV pages per attention split when the   */
                             /* step runs (default 1): a request of p pages takes          */
                             /* min(slots, ceil(p / this)) splits at batch 1 (and no more  */
@@ -140,10 +162,12 @@ typedef struct {
 typedef struct mpk_tgraph mpk_tgraph; /* opaque; owned by the library */
 
 /* Weights: device pointers to bf16 arrays, owned by the caller.
- * layer points to a HOST array of n_layers*11 device pointers, per layer in
+ * layer points to a HOST array of n_layers*12 device pointers, per layer in
  * the order in_norm[H], q[hq*d][H], k[hkv*d][H], v[hkv*d][H], q_norm[d],
- * k_norm[d], o[H][hq*d], post_norm[H], gate[F][H], up[F][H], down[H][F]
- * (q_norm/k_norm may be NULL when qk_norm is 0). */
+ * k_norm[d], o[H][hq*d], post_norm[H], gate[F][H], up[F][H], down[H][F],
+ * router (q_norm/k_norm may be NULL when qk_norm is 0; router is NULL for a
+ * dense model).  With n_experts = E > 0: gate[E][Fe][H], up[E][Fe][H],
+ * down[E][H][Fe] (Fe = moe_ffn) and router[E][H]. */
 typedef struct {
   const void* embed;      /* [vocab][H] */
   const void* lm_head;    /* [vocab][H]; NULL when tied (layout 0) */
@@ -369,14 +393,18 @@ int mpk_decode_step_baseline(mpk_tgraph* g, const mpk_weights* w, const int32_t*
 
 /* Copy intermediate tensor `tensor` of the last step to host memory `dst`
  * (`bytes` must equal its size).  All are fp32 [B][...]: ids 3 pmax[B][t_lm]
- * (fp32 value, int32 index pairs); per layer l, 5 + 13*l + k with k = 0 r
+ * (fp32 value, int32 index pairs); per layer l, 5 + 15*l + k with k = 0 r
  * (residual into the layer), 2 qkv (raw projection, group-major: per kv group
  * its query heads, key head, value head; k_qkv planes [k_qkv][B][...] whose
  * sum is the projection), 6 attention partials
  * [kv][s_attn][G][2 + head_dim] (per kv group and slot: max, sum, output;
  * a request's splits occupy consecutive slots), 7 attn, 8 o (k_o planes), 9 s
  * (residual after attention), 11 a, 12 d (k_down planes); at batch > 1 also 0 e[B][H],
- * 1 hf[B][H], and per layer k = 1 h, 10 h2 (the normalised inputs).
+ * 1 hf[B][H], and per layer k = 1 h, 10 h2 (the normalised inputs).  Mixture-of-
+ * experts layers: 10 h2 (also at batch 1), 11 a [slots][B][moe_ffn] (a slot's
+ * rows hold its tokens' SwiGLU outputs), 12 d [B][H] (the weighted expert
+ * sum), 13 router logits [B][E], 14 route records [slots][2 + 2B] (int32
+ * expert, token count, tokens[B], fp32 weights[B]).
  * The ids are the tensors of the graph's regions (MPK summary page, section
  * 2 Q2: events are inferred from the regions tasks read and write), so a
  * test can check every task's output layer by layer.  Synchronises the

@@ -147,15 +147,30 @@ def moe_route(logits, top_k, norm_topk):
     return ids, w, margin
 
 
-def moe_ffn(h, router, gate, up, down, top_k, norm_topk, dtype):
+def moe_ffn(h, router, gate, up, down, top_k, norm_topk, dtype, route_hook=None):
     """Mixture-of-experts SwiGLU FFN of rows ``h [B, H]``: router logits
     ``h router^T``, routing (``moe_route``), then for each token the sum over
     its experts e of ``w_e (silu(h gate_e^T) * (h up_e^T)) down_e^T``.
     ``gate``, ``up``, ``down`` are indexable by expert (``[E][F][H]``,
     ``[E][F][H]``, ``[E][H][F]``); only the chosen experts are read.
+
+    ``route_hook(logits, ids, margin)``, when given, may return other expert
+    ids ``[B, k]`` (or None): a near-tie between the k-th and the (k+1)-th
+    probability has more than one top-k set that is correct up to rounding,
+    and a caller comparing with another implementation takes that one's
+    choice there.  The weights are then the softmax probabilities of the
+    given experts, renormalised like ``moe_route``'s.
     Returns ``(out [B, H], logits, ids, weights, margin)``."""
     logits = gemv(h, widen(router, dtype))
     ids, w, margin = moe_route(logits, top_k, norm_topk)
+    if route_hook is not None:
+        forced = route_hook(logits, ids, margin)
+        if forced is not None:
+            ids = np.asarray(forced, dtype=np.int64)
+            p = softmax(logits)
+            w = np.take_along_axis(p, ids, axis=-1)
+            if norm_topk:
+                w = w / np.sum(w, axis=-1, keepdims=True)
     out = np.zeros_like(h)
     for b in range(h.shape[0]):
         for j in range(top_k):
@@ -187,7 +202,7 @@ def gather_cache(pool_l, page_table_b, n_tokens, page_size, dtype):
 
 
 def decode_step(cfg, weights, token_ids, k_pool, v_pool, page_table, seq_lens, page_size,
-                dtype=np.float32, capture=None):
+                dtype=np.float32, capture=None, route_hook=None):
     """One decode step of the whole batch.
 
     Parameters
@@ -206,6 +221,8 @@ def decode_step(cfg, weights, token_ids, k_pool, v_pool, page_table, seq_lens, p
         position ``L_b``.
     capture : optional dict, filled with per-layer intermediates
         (``capture[l][name]``) and the new cache rows ``k_new``/``v_new``.
+    route_hook : mixture of experts only, optional ``f(l, logits, ids,
+        margin)`` for layer l (see ``moe_ffn``).
 
     Returns ``(logits [B, V], next_ids [B])``.
     """
@@ -250,8 +267,10 @@ def decode_step(cfg, weights, token_ids, k_pool, v_pool, page_table, seq_lens, p
         h2 = rms_norm(s, widen(Wl["post_norm"], dtype), eps)
         moe = {}
         if int(cfg.get("n_experts", 0)) > 0:
+            hook = None if route_hook is None else (lambda lg, i, m, l=l: route_hook(l, lg, i, m))
             dn, rl, ids, wts, margin = moe_ffn(h2, Wl["router"], Wl["gate"], Wl["up"], Wl["down"],
-                                               int(cfg["top_k"]), bool(cfg.get("norm_topk", True)), dtype)
+                                               int(cfg["top_k"]), bool(cfg.get("norm_topk", True)), dtype,
+                                               route_hook=hook)
             a = None
             moe = dict(router_logits=rl, expert_ids=ids, expert_weights=wts, route_margin=margin)
         else:

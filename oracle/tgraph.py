@@ -78,19 +78,23 @@ import numpy as np
 
 # task types (3 and 5 are kept as ids for the generic entry; the decoder emits neither)
 EMBED, ATTN_NORM, QKV, QKNORM_ROPE, ATTN, COMBINE, OPROJ, MLP_NORM, GATEUP, DOWN, FINAL_NORM, LMHEAD, ARGMAX, \
-    EMPTY = range(14)
+    EMPTY, ROUTER, EXPERT_GU, EXPERT_DOWN = range(17)
 TYPE_NAMES = ["EMBED", "ATTN_NORM", "QKV", "QKNORM_ROPE", "ATTN", "COMBINE", "OPROJ", "MLP_NORM", "GATEUP", "DOWN",
-              "FINAL_NORM", "LMHEAD", "ARGMAX", "EMPTY"]
+              "FINAL_NORM", "LMHEAD", "ARGMAX", "EMPTY", "ROUTER", "EXPERT_GU", "EXPERT_DOWN"]
+# tasks whose work is decided by data when the step runs (the attention's
+# splits, the experts a slot serves): JIT under the hybrid policy
+DATA_DEPENDENT = (ATTN, EXPERT_GU, EXPERT_DOWN)
 MODE_AOT, MODE_JIT, MODE_EMPTY = 0, 1, 2
 FLAG_HAS_JIT, FLAG_HAS_EMPTY = 1, 2
 
-# tensors: five shared ones, then 13 per layer
+# tensors: five shared ones, then 15 per layer (rlog and route in mixture-of-experts layers)
 T_E, T_HF, T_LOGITS, T_PMAX, T_NEXT = range(5)
-L_R, L_H, L_QKV, L_Q, L_KC, L_VC, L_PART, L_ATTN, L_O, L_S, L_H2, L_A, L_D = range(13)
+L_R, L_H, L_QKV, L_Q, L_KC, L_VC, L_PART, L_ATTN, L_O, L_S, L_H2, L_A, L_D, L_RLOG, L_ROUTE = range(15)
+N_LAYER_TENSORS = 15
 
 
 def layer_tensor(l, k):
-    return 5 + 13 * l + k
+    return 5 + N_LAYER_TENSORS * l + k
 
 
 @dataclass
@@ -111,6 +115,9 @@ class Params:
     K_o: int = 1
     K_down: int = 1
     fusion: int = 0         # 0: Def 4.1 then Def 4.2; 1: no fusion (one event per overlap edge)
+    T_router: int = 1       # mixture of experts: router tiles, gate/up and down tiles per expert slot
+    T_egu: int = 1
+    T_edown: int = 1
 
 
 def tile_range(N, q, T, n):
@@ -174,6 +181,44 @@ def decompose(cfg, B, P, prm: Params):
     # [plane][b][column]; their readers take all planes
     planes = lambda tn, ks, n: _box(tn, (0, 0, 0), (ks, B, n))
     Kq, Ko, Kd = prm.K_qkv, prm.K_o, prm.K_down
+    E, Kx, Fe = cfg.get("n_experts", 0), cfg.get("top_k", 0), cfg.get("moe_ffn", 0)
+    moe = E > 0
+    M = min(E, B * Kx)        # expert slots of a layer: the distinct experts the batch chose, at most
+
+    def moe_layer(l, t, mid):
+        """The mixture-of-experts FFN of layer l (MPK summary section 5, Fig 10):
+        ROUTER tiles (router logits; at batch 1 they also normalise, and tile
+        0 stores the residual s_l and the normalised h2_l the experts read),
+        then per
+        expert slot s (the s-th distinct expert the batch chose, decided when
+        the step runs) EXPERT_GU tiles (tile 0 also writes the slot's route
+        record: expert, tokens, weights) and EXPERT_DOWN tiles, which add
+        their tokens' weighted outputs into d_l.  A slot's down tiles read only
+        its route record and its gate/up output, so they wait for that slot
+        alone.  d_l starts the step at zero: the task that stores s_l (router
+        tile 0 at batch 1, MLP_NORM b at batch > 1, row b) zeroes it, with the
+        same readers as s_l, so the zeroing adds no event."""
+        for n in range(prm.T_router):
+            elo, ehi = tile_range(E, prm.q, prm.T_router, n)
+            outs = [_box(t(L_RLOG), (0, elo), (B, ehi))]
+            if fused and n == 0:
+                outs += [full(t(L_S), H), full(t(L_H2), H), planes(t(L_D), 1, H)]
+            add(ROUTER, l, (n,), mid if fused else [full(t(L_H2), H)], outs)
+        rec = 2 + 2 * B
+        for s_ in range(M):
+            for n in range(prm.T_egu):
+                lo, hi = tile_range(Fe, prm.q, prm.T_egu, n)
+                outs = [_box(t(L_A), (s_, 0, lo), (s_ + 1, B, hi))]
+                if n == 0:
+                    outs.append(_box(t(L_ROUTE), (s_, 0), (s_ + 1, rec)))
+                add(EXPERT_GU, l, (s_, n), [full(t(L_RLOG), E), full(t(L_H2), H)], outs)
+        for s_ in range(M):
+            for n in range(prm.T_edown):
+                lo, hi = tile_range(H, prm.q, prm.T_edown, n)
+                add(EXPERT_DOWN, l, (s_, n), [_box(t(L_ROUTE), (s_, 0), (s_ + 1, rec)),
+                                              _box(t(L_A), (s_, 0, 0), (s_ + 1, B, Fe))],
+                    [_box(t(L_D), (0, 0, lo), (1, B, hi))])
+
     if not fused:
         for b in range(B):
             add(EMBED, -1, (b,), [], [row(T_E, b, H)])
@@ -215,7 +260,11 @@ def decompose(cfg, B, P, prm: Params):
         mid = [full(t(L_R), H), planes(t(L_O), Ko, H)]
         if not fused:
             for b in range(B):
-                add(MLP_NORM, l, (b,), mid, [row(t(L_S), b, H), row(t(L_H2), b, H)])
+                add(MLP_NORM, l, (b,), mid, [row(t(L_S), b, H), row(t(L_H2), b, H)]
+                    + ([_box(t(L_D), (0, b, 0), (1, b + 1, H))] if moe else []))
+        if moe:
+            moe_layer(l, t, mid)
+            continue
         for n in range(prm.T_gu):
             lo, hi = tile_range(F, prm.q, prm.T_gu, n)
             outs = [_box(t(L_A), (0, lo), (B, hi))]
@@ -389,7 +438,8 @@ def canonicalize(tasks, W, jit_attn=True, jit_all=False, fusion=FUSION_A):
     eorder = sorted(range(NE), key=lambda e: new_ev[e])
     # JIT tasks are handed over when their event fires; the root event is
     # never triggered, so its consumers stay AOT under every policy
-    mode = {EMPTY: MODE_EMPTY, ATTN: MODE_JIT if jit_attn or jit_all else MODE_AOT}
+    mode = {EMPTY: MODE_EMPTY}
+    mode.update({ty: MODE_JIT if jit_attn or jit_all else MODE_AOT for ty in DATA_DEPENDENT})
     other = MODE_JIT if jit_all else MODE_AOT
 
     def mode_of(t):
@@ -481,10 +531,11 @@ def check_semantics(g, tasks=None, closure=True):
     # are attention tasks, all of one mode (JIT or AOT), or every other
     # non-empty task is JIT
     assert np.all((md == MODE_EMPTY) == (tt == EMPTY)) and np.all(md[dep == root] != MODE_JIT), "modes: empty/JIT modes"
-    if np.any((md == MODE_JIT) & (tt != ATTN)):
+    dd = np.isin(tt, DATA_DEPENDENT)
+    if np.any((md == MODE_JIT) & ~dd):
         assert np.all(md[(tt != EMPTY) & (dep != root)] == MODE_JIT), "modes: mixed JIT policy"
     else:
-        assert len(set(md[(tt == ATTN) & (dep != root)].tolist())) <= 1, "modes: mixed attention modes"
+        assert len(set(md[dd & (dep != root)].tolist())) <= 1, "modes: mixed attention modes"
     for e in range(NE):
         cons = md[first[e]:last[e] + 1]
         f = (FLAG_HAS_JIT if np.any(cons == MODE_JIT) else 0) | (FLAG_HAS_EMPTY if np.any(cons == MODE_EMPTY) else 0)

@@ -18,7 +18,9 @@ MPK_OK = 0
 ERRORS = {-1: "MPK_ERR_INVALID_ARG", -2: "MPK_ERR_UNSUPPORTED", -3: "MPK_ERR_HIP", -4: "MPK_ERR_GRAPH",
           -5: "MPK_ERR_TIMEOUT", -6: "MPK_ERR_NOMEM"}
 (TASK_EMBED, TASK_ATTN_NORM, TASK_QKV, TASK_QKNORM_ROPE, TASK_ATTN, TASK_COMBINE, TASK_OPROJ, TASK_MLP_NORM,
- TASK_GATEUP, TASK_DOWN, TASK_FINAL_NORM, TASK_LMHEAD, TASK_ARGMAX, TASK_EMPTY) = range(14)
+ TASK_GATEUP, TASK_DOWN, TASK_FINAL_NORM, TASK_LMHEAD, TASK_ARGMAX, TASK_EMPTY, TASK_ROUTER, TASK_EXPERT_GU,
+ TASK_EXPERT_DOWN) = range(17)
+LAYER_TENSORS = 15   # per-layer tensor ids: 5 + LAYER_TENSORS * layer + kind (mpk_read_tensor)
 
 
 class MpkError(RuntimeError):
@@ -30,13 +32,15 @@ class MpkError(RuntimeError):
 class mpk_model_cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
                                          "max_seq_len", "qk_norm", "tied_embedding")] + \
-               [("rms_eps", C.c_float), ("rope_theta", C.c_float)]
+               [("rms_eps", C.c_float), ("rope_theta", C.c_float)] + \
+               [(n, C.c_int32) for n in ("n_experts", "top_k", "moe_ffn", "norm_topk")]
 
 
 class mpk_build_params(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("n_workers", "n_sched_waves", "quantum", "t_qkv", "t_o", "t_gu", "t_down",
                                          "t_lm", "s_attn", "host_only", "fusion_order", "aot_policy", "k_qkv", "k_o", "k_down",
-                                         "attn_jit", "weight_preload", "coarse_events", "attn_split_pages")]
+                                         "attn_jit", "weight_preload", "coarse_events", "t_router", "t_egu",
+                                         "t_edown", "attn_split_pages")]
 
 
 class mpk_weights(C.Structure):
@@ -144,10 +148,12 @@ def _check(rc):
 def model_cfg(shape) -> mpk_model_cfg:
     """mpk_model_cfg from any object/dict with the decoder fields."""
     g = (lambda k: shape[k]) if isinstance(shape, dict) else (lambda k: getattr(shape, k))
+    opt = (lambda k, d: shape.get(k, d)) if isinstance(shape, dict) else (lambda k, d: getattr(shape, k, d))
     return mpk_model_cfg(int(g("n_layers")), int(g("hidden")), int(g("n_q_heads")), int(g("n_kv_heads")),
                          int(g("head_dim")), int(g("ffn")), int(g("vocab")), int(g("max_seq_len")),
                          int(bool(g("qk_norm"))), int(bool(g("tied_embedding"))), float(g("rms_eps")),
-                         float(g("rope_theta")))
+                         float(g("rope_theta")), int(opt("n_experts", 0)), int(opt("top_k", 0)),
+                         int(opt("moe_ffn", 0)), int(bool(opt("norm_topk", True))))
 
 
 def _view_to_dict(v: mpk_tgraph_host_view) -> dict:
@@ -197,12 +203,13 @@ def _ptr(t):
 
 class Weights:
     """mpk_weights over a dict of bf16 device tensors (the synth layout)."""
-    NAMES = ("in_norm", "q", "k", "v", "q_norm", "k_norm", "o", "post_norm", "gate", "up", "down")
+    NAMES = ("in_norm", "q", "k", "v", "q_norm", "k_norm", "o", "post_norm", "gate", "up", "down", "router")
 
     def __init__(self, w: dict):
         self._keep = w
         layers = w["layers"]
-        self._arr = (C.c_void_p * (len(layers) * 11))(*[int(lw[n].data_ptr()) for lw in layers for n in self.NAMES])
+        self._arr = (C.c_void_p * (len(layers) * 12))(*[int(lw[n].data_ptr()) if lw.get(n) is not None else 0
+                                                          for lw in layers for n in self.NAMES])
         self.s = mpk_weights(int(w["embed"].data_ptr()), 0 if w.get("lm_head") is None else int(w["lm_head"].data_ptr()),
                              int(w["final_norm"].data_ptr()), C.cast(self._arr, C.POINTER(C.c_void_p)), 0)
 
@@ -219,7 +226,7 @@ class PreparedWeights:
         _check(lib().mpk_prepared_weights_bytes(g.h, C.byref(n)))
         self.buf = torch.empty(max(1, n.value), dtype=torch.uint8, device="cuda")
         n_layers = g.cfg.n_layers
-        self._arr = (C.c_void_p * (n_layers * 11))()
+        self._arr = (C.c_void_p * (n_layers * 12))()
         self.s = mpk_weights()
         _check(lib().mpk_prepare_weights(g.h, C.byref(w.s), C.c_void_p(self.buf.data_ptr()), n.value,
                                          C.cast(self._arr, C.POINTER(C.c_void_p)), C.byref(self.s), _stream_ptr(stream)))

@@ -58,6 +58,13 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   // steps (the attention output, hq x d, always is)
   if (B > 1 && (c.hidden % 32 || c.ffn % 32)) return uns("at batch > 1, hidden and ffn must be multiples of 32");
   if (P != 16 && P != 32 && P != 64) return uns("page_size must be 16, 32 or 64");
+  if (c.n_experts < 0 || c.n_experts > 256) return uns("n_experts must be in 0..256");
+  if (c.n_experts > 0) {
+    if (c.top_k < 1 || c.top_k > 16 || c.top_k > c.n_experts) return uns("top_k must be in 1..min(16, n_experts)");
+    if (c.moe_ffn < 8 || c.moe_ffn % 8 || (B > 1 && c.moe_ffn % 32))
+      return uns("moe_ffn must be a positive multiple of 8 (of 32 at batch > 1)");
+    if (c.norm_topk != 0 && c.norm_topk != 1) return bad("norm_topk must be 0 or 1");
+  }
   mpk_build_params z = {};
   const mpk_build_params& p = in ? *in : z;
   if (p.fusion_order < 0 || p.fusion_order > 1) return uns("fusion_order must be 0 (Def 4.1 then Def 4.2) or 1 (none)");
@@ -103,8 +110,17 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   // narrow column tiles gain nothing from it; a tile count given without its
   // k-split keeps the default only if it divides)
   r.K_qkv = p.k_qkv > 0 ? p.k_qkv : 1;
-  r.K_o = p.k_o > 0 ? p.k_o : (B > 1 && (p.t_o <= 0 || p.t_o % 3 == 0) ? 3 : 1);
-  r.K_down = p.k_down > 0 ? p.k_down : (B > 1 && (p.t_down <= 0 || p.t_down % 3 == 0) ? 3 : 1);
+  // (the O projection's k-ranges follow the kv groups: with K_o dividing
+  // n_kv_heads an attention task feeds one range, so its tiles trigger one
+  // event and the graph stays narrow -- K_o = 3 over 8 groups gave 13% empty
+  // tasks at the 8B shape, batch 16, against 5% with 4)
+  int32_t ko_def = 1;
+  for (int32_t k = 4; k >= 2; --k)
+    if (c.n_kv_heads % k == 0 && (p.t_o <= 0 || p.t_o % k == 0)) { ko_def = k; break; }
+  r.K_o = p.k_o > 0 ? p.k_o : (B > 1 ? ko_def : 1);
+  r.K_down = p.k_down > 0 ? p.k_down : (B > 1 && c.n_experts == 0 && (p.t_down <= 0 || p.t_down % 3 == 0) ? 3 : 1);
+  if (c.n_experts > 0 && r.K_down != 1)
+    return uns("k_down must be 1 with experts (their outputs accumulate into one plane)");
   if (B == 1 && (r.K_qkv != 1 || r.K_o != 1 || r.K_down != 1))
     return uns("k-splits need batch > 1 (a batch-1 tile stages its whole input)");
   if (r.K_qkv > cdiv(H, 32) || r.K_o > cdiv((int64_t)c.n_q_heads * d, 32) || r.K_down > cdiv(F, 32))
@@ -131,6 +147,32 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   r.T_down = dflt(p.t_down, H, 1, r.K_down);
   r.T_lm = dflt(p.t_lm, V, 1, 1);
   if (r.T_o < 0 || r.T_down < 0) return bad("t_o / t_down must be multiples of k_o / k_down");
+  if (c.n_experts > 0) {
+    // mixture of experts: router tiles on the column quantum (about W / 8);
+    // per expert slot, gate/up and down tiles of about W / slots, more while a
+    // tile's accumulators (columns x rows per column x batch) exceed the budget
+    const int64_t E = c.n_experts, Fe = c.moe_ffn, M = moe_slots(c, B);
+    auto per_slot = [&](int32_t v, int64_t N, int64_t rpc) {
+      if (v > 0) return (int64_t)v;
+      const int64_t U = cdiv(N, r.q), step = std::max<int64_t>(1, r.W / M);
+      int64_t T = std::min<int64_t>(step, U);
+      while (T < U && r.q * cdiv(U, T) * rpc * B > kMaxTileAcc) T = std::min<int64_t>(U, T + step);
+      return T;
+    };
+    const int64_t Tr = p.t_router > 0 ? p.t_router : std::min<int64_t>(cdiv(E, r.q), std::max<int64_t>(1, r.W / 8));
+    const int64_t Tg = per_slot(p.t_egu, Fe, 2), Td = per_slot(p.t_edown, H, 1);
+    struct { int64_t T, N, rpc; const char* name; } moe_ops[] = {
+        {Tr, E, 1, "t_router"}, {Tg, Fe, 2, "t_egu"}, {Td, H, 1, "t_edown"}};
+    for (auto& o : moe_ops) {
+      if (o.T < 1 || o.T > cdiv(o.N, r.q)) { *err = std::string(o.name) + ": tile count out of range"; return MPK_ERR_INVALID_ARG; }
+      if (r.q * cdiv(cdiv(o.N, r.q), o.T) * o.rpc * B > kMaxTileAcc) {
+        *err = std::string(o.name) + ": tile too wide (columns x rows x batch must stay within 8192 accumulators)";
+        return MPK_ERR_UNSUPPORTED;
+      }
+    }
+    if (M * std::max(Tg, Td) > 65535) return uns("more than 65535 expert tiles per layer");
+    r.T_router = (int32_t)Tr; r.T_egu = (int32_t)Tg; r.T_edown = (int32_t)Td;
+  }
   int64_t max_pages = cdiv(c.max_seq_len, P);
   // S_attn = M, the attention slots of a kv group (dealt to the requests by
   // page count when the step runs); at batch 1 they are the splits
@@ -192,6 +234,44 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
   // [plane][b][column]; their readers take all planes
   auto planes = [&](int32_t tensor, int32_t k, int32_t n) { return box(tensor, {0, 0, 0}, {k, B, n}); };
   const int32_t Kq = p.K_qkv, Ko = p.K_o, Kd = p.K_down;
+  const int32_t E = c.n_experts, Fe = c.moe_ffn, M = moe_slots(c, B), rec = route_words(B);
+  const bool moe = E > 0;
+  // The mixture-of-experts FFN of layer l: ROUTER tiles (logits; at batch 1
+  // also the residual add + RMSNorm, tile 0 storing s_l and h2_l), then per
+  // expert slot s EXPERT_GU tiles (tile 0 writes the slot's route record)
+  // and EXPERT_DOWN tiles, which add into d_l and read only their slot's
+  // record and gate/up output.  d_l starts the step at zero: the task that
+  // stores s_l (router tile 0 at batch 1, MLP_NORM b at batch > 1, row b)
+  // zeroes it; d_l and s_l have the same readers, so this adds no event.
+  auto moe_layer = [&](int32_t l, const std::vector<Box>& mid) {
+    auto t = [&](int32_t k) { return layer_tensor(l, k); };
+    for (int32_t n = 0; n < p.T_router; ++n) {
+      int32_t elo, ehi;
+      tile_range(E, p.q, p.T_router, n, &elo, &ehi);
+      std::vector<Box> outs = {box(t(L_RLOG), {0, elo}, {B, ehi})};
+      if (fused && n == 0) {
+        outs.push_back(full(t(L_S), H));
+        outs.push_back(full(t(L_H2), H));
+        outs.push_back(planes(t(L_D), 1, H));
+      }
+      add(MPK_TASK_ROUTER, l, n, 0, 0, fused ? mid : std::vector<Box>{full(t(L_H2), H)}, outs);
+    }
+    for (int32_t s = 0; s < M; ++s)
+      for (int32_t n = 0; n < p.T_egu; ++n) {
+        int32_t lo, hi;
+        tile_range(Fe, p.q, p.T_egu, n, &lo, &hi);
+        std::vector<Box> outs = {box(t(L_A), {s, 0, lo}, {s + 1, B, hi})};
+        if (n == 0) outs.push_back(box(t(L_ROUTE), {s, 0}, {s + 1, rec}));
+        add(MPK_TASK_EXPERT_GU, l, s, n, 0, {full(t(L_RLOG), E), full(t(L_H2), H)}, outs);
+      }
+    for (int32_t s = 0; s < M; ++s)
+      for (int32_t n = 0; n < p.T_edown; ++n) {
+        int32_t lo, hi;
+        tile_range(H, p.q, p.T_edown, n, &lo, &hi);
+        add(MPK_TASK_EXPERT_DOWN, l, s, n, 0, {box(t(L_ROUTE), {s, 0}, {s + 1, rec}), box(t(L_A), {s, 0, 0}, {s + 1, B, Fe})},
+            {box(t(L_D), {0, 0, lo}, {1, B, hi})});
+      }
+  };
   if (!fused)
     for (int32_t b = 0; b < B; ++b) add(MPK_TASK_EMBED, -1, b, 0, 0, {}, {row(T_E, b, H)});
   for (int32_t l = 0; l < L; ++l) {
@@ -239,7 +319,15 @@ void decompose(const mpk_model_cfg& c, int32_t B, const Params& p, std::vector<T
     }
     const std::vector<Box> mid = {full(t(L_R), H), planes(t(L_O), Ko, H)};
     if (!fused)
-      for (int32_t b = 0; b < B; ++b) add(MPK_TASK_MLP_NORM, l, b, 0, 0, mid, {row(t(L_S), b, H), row(t(L_H2), b, H)});
+      for (int32_t b = 0; b < B; ++b) {
+        std::vector<Box> outs = {row(t(L_S), b, H), row(t(L_H2), b, H)};
+        if (moe) outs.push_back(box(t(L_D), {0, b, 0}, {1, b + 1, H}));
+        add(MPK_TASK_MLP_NORM, l, b, 0, 0, mid, outs);
+      }
+    if (moe) {
+      moe_layer(l, mid);
+      continue;
+    }
     for (int32_t n = 0; n < p.T_gu; ++n) {
       int32_t lo, hi;
       tile_range(F, p.q, p.T_gu, n, &lo, &hi);
@@ -409,10 +497,13 @@ int canonicalize(const std::vector<TaskDef>& tasks, int32_t W, int jit, int fusi
   for (int32_t e = 0; e < NE; ++e) eorder[new_ev[e]] = e;
   // (JIT tasks are handed over when their event fires; the root event is
   // never triggered, so its consumers stay AOT under every policy)
+  // (attention splits and expert tiles are the tasks whose work is decided by
+  // data when the step runs: JIT under the hybrid policy)
   auto mode_of = [jit, root](int32_t type, int32_t dep_ev) {
-    return type == MPK_TASK_EMPTY                                          ? MPK_MODE_EMPTY
-           : dep_ev != root && (jit == 2 || (type == MPK_TASK_ATTN && jit == 1)) ? MPK_MODE_JIT
-                                                                           : MPK_MODE_AOT;
+    const bool dd = type == MPK_TASK_ATTN || type == MPK_TASK_EXPERT_GU || type == MPK_TASK_EXPERT_DOWN;
+    return type == MPK_TASK_EMPTY                                   ? MPK_MODE_EMPTY
+           : dep_ev != root && (jit == 2 || (dd && jit == 1)) ? MPK_MODE_JIT
+                                                                    : MPK_MODE_AOT;
   };
   g.task_type.resize(NT); g.task_mode.resize(NT); g.task_layer.resize(NT); g.task_coords.resize(3 * (size_t)NT);
   g.task_orig.resize(NT); g.task_dep.resize(NT); g.task_trig.resize(NT); g.task_worker.assign(NT, -1);

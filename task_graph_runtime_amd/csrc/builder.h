@@ -40,6 +40,7 @@ struct Params {
   bool coarse = false;    // operator-level graph: attention waits for all q/k/v tiles
   int32_t fusion = 0;     // 0: Def 4.1 then Def 4.2; 1: none (one event per overlap edge)
   int32_t split_pages = 2;  // minimum KV pages per attention split (run time)
+  int32_t T_router = 1, T_egu = 1, T_edown = 1;   // mixture of experts
   int32_t K_qkv = 1, K_o = 1, K_down = 1;   // k-splits (batch > 1)
 };
 
@@ -57,10 +58,18 @@ struct Graph {
   std::vector<uint32_t> aot_offsets, aot_tasks;
 };
 
-// Tensor ids of the decoder: 5 shared, then 13 per layer.
+// Tensor ids of the decoder: 5 shared, then 15 per layer (router logits and
+// route records in mixture-of-experts layers).
 enum { T_E = 0, T_HF = 1, T_LOGITS = 2, T_PMAX = 3, T_NEXT = 4 };
-enum { L_R = 0, L_H, L_QKV, L_Q, L_KC, L_VC, L_PART, L_ATTN, L_O, L_S, L_H2, L_A, L_D, L_COUNT };
-inline int32_t layer_tensor(int32_t l, int32_t k) { return 5 + 13 * l + k; }
+enum { L_R = 0, L_H, L_QKV, L_Q, L_KC, L_VC, L_PART, L_ATTN, L_O, L_S, L_H2, L_A, L_D, L_RLOG, L_ROUTE, L_COUNT };
+inline int32_t layer_tensor(int32_t l, int32_t k) { return 5 + L_COUNT * l + k; }
+
+// Expert slots of a mixture-of-experts layer (0 for a dense model), and the
+// words of a slot's route record: expert, token count, tokens[B], weights[B].
+inline int32_t moe_slots(const mpk_model_cfg& c, int32_t B) {
+  return c.n_experts > 0 ? (c.n_experts < B * c.top_k ? c.n_experts : B * c.top_k) : 0;
+}
+inline int32_t route_words(int32_t B) { return 2 + 2 * B; }
 
 // Balanced tile n of T over N columns on a quantum of q columns.
 inline void tile_range(int64_t N, int64_t q, int64_t T, int64_t n, int32_t* lo, int32_t* hi) {

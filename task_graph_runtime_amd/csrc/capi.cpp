@@ -182,6 +182,10 @@ void fill_descriptors(mpk_tgraph* t) {
         break;
       case MPK_TASK_LMHEAD: tile_range(c.vocab, p.q, p.T_lm, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
       case MPK_TASK_ATTN: d.a0 = c0; d.a1 = c1; d.a2 = p.K_qkv; break;
+      // (router tile n: expert columns, a2 = n; expert tiles (slot s, tile n): columns, a2 = s)
+      case MPK_TASK_ROUTER: tile_range(c.n_experts, p.q, p.T_router, c0, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_EXPERT_GU: tile_range(c.moe_ffn, p.q, p.T_egu, c1, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
+      case MPK_TASK_EXPERT_DOWN: tile_range(c.hidden, p.q, p.T_edown, c1, &lo, &hi); d.a0 = lo; d.a1 = hi; d.a2 = c0; break;
       default: d.a0 = c0; d.a1 = c1; d.a2 = c2; break;
     }
   }
@@ -247,8 +251,10 @@ void build_op_lists(mpk_tgraph* t, std::vector<int32_t>* flat) {
 int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KArgs* a) {
   auto chunks = [](int64_t b) { return (b + 1023) & ~(int64_t)1023; };
   const int64_t H = c.hidden, F = c.ffn, d = c.head_dim, hq = c.n_q_heads, hkv = c.n_kv_heads, G = hq / hkv;
-  const bool fused = fused_norm(B);
-  int64_t stage = fused ? std::max({chunks(H * 4), chunks(hq * d * 4), chunks(F * 4), 2 * chunks(H * 4) + chunks(H * 2)})
+  const bool fused = fused_norm(B), moe = c.n_experts > 0;
+  // (a mixture-of-experts model has no dense FFN: its widths are the experts')
+  const int64_t Fd = moe ? c.moe_ffn : F;
+  int64_t stage = fused ? std::max({chunks(H * 4), chunks(hq * d * 4), chunks(Fd * 4), 2 * chunks(H * 4) + chunks(H * 2)})
                         : chunks(H * 2) + (1 + std::max(p.K_o, p.K_down)) * chunks(H * 4);
   // (batch > 1: a norm task's gain, its residual row and the k-split planes it adds)
   // attention: wavefront merge states, raw q/k/v row, processed heads
@@ -262,17 +268,23 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
   // accumulators: the widest projection tile, rows per column x batch
   const int64_t tpg = p.T_qkv / hkv, Sg = (G + 2) * d;
   auto widest = [&](int64_t N, int64_t T) { return p.q * ((((N + p.q - 1) / p.q) + T - 1) / T); };
-  const int64_t acc = chunks(4 * B * std::max({widest(Sg, tpg / p.K_qkv), widest(H, p.T_o / p.K_o),
-                                               2 * widest(F, p.T_gu), widest(H, p.T_down / p.K_down),
+  int64_t widest_ffn = moe ? std::max({widest(c.n_experts, p.T_router), 2 * widest(c.moe_ffn, p.T_egu),
+                                         widest(H, p.T_edown)})
+                            : std::max(2 * widest(F, p.T_gu), widest(H, p.T_down / p.K_down));
+  const int64_t acc = chunks(4 * B * std::max({widest(Sg, tpg / p.K_qkv), widest(H, p.T_o / p.K_o), widest_ffn,
                                                widest(c.vocab, p.T_lm)}));
   const int64_t max_pages = std::min<int64_t>((c.max_seq_len + P - 1) / P, 4096);
   const int64_t pid = kLdsBytes - kLdsTop - chunks(4 * max_pages);
+  // (an expert tile's routing area under the page ids: both are live only while such a task runs, and
+  // neither may share the pre-load area, which holds the next task's weights while a JIT task runs)
+  const int64_t top = moe ? pid - chunks((int64_t)sizeof(MoeLds)) : pid;
   const int64_t pf = stage + acc;
-  if (pf > pid) return fail(MPK_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
+  if (pf > top) return fail(MPK_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
   a->lds_acc = (int32_t)stage;
   a->lds_pf = (int32_t)pf;
   a->lds_pid = (int32_t)pid;
-  a->pf_segs = fused && p.preload ? (int32_t)std::min<int64_t>(kMaxPfSegs, (pid - pf) / (kPfWaves * 1024)) : 0;
+  a->lds_moe = (int32_t)top;
+  a->pf_segs = fused && p.preload ? (int32_t)std::min<int64_t>(kMaxPfSegs, (top - pf) / (kPfWaves * 1024)) : 0;
   return MPK_OK;
 }
 
@@ -401,8 +413,13 @@ int upload(mpk_tgraph* t) {
   const int64_t B = t->B, H = c.hidden, L = c.n_layers, hq = c.n_q_heads, hkv = c.n_kv_heads, d = c.head_dim;
   const int64_t G = hq / hkv, Sg = (G + 2) * d, F = c.ffn, S_at = t->prm.S_attn;
   KArgs& a = t->base;
+  const bool moe = c.n_experts > 0;
+  const int64_t M = moe_slots(c, t->B);
   a.st_bh = B * H; a.st_q = B * hq * d; a.st_part = hkv * S_at * G * (d + 2);
-  a.st_a = B * F;
+  a.st_a = moe ? M * B * c.moe_ffn : B * F;
+  a.E = c.n_experts; a.topk = c.top_k; a.Fe = c.moe_ffn; a.norm_topk = c.norm_topk; a.M = (int32_t)M;
+  a.st_rlog = moe ? B * c.n_experts : 0;
+  a.st_route = moe ? M * route_words(t->B) : 0;
   // k-split projections write K planes [K][B][...] whose sum is the output
   a.Kq = t->prm.K_qkv; a.Ko = t->prm.K_o; a.Kd = t->prm.K_down;
   a.st_qkv = a.Kq * B * hkv * Sg; a.st_o = a.Ko * a.st_bh; a.st_dn = a.Kd * a.st_bh;
@@ -412,9 +429,12 @@ int upload(mpk_tgraph* t) {
   std::vector<Item> items = {{T_PMAX, B * (int64_t)t->prm.T_lm * 8}};
   if (!fused) items.insert(items.begin(), {{T_E, B * H * 4}, {T_HF, B * H * 4}});
   const int64_t nf = fused ? 0 : 1;
+  // (h2 exists at batch > 1, and at batch 1 in mixture-of-experts layers, whose router tile 0 writes it)
+  const int64_t nh2 = (!fused || moe) ? 1 : 0;
   const int64_t per_layer_bytes[L_COUNT] = {a.st_bh * 4, nf * a.st_bh * 4, a.st_qkv * 4, 0, 0, 0,
                                             a.st_part * 4, a.st_q * 4, a.st_o * 4, a.st_bh * 4,
-                                            nf * a.st_bh * 4, a.st_a * 4, a.st_dn * 4};
+                                            nh2 * a.st_bh * 4, a.st_a * 4, a.st_dn * 4,
+                                            a.st_rlog * 4, a.st_route * 4};
   // one contiguous [L][...] block per per-layer tensor kind
   int64_t off = 0;
   std::vector<int64_t> shared_off(5, -1), kind_off(L_COUNT, -1);
@@ -443,7 +463,9 @@ int upload(mpk_tgraph* t) {
   a.h2 = kind(L_H2);
   a.a = kind(L_A);
   a.dn = kind(L_D);
-  t->tensors.assign(5 + 13 * (size_t)L, {nullptr, 0});
+  a.rlog = kind(L_RLOG);
+  a.route = (int32_t*)kind(L_ROUTE);
+  t->tensors.assign(5 + L_COUNT * (size_t)L, {nullptr, 0});
   for (auto& it : items) t->tensors[it.id] = {ab + shared_off[it.id], it.bytes};
   for (int64_t l = 0; l < L; ++l)
     for (int k = 0; k < L_COUNT; ++k)
@@ -531,6 +553,9 @@ TaskPtrs host_task_ptrs(const DevTask& d, const std::vector<const void*>& wl, co
     case MPK_TASK_MLP_NORM: r.p0 = W(W_POST_NORM); break;
     case MPK_TASK_FINAL_NORM: r.p0 = (const uint16_t*)fnorm; break;
     case MPK_TASK_ATTN: r.p0 = W(W_Q_NORM); r.p1 = W(W_K_NORM); break;
+    case MPK_TASK_ROUTER: r.p0 = W(W_ROUTER); r.p3 = W(W_POST_NORM); break;
+    case MPK_TASK_EXPERT_GU: r.p0 = W(W_GATE); r.p1 = W(W_UP); break;
+    case MPK_TASK_EXPERT_DOWN: r.p0 = W(W_DOWN); break;
     default: break;
   }
   return r;
@@ -565,7 +590,7 @@ int step_args(mpk_tgraph* t, const mpk_weights* w, const int32_t* token_ids, con
   for (int32_t l = 0; l < c.n_layers; ++l)
     for (int k = 0; k < LAYER_PTRS; ++k) {
       const void* p = wl[(size_t)l * LAYER_PTRS + k];
-      bool optional = (k == W_Q_NORM || k == W_K_NORM) && !c.qk_norm;
+      bool optional = ((k == W_Q_NORM || k == W_K_NORM) && !c.qk_norm) || (k == W_ROUTER && c.n_experts == 0);
       if (!p && !optional) return fail(MPK_ERR_INVALID_ARG, "missing layer weight pointer");
       if (((uintptr_t)p & 15) != 0) return fail(MPK_ERR_INVALID_ARG, "weights must be 16-byte aligned");
     }
@@ -665,6 +690,7 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   r.k_qkv = prm.K_qkv; r.k_o = prm.K_o; r.k_down = prm.K_down;
   r.fusion_order = prm.fusion;
   r.attn_split_pages = prm.split_pages;
+  if (cfg->n_experts > 0) { r.t_router = prm.T_router; r.t_egu = prm.T_egu; r.t_edown = prm.T_edown; }
   t->resolved = r;
   std::vector<TaskDef> tasks;
   decompose(*cfg, batch, prm, &tasks);
@@ -715,7 +741,8 @@ int mpk_build_generic_ex(const mpk_task_spec* specs, int32_t n_tasks, const mpk_
   if (jit < 0) return fail(MPK_ERR_INVALID_ARG, "attn_jit must be 0, 1, 2 or 3");
   std::vector<TaskDef> tasks(n_tasks);
   for (int32_t i = 0; i < n_tasks; ++i) {
-    if (specs[i].type < 0 || specs[i].type >= MPK_TASK_EMPTY) return fail(MPK_ERR_INVALID_ARG, "bad task type");
+    if (specs[i].type < 0 || specs[i].type == MPK_TASK_EMPTY || specs[i].type > MPK_TASK_EXPERT_DOWN)
+      return fail(MPK_ERR_INVALID_ARG, "bad task type");
     tasks[i].type = specs[i].type; tasks[i].layer = specs[i].layer;
     tasks[i].c[0] = specs[i].c0; tasks[i].c[1] = specs[i].c1; tasks[i].c[2] = specs[i].c2;
   }
@@ -811,6 +838,7 @@ int mpk_prepare_weights(const mpk_tgraph* g, const mpk_weights* in, void* dst, s
     return fail(MPK_ERR_INVALID_ARG, "null argument");
   if (in->layout != 0) return fail(MPK_ERR_INVALID_ARG, "the input weights must be layout 0");
   if (g->B == 1) return fail(MPK_ERR_UNSUPPORTED, "batch-1 graphs stream whole weight rows: nothing to prepare");
+  if (g->cfg.n_experts > 0) return fail(MPK_ERR_UNSUPPORTED, "prepared weights are not implemented for expert layers");
   if (g->prm.q % 16) return fail(MPK_ERR_UNSUPPORTED, "prepared weights need a column quantum that is a multiple of 16");
   if (((uintptr_t)dst & 255) != 0) return fail(MPK_ERR_INVALID_ARG, "dst must be 256-byte aligned");
   const mpk_model_cfg& c = g->cfg;
@@ -878,9 +906,10 @@ int mpk_decode_step_noalloc(mpk_tgraph* g, const mpk_weights* w, const int32_t* 
   rebase(a.jit_ring, g->d_rt, g->rt_bytes, rt);
   rebase(a.state, g->d_rt, g->rt_bytes, rt);
   rebase(a.arrive, g->d_rt, g->rt_bytes, rt);
-  for (float** p : {&a.e, &a.hf, &a.r, &a.h, &a.qkv, &a.part, &a.attn, &a.o, &a.s, &a.h2, &a.a, &a.dn})
+  for (float** p : {&a.e, &a.hf, &a.r, &a.h, &a.qkv, &a.part, &a.attn, &a.o, &a.s, &a.h2, &a.a, &a.dn, &a.rlog})
     rebase(*p, g->d_act, g->act_bytes, act);
   rebase(a.pmax, g->d_act, g->act_bytes, act);
+  rebase(a.route, g->d_act, g->act_bytes, act);
   a.trace = nullptr;
   a.trace_count = nullptr;
   a.trace_cap = 0;

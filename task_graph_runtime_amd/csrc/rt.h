@@ -94,8 +94,8 @@ struct PMax {
   int32_t i;
 };
 
-enum { LAYER_PTRS = 11 };
-enum { W_IN_NORM = 0, W_Q, W_K, W_V, W_Q_NORM, W_K_NORM, W_O, W_POST_NORM, W_GATE, W_UP, W_DOWN };
+enum { LAYER_PTRS = 12 };
+enum { W_IN_NORM = 0, W_Q, W_K, W_V, W_Q_NORM, W_K_NORM, W_O, W_POST_NORM, W_GATE, W_UP, W_DOWN, W_ROUTER };
 
 // One trace record (layout of mpk_trace_record).
 struct TraceRec {
@@ -120,8 +120,23 @@ constexpr int kLdsTop = 512;
 constexpr int kPfWaves = kWaves - 1;   // wavefronts that pre-load weights (all but the polling one)
 constexpr int kMaxPfSegs = 16;         // pre-loaded 1 KB segments per wavefront, at most
 constexpr int kMaxBatch = 16;
+constexpr int kMaxTopK = 16;     // experts per token, at most (mixture of experts)
+constexpr int kMaxExperts = 256;
 constexpr int kMaxHidden = 8192;
 
+
+// LDS of an expert tile's routing (mixture of experts): each request's
+// chosen experts and their weights, the set of experts the batch chose, and
+// the route of the tile's expert slot (expert, -1 when the slot is idle;
+// token count; tokens in ascending order; their weights).
+struct MoeLds {
+  int32_t cid[kMaxBatch][kMaxTopK];
+  float cw[kMaxBatch][kMaxTopK];
+  uint32_t mask[kMaxExperts / 32];
+  int32_t e, n;
+  int32_t tok[kMaxBatch];
+  float w[kMaxBatch];
+};
 
 // Kernel arguments.  One copy lives in device memory per graph (refreshed
 // only when a caller pointer changes); the kernels receive its address, the
@@ -200,6 +215,14 @@ struct KArgs {
   // 1: the projection weights are prepared (matrix-core operand order, see
   // packed_block in tasks.h; batch > 1 only)
   int32_t wpacked;
+  // mixture of experts (E = 0: dense): experts, top k, expert width, whether
+  // the top-k weights are renormalised, expert slots per layer; per-layer
+  // strides of the router logits [B][E] and route records [M][2 + 2B];
+  // lds_moe: the LDS area of an expert tile's routing (MoeLds in tasks.h)
+  int32_t E, topk, Fe, norm_topk, M, lds_moe;
+  int64_t st_rlog, st_route;
+  MPK_GLOBAL float* rlog;
+  MPK_GLOBAL int32_t* route;
 };
 
 }  // namespace mpk

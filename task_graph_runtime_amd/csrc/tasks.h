@@ -323,6 +323,9 @@ __device__ __forceinline__ TaskPtrs task_ptrs(const KArgs& a, const DevTask& t) 
     case MPK_TASK_MLP_NORM: r.p0 = W[W_POST_NORM]; break;
     case MPK_TASK_FINAL_NORM: r.p0 = a.final_norm; break;
     case MPK_TASK_ATTN: r.p0 = W[W_Q_NORM]; r.p1 = W[W_K_NORM]; break;
+    case MPK_TASK_ROUTER: r.p0 = W[W_ROUTER]; r.p3 = W[W_POST_NORM]; break;
+    case MPK_TASK_EXPERT_GU: r.p0 = W[W_GATE]; r.p1 = W[W_UP]; break;   // (expert 0: offset by the route)
+    case MPK_TASK_EXPERT_DOWN: r.p0 = W[W_DOWN]; break;
     default: break;
   }
   return r;
@@ -354,23 +357,36 @@ __device__ __forceinline__ gptr<const uint16_t> gemv_row(const KArgs& a, int typ
     }
     case MPK_TASK_DOWN:
       return P.p0 + (int64_t)(lo + r) * a.F;
-    default:
+    case MPK_TASK_EXPERT_GU: {   // (P: the slot's expert's gate and up matrices, as for GATEUP)
+      gptr<const uint16_t> gate = P.p0, up = P.p1;
+      return ((r & 1) ? up : gate) + (int64_t)(lo + (r >> 1)) * a.H;
+    }
+    case MPK_TASK_EXPERT_DOWN:   // (P: the slot's expert's down matrix)
+      return P.p0 + (int64_t)(lo + r) * a.Fe;
+    default:   // LM head, router
       return P.p0 + (int64_t)(lo + r) * a.H;
   }
 }
 
+// The input of a matrix-core tile: contraction length K, weight rows per
+// output column, the fp32 rows x [B][K], and which rows the tile's nx
+// columns (requests) take: row j for column j, or xrow[j] (an expert
+// tile's gather of its tokens' rows, LDS) when xrow is set.
 struct GemvOp {
   int K, rpc;
   gptr<const float> x;
+  const int* xrow;
+  int nx;
 };
 __device__ __forceinline__ GemvOp gemv_op(const KArgs& a, const DevTask& t) {
   const int l = t.layer;
   switch (t.type) {
-    case MPK_TASK_QKV: return {a.H, 1, a.h + (int64_t)l * a.st_bh};
-    case MPK_TASK_OPROJ: return {a.hq * a.d, 1, a.attn + (int64_t)l * a.st_q};
-    case MPK_TASK_GATEUP: return {a.H, 2, a.h2 + (int64_t)l * a.st_bh};
-    case MPK_TASK_DOWN: return {a.F, 1, a.a + (int64_t)l * a.st_a};
-    default: return {a.H, 1, a.hf};
+    case MPK_TASK_QKV: return {a.H, 1, a.h + (int64_t)l * a.st_bh, nullptr, a.B};
+    case MPK_TASK_OPROJ: return {a.hq * a.d, 1, a.attn + (int64_t)l * a.st_q, nullptr, a.B};
+    case MPK_TASK_GATEUP: return {a.H, 2, a.h2 + (int64_t)l * a.st_bh, nullptr, a.B};
+    case MPK_TASK_DOWN: return {a.F, 1, a.a + (int64_t)l * a.st_a, nullptr, a.B};
+    case MPK_TASK_ROUTER: return {a.H, 1, a.h2 + (int64_t)l * a.st_bh, nullptr, a.B};
+    default: return {a.H, 1, a.hf, nullptr, a.B};
   }
 }
 
@@ -393,6 +409,10 @@ __device__ __forceinline__ void seg_next(const KArgs& a, const DevTask& t, const
     ++w.r;
     w.row = gemv_row(a, t.type, P, t.a0, w.r);
   }
+}
+
+__device__ __forceinline__ MoeLds* moe_lds(const KArgs& a, char* lds) {
+  return reinterpret_cast<MoeLds*>(lds + a.lds_moe);
 }
 
 // k range of projection tile n under a split of its contraction into K
@@ -438,6 +458,40 @@ __device__ __forceinline__ void gemv_epilogue(const KArgs& a, const DevTask& t, 
         int b = i / ncol, c = i - b * ncol;
         float g = acc[(2 * c) * B + b], u = acc[(2 * c + 1) * B + b];
         st_coh(out + (int64_t)b * a.F + lo + c, g / (1.0f + expf(-g)) * u);
+      }
+      break;
+    }
+    case MPK_TASK_ROUTER: {   // router logits; at batch 1 tile 0 also zeroes d_l for the down tiles to add to
+      gptr<float> out = a.rlog + (int64_t)l * a.st_rlog;
+      for (int i = tid0; i < ncol * B; i += kThreads) {
+        int b = i / ncol, c = i - b * ncol;
+        st_coh(out + (int64_t)b * a.E + lo + c, acc[c * B + b]);
+      }
+      if (B == 1 && t.a2 == 0) {
+        gptr<float> d = a.dn + (int64_t)l * a.st_dn;
+        for (int i = tid0; i < a.H; i += kThreads) st_coh(d + i, 0.f);
+      }
+      break;
+    }
+    case MPK_TASK_EXPERT_GU: {   // SwiGLU of the slot's tokens: row j of the slot holds token j (rows past them: 0)
+      const MoeLds* m = moe_lds(a, g_lds);
+      const int n = m->n;
+      gptr<float> out = a.a + (int64_t)l * a.st_a + (int64_t)t.a2 * B * a.Fe;
+      for (int i = tid0; i < ncol * B; i += kThreads) {
+        int j = i / ncol, c = i - j * ncol;
+        float g = acc[(2 * c) * B + j], u = acc[(2 * c + 1) * B + j];
+        st_coh(out + (int64_t)j * a.Fe + lo + c, j < n ? g / (1.0f + expf(-g)) * u : 0.f);
+      }
+      break;
+    }
+    case MPK_TASK_EXPERT_DOWN: {   // each token's output, times its weight, added into d_l
+      const MoeLds* m = moe_lds(a, g_lds);
+      const int n = m->n;
+      gptr<float> d = a.dn + (int64_t)l * a.st_dn;
+      for (int i = tid0; i < ncol * n; i += kThreads) {
+        int j = i / ncol, c = i - j * ncol;
+        __hip_atomic_fetch_add(d + (int64_t)m->tok[j] * a.H + lo + c, m->w[j] * acc[c * B + j], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
       }
       break;
     }
@@ -489,8 +543,8 @@ struct GemvTile {
 };
 __device__ __forceinline__ GemvTile gemv_tile(const KArgs& a, const DevTask& t, int w, bool pre) {
   GemvTile r;
-  r.K = t.type == MPK_TASK_OPROJ ? a.hq * a.d : t.type == MPK_TASK_DOWN ? a.F : a.H;
-  r.nrows = (t.a1 - t.a0) * (t.type == MPK_TASK_GATEUP ? 2 : 1);
+  r.K = t.type == MPK_TASK_OPROJ ? a.hq * a.d : t.type == MPK_TASK_DOWN ? a.F : t.type == MPK_TASK_EXPERT_DOWN ? a.Fe : a.H;
+  r.nrows = (t.a1 - t.a0) * ((t.type == MPK_TASK_GATEUP || t.type == MPK_TASK_EXPERT_GU) ? 2 : 1);
   r.nseg = (r.K + 511) >> 9;
   r.S = r.nrows * r.nseg;
   r.P0 = (pre && a.pf_segs > 0) ? min(r.S, kPfWaves * min(a.pf_segs, kMaxPfSegs)) : 0;
@@ -501,9 +555,11 @@ __device__ __forceinline__ GemvTile gemv_tile(const KArgs& a, const DevTask& t, 
 __device__ __forceinline__ char* pf_slot(const KArgs& a, char* lds, int w, int j) {
   return lds + a.lds_pf + ((w - 1) * min(a.pf_segs, kMaxPfSegs) + j) * 1024;
 }
+// Projection tiles whose weights are known before their event fires (so
+// they can be pre-loaded); expert tiles learn their expert from the routing.
 __device__ __forceinline__ bool is_gemv(int type) {
   return type == MPK_TASK_QKV || type == MPK_TASK_OPROJ || type == MPK_TASK_GATEUP || type == MPK_TASK_DOWN ||
-         type == MPK_TASK_LMHEAD;
+         type == MPK_TASK_LMHEAD || type == MPK_TASK_ROUTER;
 }
 
 // Weight pre-load of a batch-1 projection tile (MPK summary section 5,
@@ -550,11 +606,12 @@ struct XSrc {
   gptr<const float> v1, v2;     // fp32 summands (v2 null only with emb or without norm)
   gptr<const uint16_t> emb;     // bf16 embedding row instead of v1 (layer-0 QKV)
   gptr<float> res;              // where to store v, or null
+  gptr<float> hout;             // where to store x as well, or null (router tile 0)
   bool norm;
 };
 __device__ __forceinline__ XSrc gemv_xsrc(const KArgs& a, const DevTask& t, const TaskPtrs& P) {
   const int l = t.layer;
-  XSrc x{nullptr, nullptr, nullptr, nullptr, true};
+  XSrc x{nullptr, nullptr, nullptr, nullptr, nullptr, true};
   switch (t.type) {
     case MPK_TASK_QKV:
       if (l == 0) {
@@ -574,6 +631,22 @@ __device__ __forceinline__ XSrc gemv_xsrc(const KArgs& a, const DevTask& t, cons
       x.v1 = a.r + (int64_t)l * a.st_bh;
       x.v2 = a.o + (int64_t)l * a.st_o;
       if (t.a2 == 0) x.res = a.s + (int64_t)l * a.st_bh;
+      break;
+    case MPK_TASK_ROUTER:   // as GATEUP; tile 0 also stores h2_l, the experts' input
+      x.v1 = a.r + (int64_t)l * a.st_bh;
+      x.v2 = a.o + (int64_t)l * a.st_o;
+      if (t.a2 == 0) {
+        x.res = a.s + (int64_t)l * a.st_bh;
+        x.hout = a.h2 + (int64_t)l * a.st_bh;
+      }
+      break;
+    case MPK_TASK_EXPERT_GU:
+      x.v1 = a.h2 + (int64_t)l * a.st_bh;
+      x.norm = false;
+      break;
+    case MPK_TASK_EXPERT_DOWN:   // (row 0 of the slot: its one token at batch 1)
+      x.v1 = a.a + (int64_t)l * a.st_a + (int64_t)t.a2 * a.B * a.Fe;
+      x.norm = false;
       break;
     case MPK_TASK_LMHEAD:
       x.v1 = a.s + (int64_t)(a.L - 1) * a.st_bh;
@@ -654,6 +727,10 @@ __device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* l
         if (x.res) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) st_coh(x.res + e + u, v[8 * j + u]);
+        }
+        if (x.hout) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) st_coh(x.hout + e + u, o[u]);
         }
       }
     }
@@ -908,7 +985,8 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
   const int K = op.K, B = a.B;
   const int nkg = (ks1 - ks0 + KG - 1) / KG;
   const int klast = min((ks1 - 1) * 32 + lg * 8, K - 8);   // the lane's last k in range
-  const int xoff = min(li, B - 1) * K;                      // x row of the lane's request
+  // x row of the lane's request (columns past nx repeat the last one)
+  const int xoff = (op.xrow ? op.xrow[min(li, op.nx - 1)] : min(li, op.nx - 1)) * K;
   // prepared weights: the lane's 16 bytes of each 1 KB block (rows past the tile read its last block)
   gptr<const uint16_t> rows[NRB];
 #pragma unroll
@@ -986,9 +1064,9 @@ __device__ __forceinline__ void mfma_passes(const KArgs& a, const DevTask& t, co
   for (int rb0 = 0; rb0 < nrb; rb0 += NRB) mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, ks0, ks1);
 }
 
-__device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds) {
+__device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds,
+                                          const GemvOp& op) {
   const int tid0 = tidx();
-  const GemvOp op = gemv_op(a, t);
   const int K = op.K, nrows = (t.a1 - t.a0) * op.rpc, B = a.B;
   float* acc = reinterpret_cast<float*>(lds + a.lds_acc);
   float* red = reinterpret_cast<float*>(lds + kLdsRed);
@@ -1436,20 +1514,29 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
 
 // ------------------------------------------------------------------ final argmax
 // next_ids[b] = argmax over the LM-head tile partials; ties -> lowest index.
+// Wavefront w reduces requests w, w + 8, ...: each lane loads its tiles'
+// partials for all of its requests at once, then the wavefront reduces each
+// request by shuffles (no workgroup barrier per request).
 __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
+  (void)lds;
   const int tid0 = tidx();
-  float* red = reinterpret_cast<float*>(lds + kLdsRed);
-  int* redi = reinterpret_cast<int*>(red + kWaves);
   const int w = tid0 >> 6, lane = tid0 & 63;
-  for (int b = 0; b < a.B; ++b) {
+  for (int b = w; b < a.B; b += kWaves) {
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int n = tid0; n < a.T_lm; n += kThreads) {
-      const unsigned long long pv = __hip_atomic_load(
-          reinterpret_cast<MPK_GLOBAL unsigned long long*>(a.pmax + b * a.T_lm + n), __ATOMIC_RELAXED,
-          __HIP_MEMORY_SCOPE_AGENT);
-      const PMax p{__uint_as_float((uint32_t)pv), (int32_t)(pv >> 32)};
-      if (p.v > bv || (p.v == bv && p.i < bi)) { bv = p.v; bi = p.i; }
+    for (int n0 = 0; n0 < a.T_lm; n0 += 64 * 8) {
+      unsigned long long pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int n = min(n0 + u * 64 + lane, a.T_lm - 1);
+        pv[u] = __hip_atomic_load(reinterpret_cast<MPK_GLOBAL unsigned long long*>(a.pmax + b * a.T_lm + n),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const PMax p{__uint_as_float((uint32_t)pv[u]), (int32_t)(pv[u] >> 32)};
+        if (n0 + u * 64 + lane < a.T_lm && (p.v > bv || (p.v == bv && p.i < bi))) { bv = p.v; bi = p.i; }
+      }
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -1457,14 +1544,168 @@ __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
       const int oi = __shfl_xor(bi, m);
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
-    if (lane == 0) { red[w] = bv; redi[w] = bi; }
+    if (lane == 0) a.next_ids[b] = (bi == INT_MAX) ? 0 : bi;
+  }
+}
+
+// ------------------------------------------------------------------ mixture of experts
+// Routing of layer l for expert slot s (Qwen3-MoE reading of the MoE layer
+// in the MPK summary's workload list): per request, the softmax of its E
+// router logits, its top_k experts by probability (ties: the lower index)
+// and their probabilities, renormalised to sum 1 when norm_topk.  Slot s
+// serves the s-th smallest expert that any request chose (none: the slot is
+// idle, e = -1) for the requests that chose it, in ascending order, each
+// with its weight for that expert.  Wavefront w routes requests w, w + 8
+// (lane i holds logits i, i + 64, ...; top-k by k rounds of a wavefront
+// argmax); wavefront 0 then resolves the slot.  Result in MoeLds.
+__device__ __forceinline__ void moe_route(const KArgs& a, int l, int s, char* lds) {
+  const int tid0 = tidx();
+  const int w = tid0 >> 6, lane = tid0 & 63;
+  MoeLds* m = moe_lds(a, lds);
+  const int E = a.E, K = a.topk, B = a.B;
+  if (tid0 < kMaxExperts / 32) m->mask[tid0] = 0u;
+  __syncthreads();
+  gptr<const float> lg = a.rlog + (int64_t)l * a.st_rlog;
+  constexpr int NJ = kMaxExperts / 64;
+  for (int b = w; b < B; b += kWaves) {
+    float v[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = ld_coh(lg + (int64_t)b * E + min(e, E - 1));
+      if (e >= E) v[j] = -INFINITY;
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int j = 1; j < NJ; ++j) mx = fmaxf(mx, v[j]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) z += lane + 64 * j < E ? expf(v[j] - mx) : 0.f;
+    z = wave_sum(z);
+    int my_id = 0;
+    float my_p = 0.f, chosen = 0.f;
+    for (int i = 0; i < K; ++i) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (lane + 64 * j < E && v[j] > bv) { bv = v[j]; bi = lane + 64 * j; }   // increasing j: lower index kept
+#pragma unroll
+      for (int k = 1; k < 64; k <<= 1) {
+        const float ov = __shfl_xor(bv, k);
+        const int oi = __shfl_xor(bi, k);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      bi = min(bi, E - 1);   // (only a NaN logit leaves no candidate)
+      const float p = expf(bv - mx) / z;
+      if (lane == i) { my_id = bi; my_p = p; }
+      chosen += p;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (lane + 64 * j == bi) v[j] = -INFINITY;
+    }
+    if (lane < K) {
+      m->cid[b][lane] = my_id;
+      m->cw[b][lane] = a.norm_topk ? my_p / chosen : my_p;
+      atomicOr(&m->mask[my_id >> 5], 1u << (my_id & 31));
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    // the s-th set bit of the chosen set
+    int e = -1, r = s;
+    for (int i = 0; i < kMaxExperts / 32 && e < 0; ++i) {
+      uint32_t bits = m->mask[i];
+      const int c = __builtin_popcount(bits);
+      if (r >= c) { r -= c; continue; }
+      for (; r > 0; --r) bits &= bits - 1;
+      e = 32 * i + __builtin_ctz(bits);
+    }
+    int hit = -1;
+    if (lane < B && e >= 0)
+      for (int i = 0; i < K; ++i)
+        if (m->cid[lane][i] == e) hit = i;
+    const unsigned long long bal = __ballot(hit >= 0);
+    const int pos = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+    if (hit >= 0) {
+      m->tok[pos] = lane;
+      m->w[pos] = m->cw[lane][hit];
+    }
+    if (lane == 0) {
+      m->e = e;
+      m->n = __builtin_popcountll(bal);
+    }
+  }
+  __syncthreads();
+}
+
+// An expert tile of slot s = t.a2: gate/up tiles route (moe_route), and tile
+// 0 of the slot stores the route record [expert, count, tokens[B],
+// weights[B]] that the slot's down tiles read instead of routing again.  An
+// idle slot's gate/up tiles write zeros; its down tiles do nothing.
+// Otherwise the slot's expert's matrices are a projection over the slot's
+// tokens: batch 1, the one token's row; batch > 1, the tokens' rows gathered
+// into the matrix-core tile's columns.
+__device__ __forceinline__ void expert_task(const KArgs& a, const DevTask& t, const TaskPtrs& P0, char* lds) {
+  const int tid0 = tidx();
+  const int l = t.layer, s = t.a2, B = a.B, rw = 2 + 2 * B;
+  const bool gu = t.type == MPK_TASK_EXPERT_GU;
+  MoeLds* m = moe_lds(a, lds);
+  gptr<int32_t> rec = a.route + (int64_t)l * a.st_route + (int64_t)s * rw;
+  if (gu) {
+    moe_route(a, l, s, lds);
+    if (t.a0 == 0 && tid0 < rw) {
+      const int n = m->n, j = tid0 - 2, k = tid0 - 2 - B;
+      const int32_t v = tid0 == 0 ? m->e
+                      : tid0 == 1 ? n
+                      : j < B     ? (j < n ? m->tok[j] : 0)
+                                  : (k < n ? __float_as_int(m->w[k]) : 0);
+      __hip_atomic_store(rec + tid0, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    // (a record holding a token outside the batch is not used: no add lands outside d_l)
+    int* bad = reinterpret_cast<int*>(lds + kLdsRed);
+    if (tid0 == 0) *bad = 0;
     __syncthreads();
-    if (tid0 == 0) {
-      for (int i = 1; i < kWaves; ++i)
-        if (red[i] > bv || (red[i] == bv && redi[i] < bi)) { bv = red[i]; bi = redi[i]; }
-      a.next_ids[b] = (bi == INT_MAX) ? 0 : bi;
+    if (tid0 < rw) {
+      const int32_t v = __hip_atomic_load(rec + tid0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int j = tid0 - 2, k = tid0 - 2 - B;
+      if (tid0 == 0) m->e = v;
+      else if (tid0 == 1) m->n = v;
+      else if (j < B) {
+        m->tok[j] = v;
+        if (v < 0 || v >= B) atomicOr(bad, 1);
+      } else {
+        m->w[k] = __int_as_float(v);
+      }
     }
     __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(*bad)) return;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(m->e), n = __builtin_amdgcn_readfirstlane(m->n);
+  if (e < 0 || e >= a.E || n < 1 || n > B) {
+    if (gu) {
+      const int ncol = t.a1 - t.a0;
+      gptr<float> out = a.a + (int64_t)l * a.st_a + (int64_t)s * B * a.Fe;
+      for (int i = tid0; i < ncol * B; i += kThreads) {
+        const int j = i / ncol, c = i - j * ncol;
+        st_coh(out + (int64_t)j * a.Fe + t.a0 + c, 0.f);
+      }
+    }
+    return;
+  }
+  TaskPtrs P = P0;
+  const int64_t ew = (int64_t)e * a.Fe * a.H;   // elements per expert matrix
+  P.p0 = P0.p0 + ew;
+  if (gu) P.p1 = P0.p1 + ew;
+  if (B > 1) {
+    const GemvOp op = gu ? GemvOp{a.H, 2, a.h2 + (int64_t)l * a.st_bh, m->tok, n}
+                         : GemvOp{a.Fe, 1, a.a + (int64_t)l * a.st_a + (int64_t)s * B * a.Fe, nullptr, n};
+    gemv_mfma(a, t, P, lds, op);
+  } else {
+    gemv_b1<4>(a, t, P, lds, false);
   }
 }
 
@@ -1488,6 +1729,10 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
     case MPK_TASK_MLP_NORM:
       norm_task(a, t.a0, a.r + (int64_t)l * a.st_bh, a.o + (int64_t)l * a.st_o, a.Ko, a.s + (int64_t)l * a.st_bh,
                 P.p0, a.h2 + (int64_t)l * a.st_bh, lds, red);
+      if (a.E > 0) {   // (mixture of experts: row b of d_l starts at zero, the down tiles add to it)
+        gptr<float> d = a.dn + (int64_t)l * a.st_dn + (int64_t)t.a0 * a.H;
+        for (int i = tidx(); i < a.H; i += kThreads) st_coh(d + i, 0.f);
+      }
       break;
     case MPK_TASK_FINAL_NORM:
       norm_task(a, t.a0, a.s + (int64_t)(a.L - 1) * a.st_bh, a.dn + (int64_t)(a.L - 1) * a.st_dn, a.Kd, nullptr,
@@ -1498,8 +1743,13 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
     case MPK_TASK_GATEUP:
     case MPK_TASK_DOWN:
     case MPK_TASK_LMHEAD:
-      if (a.B > 1) gemv_mfma(a, t, P, lds);
+    case MPK_TASK_ROUTER:
+      if (a.B > 1) gemv_mfma(a, t, P, lds, gemv_op(a, t));
       else gemv_b1<4>(a, t, P, lds, pre);
+      break;
+    case MPK_TASK_EXPERT_GU:
+    case MPK_TASK_EXPERT_DOWN:
+      expert_task(a, t, P, lds);
       break;
     case MPK_TASK_ATTN:
       if (a.d == 128) {

@@ -26,7 +26,23 @@ class LazyLayers:
         return len(self._layers)
 
     def __getitem__(self, l):
-        return {k: self._conv(v) for k, v in self._layers[l].items()}
+        return {k: (LazyExperts(v, self._conv) if v.dim() == 3 else self._conv(v))
+                for k, v in self._layers[l].items()}
+
+
+class LazyExperts:
+    """An expert stack ``[E][...]`` whose experts are copied to the host one at a
+    time, when the oracle reads them (it reads only the chosen ones)."""
+
+    def __init__(self, t, conv):
+        self._t = t
+        self._conv = conv
+
+    def __len__(self):
+        return self._t.shape[0]
+
+    def __getitem__(self, e):
+        return self._conv(self._t[e])
 
 
 def oracle_weights(w: dict, lazy: bool = False, widen_on_device: bool = False) -> dict:
@@ -37,14 +53,14 @@ def oracle_weights(w: dict, lazy: bool = False, widen_on_device: bool = False) -
             "lm_head": None if w["lm_head"] is None else conv(w["lm_head"]), "layers": layers}
 
 
-def run_oracle(inp: dict, dtype=np.float32, capture=None, lazy=False, widen_on_device=False):
+def run_oracle(inp: dict, dtype=np.float32, capture=None, lazy=False, widen_on_device=False, route_hook=None):
     from oracle import numerics
     s = inp["shape"]
     kv = inp["kv"]
     return numerics.decode_step(s.cfg(), oracle_weights(inp["weights"], lazy=lazy, widen_on_device=widen_on_device),
                                 inp["token_ids"].cpu().numpy(), bf16_bits(kv["k_pool"]), bf16_bits(kv["v_pool"]),
                                 kv["page_table"].cpu().numpy(), inp["seq_lens"].cpu().numpy(), s.page_size,
-                                dtype=dtype, capture=capture)
+                                dtype=dtype, capture=capture, route_hook=route_hook)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

@@ -31,7 +31,8 @@ def both(shape, B, W, q=None, S=None, **over):
     from the library's header)."""
     s = shape
     names = dict(T_qkv="t_qkv", T_o="t_o", T_gu="t_gu", T_down="t_down", T_lm="t_lm", K_qkv="k_qkv", K_o="k_o",
-                 K_down="k_down", coarse="coarse_events", fusion="fusion_order")
+                 K_down="k_down", coarse="coarse_events", fusion="fusion_order", T_router="t_router", T_egu="t_egu",
+                 T_edown="t_edown")
     params = dict(n_workers=W, s_attn=S or max(4, B), attn_jit=over.pop("attn_jit", 0))
     if q is not None:
         params["quantum"] = q
@@ -42,7 +43,8 @@ def both(shape, B, W, q=None, S=None, **over):
     prm = tg.Params(W=p["n_workers"], S_sched=p["n_sched_waves"], q=p["quantum"], T_qkv=p["t_qkv"], T_o=p["t_o"],
                     T_gu=p["t_gu"], T_down=p["t_down"], T_lm=p["t_lm"], S_attn=p["s_attn"],
                     jit_attn=p["attn_jit"] == 1, jit_all=p["attn_jit"] == 3, K_qkv=p["k_qkv"], K_o=p["k_o"],
-                    K_down=p["k_down"], coarse=p["coarse_events"] == 1, fusion=p["fusion_order"])
+                    K_down=p["k_down"], coarse=p["coarse_events"] == 1, fusion=p["fusion_order"],
+                    T_router=p["t_router"] or 1, T_egu=p["t_egu"] or 1, T_edown=p["t_edown"] or 1)
     ref, tasks = tg.build(s.cfg(), B, s.page_size, prm)
     got = g.export()
     got["params"] = p
@@ -113,8 +115,8 @@ def test_coarse_operator_level_graph(B):
     assert_same(ref, got)
     tg.check_semantics(got, tasks, closure=True)
     _, fine, _ = both(s, B, 13, S=4)
-    if B > 1:
-        assert got["params"]["k_o"] == 3 and got["params"]["k_down"] == 3
+    if B > 1:   # (the tiny shape's 2 kv groups: 2 O ranges)
+        assert got["params"]["k_o"] == 2 and got["params"]["k_down"] == 3
 
     def deps(g, ty):
         real = g["task_type"] == ty
@@ -125,7 +127,7 @@ def test_coarse_operator_level_graph(B):
     att = lambda g: set(g["task_dep"][g["task_type"] == tg.ATTN].tolist())
     assert len(att(got)) == s.n_layers and len(att(fine)) == s.n_layers * s.n_kv_heads
     if B > 1:   # fine: the O and down tiles wait per k-range
-        assert len(deps(fine, tg.OPROJ)) == 3 * s.n_layers and len(deps(fine, tg.DOWN)) == 3 * s.n_layers
+        assert len(deps(fine, tg.OPROJ)) == 2 * s.n_layers and len(deps(fine, tg.DOWN)) == 3 * s.n_layers
 
 
 def test_weight_preload_switch():
@@ -139,9 +141,13 @@ def test_weight_preload_switch():
 
 def test_k_split_default_yields_to_a_given_tile_count():
     s = synth.SHAPES["tiny"]
+    # (2 kv groups: the O default is 2 ranges, kept by t_o = 4, dropped by t_o = 5; down 3, kept by 6)
     p = mpk.TGraph(s.cfg(), 3, s.page_size, dict(n_workers=13, s_attn=4, t_o=4, t_down=6), host_only=True)
     p = p.header()["params"]
-    assert (p["k_o"], p["k_down"], p["t_o"], p["t_down"]) == (1, 3, 4, 6)
+    assert (p["k_o"], p["k_down"], p["t_o"], p["t_down"]) == (2, 3, 4, 6)
+    p = mpk.TGraph(s.cfg(), 3, s.page_size, dict(n_workers=13, s_attn=4, t_o=5, t_down=4), host_only=True)
+    p = p.header()["params"]
+    assert (p["k_o"], p["k_down"], p["t_o"], p["t_down"]) == (1, 1, 5, 4)
 
 
 @pytest.mark.parametrize("B,over", [(1, dict(k_qkv=2)), (1, dict(k_down=2)), (2, dict(k_o=1000)),
@@ -188,9 +194,10 @@ def test_default_params_resolve_as_documented():
     assert h16["quantum"] == 16 and h16["s_attn"] == 32
     # 151936 columns x 16 requests need >= 297 tiles of <= 8192 accumulators: two per worker
     assert h16["t_lm"] == 512 and h16["t_gu"] == 256
-    # the output and down projections split their contraction 3 ways (85 column tiles x 3)
-    assert (h16["k_qkv"], h16["k_o"], h16["k_down"]) == (1, 3, 3)
-    assert h16["t_qkv"] == 256 and h16["t_o"] == h16["t_down"] == 255
+    # the output projection splits its contraction into 4 ranges of 2 kv groups (64 column tiles x 4),
+    # the down projection 3 ways (85 column tiles x 3)
+    assert (h16["k_qkv"], h16["k_o"], h16["k_down"]) == (1, 4, 3)
+    assert h16["t_qkv"] == 256 and h16["t_o"] == 256 and h16["t_down"] == 255
     # the hybrid policy (attention JIT): 14 scheduler wavefronts (4 workgroups) leave 252 workers
     hj = mpk.TGraph(s.cfg(), 16, 64, dict(attn_jit=1), host_only=True).header()["params"]
     assert hj["n_workers"] == 252 and hj["n_sched_waves"] == 14 and hj["attn_jit"] == 1 and hj["s_attn"] == 31
@@ -294,3 +301,53 @@ def test_partial_k_step_shapes_refused_above_batch_one(over):
         assert e.value.code == -2 and "multiples of 32" in str(e.value)
     g = mpk.TGraph(c, 1, 16, {}, host_only=True)
     assert g.header()["n_tasks"] > 0
+
+
+# ------------------------------------------------------------------ mixture of experts
+@pytest.mark.parametrize("B,attn_jit,over", [(1, 0, dict(T_router=2, T_egu=3, T_edown=2)), (1, 1, {}),
+                                              (3, 0, dict(T_egu=2, T_edown=2)), (4, 1, {}), (16, 0, {})])
+def test_moe_graph_bit_exact(B, attn_jit, over):
+    """Expert layers (router tiles, per-slot gate/up and down tiles) in the C++
+    builder against the spec, with the closure check; a slot's down tiles wait
+    for that slot's gate/up tiles only."""
+    s = synth.SHAPES["tiny_moe"]
+    ref, got, tasks = both(s, B, 8, q=1 if B == 1 else 16, S=max(4, B), attn_jit=attn_jit, **over)
+    assert_same(ref, got)
+    tg.check_semantics(got, tasks, closure=True)
+    tt, dep = got["task_type"], got["task_dep"]
+    M = min(s.n_experts, B * s.top_k)
+    assert np.sum(tt == tg.EXPERT_GU) == s.n_layers * M * got["params"]["t_egu"]
+    # one dependent event per slot (and layer) for the down tiles, one per layer for gate/up
+    assert len(set(dep[tt == tg.EXPERT_DOWN].tolist())) == s.n_layers * M
+    assert len(set(dep[tt == tg.EXPERT_GU].tolist())) == s.n_layers
+    if attn_jit == 1:   # the hybrid policy makes the data-dependent tasks JIT: attention and experts
+        assert np.all(got["task_mode"][np.isin(tt, (tg.ATTN, tg.EXPERT_GU, tg.EXPERT_DOWN))] == tg.MODE_JIT)
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b", "qwen3_30b_a3b_b16"])
+def test_moe_full_graph(name):
+    s = synth.SHAPES[name]
+    g = mpk.TGraph(s.cfg(), s.batch, s.page_size, {}, host_only=True)
+    p = g.header()["params"]
+    ex = g.export()
+    tg.check_semantics(ex, None)
+    M = min(s.n_experts, s.batch * s.top_k)
+    if s.batch == 1:
+        # 8 slots; one gate/up and one down tile per worker and slot: 32 each; 32 router tiles
+        assert (p["t_router"], p["t_egu"], p["t_edown"], p["k_down"]) == (32, 32, 32, 1)
+    else:
+        # 128 slots; 4 tiles per slot (a tile's accumulators: columns x rows x 16 requests <= 8192)
+        assert (p["t_router"], p["t_egu"], p["t_edown"]) == (8, 4, 4) and M == 128
+    h = ex["header"]
+    assert h["n_empty"] / h["NT"] < (0.01 if s.batch == 1 else 0.05)   # "deep, not wide"
+
+
+@pytest.mark.parametrize("over,code", [(dict(top_k=9, n_experts=8), -2), (dict(n_experts=300), -2),
+                                       (dict(moe_ffn=100), -2), (dict(norm_topk=2), -1)])
+def test_bad_moe_config_rejected(over, code):
+    c = mpk.model_cfg(synth.SHAPES["tiny_moe"].cfg())
+    for k, v in over.items():
+        setattr(c, k, v)
+    with pytest.raises(mpk.MpkError) as e:
+        mpk.TGraph(c, 3, 16, {}, host_only=True)
+    assert e.value.code == code

@@ -122,7 +122,7 @@ def test_tiny_intermediates_layer_by_layer(B):
         assert (Kq, Ko, Kd) != (1, 1, 1)
         np.testing.assert_allclose(g.read_tensor(0, (B, H), np.float32), cap["embed"], rtol=0, atol=0)
     for l in range(s.n_layers):
-        t = lambda k: 5 + 13 * l + k
+        t = lambda k: 5 + mpk._binding.LAYER_TENSORS * l + k
         c = cap[l]
         np.testing.assert_allclose(g.read_tensor(t(0), (B, H), np.float32), c["r"], rtol=2e-2, atol=2e-2)
         if B > 1:
