@@ -24,13 +24,19 @@ METRIC = "decode ms/token + achieved HBM TB/s (% peak), Qwen3-8B-shape batch 1"
 HBM_PEAK_GBS = 8000.0
 
 
-def algorithmic_bytes(s, seq_lens) -> int:
+def algorithmic_bytes(s, seq_lens, experts=None) -> int:
     """Bytes the step must move: every weight once (projections, norm gains,
     LM head or tied embedding), B embedding rows and the K/V of L_b + 1 tokens
-    per request and layer; all bf16."""
+    per request and layer; all bf16.  Mixture of experts: the router and the
+    gate/up/down of the experts the batch chose (experts[l] distinct ones in
+    layer l) in place of the dense FFN."""
     H, d, hq, hkv, F, V, L = s.hidden, s.head_dim, s.n_q_heads, s.n_kv_heads, s.ffn, s.vocab, s.n_layers
-    per_layer = hq * d * H + 2 * hkv * d * H + H * hq * d + 3 * F * H + 2 * H + (2 * d if s.qk_norm else 0)
-    w = L * per_layer + H + V * H
+    per_layer = hq * d * H + 2 * hkv * d * H + H * hq * d + 2 * H + (2 * d if s.qk_norm else 0)
+    if s.n_experts:
+        ffn = sum(s.n_experts * H + e * 3 * s.moe_ffn * H for e in experts)
+    else:
+        ffn = L * 3 * F * H
+    w = L * per_layer + ffn + H + V * H
     kv = sum(int(x) + 1 for x in seq_lens) * L * 2 * hkv * d
     return 2 * (w + len(seq_lens) * H + kv)
 
@@ -67,6 +73,16 @@ def measured_traffic(config: str, src_hash: str):
     if kv.get("source_sha256") != src_hash:
         return None
     return int(kv["traffic_bytes"])
+
+
+def distinct_experts(g, s, mpk, np):
+    """Per layer, the experts the batch chose in the last step (busy slots of
+    its route records); None for a dense model."""
+    if not s.n_experts:
+        return None
+    M, rw = min(s.n_experts, s.batch * s.top_k), 2 + 2 * s.batch
+    return [int((g.read_tensor(5 + mpk._binding.LAYER_TENSORS * l + 14, (M, rw), np.int32)[:, 0] >= 0).sum())
+            for l in range(s.n_layers)]
 
 
 def time_steps(fn, steps, warmup, torch):
@@ -176,7 +192,9 @@ def main():
         raise SystemExit(f"mega-kernel reported {st}")
     ms = wall_ms / args.steps
     kern_ms = statistics.mean(per)
-    nbytes = algorithmic_bytes(s, inp["seq_lens"].tolist())
+    import numpy as np
+    experts = distinct_experts(g, s, mpk, np)
+    nbytes = algorithmic_bytes(s, inp["seq_lens"].tolist(), experts)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
 
     base = {}
@@ -213,7 +231,9 @@ def main():
                                f"page {s.page_size}",
                    "global_batch": s.batch, "seq_len": int(max(inp['seq_lens'].tolist())) + 1,
                    "parallelism": "single GPU", "workers": hdr["n_workers"], "sched_waves": hdr["n_sched_waves"],
-                   "s_attn": hdr["s_attn"], "weights": "prepared" if args.prepared else "row-major"},
+                   "s_attn": hdr["s_attn"], "weights": "prepared" if args.prepared else "row-major",
+                   **({"experts": f"{s.n_experts}, top {s.top_k}, width {s.moe_ffn}",
+                       "distinct_experts_per_layer": round(sum(experts) / len(experts), 2)} if experts else {})},
         "tb_per_s": round(achieved / 1e3, 3), "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 1),
         "kernel_ms": {"mean": round(kern_ms, 4), "median": round(statistics.median(per), 4),
                       "p10": round(sorted(per)[len(per) // 10], 4), "p90": round(sorted(per)[(9 * len(per)) // 10], 4)},

@@ -2,6 +2,7 @@
 #include "builder.h"
 
 #include <algorithm>
+#include <cmath>
 #include <array>
 #include <deque>
 #include <map>
@@ -149,14 +150,22 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   if (r.T_o < 0 || r.T_down < 0) return bad("t_o / t_down must be multiples of k_o / k_down");
   if (c.n_experts > 0) {
     // mixture of experts: router tiles on the column quantum (about W / 8);
-    // per expert slot, gate/up and down tiles of about W / slots, more while a
-    // tile's accumulators (columns x rows per column x batch) exceed the budget
+    // per expert slot, gate/up and down tiles so that the slots' tiles make
+    // one task per worker at batch 1 (every slot is busy: W / slots each) and
+    // about two at batch > 1 over the slots that are busy when the batch
+    // routes uniformly, E (1 - (1 - k/E)^B) of them -- an idle slot's tiles
+    // finish at once, and two rounds leave a short tail (30B-A3B shape,
+    // batch 16: 82 busy slots of 128, 6 tiles each); more tiles while a tile's
+    // accumulators (columns x rows per column x batch) exceed the budget
     const int64_t E = c.n_experts, Fe = c.moe_ffn, M = moe_slots(c, B);
+    const double busy = (double)E * (1.0 - std::pow(1.0 - (double)c.top_k / (double)E, (double)B));
     auto per_slot = [&](int32_t v, int64_t N, int64_t rpc) {
       if (v > 0) return (int64_t)v;
-      const int64_t U = cdiv(N, r.q), step = std::max<int64_t>(1, r.W / M);
+      const int64_t U = cdiv(N, r.q);
+      const int64_t step = B == 1 ? std::max<int64_t>(1, r.W / M)
+                                  : std::max<int64_t>(1, (int64_t)(2.0 * r.W / std::max(1.0, busy)));
       int64_t T = std::min<int64_t>(step, U);
-      while (T < U && r.q * cdiv(U, T) * rpc * B > kMaxTileAcc) T = std::min<int64_t>(U, T + step);
+      while (T < U && r.q * cdiv(U, T) * rpc * B > kMaxTileAcc) T = std::min<int64_t>(U, T + 1);
       return T;
     };
     const int64_t Tr = p.t_router > 0 ? p.t_router : std::min<int64_t>(cdiv(E, r.q), std::max<int64_t>(1, r.W / 8));

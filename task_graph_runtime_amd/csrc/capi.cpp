@@ -277,7 +277,8 @@ int lds_layout(const mpk_model_cfg& c, int32_t B, int32_t P, const Params& p, KA
   const int64_t pid = kLdsBytes - kLdsTop - chunks(4 * max_pages);
   // (an expert tile's routing area under the page ids: both are live only while such a task runs, and
   // neither may share the pre-load area, which holds the next task's weights while a JIT task runs)
-  const int64_t top = moe ? pid - chunks((int64_t)sizeof(MoeLds)) : pid;
+  // (the routing area ends in the B x E logits, staged in whole runs of 64)
+  const int64_t top = moe ? pid - chunks((int64_t)sizeof(MoeLds) + 4 * ((B * (int64_t)c.n_experts + 63) & ~63)) : pid;
   const int64_t pf = stage + acc;
   if (pf > top) return fail(MPK_ERR_UNSUPPORTED, "shape needs more LDS than a compute unit has");
   a->lds_acc = (int32_t)stage;

@@ -128,7 +128,8 @@ constexpr int kMaxHidden = 8192;
 // LDS of an expert tile's routing (mixture of experts): each request's
 // chosen experts and their weights, the set of experts the batch chose, and
 // the route of the tile's expert slot (expert, -1 when the slot is idle;
-// token count; tokens in ascending order; their weights).
+// token count; tokens in ascending order; their weights); the B x E router
+// logits follow it.
 struct MoeLds {
   int32_t cid[kMaxBatch][kMaxTopK];
   float cw[kMaxBatch][kMaxTopK];

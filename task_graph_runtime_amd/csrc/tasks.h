@@ -776,7 +776,8 @@ __device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* l
 // overlap; the wait for x leaves that chunk in flight.  Loads past the tile's
 // last segment repeat it, so the wait counts stay static.
 template <int D>
-__device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds, bool pre) {
+__device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds, bool pre,
+                                        bool xready = false) {
   const int tid0 = tidx();
   const int lane = tid0 & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);   // (wavefront-uniform: scalar control flow)
@@ -793,7 +794,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
   const int kl = lane * 8;
   const XSrc xsrc = gemv_xsrc(a, t, P);
   XRegs xr;
-  xs_issue(a, xsrc, K, P, lds, xr);
+  if (!xready) xs_issue(a, xsrc, K, P, lds, xr);   // (xready: the caller staged x, an unnormalised row, and waited)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);   // the staging loads stay ahead of the weight loads (counted waits)
   // segment s -> (row, segment within the row) without an integer division
@@ -871,7 +872,7 @@ __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const 
   else wait_vm<0>();
   bar_lds();
   xs_finish(a, xsrc, lds, red, xr);
-  mark(a, 0);
+  if (!xready) mark(a, 0);
   if (r.pe > r.pb) {   // the pre-loaded prefix
     int row, ks;
     split(r.pb, row, ks);
@@ -977,10 +978,12 @@ __device__ __forceinline__ gptr<const uint16_t> packed_block(const KArgs& a, int
   }
 }
 
-// One pass: row blocks [rb0, rb0 + NRB) over the wavefront's k-steps [ks0, ks1).
+// One pass: row blocks [rb0, min(rb0 + NRB, rb1)) over the wavefront's
+// k-steps [ks0, ks1) (blocks from rb1 on belong to other wavefronts: their
+// loads repeat block rb1 - 1 and their sums are dropped).
 template <int NRB, int KG>
 __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
-                                          float* acc, int nrows, int rb0, int ks0, int ks1) {
+                                          float* acc, int nrows, int rb0, int rb1, int ks0, int ks1) {
   const int lane = tidx() & 63, li = lane & 15, lg = lane >> 4;
   const int K = op.K, B = a.B;
   const int nkg = (ks1 - ks0 + KG - 1) / KG;
@@ -991,8 +994,8 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
   gptr<const uint16_t> rows[NRB];
 #pragma unroll
   for (int r = 0; r < NRB; ++r)
-    rows[r] = a.wpacked ? packed_block(a, t.type, P, t.a0, min(rb0 + r, (nrows - 1) >> 4) * 16) + lane * 8
-                        : gemv_row(a, t.type, P, t.a0, min((rb0 + r) * 16 + li, nrows - 1));
+    rows[r] = a.wpacked ? packed_block(a, t.type, P, t.a0, min(min(rb0 + r, rb1 - 1), (nrows - 1) >> 4) * 16) + lane * 8
+                        : gemv_row(a, t.type, P, t.a0, min(min(rb0 + r, rb1 - 1) * 16 + li, nrows - 1));
   uint4 wv[NRB][KG];
   float4 xr[2 * KG];
   XOp xo[KG];
@@ -1054,14 +1057,14 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (rb0 + r) * 16 + lg * 4 + i;
-      if (li < B && row < nrows) atomicAdd(&acc[row * B + li], c[r][i]);
+      if (li < B && row < nrows && rb0 + r < rb1) atomicAdd(&acc[row * B + li], c[r][i]);
     }
 }
 
 template <int NRB, int KG>
 __device__ __forceinline__ void mfma_passes(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
-                                            float* acc, int nrows, int nrb, int ks0, int ks1) {
-  for (int rb0 = 0; rb0 < nrb; rb0 += NRB) mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, ks0, ks1);
+                                            float* acc, int nrows, int rb_lo, int rb_hi, int ks0, int ks1) {
+  for (int rb0 = rb_lo; rb0 < rb_hi; rb0 += NRB) mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, rb_hi, ks0, ks1);
 }
 
 __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds,
@@ -1079,7 +1082,14 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
   const int ks = t.type == MPK_TASK_QKV ? a.Kq : t.type == MPK_TASK_OPROJ ? a.Ko : t.type == MPK_TASK_DOWN ? a.Kd : 1;
   const int U = (K + 31) >> 5, kr = ksplit_part(ks, t.a2);
   const int kb = kr * U / ks, nks = (kr + 1) * U / ks - kb;
-  const int ks0 = kb + nks * w / kWaves, ks1 = kb + nks * (w + 1) / kWaves;
+  // A contraction of fewer than 8 k-steps per wavefront (an expert's down
+  // projection, K = 768: 3) leaves each wavefront too short a stream per row
+  // block; with enough row blocks the wavefronts split the rows instead and
+  // each walks the whole k range.
+  const bool by_rows = nks < 8 * kWaves && nrb >= kWaves;
+  const int ks0 = by_rows ? kb : kb + nks * w / kWaves, ks1 = by_rows ? kb + nks : kb + nks * (w + 1) / kWaves;
+  const int rb_lo = by_rows ? nrb * w / kWaves : 0, rb_hi = by_rows ? nrb * (w + 1) / kWaves : nrb;
+  const int nb = rb_hi - rb_lo;
   // The input rows are task-to-task data, read here with ordinary (L2-
   // cached) loads rather than agent-coherent ones, so that the tiles on one
   // XCD share one fetch per line instead of one each.  No L2 can hold a
@@ -1092,13 +1102,14 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
   // in the writer's L2 only the bytes that XCD wrote -- a write does not
   // fill the line -- so the read fetches the line, whose other bytes the
   // other tile's write-through stores have reached.
-  if (ks1 > ks0) {
+  if (ks1 > ks0 && nb > 0) {
     // weights in flight per wavefront: NRB x KG KB
-    if (nrb <= 2) mfma_passes<2, 4>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
-    else if (nrb <= 4) mfma_passes<4, 4>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
-    else mfma_passes<8, 2>(a, t, P, op, acc, nrows, nrb, ks0, ks1);
+    if (nb <= 2) mfma_passes<2, 4>(a, t, P, op, acc, nrows, rb_lo, rb_hi, ks0, ks1);
+    else if (nb <= 4) mfma_passes<4, 4>(a, t, P, op, acc, nrows, rb_lo, rb_hi, ks0, ks1);
+    else mfma_passes<8, 2>(a, t, P, op, acc, nrows, rb_lo, rb_hi, ks0, ks1);
   }
   __syncthreads();
+  mark(a, 1);
   gemv_epilogue(a, t, acc, red, kr);
 }
 
@@ -1555,61 +1566,94 @@ __device__ __forceinline__ void argmax_task(const KArgs& a, char* lds) {
 // and their probabilities, renormalised to sum 1 when norm_topk.  Slot s
 // serves the s-th smallest expert that any request chose (none: the slot is
 // idle, e = -1) for the requests that chose it, in ascending order, each
-// with its weight for that expert.  Wavefront w routes requests w, w + 8
-// (lane i holds logits i, i + 64, ...; top-k by k rounds of a wavefront
-// argmax); wavefront 0 then resolves the slot.  Result in MoeLds.
-__device__ __forceinline__ void moe_route(const KArgs& a, int l, int s, char* lds) {
+// with its weight for that expert.  Result in MoeLds.
+// moe_route_issue stages the B x E logits into LDS (direct loads, left in
+// flight so that the caller can put its own staging beside them);
+// moe_route_finish waits for them and routes, wavefront w taking requests
+// w, w + 8, ...: lane i holds logits i, i + 64, ... as order-preserving
+// integer keys; the k-th largest key is found bit by bit (32 steps of a
+// wavefront count by ballots), the chosen experts are the keys above it and
+// the lowest-index keys equal to it, stored in ascending expert order with
+// their weights; wavefront 0 then resolves the slot.
+__device__ __forceinline__ float* moe_logits(const KArgs& a, char* lds) {
+  return reinterpret_cast<float*>(lds + a.lds_moe + sizeof(MoeLds));
+}
+__device__ __forceinline__ void moe_route_issue(const KArgs& a, int l, char* lds) {
+  const int tid0 = tidx();
+  MoeLds* m = moe_lds(a, lds);
+  if (tid0 < kMaxExperts / 32) m->mask[tid0] = 0u;
+  lds_stage<4, true>(a.rlog + (int64_t)l * a.st_rlog, reinterpret_cast<char*>(moe_logits(a, lds)), a.B * a.E, tid0);
+}
+// fp32 -> uint32 with the same order (-0 and +0 equal; a NaN above +inf)
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ void moe_route_finish(const KArgs& a, int s, char* lds) {
   const int tid0 = tidx();
   const int w = tid0 >> 6, lane = tid0 & 63;
   MoeLds* m = moe_lds(a, lds);
+  const float* lg = moe_logits(a, lds);
   const int E = a.E, K = a.topk, B = a.B;
-  if (tid0 < kMaxExperts / 32) m->mask[tid0] = 0u;
-  __syncthreads();
-  gptr<const float> lg = a.rlog + (int64_t)l * a.st_rlog;
   constexpr int NJ = kMaxExperts / 64;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  lds_stage_wait();
   for (int b = w; b < B; b += kWaves) {
     float v[NJ];
+    uint32_t key[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
-      v[j] = ld_coh(lg + (int64_t)b * E + min(e, E - 1));
+      v[j] = lg[b * E + min(e, E - 1)];
+      key[j] = e < E ? order_key(v[j]) : 0u;   // (every real key is above 0: -inf maps to 0x007fffff)
       if (e >= E) v[j] = -INFINITY;
+    }
+    // the k-th largest key
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) cnt += __builtin_popcountll(__ballot(key[j] >= c));
+      if (cnt >= K) T = c;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) gt += __builtin_popcountll(__ballot(key[j] > T));
+    const int need = K - gt;   // keys equal to T that are chosen, lowest index first
+    bool ch[NJ];
+    int taken = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const unsigned long long eq = __ballot(key[j] == T);
+      ch[j] = key[j] > T || (key[j] == T && taken + __builtin_popcountll(eq & below) < need);
+      taken += __builtin_popcountll(eq);
     }
     float mx = v[0];
 #pragma unroll
     for (int j = 1; j < NJ; ++j) mx = fmaxf(mx, v[j]);
 #pragma unroll
     for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
-    float z = 0.f;
+    float p[NJ], pc = 0.f, pa = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) z += lane + 64 * j < E ? expf(v[j] - mx) : 0.f;
-    z = wave_sum(z);
-    int my_id = 0;
-    float my_p = 0.f, chosen = 0.f;
-    for (int i = 0; i < K; ++i) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (lane + 64 * j < E && v[j] > bv) { bv = v[j]; bi = lane + 64 * j; }   // increasing j: lower index kept
-#pragma unroll
-      for (int k = 1; k < 64; k <<= 1) {
-        const float ov = __shfl_xor(bv, k);
-        const int oi = __shfl_xor(bi, k);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      bi = min(bi, E - 1);   // (only a NaN logit leaves no candidate)
-      const float p = expf(bv - mx) / z;
-      if (lane == i) { my_id = bi; my_p = p; }
-      chosen += p;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (lane + 64 * j == bi) v[j] = -INFINITY;
+    for (int j = 0; j < NJ; ++j) {
+      p[j] = lane + 64 * j < E ? expf(v[j] - mx) : 0.f;
+      pa += p[j];
+      pc += ch[j] ? p[j] : 0.f;
     }
-    if (lane < K) {
-      m->cid[b][lane] = my_id;
-      m->cw[b][lane] = a.norm_topk ? my_p / chosen : my_p;
-      atomicOr(&m->mask[my_id >> 5], 1u << (my_id & 31));
+    const float den = wave_sum(a.norm_topk ? pc : pa);
+    int pos = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const unsigned long long cm = __ballot(ch[j]);
+      const int at = pos + __builtin_popcountll(cm & below);
+      if (ch[j] && at < kMaxTopK) {
+        const int e = lane + 64 * j;
+        m->cid[b][at] = e;
+        m->cw[b][at] = p[j] / den;
+        atomicOr(&m->mask[e >> 5], 1u << (e & 31));
+      }
+      pos += __builtin_popcountll(cm);
     }
   }
   __syncthreads();
@@ -1641,21 +1685,29 @@ __device__ __forceinline__ void moe_route(const KArgs& a, int l, int s, char* ld
   __syncthreads();
 }
 
-// An expert tile of slot s = t.a2: gate/up tiles route (moe_route), and tile
-// 0 of the slot stores the route record [expert, count, tokens[B],
+// An expert tile of slot s = t.a2: gate/up tiles route (moe_route_*), and
+// tile 0 of the slot stores the route record [expert, count, tokens[B],
 // weights[B]] that the slot's down tiles read instead of routing again.  An
 // idle slot's gate/up tiles write zeros; its down tiles do nothing.
 // Otherwise the slot's expert's matrices are a projection over the slot's
-// tokens: batch 1, the one token's row; batch > 1, the tokens' rows gathered
-// into the matrix-core tile's columns.
+// tokens: batch 1, the one token's row, staged in LDS while the routing's
+// loads are in flight; batch > 1, the tokens' rows gathered into the
+// matrix-core tile's columns.
 __device__ __forceinline__ void expert_task(const KArgs& a, const DevTask& t, const TaskPtrs& P0, char* lds) {
   const int tid0 = tidx();
   const int l = t.layer, s = t.a2, B = a.B, rw = 2 + 2 * B;
   const bool gu = t.type == MPK_TASK_EXPERT_GU;
   MoeLds* m = moe_lds(a, lds);
   gptr<int32_t> rec = a.route + (int64_t)l * a.st_route + (int64_t)s * rw;
+  // batch 1: the input row (h2_l, or the slot's gate/up output) goes to LDS now
+  if (B == 1) {
+    const XSrc x = gemv_xsrc(a, t, P0);
+    lds_stage<16, true>(x.v1, lds, (gu ? a.H : a.Fe) / 4, tid0);
+  }
   if (gu) {
-    moe_route(a, l, s, lds);
+    moe_route_issue(a, l, lds);
+    moe_route_finish(a, s, lds);
+    mark(a, 0);
     if (t.a0 == 0 && tid0 < rw) {
       const int n = m->n, j = tid0 - 2, k = tid0 - 2 - B;
       const int32_t v = tid0 == 0 ? m->e
@@ -1681,7 +1733,9 @@ __device__ __forceinline__ void expert_task(const KArgs& a, const DevTask& t, co
         m->w[k] = __int_as_float(v);
       }
     }
+    if (B == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // (the staged row, too)
     __syncthreads();
+    mark(a, 0);
     if (__builtin_amdgcn_readfirstlane(*bad)) return;
   }
   const int e = __builtin_amdgcn_readfirstlane(m->e), n = __builtin_amdgcn_readfirstlane(m->n);
@@ -1705,7 +1759,7 @@ __device__ __forceinline__ void expert_task(const KArgs& a, const DevTask& t, co
                          : GemvOp{a.Fe, 1, a.a + (int64_t)l * a.st_a + (int64_t)s * B * a.Fe, nullptr, n};
     gemv_mfma(a, t, P, lds, op);
   } else {
-    gemv_b1<4>(a, t, P, lds, false);
+    gemv_b1<4>(a, t, P, lds, false, true);
   }
 }
 

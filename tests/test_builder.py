@@ -336,8 +336,8 @@ def test_moe_full_graph(name):
         # 8 slots; one gate/up and one down tile per worker and slot: 32 each; 32 router tiles
         assert (p["t_router"], p["t_egu"], p["t_edown"], p["k_down"]) == (32, 32, 32, 1)
     else:
-        # 128 slots; 4 tiles per slot (a tile's accumulators: columns x rows x 16 requests <= 8192)
-        assert (p["t_router"], p["t_egu"], p["t_edown"]) == (8, 4, 4) and M == 128
+        # 128 slots; 6 tiles per slot: about two per worker over the ~82 slots a uniform routing keeps busy
+        assert (p["t_router"], p["t_egu"], p["t_edown"]) == (8, 6, 6) and M == 128
     h = ex["header"]
     assert h["n_empty"] / h["NT"] < (0.01 if s.batch == 1 else 0.05)   # "deep, not wide"
 

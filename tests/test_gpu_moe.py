@@ -157,6 +157,34 @@ def test_tiny_moe_routing_shapes(B, kw):
     check_moe_step(r, inp, logits, nxt)
 
 
+@pytest.mark.parametrize("B,zero", [(1, range(8)), (3, range(8)), (1, range(4, 8)), (3, range(4, 8)),
+                                    (16, range(2, 8, 2))])
+def test_tiny_moe_exact_ties(B, zero):
+    """Router rows of some experts set to zero: their logits are exactly 0 for
+    every token, so the choice between them is an exact tie, which goes to the
+    lowest index (all rows zero: experts 0..k-1 with weight 1/k each).  Here
+    the kernel's sets must equal the oracle's exactly, whatever the margin."""
+    say("tiny_moe ties", B, list(zero))
+    inp = device_inputs(moe_shape(B), seed=71 + B, gamma="uniform")
+    for lw in inp["weights"]["layers"]:
+        lw["router"][list(zero)] = 0
+    r = Runner(inp)
+    logits, nxt = r.run("mega")
+    routes = gpu_routes(r.g, inp["shape"])
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    k = inp["shape"].top_k
+    for l in range(inp["shape"].n_layers):
+        for b in range(B):
+            want = [int(e) for e in cap[l]["expert_ids"][b]]
+            assert set(routes[l][b]) == set(want), (l, b, routes[l][b], want)
+            np.testing.assert_allclose([routes[l][b][e] for e in want], cap[l]["expert_weights"][b], atol=W_ATOL)
+            if len(zero) == 8:
+                assert sorted(routes[l][b]) == list(range(k))
+                np.testing.assert_allclose(list(routes[l][b].values()), 1.0 / k, rtol=1e-6)
+    check(logits, nxt, ref, ref_next)
+
+
 def test_tiny_moe_consecutive_steps():
     """Three steps on one graph with different inputs each: the layer outputs
     that the experts add into start every step at zero."""
