@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--params", default="{}",
                     help="build parameters (JSON object of mpk_build_params fields, e.g. '{\"s_attn\": 16}') for "
                          "the ablations; the default build is the one measured")
+    ap.add_argument("--skew", action="store_true",
+                    help="batch > 1: one request at the longest context (max_seq_len - 1), the others at 256 "
+                         "(the skewed batch of the scheduling-policy ablation)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the step, run a plain device copy of this many MiB three times (a known-size "
                          "kernel for scaling the HBM byte counters of a profiler run)")
@@ -170,7 +173,10 @@ def main():
 
     s = synth.SHAPES[args.config]
     print(f"[bench] generating {s.name} inputs", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(s, seed=args.seed, device="cuda")
+    lens = None
+    if args.skew:
+        lens = [s.max_seq_len - 1] + [256] * (s.batch - 1)
+    inp = synth.make_inputs(s, seed=args.seed, device="cuda", seq_lens=lens)
     kv = inp["kv"]
     ids = inp["token_ids"].cuda()
     lens = inp["seq_lens"].cuda()
@@ -227,8 +233,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (random-init bf16 weights, N(0,1) KV)",
         "config": {"workload": f"{s.name} decode step, batch {s.batch}, "
-                               f"{'ctx ' + str(s.ctx) if s.ctx_range is None else 'ctx U' + str(list(s.ctx_range))}, "
-                               f"page {s.page_size}",
+                               + (f"ctx skewed: one at {s.max_seq_len - 1}, {s.batch - 1} at 256" if args.skew else
+                                  f"{'ctx ' + str(s.ctx) if s.ctx_range is None else 'ctx U' + str(list(s.ctx_range))}")
+                               + f", page {s.page_size}",
                    "global_batch": s.batch, "seq_len": int(max(inp['seq_lens'].tolist())) + 1,
                    "parallelism": "single GPU", "workers": hdr["n_workers"], "sched_waves": hdr["n_sched_waves"],
                    "s_attn": hdr["s_attn"], "weights": "prepared" if args.prepared else "row-major",

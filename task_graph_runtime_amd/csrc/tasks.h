@@ -775,6 +775,10 @@ __device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* l
 // first and the first chunk's loads right behind them, so both round trips
 // overlap; the wait for x leaves that chunk in flight.  Loads past the tile's
 // last segment repeat it, so the wait counts stay static.
+#ifndef MPK_B1_CHUNK
+#define MPK_B1_CHUNK 4
+#endif
+constexpr int kB1Chunk = MPK_B1_CHUNK;   // weight segments per chunk of a batch-1 tile (two chunks in flight)
 template <int D>
 __device__ __forceinline__ void gemv_b1(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds, bool pre,
                                         bool xready = false) {
@@ -1759,7 +1763,7 @@ __device__ __forceinline__ void expert_task(const KArgs& a, const DevTask& t, co
                          : GemvOp{a.Fe, 1, a.a + (int64_t)l * a.st_a + (int64_t)s * B * a.Fe, nullptr, n};
     gemv_mfma(a, t, P, lds, op);
   } else {
-    gemv_b1<4>(a, t, P, lds, false, true);
+    gemv_b1<kB1Chunk>(a, t, P, lds, false, true);
   }
 }
 
@@ -1799,7 +1803,7 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
     case MPK_TASK_LMHEAD:
     case MPK_TASK_ROUTER:
       if (a.B > 1) gemv_mfma(a, t, P, lds, gemv_op(a, t));
-      else gemv_b1<4>(a, t, P, lds, pre);
+      else gemv_b1<kB1Chunk>(a, t, P, lds, pre);
       break;
     case MPK_TASK_EXPERT_GU:
     case MPK_TASK_EXPERT_DOWN:
