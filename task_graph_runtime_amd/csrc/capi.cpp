@@ -664,8 +664,8 @@ uint64_t timeout_ticks(const mpk_tgraph* t) {
 
 int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const mpk_build_params* params,
                mpk_tgraph** out) {
+  if (out) *out = nullptr;
   if (!cfg || !out) return fail(MPK_ERR_INVALID_ARG, "null argument");
-  *out = nullptr;
   const bool host_only = params && params->host_only;
   int n_cus = 256;
   if (!host_only) {

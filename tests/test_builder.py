@@ -273,6 +273,20 @@ def test_bad_build_args_rejected(B, P, params, code):
     assert e.value.code == code
 
 
+def test_failed_build_clears_the_handle():
+    """On every error, including a null config, *out is NULL afterwards."""
+    h = C.c_void_p(0x1)
+    p = mpk.mpk_build_params()
+    p.host_only = 1
+    assert mpk.lib().mpk_build_tgraph_ex(None, 1, 16, C.byref(p), C.byref(h)) == -1
+    assert h.value is None
+    h = C.c_void_p(0x1)
+    c = mpk.model_cfg(synth.SHAPES["tiny"].cfg())
+    c.head_dim = 96
+    assert mpk.lib().mpk_build_tgraph_ex(C.byref(c), 1, 16, C.byref(p), C.byref(h)) == -2
+    assert h.value is None
+
+
 def test_host_only_graph_refuses_to_run():
     g = mpk.TGraph(synth.SHAPES["tiny"].cfg(), 1, 16, {}, host_only=True)
     w = mpk.mpk_weights()

@@ -364,6 +364,18 @@ def test_trace_happens_before_every_wait():
     for c in real:
         for p in real_producers(int(ex["task_dep"][c])):
             assert end[p] <= start[c], (p, c)
+    # the same records as a Perfetto (trace-event) document: one slice per task
+    # on its worker's track, the tracks' slices disjoint
+    from task_graph_runtime_amd import trace_export
+    doc = trace_export.chrome_trace(rec, tpu, ex, flows=True)
+    tasks = [e for e in doc["traceEvents"] if e["ph"] == "X" and e["cat"] not in ("wait", "trigger", "phase")]
+    assert sorted(e["args"]["task"] for e in tasks) == real.tolist()
+    by_w = {}
+    for e in tasks:
+        by_w.setdefault(e["tid"], []).append((e["ts"], e["ts"] + e["dur"]))
+    for sl in by_w.values():
+        sl.sort()
+        assert all(a[1] <= b[0] + 1e-6 for a, b in zip(sl, sl[1:]))
     r.g.set_trace(False)
 
 
