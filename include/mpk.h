@@ -473,6 +473,20 @@ int mpk_time_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t reps,
  * MPK_ERR_HIP. */
 int mpk_run_tasks(mpk_tgraph* g, const int32_t* tasks, int32_t n, int32_t poison);
 
+/* Recovery of a poisoned graph (the failure detection around the pages'
+ * runtime of event counters and task queues, MPK summary page, section 2 Q2:
+ * the watchdog and status word are this library's).  Waits for the graph's
+ * last step, then clears its runtime state -- every event counter and
+ * sub-counter, the scheduler and JIT rings with their persistent heads and
+ * tails, the split arrivals and the status word -- and restarts the step
+ * count, so that the next mpk_decode_step runs as the graph's first.
+ * Activations, weights and the KV cache are left as they are (a step that
+ * was cut short may have written the new token's key/value slot; the next
+ * step writes it again).  Also valid on a healthy graph.  The graph's
+ * device must be current.  Synchronises.  Errors: MPK_ERR_INVALID_ARG (null
+ * or host-only graph, another device current), MPK_ERR_HIP. */
+int mpk_reset_tgraph(mpk_tgraph* g);
+
 /* Watchdog for in-kernel waits in nanoseconds (default 2 s; 0 restores it):
  * every wait of a worker or scheduler gives up after it, reports
  * MPK_ERR_TIMEOUT and poisons the graph, so the persistent grid always

@@ -111,6 +111,7 @@ SIGNATURES = {
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32]),
     "mpk_read_tensor": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t]),
     "mpk_set_watchdog": (C.c_int, [C.c_void_p, C.c_uint64]),
+    "mpk_reset_tgraph": (C.c_int, [C.c_void_p]),
     "mpk_set_trace": (C.c_int, [C.c_void_p, C.c_int32]),
     "mpk_read_trace": (C.c_int, [C.c_void_p, C.POINTER(mpk_trace_record), C.c_int32, C.POINTER(C.c_int32),
                                  C.POINTER(C.c_double)]),
@@ -342,6 +343,10 @@ class TGraph:
 
     def set_watchdog(self, ns: int):
         _check(lib().mpk_set_watchdog(self.h, int(ns)))
+
+    def reset(self):
+        """Clear the runtime state of a (poisoned) graph; the next step runs as its first."""
+        _check(lib().mpk_reset_tgraph(self.h))
 
     def status(self) -> dict:
         s = mpk_status_word()

@@ -979,6 +979,19 @@ int mpk_read_tensor(const mpk_tgraph* g, int32_t tensor, void* dst, size_t bytes
   return MPK_OK;
 }
 
+int mpk_reset_tgraph(mpk_tgraph* g) {
+  if (!g || g->host_only) return fail(MPK_ERR_INVALID_ARG, g ? "host-only graph" : "null argument");
+  int dev = -1;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev != g->device) return fail(MPK_ERR_INVALID_ARG, "the graph's device is not the current device");
+  if (g->last_stream) HIPCHK(hipStreamSynchronize(g->last_stream));
+  else HIPCHK(hipDeviceSynchronize());
+  HIPCHK(hipMemset(g->d_rt, 0, (size_t)g->rt_bytes));
+  HIPCHK(hipDeviceSynchronize());
+  g->epoch = 0;
+  return MPK_OK;
+}
+
 int mpk_set_watchdog(mpk_tgraph* g, uint64_t timeout_ns) {
   if (!g) return fail(MPK_ERR_INVALID_ARG, "null argument");
   g->timeout_ns = timeout_ns ? timeout_ns : 2000000000ull;

@@ -287,6 +287,12 @@ def test_failed_build_clears_the_handle():
     assert h.value is None
 
 
+def test_reset_refuses_host_only_and_null():
+    g = mpk.TGraph(synth.SHAPES["tiny"].cfg(), 1, 16, {}, host_only=True)
+    assert mpk.lib().mpk_reset_tgraph(g.h) == -1
+    assert mpk.lib().mpk_reset_tgraph(None) == -1
+
+
 def test_host_only_graph_refuses_to_run():
     g = mpk.TGraph(synth.SHAPES["tiny"].cfg(), 1, 16, {}, host_only=True)
     w = mpk.mpk_weights()

@@ -282,6 +282,38 @@ def test_bad_token_id_reported_not_faulting():
     assert r.g.status()["code"] == -1
 
 
+def test_reset_recovers_a_poisoned_graph():
+    """mpk_reset_tgraph: a graph poisoned by a watchdog timeout, then by a bad
+    token id, runs correct steps again after a reset (several in a row, on
+    the restarted counters)."""
+    say("reset after poison")
+    for B in (1, 3):
+        s = TINY.with_(batch=B, ctx_range=(5, 130), ctx=0) if B > 1 else TINY
+        inp = device_inputs(s, seed=4)
+        refs = run_oracle(inp)
+        r = Runner(inp)
+        r.run("mega")
+        r.g.set_watchdog(1)
+        r.g.decode_step(r.w, inp["token_ids_dev"], r.kv, inp["seq_lens_dev"], r.logits, r.next)
+        torch.cuda.synchronize()
+        assert r.g.status()["code"] == -5
+        r.g.set_watchdog(0)
+        r.g.reset()
+        assert r.g.status()["code"] == 0
+        for _ in range(3):
+            logits, nxt = r.run("mega")
+            check(logits, nxt, *refs)
+        bad = inp["token_ids_dev"].clone()
+        bad[0] = s.vocab + 7
+        r.g.decode_step(r.w, bad, r.kv, inp["seq_lens_dev"], r.logits, r.next)
+        torch.cuda.synchronize()
+        assert r.g.status()["code"] == -1
+        r.g.reset()
+        for _ in range(2):
+            logits, nxt = r.run("mega")
+            check(logits, nxt, *refs)
+
+
 # ------------------------------------------------------------------ real shapes
 def _full(name, seed=0, modes=("mega",), lazy=False, builds=()):
     s = synth.SHAPES[name]
