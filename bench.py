@@ -41,15 +41,16 @@ def algorithmic_bytes(s, seq_lens, experts=None) -> int:
     return 2 * (w + len(seq_lens) * H + kv)
 
 
-SOURCE_FILES = ("include/mpk.h",)
+SOURCE_FILES = ("include/mpk.h", "task_graph_runtime_amd/build.py")   # (the build flags shape the kernels too)
 SOURCE_DIR = "task_graph_runtime_amd/csrc"
 TRAFFIC_FILE = "profiles/megakernel_{config}_traffic.txt"
 
 
 def source_hash(params: dict) -> str:
-    """sha256 over every library source (the C ABI header and all of csrc/)
-    and the graph's resolved build parameters: the HBM-traffic counters of a
-    profile are valid only for the build and graph they were taken on."""
+    """sha256 over every library source (the C ABI header, all of csrc/ and
+    the build script with its compiler flags) and the graph's resolved build
+    parameters: the HBM-traffic counters of a profile are valid only for the
+    build and graph they were taken on."""
     import hashlib
     h = hashlib.sha256()
     files = list(SOURCE_FILES) + sorted(os.path.join(SOURCE_DIR, f) for f in os.listdir(os.path.join(ROOT, SOURCE_DIR))
