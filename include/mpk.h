@@ -142,7 +142,12 @@ typedef struct {
                          /* the exported header holds the resolved value (1, 2 or 3)      */
   int32_t weight_preload; /* 0 default (on), 1 on, 2 off: batch-1 projection tiles load   */
                           /* their first weight segments before their event fires (the   */
-                          /* cross-task pipelining ablation); the header holds 1 or 2    */
+                          /* cross-task pipelining ablation); 3 paged lookahead: the     */
+                          /* pre-load area is two pages and a worker stages its next two */
+                          /* AOT tasks -- projection weights, or an attention split's    */
+                          /* cached keys and values -- into page (AOT index mod 2) (MPK  */
+                          /* summary page, section 5 techniques inventory: cross-task    */
+                          /* pipelining, paged shared memory); the header holds 1, 2, 3  */
   int32_t coarse_events;  /* 0 default (fine-grained events), 1 the operator-level graph: */
                           /* an attention split waits for every q/k/v tile, not only its */
                           /* own kv group's (every other operator already waits for the  */

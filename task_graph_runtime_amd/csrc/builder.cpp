@@ -71,7 +71,7 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   if (p.fusion_order < 0 || p.fusion_order > 1) return uns("fusion_order must be 0 (Def 4.1 then Def 4.2) or 1 (none)");
   if (p.aot_policy != 0) return uns("only AOT policy 0 (round-robin in linear order) is implemented");
   if (p.attn_jit < 0 || p.attn_jit > 3) return bad("attn_jit must be 0, 1, 2 or 3");
-  if (p.weight_preload < 0 || p.weight_preload > 2) return bad("weight_preload must be 0, 1 or 2");
+  if (p.weight_preload < 0 || p.weight_preload > 3) return bad("weight_preload must be 0, 1, 2 or 3");
   Params r;
   // scheduling policy: 1 is the hybrid policy (attention JIT, the rest
   // AOT), 3 every task JIT, 2 every task AOT.  The default is AOT at every
@@ -81,6 +81,7 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
   r.jit_all = p.attn_jit == 3;
   r.jit_attn = r.jit_all || p.attn_jit == 1;
   r.preload = p.weight_preload != 2;
+  r.lookahead = p.weight_preload == 3;
   if (p.coarse_events < 0 || p.coarse_events > 1) return bad("coarse_events must be 0 or 1");
   r.coarse = p.coarse_events == 1;
   r.fusion = p.fusion_order;

@@ -37,6 +37,7 @@ struct Params {
   bool jit_attn = true;   // attention tasks JIT (else AOT)
   bool jit_all = false;   // every non-empty task JIT (scheduling ablation)
   bool preload = true;    // weight pre-load of the next AOT projection tile
+  bool lookahead = false; // paged lookahead: the next two AOT tasks staged into two LDS pages
   bool coarse = false;    // operator-level graph: attention waits for all q/k/v tiles
   int32_t fusion = 0;     // 0: Def 4.1 then Def 4.2; 1: none (one event per overlap edge)
   int32_t split_pages = 2;  // minimum KV pages per attention split (run time)

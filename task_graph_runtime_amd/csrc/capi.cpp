@@ -18,7 +18,8 @@
 #include "rt.h"
 
 namespace mpk {
-hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
+hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream,
+                             bool lookahead);
 hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count, hipStream_t stream);
 hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream);
 int64_t packed_bytes(int64_t N, int64_t K);
@@ -657,6 +658,10 @@ void rebase(T*& p, const void* from, int64_t n, char* to) {
   if (p && c >= f && c < f + n) p = reinterpret_cast<T*>(to + (c - f));
 }
 
+// The paged lookahead's kernel runs the graph (weight_preload 3, and a
+// pre-load area that splits into two pages).
+bool lookahead(const mpk_tgraph* t) { return t->prm.lookahead && t->base.pf_segs >= 2; }
+
 uint64_t timeout_ticks(const mpk_tgraph* t) {
   uint64_t v = (uint64_t)((double)t->timeout_ns * t->wall_khz / 1e6);
   return v < 1 ? 1 : v;
@@ -686,7 +691,7 @@ int build_impl(const mpk_model_cfg* cfg, int32_t batch, int32_t page_size, const
   r.n_workers = prm.W; r.n_sched_waves = prm.S_sched; r.quantum = prm.q; r.t_qkv = prm.T_qkv; r.t_o = prm.T_o;
   r.t_gu = prm.T_gu; r.t_down = prm.T_down; r.t_lm = prm.T_lm; r.s_attn = prm.S_attn; r.host_only = host_only;
   r.attn_jit = prm.jit_all ? 3 : prm.jit_attn ? 1 : 2;
-  r.weight_preload = prm.preload ? 1 : 2;
+  r.weight_preload = prm.lookahead ? 3 : prm.preload ? 1 : 2;
   r.coarse_events = prm.coarse ? 1 : 0;
   r.k_qkv = prm.K_qkv; r.k_o = prm.K_o; r.k_down = prm.K_down;
   r.fusion_order = prm.fusion;
@@ -792,7 +797,7 @@ int mpk_decode_step(mpk_tgraph* g, const mpk_weights* w, const int32_t* token_id
   int rc = step_args(g, w, token_ids, kv, seq_lens, logits, next_ids, s, &a);
   if (rc) return rc;
   const uint32_t epoch = ++g->epoch;
-  hipError_t e = launch_megakernel(a, epoch, timeout_ticks(g), g->grid, s);
+  hipError_t e = launch_megakernel(a, epoch, timeout_ticks(g), g->grid, s, lookahead(g));
   if (e != hipSuccess) { --g->epoch; return hip_fail(e, "mega-kernel launch"); }
   g->last_stream = s;
   return MPK_OK;
@@ -917,7 +922,7 @@ int mpk_decode_step_noalloc(mpk_tgraph* g, const mpk_weights* w, const int32_t* 
   // counters, rings and arrivals start at zero, so the step runs as epoch 1
   e = scratch_zero(rt, (size_t)g->rt_bytes, s);
   if (e != hipSuccess) return hip_fail(e, "scratch clear");
-  e = launch_megakernel(a, 1u, timeout_ticks(g), g->grid, s);
+  e = launch_megakernel(a, 1u, timeout_ticks(g), g->grid, s, lookahead(g));
   if (e != hipSuccess) return hip_fail(e, "mega-kernel launch");
   g->last_stream = s;
   return MPK_OK;

@@ -193,6 +193,14 @@ __device__ __forceinline__ DevEvent unpack_event(uint32_t v) {
 // pre-load of the next AOT task when it is a batch-1 projection tile
 // (gemv_preload), so its first weight bytes stream in while the worker
 // triggers, waits and runs JIT tasks.
+//
+// The paged lookahead (weight_preload 3; this file compiled with MPK_LA = 1,
+// megakernel_la.hip): the pre-load area is two pages and AOT task j stages
+// into page j mod 2, so a worker has its next two AOT tasks staged --
+// projection weights (gemv_preload) or an attention split's cached keys and
+// values (attn_prestage) -- while it waits; after task j - 1 its page takes
+// task j + 1.  A task runs with its page as the pre-load area (the
+// arguments' lds_pf and pf_segs).
 __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t timeout, int w) {
   const KArgs a0 = *kp;
   int& s_cmd = reinterpret_cast<int*>(g_lds + kLdsCtl)[0];
@@ -213,6 +221,40 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
   const int trace_cap = a0.trace_cap;
   int n_trace = 0;
   uint64_t t_wait = 0, t_start = 0;
+#if MPK_LA
+  // the highest AOT index staged (-1: none)
+  int pre_i = -1;
+  // the arguments with task j's page as the pre-load area
+  auto page_args = [&](const KArgs& a, int j) {
+    KArgs b = a;
+    b.pf_segs = a.pf_segs / 2;
+    b.lds_pf = a.lds_pf + (j & 1) * kPfWaves * b.pf_segs * 1024;
+    return b;
+  };
+  auto stage = [&](const KArgs& a, int j, uint32_t v) {
+    const DevTask nt = unpack_task(v);
+    const KArgs b = page_args(a, j);
+    if (tid >= 64) {
+      if (is_gemv(nt.type)) gemv_preload(b, nt, unpack_ptrs(v), g_lds);
+      else if (nt.type == MPK_TASK_ATTN && a.B == 1) {
+        if (a.d == 128) attn_prestage<128>(b, nt, g_lds);
+        else attn_prestage<64>(b, nt, g_lds);
+      }
+    }
+  };
+  auto preload_next = [&](const KArgs& a) {
+    if (i < n_aot) {
+      if (pre_i < i) {
+        stage(a, i, nxt_v);
+        pre_i = i;
+      }
+      if (i + 1 < n_aot && pre_i < i + 1) {
+        stage(a, i + 1, fetch_words<16>(reinterpret_cast<gptr<const uint32_t>>(aot + i + 1)));
+        pre_i = i + 1;
+      }
+    }
+  };
+#else
   // index of the AOT task whose weight pre-load has been issued (-1: none)
   int pre_i = -1;
   auto preload_next = [&](const KArgs& a) {
@@ -222,6 +264,7 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
       pre_i = i;
     }
   };
+#endif
   preload_next(a0);
   while (true) {
     // the arguments are re-read (constant cache) in every iteration rather
@@ -276,9 +319,17 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
     // descriptor, whose weight pointers are resolved below)
     uint32_t cur_v;
     bool pre = false;
+#if MPK_LA
+    int page = 0;   // (the AOT index: its parity is the task's page)
+#endif
     if (cmd == CMD_AOT) {
       cur_v = nxt_v;
+#if MPK_LA
+      pre = pre_i >= i;
+      page = i;
+#else
       pre = pre_i == i;
+#endif
       ++i;
       nxt_v = fetch_words<16>(reinterpret_cast<gptr<const uint32_t>>(aot + (i < n_aot ? i : n_aot - 1)));
     } else {
@@ -296,7 +347,12 @@ __device__ __forceinline__ void worker_loop(kptr kp, uint32_t epoch, uint64_t ti
     // flight while the task runs
     const uint32_t ev_v = fetch_words<4>(reinterpret_cast<gptr<const uint32_t>>(a.events + t.trig));
     const uint32_t q_v = a.ev_quota[(int64_t)t.trig * kEvSub + (t.id & (kEvSub - 1))];
+#if MPK_LA
+    if (cmd == CMD_AOT) run_task(page_args(a, page), t, P, pre);
+    else run_task(a, t, P, false);
+#else
     run_task(a, t, P, pre);
+#endif
     wait_vm<0>();   // the task's stores are complete before its event advances
     __syncthreads();
     if (tid < 64) {
@@ -368,7 +424,12 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
 
 }  // namespace
 
-__global__ void __launch_bounds__(kThreads) mpk_megakernel(const KArgs args, uint32_t epoch, uint64_t timeout) {
+#if MPK_LA
+#define MPK_MEGAKERNEL mpk_megakernel_la
+#else
+#define MPK_MEGAKERNEL mpk_megakernel
+#endif
+__global__ void __launch_bounds__(kThreads) MPK_MEGAKERNEL(const KArgs args, uint32_t epoch, uint64_t timeout) {
   // `args` is the first kernel argument: it starts the kernel-argument segment
   const kptr kp = (kptr)(__builtin_amdgcn_kernarg_segment_ptr());
   const KArgs a = args;
@@ -382,6 +443,16 @@ __global__ void __launch_bounds__(kThreads) mpk_megakernel(const KArgs args, uin
   const int w = wg - a.n_sched_wgs;
   if (w < a.n_workers) worker_loop(kp, epoch, timeout, w);
 }
+
+#if MPK_LA
+hipError_t launch_megakernel_la(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream) {
+  KArgs a = args;
+  void* p[] = {&a, &epoch, &timeout};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mpk_megakernel_la), dim3(grid), dim3(kThreads),
+                                    p, 0, stream);
+}
+#else
+hipError_t launch_megakernel_la(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
 
 // Kernel-per-operator baseline: workgroup i runs task list[i], no events (a
 // projection tile issues its weight pre-load first, as in the persistent
@@ -413,7 +484,9 @@ hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned lon
   return hipGetLastError();
 }
 
-hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream) {
+hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream,
+                             bool lookahead) {
+  if (lookahead) return launch_megakernel_la(args, epoch, timeout, grid, stream);
   KArgs a = args;
   void* p[] = {&a, &epoch, &timeout};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mpk_megakernel), dim3(grid), dim3(kThreads), p,
@@ -424,5 +497,7 @@ hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count,
   hipLaunchKernelGGL(mpk_baseline_op, dim3(count), dim3(kThreads), 0, stream, args, list);
   return hipGetLastError();
 }
+
+#endif  // MPK_LA
 
 }  // namespace mpk

@@ -775,6 +775,9 @@ __device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* l
 // first and the first chunk's loads right behind them, so both round trips
 // overlap; the wait for x leaves that chunk in flight.  Loads past the tile's
 // last segment repeat it, so the wait counts stay static.
+#ifndef MPK_LA
+#define MPK_LA 0   // 1: the paged lookahead's kernel (megakernel_la.hip)
+#endif
 #ifndef MPK_B1_CHUNK
 #define MPK_B1_CHUNK 4
 #endif
@@ -1235,6 +1238,93 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
   else merge([&](int i) { return ld_coh(part + i); });
 }
 
+#if MPK_LA
+// (compiled into the paged lookahead's kernel only, megakernel_la.hip)
+// The split of slot s at batch 1 from the one request's cached length Lb
+// (the allocation attn_task makes): S = min(S_attn, staging capacity,
+// ceil(pages / Tmin)) splits, at least 1 (a slot s >= S is idle); split s
+// covers pages [j0, j1) and cached tokens [t0, tc1) (the new token at Lb is
+// not cached yet).
+struct AttnSplit {
+  int S, j0, j1, t0, tc1;
+  bool ok;
+};
+__device__ __forceinline__ AttnSplit attn_split_b1(const KArgs& a, int s, int Lb) {
+  AttnSplit r;
+  const int P = a.P;
+  r.ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
+  const int ntok = r.ok ? Lb + 1 : 0;
+  const int nb = (ntok + P - 1) / P;
+  r.S = max(1, min(min(a.S_attn, attn_stage_cap(a)), (nb + a.attn_min_pages - 1) / a.attn_min_pages));
+  r.j0 = (int)((int64_t)s * nb / r.S);
+  r.j1 = (int)((int64_t)(s + 1) * nb / r.S);
+  r.t0 = r.j0 * P;
+  r.tc1 = min(min(r.j1 * P, ntok), ntok - 1);
+  return r;
+}
+
+// Attention staging of the paged lookahead (batch 1, attention AOT): while
+// the worker waits, wavefronts 1..7 copy the cached keys and values of its
+// next attention split into that task's pre-load page (a.lds_pf, a.pf_segs:
+// the page) -- the cached keys and values are the caller's cache, constant
+// during the step; only the new token comes from the q/k/v projection.
+// Page layout: the header (valid, staged tokens n, the length Lb it was
+// computed for), then the K rows [n][D] and the V rows [n][D], bf16.  n is
+// every cached token of the split when they fit, else the largest multiple
+// of 32 that fits (the split streams the rest).  Direct global -> LDS loads,
+// 64 consecutive 16-byte units each (the rows gathered from their pages); a
+// token on a bad page is staged from page 0 and skipped by the split, which
+// reports the page.
+struct AttnPre {
+  int32_t valid, n, lb, pad;
+};
+constexpr int kPreUnits = kMaxPfSegs;   // direct loads per pre-staging lane, at most
+__device__ __forceinline__ int attn_pre_cap(const KArgs& a, int D) {
+  // (a load writes a whole 1 KB chunk: the last may pass the rows by up to 1 KB)
+  const int area = kPfWaves * min(a.pf_segs, kMaxPfSegs) * 1024 - (int)sizeof(AttnPre) - 1024;
+  return max(0, area / (4 * D));   // tokens whose K and V rows fit
+}
+template <int D>
+__device__ __forceinline__ void attn_prestage(const KArgs& a, const DevTask& t, char* lds) {
+  const int tid0 = tidx();
+  const int w = tid0 >> 6, lane = tid0 & 63;   // wavefronts 1..7
+  constexpr int UPR = D / 8;                    // 16-byte units of one row
+  const int Lb = a.seq_lens[0];
+  const AttnSplit sp = attn_split_b1(a, t.a0, Lb);
+  const int ncached = (t.a0 < sp.S && sp.ok) ? max(0, sp.tc1 - sp.t0) : 0;
+  const int cap = attn_pre_cap(a, D);
+  const int n = ncached <= cap ? ncached : (cap & ~31);
+  const int nunits = 2 * n * UPR;
+  char* kv = lds + a.lds_pf + sizeof(AttnPre);
+  const int64_t page_stride = (int64_t)a.hkv * a.P * D;
+  gptr<const uint16_t> kb = a.k_pool + ((int64_t)t.layer * a.n_pages * a.hkv + t.a1) * a.P * D;
+  gptr<const uint16_t> vb = a.v_pool + ((int64_t)t.layer * a.n_pages * a.hkv + t.a1) * a.P * D;
+  int pid[kPreUnits];
+#pragma unroll
+  for (int k = 0; k < kPreUnits; ++k) {
+    const int un = min(((w - 1) + k * kPfWaves) * 64 + lane, max(nunits - 1, 0));
+    const int row = un / UPR, tok = sp.t0 + (row < n ? row : row - n);
+    pid[k] = a.page_table[min(tok / a.P, a.max_pages - 1)];
+  }
+#pragma unroll
+  for (int k = 0; k < kPreUnits; ++k) {
+    const int c = (w - 1) + k * kPfWaves;
+    if (c * 64 < nunits) {
+      const int un = min(c * 64 + lane, nunits - 1);
+      const int row = un / UPR, part = un - row * UPR;
+      const bool isk = row < n;
+      const int tok = sp.t0 + (isk ? row : row - n);
+      const int pg = (pid[k] >= 0 && pid[k] < a.n_pages) ? pid[k] : 0;
+      const int64_t off = (int64_t)pg * page_stride + (int64_t)(tok % a.P) * D + part * 8;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<gptr<const uint4>>((isk ? kb : vb) + off),
+                                       (lds_void)(kv + c * 64 * 16), 16, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (tid0 == 64) *reinterpret_cast<AttnPre*>(lds + a.lds_pf) = AttnPre{1, n, Lb, 0};
+}
+#endif
+
 // Task of slot j of kv group g, serving split s of the S splits of request b
 // (attn_slot): decode attention of request b's new query against pages
 // [floor(s n_b / S), floor((s+1) n_b / S)) of its n_b = ceil((L_b + 1) / P)
@@ -1257,8 +1347,14 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
 //     (layer, b, g) arrival counter; the one that completes it (S arrivals)
 //     merges the request's S partials into the attention output
 //     (attn_combine) and resets the counter.
+// (the paged lookahead's kernel: the split may find its first cached keys
+// and values staged in its pre-load page, attn_prestage, when pre is set)
 template <int D, int R, int GM>
-__device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, const TaskPtrs& Pw, char* lds) {
+__device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, const TaskPtrs& Pw, char* lds
+#if MPK_LA
+                                          , bool pre
+#endif
+                                          ) {
   const int tid0 = tidx();
   constexpr int DPL = D / R;            // dims per lane
   constexpr int RPW = 64 / R;           // rows per wavefront
@@ -1295,7 +1391,14 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
     }
   }
 
+#if MPK_LA
+  const AttnPre hp = *reinterpret_cast<const AttnPre*>(lds + a.lds_pf);
+  const bool staged = pre && a.B == 1 && hp.valid;
+  const int npre = staged ? hp.n : 0;
+  const int Lb = staged ? hp.lb : a.seq_lens[b];   // (the length the staging read, the same value)
+#else
   const int Lb = a.seq_lens[b];
+#endif
   const bool ok = Lb >= 0 && Lb < a.max_seq && (Lb / P) < a.max_pages;
   const int ntok = ok ? Lb + 1 : 0;
   const int nb = (ntok + P - 1) / P;
@@ -1423,8 +1526,23 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
     }
     process(kf, vf);
   };
+#if MPK_LA
+  if (npre > 0) {   // the staged tokens [t0, t0 + npre), from the page
+    const uint16_t* kl = reinterpret_cast<const uint16_t*>(lds + a.lds_pf + sizeof(AttnPre));
+    const uint16_t* vl = kl + (int64_t)npre * D;
+    for (int it = t0 + w * RPW; it < t0 + npre; it += TPI) {
+      const int tok = it + row;
+      if (tok < t0 + npre && good(tok))
+        process_bf(*reinterpret_cast<const KV*>(kl + (tok - t0) * D + lr * DPL),
+                   *reinterpret_cast<const KV*>(vl + (tok - t0) * D + lr * DPL));
+    }
+  }
+  if (tc1 > t0 + npre) {
+    const int base = t0 + npre + w * RPW;   // the wavefront's first token of each iteration (uniform)
+#else
   if (tc1 > t0) {
     const int base = t0 + w * RPW;   // the wavefront's first token of each iteration (uniform)
+#endif
     int tok = base + row;
     KV k0, v0, k1, v1;
     int64_t o = offs(tok);
@@ -1811,11 +1929,19 @@ __device__ __forceinline__ void run_task(const KArgs& a, const DevTask& t, const
       break;
     case MPK_TASK_ATTN:
       if (a.d == 128) {
+#if MPK_LA
+        if (a.G <= 4) attn_task<128, 16, 4>(a, t, P, lds, pre);
+        else attn_task<128, 32, 8>(a, t, P, lds, pre);
+      } else {
+        attn_task<64, 16, 8>(a, t, P, lds, pre);
+      }
+#else
         if (a.G <= 4) attn_task<128, 16, 4>(a, t, P, lds);
         else attn_task<128, 32, 8>(a, t, P, lds);
       } else {
         attn_task<64, 16, 8>(a, t, P, lds);
       }
+#endif
       break;
     case MPK_TASK_ARGMAX:
       argmax_task(a, lds);

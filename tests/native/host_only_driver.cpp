@@ -25,7 +25,7 @@ namespace mpk {
   std::fprintf(stderr, "host-only run reached device path %s\n", f);
   std::abort();
 }
-hipError_t launch_megakernel(const KArgs&, uint32_t, uint64_t, int, hipStream_t) { device_path("launch_megakernel"); }
+hipError_t launch_megakernel(const KArgs&, uint32_t, uint64_t, int, hipStream_t, bool) { device_path("launch_megakernel"); }
 hipError_t launch_baseline_op(const KArgs&, const int32_t*, int, hipStream_t) { device_path("launch_baseline_op"); }
 hipError_t launch_time_task(const KArgs&, int, bool, unsigned long long*, hipStream_t) { device_path("launch_time_task"); }
 int64_t packed_bytes(int64_t, int64_t) { device_path("packed_bytes"); }

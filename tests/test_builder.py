@@ -132,11 +132,11 @@ def test_coarse_operator_level_graph(B):
 
 def test_weight_preload_switch():
     s = synth.SHAPES["tiny"]
-    for v, want in ((0, 1), (1, 1), (2, 2)):
+    for v, want in ((0, 1), (1, 1), (2, 2), (3, 3)):
         p = mpk.TGraph(s.cfg(), 1, s.page_size, dict(weight_preload=v), host_only=True).header()["params"]
         assert p["weight_preload"] == want
     with pytest.raises(mpk.MpkError):
-        mpk.TGraph(s.cfg(), 1, s.page_size, dict(weight_preload=3), host_only=True)
+        mpk.TGraph(s.cfg(), 1, s.page_size, dict(weight_preload=4), host_only=True)
 
 
 def test_k_split_default_yields_to_a_given_tile_count():

@@ -163,10 +163,12 @@ def test_tiny_k_split(K, mode):
 
 
 @pytest.mark.parametrize("B", [1, 3])
-@pytest.mark.parametrize("params", [dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2), dict(coarse_events=1)])
+@pytest.mark.parametrize("params", [dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2), dict(coarse_events=1),
+                                    dict(weight_preload=3), dict(weight_preload=3, attn_jit=1)])
 def test_tiny_scheduling_ablations(B, params):
-    """The ablation builds: every task JIT, attention JIT, no weight pre-load
-    and the operator-level graph, each against the oracle."""
+    """The ablation builds: every task JIT, attention JIT, no weight pre-load,
+    the operator-level graph and the paged lookahead (its own kernel; with
+    attention JIT only the projections are staged), each against the oracle."""
     s = TINY.with_(batch=B, ctx_range=(3, 120), ctx=0)
     say("tiny ablation", B, params)
     inp = device_inputs(s, seed=51 + B, gamma="uniform")
@@ -344,11 +346,29 @@ def test_qwen3_0p6b_shape():
     _full("qwen3_0p6b", modes=("mega", "base"))
 
 
+@pytest.mark.parametrize("s_attn", [1, 2, 4])
+def test_lookahead_long_splits(s_attn):
+    """The paged lookahead with attention splits of 64 to 256 cached tokens at
+    head_dim 64: a split whose keys and values outgrow its page stages the
+    first 32k tokens and streams the rest."""
+    s = TINY.with_(ctx=250)
+    say("lookahead long splits", s_attn)
+    inp = device_inputs(s, seed=70 + s_attn, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    r = Runner(inp, dict(weight_preload=3, s_attn=s_attn, n_workers=8))
+    for _ in range(2):
+        logits, nxt = r.run("mega")
+        check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+
+
 @pytest.mark.timeout(600)
 def test_qwen3_8b_shape():
     # (with the scheduling and pre-load ablation builds that the measurements compare)
     _full("qwen3_8b", modes=("mega", "graph"), lazy=True,
-          builds=(dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2), dict(coarse_events=1)))
+          builds=(dict(attn_jit=3), dict(attn_jit=1), dict(weight_preload=2), dict(coarse_events=1),
+                  dict(weight_preload=3)))
 
 
 @pytest.mark.timeout(600)
