@@ -424,12 +424,18 @@ __device__ __forceinline__ void scheduler_loop(const KArgs& a, uint32_t epoch, u
 
 }  // namespace
 
+// One source, three kernels: the default runtime (this file), the paged
+// lookahead (MPK_LA, megakernel_la.hip) and the batch > 1 runtime (MPK_BN,
+// megakernel_bn.hip), each a translation unit of its own so that a change
+// made for one leaves the others' code as it is.
 #if MPK_LA
-#define MPK_MEGAKERNEL mpk_megakernel_la
+#define MPK_K(name) name##_la
+#elif MPK_BN
+#define MPK_K(name) name##_bn
 #else
-#define MPK_MEGAKERNEL mpk_megakernel
+#define MPK_K(name) name
 #endif
-__global__ void __launch_bounds__(kThreads) MPK_MEGAKERNEL(const KArgs args, uint32_t epoch, uint64_t timeout) {
+__global__ void __launch_bounds__(kThreads) MPK_K(mpk_megakernel)(const KArgs args, uint32_t epoch, uint64_t timeout) {
   // `args` is the first kernel argument: it starts the kernel-argument segment
   const kptr kp = (kptr)(__builtin_amdgcn_kernarg_segment_ptr());
   const KArgs a = args;
@@ -444,20 +450,11 @@ __global__ void __launch_bounds__(kThreads) MPK_MEGAKERNEL(const KArgs args, uin
   if (w < a.n_workers) worker_loop(kp, epoch, timeout, w);
 }
 
-#if MPK_LA
-hipError_t launch_megakernel_la(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream) {
-  KArgs a = args;
-  void* p[] = {&a, &epoch, &timeout};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mpk_megakernel_la), dim3(grid), dim3(kThreads),
-                                    p, 0, stream);
-}
-#else
-hipError_t launch_megakernel_la(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
-
+#if !MPK_LA
 // Kernel-per-operator baseline: workgroup i runs task list[i], no events (a
 // projection tile issues its weight pre-load first, as in the persistent
 // kernel).  A poisoned graph runs nothing.
-__global__ void __launch_bounds__(kThreads) mpk_baseline_op(const KArgs a, const int32_t* list) {
+__global__ void __launch_bounds__(kThreads) MPK_K(mpk_baseline_op)(const KArgs a, const int32_t* list) {
   if (ld_relaxed(reinterpret_cast<gptr<const uint32_t>>(&a.status->code)) != 0u) return;
   const DevTask t = a.tasks[list[blockIdx.x]];
   const TaskPtrs P = task_ptrs(a, t);
@@ -467,8 +464,8 @@ __global__ void __launch_bounds__(kThreads) mpk_baseline_op(const KArgs a, const
 }
 
 // Body timing: one workgroup runs one task and adds its wall-clock ticks to *out.
-__global__ void __launch_bounds__(kThreads) mpk_time_task_kernel(const KArgs a, int task, int cold,
-                                                                  unsigned long long* out) {
+__global__ void __launch_bounds__(kThreads) MPK_K(mpk_time_task_kernel)(const KArgs a, int task, int cold,
+                                                                         unsigned long long* out) {
   const DevTask t = a.tasks[task];
   const TaskPtrs P = task_ptrs(a, t);
   __syncthreads();
@@ -478,8 +475,35 @@ __global__ void __launch_bounds__(kThreads) mpk_time_task_kernel(const KArgs a, 
   __syncthreads();
   if (threadIdx.x == 0) *out += wall_clock64() - t0;
 }
+#endif
 
+#if MPK_LA || MPK_BN
+hipError_t MPK_K(launch_megakernel)(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream) {
+  KArgs a = args;
+  void* p[] = {&a, &epoch, &timeout};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&MPK_K(mpk_megakernel)), dim3(grid), dim3(kThreads),
+                                    p, 0, stream);
+}
+#endif
+#if MPK_BN
+hipError_t launch_baseline_op_bn(const KArgs& args, const int32_t* list, int count, hipStream_t stream) {
+  hipLaunchKernelGGL(mpk_baseline_op_bn, dim3(count), dim3(kThreads), 0, stream, args, list);
+  return hipGetLastError();
+}
+hipError_t launch_time_task_bn(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream) {
+  hipLaunchKernelGGL(mpk_time_task_kernel_bn, dim3(1), dim3(kThreads), 0, stream, args, task, cold ? 1 : 0, out);
+  return hipGetLastError();
+}
+#endif
+#if !MPK_LA && !MPK_BN
+hipError_t launch_megakernel_la(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
+hipError_t launch_megakernel_bn(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream);
+hipError_t launch_baseline_op_bn(const KArgs& args, const int32_t* list, int count, hipStream_t stream);
+hipError_t launch_time_task_bn(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream);
+
+// (batch > 1: the batch > 1 runtime's kernels)
 hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned long long* out, hipStream_t stream) {
+  if (args.B > 1) return launch_time_task_bn(args, task, cold, out, stream);
   hipLaunchKernelGGL(mpk_time_task_kernel, dim3(1), dim3(kThreads), 0, stream, args, task, cold ? 1 : 0, out);
   return hipGetLastError();
 }
@@ -487,6 +511,7 @@ hipError_t launch_time_task(const KArgs& args, int task, bool cold, unsigned lon
 hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout, int grid, hipStream_t stream,
                              bool lookahead) {
   if (lookahead) return launch_megakernel_la(args, epoch, timeout, grid, stream);
+  if (args.B > 1) return launch_megakernel_bn(args, epoch, timeout, grid, stream);
   KArgs a = args;
   void* p[] = {&a, &epoch, &timeout};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&mpk_megakernel), dim3(grid), dim3(kThreads), p,
@@ -494,10 +519,10 @@ hipError_t launch_megakernel(const KArgs& args, uint32_t epoch, uint64_t timeout
 }
 
 hipError_t launch_baseline_op(const KArgs& args, const int32_t* list, int count, hipStream_t stream) {
+  if (args.B > 1) return launch_baseline_op_bn(args, list, count, stream);
   hipLaunchKernelGGL(mpk_baseline_op, dim3(count), dim3(kThreads), 0, stream, args, list);
   return hipGetLastError();
 }
-
-#endif  // MPK_LA
+#endif
 
 }  // namespace mpk

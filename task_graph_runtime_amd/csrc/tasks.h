@@ -778,6 +778,9 @@ __device__ __forceinline__ void xs_finish(const KArgs& a, const XSrc& x, char* l
 #ifndef MPK_LA
 #define MPK_LA 0   // 1: the paged lookahead's kernel (megakernel_la.hip)
 #endif
+#ifndef MPK_BN
+#define MPK_BN 0   // 1: the batch > 1 kernels (megakernel_bn.hip)
+#endif
 #ifndef MPK_B1_CHUNK
 #define MPK_B1_CHUNK 4
 #endif
