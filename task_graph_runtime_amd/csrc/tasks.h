@@ -1499,6 +1499,53 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
     return (int64_t)(pid >= 0 ? pid : 0) * page_stride + (int64_t)(tok % P) * D;
   };
   auto good = [&](int tok) { return tok < tc1 && pids[tok / P - j0] >= 0; };
+#if MPK_BN
+  // (batch > 1: the splits are long and the loop is bound by its VALU work.
+  // The running state (m, lsum, ov) is exact for any reference m, since
+  // lsum = sum exp(p - m) and ov = sum exp(p - m) v; m is raised only when a
+  // score exceeds it by more than kLazy, so exp(p - m) stays below e^8 and
+  // the per-key rescale of ov is skipped in all but the few steps that raise
+  // it -- a wavefront-uniform branch, taken when any of its rows needs it.)
+  constexpr float kLazy = 8.f;
+  auto process = [&](const float (&kf)[DPL], const float (&vf)[DPL]) {
+    float pr[GM];
+    bool raise = false;
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      pr[h] = 0.f;
+      if (h < G) {
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) p = fmaf(qv[h][i], kf[i], p);
+        p = row_sum(p);
+        if (R == 32) p += __shfl_xor(p, 16);
+        pr[h] = p;
+        raise |= p > m[h] + kLazy;
+      }
+    }
+    if (__ballot(raise)) {
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G && pr[h] > m[h] + kLazy) {
+          const float al = __expf(m[h] - pr[h]);
+          lsum[h] *= al;
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) ov[h][i] *= al;
+          m[h] = pr[h];
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      if (h < G) {
+        const float e = __expf(pr[h] - m[h]);
+        lsum[h] += e;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) ov[h][i] = fmaf(e, vf[i], ov[h][i]);
+      }
+    }
+  };
+#else
   auto process = [&](const float (&kf)[DPL], const float (&vf)[DPL]) {
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
@@ -1518,6 +1565,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
       }
     }
   };
+#endif
   auto process_bf = [&](const KV& kc, const KV& vc) {
     float kf[DPL], vf[DPL];
     const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kc);

@@ -520,6 +520,24 @@ def test_tiny_head_dim_64_with_qk_norm(B):
     check_cache(inp, cap)
 
 
+@pytest.mark.parametrize("B", [1, 3, 16])
+def test_tiny_peaked_attention(B):
+    """Cached keys scaled by 32 (exact in bf16): the scores spread over
+    hundreds, so the running maximum of the online softmax rises many times
+    within a split -- at batch > 1 every rise past the kernel's margin takes
+    its rescale branch -- and most weights underflow to zero."""
+    s = TINY.with_(batch=B, ctx_range=(120, 250), ctx=0)
+    say("tiny peaked attention", B)
+    inp = device_inputs(s, seed=91 + B)
+    inp["kv"]["k_pool"].mul_(32)
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    for mode in ("mega", "base"):
+        logits, nxt = Runner(inp).run(mode)
+        check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+
+
 @pytest.mark.parametrize("B,H,F", [(1, 264, 712), (1, 520, 1000), (3, 288, 352), (5, 320, 416)])
 def test_odd_widths(B, H, F):
     """Widths that are not multiples of the tile and k-step quanta: at batch 1
