@@ -159,11 +159,35 @@ __device__ __forceinline__ float wave_total(float v) {
   return (__int_as_float(__builtin_amdgcn_readlane(iv, 0)) + __int_as_float(__builtin_amdgcn_readlane(iv, 16))) +
          (__int_as_float(__builtin_amdgcn_readlane(iv, 32)) + __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
 }
+// Lanes MSK = 16 or 32 apart, through gfx950's row-swap permutes (VALU, not
+// the LDS permute network): with both operands v, `ev` gets in every lane
+// the value of the lane of its pair that lies in the even half (rows 0 and 2
+// for 16, lanes 0-31 for 32) and `od` that of the odd one, so a pairwise sum
+// or merge taken in (ev, od) order is bitwise the same in both lanes.
+template <int MSK>
+__device__ __forceinline__ void lane_pair(float v, float& ev, float& od) {
+  static_assert(MSK == 16 || MSK == 32, "rows of 16 or halves of 32");
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (MSK == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    ev = __uint_as_float(r[0]);
+    od = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    ev = __uint_as_float(r[0]);
+    od = __uint_as_float(r[1]);
+  }
+}
+template <int MSK>
+__device__ __forceinline__ float pair_sum(float v) {
+  float ev, od;
+  lane_pair<MSK>(v, ev, od);
+  return ev + od;
+}
 __device__ __forceinline__ float wave_sum(float v) {
   v = row_sum(v);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  v = pair_sum<16>(v);
+  return pair_sum<32>(v);
 }
 
 // Workgroup barrier for LDS data only: the wavefront's LDS operations are
@@ -1518,7 +1542,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
 #pragma unroll
         for (int i = 0; i < DPL; ++i) p = fmaf(qv[h][i], kf[i], p);
         p = row_sum(p);
-        if (R == 32) p += __shfl_xor(p, 16);
+        if (R == 32) p = pair_sum<16>(p);
         pr[h] = p;
         raise |= p > m[h] + kLazy;
       }
@@ -1554,7 +1578,7 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
 #pragma unroll
         for (int i = 0; i < DPL; ++i) p = fmaf(qv[h][i], kf[i], p);
         p = row_sum(p);
-        if (R == 32) p += __shfl_xor(p, 16);
+        if (R == 32) p = pair_sum<16>(p);
         const float mn = fmaxf(m[h], p);
         const float al = __expf(m[h] - mn);
         const float e = __expf(p - mn);
@@ -1621,26 +1645,33 @@ __device__ __forceinline__ void attn_task(const KArgs& a, const DevTask& t, cons
     process(kf, vf);
   }
   mark(a, 1);
-  // merge the row states of the wavefront (lanes lr, lr+R, ...)
-#pragma unroll
-  for (int msk = R; msk <= 32; msk <<= 1) {
+  // merge the row states of the wavefront (lanes lr, lr+R, ...), each pair
+  // in (even, odd) order so that both of its lanes hold the same state
+  auto merge_rows = [&](auto msk_c) {
+    constexpr int MSK = decltype(msk_c)::value;
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       if (h < G) {
-        const float m2 = __shfl_xor(m[h], msk), l2 = __shfl_xor(lsum[h], msk);
-        const float mn = fmaxf(m[h], m2);
-        const float a1 = (m[h] == -INFINITY) ? 0.f : __expf(m[h] - mn);
+        float m1, m2, l1, l2;
+        lane_pair<MSK>(m[h], m1, m2);
+        lane_pair<MSK>(lsum[h], l1, l2);
+        const float mn = fmaxf(m1, m2);
+        const float a1 = (m1 == -INFINITY) ? 0.f : __expf(m1 - mn);
         const float a2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - mn);
-        lsum[h] = lsum[h] * a1 + l2 * a2;
+        lsum[h] = l1 * a1 + l2 * a2;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) {
-          const float o2 = __shfl_xor(ov[h][i], msk);
-          ov[h][i] = ov[h][i] * a1 + o2 * a2;
+          float o1, o2;
+          lane_pair<MSK>(ov[h][i], o1, o2);
+          ov[h][i] = o1 * a1 + o2 * a2;
         }
         m[h] = mn;
       }
     }
-  }
+  };
+  static_assert(R == 16 || R == 32, "16 or 32 lanes per row");
+  if constexpr (R == 16) merge_rows(std::integral_constant<int, 16>{});
+  merge_rows(std::integral_constant<int, 32>{});
   // merge the wavefronts through LDS: per wave, per head: m, l, o[D]
   float* st = reinterpret_cast<float*>(lds);  // [kWaves][G][D + 2]
   if (row == 0) {
