@@ -317,10 +317,10 @@ def test_reset_recovers_a_poisoned_graph():
 
 
 # ------------------------------------------------------------------ real shapes
-def _full(name, seed=0, modes=("mega",), lazy=False, builds=()):
+def _full(name, seed=0, modes=("mega",), lazy=False, builds=(), seq_lens=None):
     s = synth.SHAPES[name]
-    say(name, "generate")
-    inp = device_inputs(s, seed=seed)
+    say(name, "generate", "" if seq_lens is None else f"lengths {min(seq_lens)}..{max(seq_lens)}")
+    inp = device_inputs(s, seed=seed, seq_lens=seq_lens)
     say(name, "oracle")
     ref, ref_next = run_oracle(inp, lazy=lazy, widen_on_device=True)
     r = Runner(inp)
@@ -375,6 +375,24 @@ def test_qwen3_8b_shape():
 def test_qwen3_8b_batch16_shape():
     # (default AOT attention, and the hybrid policy's JIT attention)
     _full("qwen3_8b_b16", modes=("mega",), lazy=True, builds=(dict(attn_jit=1),))
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_longest_context():
+    """The 8B step at the longest cached length the shape takes (8191 =
+    max_seq_len - 1): the request's page table full, the run-time split
+    count at its cap, the new token in the last slot of the last page."""
+    s = synth.SHAPES["qwen3_8b"]
+    _full("qwen3_8b", lazy=True, seq_lens=[s.max_seq_len - 1])
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_batch16_skewed():
+    """The skewed batch of the scheduling ablation -- one request at the
+    longest length, fifteen at 256 -- under the default placement and under
+    the hybrid policy (attention JIT)."""
+    s = synth.SHAPES["qwen3_8b_b16"]
+    _full("qwen3_8b_b16", lazy=True, seq_lens=[s.max_seq_len - 1] + [256] * (s.batch - 1), builds=(dict(attn_jit=1),))
 
 
 @pytest.mark.timeout(900)
