@@ -224,3 +224,24 @@ def test_perfetto_export_of_a_simulated_step(tmp_path):
     assert all(s_ev[i] <= f_ev[i] + 1e-9 for i in s_ev)
     names = {e["name"].split()[0] for e in tasks}
     assert {"qkv", "attn", "oproj", "gateup", "down", "lmhead", "argmax"} <= names
+
+
+def test_phase_table_of_a_simulated_step():
+    """The per-phase summary (trace_phases) on the schedule of a simulated step:
+    one row per task type of the layer, in start order, every non-empty task
+    counted once, gaps measured from the previous phase's last end."""
+    from task_graph_runtime_amd import trace_phases
+    g = export(TINY, 3, dict(n_workers=8, n_sched_waves=2, s_attn=6, attn_jit=1))
+    st = simulate(g, steps=1, seed=7, trace=True)
+    rec = st.trace
+    for layer in (0, 1, -1):
+        rows = trace_phases.phase_table(rec, TICKS_PER_UNIT, g, layer)
+        real = [t for t in np.nonzero(g["task_layer"] == layer)[0] if g["task_mode"][t] != 2]
+        assert sum(r["n"] for r in rows) == len(real)
+        assert [r["start"] for r in rows] == sorted(r["start"] for r in rows)
+        assert rows[0]["gap"] is None and rows[0]["start"] == 0.0
+        for a, b in zip(rows, rows[1:]):
+            assert abs(b["gap"] - (b["start"] - a["end"])) < 1e-9
+        assert all(r["span"] >= r["task"] - 1e-9 for r in rows)
+    text = trace_phases.markdown(trace_phases.phase_table(rec, TICKS_PER_UNIT, g, 0))
+    assert text.count("\n") == 1 + len(trace_phases.phase_table(rec, TICKS_PER_UNIT, g, 0))
