@@ -121,6 +121,28 @@ int resolve_params(const mpk_model_cfg& c, int32_t B, int32_t P, const mpk_build
     if (c.n_kv_heads % k == 0 && (p.t_o <= 0 || p.t_o % k == 0)) { ko_def = k; break; }
   r.K_o = p.k_o > 0 ? p.k_o : (B > 1 ? ko_def : 1);
   r.K_down = p.k_down > 0 ? p.k_down : (B > 1 && c.n_experts == 0 && (p.t_down <= 0 || p.t_down % 3 == 0) ? 3 : 1);
+  // (a batch > 1 norm task stages the gain, the residual row and every plane
+  // of its input in LDS: the default splits shrink, the larger first, until
+  // that takes at most 128 KB, leaving the rest of the 160 KB to the
+  // accumulators, page ids and control words; splits given stay as given)
+  if (B > 1) {
+    auto kb = [](int64_t bytes) { return (bytes + 1023) / 1024 * 1024; };
+    auto fits = [&]() { return kb(H * 2) + (1 + std::max(r.K_o, r.K_down)) * kb(H * 4) <= 128 * 1024; };
+    while (!fits()) {
+      const bool can_o = p.k_o <= 0 && r.K_o > 1, can_d = p.k_down <= 0 && r.K_down > 1;
+      if (can_o && (r.K_o >= r.K_down || !can_d)) {
+        int32_t k = r.K_o - 1;
+        while (k > 1 && (c.n_kv_heads % k || (p.t_o > 0 && p.t_o % k))) --k;
+        r.K_o = k;
+      } else if (can_d) {
+        int32_t k = r.K_down - 1;
+        while (k > 1 && p.t_down > 0 && p.t_down % k) --k;
+        r.K_down = k;
+      } else {
+        break;   // (the layout check refuses the shape)
+      }
+    }
+  }
   if (c.n_experts > 0 && r.K_down != 1)
     return uns("k_down must be 1 with experts (their outputs accumulate into one plane)");
   if (B == 1 && (r.K_qkv != 1 || r.K_o != 1 || r.K_down != 1))

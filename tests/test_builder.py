@@ -204,6 +204,27 @@ def test_default_params_resolve_as_documented():
     assert (p["k_qkv"], p["k_o"], p["k_down"]) == (1, 1, 1)
 
 
+def test_default_k_splits_fit_the_norm_staging():
+    """At batch > 1 a norm task stages the gain (bf16), the residual row and
+    every k-split plane of its input (fp32) in LDS: at hidden 8192 the
+    default splits (4 and 3) would need 176 KB, so they shrink until the
+    staging takes at most 128 KB; the 8B and 32B shapes keep theirs, and
+    splits given explicitly are kept."""
+    kb = lambda b: (b + 1023) // 1024 * 1024
+    big = synth.SHAPES["tiny"].with_(hidden=8192, n_q_heads=64, n_kv_heads=8, head_dim=128, ffn=24576)
+    for B in (3, 16):
+        p = mpk.TGraph(big.cfg(), B, big.page_size, {}, host_only=True).header()["params"]
+        assert kb(8192 * 2) + (1 + max(p["k_o"], p["k_down"])) * kb(8192 * 4) <= 128 * 1024, p
+        assert p["k_o"] >= 1 and 8 % p["k_o"] == 0 and p["k_down"] >= 1
+        assert p["t_o"] % p["k_o"] == 0 and p["t_down"] % p["k_down"] == 0
+    given = mpk.TGraph(big.cfg(), 3, big.page_size, dict(k_o=4, k_down=3), host_only=True).header()["params"]
+    assert (given["k_o"], given["k_down"]) == (4, 3)
+    for name, K in (("qwen3_8b", (4, 3)), ("qwen3_32b", (4, 3))):
+        s = synth.SHAPES[name]
+        p = mpk.TGraph(s.cfg(), 16, s.page_size, {}, host_only=True).header()["params"]
+        assert (p["k_o"], p["k_down"]) == K, (name, p)
+
+
 @settings(max_examples=120, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(programs())
 def test_generic_entry_matches_spec(prog):

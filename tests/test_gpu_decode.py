@@ -556,6 +556,29 @@ def test_tiny_peaked_attention(B):
     check_cache(inp, cap)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B", [1, 3])
+def test_largest_hidden(B):
+    """The largest hidden size the kernels take (8192: the batch-1 tiles'
+    staging registers full) with 64 query heads and FFN 24576, two layers: at
+    batch 1 the pre-load shrinks to 8 segments per wavefront behind a 96 KB
+    staging area, at batch 3 the default k-splits shrink to fit the norm
+    tasks' staging in LDS."""
+    s = TINY.with_(hidden=8192, n_q_heads=64, n_kv_heads=8, head_dim=128, ffn=24576, batch=B, ctx_range=(30, 200),
+                   ctx=0)
+    say("largest hidden", B)
+    inp = device_inputs(s, seed=131 + B, gamma="uniform")
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    r = Runner(inp)
+    for mode in ("mega", "base"):
+        logits, nxt = r.run(mode)
+        check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+    del r
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("B,H,F", [(1, 264, 712), (1, 520, 1000), (3, 288, 352), (5, 320, 416)])
 def test_odd_widths(B, H, F):
     """Widths that are not multiples of the tile and k-step quanta: at batch 1
