@@ -556,14 +556,31 @@ def test_tiny_peaked_attention(B):
     check_cache(inp, cap)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.parametrize("P", [16, 32, 64])
 @pytest.mark.parametrize("B", [1, 3])
+def test_tiny_page_sizes(P, B):
+    """Every page size the library takes (16, 32, 64 tokens) with ragged
+    lengths that end inside, and exactly at the end of, a page."""
+    s = TINY.with_(page_size=P, batch=B, ctx_range=(P - 1, 230), ctx=0)
+    say("tiny page size", P, B)
+    lens = [P - 1, 2 * P, 229][:B] if B > 1 else [3 * P - 1]
+    inp = device_inputs(s, seed=141 + P + B, gamma="uniform", seq_lens=lens)
+    cap = {}
+    ref, ref_next = run_oracle(inp, capture=cap)
+    for mode in ("mega", "base"):
+        logits, nxt = Runner(inp).run(mode)
+        check(logits, nxt, ref, ref_next)
+    check_cache(inp, cap)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("B", [1, 3, 16])
 def test_largest_hidden(B):
     """The largest hidden size the kernels take (8192: the batch-1 tiles'
     staging registers full) with 64 query heads and FFN 24576, two layers: at
     batch 1 the pre-load shrinks to 8 segments per wavefront behind a 96 KB
-    staging area, at batch 3 the default k-splits shrink to fit the norm
-    tasks' staging in LDS."""
+    staging area, at batch 3 and 16 the default k-splits shrink to fit the
+    norm tasks' staging in LDS."""
     s = TINY.with_(hidden=8192, n_q_heads=64, n_kv_heads=8, head_dim=128, ffn=24576, batch=B, ctx_range=(30, 200),
                    ctx=0)
     say("largest hidden", B)
