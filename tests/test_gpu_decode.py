@@ -197,6 +197,9 @@ def test_tiny_eight_query_heads_per_group(B):
     (3, [0, 15, 16]),              # empty context; new token ends a page; new token opens a page
     (4, [1, 31, 100, 255]),        # 255 = max_seq_len - 1: the last slot
     (16, None),                    # batch 16, ragged lengths
+    (1, [0]),                      # the first token of a request: attention over itself alone
+    (16, [0] * 16),                # a full batch of first tokens
+    (16, [255] * 16),              # a full batch at the last slot
 ])
 @pytest.mark.parametrize("mode", ["mega", "base"])
 def test_tiny_ragged(B, lens, mode):
