@@ -1017,7 +1017,11 @@ __device__ __forceinline__ gptr<const uint16_t> packed_block(const KArgs& a, int
 // loads repeat block rb1 - 1 and their sums are dropped).
 template <int NRB, int KG>
 __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
-                                          float* acc, int nrows, int rb0, int rb1, int ks0, int ks1) {
+                                          float* acc, int nrows, int rb0, int rb1, int ks0, int ks1
+#if MPK_BN
+                                          , bool own   // acc is this wavefront's own slice: store, no atomics
+#endif
+                                          ) {
   const int lane = tidx() & 63, li = lane & 15, lg = lane >> 4;
   const int K = op.K, B = a.B;
   const int nkg = (ks1 - ks0 + KG - 1) / KG;
@@ -1091,15 +1095,30 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (rb0 + r) * 16 + lg * 4 + i;
+#if MPK_BN
+      if (li < B && row < nrows && rb0 + r < rb1) {
+        if (own) acc[row * B + li] = c[r][i];
+        else atomicAdd(&acc[row * B + li], c[r][i]);
+      }
+#else
       if (li < B && row < nrows && rb0 + r < rb1) atomicAdd(&acc[row * B + li], c[r][i]);
+#endif
     }
 }
 
+#if MPK_BN
+template <int NRB, int KG>
+__device__ __forceinline__ void mfma_passes(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
+                                            float* acc, int nrows, int rb_lo, int rb_hi, int ks0, int ks1, bool own) {
+  for (int rb0 = rb_lo; rb0 < rb_hi; rb0 += NRB) mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, rb_hi, ks0, ks1, own);
+}
+#else
 template <int NRB, int KG>
 __device__ __forceinline__ void mfma_passes(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
                                             float* acc, int nrows, int rb_lo, int rb_hi, int ks0, int ks1) {
   for (int rb0 = rb_lo; rb0 < rb_hi; rb0 += NRB) mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, rb_hi, ks0, ks1);
 }
+#endif
 
 __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, const TaskPtrs& P, char* lds,
                                           const GemvOp& op) {
@@ -1136,6 +1155,33 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
   // in the writer's L2 only the bytes that XCD wrote -- a write does not
   // fill the line -- so the read fetches the line, whose other bytes the
   // other tile's write-through stores have reached.
+#if MPK_BN
+  // (the wavefronts' partial sums: when the wavefronts split the
+  // contraction and their slices fit in the staging area, which a
+  // matrix-core tile does not use, each wavefront stores its own slice and
+  // they are summed below in wavefront order; else they are added into acc
+  // with LDS atomics.  Eight atomics on every accumulator, one per
+  // wavefront, cost a tile alone 4-10 us.)
+  const bool own = !by_rows && kWaves * nrows * B * 4 <= a.lds_acc;
+  float* part = reinterpret_cast<float*>(lds);
+  float* dst = own ? part + (int64_t)w * nrows * B : acc;
+  if (ks1 > ks0 && nb > 0) {
+    // weights in flight per wavefront: NRB x KG KB
+    if (nb <= 2) mfma_passes<2, 4>(a, t, P, op, dst, nrows, rb_lo, rb_hi, ks0, ks1, own);
+    else if (nb <= 4) mfma_passes<4, 4>(a, t, P, op, dst, nrows, rb_lo, rb_hi, ks0, ks1, own);
+    else mfma_passes<8, 2>(a, t, P, op, dst, nrows, rb_lo, rb_hi, ks0, ks1, own);
+  }
+  __syncthreads();
+  if (own) {   // (a wavefront with an empty k range stored nothing)
+    for (int i = tid0; i < nrows * B; i += kThreads) {
+      float v = 0.f;
+      for (int u = 0; u < kWaves; ++u)
+        if (nks * (u + 1) / kWaves > nks * u / kWaves) v += part[(int64_t)u * nrows * B + i];
+      acc[i] = v;
+    }
+    __syncthreads();
+  }
+#else
   if (ks1 > ks0 && nb > 0) {
     // weights in flight per wavefront: NRB x KG KB
     if (nb <= 2) mfma_passes<2, 4>(a, t, P, op, acc, nrows, rb_lo, rb_hi, ks0, ks1);
@@ -1143,6 +1189,7 @@ __device__ __forceinline__ void gemv_mfma(const KArgs& a, const DevTask& t, cons
     else mfma_passes<8, 2>(a, t, P, op, acc, nrows, rb_lo, rb_hi, ks0, ks1);
   }
   __syncthreads();
+#endif
   mark(a, 1);
   gemv_epilogue(a, t, acc, red, kr);
 }
