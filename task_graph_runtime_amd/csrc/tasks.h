@@ -1290,19 +1290,36 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
     }
     __syncthreads();
   }
+  // (the splits in groups of four whose loads go out together, one wait per
+  // group instead of one per split; the sums still run in split order)
   auto merge = [&](auto at) {
     for (int e = tid0; e < G * D; e += kThreads) {
-      const int h = e / D, dd = e - h * D;
+      const int h = e / D, dd = e - h * D, hb = h * (D + 2);
       float M = -INFINITY;
-      for (int s_ = 0; s_ < S; ++s_) M = fmaxf(M, at(s_ * rec + h * (D + 2)));
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        float mm[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mm[u] = at(min(s0 + u, S - 1) * rec + hb);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) M = fmaxf(M, mm[u]);
+      }
       float L = 0.f, O = 0.f;
-      for (int s_ = 0; s_ < S; ++s_) {
-        const int r0 = s_ * rec + h * (D + 2);
-        const float ms = at(r0);
-        if (ms != -INFINITY) {
-          const float f = __expf(ms - M);
-          L = fmaf(at(r0 + 1), f, L);
-          O = fmaf(at(r0 + 2 + dd), f, O);
+      for (int s0 = 0; s0 < S; s0 += 4) {
+        float ms[4], ls[4], os[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r0 = min(s0 + u, S - 1) * rec + hb;
+          ms[u] = at(r0);
+          ls[u] = at(r0 + 1);
+          os[u] = at(r0 + 2 + dd);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (s0 + u < S && ms[u] != -INFINITY) {
+            const float f = __expf(ms[u] - M);
+            L = fmaf(ls[u], f, L);
+            O = fmaf(os[u], f, O);
+          }
         }
       }
       st_coh(out + h * D + dd, L > 0.f ? O / L : 0.f);
