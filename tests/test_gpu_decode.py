@@ -287,6 +287,28 @@ def test_bad_token_id_reported_not_faulting():
     assert r.g.status()["code"] == -1
 
 
+@pytest.mark.parametrize("params", [{}, {"attn_jit": 1}])
+@pytest.mark.parametrize("what", ["page", "length"])
+def test_bad_page_or_length_reported_not_faulting(what, params):
+    """A page id outside the pool, or a cached length past the graph's
+    longest, at batch 1: the attention splits report MPK_ERR_INVALID_ARG
+    (a bad page is read as page 0 and its keys are not used) and the step
+    ends without a fault.  With every task ahead of time the splits' page ids
+    and length are read while the workers wait; with attention JIT, by the
+    splits themselves."""
+    say("bad", what, params)
+    inp = device_inputs(TINY, seed=1)
+    if what == "page":
+        n_pages = inp["kv"]["k_pool"].shape[1]
+        inp["kv"]["page_table_dev"][0, 0] = n_pages + 3
+    else:
+        inp["seq_lens_dev"] = torch.tensor([TINY.max_seq_len + 7], dtype=torch.int32, device="cuda")
+    r = Runner(inp, params)
+    r.g.decode_step(r.w, inp["token_ids_dev"], r.kv, inp["seq_lens_dev"], r.logits, r.next)
+    torch.cuda.synchronize()
+    assert r.g.status()["code"] == -1
+
+
 def test_reset_recovers_a_poisoned_graph():
     """mpk_reset_tgraph: a graph poisoned by a watchdog timeout, then by a bad
     token id, runs correct steps again after a reset (several in a row, on
