@@ -1277,13 +1277,13 @@ __device__ __forceinline__ void attn_combine(const KArgs& a, int l, int b, int g
   float* st = reinterpret_cast<float*>(lds);
   const int n = S * rec;   // (a multiple of 4: rec = G (D + 2) with D even)
   const bool staged = ((n + 63) & ~63) * 4 <= a.lds_acc;
-  if (staged) {   // staged through registers: all loads in flight at once
-    for (int i0 = 0; i0 < n; i0 += 4 * kThreads * 4) {
-      float4 v[4];
+  if (staged) {   // staged through registers: up to 16K floats in flight at once
+    for (int i0 = 0; i0 < n; i0 += 8 * kThreads * 4) {
+      float4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = ld4_coh(part, i0 + (tid0 + u * kThreads) * 4, n);
+      for (int u = 0; u < 8; ++u) v[u] = ld4_coh(part, i0 + (tid0 + u * kThreads) * 4, n);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = i0 + (tid0 + u * kThreads) * 4;
         if (i < n) *reinterpret_cast<float4*>(st + i) = v[u];
       }
