@@ -111,9 +111,11 @@ __device__ __forceinline__ void wait_vm() {
 // displace other lines of the L2 leaves it to the data tasks share (the
 // activation vectors every tile stages, the attention's pages).  On one
 // MI355X the 8B batch-1 step went from 4.03 to 3.86 ms.  (The matrix-core
-// tiles of batch > 1 read each 128-byte weight line as two 64-byte halves in
-// consecutive contraction steps, so their loads keep the line in the L2:
-// non-temporal loads there measured 7.68 against 7.41 ms.)
+// tiles of batch > 1 read each 128-byte line of row-major weights as two
+// 64-byte halves in consecutive contraction steps, so those loads keep the
+// line in the L2: non-temporal loads there measured 7.68 against 7.41 ms.
+// Prepared weights, whose wavefront loads are whole contiguous 1 KB blocks,
+// are read non-temporally: 6.53-6.55 against 6.64-6.71 ms at 8B batch 16.)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ldw(MPK_GLOBAL const uint16_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<MPK_GLOBAL const u32x4*>(p));
@@ -1015,7 +1017,7 @@ __device__ __forceinline__ gptr<const uint16_t> packed_block(const KArgs& a, int
 // One pass: row blocks [rb0, min(rb0 + NRB, rb1)) over the wavefront's
 // k-steps [ks0, ks1) (blocks from rb1 on belong to other wavefronts: their
 // loads repeat block rb1 - 1 and their sums are dropped).
-template <int NRB, int KG>
+template <int NRB, int KG, bool NT = false>
 __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
                                           float* acc, int nrows, int rb0, int rb1, int ks0, int ks1
 #if MPK_BN
@@ -1044,8 +1046,14 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
   // (prepared weights: k-step ks of a block is the 1 KB at ks * 512 elements)
   auto wload = [&](int kg, int r) {
 #pragma unroll
-    for (int j = 0; j < KG; ++j)
+    for (int j = 0; j < KG; ++j) {
+#if MPK_BN
+      // (NT: prepared weights, each 1 KB block read once, non-temporally)
+      if constexpr (NT) wv[r][j] = ldw(rows[r] + min(ks0 + kg * KG + j, ks1 - 1) * 512);
+      else
+#endif
       wv[r][j] = ldg<uint4>(rows[r] + (a.wpacked ? min(ks0 + kg * KG + j, ks1 - 1) * 512 : kof(kg, j)));
+    }
   };
   auto xload = [&](int kg) {
 #pragma unroll
@@ -1110,7 +1118,13 @@ __device__ __forceinline__ void mfma_pass(const KArgs& a, const DevTask& t, cons
 template <int NRB, int KG>
 __device__ __forceinline__ void mfma_passes(const KArgs& a, const DevTask& t, const TaskPtrs& P, const GemvOp& op,
                                             float* acc, int nrows, int rb_lo, int rb_hi, int ks0, int ks1, bool own) {
-  for (int rb0 = rb_lo; rb0 < rb_hi; rb0 += NRB) mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, rb_hi, ks0, ks1, own);
+  if (a.wpacked) {
+    for (int rb0 = rb_lo; rb0 < rb_hi; rb0 += NRB)
+      mfma_pass<NRB, KG, true>(a, t, P, op, acc, nrows, rb0, rb_hi, ks0, ks1, own);
+  } else {
+    for (int rb0 = rb_lo; rb0 < rb_hi; rb0 += NRB)
+      mfma_pass<NRB, KG>(a, t, P, op, acc, nrows, rb0, rb_hi, ks0, ks1, own);
+  }
 }
 #else
 template <int NRB, int KG>
